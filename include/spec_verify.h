@@ -1,0 +1,209 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) verify-and-commit library for
+ * batch speculative decoding.
+ *
+ * One call per step of the step's hot path; each call is a hand-written HIP
+ * kernel.  Sources (web pages, cited by title and section):
+ *   [Forensics]   "Correctness Forensics for Batch Speculative Decoding:
+ *                 Diagnosing the Ragged Tensor Problem" (paper summary),
+ *                 sections 3, 3.1, 3.2, App. B, App. D.
+ *   [Walkthrough] zero-to-sglang "Chapter 10 Speculative Decoding (Code
+ *                 Walkthrough)", sections 3.3, 4.1, 5.1, 5.2.
+ *   [Atlas]       "Speculative decoding: proposals and verified output" (Atlas
+ *                 lesson), The mechanism; Acceptance and rejection correction;
+ *                 Interfaces.
+ *
+ * Conventions shared by every call
+ *   - Every array argument is a DEVICE pointer owned by the caller; the library
+ *     allocates, frees and keeps nothing.  Scalars are host values.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream).  It returns after enqueueing its kernel, with no host sync.
+ *   - Host-checkable argument errors return a negative code before anything is
+ *     enqueued and before any HIP runtime call.  A failed kernel launch returns
+ *     SPEC_EHIP.  Data-dependent anomalies never fail a call: they set per-
+ *     sequence status bits (SPEC_ST_*).
+ *   - Output arrays must not overlap input arrays or each other.
+ *   - Workspaces ("ws") are device memory of at least the queried size, 256-byte
+ *     aligned.  They must be ZERO-FILLED before their first use; every call that
+ *     runs to completion leaves them zero-filled again, so a workspace is
+ *     zeroed once at allocation and then reused.  Calls that may run at the same
+ *     time (different streams) need different workspaces.
+ *   - Token ids are int32 in [0, V).  Layouts are row-major, last index fastest.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *spec_stream_t; /* hipStream_t */
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+/* return codes */
+#define SPEC_OK 0
+#define SPEC_EINVAL (-1)     /* bad pointer, size, alignment or overlap */
+#define SPEC_EWORKSPACE (-2) /* ws_bytes below the queried size, or ws misaligned */
+#define SPEC_ECAPACITY (-3)  /* a size exceeds a documented maximum */
+#define SPEC_EHIP (-4)       /* the HIP runtime reported an error at launch */
+
+/* per-sequence status bits (status[b]) */
+#define SPEC_ST_DRAFT_OOR 1   /* a draft id outside [0, V): counted as mismatch / rejection */
+#define SPEC_ST_Q_ZERO 2      /* q_j(x) == 0 at a proposed x: a = 1 if p_j(x) > 0, else 0 */
+#define SPEC_ST_RESID_ZERO 4  /* the row drawn from had no positive mass; fallback used */
+#define SPEC_ST_NONFINITE 8   /* a gathered probability or a drawn row's mass is not finite */
+#define SPEC_ST_BAD_STATE 16  /* commit: n_b outside [0, E] or e_b outside [0, k+1] */
+#define SPEC_ST_CAPACITY 32   /* commit: E < 0 or E + k + 1 > C */
+
+#define SPEC_MAX_K 127          /* largest number of proposals k per sequence */
+#define SPEC_GROUP_MAX_N 4096   /* largest window for spec_group_same_length */
+
+/* Human-readable name of a return code. */
+const char *spec_strerror(int code);
+
+/* ------------------------------------------------------------------------ *
+ * Greedy verification.
+ * [Walkthrough] 3.3 (row alignment) and 4.1 (greedy commitment); [Forensics]
+ * App. D (BatchVerify).  Row j of sequence b verifies draft j; row k is the
+ * bonus row (in a full-prefix forward over L confirmed tokens these are rows
+ * L-1 .. L+k-1).  For each sequence: emit t_j = argmax(row j) for j = 0, 1, ...
+ * and stop after emitting EOS, after emitting `remaining[b]` tokens, or after
+ * the first j with t_j != draft[b, j]; if no stop happened, also emit
+ * argmax(row k).  remaining[b] == 0 emits nothing; a negative remaining[b]
+ * means no budget.  Ties: the lowest index among equal maxima; -0 == +0; a row
+ * of -inf gives index 0; NaN inputs give unspecified results.
+ *
+ *   logits      [B, k+1, V] of dt (bf16 or f32), element-aligned
+ *   draft       [B, k] int32
+ *   eos_id      EOS token id, or -1 for none
+ *   remaining   [B] int32 output budget, or NULL for none
+ *   accept_len  [B]   out: number of accepted drafts m_b
+ *   emit_count  [B]   out: number of emitted tokens e_b (0 .. k+1)
+ *   out_tokens  [B, k+1] out: emitted tokens, -1 after the first e_b
+ *   emit_offsets[B+1] out or NULL: exclusive prefix sum of emit_count
+ *   status      [B]   out or NULL: SPEC_ST_DRAFT_OOR if any draft[b, j] is
+ *                     outside [0, V)
+ *   ws          workspace of spec_verify_greedy_workspace_bytes(B, k, V, dt)
+ * Errors: SPEC_EINVAL for NULL required pointers, B < 1, k < 1, V < 1,
+ * V >= 2^31 - 1 or a misaligned logits pointer; SPEC_ECAPACITY for
+ * k > SPEC_MAX_K; SPEC_EWORKSPACE.
+ * ------------------------------------------------------------------------ */
+size_t spec_verify_greedy_workspace_bytes(int B, int k, int V, spec_dtype dt);
+int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int k, int V,
+                       const int32_t *draft, int32_t eos_id, const int32_t *remaining,
+                       int32_t *accept_len, int32_t *emit_count, int32_t *out_tokens,
+                       int32_t *emit_offsets, int32_t *status,
+                       void *ws, size_t ws_bytes, spec_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Stochastic (Leviathan-style) verification.
+ * [Atlas] The mechanism steps 2-5 and Acceptance and rejection correction;
+ * [Walkthrough] 5.1.  For j = 0, 1, ...: x = draft[b, j],
+ * a = min(1, p[b,j,x] / q[b,j,x]) (one IEEE float32 division); accept x iff
+ * uniforms[b, j] < a.  At the first rejection emit one token drawn from the
+ * positive residual r = max(p[b,j,:] - q[b,j,:], 0) and stop; after k
+ * acceptances emit one token drawn from p[b,k,:].  A draw from mass vector r
+ * with uniform u = uniforms[b, k] returns the smallest v whose inclusive prefix
+ * sum exceeds u * S, S = sum(r) (both accumulated in float64 from the float32
+ * r_v); if rounding leaves no such v, the last v with r_v > 0.  EOS and the
+ * budget stop the round as in greedy verification (no draw after such a stop).
+ * A residual with no positive mass falls back to drawing from p[b,j,:]
+ * (SPEC_ST_RESID_ZERO); a row with no positive mass yields token 0.
+ * q[b,j,x] == 0 gives a = 1 if p[b,j,x] > 0 else 0 (SPEC_ST_Q_ZERO); a draft id
+ * outside [0, V) is rejected (SPEC_ST_DRAFT_OOR).
+ *
+ *   p           [B, k+1, V] float32 target probabilities (used as given)
+ *   q           [B, k, V]   float32 draft probabilities
+ *   draft       [B, k] int32
+ *   uniforms    [B, k+1] float32 in [0, 1): u[b, j<k] decide acceptance,
+ *               u[b, k] is the single draw for the correction or the bonus
+ *   final_mass  [B] float64 out or NULL: S of the row drawn from, 0 if no draw
+ *   other arguments as in spec_verify_greedy
+ *   ws          workspace of spec_verify_sample_workspace_bytes(B, k, V)
+ * Errors: as spec_verify_greedy (p, q, uniforms must be 4-byte aligned).
+ * ------------------------------------------------------------------------ */
+size_t spec_verify_sample_workspace_bytes(int B, int k, int V);
+int spec_verify_sample(const float *p, const float *q, const int32_t *draft,
+                       const float *uniforms, int B, int k, int V,
+                       int32_t eos_id, const int32_t *remaining,
+                       int32_t *accept_len, int32_t *emit_count, int32_t *out_tokens,
+                       int32_t *emit_offsets, double *final_mass, int32_t *status,
+                       void *ws, size_t ws_bytes, spec_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Commit: realign the contiguous left-padded KV cache, position ids and mask.
+ * [Forensics] section 3 / 3.1 (rectangular alignment, position-id contiguity,
+ * position/KV correspondence) and App. B (realignment keeps retained entries,
+ * drops rejected ones, rebuilds positions from the mask; no shift under
+ * uniform acceptance); App. D and [Walkthrough] 5.2 (the last emitted token
+ * has no KV yet).
+ * Before the call, sequence b's n_b cached rows sit at columns [E - n_b, E) of
+ * every (layer, K/V, head) plane and the verify forward has written its k+1
+ * slots at [E, E + k + 1).  With e_b = emit_count[b], M = max_b e_b and
+ * E' = E + M, the call keeps the first e_b slots and moves columns
+ * [E - n_b, E + e_b) to [E' - n_b - e_b, E'), in place (a right shift by
+ * M - e_b columns; sequences with e_b == M do not move, and cells outside the
+ * destination range are not written).  Then, over all C columns,
+ * mask[b, c] = 1 iff E' - n'_b <= c < E' (n'_b = n_b + e_b), and
+ * pos[b, c] = c - (E' - n'_b) there, 0 elsewhere.
+ *
+ *   kv          [L][2][B][H][C][D] of dt, modified in place
+ *   k           proposals per sequence (the forward wrote k+1 slots)
+ *   end_col     device scalar E (int32)
+ *   kv_len_in   [B] int32 n_b
+ *   emit_count  [B] int32 e_b (as written by a verify call)
+ *   end_col_out device scalar out: E'
+ *   kv_len_out  [B] out: n'_b
+ *   pos_ids     [B, C] int32 out
+ *   mask        [B, C] int32 out (1 / 0)
+ *   bytes_moved device int64 out or NULL: sum over moved sequences of
+ *               2 * n'_b * (L * 2 * H * D * element size)
+ *   status      [B] out or NULL
+ * If E < 0 or E + k + 1 > C (SPEC_ST_CAPACITY on every sequence) or some n_b
+ * is outside [0, E] or e_b outside [0, k+1] (SPEC_ST_BAD_STATE on it), the call
+ * writes only `status` and changes nothing else.
+ * Errors: SPEC_EINVAL for NULL required pointers, L, B, H, C, D or k < 1, a kv
+ * pointer not aligned to the element size, or outputs overlapping inputs.
+ * ------------------------------------------------------------------------ */
+int spec_commit_realign_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, int D, int k,
+                           const int32_t *end_col, const int32_t *kv_len_in,
+                           const int32_t *emit_count, int32_t *end_col_out,
+                           int32_t *kv_len_out, int32_t *pos_ids, int32_t *mask,
+                           int64_t *bytes_moved, int32_t *status, spec_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Same-length grouping of a window of ragged sequences.
+ * [Forensics] 3.2 (EXSPEC: batches of identical-length sequences drawn from a
+ * window larger than the batch size, with unpad-append-repad as the fallback).
+ * The scheduler's own algorithm body is not given on the page; this call
+ * implements the following reading.  Order the window's indices by
+ * (length, index); cut each run of equal lengths into floor(count / B) full
+ * batches, plus one smaller same-length batch if the remainder is at least
+ * min_group, else send the remainder to a fallback list (in (length, index)
+ * order); cut the fallback list into mixed batches of B (the last may be
+ * short).  Same-length batches come first, in ascending length.
+ *
+ *   lengths     [N] int32 (any values)
+ *   perm        [N] out: window indices in batch order
+ *   batch_start [N + 1] out: batch t is perm[batch_start[t] .. batch_start[t+1])
+ *   batch_len   [N] out: the shared length of batch t, or -1 for a mixed batch
+ *   num_batches device int32 out
+ *   num_grouped device int32 out: sequences placed in same-length batches
+ * Entries of batch_start / batch_len past num_batches are not written.
+ * Errors: SPEC_EINVAL for NULL pointers, N < 0, B < 1, min_group < 1;
+ * SPEC_ECAPACITY for N > SPEC_GROUP_MAX_N.
+ * ------------------------------------------------------------------------ */
+int spec_group_same_length(const int32_t *lengths, int N, int B, int min_group,
+                           int32_t *perm, int32_t *batch_start, int32_t *batch_len,
+                           int32_t *num_batches, int32_t *num_grouped,
+                           spec_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,131 @@
+"""MI355X-native verify-and-commit step of batch speculative decoding.
+
+Thin Python binding over libspecverify.so (include/spec_verify.h).  The
+functions carry the C entry points' names and only marshal arguments:
+torch tensors on the GPU become device pointers, the current HIP stream is
+passed along, and a nonzero return code raises SpecError.  Every step runs in
+the library's HIP kernels; there is no other implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+
+SPEC_F32, SPEC_BF16 = 0, 1
+SPEC_OK, SPEC_EINVAL, SPEC_EWORKSPACE, SPEC_ECAPACITY, SPEC_EHIP = 0, -1, -2, -3, -4
+SPEC_ST_DRAFT_OOR, SPEC_ST_Q_ZERO, SPEC_ST_RESID_ZERO = 1, 2, 4
+SPEC_ST_NONFINITE, SPEC_ST_BAD_STATE, SPEC_ST_CAPACITY = 8, 16, 32
+SPEC_MAX_K, SPEC_GROUP_MAX_N = 127, 4096
+
+__all__ = [
+    "SpecError", "spec_strerror", "spec_verify_greedy_workspace_bytes", "spec_verify_greedy",
+    "spec_verify_sample_workspace_bytes", "spec_verify_sample", "spec_commit_realign_kv",
+    "spec_group_same_length", "workspace", "library",
+]
+
+
+class SpecError(RuntimeError):
+    def __init__(self, code: int, name: str):
+        super().__init__(f"{name} failed: {spec_strerror(code)} ({code})")
+        self.code = code
+
+
+def library() -> ctypes.CDLL:
+    return _lib.load()
+
+
+def spec_strerror(code: int) -> str:
+    return library().spec_strerror(int(code)).decode()
+
+
+def _check(code: int, name: str) -> None:
+    if code != SPEC_OK:
+        raise SpecError(code, name)
+
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def workspace(nbytes: int, device=None):
+    """A zero-filled device workspace (zeroed once; the library keeps it zero)."""
+    import torch
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def spec_verify_greedy_workspace_bytes(B: int, k: int, V: int, dtype_code: int) -> int:
+    return int(library().spec_verify_greedy_workspace_bytes(B, k, V, dtype_code))
+
+
+def spec_verify_sample_workspace_bytes(B: int, k: int, V: int) -> int:
+    return int(library().spec_verify_sample_workspace_bytes(B, k, V))
+
+
+def spec_verify_greedy(logits, draft, accept_len, emit_count, out_tokens, ws, *,
+                       eos_id: int = -1, remaining=None, emit_offsets=None, status=None,
+                       stream=None) -> None:
+    """logits [B, k+1, V] (bf16/f32), draft [B, k] int32; outputs int32 tensors."""
+    B, kp1, V = logits.shape
+    code = library().spec_verify_greedy(
+        _ptr(logits), _dtype_code(logits), B, kp1 - 1, V, _ptr(draft), int(eos_id), _ptr(remaining),
+        _ptr(accept_len), _ptr(emit_count), _ptr(out_tokens), _ptr(emit_offsets), _ptr(status),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(code, "spec_verify_greedy")
+
+
+def spec_verify_sample(p, q, draft, uniforms, accept_len, emit_count, out_tokens, ws, *,
+                       eos_id: int = -1, remaining=None, emit_offsets=None, final_mass=None,
+                       status=None, stream=None) -> None:
+    """p [B, k+1, V] f32, q [B, k, V] f32, draft [B, k] int32, uniforms [B, k+1] f32."""
+    B, kp1, V = p.shape
+    code = library().spec_verify_sample(
+        _ptr(p), _ptr(q), _ptr(draft), _ptr(uniforms), B, kp1 - 1, V, int(eos_id), _ptr(remaining),
+        _ptr(accept_len), _ptr(emit_count), _ptr(out_tokens), _ptr(emit_offsets), _ptr(final_mass),
+        _ptr(status), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(code, "spec_verify_sample")
+
+
+def spec_commit_realign_kv(kv, k: int, end_col, kv_len_in, emit_count, end_col_out, kv_len_out,
+                           pos_ids, mask, *, bytes_moved=None, status=None, stream=None) -> None:
+    """kv [L, 2, B, H, C, D] (bf16/f32) is realigned in place."""
+    L, two, B, H, C, D = kv.shape
+    if two != 2:
+        raise ValueError("kv must be [L, 2, B, H, C, D]")
+    code = library().spec_commit_realign_kv(
+        _ptr(kv), _dtype_code(kv), L, B, H, C, D, int(k), _ptr(end_col), _ptr(kv_len_in),
+        _ptr(emit_count), _ptr(end_col_out), _ptr(kv_len_out), _ptr(pos_ids), _ptr(mask),
+        _ptr(bytes_moved), _ptr(status), _stream(stream))
+    _check(code, "spec_commit_realign_kv")
+
+
+def spec_group_same_length(lengths, B: int, min_group: int, perm, batch_start, batch_len,
+                           num_batches, num_grouped, *, stream=None) -> None:
+    """lengths [N] int32; outputs perm [N], batch_start [N+1], batch_len [N], two scalars."""
+    N = lengths.numel()
+    code = library().spec_group_same_length(
+        _ptr(lengths), N, int(B), int(min_group), _ptr(perm), _ptr(batch_start), _ptr(batch_len),
+        _ptr(num_batches), _ptr(num_grouped), _stream(stream))
+    _check(code, "spec_group_same_length")

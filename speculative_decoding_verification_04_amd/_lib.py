@@ -1,0 +1,45 @@
+"""ctypes view of libspecverify.so: one Python prototype per C entry point."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes), mirroring include/spec_verify.h
+PROTOTYPES = {
+    "spec_strerror": (ctypes.c_char_p, [_I]),
+    "spec_verify_greedy_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "spec_verify_greedy": (_I, [_P, _I, _I, _I, _I, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
+                                _P, _SZ, _P]),
+    "spec_verify_sample_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "spec_verify_sample": (_I, [_P, _P, _P, _P, _I, _I, _I, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                _P, _P, _P, _SZ, _P]),
+    "spec_commit_realign_kv": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _P, _P]),
+    "spec_group_same_length": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the built HIP library; raise if it is missing (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB):
+        raise RuntimeError(
+            f"{LIB} is not built; run `python -m speculative_decoding_verification_04_amd.build` "
+            "(the verify-and-commit step has no non-HIP implementation)")
+    lib = ctypes.CDLL(LIB)
+    for name, (res, args) in PROTOTYPES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

@@ -1,0 +1,293 @@
+// Commit: in-place realignment of the contiguous left-padded KV rectangle,
+// position ids and attention mask (gfx950).
+//
+// What it computes is the unpad-append-repad realignment of the
+// "Correctness Forensics for Batch Speculative Decoding" summary (sections 3.1
+// and App. B): keep each sequence's cached rows plus the first e_b verify
+// slots (the last emitted token has no KV yet: App. D, and the zero-to-sglang
+// walkthrough 5.2), right-align every sequence to E' = E + max_b e_b, and
+// rebuild position ids from the mask.
+//
+// Design.  The move is a right shift of a contiguous column range by
+// delta_b = M - e_b columns inside each (layer, K/V, sequence, head) plane of
+// C x D elements; sequences with delta_b = 0 do not move and cost nothing.
+// It is a pure copy bound by HBM bandwidth (read + write of every moved byte).
+//   * One workgroup per plane.  A column of R = D * elt bytes is split into
+//     R / VB slices of VB (= 16) bytes; the plane's moved range is split into
+//     SEG contiguous column segments, and lane (segment s, slice q) owns slice
+//     q of every column of segment s.  It walks its segment from the right end
+//     to the left, U columns at a time: load U columns, then store them delta
+//     columns further right.  Every address a lane overwrites inside its own
+//     segment it has already read itself, so in-place overlap needs no
+//     synchronisation beyond program order.
+//   * The only cross-lane hazard is at segment boundaries: segment s-1 writes
+//     the first delta source columns of segment s.  Each segment therefore
+//     loads those delta columns into registers first, and one workgroup
+//     barrier separates all such loads from all stores.  Segments are kept at
+//     least delta columns long, so only the left neighbour reaches into a
+//     segment.
+//   * B extra workgroups write the position-id and mask rows; one more writes
+//     the scalar outputs.  Outputs never alias inputs, so no workgroup needs
+//     to wait for another.
+#include "common.h"
+
+namespace specv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kHaloMax = 8;   // halo columns held in registers; larger shifts use one segment
+constexpr int kUnroll = 8;    // columns per lane per step
+
+struct RealignParams {
+  unsigned char *kv;
+  int L, B, H, C, D, k, elt;
+  int R;                       // bytes per column (D * elt)
+  long long plane_bytes;       // C * R
+  int num_planes;              // L * 2 * B * H
+  const int32_t *end_col, *kv_len_in, *emit_count;
+  int32_t *end_col_out, *kv_len_out, *pos_ids, *mask;
+  int64_t *bytes_moved;
+  int32_t *status;
+};
+
+template <int VB>
+struct VecOf;
+template <>
+struct VecOf<16> { using T = uint4; };
+template <>
+struct VecOf<8> { using T = uint2; };
+template <>
+struct VecOf<4> { using T = uint32_t; };
+template <>
+struct VecOf<2> { using T = uint16_t; };
+
+// Makes the compiler hold a loaded value in registers at this point, so the
+// load has completed (s_waitcnt) before whatever follows.
+__device__ inline void hold(uint4 v) { asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w)); }
+__device__ inline void hold(uint2 v) { asm volatile("" ::"v"(v.x), "v"(v.y)); }
+__device__ inline void hold(uint32_t v) { asm volatile("" ::"v"(v)); }
+__device__ inline void hold(uint16_t v) { asm volatile("" ::"v"(static_cast<uint32_t>(v))); }
+
+// Shared by every workgroup: E, M = max e_b and whether the state is valid.
+// Every workgroup computes the same values from the same inputs.
+__device__ inline void commit_state(const RealignParams &P, int *sh, int &E, int &M, bool &ok) {
+  E = P.end_col[0];
+  int bad = (E < 0 || E > P.C - P.k - 1) ? 1 : 0;
+  int m = 0;
+  for (int b = threadIdx.x; b < P.B; b += blockDim.x) {
+    const int n = P.kv_len_in[b], e = P.emit_count[b];
+    if (n < 0 || n > E || e < 0 || e > P.k + 1) bad = 1;
+    m = max(m, e);
+  }
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int wb = wave_max_i(bad), wmx = wave_max_i(m);
+  if (lane == 0) {
+    sh[w] = wb;
+    sh[kWaves + w] = wmx;
+  }
+  __syncthreads();
+  int allbad = 0, mm = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    allbad = max(allbad, sh[i]);
+    mm = max(mm, sh[kWaves + i]);
+  }
+  __syncthreads();
+  ok = allbad == 0;
+  M = mm;
+}
+
+template <int VB>
+__device__ inline void move_plane(const RealignParams &P, int p, int E, int M) {
+  using VT = typename VecOf<VB>::T;
+  const int b = (p / P.H) % P.B;
+  const int n = P.kv_len_in[b], e = P.emit_count[b];
+  const int delta = M - e, len = n + e;
+  if (delta == 0 || len == 0) return;   // uniform within the workgroup: no barrier is skipped unevenly
+
+  const int S = P.R / VB;                       // slices per column
+  const int lps = S < kThreads ? S : kThreads;  // lanes per segment
+  const int SEG = kThreads / lps;
+  int segs = SEG;
+  if (delta > kHaloMax) segs = 1;
+  else segs = min(segs, len / delta);
+  if (segs < 1) segs = 1;
+
+  const int t = threadIdx.x;
+  const int seg = t / lps, q0 = t - seg * lps;
+  const bool active = seg < segs;
+  const int lo = E - n;
+  int my_lo = 0, my_hi = 0;
+  if (active) {
+    my_lo = lo + static_cast<int>(static_cast<long long>(len) * seg / segs);
+    my_hi = lo + static_cast<int>(static_cast<long long>(len) * (seg + 1) / segs);
+  }
+  const bool halo = active && seg > 0;   // only when segs > 1, hence S <= kThreads and one slice per lane
+  unsigned char *base = P.kv + static_cast<size_t>(p) * P.plane_bytes;
+  const size_t R = static_cast<size_t>(P.R);
+
+  VT hreg[kHaloMax];
+  if (halo) {
+#pragma unroll
+    for (int i = 0; i < kHaloMax; ++i)
+      if (i < delta) hreg[i] = *reinterpret_cast<const VT *>(base + (my_lo + i) * R + q0 * VB);
+#pragma unroll
+    for (int i = 0; i < kHaloMax; ++i)
+      if (i < delta) hold(hreg[i]);   // the values are in registers before the barrier
+  }
+  __syncthreads();
+  if (!active) return;
+
+  const int start = my_lo + (halo ? delta : 0);
+  for (int q = q0; q < S; q += lps) {
+    const size_t off = static_cast<size_t>(q) * VB;
+    for (int c_hi = my_hi; c_hi > start; c_hi -= kUnroll) {
+      VT r[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int col = c_hi - 1 - u;
+        if (col >= start) r[u] = *reinterpret_cast<const VT *>(base + col * R + off);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int col = c_hi - 1 - u;
+        if (col >= start) *reinterpret_cast<VT *>(base + (col + delta) * R + off) = r[u];
+      }
+    }
+  }
+  if (halo) {
+#pragma unroll
+    for (int i = 0; i < kHaloMax; ++i)
+      if (i < delta) *reinterpret_cast<VT *>(base + (my_lo + delta + i) * R + q0 * VB) = hreg[i];
+  }
+}
+
+template <int VB>
+__global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
+  __shared__ int sh[2 * kWaves + 2];
+  __shared__ long long sh_bytes[kWaves];
+  int E, M;
+  bool ok;
+  commit_state(P, sh, E, M, ok);
+  const int blk = blockIdx.x;
+  const int t = threadIdx.x;
+
+  if (blk < P.num_planes) {
+    if (ok) move_plane<VB>(P, blk, E, M);
+    return;
+  }
+  if (blk < P.num_planes + P.B) {          // position ids and mask of one sequence
+    if (!ok) return;
+    const int b = blk - P.num_planes;
+    const int En = E + M;
+    const int start = En - (P.kv_len_in[b] + P.emit_count[b]);
+    int32_t *pos = P.pos_ids + static_cast<size_t>(b) * P.C;
+    int32_t *msk = P.mask + static_cast<size_t>(b) * P.C;
+    for (int c = t; c < P.C; c += kThreads) {
+      const bool in = c >= start && c < En;
+      msk[c] = in ? 1 : 0;
+      pos[c] = in ? c - start : 0;
+    }
+    return;
+  }
+  // scalar outputs
+  if (!ok) {
+    if (P.status) {
+      const bool cap = E < 0 || E > P.C - P.k - 1;
+      for (int b = t; b < P.B; b += kThreads) {
+        const int n = P.kv_len_in[b], e = P.emit_count[b];
+        int st = cap ? SPEC_ST_CAPACITY : 0;
+        if (n < 0 || n > E || e < 0 || e > P.k + 1) st |= SPEC_ST_BAD_STATE;
+        P.status[b] = st;
+      }
+    }
+    return;
+  }
+  long long moved = 0;
+  for (int b = t; b < P.B; b += kThreads) {
+    const int n1 = P.kv_len_in[b] + P.emit_count[b];
+    P.kv_len_out[b] = n1;
+    if (P.status) P.status[b] = 0;
+    if (P.emit_count[b] != M) moved += n1;
+  }
+  const int lane = t & (kWave - 1), w = t / kWave;
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) moved += __shfl_xor(moved, m, kWave);
+  if (lane == 0) sh_bytes[w] = moved;
+  __syncthreads();
+  if (t == 0) {
+    long long tot = 0;
+    for (int i = 0; i < kWaves; ++i) tot += sh_bytes[i];
+    *P.end_col_out = E + M;
+    if (P.bytes_moved) *P.bytes_moved = 2LL * tot * P.L * 2LL * P.H * P.R;
+  }
+}
+
+}  // namespace
+}  // namespace specv
+
+using namespace specv;
+
+extern "C" int spec_commit_realign_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, int D, int k,
+                                      const int32_t *end_col, const int32_t *kv_len_in,
+                                      const int32_t *emit_count, int32_t *end_col_out,
+                                      int32_t *kv_len_out, int32_t *pos_ids, int32_t *mask,
+                                      int64_t *bytes_moved, int32_t *status, spec_stream_t stream) {
+  if (!kv || !end_col || !kv_len_in || !emit_count || !end_col_out || !kv_len_out || !pos_ids || !mask)
+    return SPEC_EINVAL;
+  if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_EINVAL;
+  if (L < 1 || B < 1 || H < 1 || C < 1 || D < 1 || k < 1) return SPEC_EINVAL;
+  const int elt = dt == SPEC_BF16 ? 2 : 4;
+  if (!aligned(kv, elt)) return SPEC_EINVAL;
+  const long long planes = 2LL * L * B * H;
+  const long long R = static_cast<long long>(D) * elt;
+  if (planes + B + 1 >= INT32_MAX || R >= INT32_MAX || static_cast<long long>(C) * R >= (1LL << 62) / planes)
+    return SPEC_EINVAL;
+  const size_t kv_bytes = static_cast<size_t>(planes) * C * R;
+  const size_t bc = static_cast<size_t>(B) * C * 4;
+  const void *ins[] = {kv, end_col, kv_len_in, emit_count};
+  const size_t in_n[] = {kv_bytes, 4, static_cast<size_t>(B) * 4, static_cast<size_t>(B) * 4};
+  const void *outs[] = {end_col_out, kv_len_out, pos_ids, mask, bytes_moved, status};
+  const size_t out_n[] = {4, static_cast<size_t>(B) * 4, bc, bc, 8, static_cast<size_t>(B) * 4};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return SPEC_EINVAL;
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return SPEC_EINVAL;
+  }
+
+  RealignParams P;
+  P.kv = static_cast<unsigned char *>(kv);
+  P.L = L;
+  P.B = B;
+  P.H = H;
+  P.C = C;
+  P.D = D;
+  P.k = k;
+  P.elt = elt;
+  P.R = static_cast<int>(R);
+  P.plane_bytes = static_cast<long long>(C) * R;
+  P.num_planes = static_cast<int>(planes);
+  P.end_col = end_col;
+  P.kv_len_in = kv_len_in;
+  P.emit_count = emit_count;
+  P.end_col_out = end_col_out;
+  P.kv_len_out = kv_len_out;
+  P.pos_ids = pos_ids;
+  P.mask = mask;
+  P.bytes_moved = bytes_moved;
+  P.status = status;
+  const dim3 grid(static_cast<unsigned>(planes + B + 1)), block(kThreads);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (R % 16 == 0 && aligned(kv, 16))
+    hipLaunchKernelGGL(realign_kernel<16>, grid, block, 0, s, P);
+  else if (R % 8 == 0 && aligned(kv, 8))
+    hipLaunchKernelGGL(realign_kernel<8>, grid, block, 0, s, P);
+  else if (R % 4 == 0 && aligned(kv, 4))
+    hipLaunchKernelGGL(realign_kernel<4>, grid, block, 0, s, P);
+  else
+    hipLaunchKernelGGL(realign_kernel<2>, grid, block, 0, s, P);
+  return launch_status();
+}

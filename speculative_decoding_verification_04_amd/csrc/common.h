@@ -1,0 +1,140 @@
+// Device and host helpers shared by the verify-and-commit kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spec_verify.h"
+
+namespace specv {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// ---------------------------------------------------------------- host ----
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+// -------------------------------------------------------------- device ----
+// Agent-scope (whole-GPU) atomics.  Partial results written by one workgroup
+// and read by another live on different XCDs, whose L2s are not coherent for
+// ordinary stores; agent-scope atomics and fences make them visible.
+template <typename T>
+__device__ inline void store_agent(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ inline T load_agent(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t ticket_agent(uint32_t *ctr) {
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Order-preserving map of a float to uint32 (larger float -> larger key).
+// -0 is folded onto +0 so the two compare equal, as they do as floats.
+__device__ inline uint32_t f32_order_key(float v) {
+  uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// 64-bit argmax key: value order in the high word, (UINT32_MAX - index) in the
+// low word, so the maximum key is the maximum value at the lowest index.
+// Key 0 is below every real key and marks "no element".
+__device__ inline uint64_t argmax_key(float v, int idx) {
+  return (static_cast<uint64_t>(f32_order_key(v)) << 32) |
+         static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(idx));
+}
+__device__ inline int argmax_key_index(uint64_t key) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ inline int wave_min(int v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ inline int wave_max_i(int v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ inline double wave_sum_d(double v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+__device__ inline int wave_sum_i(int v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Inclusive scan across one wavefront (lane order).
+template <typename T>
+__device__ inline T wave_incl_scan(T v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    T o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Block-wide exclusive sum of one int per thread (blockDim.x <= 1024).
+// `sh` must hold blockDim.x / 64 ints.  Returns the exclusive prefix; *total
+// receives the block total.  Contains barriers: call from every thread.
+__device__ inline int block_excl_scan(int v, int *sh, int *total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int nw = (blockDim.x + kWave - 1) / kWave;
+  int inc = wave_incl_scan(v);
+  if (lane == kWave - 1) sh[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    int x = lane < nw ? sh[lane] : 0;
+    int xi = wave_incl_scan(x);
+    if (lane < nw) sh[lane] = xi - x;
+    if (lane == nw - 1) sh[nw] = xi;
+  }
+  __syncthreads();
+  int r = inc - v + sh[w];
+  *total = sh[nw];
+  __syncthreads();
+  return r;
+}
+
+// Exclusive prefix sum of n ints read with agent-scope loads, written to
+// out[0..n], out[n] = total.  One block; contains barriers.
+__device__ inline void block_offsets(const int32_t *in, int32_t *out, int n, int *sh) {
+  const int T = blockDim.x;
+  const int per = (n + T - 1) / T;
+  const int lo = min(n, threadIdx.x * per), hi = min(n, lo + per);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += load_agent(in + i);
+  int total;
+  int base = block_excl_scan(s, sh, &total);
+  for (int i = lo; i < hi; ++i) {
+    out[i] = base;
+    base += load_agent(in + i);
+  }
+  if (threadIdx.x == 0) out[n] = total;
+}
+
+}  // namespace specv

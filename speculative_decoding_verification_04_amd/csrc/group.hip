@@ -1,0 +1,187 @@
+// Same-length grouping of a window of ragged sequences (gfx950).
+//
+// The "Correctness Forensics for Batch Speculative Decoding" summary, 3.2,
+// describes EXSPEC: sequences stay ragged and batches are formed from
+// sequences of identical length found in a window larger than the batch
+// size, with unpad-append-repad as the fallback.  The scheduler's algorithm
+// body (App. C) is not on the page; the rule implemented here is stated in
+// include/spec_verify.h.
+//
+// Design.  The window is small (<= SPEC_GROUP_MAX_N), so one workgroup does
+// it all in LDS: a bitonic sort of 64-bit keys (length in the high word,
+// order-corrected for sign; window index in the low word), which makes every
+// key distinct and the sort stable by construction; then run detection and
+// four block-wide scans give each sorted position its run, the run's offsets
+// among same-length members, same-length batches and fallback members, and
+// every position writes its own output slots.  The work is latency-bound
+// (microseconds); there is nothing to stream.
+#include "common.h"
+
+namespace specv {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kPer = SPEC_GROUP_MAX_N / kThreads;   // sorted positions per lane
+
+__global__ __launch_bounds__(kThreads) void group_kernel(const int32_t *lengths, int N, int B, int mg,
+                                                          int P2, int32_t *perm, int32_t *batch_start,
+                                                          int32_t *batch_len, int32_t *num_batches,
+                                                          int32_t *num_grouped) {
+  extern __shared__ unsigned long long smem[];
+  unsigned long long *keys = smem;                                  // [P2]
+  int *run_start = reinterpret_cast<int *>(smem + P2);              // [N + 1]
+  __shared__ int sh[kThreads / kWave + 1];
+  const int t = threadIdx.x;
+
+  if (N == 0) {
+    if (t == 0) {
+      batch_start[0] = 0;
+      *num_batches = 0;
+      *num_grouped = 0;
+    }
+    return;
+  }
+  for (int i = t; i < P2; i += kThreads) {
+    keys[i] = i < N ? (static_cast<unsigned long long>(static_cast<uint32_t>(lengths[i]) ^ 0x80000000u) << 32) |
+                          static_cast<uint32_t>(i)
+                    : ~0ull;
+  }
+  __syncthreads();
+  for (int size = 2; size <= P2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = t; i < P2 / 2; i += kThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const unsigned long long a = keys[lo], c = keys[hi];
+        if ((a > c) == up) {
+          keys[lo] = c;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // lane t owns sorted positions [t*per, t*per + per) within [0, N)
+  const int per = (N + kThreads - 1) / kThreads;
+  const int p0 = min(N, t * per), p1 = min(N, p0 + per);
+  int len[kPer], idx[kPer], start[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int pos = p0 + i;
+    if (pos < p1) {
+      const unsigned long long kk = keys[pos];
+      len[i] = static_cast<int>(static_cast<uint32_t>(kk >> 32) ^ 0x80000000u);
+      idx[i] = static_cast<int>(static_cast<uint32_t>(kk));
+      const int prev = pos > 0 ? static_cast<int>(static_cast<uint32_t>(keys[pos - 1] >> 32) ^ 0x80000000u) : 0;
+      start[i] = (pos == 0 || prev != len[i]) ? 1 : 0;
+    } else {
+      len[i] = idx[i] = start[i] = 0;
+    }
+  }
+  // run ids
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) cnt += start[i];
+  int runs;
+  int rid = block_excl_scan(cnt, sh, &runs) - 1;
+  int run_of[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    rid += start[i];
+    run_of[i] = rid;
+    if (p0 + i < p1 && start[i]) run_start[rid] = p0 + i;
+  }
+  if (t == 0) run_start[runs] = N;
+  __syncthreads();
+
+  // per-run counts, placed at the run's first position
+  int nu[kPer], nb[kPer], nf[kPer], off[kPer];
+  int su = 0, sb = 0, sf = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    nu[i] = nb[i] = nf[i] = 0;
+    off[i] = 0;
+    if (p0 + i < p1) {
+      const int s = run_start[run_of[i]], e = run_start[run_of[i] + 1];
+      const int c = e - s, full = c / B, rem = c - full * B;
+      nu[i] = full * B + (rem >= mg ? rem : 0);
+      nb[i] = full + (rem >= mg && rem > 0 ? 1 : 0);
+      nf[i] = c - nu[i];
+      off[i] = p0 + i - s;
+      if (start[i]) {
+        su += nu[i];
+        sb += nb[i];
+        sf += nf[i];
+      }
+    }
+  }
+  int TU, TB, TF;
+  int xu = block_excl_scan(su, sh, &TU);
+  int xb = block_excl_scan(sb, sh, &TB);
+  int xf = block_excl_scan(sf, sh, &TF);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (p0 + i >= p1) continue;
+    // offsets of this position's run: the running exclusive sums hold every
+    // earlier run, plus this run itself unless it starts at this position
+    const int ou = start[i] ? xu : xu - nu[i];
+    const int ob = start[i] ? xb : xb - nb[i];
+    const int of = start[i] ? xf : xf - nf[i];
+    const int o = off[i];
+    if (o < nu[i]) {
+      perm[ou + o] = idx[i];
+      if (o % B == 0) {
+        batch_start[ob + o / B] = ou + o;
+        batch_len[ob + o / B] = len[i];
+      }
+    } else {
+      const int f = of + (o - nu[i]);
+      perm[TU + f] = idx[i];
+      if (f % B == 0) {
+        batch_start[TB + f / B] = TU + f;
+        batch_len[TB + f / B] = -1;
+      }
+    }
+    if (start[i]) {
+      xu += nu[i];
+      xb += nb[i];
+      xf += nf[i];
+    }
+  }
+  if (t == 0) {
+    const int nbat = TB + (TF + B - 1) / B;
+    batch_start[nbat] = N;
+    *num_batches = nbat;
+    *num_grouped = TU;
+  }
+}
+
+}  // namespace
+}  // namespace specv
+
+using namespace specv;
+
+extern "C" int spec_group_same_length(const int32_t *lengths, int N, int B, int min_group, int32_t *perm,
+                                      int32_t *batch_start, int32_t *batch_len, int32_t *num_batches,
+                                      int32_t *num_grouped, spec_stream_t stream) {
+  if (!lengths || !perm || !batch_start || !batch_len || !num_batches || !num_grouped) return SPEC_EINVAL;
+  if (N < 0 || B < 1 || min_group < 1) return SPEC_EINVAL;
+  if (N > SPEC_GROUP_MAX_N) return SPEC_ECAPACITY;
+  const size_t n4 = static_cast<size_t>(N) * 4;
+  const void *outs[] = {perm, batch_start, batch_len, num_batches, num_grouped};
+  const size_t out_n[] = {n4, n4 + 4, n4, 4, 4};
+  for (int i = 0; i < 5; ++i) {
+    if (overlaps(outs[i], out_n[i], lengths, n4)) return SPEC_EINVAL;
+    for (int j = i + 1; j < 5; ++j)
+      if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return SPEC_EINVAL;
+  }
+  int P2 = 2;
+  while (P2 < N) P2 <<= 1;
+  const size_t shmem = static_cast<size_t>(P2) * 8 + static_cast<size_t>(N + 1) * 4;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), shmem, static_cast<hipStream_t>(stream), lengths, N, B,
+                     min_group, P2, perm, batch_start, batch_len, num_batches, num_grouped);
+  return launch_status();
+}

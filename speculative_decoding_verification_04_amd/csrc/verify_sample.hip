@@ -1,0 +1,421 @@
+// Stochastic (Leviathan-style) verification of a batch of speculative rounds
+// (gfx950).
+//
+// What it computes follows the Atlas lesson "Speculative decoding: proposals
+// and verified output" (The mechanism, steps 2-5; Acceptance and rejection
+// correction: a(x) = min(1, p(x)/q(x)), residual r = [p - q]_+ normalised)
+// and the zero-to-sglang walkthrough 5.1 (accept when a uniform draw is below
+// a; at a rejection draw the correction from the positive residual; bonus from
+// the target after full acceptance).
+//
+// Design.  The acceptance chain only gathers 2 scalars per draft.  The bytes
+// are in the single full row each sequence draws from: the residual
+// p_j - q_j at the first rejection (8 bytes per vocabulary entry) or the
+// target row p_k after full acceptance (4 bytes).  One workgroup per
+// (sequence, chunk) recomputes the chain from the gathers, streams its chunk
+// of that row with 16-byte loads and writes the chunk's mass as a float64
+// partial.  The last workgroup of the sequence (agent-scope ticket) adds the
+// partials in chunk order (S), finds the chunk whose running sum first
+// exceeds u * S and scans that chunk in index order to find the token.  All
+// sums are float64 over the float32 r_v in a fixed order, so results are
+// reproducible run to run and within ~1e-16 relative of a correctly rounded
+// sum.
+#include "common.h"
+
+namespace specv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kU = 4;                               // float4 loads in flight per lane
+constexpr int kChunk = kThreads * 4 * kU;           // elements per chunk
+constexpr int kEPT = kChunk / kThreads;             // elements per lane in the in-chunk scan
+constexpr int kMaxChunks = 1024;                    // V <= kMaxChunks * kChunk
+
+enum : int { MODE_NONE = 0, MODE_RESID = 1, MODE_ROW = 2 };
+
+struct SampleParams {
+  const float *p, *q;
+  const int32_t *draft;
+  const float *u;
+  int B, k, V, chunks;
+  int vec;                      // rows are 16-byte aligned (V % 4 == 0 and aligned bases)
+  int32_t eos;
+  const int32_t *remaining;
+  int32_t *accept_len, *emit_count, *out_tokens, *emit_offsets;
+  double *final_mass;
+  int32_t *status;
+  double *partial;              // [B * chunks]
+  uint32_t *seq_ctr, *done_ctr;
+};
+
+struct SampleWs {
+  size_t part, seq, done, total;
+};
+inline SampleWs sample_ws_layout(int B, int chunks) {
+  SampleWs w;
+  w.part = 0;
+  w.seq = round_up(static_cast<size_t>(B) * chunks * sizeof(double), 256);
+  w.done = w.seq + round_up(static_cast<size_t>(B) * sizeof(uint32_t), 256);
+  w.total = w.done + 256;
+  return w;
+}
+
+// The mass vector a drawn token comes from: r_v = max(a_v - b_v, 0) when b is
+// set, else r_v = a_v.
+struct Row {
+  const float *a, *b;
+  __device__ inline float at(int v) const { return b ? fmaxf(a[v] - b[v], 0.0f) : a[v]; }
+};
+
+__device__ inline double block_sum_d(double v, double *sh) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  v = wave_sum_d(v);
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) s += sh[i];
+  __syncthreads();
+  return s;
+}
+
+// Mass of chunk c of the row (fixed summation order).  Contains barriers.
+__device__ inline double chunk_mass(const Row &r, int c, int V, bool vec, double *sh) {
+  const int t = threadIdx.x;
+  const int lo = c * kChunk;
+  double acc = 0.0;
+  if (vec) {
+    float4 av[kU], bv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int v = lo + (t + u * kThreads) * 4;
+      if (v < V) {
+        av[u] = *reinterpret_cast<const float4 *>(r.a + v);
+        if (r.b) bv[u] = *reinterpret_cast<const float4 *>(r.b + v);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int v = lo + (t + u * kThreads) * 4;
+      if (v < V) {
+        if (r.b) {
+          acc += static_cast<double>(fmaxf(av[u].x - bv[u].x, 0.0f));
+          acc += static_cast<double>(fmaxf(av[u].y - bv[u].y, 0.0f));
+          acc += static_cast<double>(fmaxf(av[u].z - bv[u].z, 0.0f));
+          acc += static_cast<double>(fmaxf(av[u].w - bv[u].w, 0.0f));
+        } else {
+          acc += static_cast<double>(av[u].x);
+          acc += static_cast<double>(av[u].y);
+          acc += static_cast<double>(av[u].z);
+          acc += static_cast<double>(av[u].w);
+        }
+      }
+    }
+  } else {
+    for (int i = 0; i < kChunk / kThreads; ++i) {
+      const int v = lo + t + i * kThreads;
+      if (v < V) acc += static_cast<double>(r.at(v));
+    }
+  }
+  return block_sum_d(acc, sh);
+}
+
+template <typename T>
+__device__ inline bool finite_val(T x) { return isfinite(x); }
+
+__global__ __launch_bounds__(kThreads) void sample_verify_kernel(SampleParams P) {
+  __shared__ int sh_acc[SPEC_MAX_K];
+  __shared__ int sh_st[SPEC_MAX_K];
+  __shared__ int sh_mode, sh_row, sh_cnt, sh_m, sh_stat, sh_flag, sh_tok;
+  __shared__ double sh_red[kWaves];
+  __shared__ double sh_part[kMaxChunks];
+  __shared__ int sh_scan[kWaves + 1];
+  __shared__ double sh_dscan[kWaves + 1];
+
+  const int t = threadIdx.x;
+  const int b = blockIdx.x / P.chunks;
+  const int c = blockIdx.x - b * P.chunks;
+  const int k = P.k, kp1 = k + 1, V = P.V;
+  const int32_t *d = P.draft + static_cast<size_t>(b) * k;
+  const float *pb = P.p + static_cast<size_t>(b) * kp1 * V;
+  const float *qb = P.q + static_cast<size_t>(b) * k * V;
+  const float *ub = P.u + static_cast<size_t>(b) * kp1;
+
+  // ---- acceptance chain: every workgroup of the sequence derives the same row
+  for (int j = t; j < k; j += kThreads) {
+    const int x = d[j];
+    int st = 0, acc = 0;
+    if (x >= 0 && x < V) {
+      const float px = pb[static_cast<size_t>(j) * V + x];
+      const float qx = qb[static_cast<size_t>(j) * V + x];
+      if (!finite_val(px) || !finite_val(qx)) st |= SPEC_ST_NONFINITE;
+      float a;
+      if (qx == 0.0f) {
+        a = px > 0.0f ? 1.0f : 0.0f;
+        st |= SPEC_ST_Q_ZERO;
+      } else {
+        const float ratio = __fdiv_rn(px, qx);
+        a = ratio < 1.0f ? ratio : 1.0f;
+      }
+      acc = ub[j] < a;
+    } else {
+      st |= SPEC_ST_DRAFT_OOR;
+    }
+    sh_acc[j] = acc;
+    sh_st[j] = st;
+  }
+  __syncthreads();
+  if (t == 0) {
+    const int rem = P.remaining ? P.remaining[b] : -1;   // negative: no budget
+    int mode = MODE_ROW, row = k, cnt = 0, m = 0, st = 0;
+    if (rem == 0) {
+      mode = MODE_NONE;
+    } else {
+      for (int j = 0; j < k; ++j) {
+        st |= sh_st[j];
+        if (sh_acc[j]) {
+          ++cnt;
+          ++m;
+          if ((P.eos >= 0 && d[j] == P.eos) || cnt == rem) {
+            mode = MODE_NONE;
+            break;
+          }
+        } else {
+          mode = MODE_RESID;
+          row = j;
+          break;
+        }
+      }
+    }
+    sh_mode = mode;
+    sh_row = row;
+    sh_cnt = cnt;
+    sh_m = m;
+    sh_stat = st;
+  }
+  __syncthreads();
+  const int mode = sh_mode, jrow = sh_row;
+  Row r;
+  r.a = pb + static_cast<size_t>(jrow) * V;
+  r.b = mode == MODE_RESID ? qb + static_cast<size_t>(jrow) * V : nullptr;
+  const bool vec = P.vec != 0;
+
+  // ---- this chunk's share of the row mass
+  if (mode != MODE_NONE) {
+    const double part = chunk_mass(r, c, V, vec, sh_red);
+    if (t == 0) store_agent(&P.partial[static_cast<size_t>(b) * P.chunks + c], part);
+  }
+  if (t == 0) {
+    const uint32_t prev = ticket_agent(&P.seq_ctr[b]);
+    sh_flag = prev == static_cast<uint32_t>(P.chunks) - 1u;
+  }
+  __syncthreads();
+  if (!sh_flag) return;
+
+  // ---- last workgroup of sequence b: the draw ----
+  acquire_agent();
+  int st = sh_stat;
+  int tok = -1;
+  double S = 0.0;
+  if (mode != MODE_NONE) {
+    for (int i = t; i < P.chunks; i += kThreads) {
+      double *slot = &P.partial[static_cast<size_t>(b) * P.chunks + i];
+      sh_part[i] = load_agent(slot);
+      store_agent(slot, 0.0);   // leave the workspace zeroed
+    }
+    __syncthreads();
+    if (t == 0) {
+      double s = 0.0;
+      for (int i = 0; i < P.chunks; ++i) s += sh_part[i];
+      sh_red[0] = s;
+    }
+    __syncthreads();
+    S = sh_red[0];
+    __syncthreads();
+    if (isfinite(S) && !(S > 0.0)) {
+      st |= SPEC_ST_RESID_ZERO;
+      if (mode == MODE_RESID) {         // fall back to the target row p_j itself
+        r.b = nullptr;
+        for (int i = 0; i < P.chunks; ++i) {
+          const double part = chunk_mass(r, i, V, vec, sh_red);
+          if (t == 0) sh_part[i] = part;
+        }
+        __syncthreads();
+        if (t == 0) {
+          double s = 0.0;
+          for (int i = 0; i < P.chunks; ++i) s += sh_part[i];
+          sh_red[0] = s;
+        }
+        __syncthreads();
+        S = sh_red[0];
+        __syncthreads();
+      }
+    }
+    if (!isfinite(S)) {
+      st |= SPEC_ST_NONFINITE;
+      tok = 0;
+    } else if (!(S > 0.0)) {
+      tok = 0;
+    } else {
+      const double T = static_cast<double>(ub[k]) * S;
+      if (t == 0) {
+        double run = 0.0;
+        int cs = -1, last = -1;
+        for (int i = 0; i < P.chunks; ++i) {
+          if (sh_part[i] > 0.0) last = i;
+          if (cs < 0 && run + sh_part[i] > T) cs = i;
+          if (cs < 0) run += sh_part[i];
+        }
+        if (cs < 0) {
+          cs = last;
+          run = 0.0;
+          for (int i = 0; i < cs; ++i) run += sh_part[i];
+        }
+        sh_row = cs;
+        sh_red[0] = run;
+      }
+      __syncthreads();
+      const int cs = sh_row;
+      const double base = sh_red[0];
+      __syncthreads();
+      // in-chunk scan in index order: lane t owns kEPT consecutive elements
+      const int lo = cs * kChunk + t * kEPT;
+      double mine = 0.0;
+      for (int i = 0; i < kEPT; ++i)
+        if (lo + i < V) mine += static_cast<double>(r.at(lo + i));
+      // block exclusive scan of the lanes' sums (fixed order)
+      const int lane = t & (kWave - 1), w = t / kWave;
+      double inc = mine;
+#pragma unroll
+      for (int dd = 1; dd < kWave; dd <<= 1) {
+        const double o = __shfl_up(inc, dd, kWave);
+        if (lane >= dd) inc += o;
+      }
+      if (lane == kWave - 1) sh_dscan[w] = inc;
+      __syncthreads();
+      double wpre = 0.0;
+      for (int i = 0; i < w; ++i) wpre += sh_dscan[i];
+      double run = base + (wpre + (inc - mine));
+      int cand = INT_MAX, lastpos = -1;
+      for (int i = 0; i < kEPT; ++i) {
+        const int v = lo + i;
+        if (v >= V) break;
+        const float rv = r.at(v);
+        if (rv > 0.0f) lastpos = v;
+        run += static_cast<double>(rv);
+        if (cand == INT_MAX && run > T) cand = v;
+      }
+      const int wc = wave_min(cand), wl = wave_max_i(lastpos);
+      __syncthreads();
+      if (lane == 0) {
+        sh_scan[w] = wc;
+        sh_acc[w] = wl;
+      }
+      __syncthreads();
+      if (t == 0) {
+        int best = INT_MAX, lp = -1;
+        for (int i = 0; i < kWaves; ++i) {
+          best = min(best, sh_scan[i]);
+          lp = max(lp, sh_acc[i]);
+        }
+        sh_tok = best != INT_MAX ? best : lp;
+      }
+      __syncthreads();
+      tok = sh_tok;
+    }
+  }
+  if (t == 0) {
+    store_agent(&P.seq_ctr[b], 0u);
+    int32_t *out = P.out_tokens + static_cast<size_t>(b) * kp1;
+    const int m = sh_m;
+    int cnt = sh_cnt;
+    for (int j = 0; j < m; ++j) out[j] = d[j];
+    if (mode != MODE_NONE) out[cnt++] = tok;
+    for (int i = cnt; i < kp1; ++i) out[i] = -1;
+    P.accept_len[b] = m;
+    if (P.final_mass) P.final_mass[b] = mode != MODE_NONE ? S : 0.0;
+    if (P.status) P.status[b] = st;
+    store_agent(&P.emit_count[b], cnt);
+    const uint32_t prev = ticket_agent(P.done_ctr);
+    sh_flag = prev == static_cast<uint32_t>(P.B) - 1u;
+  }
+  __syncthreads();
+  if (!sh_flag) return;
+  acquire_agent();
+  if (P.emit_offsets) block_offsets(P.emit_count, P.emit_offsets, P.B, sh_scan);
+  if (t == 0) store_agent(P.done_ctr, 0u);
+}
+
+inline int sample_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+}  // namespace
+}  // namespace specv
+
+using namespace specv;
+
+extern "C" size_t spec_verify_sample_workspace_bytes(int B, int k, int V) {
+  if (B < 1 || k < 1 || V < 1 || k > SPEC_MAX_K || sample_chunks(V) > kMaxChunks) return 0;
+  return sample_ws_layout(B, sample_chunks(V)).total;
+}
+
+extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t *draft,
+                                  const float *uniforms, int B, int k, int V, int32_t eos_id,
+                                  const int32_t *remaining, int32_t *accept_len,
+                                  int32_t *emit_count, int32_t *out_tokens, int32_t *emit_offsets,
+                                  double *final_mass, int32_t *status, void *ws, size_t ws_bytes,
+                                  spec_stream_t stream) {
+  if (!p || !q || !draft || !uniforms || !accept_len || !emit_count || !out_tokens || !ws)
+    return SPEC_EINVAL;
+  if (B < 1 || k < 1 || V < 1 || V >= INT32_MAX - 1) return SPEC_EINVAL;
+  if (k > SPEC_MAX_K) return SPEC_ECAPACITY;
+  const int chunks = sample_chunks(V);
+  if (chunks > kMaxChunks) return SPEC_ECAPACITY;
+  if (!aligned(p, 4) || !aligned(q, 4) || !aligned(uniforms, 4)) return SPEC_EINVAL;
+  const long long nblocks = static_cast<long long>(B) * chunks;
+  if (nblocks >= INT32_MAX) return SPEC_EINVAL;
+  const SampleWs lay = sample_ws_layout(B, chunks);
+  if (ws_bytes < lay.total || !aligned(ws, 256)) return SPEC_EWORKSPACE;
+
+  const size_t np = static_cast<size_t>(B) * (k + 1) * V * 4, nq = static_cast<size_t>(B) * k * V * 4;
+  const void *ins[] = {p, q, draft, uniforms, remaining, ws};
+  const size_t in_n[] = {np, nq, static_cast<size_t>(B) * k * 4, static_cast<size_t>(B) * (k + 1) * 4,
+                         static_cast<size_t>(B) * 4, lay.total};
+  const void *outs[] = {accept_len, emit_count, out_tokens, emit_offsets, final_mass, status};
+  const size_t out_n[] = {static_cast<size_t>(B) * 4, static_cast<size_t>(B) * 4,
+                          static_cast<size_t>(B) * (k + 1) * 4, static_cast<size_t>(B + 1) * 4,
+                          static_cast<size_t>(B) * 8, static_cast<size_t>(B) * 4};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return SPEC_EINVAL;
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return SPEC_EINVAL;
+  }
+
+  SampleParams P;
+  P.p = p;
+  P.q = q;
+  P.draft = draft;
+  P.u = uniforms;
+  P.B = B;
+  P.k = k;
+  P.V = V;
+  P.chunks = chunks;
+  P.vec = (V % 4 == 0) && aligned(p, 16) && aligned(q, 16);
+  P.eos = eos_id;
+  P.remaining = remaining;
+  P.accept_len = accept_len;
+  P.emit_count = emit_count;
+  P.out_tokens = out_tokens;
+  P.emit_offsets = emit_offsets;
+  P.final_mass = final_mass;
+  P.status = status;
+  unsigned char *wb = static_cast<unsigned char *>(ws);
+  P.partial = reinterpret_cast<double *>(wb + lay.part);
+  P.seq_ctr = reinterpret_cast<uint32_t *>(wb + lay.seq);
+  P.done_ctr = reinterpret_cast<uint32_t *>(wb + lay.done);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(sample_verify_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), P);
+  return launch_status();
+}

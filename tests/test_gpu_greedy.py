@@ -1,0 +1,156 @@
+"""GPU parity of spec_verify_greedy against the oracle: bit-exact accept
+lengths, emitted tokens, offsets and status, on the greedy workloads at full
+size and on edge cases (ragged vocabularies, misaligned rows, ties across
+chunks, -inf rows, +-0, EOS and budgets)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests._gpu import DEV, host, logits_to_device, note, requires_gpu, verify_greedy, ws
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+KEYS = ["accept_len", "emit_count", "out_tokens", "emit_offsets", "status"]
+
+
+def _compare(logits, dtype, drafts, eos_id=-1, remaining=None, logits_dev=None):
+    ref = oracle.greedy_verify(logits, dtype, drafts, eos_id=eos_id, remaining=remaining)
+    dev = logits_to_device(logits, dtype) if logits_dev is None else logits_dev
+    got = host(verify_greedy(dev, drafts, eos_id=eos_id, remaining=remaining))
+    for k in KEYS:
+        assert np.array_equal(got[k], ref[k]), (k, got[k], ref[k])
+    return got, ref
+
+
+@pytest.mark.parametrize("c,rounds", [(0, 3), (1, 3), (3, 2)])
+def test_workload_parity_full_size(c, rounds):
+    for r in range(rounds):
+        note(f"greedy workload {c} round {r}")
+        g = W.greedy_round(c, round_=r)
+        got, ref = _compare(g["logits"], g["dtype"], g["drafts"])
+        assert got["emit_count"].min() >= 1
+
+
+def test_bf16_ties_are_common_and_exact():
+    """bf16 N(0, 2) rows at V=128256 tie at the maximum often; every tie must
+    resolve to the lowest index, also when the tied values sit in different
+    chunks."""
+    note("greedy bf16 ties")
+    g = W.greedy_round(3, round_=7)
+    bits = g["logits"]
+    rows = oracle.widen_bf16(bits).reshape(-1, bits.shape[-1])
+    m = rows.max(axis=1, keepdims=True)
+    ties = ((rows == m).sum(axis=1) > 1).mean()
+    assert ties > 0.02
+    # plant cross-chunk ties: the max value also at index V-1 and in the middle
+    planted = bits.copy()
+    V = bits.shape[-1]
+    for b in range(bits.shape[0]):
+        for j in range(bits.shape[1]):
+            a = int(np.argmax(oracle.widen_bf16(planted[b, j])))
+            planted[b, j, V - 1] = planted[b, j, a]
+            planted[b, j, (a + V // 2) % V] = planted[b, j, a]
+    _compare(planted, "bf16", g["drafts"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 2, 7, 9, 1001, 8191, 8193, 32771, 65537])
+def test_ragged_vocab_sizes(dtype, V):
+    note(f"greedy ragged V={V} {dtype}")
+    rng = np.random.default_rng(V)
+    B, k = 3, 4
+    z = (rng.standard_normal((B, k + 1, V)) * 2).astype(np.float32)
+    logits = W.bf16_bits_from_f32(z) if dtype == "bf16" else z
+    amax = np.argmax(oracle.widen_bf16(logits) if dtype == "bf16" else logits, axis=-1)
+    drafts = np.where(rng.random((B, k)) < 0.7, amax[:, :k], rng.integers(0, V, (B, k))).astype(np.int32)
+    _compare(logits, dtype, drafts)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shift", [1, 3])
+def test_misaligned_logits_pointer(dtype, shift):
+    """A view starting a few elements into an allocation: rows lose 16-byte alignment."""
+    note(f"greedy misaligned shift={shift} {dtype}")
+    rng = np.random.default_rng(shift)
+    B, k, V = 4, 3, 5003
+    z = rng.standard_normal(B * (k + 1) * V + shift).astype(np.float32)
+    flat = W.bf16_bits_from_f32(z) if dtype == "bf16" else z
+    dev_flat = logits_to_device(flat, dtype)
+    dev = dev_flat[shift:].view(B, k + 1, V)
+    host_logits = flat[shift:].reshape(B, k + 1, V)
+    drafts = rng.integers(0, V, (B, k)).astype(np.int32)
+    _compare(host_logits, dtype, drafts, logits_dev=dev)
+
+
+def test_special_values():
+    note("greedy special values")
+    V = 20000
+    rows = np.zeros((6, 2, V), np.float32)
+    rows[0, :, :] = -np.inf                                  # all -inf -> 0
+    rows[1, :, :] = -np.inf
+    rows[1, :, 17000] = -5.0                                 # single finite
+    rows[2, :, 3] = -0.0                                     # -0 and +0 tie -> 3
+    rows[2, :, :] -= 1.0
+    rows[2, :, 3] = -0.0
+    rows[2, :, 9000] = 0.0
+    rows[3, :, 12345] = np.inf
+    rows[3, :, 19999] = np.inf                               # +inf tie -> 12345
+    rows[4, :, :] = 1.0                                      # constant row -> 0
+    rows[5, :, 19999] = 3.0                                  # max at last index
+    drafts = np.array([[0], [17000], [3], [12345], [1], [5]], np.int32)
+    got, ref = _compare(rows, "f32", drafts)
+    assert got["out_tokens"][:, 0].tolist() == [0, 17000, 3, 12345, 0, 19999]
+
+
+def test_eos_budget_and_out_of_range_drafts():
+    note("greedy eos/budget/oor")
+    rng = np.random.default_rng(11)
+    B, k, V = 64, 6, 3000
+    z = rng.standard_normal((B, k + 1, V)).astype(np.float32)
+    amax = np.argmax(z, axis=-1)
+    drafts = np.where(rng.random((B, k)) < 0.8, amax[:, :k], rng.integers(0, V, (B, k))).astype(np.int32)
+    drafts[::7, 2] = V + 5
+    drafts[::9, 0] = -3
+    remaining = rng.integers(-1, k + 3, size=B).astype(np.int32)
+    eos = int(amax[0, 1])
+    for e in [-1, eos]:
+        for rem in [None, remaining]:
+            got, ref = _compare(z, "f32", drafts, eos_id=e, remaining=rem)
+    assert (got["status"] & oracle.ST_DRAFT_OOR).any()
+
+
+def test_max_k_and_single_sequence():
+    note("greedy k=127 and B=1")
+    rng = np.random.default_rng(5)
+    for B, k, V in [(2, 127, 300), (1, 1, 50), (1, 8, 128256)]:
+        z = rng.standard_normal((B, k + 1, V)).astype(np.float32)
+        drafts = np.argmax(z[:, :k], axis=-1).astype(np.int32)     # full acceptance
+        got, _ = _compare(z, "f32", drafts)
+        assert (got["emit_count"] == k + 1).all()
+
+
+def test_large_batch_offsets():
+    note("greedy B=5000 offsets")
+    rng = np.random.default_rng(9)
+    B, k, V = 5000, 3, 64
+    z = rng.standard_normal((B, k + 1, V)).astype(np.float32)
+    drafts = rng.integers(0, V, (B, k)).astype(np.int32)
+    _compare(z, "f32", drafts)
+
+
+def test_repeatable_and_workspace_restored():
+    note("greedy repeat x50")
+    g = W.greedy_round(1, round_=4)
+    dev = logits_to_device(g["logits"], "bf16")
+    first = host(verify_greedy(dev, g["drafts"], ws_key="rep"))
+    for _ in range(49):
+        again = host(verify_greedy(dev, g["drafts"], ws_key="rep"))
+        for k in KEYS:
+            assert np.array_equal(again[k], first[k])
+    B, kp1, V = g["logits"].shape
+    import speculative_decoding_verification_04_amd as sv
+    w = ws(sv.spec_verify_greedy_workspace_bytes(B, kp1 - 1, V, sv.SPEC_BF16), "rep")
+    torch.cuda.synchronize()
+    assert int(w.count_nonzero()) == 0        # keys and counters are all zero again

@@ -1,0 +1,237 @@
+"""GPU parity of spec_verify_sample against the oracle.
+
+Acceptance decisions use the same float32 division and uniforms on both
+sides and are expected bit-exact; the acceptance rule of the check still
+tolerates a differing decision where |u - a| < 1e-6.  Drawn tokens may differ
+only where u * S lies within 1e-5 * S of a boundary of the oracle's prefix
+sums, and the drawn row's mass S must agree to 1e-5 relative.  Small cases
+are compared exactly (including the exact output law by enumeration)."""
+import math
+from fractions import Fraction
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests._gpu import DEV, host, note, requires_gpu, verify_sample
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+TAU = 1e-5
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def _run(p, q, d, u, eos_id=-1, remaining=None, p_dev=None, q_dev=None):
+    return host(verify_sample(_dev(p) if p_dev is None else p_dev, _dev(q) if q_dev is None else q_dev,
+                              d, u, eos_id=eos_id, remaining=remaining))
+
+
+def check_within_tolerance(p, q, d, u, got, ref):
+    """Apply the acceptance rule; returns (exact, tolerated) sequence counts."""
+    B, kp1, V = p.shape
+    k = kp1 - 1
+    exact = tolerated = 0
+    for b in range(B):
+        mr, mg = int(ref["accept_len"][b]), int(got["accept_len"][b])
+        if mr != mg:
+            j = min(mr, mg)
+            a, _ = oracle.accept_probability(p[b, j, d[b, j]], q[b, j, d[b, j]])
+            assert abs(float(u[b, j]) - float(a)) < 1e-6, (b, j, u[b, j], a)
+            tolerated += 1
+            continue
+        assert got["emit_count"][b] == ref["emit_count"][b], b
+        assert got["status"][b] == ref["status"][b], b
+        e = int(ref["emit_count"][b])
+        assert np.array_equal(got["out_tokens"][b, :mr], ref["out_tokens"][b, :mr])
+        assert (got["out_tokens"][b, e:] == -1).all()
+        Sr, Sg = float(ref["final_mass"][b]), float(got["final_mass"][b])
+        if e == mr:                         # no draw
+            assert Sg == 0.0 and Sr == 0.0
+            exact += 1
+            continue
+        assert abs(Sg - Sr) <= TAU * abs(Sr), (b, Sg, Sr)
+        vg, vr = int(got["out_tokens"][b, e - 1]), int(ref["out_tokens"][b, e - 1])
+        if vg == vr:
+            exact += 1
+            continue
+        if mr < k:
+            row = osample_resid(p[b, mr], q[b, mr])
+            if ref["status"][b] & oracle.ST_RESID_ZERO:
+                row = p[b, mr]
+        else:
+            row = p[b, k]
+        C = np.cumsum(row.astype(np.float64))
+        T = float(u[b, k]) * Sr
+        lo = C[vg - 1] if vg > 0 else 0.0
+        assert row[vg] > 0 and lo - TAU * Sr <= T <= C[vg] + TAU * Sr, (b, vg, vr)
+        tolerated += 1
+    return exact, tolerated
+
+
+def osample_resid(pj, qj):
+    import oracle.sample as s
+    return s._residual(pj, qj)
+
+
+def _enumeration_inputs(p_str, q_str, k, N=10):
+    V = len(p_str)
+    p = np.array([float(x) for x in p_str], np.float32)
+    q = np.array([float(x) for x in q_str], np.float32)
+    grid = [(i + 0.5) / N for i in range(N)]
+    drafts, unis, weights = [], [], []
+    for xs in itertools.product(range(V), repeat=k):
+        w = Fraction(1)
+        for x in xs:
+            w *= Fraction(q_str[x])
+        for us in itertools.product(range(N), repeat=k + 1):
+            drafts.append(xs)
+            unis.append([grid[i] for i in us])
+            weights.append(w / N ** (k + 1))
+    B = len(drafts)
+    P = np.broadcast_to(p, (B, k + 1, V)).copy()
+    Q = np.broadcast_to(q, (B, k, V)).copy()
+    return P, Q, np.array(drafts, np.int32), np.array(unis, np.float32), weights
+
+
+@pytest.mark.parametrize("name,k", [("stochastic_two_symbol.json", 1), ("stochastic_three_symbol.json", 1),
+                                    ("stochastic_three_symbol.json", 2)])
+def test_enumeration_reproduces_target_exactly(load_golden, name, k):
+    """Every draft tuple (weight prod q) x a stratified uniform grid: the
+    emitted token at each reached slot follows p exactly (as fractions)."""
+    g = load_golden(name)
+    note(f"sample enumeration {name} k={k}")
+    P, Q, D, U, wts = _enumeration_inputs(g["p"], g["q"], k)
+    got = _run(P, Q, D, U)
+    ref = oracle.sample_verify(P, Q, D, U)
+    for key in ["accept_len", "emit_count", "out_tokens", "emit_offsets", "status"]:
+        assert np.array_equal(got[key], ref[key]), key
+    V = len(g["p"])
+    for slot in range(k + 1):
+        reach = sum(w for b, w in enumerate(wts) if got["emit_count"][b] > slot)
+        law = [sum(w for b, w in enumerate(wts) if got["emit_count"][b] > slot and got["out_tokens"][b, slot] == v)
+               / reach for v in range(V)]
+        assert law == [Fraction(x) for x in g["output_distribution"]]
+    if k == 2:
+        count = {n: sum(w for b, w in enumerate(wts) if got["emit_count"][b] == n) for n in (1, 2, 3)}
+        assert count == {int(n): Fraction(v) for n, v in g["output_count_distribution"].items()}
+
+
+def test_output_count_monte_carlo(load_golden):
+    g = load_golden("stochastic_three_symbol.json")
+    note("sample monte carlo 1e6")
+    k = 2
+    p = np.array([float(x) for x in g["p"]], np.float32)
+    q = np.array([float(x) for x in g["q"]], np.float32)
+    B = 1_000_000
+    rng = np.random.default_rng(321)
+    d = rng.choice(3, size=(B, k), p=q.astype(np.float64) / q.sum()).astype(np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    P = _dev(np.broadcast_to(p, (B, k + 1, 3)))
+    Q = _dev(np.broadcast_to(q, (B, k, 3)))
+    got = host(verify_sample(P, Q, d, u))
+    K = got["emit_count"].astype(np.float64)
+    var = 0.4 * 1 + 0.24 * 4 + 0.36 * 9 - 1.96 ** 2
+    assert abs(K.mean() - 1.96) < 5 * math.sqrt(var / B)
+    assert got["emit_offsets"][-1] == int(K.sum())
+
+
+@pytest.mark.parametrize("rnd", [0, 1, 2])
+def test_stochastic_workload_parity_full_size(rnd):
+    note(f"sample workload 2 round {rnd}")
+    r = W.sample_round(2, round_=rnd)
+    got = _run(r["p"], r["q"], r["drafts"], r["uniforms"])
+    ref = oracle.sample_verify(r["p"], r["q"], r["drafts"], r["uniforms"])
+    exact, tol = check_within_tolerance(r["p"], r["q"], r["drafts"], r["uniforms"], got, ref)
+    assert exact + tol == r["B"]
+    assert np.array_equal(got["emit_offsets"][:1], [0])
+
+
+@pytest.mark.parametrize("batch", [0, 1])
+def test_grouped_workload_batches_full_size(batch):
+    """Workload 4's verify: k=4, V=256000, p/q built as in workload 2."""
+    note(f"sample workload 4 batch {batch}")
+    r = W.sample_round(4, batch=batch, B=8)
+    got = _run(r["p"], r["q"], r["drafts"], r["uniforms"])
+    ref = oracle.sample_verify(r["p"], r["q"], r["drafts"], r["uniforms"])
+    exact, tol = check_within_tolerance(r["p"], r["q"], r["drafts"], r["uniforms"], got, ref)
+    assert exact + tol == 8
+
+
+def _small_case(rng, B, k, V, sharp=1.0):
+    z = rng.standard_normal((B, k + 1, V)) * sharp
+    p = np.exp(z) / np.exp(z).sum(-1, keepdims=True)
+    zq = z[:, :k] + rng.standard_normal((B, k, V)) * 0.5
+    q = np.exp(zq) / np.exp(zq).sum(-1, keepdims=True)
+    p, q = p.astype(np.float32), q.astype(np.float32)
+    d = np.array([[rng.choice(V, p=q[b, j].astype(np.float64) / q[b, j].astype(np.float64).sum())
+                   for j in range(k)] for b in range(B)], np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    return p, q, d, u
+
+
+@pytest.mark.parametrize("V", [1, 3, 5, 4095, 4096, 4097, 12289, 50001])
+def test_ragged_vocab_sizes(V):
+    note(f"sample ragged V={V}")
+    rng = np.random.default_rng(V)
+    p, q, d, u = _small_case(rng, 16, 3, V)
+    got = _run(p, q, d, u)
+    ref = oracle.sample_verify(p, q, d, u)
+    exact, tol = check_within_tolerance(p, q, d, u, got, ref)
+    assert exact + tol == 16
+
+
+def test_misaligned_rows():
+    note("sample misaligned")
+    rng = np.random.default_rng(8)
+    B, k, V = 6, 3, 8000
+    p, q, d, u = _small_case(rng, B, k, V)
+    fp = torch.empty(p.size + 1, dtype=torch.float32, device=DEV)
+    fq = torch.empty(q.size + 1, dtype=torch.float32, device=DEV)
+    fp[1:].copy_(_dev(p).view(-1))
+    fq[1:].copy_(_dev(q).view(-1))
+    got = _run(p, q, d, u, p_dev=fp[1:].view(B, k + 1, V), q_dev=fq[1:].view(B, k, V))
+    ref = oracle.sample_verify(p, q, d, u)
+    exact, tol = check_within_tolerance(p, q, d, u, got, ref)
+    assert exact + tol == B
+
+
+def test_anomalies_and_stops():
+    note("sample anomalies")
+    rng = np.random.default_rng(12)
+    B, k, V = 12, 4, 700
+    p, q, d, u = _small_case(rng, B, k, V)
+    d[0, 0] = V + 3                          # out-of-range draft: rejected
+    q[1, 0, d[1, 0]] = 0.0                   # q(x) = 0 with p(x) > 0: accepted
+    u[1, 0] = 0.99
+    p[2, 0] = 0.1 / V                        # p < q everywhere: empty residual, fallback to p
+    q[2, 0] = 1.0 / V
+    u[2, 0] = 0.5
+    p[3, :, :] = 0.0                         # no mass anywhere in the bonus row
+    q[3, :, :] = 1.0 / V
+    p[3, :k, :] = q[3]                       # p == q: always accepted, bonus row empty
+    remaining = np.array([3, 2, 1, 9, 0, 1, 2, 3, 4, 5, -1, 2], np.int32)
+    for eos in [-1, int(d[5, 1])]:
+        for rem in [None, remaining]:
+            got = _run(p, q, d, u, eos_id=eos, remaining=rem)
+            ref = oracle.sample_verify(p, q, d, u, eos_id=eos, remaining=rem)
+            for key in ["accept_len", "emit_count", "out_tokens", "emit_offsets", "status"]:
+                assert np.array_equal(got[key], ref[key]), (key, eos, rem is None)
+            assert np.allclose(got["final_mass"], ref["final_mass"], rtol=TAU, atol=0)
+    assert got["status"][0] & oracle.ST_DRAFT_OOR
+
+
+def test_repeatable_bitwise():
+    note("sample repeat x20")
+    r = W.sample_round(2, round_=5, B=4)
+    P, Q = _dev(r["p"]), _dev(r["q"])
+    first = host(verify_sample(P, Q, r["drafts"], r["uniforms"], ws_key="srep"))
+    for _ in range(19):
+        again = host(verify_sample(P, Q, r["drafts"], r["uniforms"], ws_key="srep"))
+        for key in first:
+            assert np.array_equal(first[key], again[key]), key
