@@ -193,7 +193,9 @@ int spec_commit_realign_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, 
  *   batch_len   [N] out: the shared length of batch t, or -1 for a mixed batch
  *   num_batches device int32 out
  *   num_grouped device int32 out: sequences placed in same-length batches
- * Entries of batch_start / batch_len past num_batches are not written.
+ * Entries of batch_start / batch_len past num_batches are not written.  With
+ * N == 0, lengths, perm and batch_len may be NULL (nothing is read or written
+ * there) and the call writes batch_start[0] = 0 and two zero counts.
  * Errors: SPEC_EINVAL for NULL pointers, N < 0, B < 1, min_group < 1;
  * SPEC_ECAPACITY for N > SPEC_GROUP_MAX_N.
  * ------------------------------------------------------------------------ */

@@ -28,10 +28,17 @@ _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """Load the built HIP library; raise if it is missing (there is no fallback)."""
+    """Load the built HIP library; raise if it is missing (there is no fallback).
+
+    torch is imported first: the library must bind to the same HIP runtime as
+    the framework whose device memory and streams it is handed.  torch ships
+    its own libamdhip64 (same SONAME as the system one); loading ours first
+    would map the system runtime and leave torch on a second one.
+    """
     global _lib
     if _lib is not None:
         return _lib
+    import torch  # noqa: F401  (maps torch's HIP runtime before ours resolves against it)
     if not os.path.exists(LIB):
         raise RuntimeError(
             f"{LIB} is not built; run `python -m speculative_decoding_verification_04_amd.build` "

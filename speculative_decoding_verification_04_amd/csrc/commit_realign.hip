@@ -12,20 +12,19 @@
 // delta_b = M - e_b columns inside each (layer, K/V, sequence, head) plane of
 // C x D elements; sequences with delta_b = 0 do not move and cost nothing.
 // It is a pure copy bound by HBM bandwidth (read + write of every moved byte).
-//   * One workgroup per plane.  A column of R = D * elt bytes is split into
-//     R / VB slices of VB (= 16) bytes; the plane's moved range is split into
-//     SEG contiguous column segments, and lane (segment s, slice q) owns slice
-//     q of every column of segment s.  It walks its segment from the right end
-//     to the left, U columns at a time: load U columns, then store them delta
-//     columns further right.  Every address a lane overwrites inside its own
-//     segment it has already read itself, so in-place overlap needs no
-//     synchronisation beyond program order.
-//   * The only cross-lane hazard is at segment boundaries: segment s-1 writes
-//     the first delta source columns of segment s.  Each segment therefore
-//     loads those delta columns into registers first, and one workgroup
-//     barrier separates all such loads from all stores.  Segments are kept at
-//     least delta columns long, so only the left neighbour reaches into a
-//     segment.
+//   * One workgroup per moving plane.  The moved bytes form one contiguous
+//     range; the workgroup walks it from the right end to the left in tiles of
+//     kThreads * kTileVec 16-byte vectors (16 KB), consecutive lanes on
+//     consecutive vectors, exactly like a streaming copy.
+//   * In-place overlap: a tile is loaded into registers, every lane waits for
+//     its loads to land, a workgroup barrier follows, and only then is the
+//     tile stored delta columns to the right.  The tile to its left is loaded
+//     before that store: its source ends delta columns before this tile's
+//     destination begins, so the two never overlap; and a tile's destination
+//     only overlaps its own source and the source of the tile to its right,
+//     both already in registers.
+//   * Planes are dispatched longest move first (ties by sequence index) so the
+//     last workgroups to start are the shortest ones.
 //   * B extra workgroups write the position-id and mask rows; one more writes
 //     the scalar outputs.  Outputs never alias inputs, so no workgroup needs
 //     to wait for another.
@@ -36,8 +35,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kHaloMax = 8;   // halo columns held in registers; larger shifts use one segment
-constexpr int kUnroll = 8;    // columns per lane per step
+constexpr int kTileVec = 4;    // 16-byte vectors per lane per tile (16 KB tiles)
+constexpr int kRankMaxB = 256;  // batches up to this size are dispatched longest move first
 
 struct RealignParams {
   unsigned char *kv;
@@ -98,68 +97,74 @@ __device__ inline void commit_state(const RealignParams &P, int *sh, int &E, int
   M = mm;
 }
 
-template <int VB>
-__device__ inline void move_plane(const RealignParams &P, int p, int E, int M) {
-  using VT = typename VecOf<VB>::T;
-  const int b = (p / P.H) % P.B;
-  const int n = P.kv_len_in[b], e = P.emit_count[b];
-  const int delta = M - e, len = n + e;
-  if (delta == 0 || len == 0) return;   // uniform within the workgroup: no barrier is skipped unevenly
-
-  const int S = P.R / VB;                       // slices per column
-  const int lps = S < kThreads ? S : kThreads;  // lanes per segment
-  const int SEG = kThreads / lps;
-  int segs = SEG;
-  if (delta > kHaloMax) segs = 1;
-  else segs = min(segs, len / delta);
-  if (segs < 1) segs = 1;
-
+// Sequence whose planes block-group `rank` moves: sequences ordered by moved
+// length (n_b + e_b if delta_b > 0, else -1), longest first, ties by index.
+// Batches up to kRankMaxB only; keys are staged in LDS, one ranking pass.
+__device__ inline int ranked_sequence(const RealignParams &P, int M, int rank, int *sh_keys, int *sh_seq) {
   const int t = threadIdx.x;
-  const int seg = t / lps, q0 = t - seg * lps;
-  const bool active = seg < segs;
-  const int lo = E - n;
-  int my_lo = 0, my_hi = 0;
-  if (active) {
-    my_lo = lo + static_cast<int>(static_cast<long long>(len) * seg / segs);
-    my_hi = lo + static_cast<int>(static_cast<long long>(len) * (seg + 1) / segs);
+  for (int b = t; b < P.B; b += blockDim.x) {
+    const int eb = P.emit_count[b];
+    sh_keys[b] = eb != M ? P.kv_len_in[b] + eb : -1;
   }
-  const bool halo = active && seg > 0;   // only when segs > 1, hence S <= kThreads and one slice per lane
-  unsigned char *base = P.kv + static_cast<size_t>(p) * P.plane_bytes;
-  const size_t R = static_cast<size_t>(P.R);
-
-  VT hreg[kHaloMax];
-  if (halo) {
-#pragma unroll
-    for (int i = 0; i < kHaloMax; ++i)
-      if (i < delta) hreg[i] = *reinterpret_cast<const VT *>(base + (my_lo + i) * R + q0 * VB);
-#pragma unroll
-    for (int i = 0; i < kHaloMax; ++i)
-      if (i < delta) hold(hreg[i]);   // the values are in registers before the barrier
+  if (t == 0) *sh_seq = -1;
+  __syncthreads();
+  for (int b = t; b < P.B; b += blockDim.x) {
+    const int kb = sh_keys[b];
+    int r = 0;
+    for (int o = 0; o < P.B; ++o) {
+      const int ko = sh_keys[o];
+      r += (ko > kb) || (ko == kb && o < b);
+    }
+    if (r == rank) *sh_seq = b;
   }
   __syncthreads();
-  if (!active) return;
+  return *sh_seq;
+}
 
-  const int start = my_lo + (halo ? delta : 0);
-  for (int q = q0; q < S; q += lps) {
-    const size_t off = static_cast<size_t>(q) * VB;
-    for (int c_hi = my_hi; c_hi > start; c_hi -= kUnroll) {
-      VT r[kUnroll];
+template <int VB>
+__device__ inline void move_plane(const RealignParams &P, int p, int b, int E, int M) {
+  using VT = typename VecOf<VB>::T;
+  const int n = P.kv_len_in[b], e = P.emit_count[b];
+  const int delta = M - e, len = n + e;
+  if (delta == 0 || len == 0) return;   // uniform in the workgroup: no barrier is skipped unevenly
+
+  const long long per_col = P.R / VB;                       // vectors per column
+  VT *base = reinterpret_cast<VT *>(P.kv + static_cast<size_t>(p) * P.plane_bytes);
+  const long long lo = static_cast<long long>(E - n) * per_col;   // first source vector
+  const long long shift = static_cast<long long>(delta) * per_col;
+  constexpr int TV = kThreads * kTileVec;                    // vectors per tile
+  const int t = threadIdx.x;
+  long long hi = lo + static_cast<long long>(len) * per_col; // one past the last source vector
+
+  VT cur[kTileVec], nxt[kTileVec];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int col = c_hi - 1 - u;
-        if (col >= start) r[u] = *reinterpret_cast<const VT *>(base + col * R + off);
-      }
+  for (int u = 0; u < kTileVec; ++u) {
+    const long long i = hi - TV + u * kThreads + t;
+    if (i >= lo) cur[u] = base[i];
+  }
+  while (true) {
+    const long long nhi = hi - TV;
+    const bool more = nhi > lo;
+    if (more) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int col = c_hi - 1 - u;
-        if (col >= start) *reinterpret_cast<VT *>(base + (col + delta) * R + off) = r[u];
+      for (int u = 0; u < kTileVec; ++u) {
+        const long long i = nhi - TV + u * kThreads + t;
+        if (i >= lo) nxt[u] = base[i];
       }
     }
-  }
-  if (halo) {
 #pragma unroll
-    for (int i = 0; i < kHaloMax; ++i)
-      if (i < delta) *reinterpret_cast<VT *>(base + (my_lo + delta + i) * R + q0 * VB) = hreg[i];
+    for (int u = 0; u < kTileVec; ++u)
+      if (hi - TV + u * kThreads + t >= lo) hold(cur[u]);   // this tile's loads have landed
+    __syncthreads();                                           // ... in every lane
+#pragma unroll
+    for (int u = 0; u < kTileVec; ++u) {
+      const long long i = hi - TV + u * kThreads + t;
+      if (i >= lo) base[i + shift] = cur[u];
+    }
+    if (!more) break;
+#pragma unroll
+    for (int u = 0; u < kTileVec; ++u) cur[u] = nxt[u];
+    hi = nhi;
   }
 }
 
@@ -167,6 +172,7 @@ template <int VB>
 __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
   __shared__ int sh[2 * kWaves + 2];
   __shared__ long long sh_bytes[kWaves];
+  __shared__ int sh_keys[kRankMaxB];
   int E, M;
   bool ok;
   commit_state(P, sh, E, M, ok);
@@ -174,7 +180,12 @@ __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
   const int t = threadIdx.x;
 
   if (blk < P.num_planes) {
-    if (ok) move_plane<VB>(P, blk, E, M);
+    if (!ok) return;
+    const int per_seq = P.num_planes / P.B;                  // L * 2 * H planes per sequence
+    const int rank = blk / per_seq, j = blk - rank * per_seq;
+    const int b = P.B <= kRankMaxB ? ranked_sequence(P, M, rank, sh_keys, &sh[2 * kWaves]) : rank;
+    const int h = j % P.H, lk = j / P.H;                     // lk = layer * 2 + kv
+    move_plane<VB>(P, (lk * P.B + b) * P.H + h, b, E, M);
     return;
   }
   if (blk < P.num_planes + P.B) {          // position ids and mask of one sequence

@@ -166,7 +166,8 @@ using namespace specv;
 extern "C" int spec_group_same_length(const int32_t *lengths, int N, int B, int min_group, int32_t *perm,
                                       int32_t *batch_start, int32_t *batch_len, int32_t *num_batches,
                                       int32_t *num_grouped, spec_stream_t stream) {
-  if (!lengths || !perm || !batch_start || !batch_len || !num_batches || !num_grouped) return SPEC_EINVAL;
+  if (!batch_start || !num_batches || !num_grouped) return SPEC_EINVAL;
+  if (N > 0 && (!lengths || !perm || !batch_len)) return SPEC_EINVAL;
   if (N < 0 || B < 1 || min_group < 1) return SPEC_EINVAL;
   if (N > SPEC_GROUP_MAX_N) return SPEC_ECAPACITY;
   const size_t n4 = static_cast<size_t>(N) * 4;

@@ -317,6 +317,7 @@ extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int 
   P.seq_ctr = reinterpret_cast<uint32_t *>(wb + lay.seq);
   P.done_ctr = reinterpret_cast<uint32_t *>(wb + lay.done);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
   if (dt == SPEC_BF16)
     hipLaunchKernelGGL(greedy_verify_kernel<true>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
   else
