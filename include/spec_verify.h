@@ -24,10 +24,11 @@
  *     sequence status bits (SPEC_ST_*).
  *   - Output arrays must not overlap input arrays or each other.
  *   - Workspaces ("ws") are device memory of at least the queried size, 256-byte
- *     aligned.  They must be ZERO-FILLED before their first use; every call that
- *     runs to completion leaves them zero-filled again, so a workspace is
- *     zeroed once at allocation and then reused.  Calls that may run at the same
+ *     aligned, holding per-call partial results.  Their contents on entry are
+ *     ignored (no initialisation is needed).  Calls that may run at the same
  *     time (different streams) need different workspaces.
+ *   - A verify call launches two kernels on `stream` (a streaming pass and a
+ *     small commit pass); the stream order is their only synchronisation.
  *   - Token ids are int32 in [0, V).  Layouts are row-major, last index fastest.
  */
 #ifndef SPEC_VERIFY_H

@@ -71,9 +71,9 @@ def _dtype_code(t) -> int:
 
 
 def workspace(nbytes: int, device=None):
-    """A zero-filled device workspace (zeroed once; the library keeps it zero)."""
+    """A device workspace of at least nbytes (its contents need no initialisation)."""
     import torch
-    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
 
 
 def spec_verify_greedy_workspace_bytes(B: int, k: int, V: int, dtype_code: int) -> int:

@@ -26,42 +26,11 @@ inline int launch_status() {
 }
 
 // -------------------------------------------------------------- device ----
-// Agent-scope (whole-GPU) atomics.  Partial results written by one workgroup
-// and read by another live on different XCDs, whose L2s are not coherent for
-// ordinary stores; agent-scope atomic stores and loads bypass those caches.
-template <typename T>
-__device__ inline void store_agent(T *p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Relaxed agent-scope (whole-GPU) atomic load: reads through the per-XCD L2s.
 template <typename T>
 __device__ inline T load_agent(const T *p) {
   return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// Ordering without cache maintenance.  On gfx950 an agent-scope release or
-// acquire fence writes back or invalidates the whole L2 of the XCD, which is
-// far too slow to pay once per workgroup.  Everything published between
-// workgroups here is written and read with agent-scope atomics, which bypass
-// the non-coherent caches, so only ordering is needed: a workgroup-scope
-// fence (compiler and L1 ordering) plus a wait until this wave's vector memory
-// operations have completed.  s_waitcnt immediate for gfx9: vmcnt(0), expcnt
-// and lgkmcnt left at their maxima.
-__device__ inline void order_release() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-__device__ inline void order_acquire() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-// Ticket on a per-call counter: publishes this thread's earlier agent-scope
-// stores, then counts.  The caller that draws the last ticket must call
-// order_acquire() before reading what the others published.
-__device__ inline uint32_t ticket_agent(uint32_t *ctr) {
-  order_release();
-  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void acquire_agent() { order_acquire(); }
 
 // Order-preserving map of a float to uint32 (larger float -> larger key).
 // -0 is folded onto +0 so the two compare equal, as they do as floats.

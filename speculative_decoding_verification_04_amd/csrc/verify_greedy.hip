@@ -7,19 +7,21 @@
 // bonus row) is the walkthrough's 3.3 table.
 //
 // Design.  The logits are the only large input (B*(k+1)*V elements), so the
-// kernel is one streaming pass over them, bound by HBM bandwidth.  Each row is
-// cut into chunks of kThreads*VEC*U elements; one workgroup per (row, chunk)
-// loads its chunk with 16-byte loads (U loads in flight per lane), takes the
-// chunk maximum with plain max instructions, and then looks up the first
-// index holding that maximum only in the lanes that hold it.  The chunk result
-// is packed into a 64-bit key (value order high, UINT32_MAX - index low) so
-// that the maximum key is the row argmax with the lowest-index tie rule.
-// The last workgroup of a sequence to finish (agent-scope ticket counter)
-// reduces its (k+1)*chunks keys, walks the drafts and writes the sequence's
-// outputs; the last sequence to finish writes the emit offsets.  Keys and
-// counters are zeroed by the workgroup that consumes them, so the whole
-// workspace is zero again when the kernel ends (and can be reused for any
-// shape).
+// step is one streaming pass over them, bound by HBM bandwidth, followed by a
+// tiny commit pass.
+//   * greedy_chunk_kernel: each row is cut into chunks of kThreads*VEC*U
+//     elements; one workgroup per (row, chunk) loads its chunk with 16-byte
+//     non-temporal loads (U in flight per lane), takes the chunk maximum with
+//     plain max instructions, then finds the first index holding it (only the
+//     lanes holding it search), and stores one 64-bit key (value order high,
+//     UINT32_MAX - index low; the largest key is the argmax at the lowest
+//     index).  No workgroup waits for another: cross-workgroup completion
+//     tickets cost far more than this whole pass on a multi-XCD part (device-
+//     scope atomics on one address serialise, and waiting on them holds the
+//     CU's wave slots), so the kernel boundary is the synchronisation.
+//   * greedy_commit_kernel: one workgroup folds the chunk keys of each row
+//     (LDS atomic max), walks each sequence's drafts, writes its outputs, and
+//     scans the emit counts into offsets, a tile of sequences at a time.
 #include "common.h"
 
 namespace specv {
@@ -47,21 +49,10 @@ struct GreedyParams {
   const int32_t *remaining;
   int32_t *accept_len, *emit_count, *out_tokens, *emit_offsets, *status;
   uint64_t *keys;     // [B*(k+1)*chunks]
-  uint32_t *seq_ctr;  // [B]
-  uint32_t *done_ctr; // [1]
 };
 
-struct GreedyWs {
-  size_t keys, seq, done, total;
-};
-
-inline GreedyWs greedy_ws_layout(int B, int k, int chunks) {
-  GreedyWs w;
-  w.keys = 0;
-  w.seq = round_up(static_cast<size_t>(B) * (k + 1) * chunks * sizeof(uint64_t), 256);
-  w.done = w.seq + round_up(static_cast<size_t>(B) * sizeof(uint32_t), 256);
-  w.total = w.done + 256;
-  return w;
+inline size_t greedy_ws_bytes(int B, int k, int chunks) {
+  return round_up(static_cast<size_t>(B) * (k + 1) * chunks * sizeof(uint64_t), 256);
 }
 
 template <bool BF16>
@@ -82,6 +73,14 @@ __device__ inline float load_elem(const unsigned char *p, int i) {
   } else {
     return reinterpret_cast<const float *>(p)[i];
   }
+}
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load: the logits are read exactly once.
+__device__ inline uint4 stream_load(const unsigned char *p) {
+  const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
 }
 
 template <bool BF16>
@@ -125,20 +124,15 @@ __device__ inline int vec_find(uint4 x, float m) {
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void greedy_verify_kernel(GreedyParams P) {
+__global__ __launch_bounds__(kThreads) void greedy_chunk_kernel(GreedyParams P) {
   using Tr = GreedyTraits<BF16>;
   constexpr int ELT = Tr::ELT, VEC = Tr::VEC, U = Tr::U;
   __shared__ float sh_max[kWaves];
   __shared__ int sh_idx[kWaves];
-  __shared__ unsigned long long sh_row[SPEC_MAX_K + 1];
-  __shared__ int sh_flag;
-  __shared__ int sh_scan[kWaves + 1];
 
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
   const int row = blockIdx.x / P.chunks;
   const int c = blockIdx.x - row * P.chunks;
-  const int kp1 = P.k + 1;
-  const int b = row / kp1;
   const unsigned char *rowp = P.logits + static_cast<size_t>(row) * P.V * ELT;
   // Elements before the row's first 16-byte boundary are handled one per lane
   // by chunk 0; the body starts aligned.
@@ -156,8 +150,7 @@ __global__ __launch_bounds__(kThreads) void greedy_verify_kernel(GreedyParams P)
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int vi = t + u * kThreads;
-    buf[u] = vi < nv ? *reinterpret_cast<const uint4 *>(rowp + static_cast<size_t>(s + vi * VEC) * ELT)
-                     : neg_inf_vec<BF16>();
+    buf[u] = vi < nv ? stream_load(rowp + static_cast<size_t>(s + vi * VEC) * ELT) : neg_inf_vec<BF16>();
   }
   if (has_tail) tv = load_elem<BF16>(rowp, s + nv * VEC + t);
 
@@ -201,59 +194,85 @@ __global__ __launch_bounds__(kThreads) void greedy_verify_kernel(GreedyParams P)
     int bi = sh_idx[0];
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) bi = min(bi, sh_idx[i]);
-    const uint64_t key = bi == INT_MAX ? 0ull : argmax_key(bmax, bi);
-    store_agent(&P.keys[static_cast<size_t>(row) * P.chunks + c], key);
-    const uint32_t prev = ticket_agent(&P.seq_ctr[b]);
-    sh_flag = prev == static_cast<uint32_t>(kp1 * P.chunks) - 1u;
+    P.keys[static_cast<size_t>(row) * P.chunks + c] = bi == INT_MAX ? 0ull : argmax_key(bmax, bi);
   }
-  __syncthreads();
-  if (!sh_flag) return;
+}
 
-  // ---- last workgroup of sequence b: row argmaxes and the commit walk ----
-  acquire_agent();
-  for (int i = t; i < kp1; i += kThreads) sh_row[i] = 0ull;
-  __syncthreads();
-  const int nkeys = kp1 * P.chunks;
-  const uint64_t *kb = P.keys + static_cast<size_t>(b) * nkeys;
-  for (int i = t; i < nkeys; i += kThreads) {
-    atomicMax(&sh_row[i / P.chunks], static_cast<unsigned long long>(load_agent(kb + i)));
-    store_agent(const_cast<uint64_t *>(kb) + i, static_cast<uint64_t>(0));   // leave the workspace zeroed
-  }
-  __syncthreads();
-  if (t == 0) {
-    store_agent(&P.seq_ctr[b], 0u);
-    const int32_t *d = P.draft + static_cast<size_t>(b) * P.k;
-    int32_t *out = P.out_tokens + static_cast<size_t>(b) * kp1;
-    const int rem = P.remaining ? P.remaining[b] : -1;   // negative: no budget
-    int st = 0;
-    for (int j = 0; j < P.k; ++j)
-      if (d[j] < 0 || d[j] >= P.V) st |= SPEC_ST_DRAFT_OOR;
-    int cnt = 0, acc = 0;
-    if (rem != 0) {
-      bool stop = false;
-      for (int j = 0; j < P.k && !stop; ++j) {
-        const int tj = argmax_key_index(sh_row[j]);
-        out[cnt++] = tj;
-        const bool match = tj == d[j];
-        acc += match;
-        if ((P.eos >= 0 && tj == P.eos) || cnt == rem || !match) stop = true;
+constexpr int kCommitThreads = 1024;
+constexpr int kCommitRows = 1024;   // row keys folded per tile (LDS)
+constexpr int kKeysPerThread = 8;   // chunk keys in flight per lane
+
+// One workgroup.  Per tile of sequences, every global read (chunk keys, drafts,
+// budgets) is issued at once into LDS; the walk then runs from LDS only.
+__global__ __launch_bounds__(kCommitThreads) void greedy_commit_kernel(GreedyParams P) {
+  __shared__ unsigned long long sh_row[kCommitRows];
+  __shared__ int sh_d[kCommitRows];
+  __shared__ int sh_rem[kCommitRows];
+  __shared__ int sh_scan[kCommitThreads / kWave + 1];
+  const int t = threadIdx.x;
+  const int kp1 = P.k + 1;
+  const int per_tile = kCommitRows / kp1;          // sequences per tile (k <= SPEC_MAX_K keeps this >= 8)
+  int carry = 0;
+  for (int s0 = 0; s0 < P.B; s0 += per_tile) {
+    const int ns = min(per_tile, P.B - s0);
+    const int nrows = ns * kp1;
+    for (int i = t; i < nrows; i += kCommitThreads) sh_row[i] = 0ull;
+    __syncthreads();
+    // one round trip: keys, drafts and budgets are all requested before any is used
+    const uint64_t *kb = P.keys + static_cast<size_t>(s0) * kp1 * P.chunks;
+    for (int i = t; i < ns * P.k; i += kCommitThreads) sh_d[i] = P.draft[static_cast<size_t>(s0) * P.k + i];
+    if (t < ns) sh_rem[t] = P.remaining ? P.remaining[s0 + t] : -1;   // negative: no budget
+    const int nkeys = nrows * P.chunks;
+    for (int base = 0; base < nkeys; base += kCommitThreads * kKeysPerThread) {
+      uint64_t kr[kKeysPerThread];
+#pragma unroll
+      for (int q = 0; q < kKeysPerThread; ++q) {   // all loads first ...
+        const int i = base + q * kCommitThreads + t;
+        kr[q] = i < nkeys ? kb[i] : 0ull;
       }
-      if (!stop) out[cnt++] = argmax_key_index(sh_row[P.k]);
+#pragma unroll
+      for (int q = 0; q < kKeysPerThread; ++q) {   // ... then fold
+        const int i = base + q * kCommitThreads + t;
+        if (i < nkeys) atomicMax(&sh_row[i / P.chunks], static_cast<unsigned long long>(kr[q]));
+      }
     }
-    for (int i = cnt; i < kp1; ++i) out[i] = -1;
-    P.accept_len[b] = acc;
-    if (P.status) P.status[b] = st;
-    store_agent(&P.emit_count[b], cnt);
-    const uint32_t prev = ticket_agent(P.done_ctr);
-    sh_flag = prev == static_cast<uint32_t>(P.B) - 1u;
+    __syncthreads();
+    int cnt = 0;
+    if (t < ns) {
+      const int b = s0 + t;
+      const int *d = sh_d + t * P.k;
+      int32_t *out = P.out_tokens + static_cast<size_t>(b) * kp1;
+      const unsigned long long *rk = sh_row + t * kp1;
+      const int rem = sh_rem[t];
+      int st = 0;
+      for (int j = 0; j < P.k; ++j)
+        if (d[j] < 0 || d[j] >= P.V) st |= SPEC_ST_DRAFT_OOR;
+      int acc = 0;
+      if (rem != 0) {
+        bool stop = false;
+        for (int j = 0; j < P.k && !stop; ++j) {
+          const int tj = argmax_key_index(rk[j]);
+          out[cnt++] = tj;
+          const bool match = tj == d[j];
+          acc += match;
+          if ((P.eos >= 0 && tj == P.eos) || cnt == rem || !match) stop = true;
+        }
+        if (!stop) out[cnt++] = argmax_key_index(rk[P.k]);
+      }
+      for (int i = cnt; i < kp1; ++i) out[i] = -1;
+      P.accept_len[b] = acc;
+      P.emit_count[b] = cnt;
+      if (P.status) P.status[b] = st;
+    }
+    if (P.emit_offsets) {
+      int total;
+      const int ex = block_excl_scan(t < ns ? cnt : 0, sh_scan, &total);
+      if (t < ns) P.emit_offsets[s0 + t] = carry + ex;
+      carry += total;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (!sh_flag) return;
-
-  // ---- last sequence: emit offsets ----
-  acquire_agent();
-  if (P.emit_offsets) block_offsets(P.emit_count, P.emit_offsets, P.B, sh_scan);
-  if (t == 0) store_agent(P.done_ctr, 0u);
+  if (P.emit_offsets && t == 0) P.emit_offsets[P.B] = carry;
 }
 
 }  // namespace
@@ -263,7 +282,7 @@ using namespace specv;
 
 extern "C" size_t spec_verify_greedy_workspace_bytes(int B, int k, int V, spec_dtype dt) {
   if (B < 1 || k < 1 || V < 1 || k > SPEC_MAX_K) return 0;
-  return greedy_ws_layout(B, k, greedy_chunks(V, dt)).total;
+  return greedy_ws_bytes(B, k, greedy_chunks(V, dt));
 }
 
 extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int k, int V,
@@ -280,12 +299,12 @@ extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int 
   const int chunks = greedy_chunks(V, dt);
   const long long nblocks = static_cast<long long>(B) * (k + 1) * chunks;
   if (nblocks >= INT32_MAX) return SPEC_EINVAL;
-  const GreedyWs lay = greedy_ws_layout(B, k, chunks);
-  if (ws_bytes < lay.total || !aligned(ws, 256)) return SPEC_EWORKSPACE;
+  const size_t wsb = greedy_ws_bytes(B, k, chunks);
+  if (ws_bytes < wsb || !aligned(ws, 256)) return SPEC_EWORKSPACE;
 
   const size_t nl = static_cast<size_t>(B) * (k + 1) * V * elt;
   const void *ins[] = {logits, draft, remaining, ws};
-  const size_t in_n[] = {nl, static_cast<size_t>(B) * k * 4, static_cast<size_t>(B) * 4, lay.total};
+  const size_t in_n[] = {nl, static_cast<size_t>(B) * k * 4, static_cast<size_t>(B) * 4, wsb};
   const void *outs[] = {accept_len, emit_count, out_tokens, emit_offsets, status};
   const size_t out_n[] = {static_cast<size_t>(B) * 4, static_cast<size_t>(B) * 4,
                           static_cast<size_t>(B) * (k + 1) * 4, static_cast<size_t>(B + 1) * 4,
@@ -312,15 +331,13 @@ extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int 
   P.out_tokens = out_tokens;
   P.emit_offsets = emit_offsets;
   P.status = status;
-  unsigned char *wb = static_cast<unsigned char *>(ws);
-  P.keys = reinterpret_cast<uint64_t *>(wb + lay.keys);
-  P.seq_ctr = reinterpret_cast<uint32_t *>(wb + lay.seq);
-  P.done_ctr = reinterpret_cast<uint32_t *>(wb + lay.done);
+  P.keys = static_cast<uint64_t *>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (dt == SPEC_BF16)
-    hipLaunchKernelGGL(greedy_verify_kernel<true>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
+    hipLaunchKernelGGL(greedy_chunk_kernel<true>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
   else
-    hipLaunchKernelGGL(greedy_verify_kernel<false>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
+    hipLaunchKernelGGL(greedy_chunk_kernel<false>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(greedy_commit_kernel, dim3(1), dim3(kCommitThreads), 0, s, P);
   return launch_status();
 }

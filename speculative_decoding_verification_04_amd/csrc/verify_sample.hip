@@ -11,13 +11,18 @@
 // Design.  The acceptance chain only gathers 2 scalars per draft.  The bytes
 // are in the single full row each sequence draws from: the residual
 // p_j - q_j at the first rejection (8 bytes per vocabulary entry) or the
-// target row p_k after full acceptance (4 bytes).  One workgroup per
-// (sequence, chunk) recomputes the chain from the gathers, streams its chunk
-// of that row with 16-byte loads and writes the chunk's mass as a float64
-// partial.  The last workgroup of the sequence (agent-scope ticket) adds the
-// partials in chunk order (S), finds the chunk whose running sum first
-// exceeds u * S and scans that chunk in index order to find the token.  All
-// sums are float64 over the float32 r_v in a fixed order, so results are
+// target row p_k after full acceptance (4 bytes).
+//   * sample_chunk_kernel: one workgroup per (sequence, chunk) re-derives the
+//     chain from the gathers, streams its chunk of the row with 16-byte loads
+//     and stores the chunk's mass as a float64 partial; chunk 0 also records
+//     the chain's outcome (accepted count, emitted count, row, status).
+//   * sample_draw_kernel: one workgroup per sequence adds the partials in
+//     chunk order (S), finds the chunk whose running sum first exceeds u * S,
+//     scans that chunk in index order and writes the token; one extra
+//     workgroup scans the emit counts into offsets.
+// No workgroup waits on another (the kernel boundary is the synchronisation:
+// device-scope completion tickets serialise on a multi-XCD part).  All sums
+// are float64 over the float32 r_v in a fixed order, so results are
 // reproducible run to run and within ~1e-16 relative of a correctly rounded
 // sum.
 #include "common.h"
@@ -46,18 +51,17 @@ struct SampleParams {
   double *final_mass;
   int32_t *status;
   double *partial;              // [B * chunks]
-  uint32_t *seq_ctr, *done_ctr;
+  int4 *chain;                  // [B]: mode, row, accepted, status bits
 };
 
 struct SampleWs {
-  size_t part, seq, done, total;
+  size_t part, chain, total;
 };
 inline SampleWs sample_ws_layout(int B, int chunks) {
   SampleWs w;
   w.part = 0;
-  w.seq = round_up(static_cast<size_t>(B) * chunks * sizeof(double), 256);
-  w.done = w.seq + round_up(static_cast<size_t>(B) * sizeof(uint32_t), 256);
-  w.total = w.done + 256;
+  w.chain = round_up(static_cast<size_t>(B) * chunks * sizeof(double), 256);
+  w.total = w.chain + round_up(static_cast<size_t>(B) * sizeof(int4), 256);
   return w;
 }
 
@@ -124,14 +128,11 @@ __device__ inline double chunk_mass(const Row &r, int c, int V, bool vec, double
 template <typename T>
 __device__ inline bool finite_val(T x) { return isfinite(x); }
 
-__global__ __launch_bounds__(kThreads) void sample_verify_kernel(SampleParams P) {
+__global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleParams P) {
   __shared__ int sh_acc[SPEC_MAX_K];
   __shared__ int sh_st[SPEC_MAX_K];
-  __shared__ int sh_mode, sh_row, sh_cnt, sh_m, sh_stat, sh_flag, sh_tok;
+  __shared__ int sh_mode, sh_row;
   __shared__ double sh_red[kWaves];
-  __shared__ double sh_part[kMaxChunks];
-  __shared__ int sh_scan[kWaves + 1];
-  __shared__ double sh_dscan[kWaves + 1];
 
   const int t = threadIdx.x;
   const int b = blockIdx.x / P.chunks;
@@ -168,16 +169,15 @@ __global__ __launch_bounds__(kThreads) void sample_verify_kernel(SampleParams P)
   __syncthreads();
   if (t == 0) {
     const int rem = P.remaining ? P.remaining[b] : -1;   // negative: no budget
-    int mode = MODE_ROW, row = k, cnt = 0, m = 0, st = 0;
+    int mode = MODE_ROW, row = k, m = 0, st = 0;
     if (rem == 0) {
       mode = MODE_NONE;
     } else {
       for (int j = 0; j < k; ++j) {
         st |= sh_st[j];
         if (sh_acc[j]) {
-          ++cnt;
           ++m;
-          if ((P.eos >= 0 && d[j] == P.eos) || cnt == rem) {
+          if ((P.eos >= 0 && d[j] == P.eos) || m == rem) {
             mode = MODE_NONE;
             break;
           }
@@ -190,49 +190,60 @@ __global__ __launch_bounds__(kThreads) void sample_verify_kernel(SampleParams P)
     }
     sh_mode = mode;
     sh_row = row;
-    sh_cnt = cnt;
-    sh_m = m;
-    sh_stat = st;
+    if (c == 0) {
+      P.chain[b] = make_int4(mode, row, m, st);
+      P.accept_len[b] = m;
+      P.emit_count[b] = m + (mode != MODE_NONE ? 1 : 0);
+    }
   }
   __syncthreads();
   const int mode = sh_mode, jrow = sh_row;
+  if (mode == MODE_NONE) return;
   Row r;
   r.a = pb + static_cast<size_t>(jrow) * V;
   r.b = mode == MODE_RESID ? qb + static_cast<size_t>(jrow) * V : nullptr;
-  const bool vec = P.vec != 0;
+  const double part = chunk_mass(r, c, V, P.vec != 0, sh_red);
+  if (t == 0) P.partial[static_cast<size_t>(b) * P.chunks + c] = part;
+}
 
-  // ---- this chunk's share of the row mass
-  if (mode != MODE_NONE) {
-    const double part = chunk_mass(r, c, V, vec, sh_red);
-    if (t == 0) store_agent(&P.partial[static_cast<size_t>(b) * P.chunks + c], part);
-  }
-  if (t == 0) {
-    const uint32_t prev = ticket_agent(&P.seq_ctr[b]);
-    sh_flag = prev == static_cast<uint32_t>(P.chunks) - 1u;
-  }
-  __syncthreads();
-  if (!sh_flag) return;
+__global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
+  __shared__ double sh_red[kWaves];
+  __shared__ double sh_part[kMaxChunks];
+  __shared__ int sh_scan[kWaves + 1];
+  __shared__ int sh_last[kWaves];
+  __shared__ double sh_dscan[kWaves + 1];
+  __shared__ int sh_cs, sh_tok;
+  __shared__ double sh_base, sh_S;
 
-  // ---- last workgroup of sequence b: the draw ----
-  acquire_agent();
-  int st = sh_stat;
+  const int t = threadIdx.x;
+  const int k = P.k, kp1 = k + 1, V = P.V;
+  if (static_cast<int>(blockIdx.x) == P.B) {     // emit offsets
+    if (P.emit_offsets) block_offsets(P.emit_count, P.emit_offsets, P.B, sh_scan);
+    return;
+  }
+  const int b = blockIdx.x;
+  const int4 ch = P.chain[b];
+  const int mode = ch.x, jrow = ch.y, m = ch.z;
+  int st = ch.w;
+  const int32_t *d = P.draft + static_cast<size_t>(b) * k;
+  const float *pb = P.p + static_cast<size_t>(b) * kp1 * V;
+  const float *qb = P.q + static_cast<size_t>(b) * k * V;
   int tok = -1;
   double S = 0.0;
   if (mode != MODE_NONE) {
-    for (int i = t; i < P.chunks; i += kThreads) {
-      double *slot = &P.partial[static_cast<size_t>(b) * P.chunks + i];
-      sh_part[i] = load_agent(slot);
-      store_agent(slot, 0.0);   // leave the workspace zeroed
-    }
+    Row r;
+    r.a = pb + static_cast<size_t>(jrow) * V;
+    r.b = mode == MODE_RESID ? qb + static_cast<size_t>(jrow) * V : nullptr;
+    const bool vec = P.vec != 0;
+    for (int i = t; i < P.chunks; i += kThreads) sh_part[i] = P.partial[static_cast<size_t>(b) * P.chunks + i];
     __syncthreads();
     if (t == 0) {
       double s = 0.0;
       for (int i = 0; i < P.chunks; ++i) s += sh_part[i];
-      sh_red[0] = s;
+      sh_S = s;
     }
     __syncthreads();
-    S = sh_red[0];
-    __syncthreads();
+    S = sh_S;
     if (isfinite(S) && !(S > 0.0)) {
       st |= SPEC_ST_RESID_ZERO;
       if (mode == MODE_RESID) {         // fall back to the target row p_j itself
@@ -245,11 +256,10 @@ __global__ __launch_bounds__(kThreads) void sample_verify_kernel(SampleParams P)
         if (t == 0) {
           double s = 0.0;
           for (int i = 0; i < P.chunks; ++i) s += sh_part[i];
-          sh_red[0] = s;
+          sh_S = s;
         }
         __syncthreads();
-        S = sh_red[0];
-        __syncthreads();
+        S = sh_S;
       }
     }
     if (!isfinite(S)) {
@@ -258,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void sample_verify_kernel(SampleParams P)
     } else if (!(S > 0.0)) {
       tok = 0;
     } else {
-      const double T = static_cast<double>(ub[k]) * S;
+      const double T = static_cast<double>(P.u[static_cast<size_t>(b) * kp1 + k]) * S;
       if (t == 0) {
         double run = 0.0;
         int cs = -1, last = -1;
@@ -272,19 +282,17 @@ __global__ __launch_bounds__(kThreads) void sample_verify_kernel(SampleParams P)
           run = 0.0;
           for (int i = 0; i < cs; ++i) run += sh_part[i];
         }
-        sh_row = cs;
-        sh_red[0] = run;
+        sh_cs = cs;
+        sh_base = run;
       }
       __syncthreads();
-      const int cs = sh_row;
-      const double base = sh_red[0];
-      __syncthreads();
+      const int cs = sh_cs;
+      const double base = sh_base;
       // in-chunk scan in index order: lane t owns kEPT consecutive elements
       const int lo = cs * kChunk + t * kEPT;
       double mine = 0.0;
       for (int i = 0; i < kEPT; ++i)
         if (lo + i < V) mine += static_cast<double>(r.at(lo + i));
-      // block exclusive scan of the lanes' sums (fixed order)
       const int lane = t & (kWave - 1), w = t / kWave;
       double inc = mine;
 #pragma unroll
@@ -307,17 +315,16 @@ __global__ __launch_bounds__(kThreads) void sample_verify_kernel(SampleParams P)
         if (cand == INT_MAX && run > T) cand = v;
       }
       const int wc = wave_min(cand), wl = wave_max_i(lastpos);
-      __syncthreads();
       if (lane == 0) {
         sh_scan[w] = wc;
-        sh_acc[w] = wl;
+        sh_last[w] = wl;
       }
       __syncthreads();
       if (t == 0) {
         int best = INT_MAX, lp = -1;
         for (int i = 0; i < kWaves; ++i) {
           best = min(best, sh_scan[i]);
-          lp = max(lp, sh_acc[i]);
+          lp = max(lp, sh_last[i]);
         }
         sh_tok = best != INT_MAX ? best : lp;
       }
@@ -326,25 +333,14 @@ __global__ __launch_bounds__(kThreads) void sample_verify_kernel(SampleParams P)
     }
   }
   if (t == 0) {
-    store_agent(&P.seq_ctr[b], 0u);
     int32_t *out = P.out_tokens + static_cast<size_t>(b) * kp1;
-    const int m = sh_m;
-    int cnt = sh_cnt;
-    for (int j = 0; j < m; ++j) out[j] = d[j];
+    int cnt = 0;
+    for (int j = 0; j < m; ++j) out[cnt++] = d[j];
     if (mode != MODE_NONE) out[cnt++] = tok;
     for (int i = cnt; i < kp1; ++i) out[i] = -1;
-    P.accept_len[b] = m;
     if (P.final_mass) P.final_mass[b] = mode != MODE_NONE ? S : 0.0;
     if (P.status) P.status[b] = st;
-    store_agent(&P.emit_count[b], cnt);
-    const uint32_t prev = ticket_agent(P.done_ctr);
-    sh_flag = prev == static_cast<uint32_t>(P.B) - 1u;
   }
-  __syncthreads();
-  if (!sh_flag) return;
-  acquire_agent();
-  if (P.emit_offsets) block_offsets(P.emit_count, P.emit_offsets, P.B, sh_scan);
-  if (t == 0) store_agent(P.done_ctr, 0u);
 }
 
 inline int sample_chunks(int V) { return (V + kChunk - 1) / kChunk; }
@@ -373,7 +369,7 @@ extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t 
   if (chunks > kMaxChunks) return SPEC_ECAPACITY;
   if (!aligned(p, 4) || !aligned(q, 4) || !aligned(uniforms, 4)) return SPEC_EINVAL;
   const long long nblocks = static_cast<long long>(B) * chunks;
-  if (nblocks >= INT32_MAX) return SPEC_EINVAL;
+  if (nblocks >= INT32_MAX || B >= INT32_MAX - 1) return SPEC_EINVAL;
   const SampleWs lay = sample_ws_layout(B, chunks);
   if (ws_bytes < lay.total || !aligned(ws, 256)) return SPEC_EWORKSPACE;
 
@@ -412,10 +408,10 @@ extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t 
   P.status = status;
   unsigned char *wb = static_cast<unsigned char *>(ws);
   P.partial = reinterpret_cast<double *>(wb + lay.part);
-  P.seq_ctr = reinterpret_cast<uint32_t *>(wb + lay.seq);
-  P.done_ctr = reinterpret_cast<uint32_t *>(wb + lay.done);
+  P.chain = reinterpret_cast<int4 *>(wb + lay.chain);
+  hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(sample_verify_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), P);
+  hipLaunchKernelGGL(sample_chunk_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(sample_draw_kernel, dim3(static_cast<unsigned>(B) + 1u), dim3(kThreads), 0, s, P);
   return launch_status();
 }
