@@ -227,6 +227,9 @@ def main() -> int:
         probe = 2 * PROBE_BYTES / min(ts)
         del src, dst
 
+    log("secondary: stochastic verify (workload 2) and same-length grouping (workload 4)")
+    secondary = secondary_measurements(dev, np, torch, sv, W)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores)")
@@ -266,10 +269,60 @@ def main() -> int:
         "realign_ms_per_call": statistics.mean(t_rea) * 1e3,
         "copy_probe_GBps": None if probe is None else probe / 1e9,
         "parity_checked": parity,
+        "secondary": secondary,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result))
     return 0
+
+
+def _time_calls(torch, fn, reps: int) -> float:
+    """Median seconds per call over `reps` calls, HIP events on the launch stream."""
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    return statistics.median(ts[2:])
+
+
+def secondary_measurements(dev, np, torch, sv, W) -> dict:
+    """The other two steps at their workload shapes (not part of `value`)."""
+    out = {}
+    r = W.sample_round(2)
+    B, k, V = r["B"], r["k"], r["V"]
+    p, q = torch.from_numpy(r["p"]).to(dev), torch.from_numpy(r["q"]).to(dev)
+    d, u = torch.from_numpy(r["drafts"]).to(dev), torch.from_numpy(r["uniforms"]).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    acc, emit, toks = torch.empty(B, **i32), torch.empty(B, **i32), torch.empty(B, k + 1, **i32)
+    offs, mass = torch.empty(B + 1, **i32), torch.empty(B, dtype=torch.float64, device=dev)
+    ws = sv.workspace(sv.spec_verify_sample_workspace_bytes(B, k, V), dev)
+    call = lambda: sv.spec_verify_sample(p, q, d, u, acc, emit, toks, ws, emit_offsets=offs, final_mass=mass)
+    t = _time_calls(torch, call, 22)
+    m, e = acc.cpu().numpy(), emit.cpu().numpy()
+    # realized algorithmic bytes: the row drawn from (p_j and q_j after a rejection,
+    # p_k after full acceptance) plus two gathered scalars per examined draft
+    row_bytes = sum(8 * V if (e[b] > m[b] and m[b] < k) else (4 * V if e[b] > m[b] else 0) for b in range(B))
+    gathers = 8 * int(sum(min(int(m[b]) + 1, k) for b in range(B)))
+    nbytes = row_bytes + gathers + 4 * B * (k + 1) * 2
+    out["sample_verify"] = {"workload": f"stochastic verify, B={B} k={k} V={V} f32", "us_per_call": t * 1e6,
+                            "rows_per_s": B * (k + 1) / t, "algorithmic_bytes": nbytes,
+                            "GBps": nbytes / t / 1e9, "frac_of_peak": nbytes / t / PEAK_HBM}
+    P = W.pool_lengths()
+    L = torch.as_tensor(P, dtype=torch.int32, device=dev)
+    N = P.size
+    perm, bstart, blen = torch.empty(N, **i32), torch.empty(N + 1, **i32), torch.empty(N, **i32)
+    nb, ng = torch.empty(1, **i32), torch.empty(1, **i32)
+    cfg = W.workload(4)
+    call = lambda: sv.spec_group_same_length(L, cfg["B"], cfg["min_group"], perm, bstart, blen, nb, ng)
+    t = _time_calls(torch, call, 52)
+    out["group_same_length"] = {"workload": f"same-length grouping, pool {N}, batch {cfg['B']}, min_group {cfg['min_group']}",
+                                "us_per_call": t * 1e6, "num_batches": int(nb.item()),
+                                "grouped_fraction": int(ng.item()) / N}
+    return out
 
 
 def cpu_baseline(r0: dict, ref_verify: dict, g: dict, np) -> dict:

@@ -14,8 +14,9 @@
 // It is a pure copy bound by HBM bandwidth (read + write of every moved byte).
 //   * One workgroup per moving plane.  The moved bytes form one contiguous
 //     range; the workgroup walks it from the right end to the left in tiles of
-//     kThreads * kTileVec 16-byte vectors (16 KB), consecutive lanes on
-//     consecutive vectors, exactly like a streaming copy.
+//     kThreads * kTileVec 16-byte vectors (64 KB), consecutive lanes on
+//     consecutive vectors, with non-temporal loads and stores (every byte is
+//     touched once).
 //   * In-place overlap: a tile is loaded into registers, every lane waits for
 //     its loads to land, a workgroup barrier follows, and only then is the
 //     tile stored delta columns to the right.  The tile to its left is loaded
@@ -23,20 +24,24 @@
 //     destination begins, so the two never overlap; and a tile's destination
 //     only overlaps its own source and the source of the tile to its right,
 //     both already in registers.
-//   * Planes are dispatched longest move first (ties by sequence index) so the
-//     last workgroups to start are the shortest ones.
-//   * B extra workgroups write the position-id and mask rows; one more writes
-//     the scalar outputs.  Outputs never alias inputs, so no workgroup needs
-//     to wait for another.
+//   * Few, wide walkers: each workgroup reserves more than half of a CU's LDS,
+//     so one runs per CU and about one plane per CU is in flight.  Planes are
+//     dispatched in address order, so the planes in flight sit in one window
+//     of memory.  Many narrow walkers (several per CU, each on its own plane
+//     far from the others) keep more DRAM pages open at once and measured
+//     about 10% slower on MI355X; so did longest-move-first dispatch.
+//   * The first B workgroups write the position-id and mask rows, the next
+//     one the scalar outputs; they finish early and never wait.  Outputs
+//     never alias inputs, so no workgroup waits for another.
 #include "common.h"
 
 namespace specv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kTileVec = 4;    // 16-byte vectors per lane per tile (16 KB tiles)
-constexpr int kRankMaxB = 256;  // batches up to this size are dispatched longest move first
+constexpr int kTileVec = 4;              // 16-byte vectors per lane per tile (64 KB tiles)
+constexpr int kReserveWords = 24 * 1024; // 96 KB of the CU's 160 KB LDS: one workgroup per CU
 
 struct RealignParams {
   unsigned char *kv;
@@ -49,6 +54,9 @@ struct RealignParams {
   int64_t *bytes_moved;
   int32_t *status;
 };
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 template <int VB>
 struct VecOf;
@@ -67,6 +75,28 @@ __device__ inline void hold(uint4 v) { asm volatile("" ::"v"(v.x), "v"(v.y), "v"
 __device__ inline void hold(uint2 v) { asm volatile("" ::"v"(v.x), "v"(v.y)); }
 __device__ inline void hold(uint32_t v) { asm volatile("" ::"v"(v)); }
 __device__ inline void hold(uint16_t v) { asm volatile("" ::"v"(static_cast<uint32_t>(v))); }
+
+// Streaming (non-temporal) access: every moved byte is read once and written once.
+template <typename VT>
+__device__ inline VT stream_ld(const VT *p) { return __builtin_nontemporal_load(p); }
+__device__ inline uint4 stream_ld(const uint4 *p) {
+  const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ inline uint2 stream_ld(const uint2 *p) {
+  const v2u x = __builtin_nontemporal_load(reinterpret_cast<const v2u *>(p));
+  return make_uint2(x.x, x.y);
+}
+template <typename VT>
+__device__ inline void stream_st(VT v, VT *p) { __builtin_nontemporal_store(v, p); }
+__device__ inline void stream_st(uint4 v, uint4 *p) {
+  v4u x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<v4u *>(p));
+}
+__device__ inline void stream_st(uint2 v, uint2 *p) {
+  v2u x = {v.x, v.y};
+  __builtin_nontemporal_store(x, reinterpret_cast<v2u *>(p));
+}
 
 // Shared by every workgroup: E, M = max e_b and whether the state is valid.
 // Every workgroup computes the same values from the same inputs.
@@ -97,30 +127,6 @@ __device__ inline void commit_state(const RealignParams &P, int *sh, int &E, int
   M = mm;
 }
 
-// Sequence whose planes block-group `rank` moves: sequences ordered by moved
-// length (n_b + e_b if delta_b > 0, else -1), longest first, ties by index.
-// Batches up to kRankMaxB only; keys are staged in LDS, one ranking pass.
-__device__ inline int ranked_sequence(const RealignParams &P, int M, int rank, int *sh_keys, int *sh_seq) {
-  const int t = threadIdx.x;
-  for (int b = t; b < P.B; b += blockDim.x) {
-    const int eb = P.emit_count[b];
-    sh_keys[b] = eb != M ? P.kv_len_in[b] + eb : -1;
-  }
-  if (t == 0) *sh_seq = -1;
-  __syncthreads();
-  for (int b = t; b < P.B; b += blockDim.x) {
-    const int kb = sh_keys[b];
-    int r = 0;
-    for (int o = 0; o < P.B; ++o) {
-      const int ko = sh_keys[o];
-      r += (ko > kb) || (ko == kb && o < b);
-    }
-    if (r == rank) *sh_seq = b;
-  }
-  __syncthreads();
-  return *sh_seq;
-}
-
 template <int VB>
 __device__ inline void move_plane(const RealignParams &P, int p, int b, int E, int M) {
   using VT = typename VecOf<VB>::T;
@@ -140,7 +146,7 @@ __device__ inline void move_plane(const RealignParams &P, int p, int b, int E, i
 #pragma unroll
   for (int u = 0; u < kTileVec; ++u) {
     const long long i = hi - TV + u * kThreads + t;
-    if (i >= lo) cur[u] = base[i];
+    if (i >= lo) cur[u] = stream_ld(base + i);
   }
   while (true) {
     const long long nhi = hi - TV;
@@ -149,7 +155,7 @@ __device__ inline void move_plane(const RealignParams &P, int p, int b, int E, i
 #pragma unroll
       for (int u = 0; u < kTileVec; ++u) {
         const long long i = nhi - TV + u * kThreads + t;
-        if (i >= lo) nxt[u] = base[i];
+        if (i >= lo) nxt[u] = stream_ld(base + i);
       }
     }
 #pragma unroll
@@ -159,7 +165,7 @@ __device__ inline void move_plane(const RealignParams &P, int p, int b, int E, i
 #pragma unroll
     for (int u = 0; u < kTileVec; ++u) {
       const long long i = hi - TV + u * kThreads + t;
-      if (i >= lo) base[i + shift] = cur[u];
+      if (i >= lo) stream_st(cur[u], base + i + shift);
     }
     if (!more) break;
 #pragma unroll
@@ -170,27 +176,19 @@ __device__ inline void move_plane(const RealignParams &P, int p, int b, int E, i
 
 template <int VB>
 __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
-  __shared__ int sh[2 * kWaves + 2];
+  __shared__ int sh[2 * kWaves];
   __shared__ long long sh_bytes[kWaves];
-  __shared__ int sh_keys[kRankMaxB];
+  __shared__ uint32_t sh_reserve[kReserveWords];
+  asm volatile("" ::"s"(sh_reserve));      // keep the reservation (it limits residency, holds no data)
   int E, M;
   bool ok;
   commit_state(P, sh, E, M, ok);
   const int blk = blockIdx.x;
   const int t = threadIdx.x;
 
-  if (blk < P.num_planes) {
+  if (blk < P.B) {                         // position ids and mask of one sequence
     if (!ok) return;
-    const int per_seq = P.num_planes / P.B;                  // L * 2 * H planes per sequence
-    const int rank = blk / per_seq, j = blk - rank * per_seq;
-    const int b = P.B <= kRankMaxB ? ranked_sequence(P, M, rank, sh_keys, &sh[2 * kWaves]) : rank;
-    const int h = j % P.H, lk = j / P.H;                     // lk = layer * 2 + kv
-    move_plane<VB>(P, (lk * P.B + b) * P.H + h, b, E, M);
-    return;
-  }
-  if (blk < P.num_planes + P.B) {          // position ids and mask of one sequence
-    if (!ok) return;
-    const int b = blk - P.num_planes;
+    const int b = blk;
     const int En = E + M;
     const int start = En - (P.kv_len_in[b] + P.emit_count[b]);
     int32_t *pos = P.pos_ids + static_cast<size_t>(b) * P.C;
@@ -200,6 +198,12 @@ __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
       msk[c] = in ? 1 : 0;
       pos[c] = in ? c - start : 0;
     }
+    return;
+  }
+  if (blk > P.B) {                         // one plane, address order: p = ((l * 2 + kv) * B + b) * H + h
+    if (!ok) return;
+    const int p = blk - P.B - 1;
+    move_plane<VB>(P, p, (p / P.H) % P.B, E, M);
     return;
   }
   // scalar outputs
@@ -289,7 +293,7 @@ extern "C" int spec_commit_realign_kv(void *kv, spec_dtype dt, int L, int B, int
   P.mask = mask;
   P.bytes_moved = bytes_moved;
   P.status = status;
-  const dim3 grid(static_cast<unsigned>(planes + B + 1)), block(kThreads);
+  const dim3 grid(static_cast<unsigned>(B + 1 + planes)), block(kThreads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (R % 16 == 0 && aligned(kv, 16))

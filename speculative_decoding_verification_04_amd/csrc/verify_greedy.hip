@@ -19,9 +19,10 @@
 //     tickets cost far more than this whole pass on a multi-XCD part (device-
 //     scope atomics on one address serialise, and waiting on them holds the
 //     CU's wave slots), so the kernel boundary is the synchronisation.
-//   * greedy_commit_kernel: one workgroup folds the chunk keys of each row
-//     (LDS atomic max), walks each sequence's drafts, writes its outputs, and
-//     scans the emit counts into offsets, a tile of sequences at a time.
+//   * greedy_commit_kernel: one workgroup; one lane per row folds that row's
+//     chunk keys in registers, then one lane per sequence walks its drafts and
+//     writes its outputs, and the emit counts are scanned into offsets, a tile
+//     of sequences at a time.
 #include "common.h"
 
 namespace specv {
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void greedy_chunk_kernel(GreedyParams P) 
 
 constexpr int kCommitThreads = 1024;
 constexpr int kCommitRows = 1024;   // row keys folded per tile (LDS)
-constexpr int kKeysPerThread = 8;   // chunk keys in flight per lane
+constexpr int kKeysPerThread = 16;  // chunk keys in flight per lane
 
 // One workgroup.  Per tile of sequences, every global read (chunk keys, drafts,
 // budgets) is issued at once into LDS; the walk then runs from LDS only.
@@ -216,25 +217,22 @@ __global__ __launch_bounds__(kCommitThreads) void greedy_commit_kernel(GreedyPar
   for (int s0 = 0; s0 < P.B; s0 += per_tile) {
     const int ns = min(per_tile, P.B - s0);
     const int nrows = ns * kp1;
-    for (int i = t; i < nrows; i += kCommitThreads) sh_row[i] = 0ull;
-    __syncthreads();
-    // one round trip: keys, drafts and budgets are all requested before any is used
+    // one round trip: drafts, budgets and every chunk key are requested before
+    // any is used; lane r folds row r's keys in registers (no LDS atomics)
     const uint64_t *kb = P.keys + static_cast<size_t>(s0) * kp1 * P.chunks;
     for (int i = t; i < ns * P.k; i += kCommitThreads) sh_d[i] = P.draft[static_cast<size_t>(s0) * P.k + i];
     if (t < ns) sh_rem[t] = P.remaining ? P.remaining[s0 + t] : -1;   // negative: no budget
-    const int nkeys = nrows * P.chunks;
-    for (int base = 0; base < nkeys; base += kCommitThreads * kKeysPerThread) {
-      uint64_t kr[kKeysPerThread];
+    for (int r = t; r < nrows; r += kCommitThreads) {
+      const uint64_t *rk = kb + static_cast<size_t>(r) * P.chunks;
+      uint64_t best = 0ull;
+      for (int c0 = 0; c0 < P.chunks; c0 += kKeysPerThread) {
+        uint64_t kr[kKeysPerThread];
 #pragma unroll
-      for (int q = 0; q < kKeysPerThread; ++q) {   // all loads first ...
-        const int i = base + q * kCommitThreads + t;
-        kr[q] = i < nkeys ? kb[i] : 0ull;
-      }
+        for (int q = 0; q < kKeysPerThread; ++q) kr[q] = c0 + q < P.chunks ? rk[c0 + q] : 0ull;
 #pragma unroll
-      for (int q = 0; q < kKeysPerThread; ++q) {   // ... then fold
-        const int i = base + q * kCommitThreads + t;
-        if (i < nkeys) atomicMax(&sh_row[i / P.chunks], static_cast<unsigned long long>(kr[q]));
+        for (int q = 0; q < kKeysPerThread; ++q) best = kr[q] > best ? kr[q] : best;
       }
+      sh_row[r] = best;
     }
     __syncthreads();
     int cnt = 0;
