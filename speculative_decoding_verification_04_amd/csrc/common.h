@@ -50,6 +50,30 @@ __device__ inline int argmax_key_index(uint64_t key) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
 }
 
+// DPP lane-move controls (CDNA): quad_perm [1,0,3,2] and [2,3,0,1] (lane xor 1
+// and xor 2), and the mirrors within half rows (8 lanes) and rows (16 lanes).
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Wave maximum through DPP lane moves (no LDS round trips): butterflies inside
+// each row of 16 lanes (xor 1, xor 2, half-row mirror, row mirror leave every
+// lane with its row's maximum), then the four row maxima are read as scalars.
+// Every lane returns the wave maximum.
+__device__ inline float wave_max_dpp(float v) {
+  int x = __float_as_int(v);
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, kDppQuadXor1, 0xF, 0xF, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, kDppQuadXor2, 0xF, 0xF, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, kDppRowHalfMirror, 0xF, 0xF, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, kDppRowMirror, 0xF, 0xF, false))));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(x, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(x, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(x, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(x, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int m = kWave / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));

@@ -11,11 +11,13 @@
 // tiny commit pass.
 //   * greedy_chunk_kernel: each row is cut into chunks of kThreads*VEC*U
 //     elements; one workgroup per (row, chunk) loads its chunk with 16-byte
-//     non-temporal loads (U in flight per lane), takes the chunk maximum with
-//     plain max instructions, then finds the first index holding it (only the
-//     lanes holding it search), and stores one 64-bit key (value order high,
-//     UINT32_MAX - index low; the largest key is the argmax at the lowest
-//     index).  No workgroup waits for another: cross-workgroup completion
+//     non-temporal loads (U in flight per lane).  The chunk maximum comes from
+//     plain max instructions, DPP lane moves inside each wave and LDS across
+//     waves; then only the lanes holding it search their own elements for its
+//     first index (an LDS minimum picks the lowest), and one 64-bit key is
+//     stored (value order high, UINT32_MAX - index low; the largest key is
+//     the argmax at the lowest index).  Searching in every lane, or reducing
+//     64-bit keys through LDS permutes, measured about 0.5 us slower.  No workgroup waits for another: cross-workgroup completion
 //     tickets cost far more than this whole pass on a multi-XCD part (device-
 //     scope atomics on one address serialise, and waiting on them holds the
 //     CU's wave slots), so the kernel boundary is the synchronisation.
@@ -106,22 +108,23 @@ __device__ inline float vec_max(uint4 x) {
   }
 }
 
-// Position (0..VEC-1) of the first element equal to m, or -1.
+// Position (0..VEC-1) of the first element equal to m, or VEC.
 template <bool BF16>
 __device__ inline int vec_find(uint4 x, float m) {
   const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  int q = BF16 ? 8 : 4;
+  // scanned from the back so the first match wins; no early exit (no branches)
   if constexpr (BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (lo_bf16(w[i]) == m) return 2 * i;
-      if (hi_bf16(w[i]) == m) return 2 * i + 1;
+    for (int i = 3; i >= 0; --i) {
+      q = hi_bf16(w[i]) == m ? 2 * i + 1 : q;
+      q = lo_bf16(w[i]) == m ? 2 * i : q;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (__uint_as_float(w[i]) == m) return i;
+    for (int i = 3; i >= 0; --i) q = __uint_as_float(w[i]) == m ? i : q;
   }
-  return -1;
+  return q;
 }
 
 template <bool BF16>
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void greedy_chunk_kernel(GreedyParams P) 
   using Tr = GreedyTraits<BF16>;
   constexpr int ELT = Tr::ELT, VEC = Tr::VEC, U = Tr::U;
   __shared__ float sh_max[kWaves];
-  __shared__ int sh_idx[kWaves];
+  __shared__ int sh_first;
 
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
   const int row = blockIdx.x / P.chunks;
@@ -155,48 +158,38 @@ __global__ __launch_bounds__(kThreads) void greedy_chunk_kernel(GreedyParams P) 
   }
   if (has_tail) tv = load_elem<BF16>(rowp, s + nv * VEC + t);
 
+  // Lane maximum (the -inf filler of missing vectors cannot exceed it unless
+  // the lane holds no element at all), then the chunk maximum: DPP inside each
+  // wave, LDS across the waves.
   float lmax = fmaxf(hv, tv);
 #pragma unroll
   for (int u = 0; u < U; ++u) lmax = fmaxf(lmax, vec_max<BF16>(buf[u]));
-
-  const float wm = wave_max(lmax);
+  const float wm = wave_max_dpp(lmax);
+  if (t == 0) sh_first = INT_MAX;
   if (lane == 0) sh_max[w] = wm;
   __syncthreads();
   float bmax = sh_max[0];
 #pragma unroll
   for (int i = 1; i < kWaves; ++i) bmax = fmaxf(bmax, sh_max[i]);
 
-  // First index of the chunk maximum: only lanes holding it search; each
-  // lane's elements are visited in increasing index order.
-  int cand = INT_MAX;
+  // Only lanes holding the chunk maximum look for its first index among their
+  // own elements, visited in increasing index order (head, vectors u = 0..U-1,
+  // tail); an LDS minimum across those lanes gives the chunk's first index.
   if (lmax == bmax) {
-    if (has_head && hv == bmax) {
-      cand = t;
-    } else {
-      bool found = false;
+    int cand = INT_MAX;
+    if (has_tail && tv == bmax) cand = s + nv * VEC + t;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int vi = t + u * kThreads;
-        if (!found && vi < nv) {
-          const int q = vec_find<BF16>(buf[u], bmax);
-          if (q >= 0) {
-            cand = s + vi * VEC + q;
-            found = true;
-          }
-        }
-      }
-      if (!found && has_tail && tv == bmax) cand = s + nv * VEC + t;
+    for (int u = U - 1; u >= 0; --u) {
+      const int vi = t + u * kThreads;
+      const int q = vec_find<BF16>(buf[u], bmax);
+      if (vi < nv && q < VEC) cand = s + vi * VEC + q;
     }
+    if (has_head && hv == bmax) cand = t;
+    if (cand != INT_MAX) atomicMin(&sh_first, cand);
   }
-  const int wc = wave_min(cand);
-  if (lane == 0) sh_idx[w] = wc;
   __syncthreads();
-  if (t == 0) {
-    int bi = sh_idx[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) bi = min(bi, sh_idx[i]);
-    P.keys[static_cast<size_t>(row) * P.chunks + c] = bi == INT_MAX ? 0ull : argmax_key(bmax, bi);
-  }
+  if (t == 0)
+    P.keys[static_cast<size_t>(row) * P.chunks + c] = sh_first == INT_MAX ? 0ull : argmax_key(bmax, sh_first);
 }
 
 constexpr int kCommitThreads = 1024;
