@@ -227,7 +227,7 @@ def main() -> int:
         probe = 2 * PROBE_BYTES / min(ts)
         del src, dst
 
-    log("secondary: stochastic verify (workload 2) and same-length grouping (workload 4)")
+    log("secondary: stochastic verify (given rows and from logits) and same-length grouping")
     secondary = secondary_measurements(dev, np, torch, sv, W)
 
     cpu = None
@@ -311,6 +311,33 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
     out["sample_verify"] = {"workload": f"stochastic verify, B={B} k={k} V={V} f32", "us_per_call": t * 1e6,
                             "rows_per_s": B * (k + 1) / t, "algorithmic_bytes": nbytes,
                             "GBps": nbytes / t / 1e9, "frac_of_peak": nbytes / t / PEAK_HBM}
+    # stochastic verification from bf16 logits with temperature 0.7, top-k 50, top-p 0.9
+    g = W.sample_logits(2)
+    T, K, TP = g["temperature"], 50, 0.9
+    zt = torch.from_numpy(g["zt"]).to(dev).to(torch.bfloat16)
+    zd = torch.from_numpy(g["zd"]).to(dev).to(torch.bfloat16)
+    # drafting (outside the step): draw from the processed draft rows by inverse CDF
+    qproc = torch.empty(zd.shape, dtype=torch.float32, device=dev)
+    wsp = sv.workspace(sv.spec_process_workspace_bytes(B * k), dev)
+    sv.spec_process_logits(zd, T, wsp, top_k=K, top_p=TP, probs=qproc)
+    gen = torch.Generator(device=dev).manual_seed(7)
+    ud = torch.rand(B, k, 1, device=dev, generator=gen, dtype=torch.float64)
+    cq = torch.cumsum(qproc.double(), dim=-1)
+    dl = torch.searchsorted(cq, ud * cq[..., -1:]).clamp_(max=V - 1).squeeze(-1).to(torch.int32).contiguous()
+    ul = torch.from_numpy(g["uniforms"]).to(dev)
+    wsl = sv.workspace(sv.spec_verify_sample_logits_workspace_bytes(B, k, V), dev)
+    call = lambda: sv.spec_verify_sample_logits(zt, zd, dl, ul, acc, emit, toks, wsl, temperature=T, top_k=K,
+                                                top_p=TP, emit_offsets=offs, final_mass=mass)
+    t = _time_calls(torch, call, 22)
+    m, e = acc.cpu().numpy(), emit.cpu().numpy()
+    rows_read = B * (2 * k + 1) * V * 2                       # the statistics pass reads every row once
+    redraw = sum(4 * V if (e[b] > m[b] and m[b] < k) else (2 * V if e[b] > m[b] else 0) for b in range(B))
+    nbytes = rows_read + redraw
+    out["sample_verify_logits"] = {"workload": f"stochastic verify from bf16 logits, B={B} k={k} V={V}, "
+                                               f"T={T} top_k={K} top_p={TP}",
+                                   "us_per_call": t * 1e6, "rows_per_s": B * (k + 1) / t,
+                                   "algorithmic_bytes": nbytes, "GBps": nbytes / t / 1e9,
+                                   "frac_of_peak": nbytes / t / PEAK_HBM}
     P = W.pool_lengths()
     L = torch.as_tensor(P, dtype=torch.int32, device=dev)
     N = P.size

@@ -62,6 +62,7 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 
 #define SPEC_MAX_K 127          /* largest number of proposals k per sequence */
 #define SPEC_GROUP_MAX_N 4096   /* largest window for spec_group_same_length */
+#define SPEC_PROC_MAX_V 524288  /* largest vocabulary for the processed-distribution calls */
 
 /* Human-readable name of a return code. */
 const char *spec_strerror(int code);
@@ -134,6 +135,62 @@ int spec_verify_sample(const float *p, const float *q, const int32_t *draft,
                        int32_t *accept_len, int32_t *emit_count, int32_t *out_tokens,
                        int32_t *emit_offsets, double *final_mass, int32_t *status,
                        void *ws, size_t ws_bytes, spec_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Processed sampling distributions from raw logits.
+ * [Walkthrough] 5.1: p and q must be the distributions actually sampled from;
+ * when temperature, top-k or top-p is applied, the processed probabilities
+ * are the ones verified.  The pages do not define the operations; the usual
+ * definitions are used, in this order, for each row z of V logits:
+ *   w(v)  = exp((z(v) - max z) / T)  (0 for z(v) = -inf), T = temperature > 0;
+ *   top-k (top_k >= 1; 0 = off): keep v iff z(v) >= the top_k-th largest
+ *         logit of the row, counting repeats (ties at the boundary are kept);
+ *   top-p (0 < top_p < 1; 1 = off), among the top-k survivors: keep v iff the
+ *         weight of the kept entries with a strictly larger logit is below
+ *         top_p times their total weight (ties at the boundary are kept);
+ *   p'(v) = w(v) / (sum of the kept w), 0 for dropped entries and for rows
+ *         with no weight.
+ * Arithmetic: w in float32 (expf of one IEEE float32 division of z - max z
+ * by T), sums in float64 in a fixed order (results are reproducible run to
+ * run); the top-p comparison uses the weights rounded to 2^-44 units.  Against
+ * a float64 evaluation, p' agrees to a relative 1e-5 (the error of a weight
+ * grows with |z - max z| / T), and a top-p boundary can differ only where the
+ * weight above it is within about V * 2^-45 of top_p times the total.
+ * Logits must be finite or -inf.
+ *
+ * spec_process_logits -- processes R rows:
+ *   logits         [R, V] float32 or bf16 (dt), element-aligned
+ *   probs          [R, V] float32 out or NULL: p'
+ *   row_max        [R] float32 out or NULL: max z
+ *   row_threshold  [R] float32 out or NULL: the smallest kept logit
+ *   row_mass       [R] float64 out or NULL: sum of the kept w
+ *   ws             workspace of spec_process_workspace_bytes(R)
+ * Errors: SPEC_EINVAL for NULL logits or ws, R < 1, V < 1 or V >
+ * SPEC_PROC_MAX_V, T not positive and finite, top_k < 0, top_p outside
+ * (0, 1], misalignment or overlap; SPEC_EWORKSPACE.
+ *
+ * spec_verify_sample_logits -- stochastic verification (as spec_verify_sample)
+ * on p' = processed target logits and q' = processed draft logits, both with
+ * the same temperature, top_k and top_p; the processed rows are never stored.
+ *   target_logits  [B, k+1, V] float32 or bf16 (dt)
+ *   draft_logits   [B, k, V]   same dtype
+ *   other arguments as in spec_verify_sample
+ *   ws             workspace of spec_verify_sample_logits_workspace_bytes(B, k, V)
+ * Errors: as spec_verify_sample, plus the processing errors above.
+ * ------------------------------------------------------------------------ */
+size_t spec_process_workspace_bytes(int R);
+int spec_process_logits(const void *logits, spec_dtype dt, int R, int V, float temperature,
+                        int top_k, float top_p, float *probs, float *row_max,
+                        float *row_threshold, double *row_mass, void *ws, size_t ws_bytes,
+                        spec_stream_t stream);
+size_t spec_verify_sample_logits_workspace_bytes(int B, int k, int V);
+int spec_verify_sample_logits(const void *target_logits, const void *draft_logits, spec_dtype dt,
+                              int B, int k, int V, float temperature, int top_k, float top_p,
+                              const int32_t *draft, const float *uniforms, int32_t eos_id,
+                              const int32_t *remaining, int32_t *accept_len,
+                              int32_t *emit_count, int32_t *out_tokens, int32_t *emit_offsets,
+                              double *final_mass, int32_t *status, void *ws, size_t ws_bytes,
+                              spec_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * Commit: realign the contiguous left-padded KV cache, position ids and mask.

@@ -16,11 +16,13 @@ SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_OK, SPEC_EINVAL, SPEC_EWORKSPACE, SPEC_ECAPACITY, SPEC_EHIP = 0, -1, -2, -3, -4
 SPEC_ST_DRAFT_OOR, SPEC_ST_Q_ZERO, SPEC_ST_RESID_ZERO = 1, 2, 4
 SPEC_ST_NONFINITE, SPEC_ST_BAD_STATE, SPEC_ST_CAPACITY = 8, 16, 32
-SPEC_MAX_K, SPEC_GROUP_MAX_N = 127, 4096
+SPEC_MAX_K, SPEC_GROUP_MAX_N, SPEC_PROC_MAX_V = 127, 4096, 524288
 
 __all__ = [
     "SpecError", "spec_strerror", "spec_verify_greedy_workspace_bytes", "spec_verify_greedy",
-    "spec_verify_sample_workspace_bytes", "spec_verify_sample", "spec_commit_realign_kv",
+    "spec_verify_sample_workspace_bytes", "spec_verify_sample", "spec_process_workspace_bytes",
+    "spec_process_logits", "spec_verify_sample_logits_workspace_bytes", "spec_verify_sample_logits",
+    "spec_commit_realign_kv",
     "spec_group_same_length", "workspace", "library",
 ]
 
@@ -106,6 +108,44 @@ def spec_verify_sample(p, q, draft, uniforms, accept_len, emit_count, out_tokens
         _ptr(accept_len), _ptr(emit_count), _ptr(out_tokens), _ptr(emit_offsets), _ptr(final_mass),
         _ptr(status), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(code, "spec_verify_sample")
+
+
+def spec_process_workspace_bytes(R: int) -> int:
+    return int(library().spec_process_workspace_bytes(R))
+
+
+def spec_verify_sample_logits_workspace_bytes(B: int, k: int, V: int) -> int:
+    return int(library().spec_verify_sample_logits_workspace_bytes(B, k, V))
+
+
+def spec_process_logits(logits, temperature: float, ws, *, top_k: int = 0, top_p: float = 1.0,
+                        probs=None, row_max=None, row_threshold=None, row_mass=None,
+                        stream=None) -> None:
+    """logits [..., V] (bf16/f32); optional outputs probs [..., V] f32, row_max / row_threshold
+    [R] f32, row_mass [R] f64 (R = number of rows)."""
+    V = logits.shape[-1]
+    R = logits.numel() // V
+    code = library().spec_process_logits(
+        _ptr(logits), _dtype_code(logits), R, V, float(temperature), int(top_k), float(top_p),
+        _ptr(probs), _ptr(row_max), _ptr(row_threshold), _ptr(row_mass), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _check(code, "spec_process_logits")
+
+
+def spec_verify_sample_logits(target_logits, draft_logits, draft, uniforms, accept_len, emit_count,
+                              out_tokens, ws, *, temperature: float, top_k: int = 0,
+                              top_p: float = 1.0, eos_id: int = -1, remaining=None,
+                              emit_offsets=None, final_mass=None, status=None, stream=None) -> None:
+    """target_logits [B, k+1, V], draft_logits [B, k, V] (same dtype, bf16/f32)."""
+    B, kp1, V = target_logits.shape
+    if draft_logits.dtype != target_logits.dtype:
+        raise ValueError("target and draft logits must share a dtype")
+    code = library().spec_verify_sample_logits(
+        _ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits), B, kp1 - 1, V,
+        float(temperature), int(top_k), float(top_p), _ptr(draft), _ptr(uniforms), int(eos_id),
+        _ptr(remaining), _ptr(accept_len), _ptr(emit_count), _ptr(out_tokens), _ptr(emit_offsets),
+        _ptr(final_mass), _ptr(status), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(code, "spec_verify_sample_logits")
 
 
 def spec_commit_realign_kv(kv, k: int, end_col, kv_len_in, emit_count, end_col_out, kv_len_out,

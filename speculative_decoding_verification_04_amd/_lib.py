@@ -9,6 +9,7 @@ LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
+_F = ctypes.c_float
 
 # name -> (restype, argtypes), mirroring include/spec_verify.h
 PROTOTYPES = {
@@ -19,6 +20,11 @@ PROTOTYPES = {
     "spec_verify_sample_workspace_bytes": (_SZ, [_I, _I, _I]),
     "spec_verify_sample": (_I, [_P, _P, _P, _P, _I, _I, _I, ctypes.c_int32, _P, _P, _P, _P, _P,
                                 _P, _P, _P, _SZ, _P]),
+    "spec_process_workspace_bytes": (_SZ, [_I]),
+    "spec_process_logits": (_I, [_P, _I, _I, _I, _F, _I, _F, _P, _P, _P, _P, _P, _SZ, _P]),
+    "spec_verify_sample_logits_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "spec_verify_sample_logits": (_I, [_P, _P, _I, _I, _I, _I, _F, _I, _F, _P, _P, ctypes.c_int32,
+                                       _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "spec_commit_realign_kv": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _P]),
     "spec_group_same_length": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),

@@ -25,7 +25,7 @@
 // are float64 over the float32 r_v in a fixed order, so results are
 // reproducible run to run and within ~1e-16 relative of a correctly rounded
 // sum.
-#include "common.h"
+#include "process.h"
 
 namespace specv {
 namespace {
@@ -40,7 +40,10 @@ constexpr int kMaxChunks = 1024;                    // V <= kMaxChunks * kChunk
 enum : int { MODE_NONE = 0, MODE_RESID = 1, MODE_ROW = 2 };
 
 struct SampleParams {
-  const float *p, *q;
+  const float *p, *q;           // dense rows (spec_verify_sample)
+  const void *zp, *zq;          // logits (spec_verify_sample_logits)
+  const ProcStats *sp, *sq;     // statistics of the processed rows
+  float T;
   const int32_t *draft;
   const float *u;
   int B, k, V, chunks;
@@ -65,11 +68,72 @@ inline SampleWs sample_ws_layout(int B, int chunks) {
   return w;
 }
 
-// The mass vector a drawn token comes from: r_v = max(a_v - b_v, 0) when b is
-// set, else r_v = a_v.
-struct Row {
+// The mass vector a drawn token comes from: r_v = max(a_v - b_v, 0) when
+// `resid` is set, else r_v = a_v.  DenseRow reads given float32 rows;
+// LogitRow<BF16> computes the processed rows p', q' from logits on the fly.
+struct DenseRow {
+  static constexpr bool kDense = true;
   const float *a, *b;
-  __device__ inline float at(int v) const { return b ? fmaxf(a[v] - b[v], 0.0f) : a[v]; }
+  bool resid;
+  __device__ inline float at(int v) const { return resid ? fmaxf(a[v] - b[v], 0.0f) : a[v]; }
+};
+
+template <bool BF16>
+struct LogitRow {
+  static constexpr bool kDense = false;
+  const void *a, *b;
+  ProcStats sa, sb;
+  float T;
+  bool resid;
+  __device__ inline float at(int v) const {
+    const float pa = proc_prob(logit_at<BF16>(a, v), sa, T);
+    return resid ? fmaxf(pa - proc_prob(logit_at<BF16>(b, v), sb, T), 0.0f) : pa;
+  }
+};
+
+struct DenseSrc {
+  using RowT = DenseRow;
+  __device__ static inline float p_at(const SampleParams &P, int b, int j, int x) {
+    return P.p[(static_cast<size_t>(b) * (P.k + 1) + j) * P.V + x];
+  }
+  __device__ static inline float q_at(const SampleParams &P, int b, int j, int x) {
+    return P.q[(static_cast<size_t>(b) * P.k + j) * P.V + x];
+  }
+  __device__ static inline DenseRow row(const SampleParams &P, int b, int j, bool resid) {
+    DenseRow r;
+    r.a = P.p + (static_cast<size_t>(b) * (P.k + 1) + j) * P.V;
+    r.b = resid ? P.q + (static_cast<size_t>(b) * P.k + j) * P.V : nullptr;
+    r.resid = resid;
+    return r;
+  }
+};
+
+template <bool BF16>
+struct LogitSrc {
+  using RowT = LogitRow<BF16>;
+  static constexpr size_t kElt = BF16 ? 2 : 4;
+  __device__ static inline const void *prow(const SampleParams &P, int b, int j) {
+    return static_cast<const unsigned char *>(P.zp) + (static_cast<size_t>(b) * (P.k + 1) + j) * P.V * kElt;
+  }
+  __device__ static inline const void *qrow(const SampleParams &P, int b, int j) {
+    return static_cast<const unsigned char *>(P.zq) + (static_cast<size_t>(b) * P.k + j) * P.V * kElt;
+  }
+  __device__ static inline float p_at(const SampleParams &P, int b, int j, int x) {
+    return proc_prob(logit_at<BF16>(prow(P, b, j), x), P.sp[static_cast<size_t>(b) * (P.k + 1) + j], P.T);
+  }
+  __device__ static inline float q_at(const SampleParams &P, int b, int j, int x) {
+    return proc_prob(logit_at<BF16>(qrow(P, b, j), x), P.sq[static_cast<size_t>(b) * P.k + j], P.T);
+  }
+  __device__ static inline LogitRow<BF16> row(const SampleParams &P, int b, int j, bool resid) {
+    LogitRow<BF16> r;
+    r.a = prow(P, b, j);
+    r.sa = P.sp[static_cast<size_t>(b) * (P.k + 1) + j];
+    r.b = resid ? qrow(P, b, j) : nullptr;
+    if (resid) r.sb = P.sq[static_cast<size_t>(b) * P.k + j];
+    r.T = P.T;
+    r.resid = resid;
+    return r;
+  }
 };
 
 __device__ inline double block_sum_d(double v, double *sh) {
@@ -85,42 +149,45 @@ __device__ inline double block_sum_d(double v, double *sh) {
 }
 
 // Mass of chunk c of the row (fixed summation order).  Contains barriers.
-__device__ inline double chunk_mass(const Row &r, int c, int V, bool vec, double *sh) {
+template <class RowT>
+__device__ inline double chunk_mass(const RowT &r, int c, int V, bool vec, double *sh) {
   const int t = threadIdx.x;
   const int lo = c * kChunk;
   double acc = 0.0;
-  if (vec) {
-    float4 av[kU], bv[kU];
+  if constexpr (RowT::kDense) {
+    if (vec) {
+      float4 av[kU], bv[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int v = lo + (t + u * kThreads) * 4;
-      if (v < V) {
-        av[u] = *reinterpret_cast<const float4 *>(r.a + v);
-        if (r.b) bv[u] = *reinterpret_cast<const float4 *>(r.b + v);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int v = lo + (t + u * kThreads) * 4;
-      if (v < V) {
-        if (r.b) {
-          acc += static_cast<double>(fmaxf(av[u].x - bv[u].x, 0.0f));
-          acc += static_cast<double>(fmaxf(av[u].y - bv[u].y, 0.0f));
-          acc += static_cast<double>(fmaxf(av[u].z - bv[u].z, 0.0f));
-          acc += static_cast<double>(fmaxf(av[u].w - bv[u].w, 0.0f));
-        } else {
-          acc += static_cast<double>(av[u].x);
-          acc += static_cast<double>(av[u].y);
-          acc += static_cast<double>(av[u].z);
-          acc += static_cast<double>(av[u].w);
+      for (int u = 0; u < kU; ++u) {
+        const int v = lo + (t + u * kThreads) * 4;
+        if (v < V) {
+          av[u] = *reinterpret_cast<const float4 *>(r.a + v);
+          if (r.resid) bv[u] = *reinterpret_cast<const float4 *>(r.b + v);
         }
       }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int v = lo + (t + u * kThreads) * 4;
+        if (v < V) {
+          if (r.resid) {
+            acc += static_cast<double>(fmaxf(av[u].x - bv[u].x, 0.0f));
+            acc += static_cast<double>(fmaxf(av[u].y - bv[u].y, 0.0f));
+            acc += static_cast<double>(fmaxf(av[u].z - bv[u].z, 0.0f));
+            acc += static_cast<double>(fmaxf(av[u].w - bv[u].w, 0.0f));
+          } else {
+            acc += static_cast<double>(av[u].x);
+            acc += static_cast<double>(av[u].y);
+            acc += static_cast<double>(av[u].z);
+            acc += static_cast<double>(av[u].w);
+          }
+        }
+      }
+      return block_sum_d(acc, sh);
     }
-  } else {
-    for (int i = 0; i < kChunk / kThreads; ++i) {
-      const int v = lo + t + i * kThreads;
-      if (v < V) acc += static_cast<double>(r.at(v));
-    }
+  }
+  for (int i = 0; i < kChunk / kThreads; ++i) {
+    const int v = lo + t + i * kThreads;
+    if (v < V) acc += static_cast<double>(r.at(v));
   }
   return block_sum_d(acc, sh);
 }
@@ -128,6 +195,7 @@ __device__ inline double chunk_mass(const Row &r, int c, int V, bool vec, double
 template <typename T>
 __device__ inline bool finite_val(T x) { return isfinite(x); }
 
+template <class Src>
 __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleParams P) {
   __shared__ int sh_acc[SPEC_MAX_K];
   __shared__ int sh_st[SPEC_MAX_K];
@@ -139,8 +207,6 @@ __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleParams P) 
   const int c = blockIdx.x - b * P.chunks;
   const int k = P.k, kp1 = k + 1, V = P.V;
   const int32_t *d = P.draft + static_cast<size_t>(b) * k;
-  const float *pb = P.p + static_cast<size_t>(b) * kp1 * V;
-  const float *qb = P.q + static_cast<size_t>(b) * k * V;
   const float *ub = P.u + static_cast<size_t>(b) * kp1;
 
   // ---- acceptance chain: every workgroup of the sequence derives the same row
@@ -148,8 +214,8 @@ __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleParams P) 
     const int x = d[j];
     int st = 0, acc = 0;
     if (x >= 0 && x < V) {
-      const float px = pb[static_cast<size_t>(j) * V + x];
-      const float qx = qb[static_cast<size_t>(j) * V + x];
+      const float px = Src::p_at(P, b, j, x);
+      const float qx = Src::q_at(P, b, j, x);
       if (!finite_val(px) || !finite_val(qx)) st |= SPEC_ST_NONFINITE;
       float a;
       if (qx == 0.0f) {
@@ -199,13 +265,12 @@ __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleParams P) 
   __syncthreads();
   const int mode = sh_mode, jrow = sh_row;
   if (mode == MODE_NONE) return;
-  Row r;
-  r.a = pb + static_cast<size_t>(jrow) * V;
-  r.b = mode == MODE_RESID ? qb + static_cast<size_t>(jrow) * V : nullptr;
+  const typename Src::RowT r = Src::row(P, b, jrow, mode == MODE_RESID);
   const double part = chunk_mass(r, c, V, P.vec != 0, sh_red);
   if (t == 0) P.partial[static_cast<size_t>(b) * P.chunks + c] = part;
 }
 
+template <class Src>
 __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
   __shared__ double sh_red[kWaves];
   __shared__ double sh_part[kMaxChunks];
@@ -226,14 +291,10 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
   const int mode = ch.x, jrow = ch.y, m = ch.z;
   int st = ch.w;
   const int32_t *d = P.draft + static_cast<size_t>(b) * k;
-  const float *pb = P.p + static_cast<size_t>(b) * kp1 * V;
-  const float *qb = P.q + static_cast<size_t>(b) * k * V;
   int tok = -1;
   double S = 0.0;
   if (mode != MODE_NONE) {
-    Row r;
-    r.a = pb + static_cast<size_t>(jrow) * V;
-    r.b = mode == MODE_RESID ? qb + static_cast<size_t>(jrow) * V : nullptr;
+    typename Src::RowT r = Src::row(P, b, jrow, mode == MODE_RESID);
     const bool vec = P.vec != 0;
     for (int i = t; i < P.chunks; i += kThreads) sh_part[i] = P.partial[static_cast<size_t>(b) * P.chunks + i];
     __syncthreads();
@@ -247,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
     if (isfinite(S) && !(S > 0.0)) {
       st |= SPEC_ST_RESID_ZERO;
       if (mode == MODE_RESID) {         // fall back to the target row p_j itself
-        r.b = nullptr;
+        r.resid = false;
         for (int i = 0; i < P.chunks; ++i) {
           const double part = chunk_mass(r, i, V, vec, sh_red);
           if (t == 0) sh_part[i] = part;
@@ -391,6 +452,9 @@ extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t 
   SampleParams P;
   P.p = p;
   P.q = q;
+  P.zp = P.zq = nullptr;
+  P.sp = P.sq = nullptr;
+  P.T = 1.0f;
   P.draft = draft;
   P.u = uniforms;
   P.B = B;
@@ -411,7 +475,101 @@ extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t 
   P.chain = reinterpret_cast<int4 *>(wb + lay.chain);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(sample_chunk_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
-  hipLaunchKernelGGL(sample_draw_kernel, dim3(static_cast<unsigned>(B) + 1u), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(sample_chunk_kernel<DenseSrc>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(sample_draw_kernel<DenseSrc>, dim3(static_cast<unsigned>(B) + 1u), dim3(kThreads), 0, s, P);
+  return launch_status();
+}
+
+// Workspace of the verification from logits: per-row statistics of the
+// B * (k+1) target and B * k draft rows, then the layout of spec_verify_sample.
+static size_t sample_logits_stats_bytes(int B, int k) {
+  return round_up(static_cast<size_t>(B) * (2 * k + 1) * sizeof(ProcStats), 256);
+}
+
+extern "C" size_t spec_verify_sample_logits_workspace_bytes(int B, int k, int V) {
+  if (B < 1 || k < 1 || V < 1 || k > SPEC_MAX_K || V > SPEC_PROC_MAX_V || sample_chunks(V) > kMaxChunks) return 0;
+  return sample_logits_stats_bytes(B, k) + sample_ws_layout(B, sample_chunks(V)).total;
+}
+
+extern "C" int spec_verify_sample_logits(const void *target_logits, const void *draft_logits,
+                                         spec_dtype dt, int B, int k, int V, float temperature,
+                                         int top_k, float top_p, const int32_t *draft,
+                                         const float *uniforms, int32_t eos_id,
+                                         const int32_t *remaining, int32_t *accept_len,
+                                         int32_t *emit_count, int32_t *out_tokens,
+                                         int32_t *emit_offsets, double *final_mass,
+                                         int32_t *status, void *ws, size_t ws_bytes,
+                                         spec_stream_t stream) {
+  if (!target_logits || !draft_logits || !draft || !uniforms || !accept_len || !emit_count ||
+      !out_tokens || !ws)
+    return SPEC_EINVAL;
+  if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_EINVAL;
+  if (B < 1 || k < 1 || !proc_args_ok(temperature, top_k, top_p, V)) return SPEC_EINVAL;
+  if (k > SPEC_MAX_K) return SPEC_ECAPACITY;
+  const int chunks = sample_chunks(V);
+  if (chunks > kMaxChunks) return SPEC_ECAPACITY;
+  const size_t elt = dt == SPEC_BF16 ? 2 : 4;
+  if (!aligned(target_logits, elt) || !aligned(draft_logits, elt) || !aligned(uniforms, 4)) return SPEC_EINVAL;
+  const long long nblocks = static_cast<long long>(B) * chunks;
+  const long long rows = static_cast<long long>(B) * (2 * k + 1);
+  if (nblocks >= INT32_MAX || rows >= INT32_MAX || B >= INT32_MAX - 1) return SPEC_EINVAL;
+  const size_t stats_bytes = sample_logits_stats_bytes(B, k);
+  const SampleWs lay = sample_ws_layout(B, chunks);
+  if (ws_bytes < stats_bytes + lay.total || !aligned(ws, 256)) return SPEC_EWORKSPACE;
+
+  const size_t np = static_cast<size_t>(B) * (k + 1) * V * elt, nq = static_cast<size_t>(B) * k * V * elt;
+  const void *ins[] = {target_logits, draft_logits, draft, uniforms, remaining, ws};
+  const size_t in_n[] = {np, nq, static_cast<size_t>(B) * k * 4, static_cast<size_t>(B) * (k + 1) * 4,
+                         static_cast<size_t>(B) * 4, stats_bytes + lay.total};
+  const void *outs[] = {accept_len, emit_count, out_tokens, emit_offsets, final_mass, status};
+  const size_t out_n[] = {static_cast<size_t>(B) * 4, static_cast<size_t>(B) * 4,
+                          static_cast<size_t>(B) * (k + 1) * 4, static_cast<size_t>(B + 1) * 4,
+                          static_cast<size_t>(B) * 8, static_cast<size_t>(B) * 4};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return SPEC_EINVAL;
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return SPEC_EINVAL;
+  }
+
+  unsigned char *wb = static_cast<unsigned char *>(ws);
+  ProcStats *stats = reinterpret_cast<ProcStats *>(wb);
+  SampleParams P;
+  P.p = P.q = nullptr;
+  P.zp = target_logits;
+  P.zq = draft_logits;
+  P.sp = stats;                                   // target rows first
+  P.sq = stats + static_cast<size_t>(B) * (k + 1); // then the draft rows
+  P.T = temperature;
+  P.draft = draft;
+  P.u = uniforms;
+  P.B = B;
+  P.k = k;
+  P.V = V;
+  P.chunks = chunks;
+  P.vec = 0;
+  P.eos = eos_id;
+  P.remaining = remaining;
+  P.accept_len = accept_len;
+  P.emit_count = emit_count;
+  P.out_tokens = out_tokens;
+  P.emit_offsets = emit_offsets;
+  P.final_mass = final_mass;
+  P.status = status;
+  P.partial = reinterpret_cast<double *>(wb + stats_bytes + lay.part);
+  P.chain = reinterpret_cast<int4 *>(wb + stats_bytes + lay.chain);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dt == SPEC_BF16;
+  (void)hipGetLastError();
+  launch_proc_stats(target_logits, draft_logits, B * (k + 1), static_cast<int>(rows), V, bf16, temperature,
+                    top_k, top_p, stats, nullptr, s);
+  const dim3 g1(static_cast<unsigned>(nblocks)), g2(static_cast<unsigned>(B) + 1u), blk(kThreads);
+  if (bf16) {
+    hipLaunchKernelGGL(sample_chunk_kernel<LogitSrc<true>>, g1, blk, 0, s, P);
+    hipLaunchKernelGGL(sample_draw_kernel<LogitSrc<true>>, g2, blk, 0, s, P);
+  } else {
+    hipLaunchKernelGGL(sample_chunk_kernel<LogitSrc<false>>, g1, blk, 0, s, P);
+    hipLaunchKernelGGL(sample_draw_kernel<LogitSrc<false>>, g2, blk, 0, s, P);
+  }
   return launch_status();
 }

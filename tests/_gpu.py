@@ -117,3 +117,40 @@ def kv_bits(kv) -> np.ndarray:
     iv = kv.view(torch.int16) if kv.element_size() == 2 else kv.view(torch.int32)
     a = iv.cpu().numpy()
     return a.view(np.uint16) if kv.element_size() == 2 else a.view(np.uint32)
+
+
+def process(logits_dev, T, top_k=0, top_p=1.0, probs=True, ws_key=None):
+    """Run spec_process_logits; returns probs [..., V] (or None) and per-row stats."""
+    V = logits_dev.shape[-1]
+    R = logits_dev.numel() // V
+    out = dict(row_max=torch.empty(R, dtype=torch.float32, device=DEV),
+               row_threshold=torch.empty(R, dtype=torch.float32, device=DEV),
+               row_mass=torch.empty(R, dtype=torch.float64, device=DEV))
+    if probs:
+        out["probs"] = torch.empty(logits_dev.shape, dtype=torch.float32, device=DEV)
+    w = ws(sv.spec_process_workspace_bytes(R), ws_key)
+    sv.spec_process_logits(logits_dev, T, w, top_k=top_k, top_p=top_p, probs=out.get("probs"),
+                           row_max=out["row_max"], row_threshold=out["row_threshold"],
+                           row_mass=out["row_mass"])
+    return out
+
+
+def verify_sample_logits(zp_dev, zq_dev, drafts, uniforms, T, top_k=0, top_p=1.0, eos_id=-1,
+                         remaining=None, ws_key=None):
+    B, kp1, V = zp_dev.shape
+    k = kp1 - 1
+    out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=DEV),
+               emit_count=torch.empty(B, dtype=torch.int32, device=DEV),
+               out_tokens=torch.empty(B, kp1, dtype=torch.int32, device=DEV),
+               emit_offsets=torch.empty(B + 1, dtype=torch.int32, device=DEV),
+               final_mass=torch.empty(B, dtype=torch.float64, device=DEV),
+               status=torch.empty(B, dtype=torch.int32, device=DEV))
+    w = ws(sv.spec_verify_sample_logits_workspace_bytes(B, k, V), ws_key)
+    d = drafts if torch.is_tensor(drafts) else i32(drafts)
+    u = uniforms if torch.is_tensor(uniforms) else torch.from_numpy(np.ascontiguousarray(uniforms, np.float32)).to(DEV)
+    rem = None if remaining is None else i32(remaining)
+    sv.spec_verify_sample_logits(zp_dev, zq_dev, d, u, out["accept_len"], out["emit_count"],
+                                 out["out_tokens"], w, temperature=T, top_k=top_k, top_p=top_p,
+                                 eos_id=eos_id, remaining=rem, emit_offsets=out["emit_offsets"],
+                                 final_mass=out["final_mass"], status=out["status"])
+    return out

@@ -59,6 +59,11 @@ def test_workspace_queries():
     b = sv.spec_verify_sample_workspace_bytes(8, 4, 151936)
     assert b > 8 * 8 and b % 256 == 0
     assert sv.spec_verify_sample_workspace_bytes(8, 4, 1 << 30) == 0   # too many chunks
+    c = sv.spec_process_workspace_bytes(72)
+    assert c >= 72 * 16 and c % 256 == 0 and sv.spec_process_workspace_bytes(0) == 0
+    d = sv.spec_verify_sample_logits_workspace_bytes(8, 4, 151936)
+    assert d > b and d % 256 == 0
+    assert sv.spec_verify_sample_logits_workspace_bytes(8, 4, sv.SPEC_PROC_MAX_V + 1) == 0
 
 
 # fake, never-dereferenced device addresses: validation fails before any use
@@ -94,6 +99,68 @@ def test_greedy_argument_errors(args, code):
 ])
 def test_sample_argument_errors(args, code):
     assert LIB.spec_verify_sample(*args) == code
+
+
+PROC_OK = (A, 1, 4, 1000, 0.7, 50, 0.9, B_, C_, D_, E_, WS, 1 << 20, N)
+
+
+def _proc(**kw):
+    names = ["logits", "dt", "R", "V", "T", "top_k", "top_p", "probs", "row_max", "row_thr",
+             "row_mass", "ws", "ws_bytes", "stream"]
+    a = dict(zip(names, PROC_OK))
+    a.update(kw)
+    return tuple(a[n] for n in names)
+
+
+@needs_lib
+@pytest.mark.parametrize("args,code", [
+    (_proc(logits=N), sv.SPEC_EINVAL),
+    (_proc(R=0), sv.SPEC_EINVAL),
+    (_proc(V=0), sv.SPEC_EINVAL),
+    (_proc(V=sv.SPEC_PROC_MAX_V + 1), sv.SPEC_EINVAL),
+    (_proc(T=0.0), sv.SPEC_EINVAL),
+    (_proc(T=-1.0), sv.SPEC_EINVAL),
+    (_proc(T=float("inf")), sv.SPEC_EINVAL),
+    (_proc(T=float("nan")), sv.SPEC_EINVAL),
+    (_proc(top_k=-1), sv.SPEC_EINVAL),
+    (_proc(top_p=0.0), sv.SPEC_EINVAL),
+    (_proc(top_p=1.5), sv.SPEC_EINVAL),
+    (_proc(dt=5), sv.SPEC_EINVAL),
+    (_proc(logits=ctypes.c_void_p(0x10001)), sv.SPEC_EINVAL),        # misaligned bf16
+    (_proc(ws_bytes=8), sv.SPEC_EWORKSPACE),
+    (_proc(probs=ctypes.c_void_p(0x10000 + 64)), sv.SPEC_EINVAL),    # probs overlap logits
+    (_proc(row_max=C_, row_thr=C_), sv.SPEC_EINVAL),                  # outputs alias
+])
+def test_process_argument_errors(args, code):
+    assert LIB.spec_process_logits(*args) == code
+
+
+VSL_OK = (A, B_, 1, 2, 4, 1000, 0.7, 0, 1.0, C_, D_, -1, N, E_, F_, G_, N, N, N, WS, 1 << 24, N)
+
+
+def _vsl(**kw):
+    names = ["zp", "zq", "dt", "B", "k", "V", "T", "top_k", "top_p", "draft", "u", "eos", "rem",
+             "acc", "emit", "toks", "offs", "mass", "status", "ws", "ws_bytes", "stream"]
+    a = dict(zip(names, VSL_OK))
+    a.update(kw)
+    return tuple(a[n] for n in names)
+
+
+@needs_lib
+@pytest.mark.parametrize("args,code", [
+    (_vsl(zp=N), sv.SPEC_EINVAL),
+    (_vsl(zq=N), sv.SPEC_EINVAL),
+    (_vsl(B=0), sv.SPEC_EINVAL),
+    (_vsl(k=0), sv.SPEC_EINVAL),
+    (_vsl(k=200), sv.SPEC_ECAPACITY),
+    (_vsl(T=0.0), sv.SPEC_EINVAL),
+    (_vsl(top_p=0.0), sv.SPEC_EINVAL),
+    (_vsl(V=sv.SPEC_PROC_MAX_V + 1), sv.SPEC_EINVAL),
+    (_vsl(ws_bytes=64), sv.SPEC_EWORKSPACE),
+    (_vsl(emit=E_), sv.SPEC_EINVAL),                                 # outputs alias
+])
+def test_sample_logits_argument_errors(args, code):
+    assert LIB.spec_verify_sample_logits(*args) == code
 
 
 @needs_lib

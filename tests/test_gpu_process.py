@@ -1,0 +1,242 @@
+"""GPU parity of the processed-distribution calls (temperature, top-k, top-p)
+against the oracle.
+
+Tolerances (from the arithmetic stated in include/spec_verify.h): the GPU
+weights are float32 (expf of one IEEE division), the oracle's float64, so a
+kept probability agrees to a relative 2e-5 and a row's kept weight to 2e-5;
+the row maximum is exact; a kept set is exact except that a top-p boundary
+may move where the oracle, run with top_p -/+ 1e-5, brackets the GPU's
+threshold.  Verification decisions then follow the rules of the stochastic
+parity tests with the same relative allowance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle.process import process_row
+from tests._gpu import DEV, _WS, host, logits_to_device, note, process, requires_gpu, verify_sample_logits
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+RTOL = 2e-5
+PTOL = 1e-5
+
+
+def _rows(rng, R, V, dtype, sd=3.0, ties=False):
+    z = (rng.standard_normal((R, V)) * sd).astype(np.float32)
+    if ties:
+        z = np.round(z * 2) / 2
+    if dtype == "bf16":
+        bits = W.bf16_bits_from_f32(z)
+        return bits, oracle.widen_bf16(bits)
+    return z, z
+
+
+def _check_rows(zw, got, T, K, P):
+    """zw: the oracle's view of the logits [R, V]; got: host outputs of process()."""
+    R, V = zw.shape
+    for r in range(R):
+        p, info = process_row(zw[r], T, K, P)
+        assert got["row_max"][r] == np.float32(info["zmax"]), r
+        thr_g = float(got["row_threshold"][r])
+        if thr_g != info["threshold"]:
+            assert P < 1.0, (r, thr_g, info["threshold"])
+            hi = process_row(zw[r], T, K, max(P - PTOL, 1e-6))[1]["threshold"]
+            lo = process_row(zw[r], T, K, min(P + PTOL, 1.0))[1]["threshold"]
+            assert lo <= thr_g <= hi, (r, thr_g, info["threshold"], lo, hi)
+            continue
+        g = got["probs"][r]
+        kept = info["kept"]
+        assert np.all(g[~kept] == 0.0), r
+        o = p.astype(np.float64)
+        assert np.all(np.abs(g[kept] - o[kept]) <= RTOL * o[kept] + 1e-37), r
+        if info["mass"] > 0:
+            assert abs(got["row_mass"][r] - info["mass"]) <= RTOL * info["mass"], r
+        else:
+            assert got["row_mass"][r] == 0.0
+
+
+CASES = [(1.0, 0, 1.0), (0.7, 0, 1.0), (0.7, 50, 1.0), (0.7, 0, 0.9), (0.7, 50, 0.9), (1.3, 1, 1.0),
+         (0.5, 0, 0.5), (2.0, 1000, 0.95), (0.05, 0, 0.99), (1.0, 3, 0.3)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 7, 1000, 4097, 32001])
+def test_process_rows_parity(dtype, V):
+    rng = np.random.default_rng(V + (7 if dtype == "bf16" else 0))
+    dev_in, zw = _rows(rng, 4, V, dtype)
+    zd = logits_to_device(dev_in, dtype)
+    for T, K, P in CASES:
+        note(f"process {dtype} V={V} T={T} K={K} P={P}")
+        got = host(process(zd, T, K, P))
+        _check_rows(zw, got, T, K, P)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_process_ties_and_special_rows(dtype):
+    rng = np.random.default_rng(11)
+    dev_in, zw = _rows(rng, 6, 3001, dtype, sd=2.0, ties=True)     # many exact ties
+    if dtype == "f32":
+        dev_in[2] = -np.inf                                         # a row without mass
+        dev_in[3, ::3] = -np.inf                                    # masked entries
+        zw = dev_in
+    else:
+        dev_in[2] = 0xFF80                                          # bf16 -inf
+        dev_in[3, ::3] = 0xFF80
+        zw = oracle.widen_bf16(dev_in)
+    zd = logits_to_device(dev_in, dtype)
+    for T, K, P in CASES + [(1.0, 3001, 1.0), (1.0, 5000, 0.5), (0.9, 2, 0.999)]:
+        note(f"process ties {dtype} T={T} K={K} P={P}")
+        got = host(process(zd, T, K, P))
+        _check_rows(zw, got, T, K, P)
+    got = host(process(zd, 1.0, 7, 0.5))
+    assert np.all(got["probs"][2] == 0.0) and got["row_mass"][2] == 0.0
+
+
+def test_process_misaligned_rows():
+    rng = np.random.default_rng(12)
+    V = 1001                                                        # odd: bf16 rows start misaligned
+    bits, zw = _rows(rng, 5, V, "bf16")
+    buf = torch.empty(bits.size + 1, dtype=torch.int16, device=DEV)
+    buf[1:].copy_(torch.from_numpy(bits.view(np.int16).reshape(-1)).to(DEV))
+    zd = buf[1:].view(torch.bfloat16).view(5, V)
+    note("process misaligned bf16")
+    _check_rows(zw, host(process(zd, 0.8, 20, 0.8)), 0.8, 20, 0.8)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,K,P", [(0.7, 50, 0.9), (0.7, 0, 0.9)])
+def test_process_workload_rows_full_size(dtype, T, K, P):
+    """Stochastic workload shapes: V = 151936, temperature 0.7."""
+    g = W.sample_logits(2)
+    z = g["zt"].reshape(-1, g["V"])[[0, 9, 17, 30]]
+    if dtype == "bf16":
+        bits = W.bf16_bits_from_f32(z)
+        dev_in, zw = bits, oracle.widen_bf16(bits)
+    else:
+        dev_in, zw = z, z
+    note(f"process workload rows {dtype} T={T} K={K} P={P}")
+    got = host(process(logits_to_device(dev_in, dtype), T, K, P))
+    _check_rows(zw, got, T, K, P)
+
+
+def _check_verify(p, q, d, u, got, ref, tol=RTOL):
+    """Verification outputs on processed rows p, q (the oracle's)."""
+    B, kp1, V = p.shape
+    k = kp1 - 1
+    exact = 0
+    for b in range(B):
+        mr, mg = int(ref["accept_len"][b]), int(got["accept_len"][b])
+        if mr != mg:
+            j = min(mr, mg)
+            x = int(d[b, j])
+            a = min(1.0, float(p[b, j, x]) / float(q[b, j, x])) if q[b, j, x] > 0 else float(p[b, j, x] > 0)
+            assert abs(float(u[b, j]) - a) <= 3 * tol * max(a, 1e-30), (b, j, u[b, j], a)
+            continue
+        assert got["emit_count"][b] == ref["emit_count"][b], b
+        assert got["status"][b] == ref["status"][b], b
+        e = int(ref["emit_count"][b])
+        assert np.array_equal(got["out_tokens"][b, :mr], ref["out_tokens"][b, :mr])
+        assert (got["out_tokens"][b, e:] == -1).all()
+        Sr, Sg = float(ref["final_mass"][b]), float(got["final_mass"][b])
+        if e == mr:
+            assert Sg == 0.0 and Sr == 0.0
+            exact += 1
+            continue
+        assert abs(Sg - Sr) <= 3 * tol * abs(Sr), (b, Sg, Sr)
+        vg, vr = int(got["out_tokens"][b, e - 1]), int(ref["out_tokens"][b, e - 1])
+        if vg == vr:
+            exact += 1
+            continue
+        row = np.maximum(p[b, mr] - q[b, mr], 0) if mr < k else p[b, k]
+        if mr < k and ref["status"][b] & oracle.ST_RESID_ZERO:
+            row = p[b, mr]
+        C = np.cumsum(row.astype(np.float64))
+        Tt = float(u[b, k]) * Sr
+        lo = C[vg - 1] if vg > 0 else 0.0
+        assert row[vg] > 0 and lo - 3 * tol * Sr <= Tt <= C[vg] + 3 * tol * Sr, (b, vg, vr)
+    return exact
+
+
+def _verify_case(zt, zd_, T, K, P, seed, dtype):
+    """Drafts are drawn from the oracle's q' (drafting is outside the step)."""
+    B, kp1, V = zt.shape
+    k = kp1 - 1
+    if dtype == "bf16":
+        bt, bd = W.bf16_bits_from_f32(zt), W.bf16_bits_from_f32(zd_)
+        zt_w, zd_w = oracle.widen_bf16(bt), oracle.widen_bf16(bd)
+        dev_t, dev_d = logits_to_device(bt, "bf16"), logits_to_device(bd, "bf16")
+    else:
+        zt_w, zd_w = zt, zd_
+        dev_t, dev_d = logits_to_device(zt, "f32"), logits_to_device(zd_, "f32")
+    p, _ = oracle.process_rows(zt_w, T, K, P)
+    q, _ = oracle.process_rows(zd_w, T, K, P)
+    rng = np.random.default_rng(seed)
+    d = W.draw_inverse_cdf(q, rng.random((B, k)))
+    u = rng.random((B, kp1), dtype=np.float32)
+    got = host(verify_sample_logits(dev_t, dev_d, d, u, T, K, P))
+    ref = oracle.sample_verify(p, q, d, u)
+    return _check_verify(p, q, d, u, got, ref), got, ref
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [5, 1000, 4097])
+def test_verify_from_logits_parity(dtype, V):
+    rng = np.random.default_rng(100 + V)
+    B, k = 24, 3
+    zt = (rng.standard_normal((B, k + 1, V)) * 2).astype(np.float32)
+    zd_ = (zt[:, :k] + rng.standard_normal((B, k, V)) * 0.7).astype(np.float32)
+    for T, K, P in [(1.0, 0, 1.0), (0.7, 20, 0.9), (1.5, 0, 0.8), (0.6, 3, 1.0)]:
+        note(f"verify logits {dtype} V={V} T={T} K={K} P={P}")
+        exact, got, ref = _verify_case(zt, zd_, T, K, P, V, dtype)
+        assert exact >= B - 1
+        assert got["emit_offsets"][-1] == got["emit_count"].sum()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_verify_from_logits_workload_full_size(dtype):
+    """Stochastic workload: B=8, k=4, V=151936, T=0.7, top-k 50, top-p 0.9."""
+    g = W.sample_logits(2)
+    note(f"verify logits workload {dtype}")
+    exact, got, ref = _verify_case(g["zt"], g["zd"], g["temperature"], 50, 0.9, 2, dtype)
+    assert exact >= 7
+
+
+def test_verify_from_logits_output_law():
+    """The emitted token follows p' (drafts weighted by q', stratified grids)."""
+    zt1 = np.log(np.array([0.5, 0.3, 0.15, 0.05])).astype(np.float32)
+    zd1 = np.log(np.array([0.1, 0.2, 0.3, 0.4])).astype(np.float32)
+    T, K, P = 0.8, 3, 0.95
+    p1, _ = process_row(zt1, T, K, P)
+    q1, _ = process_row(zd1, T, K, P)
+    N = 200
+    grid = np.array([(i + 0.5) / N for i in range(N)], np.float32)
+    xs = [x for x in range(4) if q1[x] > 0]
+    X, A, D = np.meshgrid(np.array(xs), grid, grid, indexing="ij")
+    d = X.reshape(-1, 1).astype(np.int32)
+    u = np.stack([A.reshape(-1), D.reshape(-1)], axis=1).astype(np.float32)
+    wts = q1[d[:, 0]].astype(np.float64) / (N * N)
+    B = d.shape[0]
+    zt = np.broadcast_to(zt1, (B, 2, 4)).copy()
+    zd_ = np.broadcast_to(zd1, (B, 1, 4)).copy()
+    note(f"verify logits output law B={B}")
+    got = host(verify_sample_logits(logits_to_device(zt, "f32"), logits_to_device(zd_, "f32"), d, u, T, K, P))
+    law = np.bincount(got["out_tokens"][:, 0], weights=wts, minlength=4)
+    assert np.allclose(law, p1, atol=2e-3)
+
+
+def test_verify_from_logits_repeatable():
+    g = W.sample_logits(2, round_=3, B=4)
+    zt = logits_to_device(g["zt"], "f32")
+    zd_ = logits_to_device(g["zd"], "f32")
+    rng = np.random.default_rng(3)
+    d = rng.integers(0, g["V"], size=(4, g["k"])).astype(np.int32)
+    note("verify logits repeatable")
+    first = host(verify_sample_logits(zt, zd_, d, g["uniforms"], 0.7, 40, 0.9, ws_key="vl"))
+    for it in range(6):
+        _WS["vl"].fill_(0x5A)
+        again = host(verify_sample_logits(zt, zd_, d, g["uniforms"], 0.7, 40, 0.9, ws_key="vl"))
+        for key in first:
+            assert np.array_equal(first[key], again[key]), key

@@ -19,6 +19,8 @@ from .configs import (  # noqa: F401
     planted_greedy,
     greedy_round,
     sample_round,
+    sample_logits,
+    draw_inverse_cdf,
     kv_geometry,
     prefix_tokens,
     pool_lengths,

@@ -151,6 +151,36 @@ def sample_round(c: int, round_: int = 0, batch: int = 0, B: int | None = None,
     return dict(p=p, q=q, drafts=drafts, uniforms=u, B=B, k=k, V=V)
 
 
+def sample_logits(c: int, round_: int = 0, batch: int = 0, B: int | None = None,
+                  V: int | None = None, k: int | None = None) -> dict:
+    """Raw logits of the stochastic workloads before any processing: target
+    logits z [B, k+1, V] and draft logits z[:, :k] + eps [B, k, V] (float32),
+    from the same streams as sample_round, plus its uniforms [B, k+1]."""
+    cfg = WORKLOADS[c]
+    B = cfg["B"] if B is None else B
+    k = cfg["k"] if k is None else k
+    V = cfg["V"] if V is None else V
+    z = stream(c, "logits", round_, batch).standard_normal((B, k + 1, V), dtype=np.float32)
+    z *= np.float32(cfg["z_sd"])
+    eps = stream(c, "eps", round_, batch).standard_normal((B, k, V), dtype=np.float32)
+    eps *= np.float32(cfg["eps_sd"])
+    zd = z[:, :k] + eps
+    u = stream(c, "uniforms", round_, batch).random((B, k + 1), dtype=np.float32)
+    return dict(zt=z, zd=zd, uniforms=u, B=B, k=k, V=V, temperature=cfg["temperature"])
+
+
+def draw_inverse_cdf(probs: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Ids drawn from the rows of probs [..., V] by inverse CDF with uniforms u [...]
+    (drafting, outside the step under test)."""
+    flat = probs.reshape(-1, probs.shape[-1]).astype(np.float64)
+    uf = np.asarray(u, np.float64).reshape(-1)
+    out = np.empty(flat.shape[0], np.int32)
+    for r in range(flat.shape[0]):
+        c = np.cumsum(flat[r])
+        out[r] = min(int(np.searchsorted(c, uf[r] * c[-1], side="right")), flat.shape[1] - 1)
+    return out.reshape(probs.shape[:-1])
+
+
 def kv_geometry(c: int, rounds: int = 1, B: int | None = None) -> dict:
     """Shape of the left-padded rectangle: n_b cached rows, end column E, capacity C.
 
