@@ -150,12 +150,12 @@ int spec_verify_sample(const float *p, const float *q, const int32_t *draft,
  *         top_p times their total weight (ties at the boundary are kept);
  *   p'(v) = w(v) / (sum of the kept w), 0 for dropped entries and for rows
  *         with no weight.
- * Arithmetic: w in float32 (expf of one IEEE float32 division of z - max z
- * by T), sums in float64 in a fixed order (results are reproducible run to
- * run); the top-p comparison uses the weights rounded to 2^-44 units.  Against
- * a float64 evaluation, p' agrees to a relative 1e-5 (the error of a weight
- * grows with |z - max z| / T), and a top-p boundary can differ only where the
- * weight above it is within about V * 2^-45 of top_p times the total.
+ * Arithmetic: w in float32, the hardware exp2 of (z - max z) * (1/T) * log2(e);
+ * sums and the top-p comparison use the weights truncated to 2^-40 units and
+ * added exactly, so results are reproducible run to run.  Against a float64
+ * evaluation, p' agrees to a relative 2e-5 (the error of a weight grows with
+ * |z - max z| / T), and a top-p boundary can differ only where the weight
+ * above it is within about V * 2^-40 of top_p times the total.
  * Logits must be finite or -inf.
  *
  * spec_process_logits -- processes R rows:

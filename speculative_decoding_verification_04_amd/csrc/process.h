@@ -12,9 +12,10 @@
 //   * top-p keeps v (among the top-k survivors) when the weight of the kept
 //     entries with a strictly larger logit is below top_p times their total;
 //   * p'(v) = w(v) / (kept weight); 0 when dropped.
-// Weights are float32 (expf), sums float64 in a fixed order, so results are
-// reproducible run to run and agree with a float64 evaluation to a relative
-// 1e-5 or better (the error of a weight grows with |z - max z| / T).
+// Weights are float32 (hardware exp2); sums are exact integer sums of the
+// weights truncated to 2^-40, so results are reproducible run to run and agree
+// with a float64 evaluation to a relative 2e-5 or better for weights above
+// 1e-30 (the error of a weight grows with |z - max z| / T).
 // Both truncations keep every logit at or above a threshold, so a row is
 // described by three numbers: its maximum, the threshold (as an order key of
 // float32 values) and the kept weight.
@@ -27,18 +28,18 @@ namespace specv {
 struct ProcStats {
   float zmax;       // largest logit of the row (-inf when every logit is -inf)
   uint32_t theta;   // entry v is kept iff f32_order_key(z(v)) >= theta
-  double mass;      // kept weight, float64 sum of the float32 weights; 0: no mass
+  double mass;      // kept weight: exact sum of the weights in 2^-40 units; 0: no mass
   float inv_mass;   // 1 / mass rounded to float32 (0 when the row has no mass)
   float zmin_kept;  // smallest kept logit
 };
 
 int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int V, bool bf16,
-                      float T, int top_k, float top_p, ProcStats *stats, float *probs,
+                      float invT, int top_k, float top_p, ProcStats *stats, float *probs,
                       hipStream_t s);
 bool proc_args_ok(float T, int top_k, float top_p, int V);
 
 struct ProcConfig {
-  float T;          // temperature > 0
+  float invT;       // 1 / temperature (IEEE float32)
   int top_k;        // 0 = off
   float top_p;      // >= 1 = off
 };
@@ -52,17 +53,29 @@ __device__ inline float logit_at(const void *row, int v) {
   }
 }
 
-// Weight exp((z - zmax) / T) in float32: one rounded subtraction (exact for
-// bf16 logits of ordinary range), one IEEE division and expf.
-__device__ inline float proc_weight(float z, float zmax, float T) {
+// Weight exp((z - zmax) / T) in float32: (z - zmax) (exact for bf16 logits
+// of ordinary range) times 1/T, then the hardware exp2 of that times log2(e).
+// Relative error about 2e-7 * |z - zmax| / T.
+__device__ inline float proc_weight(float z, float zmax, float invT) {
   if (z == -INFINITY) return 0.0f;
-  return expf(__fdiv_rn(z - zmax, T));
+  return __expf((z - zmax) * invT);
+}
+
+// A weight in [0, 1] as an integer number of 2^-40 units (truncated), from
+// its float32 bits: mantissa shifted by (exponent - 110).
+__device__ inline unsigned long long fixed_weight(float w) {
+  const uint32_t b = __float_as_uint(w);
+  const int e = static_cast<int>(b >> 23) & 0xFF;
+  const unsigned long long m = (b & 0x7FFFFFu) | 0x800000u;
+  const int sh = e - 110;
+  if (e == 0 || sh <= -24) return 0ull;      // zero, subnormal, or below one unit
+  return sh >= 0 ? (m << sh) : (m >> (-sh));
 }
 
 // Processed probability of one entry of a row with statistics s.
-__device__ inline float proc_prob(float z, const ProcStats &s, float T) {
+__device__ inline float proc_prob(float z, const ProcStats &s, float invT) {
   if (!(s.mass > 0.0) || f32_order_key(z) < s.theta) return 0.0f;
-  return proc_weight(z, s.zmax, T) * s.inv_mass;
+  return proc_weight(z, s.zmax, invT) * s.inv_mass;
 }
 
 }  // namespace specv

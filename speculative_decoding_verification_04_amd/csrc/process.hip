@@ -4,20 +4,26 @@
 // Definitions: process.h (after the zero-to-sglang walkthrough 5.1, which
 // requires the processed probabilities to be the ones verified).
 //
-// Design.  One 1024-lane workgroup per row; the row is read once from HBM and
-// then re-read from L2 by the later passes (a 151936-entry bf16 row is 297 KB,
-// a few rows per XCD fit its 4 MB L2):
-//   1. row maximum;
-//   2. top-k: radix selection of the K-th largest order key, 8 bits per pass
-//      (2 passes for bf16, whose keys carry 16 significant bits; 4 for f32),
-//      with a 256-bin count histogram in LDS;
-//   3. top-p: the same descent over the top-k survivors with a 256-bin
-//      histogram of counts and of fixed-point weights (2^-44 units, integer
-//      LDS atomics, so the selection is reproducible): at each level the
-//      lowest bucket whose top value still has less than top_p of the total
-//      weight above it holds the boundary value;
-//   4. the kept weight as a float64 sum in a fixed order, and, if asked, p'
-//      written for every entry.
+// Design.  One 1024-lane workgroup per row.
+//   1. One pass over the row takes its maximum and, with top-k, a histogram of
+//      the top 8 bits of the order keys.  Without top-k but with top-p, a
+//      second pass takes the same histogram of counts and fixed-point weights
+//      (2^-40 units, truncated).  The bucket holding the K-th largest key (or the top-p
+//      boundary) is read off the histogram.
+//   2. Every logit in that bucket or above is copied into LDS (it fits when at
+//      most 32768 logits qualify, which covers top-k up to that size and any
+//      top-p boundary whose bucket and everything above hold that few); the
+//      remaining radix levels (8 bits each: 2 in all for bf16 keys, 4 for f32)
+//      and the kept weight then run on that list.  Otherwise they re-read the
+//      row (from L2).
+//   3. The kept weight is an exact integer sum of the fixed-point weights, so
+//      the result does not depend on the order logits are visited in.
+// Whole-row histograms are kept per lane index: bucket b, column l (256 x 64
+// packed 64-bit words, 128 KB of LDS), so the 64 lanes of an atomic add hit 64
+// different words.  Logits cluster in a few buckets of the top digit; one
+// shared histogram serialised those adds.  A word packs a count (top 10 bits)
+// and a weight (low 54 bits); columns are summed per bucket afterwards.  The
+// bucket scans are parallel suffix sums.
 // Every selection keeps all logits at or above one threshold, so ties at a
 // boundary are kept, as the definitions require.
 #include "process.h"
@@ -28,7 +34,9 @@ namespace {
 constexpr int kProcThreads = 1024;
 constexpr int kProcWaves = kProcThreads / kWave;
 constexpr int kProcU = 4;                      // 16-byte loads in flight per lane
-constexpr double kFixScale = 17592186044416.0;  // 2^44 fixed-point units per unit weight
+constexpr double kFixScale = 1099511627776.0;  // 2^40 fixed-point units per unit weight
+constexpr int kCntShift = 54;                   // packed histogram word: count << 54 | weight
+constexpr unsigned long long kMassMask = (1ull << kCntShift) - 1;
 
 struct ProcParams {
   const void *za, *zb;   // rows [0, rows_a) come from za, the rest from zb
@@ -46,11 +54,13 @@ __device__ inline const void *proc_row(const ProcParams &P, int r) {
 }
 
 // Calls f(v, z) for every entry of the row this lane owns: a scalar head up to
-// the first 16-byte boundary, 16-byte vectors (kProcU in flight per lane),
-// a scalar tail.  The order within a lane is fixed, so sums are reproducible.
+// the first 16-byte boundary, 16-byte vectors (kProcU per lane per step, the
+// next step's loads issued before this step's entries are visited), a scalar
+// tail.  The order within a lane is fixed.
 template <bool BF16, class F>
 __device__ inline void row_foreach(const void *row, int V, F &&f) {
   constexpr int ELT = BF16 ? 2 : 4, VEC = 16 / ELT;
+  constexpr int kStep = kProcThreads * kProcU;
   const int t = threadIdx.x;
   const uintptr_t a = reinterpret_cast<uintptr_t>(row);
   const int head = min(V, static_cast<int>(((16u - (a & 15u)) & 15u) / ELT));
@@ -58,18 +68,26 @@ __device__ inline void row_foreach(const void *row, int V, F &&f) {
   const int tail0 = head + nvec * VEC;
   if (t < head) f(t, logit_at<BF16>(row, t));
   const uint4 *body = reinterpret_cast<const uint4 *>(static_cast<const unsigned char *>(row) + head * ELT);
-  for (int i0 = 0; i0 < nvec; i0 += kProcThreads * kProcU) {
-    uint4 x[kProcU];
+  uint4 cur[kProcU], nxt[kProcU];
 #pragma unroll
-    for (int u = 0; u < kProcU; ++u) {
-      const int i = i0 + u * kProcThreads + t;
-      if (i < nvec) x[u] = body[i];
+  for (int u = 0; u < kProcU; ++u) {
+    const int i = u * kProcThreads + t;
+    if (i < nvec) cur[u] = body[i];
+  }
+  for (int i0 = 0; i0 < nvec; i0 += kStep) {
+    const bool more = i0 + kStep < nvec;
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < kProcU; ++u) {
+        const int i = i0 + kStep + u * kProcThreads + t;
+        if (i < nvec) nxt[u] = body[i];
+      }
     }
 #pragma unroll
     for (int u = 0; u < kProcU; ++u) {
       const int i = i0 + u * kProcThreads + t;
       if (i < nvec) {
-        const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+        const uint32_t w[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
         const int v0 = head + i * VEC;
         if constexpr (BF16) {
 #pragma unroll
@@ -83,6 +101,8 @@ __device__ inline void row_foreach(const void *row, int V, F &&f) {
         }
       }
     }
+#pragma unroll
+    for (int u = 0; u < kProcU; ++u) cur[u] = nxt[u];
   }
   if (t < V - tail0) f(tail0 + t, logit_at<BF16>(row, tail0 + t));
 }
@@ -111,129 +131,292 @@ __device__ inline double block_sum_dd(double v, double *sh) {
   return s;
 }
 
+// Sums the 64 columns of every bucket of the per-lane histogram into
+// h_cnt / h_mass.  Contains barriers.
+__device__ inline void fold_columns(const unsigned long long *lh, uint32_t *h_cnt,
+                                   unsigned long long *h_mass) {
+  const int t = threadIdx.x;
+  const int b = t >> 2, part = t & 3;          // 4 lanes per bucket, 16 columns each
+  unsigned long long c = 0, m = 0;
+#pragma unroll
+  for (int i = 0; i < kWave / 4; ++i) {
+    const unsigned long long x = lh[b * kWave + part * (kWave / 4) + i];
+    c += x >> kCntShift;
+    m += x & kMassMask;
+  }
+#pragma unroll
+  for (int o = 1; o < 4; o <<= 1) {
+    c += __shfl_xor(c, o, kWave);
+    m += __shfl_xor(m, o, kWave);
+  }
+  if (part == 0) {
+    h_cnt[b] = static_cast<uint32_t>(c);
+    h_mass[b] = m;
+  }
+  __syncthreads();
+}
+
+__device__ inline unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ inline void clear_columns(unsigned long long *lh) {
+  for (int i = threadIdx.x; i < 256 * kWave; i += kProcThreads) lh[i] = 0ull;
+}
+
+// Lanes t < 256 own bucket 255 - t (descending buckets in lane order).  Returns
+// for those lanes the sum of v over the buckets above their own (an exclusive
+// prefix in lane order).  Every lane of the block must call it (barriers).
+__device__ inline unsigned long long sum_above(unsigned long long v, unsigned long long *sh4) {
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+  const unsigned long long inc = wave_incl_scan(v);
+  if (lane == kWave - 1 && w < 4) sh4[w] = inc;
+  __syncthreads();
+  unsigned long long base = 0;
+  for (int i = 0; i < w && i < 4; ++i) base += sh4[i];
+  __syncthreads();
+  return base + inc - v;
+}
+
+// Largest value of x over the block (x >= -1), broadcast.  Barriers.
+__device__ inline int block_max_int(int x, int *sh) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  x = wave_max_i(x);
+  if (lane == 0) sh[w] = x;
+  __syncthreads();
+  int r = sh[0];
+  for (int i = 1; i < kProcWaves; ++i) r = max(r, sh[i]);
+  __syncthreads();
+  return r;
+}
+
+constexpr int kCandCap = 256 * kWave * 2;        // candidate logits that fit in the histogram's LDS
+
 template <bool BF16>
 __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) {
+  // per-lane histogram columns (128 KB); reused as the candidate list
+  __shared__ unsigned long long lh[256 * kWave];
   __shared__ uint32_t h_cnt[256];
   __shared__ unsigned long long h_mass[256];
   __shared__ float sh_f[kProcWaves];
-  __shared__ double sh_d[kProcWaves];
   __shared__ uint32_t sh_prefix;
-  __shared__ int sh_need;
-  __shared__ unsigned long long sh_above;
-  __shared__ double sh_thr;
+  __shared__ int sh_need, sh_ncand, sh_n;
+  __shared__ unsigned long long sh_above, sh_tot;
+  __shared__ unsigned long long sh4[4];
+  __shared__ int sh_i[kProcWaves];
+  __shared__ unsigned long long sh_u[kProcWaves];
 
+  static_assert(kProcThreads == 4 * 256, "fold_columns assigns 4 lanes per bucket");
   const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
   const int r = blockIdx.x;
   const int V = P.V;
   const void *row = proc_row<BF16>(P, r);
   constexpr int kLevels = BF16 ? 2 : 4;        // 8-bit digits of the significant key bits
-  const float T = P.cfg.T;
-
-  // 1. row maximum
-  float m = -INFINITY;
-  row_foreach<BF16>(row, V, [&](int, float z) { m = fmaxf(m, z); });
-  const float zmax = block_max_f(m, sh_f);
-
-  // 2. top-k: the K-th largest key, one 8-bit digit per pass
-  uint32_t tau = 0;
+  const float invT = P.cfg.invT;
   const int K = P.cfg.top_k;
-  if (K > 0 && K < V) {
-    uint32_t prefix = 0, pmask = 0;
-    int need = K;
-    for (int lvl = 0; lvl < kLevels; ++lvl) {
-      const int shift = 24 - 8 * lvl;
-      for (int i = t; i < 256; i += kProcThreads) h_cnt[i] = 0;
+  const bool topk = K > 0 && K < V;
+  const bool topp = P.cfg.top_p < 1.0f;
+  const unsigned long long one = 1ull << kCntShift;
+  float *cand = reinterpret_cast<float *>(lh);
+
+  // ---- pass 1 over the row: maximum, and the first top-k digit histogram
+  clear_columns(lh);
+  __syncthreads();
+  float m = -INFINITY;
+  row_foreach<BF16>(row, V, [&](int, float z) {
+    m = fmaxf(m, z);
+    if (topk) atomicAdd(&lh[(f32_order_key(z) >> 24) * kWave + lane], one);
+  });
+  const float zmax = block_max_f(m, sh_f);     // (contains barriers)
+  const bool topp_on = topp && zmax != -INFINITY;
+
+  // Selection state.  Level-0 digits are chosen from whole-row histograms;
+  // everything at or above the chosen level-0 bucket is then copied into LDS
+  // (when it fits) and the remaining levels run on that list.
+  uint32_t kprefix = 0, kmask = 0;   // top-k descent
+  int need = K;
+  uint32_t pprefix = 0, pmask = 0;   // top-p descent
+  unsigned long long above = 0;
+  double thr = 0.0;
+  bool p_started = false, p_dead = false;
+
+  // Picks the top-k bucket at `shift` from h_cnt; returns the count of keys
+  // in the chosen bucket and above.  Barriers.
+  auto select_k = [&](int shift) -> int {
+    const int tb = 255 - t;
+    const unsigned long long c = t < 256 ? h_cnt[tb] : 0ull;
+    const unsigned long long S = sum_above(c, sh4);
+    if (t < 256 && S < static_cast<unsigned long long>(need) && static_cast<unsigned long long>(need) <= S + c) {
+      sh_need = need - static_cast<int>(S);
+      sh_prefix = kprefix | (static_cast<uint32_t>(tb) << shift);
+      sh_ncand = static_cast<int>(S + c);
+    }
+    __syncthreads();
+    need = sh_need;
+    kprefix = sh_prefix;
+    kmask |= 255u << shift;
+    const int n = sh_ncand;
+    __syncthreads();
+    return n;
+  };
+  // Picks the top-p bucket at `shift` from h_cnt / h_mass (level 0 also fixes
+  // the threshold top_p * total); returns the count in the bucket and above.
+  auto select_p = [&](int shift, bool first) -> int {
+    const int tb = 255 - t;
+    const unsigned long long mw = t < 256 ? h_mass[tb] : 0ull;
+    const unsigned long long cw = t < 256 ? h_cnt[tb] : 0ull;
+    const unsigned long long S = sum_above(mw, sh4);
+    const unsigned long long SC = sum_above(cw, sh4);
+    if (first) {
+      if (t == 255) sh_tot = S + mw;
       __syncthreads();
-      row_foreach<BF16>(row, V, [&](int, float z) {
-        const uint32_t key = f32_order_key(z);
-        if ((key & pmask) == prefix) atomicAdd(&h_cnt[(key >> shift) & 255u], 1u);
-      });
-      __syncthreads();
-      if (t == 0) {
-        int above = 0, d = 255;
-        for (; d > 0; --d) {
-          if (above + static_cast<int>(h_cnt[d]) >= need) break;
-          above += static_cast<int>(h_cnt[d]);
-        }
-        sh_need = need - above;
-        sh_prefix = prefix | (static_cast<uint32_t>(d) << shift);
-      }
-      __syncthreads();
-      need = sh_need;
-      prefix = sh_prefix;
+      thr = static_cast<double>(P.cfg.top_p) * static_cast<double>(sh_tot);
+    }
+    const bool ok = t < 256 && cw > 0 && static_cast<double>(above + S) < thr;
+    const int win = block_max_int(ok ? t : -1, sh_i);   // largest lane = lowest bucket
+    if (win < 0) {
+      if (t == 0) sh_prefix = 0xFFFFFFFFu;
+    } else if (t == win) {
+      sh_prefix = pprefix | (static_cast<uint32_t>(tb) << shift);
+      sh_above = above + S;
+      sh_ncand = static_cast<int>(SC + cw);
+    }
+    __syncthreads();
+    const uint32_t np = sh_prefix;
+    const int n = sh_ncand;
+    if (np == 0xFFFFFFFFu) {
+      p_dead = true;                              // no weight at all: keep the top-k set
+    } else {
+      pprefix = np;
+      above = sh_above;
       pmask |= 255u << shift;
     }
-    tau = prefix;   // the smallest key with the selected significant bits
+    __syncthreads();
+    return n;
+  };
+
+  int ncand = V;
+  uint32_t cutoff = 0;
+  if (topk) {
+    fold_columns(lh, h_cnt, h_mass);
+    ncand = select_k(24);
+    cutoff = kprefix;
+  } else if (topp_on) {
+    // pass 2 over the row: first top-p digit histogram (counts and weights)
+    clear_columns(lh);
+    __syncthreads();
+    row_foreach<BF16>(row, V, [&](int, float z) {
+      const uint32_t key = f32_order_key(z);
+      atomicAdd(&lh[(key >> 24) * kWave + lane], one + fixed_weight(proc_weight(z, zmax, invT)));
+    });
+    __syncthreads();
+    fold_columns(lh, h_cnt, h_mass);
+    ncand = select_p(24, true);
+    p_started = true;
+    if (!p_dead) cutoff = pprefix;
+  }
+  const bool listed = (topk || (topp_on && !p_dead)) && ncand <= kCandCap;
+  int n = 0;
+  if (listed) {
+    // pass over the row: copy every logit at or above the cutoff into LDS
+    if (t == 0) sh_n = 0;
+    __syncthreads();
+    row_foreach<BF16>(row, V, [&](int, float z) {
+      if (f32_order_key(z) >= cutoff) cand[atomicAdd(&sh_n, 1)] = z;
+    });
+    __syncthreads();
+    n = sh_n;
   }
 
-  // 3. top-p over the top-k survivors
-  uint32_t theta = tau;
-  if (P.cfg.top_p < 1.0f && zmax != -INFINITY) {
-    uint32_t prefix = 0, pmask = 0;
-    unsigned long long above = 0;
-    bool found = true;
-    for (int lvl = 0; lvl < kLevels; ++lvl) {
-      const int shift = 24 - 8 * lvl;
+  // Visits every logit that can still matter: the LDS list, or the row.
+  auto each = [&](auto &&f) {
+    if (listed) {
+      for (int i = t; i < n; i += kProcThreads) f(cand[i]);
+    } else {
+      row_foreach<BF16>(row, V, [&](int, float z) { f(z); });
+    }
+  };
+  // Histogram of digit (key >> shift) & 255 over the logits passing `pred`,
+  // with weights if asked, into h_cnt / h_mass.  Barriers.
+  auto histogram = [&](int shift, bool weights, auto &&pred) {
+    if (listed) {
       for (int i = t; i < 256; i += kProcThreads) {
         h_cnt[i] = 0;
         h_mass[i] = 0ull;
       }
       __syncthreads();
-      row_foreach<BF16>(row, V, [&](int, float z) {
+      each([&](float z) {
         const uint32_t key = f32_order_key(z);
-        if (key >= tau && (key & pmask) == prefix) {
+        if (pred(key)) {
           const uint32_t d = (key >> shift) & 255u;
           atomicAdd(&h_cnt[d], 1u);
-          const double wq = static_cast<double>(proc_weight(z, zmax, T)) * kFixScale;
-          atomicAdd(&h_mass[d], static_cast<unsigned long long>(__double2ull_rn(wq)));
+          if (weights) atomicAdd(&h_mass[d], fixed_weight(proc_weight(z, zmax, invT)));
         }
       });
       __syncthreads();
-      if (t == 0) {
-        if (lvl == 0) {
-          unsigned long long tot = 0;
-          for (int d = 0; d < 256; ++d) tot += h_mass[d];
-          sh_thr = static_cast<double>(P.cfg.top_p) * static_cast<double>(tot);
-        }
-        const double thr = sh_thr;
-        unsigned long long run = above, astar = above;
-        int dstar = -1;
-        for (int d = 255; d >= 0; --d) {       // buckets from the largest logits down
-          if (h_cnt[d] == 0) continue;
-          if (static_cast<double>(run) < thr) {
-            dstar = d;                           // this bucket's top value is kept
-            astar = run;
-          } else {
-            break;
-          }
-          run += h_mass[d];
-        }
-        sh_prefix = dstar < 0 ? 0xFFFFFFFFu : (prefix | (static_cast<uint32_t>(dstar) << shift));
-        sh_above = astar;
-      }
+    } else {
+      clear_columns(lh);
       __syncthreads();
-      if (sh_prefix == 0xFFFFFFFFu) {          // no weight at all: keep the top-k set
-        found = false;
-        break;
-      }
-      prefix = sh_prefix;
-      above = sh_above;
-      pmask |= 255u << shift;
+      each([&](float z) {
+        const uint32_t key = f32_order_key(z);
+        if (pred(key)) {
+          unsigned long long add = one;
+          if (weights) add += fixed_weight(proc_weight(z, zmax, invT));
+          atomicAdd(&lh[((key >> shift) & 255u) * kWave + lane], add);
+        }
+      });
+      __syncthreads();
+      fold_columns(lh, h_cnt, h_mass);
     }
-    if (found) theta = prefix;
+  };
+
+  // ---- top-k: remaining digits
+  uint32_t tau = 0;
+  if (topk) {
+    for (int lvl = 1; lvl < kLevels; ++lvl) {
+      const int shift = 24 - 8 * lvl;
+      const uint32_t pf = kprefix, pm = kmask;
+      histogram(shift, false, [&](uint32_t key) { return (key & pm) == pf; });
+      select_k(shift);
+    }
+    tau = kprefix;   // the smallest key with the selected significant bits
   }
 
-  // 4. kept weight (fixed order), smallest kept logit and, if asked, the
-  //    processed row
-  double acc = 0.0;
+  // ---- top-p over the top-k survivors
+  uint32_t theta = tau;
+  if (topp_on) {
+    for (int lvl = p_started ? 1 : 0; lvl < kLevels && !p_dead; ++lvl) {
+      const int shift = 24 - 8 * lvl;
+      const uint32_t pf = pprefix, pm = pmask, tk = tau;
+      histogram(shift, true, [&](uint32_t key) { return key >= tk && (key & pm) == pf; });
+      select_p(shift, lvl == 0);
+    }
+    if (!p_dead) theta = pprefix;
+  }
+
+  // ---- kept weight (exact integer sum of fixed-point weights, so any visiting
+  //      order gives the same bits) and the smallest kept logit
+  unsigned long long acc = 0;
   float zlo = INFINITY;
-  row_foreach<BF16>(row, V, [&](int, float z) {
+  each([&](float z) {
     if (f32_order_key(z) >= theta) {
-      acc += static_cast<double>(proc_weight(z, zmax, T));
+      acc += fixed_weight(proc_weight(z, zmax, invT));
       zlo = fminf(zlo, z);
     }
   });
-  const double mass = block_sum_dd(acc, sh_d);
+  {
+    acc = wave_sum_u64(acc);
+    if (lane == 0) sh_u[t / kWave] = acc;
+    __syncthreads();
+    unsigned long long tot = 0;
+    for (int i = 0; i < kProcWaves; ++i) tot += sh_u[i];
+    acc = tot;
+    __syncthreads();
+  }
+  const double mass = static_cast<double>(acc) / kFixScale;
   const float zmin_kept = -block_max_f(-zlo, sh_f);
   ProcStats st;
   st.zmax = zmax;
@@ -244,7 +427,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   if (t == 0) P.stats[r] = st;
   if (P.probs) {
     float *out = P.probs + static_cast<size_t>(r) * V;
-    row_foreach<BF16>(row, V, [&](int v, float z) { out[v] = proc_prob(z, st, T); });
+    row_foreach<BF16>(row, V, [&](int v, float z) { out[v] = proc_prob(z, st, invT); });
   }
 }
 
@@ -263,7 +446,7 @@ __global__ __launch_bounds__(256) void proc_export_kernel(const ProcStats *stats
 // Launches the statistics kernel over rows [0, rows); shared with the
 // stochastic verification from logits.
 int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int V, bool bf16,
-                      float T, int top_k, float top_p, ProcStats *stats, float *probs,
+                      float invT, int top_k, float top_p, ProcStats *stats, float *probs,
                       hipStream_t s) {
   ProcParams P;
   P.za = za;
@@ -271,7 +454,7 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
   P.rows_a = rows_a;
   P.rows = rows;
   P.V = V;
-  P.cfg.T = T;
+  P.cfg.invT = invT;
   P.cfg.top_k = top_k;
   P.cfg.top_p = top_p;
   P.stats = stats;
@@ -323,7 +506,8 @@ extern "C" int spec_process_logits(const void *logits, spec_dtype dt, int R, int
   hipStream_t s = static_cast<hipStream_t>(stream);
   ProcStats *stats = static_cast<ProcStats *>(ws);
   (void)hipGetLastError();
-  launch_proc_stats(logits, logits, R, R, V, dt == SPEC_BF16, temperature, top_k, top_p, stats, probs, s);
+  launch_proc_stats(logits, logits, R, R, V, dt == SPEC_BF16, 1.0f / temperature, top_k, top_p, stats,
+                    probs, s);
   if (row_max || row_threshold || row_mass)
     hipLaunchKernelGGL(proc_export_kernel, dim3((R + 255) / 256), dim3(256), 0, s, stats, R, row_max,
                        row_threshold, row_mass);

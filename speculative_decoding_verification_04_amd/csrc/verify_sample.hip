@@ -43,7 +43,7 @@ struct SampleParams {
   const float *p, *q;           // dense rows (spec_verify_sample)
   const void *zp, *zq;          // logits (spec_verify_sample_logits)
   const ProcStats *sp, *sq;     // statistics of the processed rows
-  float T;
+  float invT;                   // 1 / temperature
   const int32_t *draft;
   const float *u;
   int B, k, V, chunks;
@@ -83,11 +83,11 @@ struct LogitRow {
   static constexpr bool kDense = false;
   const void *a, *b;
   ProcStats sa, sb;
-  float T;
+  float invT;
   bool resid;
   __device__ inline float at(int v) const {
-    const float pa = proc_prob(logit_at<BF16>(a, v), sa, T);
-    return resid ? fmaxf(pa - proc_prob(logit_at<BF16>(b, v), sb, T), 0.0f) : pa;
+    const float pa = proc_prob(logit_at<BF16>(a, v), sa, invT);
+    return resid ? fmaxf(pa - proc_prob(logit_at<BF16>(b, v), sb, invT), 0.0f) : pa;
   }
 };
 
@@ -119,10 +119,10 @@ struct LogitSrc {
     return static_cast<const unsigned char *>(P.zq) + (static_cast<size_t>(b) * P.k + j) * P.V * kElt;
   }
   __device__ static inline float p_at(const SampleParams &P, int b, int j, int x) {
-    return proc_prob(logit_at<BF16>(prow(P, b, j), x), P.sp[static_cast<size_t>(b) * (P.k + 1) + j], P.T);
+    return proc_prob(logit_at<BF16>(prow(P, b, j), x), P.sp[static_cast<size_t>(b) * (P.k + 1) + j], P.invT);
   }
   __device__ static inline float q_at(const SampleParams &P, int b, int j, int x) {
-    return proc_prob(logit_at<BF16>(qrow(P, b, j), x), P.sq[static_cast<size_t>(b) * P.k + j], P.T);
+    return proc_prob(logit_at<BF16>(qrow(P, b, j), x), P.sq[static_cast<size_t>(b) * P.k + j], P.invT);
   }
   __device__ static inline LogitRow<BF16> row(const SampleParams &P, int b, int j, bool resid) {
     LogitRow<BF16> r;
@@ -130,7 +130,7 @@ struct LogitSrc {
     r.sa = P.sp[static_cast<size_t>(b) * (P.k + 1) + j];
     r.b = resid ? qrow(P, b, j) : nullptr;
     if (resid) r.sb = P.sq[static_cast<size_t>(b) * P.k + j];
-    r.T = P.T;
+    r.invT = P.invT;
     r.resid = resid;
     return r;
   }
@@ -454,7 +454,7 @@ extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t 
   P.q = q;
   P.zp = P.zq = nullptr;
   P.sp = P.sq = nullptr;
-  P.T = 1.0f;
+  P.invT = 1.0f;
   P.draft = draft;
   P.u = uniforms;
   P.B = B;
@@ -540,7 +540,7 @@ extern "C" int spec_verify_sample_logits(const void *target_logits, const void *
   P.zq = draft_logits;
   P.sp = stats;                                   // target rows first
   P.sq = stats + static_cast<size_t>(B) * (k + 1); // then the draft rows
-  P.T = temperature;
+  P.invT = 1.0f / temperature;
   P.draft = draft;
   P.u = uniforms;
   P.B = B;
@@ -561,7 +561,7 @@ extern "C" int spec_verify_sample_logits(const void *target_logits, const void *
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dt == SPEC_BF16;
   (void)hipGetLastError();
-  launch_proc_stats(target_logits, draft_logits, B * (k + 1), static_cast<int>(rows), V, bf16, temperature,
+  launch_proc_stats(target_logits, draft_logits, B * (k + 1), static_cast<int>(rows), V, bf16, P.invT,
                     top_k, top_p, stats, nullptr, s);
   const dim3 g1(static_cast<unsigned>(nblocks)), g2(static_cast<unsigned>(B) + 1u), blk(kThreads);
   if (bf16) {
