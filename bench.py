@@ -69,12 +69,19 @@ def _counter_rows(directory: str, counter: str):
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r.get("Counter_Name") == counter:
-                    rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
+                    rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"]), int(r.get("Grid_Size", 0))))
     return rows
 
 
-def _per_kernel(rows, key):
-    vals = [v for name, v in rows if key in name]
+def _per_kernel(rows, key, largest_grid=False):
+    """Mean counter value per dispatch of the kernels named like key.  With
+    largest_grid, only the dispatches of the largest grid: the step loop's
+    realign, not the smaller batch-scaling runs of the same kernel."""
+    sel = [(v, g) for name, v, g in rows if key in name]
+    if largest_grid and sel:
+        top = max(g for _, g in sel)
+        sel = [(v, g) for v, g in sel if g == top]
+    vals = [v for v, _ in sel]
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
 
@@ -82,8 +89,8 @@ def record_traffic(fetch_dir: str, write_dir: str) -> None:
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
     dispatch) of this benchmark into the committed traffic summary."""
     f_rows, w_rows = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
-    pf, _ = _per_kernel([r for r in f_rows if "neg" in r[0].lower()], "")
-    pw, _ = _per_kernel([r for r in w_rows if "neg" in r[0].lower()], "")
+    pf, _ = _per_kernel([r for r in f_rows if "neg" in r[0].lower()], "", largest_grid=True)
+    pw, _ = _per_kernel([r for r in w_rows if "neg" in r[0].lower()], "", largest_grid=True)
     out = {"probe": {"kernel": "torch int32 negation (one 4-byte read and one 4-byte write per element)",
                      "bytes_read": PROBE_BYTES, "bytes_written": PROBE_BYTES,
                      "fetch_kib": pf, "write_kib": pw,
@@ -91,8 +98,8 @@ def record_traffic(fetch_dir: str, write_dir: str) -> None:
                      "write_factor": (pw * 1024 / PROBE_BYTES) if pw else None},
            "kernels": {}, "sources_sha256": sources_digest()}
     for key in ("greedy_chunk_kernel", "greedy_commit_kernel", "realign_kernel"):
-        fk, nf = _per_kernel(f_rows, key)
-        wk, nw = _per_kernel(w_rows, key)
+        fk, nf = _per_kernel(f_rows, key, largest_grid=True)
+        wk, nw = _per_kernel(w_rows, key, largest_grid=True)
         out["kernels"][key] = {"fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
                                "dispatches": [nf, nw]}
     os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
@@ -229,6 +236,8 @@ def main() -> int:
 
     log("secondary: stochastic verify (given rows and from logits) and same-length grouping")
     secondary = secondary_measurements(dev, np, torch, sv, W)
+    log("batch scaling: realign cost and grouping rate against batch size")
+    secondary.update(batch_scaling(dev, np, torch, sv, W))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -350,6 +359,70 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
                                 "us_per_call": t * 1e6, "num_batches": int(nb.item()),
                                 "grouped_fraction": int(ng.item()) / N}
     return out
+
+
+def batch_scaling(dev, np, torch, sv, W) -> dict:
+    """How the commit's cost and the grouping rate move with batch size.
+
+    Realign: the bench workload's per-sequence geometry (prefixes 512-4096,
+    8 KV heads x 128 bf16) with 4 layers instead of 32 (bytes scale with the
+    layer count; the trend does not), 8 chained rounds per batch size with
+    synthetic emitted counts from the workload's acceptance law.  Grouping: a
+    pool of 256 with the grouped workload's drifted lengths, and a pool of 256
+    drawn from 4 lengths only (a near-identical-length subset).
+    """
+    c, Lr, R = 3, 4, 8
+    cfg = W.workload(c)
+    k, H, D = cfg["k"], cfg["H"], cfg["D"]
+    i32 = dict(dtype=torch.int32, device=dev)
+    rows = []
+    for B in (1, 2, 4, 8, 16, 32):
+        g = W.kv_geometry(c, rounds=R, B=B)
+        n, E, C = g["n"], g["E"], g["C"]
+        kv = torch.empty((Lr, 2, B, H, C, D), dtype=torch.bfloat16, device=dev)
+        W.fill_kv_torch(kv, E, n, torch.as_tensor(W.prefix_tokens(c, B, E + 1), device=dev), "bf16")
+        Eb = [torch.tensor([E], **i32), torch.empty(1, **i32)]
+        Nb = [torch.as_tensor(n, **i32), torch.empty(B, **i32)]
+        pos, mask = torch.empty(B, C, **i32), torch.empty(B, C, **i32)
+        moved = torch.zeros(R, dtype=torch.int64, device=dev)
+        es = [torch.as_tensor(W.accept_counts(c, r, B), **i32) for r in range(R)]
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for r in range(R):
+            sv.spec_commit_realign_kv(kv, k, Eb[r % 2], Nb[r % 2], es[r], Eb[(r + 1) % 2], Nb[(r + 1) % 2],
+                                      pos, mask, bytes_moved=moved[r:r + 1])
+        b_.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b_) * 1e-3 / R
+        mv = moved.cpu().numpy().astype(np.float64)
+        pad = float(np.mean([np.mean(e.max() - e) for e in (x.cpu().numpy() for x in es)]))
+        rows.append({"B": B, "bytes_moved_per_round": float(mv.mean()),
+                     "bytes_moved_per_sequence": float(mv.mean() / B),
+                     "padding_columns_per_sequence": pad, "ms_per_round": t * 1e3,
+                     "GBps": float(mv.mean()) / t / 1e9 if mv.mean() > 0 else 0.0})
+        del kv
+    torch.cuda.empty_cache()
+    P = W.pool_lengths()
+    same = W.stream(4, "pool", 99).choice(np.array([512, 513, 900, 1500]), size=P.size)
+    grouping = []
+    for B in (2, 4, 8, 16, 32):
+        out = {"B": B}
+        for name, lens in (("drifted_pool", P), ("four_lengths_pool", same)):
+            L = torch.as_tensor(lens, **i32)
+            N = L.numel()
+            perm, bs, bl = torch.empty(N, **i32), torch.empty(N + 1, **i32), torch.empty(N, **i32)
+            nb, ng = torch.empty(1, **i32), torch.empty(1, **i32)
+            for tag, mg in (("2", 2), ("B", B)):   # partial same-length batches allowed / full batches only
+                sv.spec_group_same_length(L, B, mg, perm, bs, bl, nb, ng)
+                out[f"{name}_min_group_{tag}"] = int(ng.item()) / N
+        grouping.append(out)
+    return {"realign_vs_batch": {"workload": f"bench geometry with {Lr} layers, {R} rounds per batch size",
+                                 "rows": rows,
+                                 # (k+1) - E[e], E[e] = (1 - a^(k+1)) / (1 - a) averaged over the workload's a_b
+                                 "padding_limit_columns": float((k + 1) - np.mean(
+                                     (1 - W.alphas(c) ** (k + 1)) / (1 - W.alphas(c))))},
+            "grouping_rate_vs_batch": grouping}
 
 
 def cpu_baseline(r0: dict, ref_verify: dict, g: dict, np) -> dict:

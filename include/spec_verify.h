@@ -234,6 +234,32 @@ int spec_commit_realign_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, 
                            int64_t *bytes_moved, int32_t *status, spec_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * Draft-cache re-sync.
+ * [Design] Standard Greedy Algorithm step 7 and "KV Cache Synchronization":
+ * after each step the draft model's cache must hold the accepted prefix,
+ * copying the accepted entries (rather than re-running the draft).  An
+ * autoregressive draft that proposed k tokens consumed the last confirmed token
+ * and d_1..d_{k-1}, so its forward wrote k slots at columns [E, E + k) of its
+ * own left-padded rectangle.  Sequence b keeps the first min(e_b, k) of them
+ * (after full acceptance the draft has no entry for d_k yet and stays one
+ * entry behind the target), and the rectangle is right-aligned to
+ * E' = E + max_b min(e_b, k), exactly as spec_commit_realign_kv does with
+ * min(e_b, k) kept slots:
+ *   n'_b = n_b + min(e_b, k); bytes_moved counts the sequences that shift.
+ *   kv          [L][2][B][H][C][D] draft cache (its own L, H, D), in place
+ *   emit_count  [B] the target verification's e_b, in [0, k + 1]
+ *   pos_ids, mask  [B, C] out or NULL (each may be NULL independently)
+ *   other arguments as in spec_commit_realign_kv; needs E + k <= C.
+ * Errors and status bits as spec_commit_realign_kv (SPEC_ST_CAPACITY when
+ * E + k > C).
+ * ------------------------------------------------------------------------ */
+int spec_resync_draft_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, int D, int k,
+                         const int32_t *end_col, const int32_t *kv_len_in,
+                         const int32_t *emit_count, int32_t *end_col_out, int32_t *kv_len_out,
+                         int32_t *pos_ids, int32_t *mask, int64_t *bytes_moved, int32_t *status,
+                         spec_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Same-length grouping of a window of ragged sequences.
  * [Forensics] 3.2 (EXSPEC: batches of identical-length sequences drawn from a
  * window larger than the batch size, with unpad-append-repad as the fallback).

@@ -93,3 +93,38 @@ def commit_realign(kv, E: int, n, e, k: int, C: int | None = None) -> dict:
 def moved_bytes(n_new, delta, col_bytes: int) -> int:
     """bytes_moved without touching the cache (for shapes too large to copy on the host)."""
     return int(sum(2 * int(n_new[b]) * col_bytes for b in range(len(n_new)) if delta[b] > 0))
+
+
+def resync_draft(kv, E: int, n, e, k: int, C: int | None = None) -> dict:
+    """Re-sync of the draft model's KV rectangle to the accepted prefix.
+
+    [Design] "KV Cache Synchronization" and step 7 of the Standard Greedy
+    Algorithm: after each step the draft cache must hold the accepted prefix,
+    copying the accepted entries rather than re-running the draft.  An
+    autoregressive draft that proposed d_1..d_k consumed the last confirmed
+    token and d_1..d_{k-1}, so its forward wrote k slots [E, E + k), one fewer
+    than the verify forward.  A sequence that emitted e tokens keeps the first
+    min(e, k) of them; after full acceptance (e = k + 1) the draft holds no KV
+    for d_k yet and is one entry behind the target.  Realignment is then the
+    unpad-append-repad of commit_realign with min(e, k) in place of e:
+    n'_b = n_b + min(e_b, k), E' = E + max_b min(e_b, k).
+    Preconditions: E + k <= C, n_b in [0, E], e_b in [0, k + 1].
+    """
+    if C is None:
+        C = kv.shape[4]
+    e = [int(x) for x in e]
+    n = [int(x) for x in n]
+    B = len(n)
+    status = np.zeros(B, np.int32)
+    if E < 0 or E + k > C:
+        status[:] = ST_CAPACITY
+    for b in range(B):
+        if n[b] < 0 or n[b] > E or e[b] < 0 or e[b] > k + 1:
+            status[b] |= ST_BAD_STATE
+    if status.any():
+        return dict(ok=False, status=status)
+    kept = [min(x, k) for x in e]
+    # the same repad with k - 1 in the role of k: k + 1 - 1 = k slots written
+    out = commit_realign(kv, E, n, kept, k - 1, C)
+    out["kept"] = np.array(kept, np.int64)
+    return out

@@ -43,23 +43,26 @@ class UnbatchedModel:
         for b in range(self.B):
             self.tokens[b].extend(int(x) for x in out_tokens[b][:int(emit_count[b])])
 
-    def check(self, kv, pos, mask, E: int, content) -> list:
+    def check(self, kv, pos, mask, E: int, content, lag=None) -> list:
         """List of violated invariants (empty when the state is correct).
 
         kv: element bits [L, 2, B, H, C, D]; content(b, pos, tok, plane, d)
-        returns element bits broadcast over its arguments.
+        returns element bits broadcast over its arguments.  lag[b] (default 0)
+        is how many more confirmed tokens this cache lacks beyond the last one
+        (a draft cache after full acceptance lacks one).  pos / mask may be
+        None to skip their checks.
         """
         L, _, B, H, C, D = kv.shape
         bad = []
         for b in range(B):
-            n = self.n(b)
+            n = self.n(b) - (0 if lag is None else int(lag[b]))
             want_mask = np.zeros(C, np.int32)
             want_mask[E - n:E] = 1
-            if not np.array_equal(mask[b], want_mask):
+            if mask is not None and not np.array_equal(mask[b], want_mask):
                 bad.append(f"I1 mask b={b}")
             want_pos = np.zeros(C, np.int32)
             want_pos[E - n:E] = np.arange(n, dtype=np.int32)
-            if not np.array_equal(pos[b], want_pos):
+            if pos is not None and not np.array_equal(pos[b], want_pos):
                 bad.append(f"contiguity pos b={b}")
             if n == 0:
                 continue

@@ -22,7 +22,7 @@ __all__ = [
     "SpecError", "spec_strerror", "spec_verify_greedy_workspace_bytes", "spec_verify_greedy",
     "spec_verify_sample_workspace_bytes", "spec_verify_sample", "spec_process_workspace_bytes",
     "spec_process_logits", "spec_verify_sample_logits_workspace_bytes", "spec_verify_sample_logits",
-    "spec_commit_realign_kv",
+    "spec_commit_realign_kv", "spec_resync_draft_kv",
     "spec_group_same_length", "workspace", "library",
 ]
 
@@ -159,6 +159,19 @@ def spec_commit_realign_kv(kv, k: int, end_col, kv_len_in, emit_count, end_col_o
         _ptr(emit_count), _ptr(end_col_out), _ptr(kv_len_out), _ptr(pos_ids), _ptr(mask),
         _ptr(bytes_moved), _ptr(status), _stream(stream))
     _check(code, "spec_commit_realign_kv")
+
+
+def spec_resync_draft_kv(kv, k: int, end_col, kv_len_in, emit_count, end_col_out, kv_len_out, *,
+                         pos_ids=None, mask=None, bytes_moved=None, status=None, stream=None) -> None:
+    """Draft cache kv [L, 2, B, H, C, D] (bf16/f32) keeps min(e_b, k) of its k forward slots."""
+    L, two, B, H, C, D = kv.shape
+    if two != 2:
+        raise ValueError("kv must be [L, 2, B, H, C, D]")
+    code = library().spec_resync_draft_kv(
+        _ptr(kv), _dtype_code(kv), L, B, H, C, D, int(k), _ptr(end_col), _ptr(kv_len_in),
+        _ptr(emit_count), _ptr(end_col_out), _ptr(kv_len_out), _ptr(pos_ids), _ptr(mask),
+        _ptr(bytes_moved), _ptr(status), _stream(stream))
+    _check(code, "spec_resync_draft_kv")
 
 
 def spec_group_same_length(lengths, B: int, min_group: int, perm, batch_start, batch_len,

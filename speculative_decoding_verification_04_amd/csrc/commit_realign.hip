@@ -46,6 +46,7 @@ constexpr int kReserveWords = 24 * 1024; // 96 KB of the CU's 160 KB LDS: one wo
 struct RealignParams {
   unsigned char *kv;
   int L, B, H, C, D, k, elt;
+  int slots;                   // forward slots written per sequence: k + 1 (target) or k (draft)
   int R;                       // bytes per column (D * elt)
   long long plane_bytes;       // C * R
   int num_planes;              // L * 2 * B * H
@@ -57,6 +58,10 @@ struct RealignParams {
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+// Forward slots sequence b keeps: its e_b emitted tokens' worth, at most the
+// slots the forward wrote.
+__device__ inline int kept_slots(const RealignParams &P, int b) { return min(P.emit_count[b], P.slots); }
 
 template <int VB>
 struct VecOf;
@@ -102,12 +107,12 @@ __device__ inline void stream_st(uint2 v, uint2 *p) {
 // Every workgroup computes the same values from the same inputs.
 __device__ inline void commit_state(const RealignParams &P, int *sh, int &E, int &M, bool &ok) {
   E = P.end_col[0];
-  int bad = (E < 0 || E > P.C - P.k - 1) ? 1 : 0;
+  int bad = (E < 0 || E > P.C - P.slots) ? 1 : 0;
   int m = 0;
   for (int b = threadIdx.x; b < P.B; b += blockDim.x) {
     const int n = P.kv_len_in[b], e = P.emit_count[b];
     if (n < 0 || n > E || e < 0 || e > P.k + 1) bad = 1;
-    m = max(m, e);
+    m = max(m, min(e, P.slots));
   }
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const int wb = wave_max_i(bad), wmx = wave_max_i(m);
@@ -130,7 +135,7 @@ __device__ inline void commit_state(const RealignParams &P, int *sh, int &E, int
 template <int VB>
 __device__ inline void move_plane(const RealignParams &P, int p, int b, int E, int M) {
   using VT = typename VecOf<VB>::T;
-  const int n = P.kv_len_in[b], e = P.emit_count[b];
+  const int n = P.kv_len_in[b], e = kept_slots(P, b);
   const int delta = M - e, len = n + e;
   if (delta == 0 || len == 0) return;   // uniform in the workgroup: no barrier is skipped unevenly
 
@@ -190,13 +195,13 @@ __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
     if (!ok) return;
     const int b = blk;
     const int En = E + M;
-    const int start = En - (P.kv_len_in[b] + P.emit_count[b]);
-    int32_t *pos = P.pos_ids + static_cast<size_t>(b) * P.C;
-    int32_t *msk = P.mask + static_cast<size_t>(b) * P.C;
+    const int start = En - (P.kv_len_in[b] + kept_slots(P, b));
+    int32_t *pos = P.pos_ids ? P.pos_ids + static_cast<size_t>(b) * P.C : nullptr;
+    int32_t *msk = P.mask ? P.mask + static_cast<size_t>(b) * P.C : nullptr;
     for (int c = t; c < P.C; c += kThreads) {
       const bool in = c >= start && c < En;
-      msk[c] = in ? 1 : 0;
-      pos[c] = in ? c - start : 0;
+      if (msk) msk[c] = in ? 1 : 0;
+      if (pos) pos[c] = in ? c - start : 0;
     }
     return;
   }
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
   // scalar outputs
   if (!ok) {
     if (P.status) {
-      const bool cap = E < 0 || E > P.C - P.k - 1;
+      const bool cap = E < 0 || E > P.C - P.slots;
       for (int b = t; b < P.B; b += kThreads) {
         const int n = P.kv_len_in[b], e = P.emit_count[b];
         int st = cap ? SPEC_ST_CAPACITY : 0;
@@ -221,10 +226,11 @@ __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
   }
   long long moved = 0;
   for (int b = t; b < P.B; b += kThreads) {
-    const int n1 = P.kv_len_in[b] + P.emit_count[b];
+    const int e = kept_slots(P, b);
+    const int n1 = P.kv_len_in[b] + e;
     P.kv_len_out[b] = n1;
     if (P.status) P.status[b] = 0;
-    if (P.emit_count[b] != M) moved += n1;
+    if (e != M) moved += n1;
   }
   const int lane = t & (kWave - 1), w = t / kWave;
 #pragma unroll
@@ -244,13 +250,11 @@ __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
 
 using namespace specv;
 
-extern "C" int spec_commit_realign_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, int D, int k,
-                                      const int32_t *end_col, const int32_t *kv_len_in,
-                                      const int32_t *emit_count, int32_t *end_col_out,
-                                      int32_t *kv_len_out, int32_t *pos_ids, int32_t *mask,
-                                      int64_t *bytes_moved, int32_t *status, spec_stream_t stream) {
-  if (!kv || !end_col || !kv_len_in || !emit_count || !end_col_out || !kv_len_out || !pos_ids || !mask)
-    return SPEC_EINVAL;
+static int realign_launch(void *kv, spec_dtype dt, int L, int B, int H, int C, int D, int k, int slots,
+                          const int32_t *end_col, const int32_t *kv_len_in, const int32_t *emit_count,
+                          int32_t *end_col_out, int32_t *kv_len_out, int32_t *pos_ids, int32_t *mask,
+                          int64_t *bytes_moved, int32_t *status, spec_stream_t stream) {
+  if (!kv || !end_col || !kv_len_in || !emit_count || !end_col_out || !kv_len_out) return SPEC_EINVAL;
   if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_EINVAL;
   if (L < 1 || B < 1 || H < 1 || C < 1 || D < 1 || k < 1) return SPEC_EINVAL;
   const int elt = dt == SPEC_BF16 ? 2 : 4;
@@ -280,6 +284,7 @@ extern "C" int spec_commit_realign_kv(void *kv, spec_dtype dt, int L, int B, int
   P.C = C;
   P.D = D;
   P.k = k;
+  P.slots = slots;
   P.elt = elt;
   P.R = static_cast<int>(R);
   P.plane_bytes = static_cast<long long>(C) * R;
@@ -305,4 +310,23 @@ extern "C" int spec_commit_realign_kv(void *kv, spec_dtype dt, int L, int B, int
   else
     hipLaunchKernelGGL(realign_kernel<2>, grid, block, 0, s, P);
   return launch_status();
+}
+
+extern "C" int spec_commit_realign_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, int D, int k,
+                                      const int32_t *end_col, const int32_t *kv_len_in,
+                                      const int32_t *emit_count, int32_t *end_col_out,
+                                      int32_t *kv_len_out, int32_t *pos_ids, int32_t *mask,
+                                      int64_t *bytes_moved, int32_t *status, spec_stream_t stream) {
+  if (!pos_ids || !mask) return SPEC_EINVAL;
+  return realign_launch(kv, dt, L, B, H, C, D, k, k + 1, end_col, kv_len_in, emit_count, end_col_out,
+                        kv_len_out, pos_ids, mask, bytes_moved, status, stream);
+}
+
+extern "C" int spec_resync_draft_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, int D, int k,
+                                    const int32_t *end_col, const int32_t *kv_len_in,
+                                    const int32_t *emit_count, int32_t *end_col_out,
+                                    int32_t *kv_len_out, int32_t *pos_ids, int32_t *mask,
+                                    int64_t *bytes_moved, int32_t *status, spec_stream_t stream) {
+  return realign_launch(kv, dt, L, B, H, C, D, k, k, end_col, kv_len_in, emit_count, end_col_out,
+                        kv_len_out, pos_ids, mask, bytes_moved, status, stream);
 }

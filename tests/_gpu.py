@@ -154,3 +154,21 @@ def verify_sample_logits(zp_dev, zq_dev, drafts, uniforms, T, top_k=0, top_p=1.0
                                  eos_id=eos_id, remaining=rem, emit_offsets=out["emit_offsets"],
                                  final_mass=out["final_mass"], status=out["status"])
     return out
+
+
+def resync(kv, k, E, kv_len, emit_count, pos_mask=True):
+    """Run spec_resync_draft_kv; pos/mask are passed only when pos_mask."""
+    L, _, B, H, C, D = kv.shape
+    end_col = E if torch.is_tensor(E) else torch.tensor([E], dtype=torch.int32, device=DEV)
+    n = kv_len if torch.is_tensor(kv_len) else i32(kv_len)
+    e = emit_count if torch.is_tensor(emit_count) else i32(emit_count)
+    out = dict(end_col=torch.empty(1, dtype=torch.int32, device=DEV),
+               kv_len=torch.empty(B, dtype=torch.int32, device=DEV),
+               bytes_moved=torch.empty(1, dtype=torch.int64, device=DEV),
+               status=torch.empty(B, dtype=torch.int32, device=DEV))
+    if pos_mask:
+        out["pos"] = torch.empty(B, C, dtype=torch.int32, device=DEV)
+        out["mask"] = torch.empty(B, C, dtype=torch.int32, device=DEV)
+    sv.spec_resync_draft_kv(kv, k, end_col, n, e, out["end_col"], out["kv_len"], pos_ids=out.get("pos"),
+                            mask=out.get("mask"), bytes_moved=out["bytes_moved"], status=out["status"])
+    return out

@@ -178,6 +178,18 @@ def test_commit_argument_errors(args, code):
 
 @needs_lib
 @pytest.mark.parametrize("args,code", [
+    ((N, 1, 2, 2, 2, 16, 8, 3, A, B_, C_, D_, E_, N, N, N, N, N), sv.SPEC_EINVAL),        # NULL kv
+    ((H_, 1, 2, 2, 2, 16, 8, 0, A, B_, C_, D_, E_, N, N, N, N, N), sv.SPEC_EINVAL),       # k < 1
+    ((H_, 1, 2, 2, 2, 16, 8, 3, A, B_, C_, N, E_, N, N, N, N, N), sv.SPEC_EINVAL),        # NULL E'
+    ((H_, 1, 2, 2, 2, 16, 8, 3, A, B_, C_, D_, B_, N, N, N, N, N), sv.SPEC_EINVAL),       # n' aliases n
+    ((H_, 9, 2, 2, 2, 16, 8, 3, A, B_, C_, D_, E_, N, N, N, N, N), sv.SPEC_EINVAL),       # dtype
+])
+def test_resync_argument_errors(args, code):
+    assert LIB.spec_resync_draft_kv(*args) == code
+
+
+@needs_lib
+@pytest.mark.parametrize("args,code", [
     ((N, 10, 8, 2, B_, C_, D_, E_, F_, N), sv.SPEC_EINVAL),
     ((A, -1, 8, 2, B_, C_, D_, E_, F_, N), sv.SPEC_EINVAL),
     ((A, 10, 0, 2, B_, C_, D_, E_, F_, N), sv.SPEC_EINVAL),

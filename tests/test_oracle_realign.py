@@ -169,3 +169,65 @@ def test_invalid_state_reports_status_only(E, n, e, C, bits):
     assert not res["ok"]
     assert res["status"].tolist() == bits
     assert "pos" not in res and "kv" not in res
+
+
+def _draft_round(st, alpha):
+    """One round on a draft cache: the draft forward writes k slots (the last
+    confirmed token and d_1..d_{k-1}); verification of the target decides e."""
+    model, kv, k, V = st["model"], st["kv"], st["k"], st["V"]
+    rng = st["rng"]
+    r = planted_greedy(rng, rng, model.B, k, V, 1.0, "f32", alpha)
+    slots = model.slot_tokens(r["drafts"])[:, :k]
+    write_forward_slots_np(kv, st["E"], model.n_all(), slots, st["dtype"])
+    ver = oracle.greedy_verify(r["logits"], "f32", r["drafts"])
+    return ver
+
+
+@pytest.mark.parametrize("alpha", [0.2, 0.9, 1.0])
+def test_draft_resync_keeps_the_accepted_prefix(alpha):
+    """[Design] KV Cache Synchronization: after re-sync the draft cache holds
+    the accepted prefix; after full acceptance it lacks only d_k (lag 1)."""
+    st = _state(B=6, k=4, rounds=2, seed=int(alpha * 10))
+    ver = _draft_round(st, alpha)
+    e = ver["emit_count"]
+    out = oracle.resync_draft(st["kv"], st["E"], st["model"].n_all(), e, st["k"])
+    assert out["ok"]
+    assert np.array_equal(out["kept"], np.minimum(e, st["k"]))
+    st["model"].commit(ver["out_tokens"], e)
+    lag = (e == st["k"] + 1).astype(np.int64)
+    if alpha == 1.0:
+        assert lag.all()
+    assert st["model"].check(out["kv"], out["pos"], out["mask"], out["E_new"], _content("bf16"), lag=lag) == []
+
+
+def test_draft_resync_equals_target_commit_when_no_sequence_accepts_all():
+    st = _state(B=5, k=3, rounds=2, seed=3)
+    _draft_round(st, 0.5)
+    e = np.array([1, 3, 2, 3, 1])                       # every e <= k
+    a = oracle.resync_draft(st["kv"], st["E"], st["model"].n_all(), e, st["k"])
+    b = oracle.commit_realign(st["kv"], st["E"], st["model"].n_all(), e, st["k"])
+    for key in ["kv", "pos", "mask", "E_new", "kv_len", "bytes_moved"]:
+        assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), key
+
+
+def test_negative_control_draft_keeps_an_unwritten_slot():
+    """Keeping k + 1 draft slots after full acceptance keeps a column the draft
+    never wrote; the invariant check catches it."""
+    st = _state(B=4, k=3, rounds=2, seed=5)
+    ver = _draft_round(st, 1.0)
+    e = ver["emit_count"]
+    wrong = oracle.commit_realign(st["kv"], st["E"], st["model"].n_all(), e, st["k"])
+    st["model"].commit(ver["out_tokens"], e)
+    assert st["model"].check(wrong["kv"], None, None, wrong["E_new"], _content("bf16"))
+
+
+def test_draft_resync_capacity_and_bad_state():
+    st = _state(B=3, k=3, rounds=1, seed=6)
+    n = st["model"].n_all()
+    C = st["E"] + st["k"]                              # room for exactly k draft slots
+    ok = oracle.resync_draft(st["kv"][:, :, :, :, :C], st["E"], n, [1, 2, 3], st["k"])
+    assert ok["ok"]
+    bad = oracle.resync_draft(st["kv"][:, :, :, :, :C - 1], st["E"], n, [1, 2, 3], st["k"])
+    assert not bad["ok"] and (bad["status"] & oracle.ST_CAPACITY).all()
+    bad = oracle.resync_draft(st["kv"], st["E"], n, [1, 5, 3], st["k"])
+    assert not bad["ok"] and bad["status"][1] & oracle.ST_BAD_STATE

@@ -72,3 +72,16 @@ def test_kv_fill_numpy_torch_agree(dtype):
     assert np.array_equal(iv, a)
     vals = t.float().numpy()
     assert np.isfinite(vals).all() and (vals != 0).all()
+
+
+def test_accept_counts_follow_the_planted_law():
+    """Synthetic emitted counts: mean over rounds equals (1 - a^(k+1)) / (1 - a)."""
+    import workloads as W
+    k = W.workload(3)["k"]
+    a = W.alphas(3)
+    e = np.stack([W.accept_counts(3, r) for r in range(4000)])
+    assert e.min() >= 1 and e.max() <= k + 1
+    want = (1 - a ** (k + 1)) / (1 - a)
+    se = e.std(axis=0) / np.sqrt(e.shape[0])
+    assert np.all(np.abs(e.mean(axis=0) - want) < 5 * se + 1e-9)
+    assert np.array_equal(W.accept_counts(3, 7, B=5), W.accept_counts(3, 7)[:5])

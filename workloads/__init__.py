@@ -20,6 +20,7 @@ from .configs import (  # noqa: F401
     greedy_round,
     sample_round,
     sample_logits,
+    accept_counts,
     draw_inverse_cdf,
     kv_geometry,
     prefix_tokens,

@@ -181,6 +181,19 @@ def draw_inverse_cdf(probs: np.ndarray, u: np.ndarray) -> np.ndarray:
     return out.reshape(probs.shape[:-1])
 
 
+def accept_counts(c: int, round_: int, B: int | None = None) -> np.ndarray:
+    """Emitted counts e_b of one synthetic round (inputs for commit-only runs):
+    e_b - 1 is the number of leading successes among k iid trials of
+    probability alpha_b (the planted-draft law), so e_b is in 1..k+1."""
+    cfg = WORKLOADS[c]
+    B = cfg["B"] if B is None else B
+    k = cfg["k"]
+    a = alphas(c, B)
+    trials = stream(c, "accept", round_).random((B, k)) < a[:, None]
+    lead = np.argmin(np.concatenate([trials, np.zeros((B, 1), bool)], axis=1), axis=1)
+    return (lead + 1).astype(np.int32)
+
+
 def kv_geometry(c: int, rounds: int = 1, B: int | None = None) -> dict:
     """Shape of the left-padded rectangle: n_b cached rows, end column E, capacity C.
 
