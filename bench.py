@@ -299,7 +299,7 @@ def _time_calls(torch, fn, reps: int) -> float:
 
 
 def secondary_measurements(dev, np, torch, sv, W) -> dict:
-    """The other two steps at their workload shapes (not part of `value`)."""
+    """The other calls at their workload shapes (not part of `value`)."""
     out = {}
     r = W.sample_round(2)
     B, k, V = r["B"], r["k"], r["V"]
@@ -347,6 +347,21 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
                                    "us_per_call": t * 1e6, "rows_per_s": B * (k + 1) / t,
                                    "algorithmic_bytes": nbytes, "GBps": nbytes / t / 1e9,
                                    "frac_of_peak": nbytes / t / PEAK_HBM}
+    # paged layout: the commit is a rollback of lengths and pages, no KV bytes move
+    g3 = W.kv_geometry(3)
+    B3, k3, page = g3["B"], g3["k"], 16
+    n3 = torch.as_tensor(g3["n"], dtype=torch.int32, device=dev)
+    e3 = torch.as_tensor(W.accept_counts(3, 0), dtype=torch.int32, device=dev)
+    maxp = (int(g3["n"].max()) + k3 + 1 + page - 1) // page
+    bt = torch.arange(B3 * maxp, dtype=torch.int32, device=dev).view(B3, maxp)
+    per = (k3 + page) // page
+    kl, pk = torch.empty(B3, **i32), torch.empty(B3, **i32)
+    fr, fo = torch.empty(B3 * per, **i32), torch.empty(B3 + 1, **i32)
+    call = lambda: sv.spec_commit_paged(k3, page, n3, e3, bt, kl, pk, fr, fo)
+    t = _time_calls(torch, call, 52)
+    out["paged_commit"] = {"workload": f"paged rollback, B={B3} k={k3} page {page} rows, prefixes 512-4096",
+                           "us_per_call": t * 1e6, "pages_released": int(fo[-1].item()),
+                           "kv_bytes_moved": 0}
     P = W.pool_lengths()
     L = torch.as_tensor(P, dtype=torch.int32, device=dev)
     N = P.size

@@ -260,6 +260,35 @@ int spec_resync_draft_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, in
                          spec_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * Commit for a variable-length (paged) KV layout: rollback only.
+ * [Forensics] section 2 and App. F: variable-length layouts need no
+ * repadding, but rejected tokens must be rolled back in the position ids and
+ * the KV cache.  In a paged cache that moves no KV bytes.  Before the verify
+ * forward sequence b held n_b rows and the caller gave it pages for the k + 1
+ * forward slots, so its first a_b = ceil((n_b + k + 1) / page_size) block-table
+ * entries are in use.  It keeps n'_b = n_b + e_b rows (the last emitted token
+ * has no KV yet, App. D); its next input position is n'_b; the entries
+ * ceil(n'_b / page_size) .. a_b - 1 are released.
+ *   kv_len_in      [B] n_b            emit_count [B] e_b in [0, k + 1]
+ *   block_table    [B, max_pages] int32 page ids (row b lists b's pages in order)
+ *   kv_len_out     [B] out: n'_b (also the next input position)
+ *   pages_kept     [B] out: ceil(n'_b / page_size)
+ *   freed_pages    out, room for B * ceil((k + 1) / page_size) ids: the
+ *                  released entries, block-table order, sequences in order
+ *   freed_offsets  [B + 1] out: sequence b's released ids are
+ *                  freed_pages[freed_offsets[b] .. freed_offsets[b + 1])
+ *   status         [B] out or NULL: SPEC_ST_BAD_STATE (n_b < 0 or e_b outside
+ *                  [0, k + 1]) or SPEC_ST_CAPACITY (a_b > max_pages); such a
+ *                  sequence keeps n_b and releases nothing.
+ * Errors: SPEC_EINVAL for NULL required pointers, B, k, page_size or
+ * max_pages < 1, sizes that overflow int32, overlapping outputs.
+ * ------------------------------------------------------------------------ */
+int spec_commit_paged(int B, int k, int page_size, int max_pages, const int32_t *kv_len_in,
+                      const int32_t *emit_count, const int32_t *block_table, int32_t *kv_len_out,
+                      int32_t *pages_kept, int32_t *freed_pages, int32_t *freed_offsets,
+                      int32_t *status, spec_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Same-length grouping of a window of ragged sequences.
  * [Forensics] 3.2 (EXSPEC: batches of identical-length sequences drawn from a
  * window larger than the batch size, with unpad-append-repad as the fallback).

@@ -22,7 +22,7 @@ __all__ = [
     "SpecError", "spec_strerror", "spec_verify_greedy_workspace_bytes", "spec_verify_greedy",
     "spec_verify_sample_workspace_bytes", "spec_verify_sample", "spec_process_workspace_bytes",
     "spec_process_logits", "spec_verify_sample_logits_workspace_bytes", "spec_verify_sample_logits",
-    "spec_commit_realign_kv", "spec_resync_draft_kv",
+    "spec_commit_realign_kv", "spec_resync_draft_kv", "spec_commit_paged",
     "spec_group_same_length", "workspace", "library",
 ]
 
@@ -172,6 +172,17 @@ def spec_resync_draft_kv(kv, k: int, end_col, kv_len_in, emit_count, end_col_out
         _ptr(emit_count), _ptr(end_col_out), _ptr(kv_len_out), _ptr(pos_ids), _ptr(mask),
         _ptr(bytes_moved), _ptr(status), _stream(stream))
     _check(code, "spec_resync_draft_kv")
+
+
+def spec_commit_paged(k: int, page_size: int, kv_len_in, emit_count, block_table, kv_len_out,
+                      pages_kept, freed_pages, freed_offsets, *, status=None, stream=None) -> None:
+    """block_table [B, max_pages] int32; freed_pages holds B * ceil((k+1)/page_size) ids."""
+    B, max_pages = block_table.shape
+    code = library().spec_commit_paged(
+        B, int(k), int(page_size), max_pages, _ptr(kv_len_in), _ptr(emit_count), _ptr(block_table),
+        _ptr(kv_len_out), _ptr(pages_kept), _ptr(freed_pages), _ptr(freed_offsets), _ptr(status),
+        _stream(stream))
+    _check(code, "spec_commit_paged")
 
 
 def spec_group_same_length(lengths, B: int, min_group: int, perm, batch_start, batch_len,

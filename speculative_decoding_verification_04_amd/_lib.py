@@ -29,6 +29,7 @@ PROTOTYPES = {
                                     _P, _P, _P]),
     "spec_resync_draft_kv": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                   _P, _P, _P]),
+    "spec_commit_paged": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "spec_group_same_length": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
 }
 

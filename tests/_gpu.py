@@ -172,3 +172,19 @@ def resync(kv, k, E, kv_len, emit_count, pos_mask=True):
     sv.spec_resync_draft_kv(kv, k, end_col, n, e, out["end_col"], out["kv_len"], pos_ids=out.get("pos"),
                             mask=out.get("mask"), bytes_moved=out["bytes_moved"], status=out["status"])
     return out
+
+
+def commit_paged(k, page, kv_len, emit_count, block_table):
+    B, max_pages = block_table.shape
+    per = (k + page) // page
+    bt = block_table if torch.is_tensor(block_table) else i32(block_table)
+    n = kv_len if torch.is_tensor(kv_len) else i32(kv_len)
+    e = emit_count if torch.is_tensor(emit_count) else i32(emit_count)
+    out = dict(kv_len=torch.empty(B, dtype=torch.int32, device=DEV),
+               pages_kept=torch.empty(B, dtype=torch.int32, device=DEV),
+               freed=torch.full((B * per,), -7, dtype=torch.int32, device=DEV),
+               freed_offsets=torch.empty(B + 1, dtype=torch.int32, device=DEV),
+               status=torch.empty(B, dtype=torch.int32, device=DEV))
+    sv.spec_commit_paged(k, page, n, e, bt, out["kv_len"], out["pages_kept"], out["freed"],
+                         out["freed_offsets"], status=out["status"])
+    return out

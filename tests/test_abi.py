@@ -190,6 +190,21 @@ def test_resync_argument_errors(args, code):
 
 @needs_lib
 @pytest.mark.parametrize("args,code", [
+    ((4, 3, 16, 8, N, B_, C_, D_, E_, F_, G_, N, N), sv.SPEC_EINVAL),          # NULL n
+    ((0, 3, 16, 8, A, B_, C_, D_, E_, F_, G_, N, N), sv.SPEC_EINVAL),          # B < 1
+    ((4, 0, 16, 8, A, B_, C_, D_, E_, F_, G_, N, N), sv.SPEC_EINVAL),          # k < 1
+    ((4, 3, 0, 8, A, B_, C_, D_, E_, F_, G_, N, N), sv.SPEC_EINVAL),           # page < 1
+    ((4, 3, 16, 0, A, B_, C_, D_, E_, F_, G_, N, N), sv.SPEC_EINVAL),          # max_pages < 1
+    ((4, 3, 16, 8, A, B_, C_, D_, D_, F_, G_, N, N), sv.SPEC_EINVAL),          # outputs alias
+    ((4, 3, 16, 8, A, B_, C_, A, E_, F_, G_, N, N), sv.SPEC_EINVAL),           # output aliases input
+    ((1 << 20, 3, 16, 1 << 12, A, B_, C_, D_, E_, F_, G_, N, N), sv.SPEC_EINVAL),  # table too large
+])
+def test_paged_argument_errors(args, code):
+    assert LIB.spec_commit_paged(*args) == code
+
+
+@needs_lib
+@pytest.mark.parametrize("args,code", [
     ((N, 10, 8, 2, B_, C_, D_, E_, F_, N), sv.SPEC_EINVAL),
     ((A, -1, 8, 2, B_, C_, D_, E_, F_, N), sv.SPEC_EINVAL),
     ((A, 10, 0, 2, B_, C_, D_, E_, F_, N), sv.SPEC_EINVAL),
