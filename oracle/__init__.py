@@ -38,4 +38,5 @@ from .process import process_row, process_rows, sample_verify_logits  # noqa: F4
 from .realign import commit_bookkeeping, position_and_mask, commit_realign, resync_draft  # noqa: F401
 from .group import group_same_length  # noqa: F401
 from .paged import commit_paged  # noqa: F401
+from .tree import tree_verify, compact_tree_slots  # noqa: F401
 from .unbatched import UnbatchedModel  # noqa: F401
