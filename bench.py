@@ -362,6 +362,45 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
     out["paged_commit"] = {"workload": f"paged rollback, B={B3} k={k3} page {page} rows, prefixes 512-4096",
                            "us_per_call": t * 1e6, "pages_released": int(fo[-1].item()),
                            "kv_bytes_moved": 0}
+    # tree verification: a 16-node candidate tree per sequence (parents among the
+    # 3 nodes just below), bf16 logits over the large-batch vocabulary, then the
+    # compaction of the accepted path's KV slots in the large-batch cache
+    cfg3 = W.workload(3)
+    NT, Vt = 16, cfg3["V"]
+    gt = W.planted_tree(W.stream(3, "logits", 0, 1), W.stream(3, "drafts", 0, 1), B3, NT, Vt,
+                        cfg3["logit_sd"], "bf16", W.alphas(3), 3)
+    zt = torch.from_numpy(gt["logits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    dtr, fct, nst = (torch.from_numpy(gt[key]).to(dev) for key in ("draft", "first_child", "next_sibling"))
+    acct, emitt, tokt = torch.empty(B3, **i32), torch.empty(B3, **i32), torch.empty(B3, NT, **i32)
+    patht, offt = torch.empty(B3, NT, **i32), torch.empty(B3 + 1, **i32)
+    wst = sv.workspace(sv.spec_verify_tree_workspace_bytes(B3, NT, Vt, sv.SPEC_BF16), dev)
+    call = lambda: sv.spec_verify_tree(zt, dtr, fct, nst, acct, emitt, tokt, patht, wst, emit_offsets=offt)
+    t = _time_calls(torch, call, 22)
+    nbytes = B3 * NT * Vt * 2
+    out["tree_verify"] = {"workload": f"greedy tree verify, B={B3} N={NT} nodes (parents among the 3 below), "
+                                      f"V={Vt} bf16",
+                          "us_per_call": t * 1e6, "rows_per_s": B3 * NT / t,
+                          "mean_accept_len": float(acct.float().mean().item()),
+                          "algorithmic_bytes": nbytes, "GBps": nbytes / t / 1e9,
+                          "frac_of_peak": nbytes / t / PEAK_HBM}
+    del zt, wst
+    Et = g3["E"]
+    kvt = torch.empty((g3["L"], 2, B3, g3["H"], Et + NT, g3["D"]), dtype=torch.bfloat16, device=dev)
+    end = torch.tensor([Et], **i32)
+    stt = torch.empty(B3, **i32)
+    # the same accepted paths every call: each call moves the same slots again
+    call = lambda: sv.spec_compact_tree_kv(kvt, NT, end, patht, emitt, status=stt)
+    t = _time_calls(torch, call, 52)
+    ph, eh = patht.cpu().numpy(), emitt.cpu().numpy()
+    moved = sum(int((ph[b, :eh[b]] != np.arange(eh[b])).sum()) for b in range(B3))
+    col = g3["L"] * 2 * g3["H"] * g3["D"] * 2                  # one slot of one sequence, all planes
+    nbytes = 2 * moved * col
+    out["tree_compact"] = {"workload": f"tree slot compaction, B={B3} N={NT}, KV L={g3['L']} H={g3['H']} "
+                                       f"D={g3['D']} bf16, E={Et}",
+                           "us_per_call": t * 1e6, "slots_moved": moved, "algorithmic_bytes": nbytes,
+                           "GBps": nbytes / t / 1e9, "frac_of_peak": nbytes / t / PEAK_HBM,
+                           "status_ok": bool((stt == 0).all().item())}
+    del kvt
     P = W.pool_lengths()
     L = torch.as_tensor(P, dtype=torch.int32, device=dev)
     N = P.size

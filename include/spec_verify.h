@@ -63,6 +63,7 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 #define SPEC_MAX_K 127          /* largest number of proposals k per sequence */
 #define SPEC_GROUP_MAX_N 4096   /* largest window for spec_group_same_length */
 #define SPEC_PROC_MAX_V 524288  /* largest vocabulary for the processed-distribution calls */
+#define SPEC_TREE_MAX_N 256     /* largest candidate tree (nodes per sequence) */
 
 /* Human-readable name of a return code. */
 const char *spec_strerror(int code);
@@ -287,6 +288,55 @@ int spec_commit_paged(int B, int k, int page_size, int max_pages, const int32_t 
                       const int32_t *emit_count, const int32_t *block_table, int32_t *kv_len_out,
                       int32_t *pages_kept, int32_t *freed_pages, int32_t *freed_offsets,
                       int32_t *status, spec_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Greedy verification of a candidate tree, and compaction of its KV slots.
+ * [Forensics] section 5 names tree-structured verification and [Walkthrough]
+ * 5.2 the fields a tree verifier records (draft tokens, positions, a
+ * visibility mask, retrieve_* links) without an algorithm.  Reading: the
+ * greedy rule of [Walkthrough] 4.1 applied along the tree.  Each sequence has
+ * N nodes in topological order; node 0 is the root (the last confirmed token)
+ * and node i > 0 proposes draft[b, i]; first_child / next_sibling (-1 = none)
+ * list each node's children in order, links pointing forward (to a larger
+ * index below N).  Row i of the logits is the target's distribution after the
+ * path ending at node i.  From the root: t = argmax of the current node's row
+ * (lowest index on ties); the first child proposing t is accepted and becomes
+ * the current node; otherwise t is emitted (correction, or bonus at a leaf)
+ * and the round stops.  EOS and the budget stop it as in spec_verify_greedy.
+ * A linear chain (node i's only child is i + 1) is exactly spec_verify_greedy.
+ *
+ * spec_verify_tree:
+ *   logits       [B, N, V] float32 or bf16
+ *   draft, first_child, next_sibling  [B, N] int32 (draft[b, 0] is ignored)
+ *   out_tokens   [B, N] out, -1 padded; accept_len, emit_count [B] out
+ *   path         [B, N] out, -1 padded: the nodes whose rows were read, from
+ *                the root, one per emitted token (their KV slots are kept)
+ *   emit_offsets [B + 1] out or NULL; status [B] out or NULL
+ *                (SPEC_ST_DRAFT_OOR; SPEC_ST_BAD_STATE for links that do not
+ *                point forward inside the tree: that sequence emits nothing)
+ *   ws           workspace of spec_verify_tree_workspace_bytes(B, N, V, dt)
+ * Errors: as spec_verify_greedy; SPEC_ECAPACITY for N > SPEC_TREE_MAX_N.
+ *
+ * spec_compact_tree_kv: the tree forward wrote node i's KV at column E + i of
+ * the left-padded cache [L][2][B][H][C][D]; sequence b's slots
+ * path[b, 0..e_b-1] are moved, in order, to columns E .. E + e_b - 1 (in
+ * place), after which spec_commit_realign_kv(k = N - 1) commits as usual.
+ *   end_col      device int32 E; path, emit_count as returned above
+ *   status       [B] out or NULL: SPEC_ST_BAD_STATE when E + N > C, e_b is
+ *                outside [0, N] or the path does not start at 0 and increase
+ *                (that sequence is left unchanged)
+ * Errors: SPEC_EINVAL for NULL pointers, sizes < 1, misalignment, overflow;
+ * SPEC_ECAPACITY for N > SPEC_TREE_MAX_N.
+ * ------------------------------------------------------------------------ */
+size_t spec_verify_tree_workspace_bytes(int B, int N, int V, spec_dtype dt);
+int spec_verify_tree(const void *logits, spec_dtype dt, int B, int N, int V, const int32_t *draft,
+                     const int32_t *first_child, const int32_t *next_sibling, int32_t eos_id,
+                     const int32_t *remaining, int32_t *accept_len, int32_t *emit_count,
+                     int32_t *out_tokens, int32_t *path, int32_t *emit_offsets, int32_t *status,
+                     void *ws, size_t ws_bytes, spec_stream_t stream);
+int spec_compact_tree_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, int D, int N,
+                         const int32_t *end_col, const int32_t *path, const int32_t *emit_count,
+                         int32_t *status, spec_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * Same-length grouping of a window of ragged sequences.

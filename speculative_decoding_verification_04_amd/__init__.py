@@ -16,13 +16,14 @@ SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_OK, SPEC_EINVAL, SPEC_EWORKSPACE, SPEC_ECAPACITY, SPEC_EHIP = 0, -1, -2, -3, -4
 SPEC_ST_DRAFT_OOR, SPEC_ST_Q_ZERO, SPEC_ST_RESID_ZERO = 1, 2, 4
 SPEC_ST_NONFINITE, SPEC_ST_BAD_STATE, SPEC_ST_CAPACITY = 8, 16, 32
-SPEC_MAX_K, SPEC_GROUP_MAX_N, SPEC_PROC_MAX_V = 127, 4096, 524288
+SPEC_MAX_K, SPEC_GROUP_MAX_N, SPEC_PROC_MAX_V, SPEC_TREE_MAX_N = 127, 4096, 524288, 256
 
 __all__ = [
     "SpecError", "spec_strerror", "spec_verify_greedy_workspace_bytes", "spec_verify_greedy",
     "spec_verify_sample_workspace_bytes", "spec_verify_sample", "spec_process_workspace_bytes",
     "spec_process_logits", "spec_verify_sample_logits_workspace_bytes", "spec_verify_sample_logits",
     "spec_commit_realign_kv", "spec_resync_draft_kv", "spec_commit_paged",
+    "spec_verify_tree_workspace_bytes", "spec_verify_tree", "spec_compact_tree_kv",
     "spec_group_same_length", "workspace", "library",
 ]
 
@@ -183,6 +184,33 @@ def spec_commit_paged(k: int, page_size: int, kv_len_in, emit_count, block_table
         _ptr(kv_len_out), _ptr(pages_kept), _ptr(freed_pages), _ptr(freed_offsets), _ptr(status),
         _stream(stream))
     _check(code, "spec_commit_paged")
+
+
+def spec_verify_tree_workspace_bytes(B: int, N: int, V: int, dtype_code: int) -> int:
+    return int(library().spec_verify_tree_workspace_bytes(B, N, V, dtype_code))
+
+
+def spec_verify_tree(logits, draft, first_child, next_sibling, accept_len, emit_count, out_tokens, path,
+                     ws, *, eos_id: int = -1, remaining=None, emit_offsets=None, status=None,
+                     stream=None) -> None:
+    """logits [B, N, V] (bf16/f32); draft, first_child, next_sibling [B, N] int32."""
+    B, N, V = logits.shape
+    code = library().spec_verify_tree(
+        _ptr(logits), _dtype_code(logits), B, N, V, _ptr(draft), _ptr(first_child), _ptr(next_sibling),
+        int(eos_id), _ptr(remaining), _ptr(accept_len), _ptr(emit_count), _ptr(out_tokens), _ptr(path),
+        _ptr(emit_offsets), _ptr(status), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(code, "spec_verify_tree")
+
+
+def spec_compact_tree_kv(kv, N: int, end_col, path, emit_count, *, status=None, stream=None) -> None:
+    """kv [L, 2, B, H, C, D] (bf16/f32): kept tree slots moved to columns E .. E+e-1 in place."""
+    L, two, B, H, C, D = kv.shape
+    if two != 2:
+        raise ValueError("kv must be [L, 2, B, H, C, D]")
+    code = library().spec_compact_tree_kv(
+        _ptr(kv), _dtype_code(kv), L, B, H, C, D, int(N), _ptr(end_col), _ptr(path), _ptr(emit_count),
+        _ptr(status), _stream(stream))
+    _check(code, "spec_compact_tree_kv")
 
 
 def spec_group_same_length(lengths, B: int, min_group: int, perm, batch_start, batch_len,

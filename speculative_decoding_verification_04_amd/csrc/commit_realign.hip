@@ -245,6 +245,86 @@ __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
   }
 }
 
+// ---- tree verification: move the accepted path's slots together -----------
+// The forward over a candidate tree wrote one slot per node at columns E + i.
+// Sequence b keeps the slots path[b, 0..e_b-1] (increasing node indices, path
+// starting at the root 0) and they must sit at columns E .. E + e_b - 1 before
+// the usual realignment.  One workgroup per (layer, K/V, sequence, head) plane.
+// Column j receives column path[j] >= j: it is never the source of a later
+// j' (path[j'] > path[j] >= j) but may be the source of an earlier one, so
+// every pass reads all of its sources before any of its writes (registers,
+// then a barrier), and passes go in increasing j.
+constexpr int kCompactThreads = 256;
+constexpr int kCompactU = 4;
+
+struct CompactParams {
+  unsigned char *kv;
+  int B, H, C, N, R;           // R: bytes per column
+  long long plane_bytes;
+  int num_planes;
+  const int32_t *end_col, *path, *emit_count;
+  int32_t *status;
+};
+
+__device__ inline bool compact_ok(const CompactParams &P, int b, int E) {
+  if (E < 0 || E > P.C - P.N) return false;
+  const int e = P.emit_count[b];
+  if (e < 0 || e > P.N) return false;
+  const int32_t *pb = P.path + static_cast<size_t>(b) * P.N;
+  int prev = -1;
+  for (int j = 0; j < e; ++j) {
+    const int x = pb[j];
+    if (x <= prev || x >= P.N || (j == 0 && x != 0)) return false;
+    prev = x;
+  }
+  return true;
+}
+
+template <int VB>
+__global__ __launch_bounds__(kCompactThreads) void tree_compact_kernel(CompactParams P) {
+  using VT = typename VecOf<VB>::T;
+  const int blk = blockIdx.x, t = threadIdx.x;
+  const int E = P.end_col[0];
+  if (blk < P.B) {                          // status of sequence blk
+    if (P.status && t == 0) P.status[blk] = compact_ok(P, blk, E) ? 0 : SPEC_ST_BAD_STATE;
+    return;
+  }
+  const int p = blk - P.B;
+  const int b = (p / P.H) % P.B;
+  if (!compact_ok(P, b, E)) return;
+  const int e = P.emit_count[b];
+  const int32_t *pb = P.path + static_cast<size_t>(b) * P.N;
+  VT *base = reinterpret_cast<VT *>(P.kv + static_cast<size_t>(p) * P.plane_bytes);
+  const int per_col = P.R / VB;
+  const int units = e * per_col;            // (column j, vector v) pairs, j-major
+  constexpr int kPass = kCompactThreads * kCompactU;
+  for (int u0 = 0; u0 < units; u0 += kPass) {
+    VT x[kCompactU];
+    int dst[kCompactU];
+#pragma unroll
+    for (int q = 0; q < kCompactU; ++q) {
+      const int u = u0 + q * kCompactThreads + t;
+      dst[q] = -1;
+      if (u < units) {
+        const int j = u / per_col, v = u - j * per_col;
+        const int src = pb[j];
+        if (src != j) {
+          x[q] = base[static_cast<size_t>(E + src) * per_col + v];
+          dst[q] = (E + j) * per_col + v;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kCompactU; ++q)
+      if (dst[q] >= 0) hold(x[q]);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kCompactU; ++q)
+      if (dst[q] >= 0) base[dst[q]] = x[q];
+    __syncthreads();
+  }
+}
+
 }  // namespace
 }  // namespace specv
 
@@ -329,4 +409,50 @@ extern "C" int spec_resync_draft_kv(void *kv, spec_dtype dt, int L, int B, int H
                                     int64_t *bytes_moved, int32_t *status, spec_stream_t stream) {
   return realign_launch(kv, dt, L, B, H, C, D, k, k, end_col, kv_len_in, emit_count, end_col_out,
                         kv_len_out, pos_ids, mask, bytes_moved, status, stream);
+}
+
+extern "C" int spec_compact_tree_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, int D, int N,
+                                    const int32_t *end_col, const int32_t *path,
+                                    const int32_t *emit_count, int32_t *status, spec_stream_t stream) {
+  if (!kv || !end_col || !path || !emit_count) return SPEC_EINVAL;
+  if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_EINVAL;
+  if (L < 1 || B < 1 || H < 1 || C < 1 || D < 1 || N < 1) return SPEC_EINVAL;
+  if (N > SPEC_TREE_MAX_N) return SPEC_ECAPACITY;
+  const int elt = dt == SPEC_BF16 ? 2 : 4;
+  if (!aligned(kv, elt)) return SPEC_EINVAL;
+  const long long planes = 2LL * L * B * H;
+  const long long R = static_cast<long long>(D) * elt;
+  if (planes + B >= INT32_MAX || static_cast<long long>(C) * R / elt >= INT32_MAX ||
+      static_cast<long long>(C) * R >= (1LL << 62) / planes)
+    return SPEC_EINVAL;
+  const size_t kv_bytes = static_cast<size_t>(planes) * C * R;
+  const size_t b4 = static_cast<size_t>(B) * 4;
+  if (overlaps(status, b4, kv, kv_bytes) || overlaps(status, b4, path, b4 * N) ||
+      overlaps(status, b4, emit_count, b4) || overlaps(status, b4, end_col, 4))
+    return SPEC_EINVAL;
+  CompactParams P;
+  P.kv = static_cast<unsigned char *>(kv);
+  P.B = B;
+  P.H = H;
+  P.C = C;
+  P.N = N;
+  P.R = static_cast<int>(R);
+  P.plane_bytes = static_cast<long long>(C) * R;
+  P.num_planes = static_cast<int>(planes);
+  P.end_col = end_col;
+  P.path = path;
+  P.emit_count = emit_count;
+  P.status = status;
+  const dim3 grid(static_cast<unsigned>(B + planes)), block(kCompactThreads);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (R % 16 == 0 && aligned(kv, 16))
+    hipLaunchKernelGGL(tree_compact_kernel<16>, grid, block, 0, s, P);
+  else if (R % 8 == 0 && aligned(kv, 8))
+    hipLaunchKernelGGL(tree_compact_kernel<8>, grid, block, 0, s, P);
+  else if (R % 4 == 0 && aligned(kv, 4))
+    hipLaunchKernelGGL(tree_compact_kernel<4>, grid, block, 0, s, P);
+  else
+    hipLaunchKernelGGL(tree_compact_kernel<2>, grid, block, 0, s, P);
+  return launch_status();
 }

@@ -52,6 +52,9 @@ struct GreedyParams {
   const int32_t *remaining;
   int32_t *accept_len, *emit_count, *out_tokens, *emit_offsets, *status;
   uint64_t *keys;     // [B*(k+1)*chunks]
+  // tree verification only (k + 1 = N nodes per sequence)
+  const int32_t *first_child, *next_sibling;
+  int32_t *path;
 };
 
 inline size_t greedy_ws_bytes(int B, int k, int chunks) {
@@ -266,6 +269,100 @@ __global__ __launch_bounds__(kCommitThreads) void greedy_commit_kernel(GreedyPar
   if (P.emit_offsets && t == 0) P.emit_offsets[P.B] = carry;
 }
 
+// Greedy verification of a candidate tree (one logit row per node, rows from
+// greedy_chunk_kernel's keys).  One workgroup; per tile of sequences every
+// global read (keys, drafts, links, budgets) is issued first, then one lane
+// per sequence walks its tree from LDS: take the argmax of the current node's
+// row, accept the first child (in sibling order) proposing it, else emit it
+// and stop.  Links must point forward inside the tree, so a walk visits at
+// most N nodes and every sibling scan ends.
+constexpr int kTreeRows = 1024;
+
+__global__ __launch_bounds__(kCommitThreads) void tree_commit_kernel(GreedyParams P) {
+  __shared__ unsigned long long sh_row[kTreeRows];
+  __shared__ int sh_d[kTreeRows];
+  __shared__ int sh_fc[kTreeRows];
+  __shared__ int sh_ns[kTreeRows];
+  __shared__ int sh_rem[kTreeRows];
+  __shared__ int sh_scan[kCommitThreads / kWave + 1];
+  const int t = threadIdx.x;
+  const int N = P.k + 1;
+  const int per_tile = kTreeRows / N;                // N <= SPEC_TREE_MAX_N keeps this >= 4
+  int carry = 0;
+  for (int s0 = 0; s0 < P.B; s0 += per_tile) {
+    const int nseq = min(per_tile, P.B - s0);
+    const int nrows = nseq * N;
+    const size_t r0 = static_cast<size_t>(s0) * N;
+    for (int i = t; i < nrows; i += kCommitThreads) {
+      sh_d[i] = P.draft[r0 + i];
+      sh_fc[i] = P.first_child[r0 + i];
+      sh_ns[i] = P.next_sibling[r0 + i];
+    }
+    if (t < nseq) sh_rem[t] = P.remaining ? P.remaining[s0 + t] : -1;
+    const uint64_t *kb = P.keys + r0 * P.chunks;
+    for (int r = t; r < nrows; r += kCommitThreads) {
+      const uint64_t *rk = kb + static_cast<size_t>(r) * P.chunks;
+      uint64_t best = 0ull;
+      for (int c0 = 0; c0 < P.chunks; c0 += kKeysPerThread) {
+        uint64_t kr[kKeysPerThread];
+#pragma unroll
+        for (int q = 0; q < kKeysPerThread; ++q) kr[q] = c0 + q < P.chunks ? rk[c0 + q] : 0ull;
+#pragma unroll
+        for (int q = 0; q < kKeysPerThread; ++q) best = kr[q] > best ? kr[q] : best;
+      }
+      sh_row[r] = best;
+    }
+    __syncthreads();
+    int cnt = 0;
+    if (t < nseq) {
+      const int b = s0 + t;
+      const int base = t * N;
+      int32_t *out = P.out_tokens + static_cast<size_t>(b) * N;
+      int32_t *path = P.path + static_cast<size_t>(b) * N;
+      int st = 0;
+      bool links_ok = true;
+      for (int i = 0; i < N; ++i) {
+        if (i > 0 && (sh_d[base + i] < 0 || sh_d[base + i] >= P.V)) st |= SPEC_ST_DRAFT_OOR;
+        const int fc = sh_fc[base + i], ns = sh_ns[base + i];
+        if ((fc != -1 && (fc <= i || fc >= N)) || (ns != -1 && (ns <= i || ns >= N))) links_ok = false;
+      }
+      int acc = 0;
+      const int rem = sh_rem[t];
+      if (!links_ok) {
+        st |= SPEC_ST_BAD_STATE;
+      } else if (rem != 0) {
+        int cur = 0;
+        path[0] = 0;
+        while (true) {
+          const int tok = argmax_key_index(sh_row[base + cur]);
+          out[cnt++] = tok;
+          int c = sh_fc[base + cur];
+          while (c != -1 && sh_d[base + c] != tok) c = sh_ns[base + c];
+          if (c != -1) ++acc;
+          if ((P.eos >= 0 && tok == P.eos) || cnt == rem || c == -1) break;
+          path[cnt] = c;
+          cur = c;
+        }
+      }
+      for (int i = cnt; i < N; ++i) {
+        out[i] = -1;
+        path[i] = -1;
+      }
+      P.accept_len[b] = acc;
+      P.emit_count[b] = cnt;
+      if (P.status) P.status[b] = st;
+    }
+    if (P.emit_offsets) {
+      int total;
+      const int ex = block_excl_scan(t < nseq ? cnt : 0, sh_scan, &total);
+      if (t < nseq) P.emit_offsets[s0 + t] = carry + ex;
+      carry += total;
+    }
+    __syncthreads();
+  }
+  if (P.emit_offsets && t == 0) P.emit_offsets[P.B] = carry;
+}
+
 }  // namespace
 }  // namespace specv
 
@@ -323,6 +420,8 @@ extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int 
   P.emit_offsets = emit_offsets;
   P.status = status;
   P.keys = static_cast<uint64_t *>(ws);
+  P.first_child = P.next_sibling = nullptr;
+  P.path = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (dt == SPEC_BF16)
@@ -330,5 +429,69 @@ extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int 
   else
     hipLaunchKernelGGL(greedy_chunk_kernel<false>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
   hipLaunchKernelGGL(greedy_commit_kernel, dim3(1), dim3(kCommitThreads), 0, s, P);
+  return launch_status();
+}
+
+extern "C" size_t spec_verify_tree_workspace_bytes(int B, int N, int V, spec_dtype dt) {
+  if (B < 1 || N < 1 || V < 1 || N > SPEC_TREE_MAX_N) return 0;
+  return greedy_ws_bytes(B, N - 1, greedy_chunks(V, dt));
+}
+
+extern "C" int spec_verify_tree(const void *logits, spec_dtype dt, int B, int N, int V,
+                                const int32_t *draft, const int32_t *first_child,
+                                const int32_t *next_sibling, int32_t eos_id, const int32_t *remaining,
+                                int32_t *accept_len, int32_t *emit_count, int32_t *out_tokens,
+                                int32_t *path, int32_t *emit_offsets, int32_t *status, void *ws,
+                                size_t ws_bytes, spec_stream_t stream) {
+  if (!logits || !draft || !first_child || !next_sibling || !accept_len || !emit_count || !out_tokens ||
+      !path || !ws)
+    return SPEC_EINVAL;
+  if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_EINVAL;
+  if (B < 1 || N < 1 || V < 1 || V >= INT32_MAX - 1) return SPEC_EINVAL;
+  if (N > SPEC_TREE_MAX_N) return SPEC_ECAPACITY;
+  const size_t elt = dt == SPEC_BF16 ? 2 : 4;
+  if (!aligned(logits, elt)) return SPEC_EINVAL;
+  const int chunks = greedy_chunks(V, dt);
+  const long long nblocks = static_cast<long long>(B) * N * chunks;
+  if (nblocks >= INT32_MAX) return SPEC_EINVAL;
+  const size_t wsb = greedy_ws_bytes(B, N - 1, chunks);
+  if (ws_bytes < wsb || !aligned(ws, 256)) return SPEC_EWORKSPACE;
+  const size_t bn4 = static_cast<size_t>(B) * N * 4, b4 = static_cast<size_t>(B) * 4;
+  const void *ins[] = {logits, draft, first_child, next_sibling, remaining, ws};
+  const size_t in_n[] = {static_cast<size_t>(B) * N * V * elt, bn4, bn4, bn4, b4, wsb};
+  const void *outs[] = {accept_len, emit_count, out_tokens, path, emit_offsets, status};
+  const size_t out_n[] = {b4, b4, bn4, bn4, b4 + 4, b4};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return SPEC_EINVAL;
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return SPEC_EINVAL;
+  }
+  GreedyParams P;
+  P.logits = static_cast<const unsigned char *>(logits);
+  P.B = B;
+  P.k = N - 1;
+  P.V = V;
+  P.chunks = chunks;
+  P.chunk_elems = dt == SPEC_BF16 ? greedy_chunk_elems<true>() : greedy_chunk_elems<false>();
+  P.draft = draft;
+  P.eos = eos_id;
+  P.remaining = remaining;
+  P.accept_len = accept_len;
+  P.emit_count = emit_count;
+  P.out_tokens = out_tokens;
+  P.emit_offsets = emit_offsets;
+  P.status = status;
+  P.keys = static_cast<uint64_t *>(ws);
+  P.first_child = first_child;
+  P.next_sibling = next_sibling;
+  P.path = path;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (dt == SPEC_BF16)
+    hipLaunchKernelGGL(greedy_chunk_kernel<true>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
+  else
+    hipLaunchKernelGGL(greedy_chunk_kernel<false>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(tree_commit_kernel, dim3(1), dim3(kCommitThreads), 0, s, P);
   return launch_status();
 }

@@ -188,3 +188,32 @@ def commit_paged(k, page, kv_len, emit_count, block_table):
     sv.spec_commit_paged(k, page, n, e, bt, out["kv_len"], out["pages_kept"], out["freed"],
                          out["freed_offsets"], status=out["status"])
     return out
+
+
+def verify_tree(logits_dev, draft, first_child, next_sibling, eos_id=-1, remaining=None, ws_key=None):
+    B, N, V = logits_dev.shape
+    dt = sv.SPEC_BF16 if logits_dev.dtype == torch.bfloat16 else sv.SPEC_F32
+    out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=DEV),
+               emit_count=torch.empty(B, dtype=torch.int32, device=DEV),
+               out_tokens=torch.empty(B, N, dtype=torch.int32, device=DEV),
+               path=torch.empty(B, N, dtype=torch.int32, device=DEV),
+               emit_offsets=torch.empty(B + 1, dtype=torch.int32, device=DEV),
+               status=torch.empty(B, dtype=torch.int32, device=DEV))
+    w = ws(sv.spec_verify_tree_workspace_bytes(B, N, V, dt), ws_key)
+    dev = [a if torch.is_tensor(a) else i32(a) for a in (draft, first_child, next_sibling)]
+    rem = None if remaining is None else i32(remaining)
+    sv.spec_verify_tree(logits_dev, dev[0], dev[1], dev[2], out["accept_len"], out["emit_count"],
+                        out["out_tokens"], out["path"], w, eos_id=eos_id, remaining=rem,
+                        emit_offsets=out["emit_offsets"], status=out["status"])
+    return out
+
+
+def compact_tree(kv, N, E, path, emit_count):
+    """Run spec_compact_tree_kv in place; returns the per-sequence status."""
+    B = kv.shape[2]
+    end_col = E if torch.is_tensor(E) else torch.tensor([E], dtype=torch.int32, device=DEV)
+    p = path if torch.is_tensor(path) else i32(path)
+    e = emit_count if torch.is_tensor(emit_count) else i32(emit_count)
+    status = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    sv.spec_compact_tree_kv(kv, N, end_col, p, e, status=status)
+    return status

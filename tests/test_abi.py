@@ -205,6 +205,31 @@ def test_paged_argument_errors(args, code):
 
 @needs_lib
 @pytest.mark.parametrize("args,code", [
+    ((N, 1, 2, 4, 100, B_, C_, D_, -1, N, E_, F_, G_, H_, N, N, WS, 1 << 20, N), sv.SPEC_EINVAL),      # NULL logits
+    ((A, 1, 2, 0, 100, B_, C_, D_, -1, N, E_, F_, G_, H_, N, N, WS, 1 << 20, N), sv.SPEC_EINVAL),      # N < 1
+    ((A, 1, 2, 300, 100, B_, C_, D_, -1, N, E_, F_, G_, H_, N, N, WS, 1 << 20, N), sv.SPEC_ECAPACITY),  # N > max
+    ((A, 1, 2, 4, 100, B_, N, D_, -1, N, E_, F_, G_, H_, N, N, WS, 1 << 20, N), sv.SPEC_EINVAL),       # NULL links
+    ((A, 1, 2, 4, 100, B_, C_, D_, -1, N, E_, F_, G_, H_, N, N, WS, 8, N), sv.SPEC_EWORKSPACE),
+    ((A, 1, 2, 4, 100, B_, C_, D_, -1, N, E_, E_, G_, H_, N, N, WS, 1 << 20, N), sv.SPEC_EINVAL),      # alias
+])
+def test_tree_argument_errors(args, code):
+    assert LIB.spec_verify_tree(*args) == code
+
+
+@needs_lib
+@pytest.mark.parametrize("args,code", [
+    ((N, 1, 2, 2, 2, 16, 8, 4, A, B_, C_, N, N), sv.SPEC_EINVAL),
+    ((H_, 1, 2, 2, 2, 16, 8, 0, A, B_, C_, N, N), sv.SPEC_EINVAL),
+    ((H_, 1, 2, 2, 2, 16, 8, 300, A, B_, C_, N, N), sv.SPEC_ECAPACITY),
+    ((H_, 1, 2, 2, 2, 16, 8, 4, A, N, C_, N, N), sv.SPEC_EINVAL),
+    ((ctypes.c_void_p(0x80001), 1, 2, 2, 2, 16, 8, 4, A, B_, C_, N, N), sv.SPEC_EINVAL),
+])
+def test_compact_argument_errors(args, code):
+    assert LIB.spec_compact_tree_kv(*args) == code
+
+
+@needs_lib
+@pytest.mark.parametrize("args,code", [
     ((N, 10, 8, 2, B_, C_, D_, E_, F_, N), sv.SPEC_EINVAL),
     ((A, -1, 8, 2, B_, C_, D_, E_, F_, N), sv.SPEC_EINVAL),
     ((A, 10, 0, 2, B_, C_, D_, E_, F_, N), sv.SPEC_EINVAL),

@@ -17,6 +17,8 @@ from .configs import (  # noqa: F401
     alphas,
     bf16_bits_from_f32,
     planted_greedy,
+    random_tree,
+    planted_tree,
     greedy_round,
     sample_round,
     sample_logits,

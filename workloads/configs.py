@@ -105,6 +105,60 @@ def planted_greedy(g_logits: np.random.Generator, g_drafts: np.random.Generator,
     return dict(logits=logits, dtype=dtype, drafts=drafts, B=B, k=k, V=V)
 
 
+def random_tree(rng: np.random.Generator, N: int, branching: int = 3):
+    """A random tree of N nodes in topological order: node i's parent is drawn
+    uniformly from the `branching` nodes just below i.  Returns the parent list
+    and the first_child / next_sibling links (children in index order)."""
+    parent = np.full(N, -1, np.int64)
+    fc = np.full(N, -1, np.int32)
+    ns = np.full(N, -1, np.int32)
+    last = np.full(N, -1, np.int64)
+    for i in range(1, N):
+        p = int(rng.integers(max(0, i - branching), i))
+        parent[i] = p
+        if fc[p] == -1:
+            fc[p] = i
+        else:
+            ns[last[p]] = i
+        last[p] = i
+    return parent, fc, ns
+
+
+def planted_tree(g_logits: np.random.Generator, g_drafts: np.random.Generator,
+                 B: int, N: int, V: int, sd: float, dtype: str, alpha, branching: int = 3) -> dict:
+    """A candidate tree per sequence with logits [B, N, V] ~ N(0, sd).
+
+    Node i > 0 proposes, with probability alpha_b, the argmax of its parent's
+    row (so siblings may propose the same id), else a uniform id other than
+    it; draft[b, 0] is 0.  As in planted_greedy the argmax only shapes how deep
+    verification goes.  bf16 logits are returned as uint16 bits."""
+    z = g_logits.standard_normal((B, N, V), dtype=np.float32)
+    z *= np.float32(sd)
+    if dtype == "bf16":
+        logits = bf16_bits_from_f32(z)
+        view = _widen_for_planting(logits)
+    else:
+        logits = z
+        view = z
+    amax = np.argmax(view, axis=-1)
+    a = np.broadcast_to(np.asarray(alpha, dtype=np.float64), (B,))
+    parent = np.full((B, N), -1, np.int64)
+    fc = np.full((B, N), -1, np.int32)
+    ns = np.full((B, N), -1, np.int32)
+    draft = np.zeros((B, N), np.int32)
+    for b in range(B):
+        parent[b], fc[b], ns[b] = random_tree(g_drafts, N, branching)
+        for i in range(1, N):
+            want = int(amax[b, parent[b, i]])
+            if g_drafts.random() < a[b]:
+                draft[b, i] = want
+            else:
+                o = int(g_drafts.integers(0, V - 1))
+                draft[b, i] = o + (o >= want)
+    return dict(logits=logits, dtype=dtype, draft=draft, first_child=fc, next_sibling=ns,
+                parent=parent, B=B, N=N, V=V)
+
+
 def greedy_round(c: int, round_: int = 0, B: int | None = None) -> dict:
     """Target logits and planted drafts of workload c for one verify round."""
     cfg = WORKLOADS[c]
