@@ -29,6 +29,7 @@ from __future__ import annotations
 import argparse
 import glob
 import hashlib
+import itertools
 import json
 import os
 import statistics
@@ -73,13 +74,17 @@ def _counter_rows(directory: str, counter: str):
     return rows
 
 
-def _per_kernel(rows, key, largest_grid=False):
+def _per_kernel(rows, key, step_grid=False):
     """Mean counter value per dispatch of the kernels named like key.  With
-    largest_grid, only the dispatches of the largest grid: the step loop's
-    realign, not the smaller batch-scaling runs of the same kernel."""
+    step_grid, only the dispatches of the grid launched most often (the
+    largest on a tie): the step loop's, not a secondary call or a smaller
+    batch-size run of the same kernel."""
     sel = [(v, g) for name, v, g in rows if key in name]
-    if largest_grid and sel:
-        top = max(g for _, g in sel)
+    if step_grid and sel:
+        count = {}
+        for _, g in sel:
+            count[g] = count.get(g, 0) + 1
+        top = max(count, key=lambda g: (count[g], g))
         sel = [(v, g) for v, g in sel if g == top]
     vals = [v for v, _ in sel]
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
@@ -89,8 +94,8 @@ def record_traffic(fetch_dir: str, write_dir: str) -> None:
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
     dispatch) of this benchmark into the committed traffic summary."""
     f_rows, w_rows = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
-    pf, _ = _per_kernel([r for r in f_rows if "neg" in r[0].lower()], "", largest_grid=True)
-    pw, _ = _per_kernel([r for r in w_rows if "neg" in r[0].lower()], "", largest_grid=True)
+    pf, _ = _per_kernel([r for r in f_rows if "neg" in r[0].lower()], "", step_grid=True)
+    pw, _ = _per_kernel([r for r in w_rows if "neg" in r[0].lower()], "", step_grid=True)
     out = {"probe": {"kernel": "torch int32 negation (one 4-byte read and one 4-byte write per element)",
                      "bytes_read": PROBE_BYTES, "bytes_written": PROBE_BYTES,
                      "fetch_kib": pf, "write_kib": pw,
@@ -98,8 +103,8 @@ def record_traffic(fetch_dir: str, write_dir: str) -> None:
                      "write_factor": (pw * 1024 / PROBE_BYTES) if pw else None},
            "kernels": {}, "sources_sha256": sources_digest()}
     for key in ("greedy_chunk_kernel", "greedy_commit_kernel", "realign_kernel"):
-        fk, nf = _per_kernel(f_rows, key, largest_grid=True)
-        wk, nw = _per_kernel(w_rows, key, largest_grid=True)
+        fk, nf = _per_kernel(f_rows, key, step_grid=True)
+        wk, nw = _per_kernel(w_rows, key, step_grid=True)
         out["kernels"][key] = {"fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
                                "dispatches": [nf, nw]}
     os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
@@ -133,6 +138,8 @@ def main() -> int:
     ap.add_argument("--buffers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step only: no secondary calls or batch-size sweeps (for counter runs)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.record_traffic:
@@ -234,10 +241,12 @@ def main() -> int:
         probe = 2 * PROBE_BYTES / min(ts)
         del src, dst
 
-    log("secondary: stochastic verify (given rows and from logits) and same-length grouping")
-    secondary = secondary_measurements(dev, np, torch, sv, W)
-    log("batch scaling: realign cost and grouping rate against batch size")
-    secondary.update(batch_scaling(dev, np, torch, sv, W))
+    secondary = None
+    if not args.step_only:
+        log("secondary: stochastic verify, tree verify, paged commit, same-length grouping")
+        secondary = secondary_measurements(dev, np, torch, sv, W)
+        log("batch scaling: realign cost and grouping rate against batch size")
+        secondary.update(batch_scaling(dev, np, torch, sv, W))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -285,8 +294,17 @@ def main() -> int:
     return 0
 
 
-def _time_calls(torch, fn, reps: int) -> float:
-    """Median seconds per call over `reps` calls, HIP events on the launch stream."""
+def _time_calls(torch, fn, reps: int, inner: int = 24):
+    """Seconds per call: (GPU time, host-inclusive time).
+
+    GPU time: `inner` calls captured in one HIP graph (the calls launch kernels
+    only), replayed `reps` times between HIP events on the replay stream; the
+    median replay divided by `inner`.  Host-inclusive: HIP events around single
+    eager calls, median; for calls of a few microseconds this is mostly the
+    Python binding and launch latency."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -295,7 +313,35 @@ def _time_calls(torch, fn, reps: int) -> float:
         b.record()
         torch.cuda.synchronize()
         ts.append(a.elapsed_time(b) * 1e-3)
-    return statistics.median(ts[2:])
+    eager = statistics.median(ts[2:])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(inner):
+            fn()
+    torch.cuda.synchronize()
+    gs = []
+    for _ in range(max(5, reps // 4)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        gs.append(a.elapsed_time(b) * 1e-3 / inner)
+    del g
+    fn()                                    # outputs read afterwards come from an eager call
+    torch.cuda.synchronize()
+    return statistics.median(gs), eager
+
+
+def _rates(t: float, th: float, nbytes: int) -> dict:
+    return {"us_per_call": t * 1e6, "us_per_call_host": th * 1e6, "algorithmic_bytes": nbytes,
+            "GBps": nbytes / t / 1e9, "frac_of_peak": nbytes / t / PEAK_HBM}
 
 
 def secondary_measurements(dev, np, torch, sv, W) -> dict:
@@ -309,17 +355,24 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
     acc, emit, toks = torch.empty(B, **i32), torch.empty(B, **i32), torch.empty(B, k + 1, **i32)
     offs, mass = torch.empty(B + 1, **i32), torch.empty(B, dtype=torch.float64, device=dev)
     ws = sv.workspace(sv.spec_verify_sample_workspace_bytes(B, k, V), dev)
-    call = lambda: sv.spec_verify_sample(p, q, d, u, acc, emit, toks, ws, emit_offsets=offs, final_mass=mass)
-    t = _time_calls(torch, call, 22)
+    # 6 copies of p and q (262 MB, more than the 256 MB last-level cache), used in turn
+    pq = [(p, q)] + [(p.clone(), q.clone()) for _ in range(5)]
+    ip = itertools.count()
+
+    def call():
+        pc, qc = pq[next(ip) % len(pq)]
+        sv.spec_verify_sample(pc, qc, d, u, acc, emit, toks, ws, emit_offsets=offs, final_mass=mass)
+
+    t, th = _time_calls(torch, call, 22)
     m, e = acc.cpu().numpy(), emit.cpu().numpy()
     # realized algorithmic bytes: the row drawn from (p_j and q_j after a rejection,
     # p_k after full acceptance) plus two gathered scalars per examined draft
     row_bytes = sum(8 * V if (e[b] > m[b] and m[b] < k) else (4 * V if e[b] > m[b] else 0) for b in range(B))
     gathers = 8 * int(sum(min(int(m[b]) + 1, k) for b in range(B)))
     nbytes = row_bytes + gathers + 4 * B * (k + 1) * 2
-    out["sample_verify"] = {"workload": f"stochastic verify, B={B} k={k} V={V} f32", "us_per_call": t * 1e6,
-                            "rows_per_s": B * (k + 1) / t, "algorithmic_bytes": nbytes,
-                            "GBps": nbytes / t / 1e9, "frac_of_peak": nbytes / t / PEAK_HBM}
+    out["sample_verify"] = {"workload": f"stochastic verify, B={B} k={k} V={V} f32, 6 rotating p/q copies",
+                            **_rates(t, th, nbytes), "rows_per_s": B * (k + 1) / t}
+    del pq
     # stochastic verification from bf16 logits with temperature 0.7, top-k 50, top-p 0.9
     g = W.sample_logits(2)
     T, K, TP = g["temperature"], 50, 0.9
@@ -335,18 +388,24 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
     dl = torch.searchsorted(cq, ud * cq[..., -1:]).clamp_(max=V - 1).squeeze(-1).to(torch.int32).contiguous()
     ul = torch.from_numpy(g["uniforms"]).to(dev)
     wsl = sv.workspace(sv.spec_verify_sample_logits_workspace_bytes(B, k, V), dev)
-    call = lambda: sv.spec_verify_sample_logits(zt, zd, dl, ul, acc, emit, toks, wsl, temperature=T, top_k=K,
-                                                top_p=TP, emit_offsets=offs, final_mass=mass)
-    t = _time_calls(torch, call, 22)
+    # 12 copies of the two logit tensors (267 MB), used in turn
+    zz = [(zt, zd)] + [(zt.clone(), zd.clone()) for _ in range(11)]
+    iz = itertools.count()
+
+    def call():
+        a, b = zz[next(iz) % len(zz)]
+        sv.spec_verify_sample_logits(a, b, dl, ul, acc, emit, toks, wsl, temperature=T, top_k=K,
+                                     top_p=TP, emit_offsets=offs, final_mass=mass)
+
+    t, th = _time_calls(torch, call, 22)
     m, e = acc.cpu().numpy(), emit.cpu().numpy()
     rows_read = B * (2 * k + 1) * V * 2                       # the statistics pass reads every row once
     redraw = sum(4 * V if (e[b] > m[b] and m[b] < k) else (2 * V if e[b] > m[b] else 0) for b in range(B))
     nbytes = rows_read + redraw
     out["sample_verify_logits"] = {"workload": f"stochastic verify from bf16 logits, B={B} k={k} V={V}, "
-                                               f"T={T} top_k={K} top_p={TP}",
-                                   "us_per_call": t * 1e6, "rows_per_s": B * (k + 1) / t,
-                                   "algorithmic_bytes": nbytes, "GBps": nbytes / t / 1e9,
-                                   "frac_of_peak": nbytes / t / PEAK_HBM}
+                                               f"T={T} top_k={K} top_p={TP}, 12 rotating logit copies",
+                                   **_rates(t, th, nbytes), "rows_per_s": B * (k + 1) / t}
+    del zz
     # paged layout: the commit is a rollback of lengths and pages, no KV bytes move
     g3 = W.kv_geometry(3)
     B3, k3, page = g3["B"], g3["k"], 16
@@ -358,47 +417,63 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
     kl, pk = torch.empty(B3, **i32), torch.empty(B3, **i32)
     fr, fo = torch.empty(B3 * per, **i32), torch.empty(B3 + 1, **i32)
     call = lambda: sv.spec_commit_paged(k3, page, n3, e3, bt, kl, pk, fr, fo)
-    t = _time_calls(torch, call, 52)
+    t, th = _time_calls(torch, call, 52)
     out["paged_commit"] = {"workload": f"paged rollback, B={B3} k={k3} page {page} rows, prefixes 512-4096",
-                           "us_per_call": t * 1e6, "pages_released": int(fo[-1].item()),
+                           "us_per_call": t * 1e6, "us_per_call_host": th * 1e6,
+                           "pages_released": int(fo[-1].item()),
                            "kv_bytes_moved": 0}
     # tree verification: a 16-node candidate tree per sequence (parents among the
-    # 3 nodes just below), bf16 logits over the large-batch vocabulary, then the
-    # compaction of the accepted path's KV slots in the large-batch cache
+    # 3 nodes just below), bf16 logits over the large-batch vocabulary, rotating
+    # over 3 logit buffers (394 MB, more than the 256 MB last-level cache); then
+    # the compaction of the accepted path's KV slots in the large-batch cache
     cfg3 = W.workload(3)
-    NT, Vt = 16, cfg3["V"]
-    gt = W.planted_tree(W.stream(3, "logits", 0, 1), W.stream(3, "drafts", 0, 1), B3, NT, Vt,
-                        cfg3["logit_sd"], "bf16", W.alphas(3), 3)
-    zt = torch.from_numpy(gt["logits"].view(np.int16)).to(dev).view(torch.bfloat16)
-    dtr, fct, nst = (torch.from_numpy(gt[key]).to(dev) for key in ("draft", "first_child", "next_sibling"))
+    NT, Vt, nbt = 16, cfg3["V"], 3
+    trees = []
+    for i in range(nbt):
+        gt = W.planted_tree(W.stream(3, "logits", i, 1), W.stream(3, "drafts", i, 1), B3, NT, Vt,
+                            cfg3["logit_sd"], "bf16", W.alphas(3), 3)
+        trees.append([torch.from_numpy(gt["logits"].view(np.int16)).to(dev).view(torch.bfloat16)] +
+                     [torch.from_numpy(gt[key]).to(dev) for key in ("draft", "first_child", "next_sibling")])
+        del gt
     acct, emitt, tokt = torch.empty(B3, **i32), torch.empty(B3, **i32), torch.empty(B3, NT, **i32)
     patht, offt = torch.empty(B3, NT, **i32), torch.empty(B3 + 1, **i32)
     wst = sv.workspace(sv.spec_verify_tree_workspace_bytes(B3, NT, Vt, sv.SPEC_BF16), dev)
-    call = lambda: sv.spec_verify_tree(zt, dtr, fct, nst, acct, emitt, tokt, patht, wst, emit_offsets=offt)
-    t = _time_calls(torch, call, 22)
+    it = itertools.count()
+
+    def tree_call():
+        z, dtr, fct, nst = trees[next(it) % nbt]
+        sv.spec_verify_tree(z, dtr, fct, nst, acct, emitt, tokt, patht, wst, emit_offsets=offt)
+
+    reps = 22
+    t, th = _time_calls(torch, tree_call, reps, inner=3 * nbt)
     nbytes = B3 * NT * Vt * 2
+    accs = []
+    for i in range(nbt):                                 # mean accept length over the buffers
+        tree_call()
+        accs.append(float(acct.float().mean().item()))
     out["tree_verify"] = {"workload": f"greedy tree verify, B={B3} N={NT} nodes (parents among the 3 below), "
-                                      f"V={Vt} bf16",
-                          "us_per_call": t * 1e6, "rows_per_s": B3 * NT / t,
-                          "mean_accept_len": float(acct.float().mean().item()),
-                          "algorithmic_bytes": nbytes, "GBps": nbytes / t / 1e9,
-                          "frac_of_peak": nbytes / t / PEAK_HBM}
-    del zt, wst
+                                      f"V={Vt} bf16, {nbt} rotating logit buffers",
+                          **_rates(t, th, nbytes), "rows_per_s": B3 * NT / t,
+                          "mean_accept_len": sum(accs) / nbt}
+    del trees, wst
+    # compaction of the last buffer's paths; successive calls use end columns
+    # NT apart, so 48 calls touch 48 disjoint column ranges (more than the
+    # last-level cache holds) and each call moves cold bytes
     Et = g3["E"]
+    nE = 48
     kvt = torch.empty((g3["L"], 2, B3, g3["H"], Et + NT, g3["D"]), dtype=torch.bfloat16, device=dev)
-    end = torch.tensor([Et], **i32)
+    ends = [torch.tensor([Et - i * NT], **i32) for i in range(nE)]
     stt = torch.empty(B3, **i32)
-    # the same accepted paths every call: each call moves the same slots again
-    call = lambda: sv.spec_compact_tree_kv(kvt, NT, end, patht, emitt, status=stt)
-    t = _time_calls(torch, call, 52)
+    ic = itertools.count()
+    call = lambda: sv.spec_compact_tree_kv(kvt, NT, ends[next(ic) % nE], patht, emitt, status=stt)
+    t, th = _time_calls(torch, call, 52, inner=nE)
     ph, eh = patht.cpu().numpy(), emitt.cpu().numpy()
     moved = sum(int((ph[b, :eh[b]] != np.arange(eh[b])).sum()) for b in range(B3))
     col = g3["L"] * 2 * g3["H"] * g3["D"] * 2                  # one slot of one sequence, all planes
     nbytes = 2 * moved * col
     out["tree_compact"] = {"workload": f"tree slot compaction, B={B3} N={NT}, KV L={g3['L']} H={g3['H']} "
-                                       f"D={g3['D']} bf16, E={Et}",
-                           "us_per_call": t * 1e6, "slots_moved": moved, "algorithmic_bytes": nbytes,
-                           "GBps": nbytes / t / 1e9, "frac_of_peak": nbytes / t / PEAK_HBM,
+                                       f"D={g3['D']} bf16, end columns {Et - (nE - 1) * NT}..{Et}",
+                           **_rates(t, th, nbytes), "slots_moved": moved,
                            "status_ok": bool((stt == 0).all().item())}
     del kvt
     P = W.pool_lengths()
@@ -408,9 +483,9 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
     nb, ng = torch.empty(1, **i32), torch.empty(1, **i32)
     cfg = W.workload(4)
     call = lambda: sv.spec_group_same_length(L, cfg["B"], cfg["min_group"], perm, bstart, blen, nb, ng)
-    t = _time_calls(torch, call, 52)
+    t, th = _time_calls(torch, call, 52)
     out["group_same_length"] = {"workload": f"same-length grouping, pool {N}, batch {cfg['B']}, min_group {cfg['min_group']}",
-                                "us_per_call": t * 1e6, "num_batches": int(nb.item()),
+                                "us_per_call": t * 1e6, "us_per_call_host": th * 1e6, "num_batches": int(nb.item()),
                                 "grouped_fraction": int(ng.item()) / N}
     return out
 

@@ -249,78 +249,90 @@ __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
 // The forward over a candidate tree wrote one slot per node at columns E + i.
 // Sequence b keeps the slots path[b, 0..e_b-1] (increasing node indices, path
 // starting at the root 0) and they must sit at columns E .. E + e_b - 1 before
-// the usual realignment.  One workgroup per (layer, K/V, sequence, head) plane.
-// Column j receives column path[j] >= j: it is never the source of a later
-// j' (path[j'] > path[j] >= j) but may be the source of an earlier one, so
-// every pass reads all of its sources before any of its writes (registers,
-// then a barrier), and passes go in increasing j.
+// the usual realignment.  A valid path has path[j] >= j, with equality
+// exactly on a prefix j < j0 (once a node is skipped every later one sits
+// further right), so the slots to move are the contiguous tail j0 .. e_b - 1.
+// Column j receives column path[j] > j: it is never the source of a later j'
+// (path[j'] > path[j]) but may be the source of an earlier one, so every pass
+// reads all of its sources before any of its writes (registers, then a
+// barrier), and each plane's units go in increasing j across passes.
+//
+// One workgroup per (sequence, layer, K/V, group of heads): the group's
+// planes lie hpb * C * R bytes apart at most, and the workgroup reads the
+// sequence's path once, checking it in parallel, instead of once per plane.
 constexpr int kCompactThreads = 256;
 constexpr int kCompactU = 4;
+static_assert(kCompactThreads >= SPEC_TREE_MAX_N, "one lane per tree node");
 
 struct CompactParams {
   unsigned char *kv;
   int B, H, C, N, R;           // R: bytes per column
+  int hpb, hsplit;             // heads per workgroup, workgroups per (layer, K/V, sequence)
   long long plane_bytes;
-  int num_planes;
   const int32_t *end_col, *path, *emit_count;
   int32_t *status;
 };
 
-__device__ inline bool compact_ok(const CompactParams &P, int b, int E) {
-  if (E < 0 || E > P.C - P.N) return false;
-  const int e = P.emit_count[b];
-  if (e < 0 || e > P.N) return false;
-  const int32_t *pb = P.path + static_cast<size_t>(b) * P.N;
-  int prev = -1;
-  for (int j = 0; j < e; ++j) {
-    const int x = pb[j];
-    if (x <= prev || x >= P.N || (j == 0 && x != 0)) return false;
-    prev = x;
-  }
-  return true;
-}
-
 template <int VB>
 __global__ __launch_bounds__(kCompactThreads) void tree_compact_kernel(CompactParams P) {
   using VT = typename VecOf<VB>::T;
-  const int blk = blockIdx.x, t = threadIdx.x;
+  const int t = threadIdx.x;
+  const int blk = blockIdx.x;
+  const int b = blk % P.B;                  // consecutive workgroups: consecutive sequences
+  const int rest = blk / P.B;
+  const int hs = rest % P.hsplit;
+  const int lk = rest / P.hsplit;           // layer * 2 + (K or V)
   const int E = P.end_col[0];
-  if (blk < P.B) {                          // status of sequence blk
-    if (P.status && t == 0) P.status[blk] = compact_ok(P, blk, E) ? 0 : SPEC_ST_BAD_STATE;
-    return;
-  }
-  const int p = blk - P.B;
-  const int b = (p / P.H) % P.B;
-  if (!compact_ok(P, b, E)) return;
   const int e = P.emit_count[b];
-  const int32_t *pb = P.path + static_cast<size_t>(b) * P.N;
-  VT *base = reinterpret_cast<VT *>(P.kv + static_cast<size_t>(p) * P.plane_bytes);
+  const bool shape_ok = E >= 0 && E <= P.C - P.N && e >= 0 && e <= P.N;
+  int node = -1, prev = -1;
+  if (shape_ok && t < e) {
+    const int32_t *pb = P.path + static_cast<size_t>(b) * P.N;
+    node = pb[t];
+    prev = t > 0 ? pb[t - 1] : -1;
+  }
+  const bool lane_ok = t >= e || (node > prev && node < P.N && (t > 0 || node == 0));
+  const bool ok = shape_ok && __syncthreads_and(lane_ok);
+  if (P.status && lk == 0 && hs == 0 && t == 0) P.status[b] = ok ? 0 : SPEC_ST_BAD_STATE;
+  if (!ok) return;
+  __shared__ int sh_path[SPEC_TREE_MAX_N];
+  if (t < e) sh_path[t] = node;
+  const int j0 = __syncthreads_count(t < e && node == t);   // barrier: sh_path is visible
+  const int moved = e - j0;
+  const int h0 = hs * P.hpb;
+  const int nh = min(P.hpb, P.H - h0);
+  if (moved <= 0 || nh <= 0) return;
   const int per_col = P.R / VB;
-  const int units = e * per_col;            // (column j, vector v) pairs, j-major
+  const int per_plane = moved * per_col;     // (column j0 + m, vector v) pairs, column-major
+  const int units = nh * per_plane;
+  const size_t plane0 = (static_cast<size_t>(lk) * P.B + b) * P.H + h0;
+  unsigned char *base = P.kv + plane0 * P.plane_bytes;
   constexpr int kPass = kCompactThreads * kCompactU;
   for (int u0 = 0; u0 < units; u0 += kPass) {
     VT x[kCompactU];
-    int dst[kCompactU];
+    VT *dst[kCompactU];
 #pragma unroll
     for (int q = 0; q < kCompactU; ++q) {
       const int u = u0 + q * kCompactThreads + t;
-      dst[q] = -1;
+      dst[q] = nullptr;
       if (u < units) {
-        const int j = u / per_col, v = u - j * per_col;
-        const int src = pb[j];
-        if (src != j) {
-          x[q] = base[static_cast<size_t>(E + src) * per_col + v];
-          dst[q] = (E + j) * per_col + v;
-        }
+        const int h = u / per_plane;
+        const int r = u - h * per_plane;
+        const int m = r / per_col;
+        const int v = r - m * per_col;
+        const int j = j0 + m;
+        VT *pl = reinterpret_cast<VT *>(base + static_cast<size_t>(h) * P.plane_bytes);
+        x[q] = pl[static_cast<size_t>(E + sh_path[j]) * per_col + v];
+        dst[q] = pl + static_cast<size_t>(E + j) * per_col + v;
       }
     }
 #pragma unroll
     for (int q = 0; q < kCompactU; ++q)
-      if (dst[q] >= 0) hold(x[q]);
+      if (dst[q]) hold(x[q]);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < kCompactU; ++q)
-      if (dst[q] >= 0) base[dst[q]] = x[q];
+      if (dst[q]) *dst[q] = x[q];
     __syncthreads();
   }
 }
@@ -423,13 +435,18 @@ extern "C" int spec_compact_tree_kv(void *kv, spec_dtype dt, int L, int B, int H
   const long long planes = 2LL * L * B * H;
   const long long R = static_cast<long long>(D) * elt;
   if (planes + B >= INT32_MAX || static_cast<long long>(C) * R / elt >= INT32_MAX ||
-      static_cast<long long>(C) * R >= (1LL << 62) / planes)
+      static_cast<long long>(C) * R >= (1LL << 62) / planes || static_cast<long long>(H) * N * R >= INT32_MAX)
     return SPEC_EINVAL;
   const size_t kv_bytes = static_cast<size_t>(planes) * C * R;
   const size_t b4 = static_cast<size_t>(B) * 4;
   if (overlaps(status, b4, kv, kv_bytes) || overlaps(status, b4, path, b4 * N) ||
       overlaps(status, b4, emit_count, b4) || overlaps(status, b4, end_col, 4))
     return SPEC_EINVAL;
+  // enough workgroups to fill the chip: split each sequence's heads when the
+  // (sequence, layer, K/V) count alone is small
+  const long long groups = static_cast<long long>(B) * 2 * L;
+  const int hsplit = static_cast<int>(std::min<long long>(H, std::max<long long>(1, (2048 + groups - 1) / groups)));
+  const int hpb = (H + hsplit - 1) / hsplit;
   CompactParams P;
   P.kv = static_cast<unsigned char *>(kv);
   P.B = B;
@@ -437,13 +454,14 @@ extern "C" int spec_compact_tree_kv(void *kv, spec_dtype dt, int L, int B, int H
   P.C = C;
   P.N = N;
   P.R = static_cast<int>(R);
+  P.hpb = hpb;
+  P.hsplit = (H + hpb - 1) / hpb;
   P.plane_bytes = static_cast<long long>(C) * R;
-  P.num_planes = static_cast<int>(planes);
   P.end_col = end_col;
   P.path = path;
   P.emit_count = emit_count;
   P.status = status;
-  const dim3 grid(static_cast<unsigned>(B + planes)), block(kCompactThreads);
+  const dim3 grid(static_cast<unsigned>(groups * P.hsplit)), block(kCompactThreads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (R % 16 == 0 && aligned(kv, 16))

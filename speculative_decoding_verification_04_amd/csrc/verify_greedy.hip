@@ -277,13 +277,21 @@ __global__ __launch_bounds__(kCommitThreads) void greedy_commit_kernel(GreedyPar
 // and stop.  Links must point forward inside the tree, so a walk visits at
 // most N nodes and every sibling scan ends.
 constexpr int kTreeRows = 1024;
+static_assert(kTreeRows == kCommitThreads, "one lane per tree node of a tile");
 
+// One workgroup; tiles of whole sequences, one lane per node (row).  Each lane
+// folds its row's chunk keys into the row's argmax, checks its own links and
+// draft id, and finds which of its children (if any) proposes that argmax;
+// one lane per sequence then only follows those precomputed edges from the
+// root, and the emitted tokens and path are written back by all lanes.
 __global__ __launch_bounds__(kCommitThreads) void tree_commit_kernel(GreedyParams P) {
-  __shared__ unsigned long long sh_row[kTreeRows];
-  __shared__ int sh_d[kTreeRows];
-  __shared__ int sh_fc[kTreeRows];
+  __shared__ int sh_d[kTreeRows];     // draft ids; after the walk: emitted tokens
+  __shared__ int sh_fc[kTreeRows];    // first child; after the walk: path nodes
   __shared__ int sh_ns[kTreeRows];
-  __shared__ int sh_rem[kTreeRows];
+  __shared__ int sh_tok[kTreeRows];   // argmax of each node's row
+  __shared__ int sh_nxt[kTreeRows];   // child proposing that argmax, or -1
+  __shared__ int sh_st[kTreeRows];    // per-sequence status bits
+  __shared__ int sh_cnt[kTreeRows];   // per-sequence budget, then emitted count
   __shared__ int sh_scan[kCommitThreads / kWave + 1];
   const int t = threadIdx.x;
   const int N = P.k + 1;
@@ -293,16 +301,15 @@ __global__ __launch_bounds__(kCommitThreads) void tree_commit_kernel(GreedyParam
     const int nseq = min(per_tile, P.B - s0);
     const int nrows = nseq * N;
     const size_t r0 = static_cast<size_t>(s0) * N;
-    for (int i = t; i < nrows; i += kCommitThreads) {
-      sh_d[i] = P.draft[r0 + i];
-      sh_fc[i] = P.first_child[r0 + i];
-      sh_ns[i] = P.next_sibling[r0 + i];
-    }
-    if (t < nseq) sh_rem[t] = P.remaining ? P.remaining[s0 + t] : -1;
-    const uint64_t *kb = P.keys + r0 * P.chunks;
-    for (int r = t; r < nrows; r += kCommitThreads) {
-      const uint64_t *rk = kb + static_cast<size_t>(r) * P.chunks;
-      uint64_t best = 0ull;
+    const bool row = t < nrows;
+    const int seq = t / N, node = t - seq * N, base = seq * N;
+    int d = 0, fc = -1, ns = -1;
+    uint64_t best = 0ull;
+    if (row) {
+      d = P.draft[r0 + t];
+      fc = P.first_child[r0 + t];
+      ns = P.next_sibling[r0 + t];
+      const uint64_t *rk = P.keys + (r0 + t) * P.chunks;
       for (int c0 = 0; c0 < P.chunks; c0 += kKeysPerThread) {
         uint64_t kr[kKeysPerThread];
 #pragma unroll
@@ -310,47 +317,66 @@ __global__ __launch_bounds__(kCommitThreads) void tree_commit_kernel(GreedyParam
 #pragma unroll
         for (int q = 0; q < kKeysPerThread; ++q) best = kr[q] > best ? kr[q] : best;
       }
-      sh_row[r] = best;
+    }
+    if (t < nseq) {
+      sh_st[t] = 0;
+      sh_cnt[t] = P.remaining ? P.remaining[s0 + t] : -1;
+    }
+    const int tok = argmax_key_index(best);
+    if (row) {
+      sh_d[t] = d;
+      sh_fc[t] = fc;
+      sh_ns[t] = ns;
+      sh_tok[t] = tok;
+    }
+    __syncthreads();
+    if (row) {
+      int bits = 0;
+      if (node > 0 && (d < 0 || d >= P.V)) bits |= SPEC_ST_DRAFT_OOR;
+      if ((fc != -1 && (fc <= node || fc >= N)) || (ns != -1 && (ns <= node || ns >= N)))
+        bits |= SPEC_ST_BAD_STATE;
+      if (bits) atomicOr(&sh_st[seq], bits);
+    }
+    __syncthreads();
+    if (row) {
+      int c = -1;
+      if (!(sh_st[seq] & SPEC_ST_BAD_STATE)) {        // every link of this tree points forward
+        c = fc;
+        while (c != -1 && sh_d[base + c] != tok) c = sh_ns[base + c];
+      }
+      sh_nxt[t] = c;
     }
     __syncthreads();
     int cnt = 0;
     if (t < nseq) {
       const int b = s0 + t;
-      const int base = t * N;
-      int32_t *out = P.out_tokens + static_cast<size_t>(b) * N;
-      int32_t *path = P.path + static_cast<size_t>(b) * N;
-      int st = 0;
-      bool links_ok = true;
-      for (int i = 0; i < N; ++i) {
-        if (i > 0 && (sh_d[base + i] < 0 || sh_d[base + i] >= P.V)) st |= SPEC_ST_DRAFT_OOR;
-        const int fc = sh_fc[base + i], ns = sh_ns[base + i];
-        if ((fc != -1 && (fc <= i || fc >= N)) || (ns != -1 && (ns <= i || ns >= N))) links_ok = false;
-      }
+      const int sb = t * N;
+      const int st = sh_st[t];
+      const int rem = sh_cnt[t];
       int acc = 0;
-      const int rem = sh_rem[t];
-      if (!links_ok) {
-        st |= SPEC_ST_BAD_STATE;
-      } else if (rem != 0) {
+      if (!(st & SPEC_ST_BAD_STATE) && rem != 0) {
         int cur = 0;
-        path[0] = 0;
         while (true) {
-          const int tok = argmax_key_index(sh_row[base + cur]);
-          out[cnt++] = tok;
-          int c = sh_fc[base + cur];
-          while (c != -1 && sh_d[base + c] != tok) c = sh_ns[base + c];
+          const int tk = sh_tok[sb + cur];
+          const int c = sh_nxt[sb + cur];
+          sh_d[sb + cnt] = tk;                          // drafts and links are no longer read:
+          sh_fc[sb + cnt] = cur;                        // their rows now hold tokens and path
+          ++cnt;
           if (c != -1) ++acc;
-          if ((P.eos >= 0 && tok == P.eos) || cnt == rem || c == -1) break;
-          path[cnt] = c;
+          if ((P.eos >= 0 && tk == P.eos) || cnt == rem || c == -1) break;
           cur = c;
         }
       }
-      for (int i = cnt; i < N; ++i) {
-        out[i] = -1;
-        path[i] = -1;
-      }
+      sh_cnt[t] = cnt;
       P.accept_len[b] = acc;
       P.emit_count[b] = cnt;
       if (P.status) P.status[b] = st;
+    }
+    __syncthreads();
+    if (row) {
+      const bool kept = node < sh_cnt[seq];
+      P.out_tokens[r0 + t] = kept ? sh_d[t] : -1;
+      P.path[r0 + t] = kept ? sh_fc[t] : -1;
     }
     if (P.emit_offsets) {
       int total;

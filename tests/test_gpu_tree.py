@@ -130,6 +130,28 @@ def test_compaction_matches_oracle():
         assert np.array_equal(kv_bits(kv), oracle.compact_tree_slots(pre, E, paths, e))
 
 
+@pytest.mark.parametrize("L,B,H,D,N,dt", [(8, 2, 101, 8, 7, "f32"),      # heads split across workgroups, ragged
+                                           (1, 3, 3, 128, 256, "bf16"),   # longest paths: many passes
+                                           (2, 1, 1, 5, 33, "bf16")])     # 10-byte columns
+def test_compaction_shapes(L, B, H, D, N, dt):
+    rng = np.random.default_rng(L * 100 + N)
+    E = 3
+    C = E + N + 1
+    e = np.array([N, N // 2, 1][:B], np.int32)
+    paths = np.full((B, N), -1, np.int32)
+    for b in range(B):
+        rest = np.sort(rng.choice(np.arange(1, N), int(e[b]) - 1, replace=False)) if e[b] > 1 else []
+        paths[b, :e[b]] = np.concatenate([[0], rest])
+    if B > 1:
+        paths[1, :e[1]] = np.concatenate([[0], np.arange(N - int(e[1]) + 1, N)])    # skips to the far end
+    kv = _random_kv(rng, (L, 2, B, H, C, D), dt)
+    pre = kv_bits(kv)
+    note(f"compact shape L={L} B={B} H={H} D={D} N={N} {dt}")
+    st = host(dict(s=compact_tree(kv, N, E, paths, e)))["s"]
+    assert (st == 0).all()
+    assert np.array_equal(kv_bits(kv), oracle.compact_tree_slots(pre, E, paths, e))
+
+
 def test_compaction_rejects_bad_sequences_and_leaves_them():
     rng = np.random.default_rng(12)
     L, H, D, B, N, E = 1, 2, 64, 5, 6, 4
