@@ -76,6 +76,39 @@ struct DenseRow {
   const float *a, *b;
   bool resid;
   __device__ inline float at(int v) const { return resid ? fmaxf(a[v] - b[v], 0.0f) : a[v]; }
+  // The 16 values v0 .. v0 + 15 (0 past V); 16-byte loads when `vec` (16-byte
+  // aligned rows, v0 a multiple of 4) and the run is inside the row.
+  __device__ inline void load16(float (&x)[16], int v0, int V, bool vec) const {
+    if (vec && v0 + 16 <= V) {
+      float4 A[4], Bv[4];
+      const float4 *pa = reinterpret_cast<const float4 *>(a + v0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) A[u] = pa[u];
+      if (resid) {
+        const float4 *pb = reinterpret_cast<const float4 *>(b + v0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Bv[u] = pb[u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x[4 * u + 0] = fmaxf(A[u].x - Bv[u].x, 0.0f);
+          x[4 * u + 1] = fmaxf(A[u].y - Bv[u].y, 0.0f);
+          x[4 * u + 2] = fmaxf(A[u].z - Bv[u].z, 0.0f);
+          x[4 * u + 3] = fmaxf(A[u].w - Bv[u].w, 0.0f);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x[4 * u + 0] = A[u].x;
+          x[4 * u + 1] = A[u].y;
+          x[4 * u + 2] = A[u].z;
+          x[4 * u + 3] = A[u].w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = v0 + i < V ? at(v0 + i) : 0.0f;
+    }
+  }
 };
 
 template <bool BF16>
@@ -88,6 +121,46 @@ struct LogitRow {
   __device__ inline float at(int v) const {
     const float pa = proc_prob(logit_at<BF16>(a, v), sa, invT);
     return resid ? fmaxf(pa - proc_prob(logit_at<BF16>(b, v), sb, invT), 0.0f) : pa;
+  }
+  // 16 logits from v0 (a multiple of 8 for bf16, 4 for f32) as float32.
+  __device__ static inline void load_z(float (&z)[16], const void *row, int v0) {
+    if constexpr (BF16) {
+      const uint4 *pr = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(row) + v0);
+      const uint4 w0 = pr[0], w1 = pr[1];
+      const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        z[2 * i] = __uint_as_float(w[i] << 16);
+        z[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+      const float4 *pr = reinterpret_cast<const float4 *>(static_cast<const float *>(row) + v0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 f = pr[u];
+        z[4 * u + 0] = f.x;
+        z[4 * u + 1] = f.y;
+        z[4 * u + 2] = f.z;
+        z[4 * u + 3] = f.w;
+      }
+    }
+  }
+  // The 16 processed values v0 .. v0 + 15 (0 past V); 16-byte loads when
+  // `vec` (16-byte aligned rows) and the run is inside the row.
+  __device__ inline void load16(float (&x)[16], int v0, int V, bool vec) const {
+    if (vec && v0 + 16 <= V) {
+      float za[16], zb[16];
+      load_z(za, a, v0);
+      if (resid) load_z(zb, b, v0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pa = proc_prob(za[i], sa, invT);
+        x[i] = resid ? fmaxf(pa - proc_prob(zb[i], sb, invT), 0.0f) : pa;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = v0 + i < V ? at(v0 + i) : 0.0f;
+    }
   }
 };
 
@@ -148,47 +221,36 @@ __device__ inline double block_sum_d(double v, double *sh) {
   return s;
 }
 
-// Mass of chunk c of the row (fixed summation order).  Contains barriers.
+// Block-wide exclusive sum of one double per lane, in a fixed order (lane
+// order within a wave, then waves).  `sh` holds kWaves + 1 doubles; *total
+// receives the block total.  Contains barriers.
+__device__ inline double block_excl_scan_d(double v, double *sh, double *total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const double inc = wave_incl_scan(v);
+  if (lane == kWave - 1) sh[w] = inc;
+  __syncthreads();
+  double base = 0.0, tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < w) base += sh[i];
+    tot += sh[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + (inc - v);
+}
+
+static_assert(kEPT == 16, "a lane owns 16 consecutive entries of a chunk");
+
+// Mass of chunk c of the row: lane t sums its 16 consecutive entries in order,
+// then the lanes are added in a fixed tree.  Contains barriers.
 template <class RowT>
 __device__ inline double chunk_mass(const RowT &r, int c, int V, bool vec, double *sh) {
-  const int t = threadIdx.x;
-  const int lo = c * kChunk;
+  float x[kEPT];
+  r.load16(x, c * kChunk + threadIdx.x * kEPT, V, vec);
   double acc = 0.0;
-  if constexpr (RowT::kDense) {
-    if (vec) {
-      float4 av[kU], bv[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int v = lo + (t + u * kThreads) * 4;
-        if (v < V) {
-          av[u] = *reinterpret_cast<const float4 *>(r.a + v);
-          if (r.resid) bv[u] = *reinterpret_cast<const float4 *>(r.b + v);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int v = lo + (t + u * kThreads) * 4;
-        if (v < V) {
-          if (r.resid) {
-            acc += static_cast<double>(fmaxf(av[u].x - bv[u].x, 0.0f));
-            acc += static_cast<double>(fmaxf(av[u].y - bv[u].y, 0.0f));
-            acc += static_cast<double>(fmaxf(av[u].z - bv[u].z, 0.0f));
-            acc += static_cast<double>(fmaxf(av[u].w - bv[u].w, 0.0f));
-          } else {
-            acc += static_cast<double>(av[u].x);
-            acc += static_cast<double>(av[u].y);
-            acc += static_cast<double>(av[u].z);
-            acc += static_cast<double>(av[u].w);
-          }
-        }
-      }
-      return block_sum_d(acc, sh);
-    }
-  }
-  for (int i = 0; i < kChunk / kThreads; ++i) {
-    const int v = lo + t + i * kThreads;
-    if (v < V) acc += static_cast<double>(r.at(v));
-  }
+  for (int i = 0; i < kEPT; ++i) acc += static_cast<double>(x[i]);
   return block_sum_d(acc, sh);
 }
 
@@ -278,9 +340,10 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
   __shared__ int sh_last[kWaves];
   __shared__ double sh_dscan[kWaves + 1];
   __shared__ int sh_cs, sh_tok;
-  __shared__ double sh_base, sh_S;
+  __shared__ double sh_base;
 
   const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), w = t / kWave;
   const int k = P.k, kp1 = k + 1, V = P.V;
   if (static_cast<int>(blockIdx.x) == P.B) {     // emit offsets
     if (P.emit_offsets) block_offsets(P.emit_count, P.emit_offsets, P.B, sh_scan);
@@ -296,31 +359,30 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
   if (mode != MODE_NONE) {
     typename Src::RowT r = Src::row(P, b, jrow, mode == MODE_RESID);
     const bool vec = P.vec != 0;
-    for (int i = t; i < P.chunks; i += kThreads) sh_part[i] = P.partial[static_cast<size_t>(b) * P.chunks + i];
+    const int nc = P.chunks;
+    const int per = (nc + kThreads - 1) / kThreads;  // chunks per lane, consecutive
+    const int c0 = t * per;
+    for (int i = t; i < nc; i += kThreads) sh_part[i] = P.partial[static_cast<size_t>(b) * nc + i];
     __syncthreads();
-    if (t == 0) {
-      double s = 0.0;
-      for (int i = 0; i < P.chunks; ++i) s += sh_part[i];
-      sh_S = s;
-    }
-    __syncthreads();
-    S = sh_S;
+    // total mass and each lane's exclusive prefix over the chunk masses
+    double pre = 0.0;
+    auto scan_parts = [&]() {
+      double mine = 0.0;
+      for (int i = 0; i < per; ++i)
+        if (c0 + i < nc) mine += sh_part[c0 + i];
+      pre = block_excl_scan_d(mine, sh_dscan, &S);
+    };
+    scan_parts();
     if (isfinite(S) && !(S > 0.0)) {
       st |= SPEC_ST_RESID_ZERO;
       if (mode == MODE_RESID) {         // fall back to the target row p_j itself
         r.resid = false;
-        for (int i = 0; i < P.chunks; ++i) {
+        for (int i = 0; i < nc; ++i) {
           const double part = chunk_mass(r, i, V, vec, sh_red);
           if (t == 0) sh_part[i] = part;
         }
         __syncthreads();
-        if (t == 0) {
-          double s = 0.0;
-          for (int i = 0; i < P.chunks; ++i) s += sh_part[i];
-          sh_S = s;
-        }
-        __syncthreads();
-        S = sh_S;
+        scan_parts();
       }
     }
     if (!isfinite(S)) {
@@ -330,55 +392,65 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
       tok = 0;
     } else {
       const double T = static_cast<double>(P.u[static_cast<size_t>(b) * kp1 + k]) * S;
-      if (t == 0) {
-        double run = 0.0;
-        int cs = -1, last = -1;
-        for (int i = 0; i < P.chunks; ++i) {
-          if (sh_part[i] > 0.0) last = i;
-          if (cs < 0 && run + sh_part[i] > T) cs = i;
-          if (cs < 0) run += sh_part[i];
+      // the first chunk whose running mass exceeds T (else the last chunk with mass)
+      int cand = INT_MAX, last = -1;
+      {
+        double run = pre;
+        for (int i = 0; i < per; ++i) {
+          const int c = c0 + i;
+          if (c >= nc) break;
+          const double pc = sh_part[c];
+          if (pc > 0.0) last = c;
+          if (cand == INT_MAX && run + pc > T) cand = c;
+          run += pc;
         }
-        if (cs < 0) {
-          cs = last;
-          run = 0.0;
-          for (int i = 0; i < cs; ++i) run += sh_part[i];
-        }
-        sh_cs = cs;
-        sh_base = run;
       }
-      __syncthreads();
-      const int cs = sh_cs;
-      const double base = sh_base;
-      // in-chunk scan in index order: lane t owns kEPT consecutive elements
-      const int lo = cs * kChunk + t * kEPT;
-      double mine = 0.0;
-      for (int i = 0; i < kEPT; ++i)
-        if (lo + i < V) mine += static_cast<double>(r.at(lo + i));
-      const int lane = t & (kWave - 1), w = t / kWave;
-      double inc = mine;
-#pragma unroll
-      for (int dd = 1; dd < kWave; dd <<= 1) {
-        const double o = __shfl_up(inc, dd, kWave);
-        if (lane >= dd) inc += o;
-      }
-      if (lane == kWave - 1) sh_dscan[w] = inc;
-      __syncthreads();
-      double wpre = 0.0;
-      for (int i = 0; i < w; ++i) wpre += sh_dscan[i];
-      double run = base + (wpre + (inc - mine));
-      int cand = INT_MAX, lastpos = -1;
-      for (int i = 0; i < kEPT; ++i) {
-        const int v = lo + i;
-        if (v >= V) break;
-        const float rv = r.at(v);
-        if (rv > 0.0f) lastpos = v;
-        run += static_cast<double>(rv);
-        if (cand == INT_MAX && run > T) cand = v;
-      }
-      const int wc = wave_min(cand), wl = wave_max_i(lastpos);
+      const int wc = wave_min(cand), wl = wave_max_i(last);
       if (lane == 0) {
         sh_scan[w] = wc;
         sh_last[w] = wl;
+      }
+      __syncthreads();
+      if (t == 0) {
+        int best = INT_MAX, lp = -1;
+        for (int i = 0; i < kWaves; ++i) {
+          best = min(best, sh_scan[i]);
+          lp = max(lp, sh_last[i]);
+        }
+        sh_cs = best != INT_MAX ? best : lp;
+      }
+      __syncthreads();
+      const int cs = sh_cs;
+      if (cs >= c0 && cs < c0 + per) {                // the lane owning chunk cs: mass before it
+        double run = pre;
+        for (int c = c0; c < cs; ++c) run += sh_part[c];
+        sh_base = run;
+      }
+      __syncthreads();
+      const double base = sh_base;
+      // in-chunk scan in index order: lane t owns kEPT consecutive entries
+      const int lo = cs * kChunk + t * kEPT;
+      float x[kEPT];
+      r.load16(x, lo, V, vec);
+      double mine = 0.0;
+#pragma unroll
+      for (int i = 0; i < kEPT; ++i) mine += static_cast<double>(x[i]);
+      double ctot;
+      double run = base + block_excl_scan_d(mine, sh_dscan, &ctot);
+      int cpos = INT_MAX, lastpos = -1;
+#pragma unroll
+      for (int i = 0; i < kEPT; ++i) {
+        const int v = lo + i;
+        if (v < V) {
+          if (x[i] > 0.0f) lastpos = v;
+          run += static_cast<double>(x[i]);
+          if (cpos == INT_MAX && run > T) cpos = v;
+        }
+      }
+      const int wcp = wave_min(cpos), wlp = wave_max_i(lastpos);
+      if (lane == 0) {
+        sh_scan[w] = wcp;
+        sh_last[w] = wlp;
       }
       __syncthreads();
       if (t == 0) {
@@ -393,12 +465,13 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
       tok = sh_tok;
     }
   }
+  if (t < kp1) {                                      // accepted drafts, then the drawn token
+    int val = -1;
+    if (t < m) val = d[t];
+    else if (t == m && mode != MODE_NONE) val = tok;
+    P.out_tokens[static_cast<size_t>(b) * kp1 + t] = val;
+  }
   if (t == 0) {
-    int32_t *out = P.out_tokens + static_cast<size_t>(b) * kp1;
-    int cnt = 0;
-    for (int j = 0; j < m; ++j) out[cnt++] = d[j];
-    if (mode != MODE_NONE) out[cnt++] = tok;
-    for (int i = cnt; i < kp1; ++i) out[i] = -1;
     if (P.final_mass) P.final_mass[b] = mode != MODE_NONE ? S : 0.0;
     if (P.status) P.status[b] = st;
   }
@@ -547,7 +620,7 @@ extern "C" int spec_verify_sample_logits(const void *target_logits, const void *
   P.k = k;
   P.V = V;
   P.chunks = chunks;
-  P.vec = 0;
+  P.vec = (V % (dt == SPEC_BF16 ? 8 : 4) == 0) && aligned(target_logits, 16) && aligned(draft_logits, 16);
   P.eos = eos_id;
   P.remaining = remaining;
   P.accept_len = accept_len;
