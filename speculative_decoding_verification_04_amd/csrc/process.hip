@@ -37,6 +37,10 @@ constexpr int kProcU = 4;                      // 16-byte loads in flight per la
 constexpr double kFixScale = 1099511627776.0;  // 2^40 fixed-point units per unit weight
 constexpr int kCntShift = 54;                   // packed histogram word: count << 54 | weight
 constexpr unsigned long long kMassMask = (1ull << kCntShift) - 1;
+constexpr int kSliceThreads = 256;              // top-k slice kernel
+constexpr int kSliceLoads = 8;                  // 16-byte loads per lane: one slice
+constexpr int kSliceMaxS = (SPEC_PROC_MAX_V + kSliceThreads * kSliceLoads * 4 - 1) / (kSliceThreads * kSliceLoads * 4);
+constexpr int kCandCap = 256 * 64 * 2;          // candidate logits that fit in the statistics kernel's LDS
 
 struct ProcParams {
   const void *za, *zb;   // rows [0, rows_a) come from za, the rest from zb
@@ -44,6 +48,11 @@ struct ProcParams {
   ProcConfig cfg;
   ProcStats *stats;      // [rows]
   float *probs;          // [rows, V] or null
+  // top-k candidate lists from the slice kernel (null: read the whole row)
+  float *lists;          // [rows][kCandCap]: per slice, a segment of seg_cap
+  int *list_cnt;         // [rows][S]: entries per segment (more than seg_cap: overflow)
+  uint32_t *list_cut;    // [rows][S]: each slice listed every entry with a key at or above
+  int S, seg_cap;        // slices per row, entries per segment
 };
 
 template <bool BF16>
@@ -57,10 +66,10 @@ __device__ inline const void *proc_row(const ProcParams &P, int r) {
 // the first 16-byte boundary, 16-byte vectors (kProcU per lane per step, the
 // next step's loads issued before this step's entries are visited), a scalar
 // tail.  The order within a lane is fixed.
-template <bool BF16, class F>
+template <bool BF16, int NT = kProcThreads, class F>
 __device__ inline void row_foreach(const void *row, int V, F &&f) {
   constexpr int ELT = BF16 ? 2 : 4, VEC = 16 / ELT;
-  constexpr int kStep = kProcThreads * kProcU;
+  constexpr int kStep = NT * kProcU;
   const int t = threadIdx.x;
   const uintptr_t a = reinterpret_cast<uintptr_t>(row);
   const int head = min(V, static_cast<int>(((16u - (a & 15u)) & 15u) / ELT));
@@ -71,7 +80,7 @@ __device__ inline void row_foreach(const void *row, int V, F &&f) {
   uint4 cur[kProcU], nxt[kProcU];
 #pragma unroll
   for (int u = 0; u < kProcU; ++u) {
-    const int i = u * kProcThreads + t;
+    const int i = u * NT + t;
     if (i < nvec) cur[u] = body[i];
   }
   for (int i0 = 0; i0 < nvec; i0 += kStep) {
@@ -79,13 +88,13 @@ __device__ inline void row_foreach(const void *row, int V, F &&f) {
     if (more) {
 #pragma unroll
       for (int u = 0; u < kProcU; ++u) {
-        const int i = i0 + kStep + u * kProcThreads + t;
+        const int i = i0 + kStep + u * NT + t;
         if (i < nvec) nxt[u] = body[i];
       }
     }
 #pragma unroll
     for (int u = 0; u < kProcU; ++u) {
-      const int i = i0 + u * kProcThreads + t;
+      const int i = i0 + u * NT + t;
       if (i < nvec) {
         const uint32_t w[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
         const int v0 = head + i * VEC;
@@ -139,8 +148,8 @@ __device__ inline void fold_columns(const unsigned long long *lh, uint32_t *h_cn
   const int b = t >> 2, part = t & 3;          // 4 lanes per bucket, 16 columns each
   unsigned long long c = 0, m = 0;
 #pragma unroll
-  for (int i = 0; i < kWave / 4; ++i) {
-    const unsigned long long x = lh[b * kWave + part * (kWave / 4) + i];
+  for (int i = 0; i < kWave / 4; ++i) {        // columns visited in a bucket-rotated order: no bank conflicts
+    const unsigned long long x = lh[b * kWave + part * (kWave / 4) + ((i + b) & (kWave / 4 - 1))];
     c += x >> kCntShift;
     m += x & kMassMask;
   }
@@ -192,7 +201,29 @@ __device__ inline int block_max_int(int x, int *sh) {
   return r;
 }
 
-constexpr int kCandCap = 256 * kWave * 2;        // candidate logits that fit in the histogram's LDS
+static_assert(kCandCap == 256 * kWave * 2, "the candidate list reuses the histogram's LDS");
+
+// The float a (non-NaN) order key stands for; -0 comes back as +0, which is
+// equal to it in every comparison and weight.
+__device__ inline float f32_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Appends the lanes with `want` set, in lane order, at a counter in LDS: one
+// atomic per wave.  Every lane of the wave must call it; returns the lane's
+// slot (meaningful where `want`).
+__device__ inline int wave_append(bool want, int *counter) {
+  const unsigned long long mask = __ballot(want);
+  const int lane = threadIdx.x & (kWave - 1);
+  int base = 0;
+  if (mask != 0ull) {
+    const int leader = __ffsll(static_cast<long long>(mask)) - 1;
+    if (lane == leader) base = atomicAdd(counter, __popcll(mask));
+    base = __shfl(base, leader, kWave);
+  }
+  return base + __popcll(mask & ((1ull << lane) - 1ull));
+}
+
 
 template <bool BF16>
 __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) {
@@ -207,6 +238,9 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   __shared__ unsigned long long sh4[4];
   __shared__ int sh_i[kProcWaves];
   __shared__ unsigned long long sh_u[kProcWaves];
+  __shared__ int sh_seg[kSliceMaxS + 1];
+  __shared__ uint32_t sh_cutw[kSliceMaxS];
+  __shared__ bool sh_fast;
 
   static_assert(kProcThreads == 4 * 256, "fold_columns assigns 4 lanes per bucket");
   const int t = threadIdx.x;
@@ -222,15 +256,72 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   const unsigned long long one = 1ull << kCntShift;
   float *cand = reinterpret_cast<float *>(lh);
 
-  // ---- pass 1 over the row: maximum, and the first top-k digit histogram
-  clear_columns(lh);
-  __syncthreads();
+  // ---- the row's candidates: with top-k, the slice kernel's lists when every
+  //      slice's fit (their union holds every logit at or above the K-th
+  //      largest, and the largest); else pass 1 over the row: maximum, and the
+  //      first top-k digit histogram
+  bool fast = false;
+  int nfast = 0;
+  uint32_t cutmax = 0;
+  if (P.lists && topk) {
+    // segment offsets (prefix of the list lengths) and the largest slice cut
+    if (t < P.S) {
+      const int c = P.list_cnt[static_cast<size_t>(r) * P.S + t];
+      sh_seg[t] = c;
+      sh_cutw[t] = P.list_cut[static_cast<size_t>(r) * P.S + t];
+    }
+    __syncthreads();
+    if (t == 0) {
+      int off = 0;
+      uint32_t cm = 0;
+      bool ok = true;
+      for (int q = 0; q < P.S; ++q) {
+        const int c = sh_seg[q];
+        ok = ok && c <= P.seg_cap;
+        sh_seg[q] = off;
+        off += c;
+        cm = max(cm, sh_cutw[q]);
+      }
+      sh_seg[P.S] = off;
+      sh_fast = ok;
+      sh_cutw[0] = cm;
+      sh_n = 0;
+    }
+    __syncthreads();
+    fast = sh_fast;
+    cutmax = sh_cutw[0];
+  }
   float m = -INFINITY;
-  row_foreach<BF16>(row, V, [&](int, float z) {
-    m = fmaxf(m, z);
-    if (topk) atomicAdd(&lh[(f32_order_key(z) >> 24) * kWave + lane], one);
-  });
+  if (fast) {
+    // every slice's cut is at most the row's K-th largest key: entries below
+    // the largest cut cannot be kept.  One independent load per entry.
+    const int tot = sh_seg[P.S];
+    for (int g0 = 0; g0 < tot; g0 += kProcThreads) {   // same trip count in every lane
+      const int g = g0 + t;
+      float z = -INFINITY;
+      bool keep = false;
+      if (g < tot) {
+        int q = 0;
+        while (sh_seg[q + 1] <= g) ++q;
+        z = P.lists[static_cast<size_t>(r) * kCandCap + static_cast<size_t>(q) * P.seg_cap + (g - sh_seg[q])];
+        keep = f32_order_key(z) >= cutmax;
+      }
+      const int slot = wave_append(keep, &sh_n);
+      if (keep) {
+        cand[slot] = z;
+        m = fmaxf(m, z);
+      }
+    }
+  } else {
+    clear_columns(lh);
+    __syncthreads();
+    row_foreach<BF16>(row, V, [&](int, float z) {
+      m = fmaxf(m, z);
+      if (topk) atomicAdd(&lh[(f32_order_key(z) >> 24) * kWave + lane], one);
+    });
+  }
   const float zmax = block_max_f(m, sh_f);     // (contains barriers)
+  if (fast) nfast = sh_n;
   const bool topp_on = topp && zmax != -INFINITY;
 
   // Selection state.  Level-0 digits are chosen from whole-row histograms;
@@ -300,7 +391,9 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
 
   int ncand = V;
   uint32_t cutoff = 0;
-  if (topk) {
+  if (fast) {
+    // every top-k level, the first included, runs on the list below
+  } else if (topk) {
     fold_columns(lh, h_cnt, h_mass);
     ncand = select_k(24);
     cutoff = kprefix;
@@ -318,9 +411,9 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
     p_started = true;
     if (!p_dead) cutoff = pprefix;
   }
-  const bool listed = (topk || (topp_on && !p_dead)) && ncand <= kCandCap;
-  int n = 0;
-  if (listed) {
+  const bool listed = fast || ((topk || (topp_on && !p_dead)) && ncand <= kCandCap);
+  int n = nfast;
+  if (listed && !fast) {
     // pass over the row: copy every logit at or above the cutoff into LDS
     if (t == 0) sh_n = 0;
     __syncthreads();
@@ -376,7 +469,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   // ---- top-k: remaining digits
   uint32_t tau = 0;
   if (topk) {
-    for (int lvl = 1; lvl < kLevels; ++lvl) {
+    for (int lvl = fast ? 0 : 1; lvl < kLevels; ++lvl) {
       const int shift = 24 - 8 * lvl;
       const uint32_t pf = kprefix, pm = kmask;
       histogram(shift, false, [&](uint32_t key) { return (key & pm) == pf; });
@@ -431,6 +524,99 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   }
 }
 
+// Top-k candidates of one slice of a row (kSliceThreads * kSliceLoads 16-byte
+// vectors).  Each lane keeps its entries' order keys in registers and takes
+// their maximum; theta is the K-th largest of the 256 lane maxima.  At least K
+// entries (those maxima) are at or above theta, so theta is at most the
+// slice's K-th largest key, and the lanes list every entry at or above it.  A
+// logit at or above the row's K-th largest is among the K largest of its
+// slice, so the union of the slices' lists holds all of them, and no slice's
+// theta exceeds the row's K-th largest key.  A list that does not fit reports
+// its length; the statistics kernel then reads the row whole.  (K <= 256.)
+static_assert(kSliceThreads == 256 && (kSliceThreads & (kSliceThreads - 1)) == 0, "bitonic sort over the lanes");
+template <bool BF16>
+__global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P) {
+  constexpr int VEC = BF16 ? 8 : 4, EPL = kSliceLoads * VEC, SL = kSliceThreads * EPL;
+  __shared__ uint32_t sh_m[kSliceThreads];
+  __shared__ uint32_t sh_theta;
+  __shared__ int sh_n;
+  const int t = threadIdx.x;
+  const int r = blockIdx.x / P.S, s = blockIdx.x - r * P.S;
+  const int K = P.cfg.top_k;
+  const int v0 = s * SL;
+  const int n = min(P.V - v0, SL);
+  const unsigned char *base = static_cast<const unsigned char *>(proc_row<BF16>(P, r)) + static_cast<size_t>(v0) * (BF16 ? 2 : 4);
+  const bool vec = (reinterpret_cast<uintptr_t>(base) & 15u) == 0;
+  // keys: entry (u * kSliceThreads + t) * VEC + e; 0 marks an entry past the row
+  // (every real key is at least the key of -inf, 0x007FFFFF)
+  uint32_t key[EPL];
+#pragma unroll
+  for (int u = 0; u < kSliceLoads; ++u) {
+    const int i0 = (u * kSliceThreads + t) * VEC;
+    if (vec && i0 + VEC <= n) {
+      const uint4 q = reinterpret_cast<const uint4 *>(base)[u * kSliceThreads + t];
+      const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (BF16) {
+          key[u * VEC + 2 * c] = f32_order_key(__uint_as_float(wd[c] << 16));
+          key[u * VEC + 2 * c + 1] = f32_order_key(__uint_as_float(wd[c] & 0xFFFF0000u));
+        } else {
+          key[u * VEC + c] = f32_order_key(__uint_as_float(wd[c]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+        key[u * VEC + e] = i0 + e < n ? f32_order_key(logit_at<BF16>(base, i0 + e)) : 0u;
+    }
+  }
+  uint32_t ml = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) ml = max(ml, key[i]);
+  if (t == 0) sh_n = 0;
+  // bitonic sort of the 256 lane maxima, descending (strides below a wave by
+  // lane shuffles, the others through LDS); lane K - 1 then holds theta
+  uint32_t v = ml;
+#pragma unroll
+  for (int k = 2; k <= kSliceThreads; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      uint32_t o;
+      if (j >= kWave) {
+        sh_m[t] = v;
+        __syncthreads();
+        o = sh_m[t ^ j];
+        __syncthreads();
+      } else {
+        o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), j, kWave));
+      }
+      const bool desc = (t & k) == 0;        // this run is sorted descending
+      const bool low = (t & j) == 0;         // lower index of the pair
+      v = (desc == low) ? max(v, o) : min(v, o);
+    }
+  }
+  if (t == K - 1) sh_theta = v;
+  __syncthreads();
+  const uint32_t cut = max(sh_theta, 1u);    // a maximum of 0 (no entry) lists every entry
+  const int cap = P.seg_cap;
+  float *out = P.lists + static_cast<size_t>(r) * kCandCap + static_cast<size_t>(s) * cap;
+  if (ml >= cut) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      if (key[i] >= cut) {
+        const int pos = atomicAdd(&sh_n, 1);
+        if (pos < cap) out[pos] = f32_from_order_key(key[i]);
+      }
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    P.list_cnt[static_cast<size_t>(r) * P.S + s] = sh_n;
+    P.list_cut[static_cast<size_t>(r) * P.S + s] = sh_theta;
+  }
+}
+
 __global__ __launch_bounds__(256) void proc_export_kernel(const ProcStats *stats, int R, float *row_max,
                                                           float *row_threshold, double *row_mass) {
   const int r = blockIdx.x * 256 + threadIdx.x;
@@ -445,9 +631,15 @@ __global__ __launch_bounds__(256) void proc_export_kernel(const ProcStats *stats
 
 // Launches the statistics kernel over rows [0, rows); shared with the
 // stochastic verification from logits.
+size_t proc_list_bytes(int rows) {
+  return round_up(static_cast<size_t>(rows) * kCandCap * sizeof(float), 256) +
+         round_up(static_cast<size_t>(rows) * kSliceMaxS * sizeof(int), 256) +
+         round_up(static_cast<size_t>(rows) * kSliceMaxS * sizeof(uint32_t), 256);
+}
+
 int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int V, bool bf16,
                       float invT, int top_k, float top_p, ProcStats *stats, float *probs,
-                      hipStream_t s) {
+                      void *list_ws, hipStream_t s) {
   ProcParams P;
   P.za = za;
   P.zb = zb;
@@ -459,6 +651,26 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
   P.cfg.top_p = top_p;
   P.stats = stats;
   P.probs = probs;
+  P.lists = nullptr;
+  P.list_cnt = nullptr;
+  P.list_cut = nullptr;
+  const int slice = kSliceThreads * kSliceLoads * (bf16 ? 8 : 4);
+  P.S = (V + slice - 1) / slice;
+  P.seg_cap = kCandCap / P.S;
+  // top-k through the slice lists (the cut is the K-th largest of a slice's 256 lane maxima)
+  if (list_ws && top_k > 0 && top_k < V && top_k <= kSliceThreads && top_k <= P.seg_cap / 2) {
+    unsigned char *w = static_cast<unsigned char *>(list_ws);
+    const size_t nl = round_up(static_cast<size_t>(rows) * kCandCap * sizeof(float), 256);
+    const size_t nc = round_up(static_cast<size_t>(rows) * kSliceMaxS * sizeof(int), 256);
+    P.lists = reinterpret_cast<float *>(w);
+    P.list_cnt = reinterpret_cast<int *>(w + nl);
+    P.list_cut = reinterpret_cast<uint32_t *>(w + nl + nc);
+    const dim3 g(static_cast<unsigned>(rows * P.S));
+    if (bf16)
+      hipLaunchKernelGGL(proc_slice_kernel<true>, g, dim3(kSliceThreads), 0, s, P);
+    else
+      hipLaunchKernelGGL(proc_slice_kernel<false>, g, dim3(kSliceThreads), 0, s, P);
+  }
   if (bf16)
     hipLaunchKernelGGL(proc_stats_kernel<true>, dim3(static_cast<unsigned>(rows)), dim3(kProcThreads), 0, s, P);
   else
@@ -477,7 +689,7 @@ using namespace specv;
 
 extern "C" size_t spec_process_workspace_bytes(int R) {
   if (R < 1) return 0;
-  return round_up(static_cast<size_t>(R) * sizeof(ProcStats), 256);
+  return round_up(static_cast<size_t>(R) * sizeof(ProcStats), 256) + proc_list_bytes(R);
 }
 
 extern "C" int spec_process_logits(const void *logits, spec_dtype dt, int R, int V, float temperature,
@@ -505,9 +717,10 @@ extern "C" int spec_process_logits(const void *logits, spec_dtype dt, int R, int
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   ProcStats *stats = static_cast<ProcStats *>(ws);
+  void *lists = static_cast<unsigned char *>(ws) + round_up(static_cast<size_t>(R) * sizeof(ProcStats), 256);
   (void)hipGetLastError();
   launch_proc_stats(logits, logits, R, R, V, dt == SPEC_BF16, 1.0f / temperature, top_k, top_p, stats,
-                    probs, s);
+                    probs, lists, s);
   if (row_max || row_threshold || row_mass)
     hipLaunchKernelGGL(proc_export_kernel, dim3((R + 255) / 256), dim3(256), 0, s, stats, R, row_max,
                        row_threshold, row_mass);

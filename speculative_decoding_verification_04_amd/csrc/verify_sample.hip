@@ -556,7 +556,8 @@ extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t 
 // Workspace of the verification from logits: per-row statistics of the
 // B * (k+1) target and B * k draft rows, then the layout of spec_verify_sample.
 static size_t sample_logits_stats_bytes(int B, int k) {
-  return round_up(static_cast<size_t>(B) * (2 * k + 1) * sizeof(ProcStats), 256);
+  return round_up(static_cast<size_t>(B) * (2 * k + 1) * sizeof(ProcStats), 256) +
+         proc_list_bytes(B * (2 * k + 1));
 }
 
 extern "C" size_t spec_verify_sample_logits_workspace_bytes(int B, int k, int V) {
@@ -635,7 +636,8 @@ extern "C" int spec_verify_sample_logits(const void *target_logits, const void *
   const bool bf16 = dt == SPEC_BF16;
   (void)hipGetLastError();
   launch_proc_stats(target_logits, draft_logits, B * (k + 1), static_cast<int>(rows), V, bf16, P.invT,
-                    top_k, top_p, stats, nullptr, s);
+                    top_k, top_p, stats, nullptr,
+                    wb + round_up(static_cast<size_t>(rows) * sizeof(ProcStats), 256), s);
   const dim3 g1(static_cast<unsigned>(nblocks)), g2(static_cast<unsigned>(B) + 1u), blk(kThreads);
   if (bf16) {
     hipLaunchKernelGGL(sample_chunk_kernel<LogitSrc<true>>, g1, blk, 0, s, P);

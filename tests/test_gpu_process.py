@@ -95,6 +95,29 @@ def test_process_ties_and_special_rows(dtype):
     assert np.all(got["probs"][2] == 0.0) and got["row_mass"][2] == 0.0
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_process_topk_crowded_rows(dtype):
+    """Rows whose top bucket holds far more than K entries (all equal, a narrow
+    spread, half -inf): the per-slice candidate lists overflow and the row is
+    read whole; K near and above the list path's limit."""
+    rng = np.random.default_rng(13)
+    V = 60000
+    z = np.zeros((4, V), np.float32)
+    z[1] = rng.standard_normal(V).astype(np.float32) * 0.01
+    z[2, ::2] = -np.inf
+    z[2, 1::2] = 1.5
+    z[3] = rng.standard_normal(V).astype(np.float32) * 3.0
+    if dtype == "bf16":
+        dev_in = W.bf16_bits_from_f32(z)
+        zw = oracle.widen_bf16(dev_in)
+    else:
+        dev_in, zw = z, z
+    zd = logits_to_device(dev_in, dtype)
+    for T, K, P in [(1.0, 50, 1.0), (0.7, 50, 0.9), (1.0, 1024, 0.95), (1.0, 1025, 1.0), (0.8, 4000, 0.9)]:
+        note(f"process crowded {dtype} T={T} K={K} P={P}")
+        _check_rows(zw, host(process(zd, T, K, P)), T, K, P)
+
+
 def test_process_misaligned_rows():
     rng = np.random.default_rng(12)
     V = 1001                                                        # odd: bf16 rows start misaligned
