@@ -132,27 +132,42 @@ __device__ inline void commit_state(const RealignParams &P, int *sh, int &E, int
   M = mm;
 }
 
+// One plane: the moved range [E - n, E + e) shifted right by M - e columns,
+// walked from right to left in tiles.  The plane's own sequence is read first
+// and, when it can move, the first tile's loads are issued before the
+// batch-wide state (M, validity) is reduced: the source range does not depend
+// on M.  Loads are checked against this sequence's own values, so they stay in
+// bounds whatever the rest of the batch holds; nothing is stored unless the
+// whole batch is valid.
 template <int VB>
-__device__ inline void move_plane(const RealignParams &P, int p, int b, int E, int M) {
+__device__ inline void move_plane(const RealignParams &P, int p, int b, int *sh) {
   using VT = typename VecOf<VB>::T;
-  const int n = P.kv_len_in[b], e = kept_slots(P, b);
-  const int delta = M - e, len = n + e;
-  if (delta == 0 || len == 0) return;   // uniform in the workgroup: no barrier is skipped unevenly
-
+  const int E0 = P.end_col[0];
+  const int n = P.kv_len_in[b], e_in = P.emit_count[b];
+  const int e = min(e_in, P.slots);
+  // e == slots: this sequence kept the most any can, so it does not move
+  const bool may_move = E0 >= 0 && E0 <= P.C - P.slots && n >= 0 && n <= E0 && e_in >= 0 &&
+                        e_in <= P.k + 1 && e < P.slots && n + e > 0;
   const long long per_col = P.R / VB;                       // vectors per column
   VT *base = reinterpret_cast<VT *>(P.kv + static_cast<size_t>(p) * P.plane_bytes);
-  const long long lo = static_cast<long long>(E - n) * per_col;   // first source vector
-  const long long shift = static_cast<long long>(delta) * per_col;
+  const long long lo = static_cast<long long>(E0 - n) * per_col;   // first source vector
   constexpr int TV = kThreads * kTileVec;                    // vectors per tile
   const int t = threadIdx.x;
-  long long hi = lo + static_cast<long long>(len) * per_col; // one past the last source vector
+  long long hi = lo + static_cast<long long>(n + e) * per_col; // one past the last source vector
 
   VT cur[kTileVec], nxt[kTileVec];
+  if (may_move) {
 #pragma unroll
-  for (int u = 0; u < kTileVec; ++u) {
-    const long long i = hi - TV + u * kThreads + t;
-    if (i >= lo) cur[u] = stream_ld(base + i);
+    for (int u = 0; u < kTileVec; ++u) {
+      const long long i = hi - TV + u * kThreads + t;
+      if (i >= lo) cur[u] = stream_ld(base + i);
+    }
   }
+  int E, M;
+  bool ok;
+  commit_state(P, sh, E, M, ok);           // barriers: every lane of the workgroup gets here
+  if (!ok || !may_move || M == e) return;  // uniform in the workgroup
+  const long long shift = static_cast<long long>(M - e) * per_col;
   while (true) {
     const long long nhi = hi - TV;
     const bool more = nhi > lo;
@@ -185,11 +200,16 @@ __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
   __shared__ long long sh_bytes[kWaves];
   __shared__ uint32_t sh_reserve[kReserveWords];
   asm volatile("" ::"s"(sh_reserve));      // keep the reservation (it limits residency, holds no data)
+  const int blk = blockIdx.x;
+  const int t = threadIdx.x;
+  if (blk > P.B) {                         // one plane, address order: p = ((l * 2 + kv) * B + b) * H + h
+    const int p = blk - P.B - 1;
+    move_plane<VB>(P, p, (p / P.H) % P.B, sh);
+    return;
+  }
   int E, M;
   bool ok;
   commit_state(P, sh, E, M, ok);
-  const int blk = blockIdx.x;
-  const int t = threadIdx.x;
 
   if (blk < P.B) {                         // position ids and mask of one sequence
     if (!ok) return;
@@ -203,12 +223,6 @@ __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
       if (msk) msk[c] = in ? 1 : 0;
       if (pos) pos[c] = in ? c - start : 0;
     }
-    return;
-  }
-  if (blk > P.B) {                         // one plane, address order: p = ((l * 2 + kv) * B + b) * H + h
-    if (!ok) return;
-    const int p = blk - P.B - 1;
-    move_plane<VB>(P, p, (p / P.H) % P.B, E, M);
     return;
   }
   // scalar outputs
