@@ -380,7 +380,7 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
     zd = torch.from_numpy(g["zd"]).to(dev).to(torch.bfloat16)
     # drafting (outside the step): draw from the processed draft rows by inverse CDF
     qproc = torch.empty(zd.shape, dtype=torch.float32, device=dev)
-    wsp = sv.workspace(sv.spec_process_workspace_bytes(B * k), dev)
+    wsp = sv.workspace(sv.spec_process_workspace_bytes(B * k, V), dev)
     sv.spec_process_logits(zd, T, wsp, top_k=K, top_p=TP, probs=qproc)
     gen = torch.Generator(device=dev).manual_seed(7)
     ud = torch.rand(B, k, 1, device=dev, generator=gen, dtype=torch.float64)
@@ -405,6 +405,21 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
     out["sample_verify_logits"] = {"workload": f"stochastic verify from bf16 logits, B={B} k={k} V={V}, "
                                                f"T={T} top_k={K} top_p={TP}, 12 rotating logit copies",
                                    **_rates(t, th, nbytes), "rows_per_s": B * (k + 1) / t}
+    # the same call with top-p alone (no top-k): the slice path with exact row weights
+    iz2 = itertools.count()
+
+    def call2():
+        a, b = zz[next(iz2) % len(zz)]
+        sv.spec_verify_sample_logits(a, b, dl, ul, acc, emit, toks, wsl, temperature=T, top_k=0, top_p=TP,
+                                     emit_offsets=offs, final_mass=mass)
+
+    t2, th2 = _time_calls(torch, call2, 22)
+    m, e = acc.cpu().numpy(), emit.cpu().numpy()
+    redraw = sum(4 * V if (e[b] > m[b] and m[b] < k) else (2 * V if e[b] > m[b] else 0) for b in range(B))
+    nbytes = rows_read + redraw
+    out["sample_verify_logits_top_p"] = {"workload": f"stochastic verify from bf16 logits, B={B} k={k} V={V}, "
+                                                     f"T={T} top_p={TP} (no top-k), 12 rotating logit copies",
+                                         **_rates(t2, th2, nbytes), "rows_per_s": B * (k + 1) / t2}
     del zz
     # paged layout: the commit is a rollback of lengths and pages, no KV bytes move
     g3 = W.kv_geometry(3)

@@ -165,7 +165,7 @@ int spec_verify_sample(const float *p, const float *q, const int32_t *draft,
  *   row_max        [R] float32 out or NULL: max z
  *   row_threshold  [R] float32 out or NULL: the smallest kept logit
  *   row_mass       [R] float64 out or NULL: sum of the kept w
- *   ws             workspace of spec_process_workspace_bytes(R)
+ *   ws             workspace of spec_process_workspace_bytes(R, V)
  * Errors: SPEC_EINVAL for NULL logits or ws, R < 1, V < 1 or V >
  * SPEC_PROC_MAX_V, T not positive and finite, top_k < 0, top_p outside
  * (0, 1], misalignment or overlap; SPEC_EWORKSPACE.
@@ -179,7 +179,7 @@ int spec_verify_sample(const float *p, const float *q, const int32_t *draft,
  *   ws             workspace of spec_verify_sample_logits_workspace_bytes(B, k, V)
  * Errors: as spec_verify_sample, plus the processing errors above.
  * ------------------------------------------------------------------------ */
-size_t spec_process_workspace_bytes(int R);
+size_t spec_process_workspace_bytes(int R, int V);
 int spec_process_logits(const void *logits, spec_dtype dt, int R, int V, float temperature,
                         int top_k, float top_p, float *probs, float *row_max,
                         float *row_threshold, double *row_mass, void *ws, size_t ws_bytes,

@@ -111,8 +111,8 @@ def spec_verify_sample(p, q, draft, uniforms, accept_len, emit_count, out_tokens
     _check(code, "spec_verify_sample")
 
 
-def spec_process_workspace_bytes(R: int) -> int:
-    return int(library().spec_process_workspace_bytes(R))
+def spec_process_workspace_bytes(R: int, V: int) -> int:
+    return int(library().spec_process_workspace_bytes(R, V))
 
 
 def spec_verify_sample_logits_workspace_bytes(B: int, k: int, V: int) -> int:

@@ -20,7 +20,7 @@ PROTOTYPES = {
     "spec_verify_sample_workspace_bytes": (_SZ, [_I, _I, _I]),
     "spec_verify_sample": (_I, [_P, _P, _P, _P, _I, _I, _I, ctypes.c_int32, _P, _P, _P, _P, _P,
                                 _P, _P, _P, _SZ, _P]),
-    "spec_process_workspace_bytes": (_SZ, [_I]),
+    "spec_process_workspace_bytes": (_SZ, [_I, _I]),
     "spec_process_logits": (_I, [_P, _I, _I, _I, _F, _I, _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "spec_verify_sample_logits_workspace_bytes": (_SZ, [_I, _I, _I]),
     "spec_verify_sample_logits": (_I, [_P, _P, _I, _I, _I, _I, _F, _I, _F, _P, _P, ctypes.c_int32,

@@ -34,12 +34,12 @@ struct ProcStats {
 };
 
 // Statistics of rows [0, rows) (rows_a from za, the rest from zb) into stats;
-// list_ws (proc_list_bytes(rows), or null to always read whole rows) holds the
-// slice kernel's top-k candidate lists.
+// list_ws (proc_list_bytes(rows, V), or null to always read whole rows) holds
+// the slice kernels' candidate lists and per-slice sums.
 int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int V, bool bf16,
                       float invT, int top_k, float top_p, ProcStats *stats, float *probs,
                       void *list_ws, hipStream_t s);
-size_t proc_list_bytes(int rows);
+size_t proc_list_bytes(int rows, int V);
 bool proc_args_ok(float T, int top_k, float top_p, int V);
 
 struct ProcConfig {

@@ -41,6 +41,11 @@ constexpr int kSliceThreads = 256;              // top-k slice kernel
 constexpr int kSliceLoads = 8;                  // 16-byte loads per lane: one slice
 constexpr int kSliceMaxS = (SPEC_PROC_MAX_V + kSliceThreads * kSliceLoads * 4 - 1) / (kSliceThreads * kSliceLoads * 4);
 constexpr int kCandCap = 256 * 64 * 2;          // candidate logits that fit in the statistics kernel's LDS
+// Top-p without top-k: each slice lists its entries at or above its 128th
+// largest lane maximum (about 1% of the slice for Gaussian logits).  The
+// statistics kernel uses the union when it carries at least top_p of the row's
+// weight, which it checks exactly; else it reads the row.
+constexpr int kToppRank = 128;
 
 struct ProcParams {
   const void *za, *zb;   // rows [0, rows_a) come from za, the rest from zb
@@ -53,6 +58,11 @@ struct ProcParams {
   int *list_cnt;         // [rows][S]: entries per segment (more than seg_cap: overflow)
   uint32_t *list_cut;    // [rows][S]: each slice listed every entry with a key at or above
   int S, seg_cap;        // slices per row, entries per segment
+  int cut_rank;          // the slice kernel's cut: the cut_rank-th largest lane maximum
+  // rows without top-k: per slice, the key range and the fixed-point weight
+  // (null: read the whole row)
+  uint32_t *sl_max, *sl_min;        // [rows][S]
+  unsigned long long *sl_tot;       // [rows][S]
 };
 
 template <bool BF16>
@@ -263,7 +273,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   bool fast = false;
   int nfast = 0;
   uint32_t cutmax = 0;
-  if (P.lists && topk) {
+  if (P.lists && (topk || (P.sl_max != nullptr && topp))) {
     // segment offsets (prefix of the list lengths) and the largest slice cut
     if (t < P.S) {
       const int c = P.list_cnt[static_cast<size_t>(r) * P.S + t];
@@ -291,7 +301,14 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
     fast = sh_fast;
     cutmax = sh_cutw[0];
   }
+  // rows without top-k through the slice kernels: the maximum from the slices
+  const bool smode = P.sl_max != nullptr && !topk;
   float m = -INFINITY;
+  if (smode) {
+    uint32_t mk = 0;
+    for (int q = 0; q < P.S; ++q) mk = max(mk, P.sl_max[static_cast<size_t>(r) * P.S + q]);
+    m = f32_from_order_key(mk);
+  }
   if (fast) {
     // every slice's cut is at most the row's K-th largest key: entries below
     // the largest cut cannot be kept.  One independent load per entry.
@@ -312,7 +329,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
         m = fmaxf(m, z);
       }
     }
-  } else {
+  } else if (!smode) {
     clear_columns(lh);
     __syncthreads();
     row_foreach<BF16>(row, V, [&](int, float z) {
@@ -355,7 +372,8 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   };
   // Picks the top-p bucket at `shift` from h_cnt / h_mass (level 0 also fixes
   // the threshold top_p * total); returns the count in the bucket and above.
-  auto select_p = [&](int shift, bool first) -> int {
+  unsigned long long hist_total = 0;          // level 0: the weight the histogram saw
+  auto select_p = [&](int shift, bool first, unsigned long long row_total) -> int {
     const int tb = 255 - t;
     const unsigned long long mw = t < 256 ? h_mass[tb] : 0ull;
     const unsigned long long cw = t < 256 ? h_cnt[tb] : 0ull;
@@ -364,7 +382,8 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
     if (first) {
       if (t == 255) sh_tot = S + mw;
       __syncthreads();
-      thr = static_cast<double>(P.cfg.top_p) * static_cast<double>(sh_tot);
+      hist_total = sh_tot;
+      thr = static_cast<double>(P.cfg.top_p) * static_cast<double>(row_total ? row_total : hist_total);
     }
     const bool ok = t < 256 && cw > 0 && static_cast<double>(above + S) < thr;
     const int win = block_max_int(ok ? t : -1, sh_i);   // largest lane = lowest bucket
@@ -391,29 +410,62 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
 
   int ncand = V;
   uint32_t cutoff = 0;
-  if (fast) {
+  bool use_list = fast && topk;                // every level runs on the slice lists
+  if (fast && topk) {
     // every top-k level, the first included, runs on the list below
   } else if (topk) {
     fold_columns(lh, h_cnt, h_mass);
     ncand = select_k(24);
     cutoff = kprefix;
   } else if (topp_on) {
-    // pass 2 over the row: first top-p digit histogram (counts and weights)
-    clear_columns(lh);
-    __syncthreads();
-    row_foreach<BF16>(row, V, [&](int, float z) {
-      const uint32_t key = f32_order_key(z);
-      atomicAdd(&lh[(key >> 24) * kWave + lane], one + fixed_weight(proc_weight(z, zmax, invT)));
-    });
-    __syncthreads();
-    fold_columns(lh, h_cnt, h_mass);
-    ncand = select_p(24, true);
-    p_started = true;
-    if (!p_dead) cutoff = pprefix;
+    if (fast) {
+      // slice mode: the union of the lists holds every logit at or above the
+      // largest slice cut.  Level 0 from the union's histogram, with the
+      // threshold from the row's exact weight; valid when the union itself
+      // weighs at least top_p of the row (then no logit outside it is kept).
+      unsigned long long row_total = 0;
+      for (int q = 0; q < P.S; ++q) row_total += P.sl_tot[static_cast<size_t>(r) * P.S + q];
+      if (t < 256) {
+        h_cnt[t] = 0u;
+        h_mass[t] = 0ull;
+      }
+      __syncthreads();
+      for (int i = t; i < nfast; i += kProcThreads) {
+        const float z = cand[i];
+        const uint32_t key = f32_order_key(z);
+        atomicAdd(&h_cnt[key >> 24], 1u);
+        atomicAdd(&h_mass[key >> 24], fixed_weight(proc_weight(z, zmax, invT)));
+      }
+      __syncthreads();
+      ncand = select_p(24, true, row_total);
+      if (!p_dead && static_cast<double>(hist_total) >= thr) {
+        use_list = true;
+        p_started = true;
+        cutoff = pprefix;
+      } else {                                   // read the row after all
+        p_dead = false;
+        pprefix = pmask = 0u;
+        above = 0ull;
+      }
+    }
+    if (!use_list) {
+      // pass 2 over the row: first top-p digit histogram (counts and weights)
+      clear_columns(lh);
+      __syncthreads();
+      row_foreach<BF16>(row, V, [&](int, float z) {
+        const uint32_t key = f32_order_key(z);
+        atomicAdd(&lh[(key >> 24) * kWave + lane], one + fixed_weight(proc_weight(z, zmax, invT)));
+      });
+      __syncthreads();
+      fold_columns(lh, h_cnt, h_mass);
+      ncand = select_p(24, true, 0ull);
+      p_started = true;
+      if (!p_dead) cutoff = pprefix;
+    }
   }
-  const bool listed = fast || ((topk || (topp_on && !p_dead)) && ncand <= kCandCap);
-  int n = nfast;
-  if (listed && !fast) {
+  const bool listed = use_list || ((topk || (topp_on && !p_dead)) && ncand <= kCandCap);
+  int n = use_list ? nfast : 0;
+  if (listed && !use_list) {
     // pass over the row: copy every logit at or above the cutoff into LDS
     if (t == 0) sh_n = 0;
     __syncthreads();
@@ -469,7 +521,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   // ---- top-k: remaining digits
   uint32_t tau = 0;
   if (topk) {
-    for (int lvl = fast ? 0 : 1; lvl < kLevels; ++lvl) {
+    for (int lvl = use_list ? 0 : 1; lvl < kLevels; ++lvl) {
       const int shift = 24 - 8 * lvl;
       const uint32_t pf = kprefix, pm = kmask;
       histogram(shift, false, [&](uint32_t key) { return (key & pm) == pf; });
@@ -485,7 +537,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
       const int shift = 24 - 8 * lvl;
       const uint32_t pf = pprefix, pm = pmask, tk = tau;
       histogram(shift, true, [&](uint32_t key) { return key >= tk && (key & pm) == pf; });
-      select_p(shift, lvl == 0);
+      select_p(shift, lvl == 0, 0ull);
     }
     if (!p_dead) theta = pprefix;
   }
@@ -494,12 +546,22 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   //      order gives the same bits) and the smallest kept logit
   unsigned long long acc = 0;
   float zlo = INFINITY;
-  each([&](float z) {
-    if (f32_order_key(z) >= theta) {
-      acc += fixed_weight(proc_weight(z, zmax, invT));
-      zlo = fminf(zlo, z);
+  if (smode && theta == 0u) {
+    // every entry is kept: the slices' weights and smallest keys
+    if (t == 0) {
+      for (int q = 0; q < P.S; ++q) {
+        acc += P.sl_tot[static_cast<size_t>(r) * P.S + q];
+        zlo = fminf(zlo, f32_from_order_key(P.sl_min[static_cast<size_t>(r) * P.S + q]));
+      }
     }
-  });
+  } else {
+    each([&](float z) {
+      if (f32_order_key(z) >= theta) {
+        acc += fixed_weight(proc_weight(z, zmax, invT));
+        zlo = fminf(zlo, z);
+      }
+    });
+  }
   {
     acc = wave_sum_u64(acc);
     if (lane == 0) sh_u[t / kWave] = acc;
@@ -524,32 +586,18 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   }
 }
 
-// Top-k candidates of one slice of a row (kSliceThreads * kSliceLoads 16-byte
-// vectors).  Each lane keeps its entries' order keys in registers and takes
-// their maximum; theta is the K-th largest of the 256 lane maxima.  At least K
-// entries (those maxima) are at or above theta, so theta is at most the
-// slice's K-th largest key, and the lanes list every entry at or above it.  A
-// logit at or above the row's K-th largest is among the K largest of its
-// slice, so the union of the slices' lists holds all of them, and no slice's
-// theta exceeds the row's K-th largest key.  A list that does not fit reports
-// its length; the statistics kernel then reads the row whole.  (K <= 256.)
-static_assert(kSliceThreads == 256 && (kSliceThreads & (kSliceThreads - 1)) == 0, "bitonic sort over the lanes");
+// The order keys of slice s of row r (kSliceThreads * kSliceLoads 16-byte
+// vectors): lane t holds entries (u * kSliceThreads + t) * VEC + e.  0 marks
+// an entry past the row (every real key is at least the key of -inf,
+// 0x007FFFFF).  16-byte loads when the slice is aligned, else scalar loads.
 template <bool BF16>
-__global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P) {
-  constexpr int VEC = BF16 ? 8 : 4, EPL = kSliceLoads * VEC, SL = kSliceThreads * EPL;
-  __shared__ uint32_t sh_m[kSliceThreads];
-  __shared__ uint32_t sh_theta;
-  __shared__ int sh_n;
+__device__ inline void slice_keys(const ProcParams &P, int r, int s, uint32_t (&key)[kSliceLoads * (BF16 ? 8 : 4)]) {
+  constexpr int VEC = BF16 ? 8 : 4, SL = kSliceThreads * kSliceLoads * VEC;
   const int t = threadIdx.x;
-  const int r = blockIdx.x / P.S, s = blockIdx.x - r * P.S;
-  const int K = P.cfg.top_k;
   const int v0 = s * SL;
   const int n = min(P.V - v0, SL);
   const unsigned char *base = static_cast<const unsigned char *>(proc_row<BF16>(P, r)) + static_cast<size_t>(v0) * (BF16 ? 2 : 4);
   const bool vec = (reinterpret_cast<uintptr_t>(base) & 15u) == 0;
-  // keys: entry (u * kSliceThreads + t) * VEC + e; 0 marks an entry past the row
-  // (every real key is at least the key of -inf, 0x007FFFFF)
-  uint32_t key[EPL];
 #pragma unroll
   for (int u = 0; u < kSliceLoads; ++u) {
     const int i0 = (u * kSliceThreads + t) * VEC;
@@ -571,6 +619,29 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P)
         key[u * VEC + e] = i0 + e < n ? f32_order_key(logit_at<BF16>(base, i0 + e)) : 0u;
     }
   }
+}
+
+// Top-k candidates of one slice of a row (kSliceThreads * kSliceLoads 16-byte
+// vectors).  Each lane keeps its entries' order keys in registers and takes
+// their maximum; theta is the K-th largest of the 256 lane maxima.  At least K
+// entries (those maxima) are at or above theta, so theta is at most the
+// slice's K-th largest key, and the lanes list every entry at or above it.  A
+// logit at or above the row's K-th largest is among the K largest of its
+// slice, so the union of the slices' lists holds all of them, and no slice's
+// theta exceeds the row's K-th largest key.  A list that does not fit reports
+// its length; the statistics kernel then reads the row whole.  (K <= 256.)
+static_assert(kSliceThreads == 256 && (kSliceThreads & (kSliceThreads - 1)) == 0, "bitonic sort over the lanes");
+template <bool BF16>
+__global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P) {
+  constexpr int EPL = kSliceLoads * (BF16 ? 8 : 4);
+  __shared__ uint32_t sh_m[kSliceThreads];
+  __shared__ uint32_t sh_theta;
+  __shared__ int sh_n;
+  const int t = threadIdx.x;
+  const int r = blockIdx.x / P.S, s = blockIdx.x - r * P.S;
+  const int K = P.cut_rank;
+  uint32_t key[EPL];
+  slice_keys<BF16>(P, r, s, key);
   uint32_t ml = 0;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) ml = max(ml, key[i]);
@@ -597,6 +668,7 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P)
     }
   }
   if (t == K - 1) sh_theta = v;
+  if (t == 0 && P.sl_max) P.sl_max[static_cast<size_t>(r) * P.S + s] = v;   // the slice's largest key
   __syncthreads();
   const uint32_t cut = max(sh_theta, 1u);    // a maximum of 0 (no entry) lists every entry
   const int cap = P.seg_cap;
@@ -617,6 +689,80 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P)
   }
 }
 
+__device__ inline uint32_t wave_max_u(uint32_t v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, kWave)));
+  return v;
+}
+__device__ inline uint32_t wave_min_u(uint32_t v) {
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, kWave)));
+  return v;
+}
+
+// Rows without top-k or top-p, step 1: the largest key of each slice.
+template <bool BF16>
+__global__ __launch_bounds__(kSliceThreads) void proc_slrange_kernel(ProcParams P) {
+  constexpr int EPL = kSliceLoads * (BF16 ? 8 : 4), NW = kSliceThreads / kWave;
+  __shared__ uint32_t sh_hi[NW];
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+  const int r = blockIdx.x / P.S, s = blockIdx.x - r * P.S;
+  uint32_t key[EPL];
+  slice_keys<BF16>(P, r, s, key);
+  uint32_t hi = 0u;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) hi = max(hi, key[i]);
+  hi = wave_max_u(hi);
+  if (lane == 0) sh_hi[w] = hi;
+  __syncthreads();
+  if (t == 0) {
+    for (int i = 0; i < NW; ++i) hi = max(hi, sh_hi[i]);
+    P.sl_max[static_cast<size_t>(r) * P.S + s] = hi;
+  }
+}
+
+// Rows without top-k, step 2: the row maximum from the slices' maxima, then
+// each slice's fixed-point weight (an exact integer sum) and smallest key.
+template <bool BF16>
+__global__ __launch_bounds__(kSliceThreads) void proc_slmass_kernel(ProcParams P) {
+  constexpr int EPL = kSliceLoads * (BF16 ? 8 : 4), NW = kSliceThreads / kWave;
+  __shared__ unsigned long long sh_t[NW];
+  __shared__ uint32_t sh_lo[NW];
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+  const int r = blockIdx.x / P.S, s = blockIdx.x - r * P.S;
+  uint32_t mk = 0u;
+  for (int q = 0; q < P.S; ++q) mk = max(mk, P.sl_max[static_cast<size_t>(r) * P.S + q]);
+  const float zmax = f32_from_order_key(mk);
+  const float invT = P.cfg.invT;
+  uint32_t key[EPL];
+  slice_keys<BF16>(P, r, s, key);
+  unsigned long long tot = 0ull;
+  uint32_t lo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    if (key[i] != 0u) {
+      tot += fixed_weight(proc_weight(f32_from_order_key(key[i]), zmax, invT));
+      lo = min(lo, key[i]);
+    }
+  }
+  tot = wave_sum_u64(tot);
+  lo = wave_min_u(lo);
+  if (lane == 0) {
+    sh_t[w] = tot;
+    sh_lo[w] = lo;
+  }
+  __syncthreads();
+  if (t == 0) {
+    unsigned long long a = 0ull;
+    for (int i = 0; i < NW; ++i) {
+      a += sh_t[i];
+      lo = min(lo, sh_lo[i]);
+    }
+    P.sl_tot[static_cast<size_t>(r) * P.S + s] = a;
+    P.sl_min[static_cast<size_t>(r) * P.S + s] = lo;
+  }
+}
+
 __global__ __launch_bounds__(256) void proc_export_kernel(const ProcStats *stats, int R, float *row_max,
                                                           float *row_threshold, double *row_mass) {
   const int r = blockIdx.x * 256 + threadIdx.x;
@@ -631,11 +777,26 @@ __global__ __launch_bounds__(256) void proc_export_kernel(const ProcStats *stats
 
 // Launches the statistics kernel over rows [0, rows); shared with the
 // stochastic verification from logits.
-size_t proc_list_bytes(int rows) {
-  return round_up(static_cast<size_t>(rows) * kCandCap * sizeof(float), 256) +
-         round_up(static_cast<size_t>(rows) * kSliceMaxS * sizeof(int), 256) +
-         round_up(static_cast<size_t>(rows) * kSliceMaxS * sizeof(uint32_t), 256);
+// Workspace after the row statistics: candidate lists, then the per-slice
+// arrays, sized for the larger slice count (float32 slices of 8192 logits).
+struct ProcWs {
+  size_t lists, cnt, cut, smax, smin, stot, total;
+};
+static ProcWs proc_ws_layout(int rows, int V) {
+  const size_t R = static_cast<size_t>(rows);
+  const size_t S = (static_cast<size_t>(V) + kSliceThreads * kSliceLoads * 4 - 1) / (kSliceThreads * kSliceLoads * 4);
+  ProcWs L;
+  L.lists = 0;
+  L.cnt = L.lists + round_up(R * kCandCap * sizeof(float), 256);
+  L.cut = L.cnt + round_up(R * S * sizeof(int), 256);
+  L.smax = L.cut + round_up(R * S * sizeof(uint32_t), 256);
+  L.smin = L.smax + round_up(R * S * sizeof(uint32_t), 256);
+  L.stot = L.smin + round_up(R * S * sizeof(uint32_t), 256);
+  L.total = L.stot + round_up(R * S * sizeof(unsigned long long), 256);
+  return L;
 }
+
+size_t proc_list_bytes(int rows, int V) { return proc_ws_layout(rows, V).total; }
 
 int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int V, bool bf16,
                       float invT, int top_k, float top_p, ProcStats *stats, float *probs,
@@ -654,22 +815,48 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
   P.lists = nullptr;
   P.list_cnt = nullptr;
   P.list_cut = nullptr;
+  P.sl_max = P.sl_min = nullptr;
+  P.sl_tot = nullptr;
   const int slice = kSliceThreads * kSliceLoads * (bf16 ? 8 : 4);
   P.S = (V + slice - 1) / slice;
   P.seg_cap = kCandCap / P.S;
-  // top-k through the slice lists (the cut is the K-th largest of a slice's 256 lane maxima)
-  if (list_ws && top_k > 0 && top_k < V && top_k <= kSliceThreads && top_k <= P.seg_cap / 2) {
+  P.cut_rank = 0;
+  if (list_ws) {
+    const ProcWs L = proc_ws_layout(rows, V);
     unsigned char *w = static_cast<unsigned char *>(list_ws);
-    const size_t nl = round_up(static_cast<size_t>(rows) * kCandCap * sizeof(float), 256);
-    const size_t nc = round_up(static_cast<size_t>(rows) * kSliceMaxS * sizeof(int), 256);
-    P.lists = reinterpret_cast<float *>(w);
-    P.list_cnt = reinterpret_cast<int *>(w + nl);
-    P.list_cut = reinterpret_cast<uint32_t *>(w + nl + nc);
-    const dim3 g(static_cast<unsigned>(rows * P.S));
-    if (bf16)
-      hipLaunchKernelGGL(proc_slice_kernel<true>, g, dim3(kSliceThreads), 0, s, P);
-    else
-      hipLaunchKernelGGL(proc_slice_kernel<false>, g, dim3(kSliceThreads), 0, s, P);
+    const dim3 g(static_cast<unsigned>(rows * P.S)), blk(kSliceThreads);
+    auto lists = [&](int rank) {
+      P.lists = reinterpret_cast<float *>(w + L.lists);
+      P.list_cnt = reinterpret_cast<int *>(w + L.cnt);
+      P.list_cut = reinterpret_cast<uint32_t *>(w + L.cut);
+      P.cut_rank = rank;
+      if (bf16)
+        hipLaunchKernelGGL(proc_slice_kernel<true>, g, blk, 0, s, P);
+      else
+        hipLaunchKernelGGL(proc_slice_kernel<false>, g, blk, 0, s, P);
+    };
+    if (top_k > 0 && top_k < V) {
+      // top-k through the slice lists (the cut is the K-th largest of a slice's 256 lane maxima)
+      if (top_k <= kSliceThreads && top_k <= P.seg_cap / 2) lists(top_k);
+    } else {
+      // no top-k: slice maxima (with top-p: the lists cut at the kToppRank-th
+      // largest lane maximum, which also give them), then slice weights and
+      // minima
+      P.sl_max = reinterpret_cast<uint32_t *>(w + L.smax);
+      P.sl_min = reinterpret_cast<uint32_t *>(w + L.smin);
+      P.sl_tot = reinterpret_cast<unsigned long long *>(w + L.stot);
+      if (top_p < 1.0f && kToppRank <= P.seg_cap / 2) {
+        lists(kToppRank);
+      } else if (bf16) {
+        hipLaunchKernelGGL(proc_slrange_kernel<true>, g, blk, 0, s, P);
+      } else {
+        hipLaunchKernelGGL(proc_slrange_kernel<false>, g, blk, 0, s, P);
+      }
+      if (bf16)
+        hipLaunchKernelGGL(proc_slmass_kernel<true>, g, blk, 0, s, P);
+      else
+        hipLaunchKernelGGL(proc_slmass_kernel<false>, g, blk, 0, s, P);
+    }
   }
   if (bf16)
     hipLaunchKernelGGL(proc_stats_kernel<true>, dim3(static_cast<unsigned>(rows)), dim3(kProcThreads), 0, s, P);
@@ -687,9 +874,9 @@ bool proc_args_ok(float T, int top_k, float top_p, int V) {
 
 using namespace specv;
 
-extern "C" size_t spec_process_workspace_bytes(int R) {
-  if (R < 1) return 0;
-  return round_up(static_cast<size_t>(R) * sizeof(ProcStats), 256) + proc_list_bytes(R);
+extern "C" size_t spec_process_workspace_bytes(int R, int V) {
+  if (R < 1 || V < 1 || V > SPEC_PROC_MAX_V) return 0;
+  return round_up(static_cast<size_t>(R) * sizeof(ProcStats), 256) + proc_list_bytes(R, V);
 }
 
 extern "C" int spec_process_logits(const void *logits, spec_dtype dt, int R, int V, float temperature,
@@ -701,7 +888,7 @@ extern "C" int spec_process_logits(const void *logits, spec_dtype dt, int R, int
   if (R < 1 || !proc_args_ok(temperature, top_k, top_p, V)) return SPEC_EINVAL;
   const size_t elt = dt == SPEC_BF16 ? 2 : 4;
   if (!aligned(logits, elt)) return SPEC_EINVAL;
-  const size_t need = spec_process_workspace_bytes(R);
+  const size_t need = spec_process_workspace_bytes(R, V);
   if (ws_bytes < need || !aligned(ws, 256)) return SPEC_EWORKSPACE;
   const size_t nz = static_cast<size_t>(R) * V * elt;
   const void *ins[] = {logits, ws};

@@ -555,14 +555,14 @@ extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t 
 
 // Workspace of the verification from logits: per-row statistics of the
 // B * (k+1) target and B * k draft rows, then the layout of spec_verify_sample.
-static size_t sample_logits_stats_bytes(int B, int k) {
+static size_t sample_logits_stats_bytes(int B, int k, int V) {
   return round_up(static_cast<size_t>(B) * (2 * k + 1) * sizeof(ProcStats), 256) +
-         proc_list_bytes(B * (2 * k + 1));
+         proc_list_bytes(B * (2 * k + 1), V);
 }
 
 extern "C" size_t spec_verify_sample_logits_workspace_bytes(int B, int k, int V) {
   if (B < 1 || k < 1 || V < 1 || k > SPEC_MAX_K || V > SPEC_PROC_MAX_V || sample_chunks(V) > kMaxChunks) return 0;
-  return sample_logits_stats_bytes(B, k) + sample_ws_layout(B, sample_chunks(V)).total;
+  return sample_logits_stats_bytes(B, k, V) + sample_ws_layout(B, sample_chunks(V)).total;
 }
 
 extern "C" int spec_verify_sample_logits(const void *target_logits, const void *draft_logits,
@@ -587,7 +587,7 @@ extern "C" int spec_verify_sample_logits(const void *target_logits, const void *
   const long long nblocks = static_cast<long long>(B) * chunks;
   const long long rows = static_cast<long long>(B) * (2 * k + 1);
   if (nblocks >= INT32_MAX || rows >= INT32_MAX || B >= INT32_MAX - 1) return SPEC_EINVAL;
-  const size_t stats_bytes = sample_logits_stats_bytes(B, k);
+  const size_t stats_bytes = sample_logits_stats_bytes(B, k, V);
   const SampleWs lay = sample_ws_layout(B, chunks);
   if (ws_bytes < stats_bytes + lay.total || !aligned(ws, 256)) return SPEC_EWORKSPACE;
 

@@ -128,7 +128,7 @@ def process(logits_dev, T, top_k=0, top_p=1.0, probs=True, ws_key=None):
                row_mass=torch.empty(R, dtype=torch.float64, device=DEV))
     if probs:
         out["probs"] = torch.empty(logits_dev.shape, dtype=torch.float32, device=DEV)
-    w = ws(sv.spec_process_workspace_bytes(R), ws_key)
+    w = ws(sv.spec_process_workspace_bytes(R, V), ws_key)
     sv.spec_process_logits(logits_dev, T, w, top_k=top_k, top_p=top_p, probs=out.get("probs"),
                            row_max=out["row_max"], row_threshold=out["row_threshold"],
                            row_mass=out["row_mass"])

@@ -59,8 +59,9 @@ def test_workspace_queries():
     b = sv.spec_verify_sample_workspace_bytes(8, 4, 151936)
     assert b > 8 * 8 and b % 256 == 0
     assert sv.spec_verify_sample_workspace_bytes(8, 4, 1 << 30) == 0   # too many chunks
-    c = sv.spec_process_workspace_bytes(72)
-    assert c >= 72 * 16 and c % 256 == 0 and sv.spec_process_workspace_bytes(0) == 0
+    c = sv.spec_process_workspace_bytes(72, 151936)
+    assert c >= 72 * 16 and c % 256 == 0 and sv.spec_process_workspace_bytes(0, 100) == 0
+    assert sv.spec_process_workspace_bytes(4, 0) == 0 and sv.spec_process_workspace_bytes(4, sv.SPEC_PROC_MAX_V + 1) == 0
     d = sv.spec_verify_sample_logits_workspace_bytes(8, 4, 151936)
     assert d > b and d % 256 == 0
     assert sv.spec_verify_sample_logits_workspace_bytes(8, 4, sv.SPEC_PROC_MAX_V + 1) == 0

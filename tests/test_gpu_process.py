@@ -113,7 +113,8 @@ def test_process_topk_crowded_rows(dtype):
     else:
         dev_in, zw = z, z
     zd = logits_to_device(dev_in, dtype)
-    for T, K, P in [(1.0, 50, 1.0), (0.7, 50, 0.9), (1.0, 1024, 0.95), (1.0, 1025, 1.0), (0.8, 4000, 0.9)]:
+    for T, K, P in [(1.0, 50, 1.0), (0.7, 50, 0.9), (1.0, 1024, 0.95), (1.0, 1025, 1.0), (0.8, 4000, 0.9),
+                    (1.0, 0, 0.9), (0.7, 0, 1.0), (2.0, 0, 0.3)]:
         note(f"process crowded {dtype} T={T} K={K} P={P}")
         _check_rows(zw, host(process(zd, T, K, P)), T, K, P)
 
@@ -125,8 +126,9 @@ def test_process_misaligned_rows():
     buf = torch.empty(bits.size + 1, dtype=torch.int16, device=DEV)
     buf[1:].copy_(torch.from_numpy(bits.view(np.int16).reshape(-1)).to(DEV))
     zd = buf[1:].view(torch.bfloat16).view(5, V)
-    note("process misaligned bf16")
-    _check_rows(zw, host(process(zd, 0.8, 20, 0.8)), 0.8, 20, 0.8)
+    for T, K, P in [(0.8, 20, 0.8), (0.8, 0, 0.8), (1.0, 0, 1.0)]:
+        note(f"process misaligned bf16 T={T} K={K} P={P}")
+        _check_rows(zw, host(process(zd, T, K, P)), T, K, P)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
