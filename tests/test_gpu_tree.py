@@ -221,3 +221,39 @@ def test_tree_round_then_commit_matches_per_sequence_decoding(dt):
     model.commit(th["out_tokens"], th["emit_count"])
     content = lambda b, pos, tok, pl, d: W.kv_bits_np(b, pos, tok, pl, d, dt)
     assert model.check(kv_bits(kv), c["pos"], c["mask"], int(c["end_col"][0]), content) == []
+
+
+def test_tree_bench_shape():
+    """The benchmark's tree shape: B=32 sequences of 16-node trees over V=128256
+    bf16 logits (generated as the benchmark does), verified exactly; then the
+    compaction in the full 32 x 8 x 128 bf16 cache, checked on sampled planes."""
+    cfg = W.workload(3)
+    g3 = W.kv_geometry(3)
+    B, NT, V = g3["B"], 16, cfg["V"]
+    g = W.planted_tree(W.stream(3, "logits", 0, 1), W.stream(3, "drafts", 0, 1), B, NT, V, cfg["logit_sd"],
+                       "bf16", W.alphas(3), 3)
+    note(f"tree bench shape verify B={B} N={NT} V={V}")
+    ref = _check_tree(g)
+    assert ref["accept_len"].max() >= 2
+    L, H, D, E = g3["L"], g3["H"], g3["D"], g3["E"]
+    C = E + NT
+    note(f"tree bench shape compaction L={L} H={H} D={D} C={C}")
+    kv = torch.empty((L, 2, B, H, C, D), dtype=torch.bfloat16, device=DEV)
+    iv = kv.view(torch.int16)
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    iv[:, :, :, :, E:, :] = torch.randint(-32768, 32767, (L, 2, B, H, NT, D), dtype=torch.int16, device=DEV,
+                                          generator=gen)
+    rng = np.random.default_rng(6)
+    planes = [(int(rng.integers(L)), int(rng.integers(2)), int(rng.integers(B)), int(rng.integers(H)))
+              for _ in range(48)]
+    before = [iv[l, c, b, h, E:, :].cpu().numpy() for l, c, b, h in planes]
+    st = host(dict(s=compact_tree(kv, NT, E, ref["path"], ref["emit_count"])))["s"]
+    assert (st == 0).all()
+    for (l, c, b, h), pre in zip(planes, before):
+        got = iv[l, c, b, h, E:, :].cpu().numpy()
+        want = pre.copy()
+        for j in range(int(ref["emit_count"][b])):
+            want[j] = pre[int(ref["path"][b, j])]
+        assert np.array_equal(got, want), (l, c, b, h)
+    del kv, iv
+    torch.cuda.empty_cache()
