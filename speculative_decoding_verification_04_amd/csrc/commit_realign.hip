@@ -30,6 +30,9 @@
 //     of memory.  Many narrow walkers (several per CU, each on its own plane
 //     far from the others) keep more DRAM pages open at once and measured
 //     about 10% slower on MI355X; so did longest-move-first dispatch.
+//   * A plane's workgroup reads its own sequence first and issues its first
+//     tile's loads before reducing the batch-wide state (M, validity): the
+//     source range does not depend on M.
 //   * The first B workgroups write the position-id and mask rows, the next
 //     one the scalar outputs; they finish early and never wait.  Outputs
 //     never alias inputs, so no workgroup waits for another.

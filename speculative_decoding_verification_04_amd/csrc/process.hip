@@ -4,12 +4,27 @@
 // Definitions: process.h (after the zero-to-sglang walkthrough 5.1, which
 // requires the processed probabilities to be the ones verified).
 //
-// Design.  One 1024-lane workgroup per row.
+// Design.  Rows are first cut into slices of 16 KB (16384 bf16 or 8192 f32
+// logits), one 256-lane workgroup each, holding the slice's order keys in
+// registers; a 1024-lane statistics workgroup per row then finishes.
+//   * Top-k (K <= 256): proc_slice_kernel cuts each slice at the K-th largest
+//     of its 256 lane maxima (a bitonic sort of the maxima) and lists the
+//     entries at or above that cut; the union of the lists holds every logit at
+//     or above the row's K-th largest.  The statistics kernel runs every
+//     radix level on the union.
+//   * No top-k: slice maxima (proc_slrange_kernel, or with top-p the slice
+//     kernel cut at the 128th lane maximum), then the exact fixed-point weight
+//     and smallest key of every slice (proc_slmass_kernel).  Temperature
+//     alone keeps everything, so those sums are the result; with top-p the
+//     statistics kernel runs the top-p levels on the union when the union
+//     carries at least top_p of the row's weight (checked exactly).
+// Rows whose lists overflow, and top-k beyond 256, take the whole-row path of
+// the statistics kernel:
 //   1. One pass over the row takes its maximum and, with top-k, a histogram of
 //      the top 8 bits of the order keys.  Without top-k but with top-p, a
 //      second pass takes the same histogram of counts and fixed-point weights
-//      (2^-40 units, truncated).  The bucket holding the K-th largest key (or the top-p
-//      boundary) is read off the histogram.
+//      (2^-40 units, truncated).  The bucket holding the K-th largest key (or
+//      the top-p boundary) is read off the histogram.
 //   2. Every logit in that bucket or above is copied into LDS (it fits when at
 //      most 32768 logits qualify, which covers top-k up to that size and any
 //      top-p boundary whose bucket and everything above hold that few); the
@@ -17,7 +32,8 @@
 //      and the kept weight then run on that list.  Otherwise they re-read the
 //      row (from L2).
 //   3. The kept weight is an exact integer sum of the fixed-point weights, so
-//      the result does not depend on the order logits are visited in.
+//      the result does not depend on the order logits are visited in, nor on
+//      the path taken.
 // Whole-row histograms are kept per lane index: bucket b, column l (256 x 64
 // packed 64-bit words, 128 KB of LDS), so the 64 lanes of an atomic add hit 64
 // different words.  Logits cluster in a few buckets of the top digit; one
