@@ -62,6 +62,7 @@ constexpr int kCandCap = 256 * 64 * 2;          // candidate logits that fit in 
 // statistics kernel uses the union when it carries at least top_p of the row's
 // weight, which it checks exactly; else it reads the row.
 constexpr int kToppRank = 128;
+constexpr int kWaveList = 2048;                 // lists up to this length are finished by one wave
 
 struct ProcParams {
   const void *za, *zb;   // rows [0, rows_a) come from za, the rest from zb
@@ -251,6 +252,133 @@ __device__ inline int wave_append(bool want, int *counter) {
 }
 
 
+// Statistics of a short top-k candidate list by one wave, with the choices
+// of the workgroup-wide code below: the same radix digits, tie rules and
+// exact fixed-point sums, in one wave so that no step waits at a workgroup
+// barrier.  The list holds every logit at or above the row's K-th largest
+// and the row's largest.  Lane l owns buckets 255 - 4l .. 252 - 4l
+// (descending) of hc / hm.
+template <bool BF16>
+__device__ inline void wave_list_stats(const float *cand, int n, float zmax, float invT, int K, bool topp_on,
+                                       float top_p, uint32_t *hc, unsigned long long *hm, ProcStats &st) {
+  constexpr int kLevels = BF16 ? 2 : 4;
+  const int lane = threadIdx.x & (kWave - 1);
+  auto clear = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hc[4 * lane + j] = 0u;
+      hm[4 * lane + j] = 0ull;
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto excl_scan_u64 = [&](unsigned long long v) { return wave_incl_scan(v) - v; };
+  // ---- top-k: the K-th largest key, one 8-bit digit per level
+  uint32_t kprefix = 0u, kmask = 0u;
+  if (K > 0) {
+    uint32_t need = static_cast<uint32_t>(K);
+    for (int lvl = 0; lvl < kLevels; ++lvl) {
+      const int shift = 24 - 8 * lvl;
+      clear();
+      for (int i = lane; i < n; i += kWave) {
+        const uint32_t key = f32_order_key(cand[i]);
+        if ((key & kmask) == kprefix) atomicAdd(&hc[(key >> shift) & 255u], 1u);
+      }
+      __builtin_amdgcn_wave_barrier();
+      uint32_t c[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = hc[255 - 4 * lane - j];
+      unsigned long long run = excl_scan_u64(static_cast<unsigned long long>(c[0] + c[1] + c[2] + c[3]));
+      int found = -1;
+      uint32_t rest = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (found < 0 && run < need && need <= run + c[j]) {
+          found = 255 - 4 * lane - j;
+          rest = need - static_cast<uint32_t>(run);
+        }
+        run += c[j];
+      }
+      const unsigned long long m = __ballot(found >= 0);
+      const int src = __ffsll(static_cast<long long>(m)) - 1;
+      const int b = __shfl(found, src, kWave);
+      need = static_cast<uint32_t>(__shfl(static_cast<int>(rest), src, kWave));
+      kprefix |= static_cast<uint32_t>(b) << shift;
+      kmask |= 255u << shift;
+    }
+  }
+  const uint32_t tau = kprefix;
+  // ---- top-p over the survivors: the lowest non-empty bucket whose heavier
+  //      buckets weigh less than top_p times the total, one digit per level
+  uint32_t theta = tau;
+  if (topp_on) {
+    uint32_t pprefix = 0u, pmask = 0u;
+    unsigned long long above = 0ull;
+    double thr = 0.0;
+    bool dead = false;
+    for (int lvl = 0; lvl < kLevels; ++lvl) {
+      const int shift = 24 - 8 * lvl;
+      clear();
+      for (int i = lane; i < n; i += kWave) {
+        const float z = cand[i];
+        const uint32_t key = f32_order_key(z);
+        if (key >= tau && (key & pmask) == pprefix) {
+          const uint32_t d = (key >> shift) & 255u;
+          atomicAdd(&hc[d], 1u);
+          atomicAdd(&hm[d], fixed_weight(proc_weight(z, zmax, invT)));
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      uint32_t c[4];
+      unsigned long long mw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hc[255 - 4 * lane - j];
+        mw[j] = hm[255 - 4 * lane - j];
+      }
+      const unsigned long long lsum = mw[0] + mw[1] + mw[2] + mw[3];
+      unsigned long long run = excl_scan_u64(lsum);
+      if (lvl == 0) thr = static_cast<double>(top_p) * static_cast<double>(wave_sum_u64(lsum));
+      int best = -1;
+      unsigned long long sbest = 0ull;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (c[j] > 0u && static_cast<double>(above + run) < thr) {
+          best = 4 * lane + j;
+          sbest = run;
+        }
+        run += mw[j];
+      }
+      const int pos = wave_max_i(best);             // the lowest eligible bucket
+      if (pos < 0) {
+        dead = true;
+        break;
+      }
+      above += static_cast<unsigned long long>(__shfl(static_cast<long long>(sbest), pos >> 2, kWave));
+      pprefix |= static_cast<uint32_t>(255 - pos) << shift;
+      pmask |= 255u << shift;
+    }
+    if (!dead) theta = pprefix;
+  }
+  // ---- kept weight and smallest kept logit
+  unsigned long long acc = 0ull;
+  float zlo = INFINITY;
+  for (int i = lane; i < n; i += kWave) {
+    const float z = cand[i];
+    if (f32_order_key(z) >= theta) {
+      acc += fixed_weight(proc_weight(z, zmax, invT));
+      zlo = fminf(zlo, z);
+    }
+  }
+  acc = wave_sum_u64(acc);
+  zlo = -wave_max(-zlo);
+  const double mass = static_cast<double>(acc) / kFixScale;
+  st.zmax = zmax;
+  st.theta = theta;
+  st.mass = mass;
+  st.inv_mass = mass > 0.0 ? static_cast<float>(1.0 / mass) : 0.0f;
+  st.zmin_kept = zlo;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) {
   // per-lane histogram columns (128 KB); reused as the candidate list
@@ -267,6 +395,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   __shared__ int sh_seg[kSliceMaxS + 1];
   __shared__ uint32_t sh_cutw[kSliceMaxS];
   __shared__ bool sh_fast;
+  __shared__ ProcStats sh_st;
 
   static_assert(kProcThreads == 4 * 256, "fold_columns assigns 4 lanes per bucket");
   const int t = threadIdx.x;
@@ -356,6 +485,25 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   const float zmax = block_max_f(m, sh_f);     // (contains barriers)
   if (fast) nfast = sh_n;
   const bool topp_on = topp && zmax != -INFINITY;
+
+  // ---- a short top-k list: one wave decides everything (no workgroup
+  //      barriers).  (Top-p lists without top-k are longer; the workgroup
+  //      code below is faster for them.)
+  if (fast && topk && nfast <= kWaveList) {
+    if (t < kWave) {
+      ProcStats st;
+      wave_list_stats<BF16>(cand, nfast, zmax, invT, K, topp_on, P.cfg.top_p, h_cnt, h_mass, st);
+      if (t == 0) sh_st = st;
+    }
+    __syncthreads();
+    const ProcStats st = sh_st;
+    if (t == 0) P.stats[r] = st;
+    if (P.probs) {
+      float *out = P.probs + static_cast<size_t>(r) * V;
+      row_foreach<BF16>(row, V, [&](int v, float z) { out[v] = proc_prob(z, st, invT); });
+    }
+    return;
+  }
 
   // Selection state.  Level-0 digits are chosen from whole-row histograms;
   // everything at or above the chosen level-0 bucket is then copied into LDS
