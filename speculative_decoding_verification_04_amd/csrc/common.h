@@ -94,11 +94,6 @@ __device__ inline double wave_sum_d(double v) {
   for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
   return v;
 }
-__device__ inline int wave_sum_i(int v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
 
 // Inclusive scan across one wavefront (lane order).
 template <typename T>

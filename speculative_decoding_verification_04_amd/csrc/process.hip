@@ -155,18 +155,6 @@ __device__ inline float block_max_f(float v, float *sh) {
   return m;
 }
 
-__device__ inline double block_sum_dd(double v, double *sh) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  v = wave_sum_d(v);
-  if (lane == 0) sh[w] = v;
-  __syncthreads();
-  double s = 0.0;
-#pragma unroll
-  for (int i = 0; i < kProcWaves; ++i) s += sh[i];
-  __syncthreads();
-  return s;
-}
-
 // Sums the 64 columns of every bucket of the per-lane histogram into
 // h_cnt / h_mass.  Contains barriers.
 __device__ inline void fold_columns(const unsigned long long *lh, uint32_t *h_cnt,

@@ -72,7 +72,6 @@ inline SampleWs sample_ws_layout(int B, int chunks) {
 // `resid` is set, else r_v = a_v.  DenseRow reads given float32 rows;
 // LogitRow<BF16> computes the processed rows p', q' from logits on the fly.
 struct DenseRow {
-  static constexpr bool kDense = true;
   const float *a, *b;
   bool resid;
   __device__ inline float at(int v) const { return resid ? fmaxf(a[v] - b[v], 0.0f) : a[v]; }
@@ -113,7 +112,6 @@ struct DenseRow {
 
 template <bool BF16>
 struct LogitRow {
-  static constexpr bool kDense = false;
   const void *a, *b;
   ProcStats sa, sb;
   float invT;
