@@ -13,6 +13,8 @@ import numpy as np
 import pytest
 import torch
 
+import speculative_decoding_verification_04_amd as sv
+
 import oracle
 import workloads as W
 from oracle.process import process_row
@@ -265,3 +267,16 @@ def test_verify_from_logits_repeatable():
         again = host(verify_sample_logits(zt, zd_, d, g["uniforms"], 0.7, 40, 0.9, ws_key="vl"))
         for key in first:
             assert np.array_equal(first[key], again[key]), key
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_process_largest_vocabulary(dtype):
+    """V = SPEC_PROC_MAX_V: the most slices per row (64 for f32), the smallest
+    per-slice list capacity, and the union path for top-p alone."""
+    rng = np.random.default_rng(14)
+    V = sv.SPEC_PROC_MAX_V
+    dev_in, zw = _rows(rng, 3, V, dtype, sd=3.0)
+    zd = logits_to_device(dev_in, dtype)
+    for T, K, P in [(0.7, 50, 0.9), (1.0, 128, 1.0), (0.7, 0, 0.9), (1.0, 0, 1.0), (0.7, 300, 0.95)]:
+        note(f"process largest V {dtype} T={T} K={K} P={P}")
+        _check_rows(zw, host(process(zd, T, K, P)), T, K, P)
