@@ -258,3 +258,34 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load()
+
+
+def test_header_is_plain_c(tmp_path):
+    """The boundary is plain C: the header compiles as C99 on its own (no HIP,
+    no torch types), and a C program can take the address of every entry
+    point (linked against the library when it is built)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = _declared()
+    src = tmp_path / "use.c"
+    src.write_text('#include "spec_verify.h"\n#include <stdio.h>\n'
+                   "typedef void (*any_fn)(void);\n"
+                   "int main(void) {\n  any_fn fns[] = {\n"
+                   + "".join(f"    (any_fn)&{n},\n" for n in names)
+                   + "  };\n  printf(\"%d\\n\", (int)(sizeof fns / sizeof fns[0]));\n  return 0;\n}\n")
+    inc = os.path.join(ROOT, "include")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-fsyntax-only", "-I", inc, str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    if LIB is None:
+        return
+    libdir = os.path.join(ROOT, "speculative_decoding_verification_04_amd")
+    exe = tmp_path / "use"
+    r = subprocess.run([cc, "-std=c99", "-I", inc, str(src), "-L", libdir, "-lspecverify",
+                        f"-Wl,-rpath,{libdir}", "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and int(r.stdout) == len(names)
