@@ -58,6 +58,28 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _arg(t, dtype: str, numel: int, name: str, optional: bool = False):
+    """Device pointer of an argument tensor after host checks of its dtype
+    (e.g. "int32"), size (at least numel elements), layout and device; the
+    C library takes plain pointers and cannot check these itself."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if str(t.dtype) != "torch." + dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} needs at least {numel} elements, has {t.numel()}")
+    return _ptr(t)
+
+
+def _same(t, ref, name: str):
+    """Pointer of a tensor that must have ref's dtype and shape."""
+    if t.dtype != ref.dtype or tuple(t.shape) != tuple(ref.shape):
+        raise ValueError(f"{name} must match {tuple(ref.shape)} {ref.dtype}, got {tuple(t.shape)} {t.dtype}")
+    return _ptr(t)
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -92,9 +114,12 @@ def spec_verify_greedy(logits, draft, accept_len, emit_count, out_tokens, ws, *,
                        stream=None) -> None:
     """logits [B, k+1, V] (bf16/f32), draft [B, k] int32; outputs int32 tensors."""
     B, kp1, V = logits.shape
+    k = kp1 - 1
     code = library().spec_verify_greedy(
-        _ptr(logits), _dtype_code(logits), B, kp1 - 1, V, _ptr(draft), int(eos_id), _ptr(remaining),
-        _ptr(accept_len), _ptr(emit_count), _ptr(out_tokens), _ptr(emit_offsets), _ptr(status),
+        _ptr(logits), _dtype_code(logits), B, k, V, _arg(draft, "int32", B * k, "draft"), int(eos_id),
+        _arg(remaining, "int32", B, "remaining", True), _arg(accept_len, "int32", B, "accept_len"),
+        _arg(emit_count, "int32", B, "emit_count"), _arg(out_tokens, "int32", B * kp1, "out_tokens"),
+        _arg(emit_offsets, "int32", B + 1, "emit_offsets", True), _arg(status, "int32", B, "status", True),
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(code, "spec_verify_greedy")
 
@@ -104,10 +129,15 @@ def spec_verify_sample(p, q, draft, uniforms, accept_len, emit_count, out_tokens
                        status=None, stream=None) -> None:
     """p [B, k+1, V] f32, q [B, k, V] f32, draft [B, k] int32, uniforms [B, k+1] f32."""
     B, kp1, V = p.shape
+    k = kp1 - 1
     code = library().spec_verify_sample(
-        _ptr(p), _ptr(q), _ptr(draft), _ptr(uniforms), B, kp1 - 1, V, int(eos_id), _ptr(remaining),
-        _ptr(accept_len), _ptr(emit_count), _ptr(out_tokens), _ptr(emit_offsets), _ptr(final_mass),
-        _ptr(status), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+        _arg(p, "float32", B * kp1 * V, "p"), _arg(q, "float32", B * k * V, "q"),
+        _arg(draft, "int32", B * k, "draft"), _arg(uniforms, "float32", B * kp1, "uniforms"), B, k, V,
+        int(eos_id), _arg(remaining, "int32", B, "remaining", True), _arg(accept_len, "int32", B, "accept_len"),
+        _arg(emit_count, "int32", B, "emit_count"), _arg(out_tokens, "int32", B * kp1, "out_tokens"),
+        _arg(emit_offsets, "int32", B + 1, "emit_offsets", True),
+        _arg(final_mass, "float64", B, "final_mass", True), _arg(status, "int32", B, "status", True),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(code, "spec_verify_sample")
 
 
@@ -128,8 +158,9 @@ def spec_process_logits(logits, temperature: float, ws, *, top_k: int = 0, top_p
     R = logits.numel() // V
     code = library().spec_process_logits(
         _ptr(logits), _dtype_code(logits), R, V, float(temperature), int(top_k), float(top_p),
-        _ptr(probs), _ptr(row_max), _ptr(row_threshold), _ptr(row_mass), _ptr(ws),
-        ws.numel() * ws.element_size(), _stream(stream))
+        _arg(probs, "float32", R * V, "probs", True), _arg(row_max, "float32", R, "row_max", True),
+        _arg(row_threshold, "float32", R, "row_threshold", True), _arg(row_mass, "float64", R, "row_mass", True),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(code, "spec_process_logits")
 
 
@@ -139,13 +170,19 @@ def spec_verify_sample_logits(target_logits, draft_logits, draft, uniforms, acce
                               emit_offsets=None, final_mass=None, status=None, stream=None) -> None:
     """target_logits [B, k+1, V], draft_logits [B, k, V] (same dtype, bf16/f32)."""
     B, kp1, V = target_logits.shape
+    k = kp1 - 1
     if draft_logits.dtype != target_logits.dtype:
         raise ValueError("target and draft logits must share a dtype")
+    if tuple(draft_logits.shape) != (B, k, V):
+        raise ValueError(f"draft_logits must be {(B, k, V)}, got {tuple(draft_logits.shape)}")
     code = library().spec_verify_sample_logits(
-        _ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits), B, kp1 - 1, V,
-        float(temperature), int(top_k), float(top_p), _ptr(draft), _ptr(uniforms), int(eos_id),
-        _ptr(remaining), _ptr(accept_len), _ptr(emit_count), _ptr(out_tokens), _ptr(emit_offsets),
-        _ptr(final_mass), _ptr(status), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+        _ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits), B, k, V,
+        float(temperature), int(top_k), float(top_p), _arg(draft, "int32", B * k, "draft"),
+        _arg(uniforms, "float32", B * kp1, "uniforms"), int(eos_id), _arg(remaining, "int32", B, "remaining", True),
+        _arg(accept_len, "int32", B, "accept_len"), _arg(emit_count, "int32", B, "emit_count"),
+        _arg(out_tokens, "int32", B * kp1, "out_tokens"), _arg(emit_offsets, "int32", B + 1, "emit_offsets", True),
+        _arg(final_mass, "float64", B, "final_mass", True), _arg(status, "int32", B, "status", True),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(code, "spec_verify_sample_logits")
 
 
@@ -156,9 +193,12 @@ def spec_commit_realign_kv(kv, k: int, end_col, kv_len_in, emit_count, end_col_o
     if two != 2:
         raise ValueError("kv must be [L, 2, B, H, C, D]")
     code = library().spec_commit_realign_kv(
-        _ptr(kv), _dtype_code(kv), L, B, H, C, D, int(k), _ptr(end_col), _ptr(kv_len_in),
-        _ptr(emit_count), _ptr(end_col_out), _ptr(kv_len_out), _ptr(pos_ids), _ptr(mask),
-        _ptr(bytes_moved), _ptr(status), _stream(stream))
+        _ptr(kv), _dtype_code(kv), L, B, H, C, D, int(k), _arg(end_col, "int32", 1, "end_col"),
+        _arg(kv_len_in, "int32", B, "kv_len_in"), _arg(emit_count, "int32", B, "emit_count"),
+        _arg(end_col_out, "int32", 1, "end_col_out"), _arg(kv_len_out, "int32", B, "kv_len_out"),
+        _arg(pos_ids, "int32", B * C, "pos_ids"), _arg(mask, "int32", B * C, "mask"),
+        _arg(bytes_moved, "int64", 1, "bytes_moved", True), _arg(status, "int32", B, "status", True),
+        _stream(stream))
     _check(code, "spec_commit_realign_kv")
 
 
@@ -169,9 +209,12 @@ def spec_resync_draft_kv(kv, k: int, end_col, kv_len_in, emit_count, end_col_out
     if two != 2:
         raise ValueError("kv must be [L, 2, B, H, C, D]")
     code = library().spec_resync_draft_kv(
-        _ptr(kv), _dtype_code(kv), L, B, H, C, D, int(k), _ptr(end_col), _ptr(kv_len_in),
-        _ptr(emit_count), _ptr(end_col_out), _ptr(kv_len_out), _ptr(pos_ids), _ptr(mask),
-        _ptr(bytes_moved), _ptr(status), _stream(stream))
+        _ptr(kv), _dtype_code(kv), L, B, H, C, D, int(k), _arg(end_col, "int32", 1, "end_col"),
+        _arg(kv_len_in, "int32", B, "kv_len_in"), _arg(emit_count, "int32", B, "emit_count"),
+        _arg(end_col_out, "int32", 1, "end_col_out"), _arg(kv_len_out, "int32", B, "kv_len_out"),
+        _arg(pos_ids, "int32", B * C, "pos_ids", True), _arg(mask, "int32", B * C, "mask", True),
+        _arg(bytes_moved, "int64", 1, "bytes_moved", True), _arg(status, "int32", B, "status", True),
+        _stream(stream))
     _check(code, "spec_resync_draft_kv")
 
 
@@ -179,10 +222,13 @@ def spec_commit_paged(k: int, page_size: int, kv_len_in, emit_count, block_table
                       pages_kept, freed_pages, freed_offsets, *, status=None, stream=None) -> None:
     """block_table [B, max_pages] int32; freed_pages holds B * ceil((k+1)/page_size) ids."""
     B, max_pages = block_table.shape
+    per = (int(k) + int(page_size)) // max(int(page_size), 1)
     code = library().spec_commit_paged(
-        B, int(k), int(page_size), max_pages, _ptr(kv_len_in), _ptr(emit_count), _ptr(block_table),
-        _ptr(kv_len_out), _ptr(pages_kept), _ptr(freed_pages), _ptr(freed_offsets), _ptr(status),
-        _stream(stream))
+        B, int(k), int(page_size), max_pages, _arg(kv_len_in, "int32", B, "kv_len_in"),
+        _arg(emit_count, "int32", B, "emit_count"), _arg(block_table, "int32", B * max_pages, "block_table"),
+        _arg(kv_len_out, "int32", B, "kv_len_out"), _arg(pages_kept, "int32", B, "pages_kept"),
+        _arg(freed_pages, "int32", B * per, "freed_pages"), _arg(freed_offsets, "int32", B + 1, "freed_offsets"),
+        _arg(status, "int32", B, "status", True), _stream(stream))
     _check(code, "spec_commit_paged")
 
 
@@ -196,9 +242,12 @@ def spec_verify_tree(logits, draft, first_child, next_sibling, accept_len, emit_
     """logits [B, N, V] (bf16/f32); draft, first_child, next_sibling [B, N] int32."""
     B, N, V = logits.shape
     code = library().spec_verify_tree(
-        _ptr(logits), _dtype_code(logits), B, N, V, _ptr(draft), _ptr(first_child), _ptr(next_sibling),
-        int(eos_id), _ptr(remaining), _ptr(accept_len), _ptr(emit_count), _ptr(out_tokens), _ptr(path),
-        _ptr(emit_offsets), _ptr(status), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+        _ptr(logits), _dtype_code(logits), B, N, V, _arg(draft, "int32", B * N, "draft"),
+        _arg(first_child, "int32", B * N, "first_child"), _arg(next_sibling, "int32", B * N, "next_sibling"),
+        int(eos_id), _arg(remaining, "int32", B, "remaining", True), _arg(accept_len, "int32", B, "accept_len"),
+        _arg(emit_count, "int32", B, "emit_count"), _arg(out_tokens, "int32", B * N, "out_tokens"),
+        _arg(path, "int32", B * N, "path"), _arg(emit_offsets, "int32", B + 1, "emit_offsets", True),
+        _arg(status, "int32", B, "status", True), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(code, "spec_verify_tree")
 
 
@@ -208,8 +257,9 @@ def spec_compact_tree_kv(kv, N: int, end_col, path, emit_count, *, status=None, 
     if two != 2:
         raise ValueError("kv must be [L, 2, B, H, C, D]")
     code = library().spec_compact_tree_kv(
-        _ptr(kv), _dtype_code(kv), L, B, H, C, D, int(N), _ptr(end_col), _ptr(path), _ptr(emit_count),
-        _ptr(status), _stream(stream))
+        _ptr(kv), _dtype_code(kv), L, B, H, C, D, int(N), _arg(end_col, "int32", 1, "end_col"),
+        _arg(path, "int32", B * int(N), "path"), _arg(emit_count, "int32", B, "emit_count"),
+        _arg(status, "int32", B, "status", True), _stream(stream))
     _check(code, "spec_compact_tree_kv")
 
 
@@ -218,6 +268,8 @@ def spec_group_same_length(lengths, B: int, min_group: int, perm, batch_start, b
     """lengths [N] int32; outputs perm [N], batch_start [N+1], batch_len [N], two scalars."""
     N = lengths.numel()
     code = library().spec_group_same_length(
-        _ptr(lengths), N, int(B), int(min_group), _ptr(perm), _ptr(batch_start), _ptr(batch_len),
-        _ptr(num_batches), _ptr(num_grouped), _stream(stream))
+        _arg(lengths, "int32", N, "lengths") if N else None, N, int(B), int(min_group),
+        _arg(perm, "int32", N, "perm"), _arg(batch_start, "int32", N + 1, "batch_start"),
+        _arg(batch_len, "int32", N, "batch_len"), _arg(num_batches, "int32", 1, "num_batches"),
+        _arg(num_grouped, "int32", 1, "num_grouped"), _stream(stream))
     _check(code, "spec_group_same_length")
