@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 #include "spec_verify.h"
@@ -56,6 +58,57 @@ constexpr int kDppQuadXor1 = 0xB1;
 constexpr int kDppQuadXor2 = 0x4E;
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
+// row_shr:n (n = 1, 2, 4, 8): lane i of a row of 16 reads lane i - n of the
+// same row; the first n lanes of each row keep the `old` operand.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+
+// One DPP lane move of a 32- or 64-bit value (64-bit values move as two
+// halves); lanes without a source take `old`.  Every lane of the wave must be
+// active.
+template <int CTRL, typename T>
+__device__ inline T dpp_move(T v, T old) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit lanes");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                             CTRL, 0xF, 0xF, false));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v), o = __builtin_bit_cast(uint64_t, old);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        static_cast<int>(static_cast<uint32_t>(o)), static_cast<int>(static_cast<uint32_t>(u)), CTRL, 0xF, 0xF, false));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        static_cast<int>(o >> 32), static_cast<int>(u >> 32), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(T, (static_cast<uint64_t>(hi) << 32) | lo);
+  }
+}
+
+// The value of lane `l` (uniform) of a 32- or 64-bit value.
+template <typename T>
+__device__ inline T read_lane(T v, int l) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), l));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), l));
+    return __builtin_bit_cast(T, (static_cast<uint64_t>(hi) << 32) | lo);
+  }
+}
+
+// Wave reduction by a commutative, associative op through DPP: butterflies
+// inside each row of 16 lanes (xor 1, xor 2, half-row mirror, row mirror),
+// then the four row results read as scalars.  Every lane of the wave must be
+// active; every lane returns the result.
+template <typename T, class Op>
+__device__ inline T wave_reduce(T v, Op op) {
+  v = op(v, dpp_move<kDppQuadXor1>(v, v));
+  v = op(v, dpp_move<kDppQuadXor2>(v, v));
+  v = op(v, dpp_move<kDppRowHalfMirror>(v, v));
+  v = op(v, dpp_move<kDppRowMirror>(v, v));
+  return op(op(read_lane(v, 0), read_lane(v, 16)), op(read_lane(v, 32), read_lane(v, 48)));
+}
 
 // Wave maximum through DPP lane moves (no LDS round trips): butterflies inside
 // each row of 16 lanes (xor 1, xor 2, half-row mirror, row mirror leave every
@@ -80,14 +133,10 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 __device__ inline int wave_min(int v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, kWave));
-  return v;
+  return wave_reduce(v, [](int a, int b) { return min(a, b); });
 }
 __device__ inline int wave_max_i(int v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, kWave));
-  return v;
+  return wave_reduce(v, [](int a, int b) { return max(a, b); });
 }
 __device__ inline double wave_sum_d(double v) {
 #pragma unroll
@@ -95,14 +144,29 @@ __device__ inline double wave_sum_d(double v) {
   return v;
 }
 
-// Inclusive scan across one wavefront (lane order).
+// Inclusive scan across one wavefront (lane order); every lane of the wave
+// must be active.  Integers: DPP row shifts give each row of 16 its own
+// prefix, then the rows' totals (lanes 15, 31, 47) are added to the rows
+// above.  Floating point keeps the lane-shuffle order of additions.
 template <typename T>
 __device__ inline T wave_incl_scan(T v) {
   const int lane = threadIdx.x & (kWave - 1);
+  if constexpr (std::is_integral<T>::value) {
+    v += dpp_move<kDppRowShr1>(v, T(0));
+    v += dpp_move<kDppRowShr2>(v, T(0));
+    v += dpp_move<kDppRowShr4>(v, T(0));
+    v += dpp_move<kDppRowShr8>(v, T(0));
+    const T r0 = read_lane(v, 15), r1 = read_lane(v, 31), r2 = read_lane(v, 47);
+    const int row = lane >> 4;
+    if (row >= 1) v += r0;
+    if (row >= 2) v += r1;
+    if (row >= 3) v += r2;
+  } else {
 #pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    T o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
+    for (int d = 1; d < kWave; d <<= 1) {
+      T o = __shfl_up(v, d, kWave);
+      if (lane >= d) v += o;
+    }
   }
   return v;
 }

@@ -5,19 +5,28 @@
 // requires the processed probabilities to be the ones verified).
 //
 // Design.  Rows are first cut into slices of 16 KB (16384 bf16 or 8192 f32
-// logits), one 256-lane workgroup each, holding the slice's order keys in
-// registers; a 1024-lane statistics workgroup per row then finishes.
+// logits), one 256-lane workgroup each, holding the slice's raw 16-byte
+// vectors in registers and working on float values (a shift or mask per bf16
+// entry, three-operand maxima); a statistics workgroup per row then finishes.
 //   * Top-k (K <= 256): proc_slice_kernel cuts each slice at the K-th largest
 //     of its 256 lane maxima (a bitonic sort of the maxima) and lists the
-//     entries at or above that cut; the union of the lists holds every logit at
-//     or above the row's K-th largest.  The statistics kernel runs every
-//     radix level on the union.
+//     entries at or above that cut: the vectors whose maximum reaches the cut
+//     (about K) are staged in LDS and filtered by the whole workgroup.  The
+//     union of the lists holds every logit at or above the row's K-th
+//     largest.  Each slice also reports its ceil(K / S)-th largest lane
+//     maximum; the smallest of those over the S slices is another lower bound
+//     of the row's K-th largest, usually much tighter than the largest cut, so
+//     the statistics see about 2K candidates instead of about K per slice.
+//     When every list fits one wave, wave 0 of the statistics workgroup
+//     gathers them in a single round of loads and runs every radix level on
+//     them alone, with no workgroup barrier.
 //   * No top-k: slice maxima (proc_slrange_kernel, or with top-p the slice
 //     kernel cut at the 128th lane maximum), then the exact fixed-point weight
 //     and smallest key of every slice (proc_slmass_kernel).  Temperature
-//     alone keeps everything, so those sums are the result; with top-p the
-//     statistics kernel runs the top-p levels on the union when the union
-//     carries at least top_p of the row's weight (checked exactly).
+//     alone keeps everything, so those sums are the result (one wave combines
+//     them); with top-p the statistics kernel runs the top-p levels on the
+//     union when the union carries at least top_p of the row's weight
+//     (checked exactly).
 // Rows whose lists overflow, and top-k beyond 256, take the whole-row path of
 // the statistics kernel:
 //   1. One pass over the row takes its maximum and, with top-k, a histogram of
@@ -63,6 +72,7 @@ constexpr int kCandCap = 256 * 64 * 2;          // candidate logits that fit in 
 // weight, which it checks exactly; else it reads the row.
 constexpr int kToppRank = 128;
 constexpr int kWaveList = 2048;                 // lists up to this length are finished by one wave
+constexpr int kGatherS = 24;                    // wave 0 gathers the top-k lists of up to this many slices
 
 struct ProcParams {
   const void *za, *zb;   // rows [0, rows_a) come from za, the rest from zb
@@ -76,6 +86,8 @@ struct ProcParams {
   uint32_t *list_cut;    // [rows][S]: each slice listed every entry with a key at or above
   int S, seg_cap;        // slices per row, entries per segment
   int cut_rank;          // the slice kernel's cut: the cut_rank-th largest lane maximum
+  uint32_t *list_lb;     // [rows][S] or null: each slice's lb_rank-th largest lane maximum
+  int lb_rank;           // ceil(K / S): at least K logits of the row are at or above the smallest
   // rows without top-k: per slice, the key range and the fixed-point weight
   // (null: read the whole row)
   uint32_t *sl_max, *sl_min;        // [rows][S]
@@ -181,9 +193,14 @@ __device__ inline void fold_columns(const unsigned long long *lh, uint32_t *h_cn
 }
 
 __device__ inline unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  return wave_reduce(v, [](unsigned long long a, unsigned long long b) { return a + b; });
+}
+
+__device__ inline uint32_t wave_max_u(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return max(a, b); });
+}
+__device__ inline uint32_t wave_min_u(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return min(a, b); });
 }
 
 __device__ inline void clear_columns(unsigned long long *lh) {
@@ -234,7 +251,7 @@ __device__ inline int wave_append(bool want, int *counter) {
   if (mask != 0ull) {
     const int leader = __ffsll(static_cast<long long>(mask)) - 1;
     if (lane == leader) base = atomicAdd(counter, __popcll(mask));
-    base = __shfl(base, leader, kWave);
+    base = read_lane(base, leader);
   }
   return base + __popcll(mask & ((1ull << lane) - 1ull));
 }
@@ -243,11 +260,12 @@ __device__ inline int wave_append(bool want, int *counter) {
 // Statistics of a short top-k candidate list by one wave, with the choices
 // of the workgroup-wide code below: the same radix digits, tie rules and
 // exact fixed-point sums, in one wave so that no step waits at a workgroup
-// barrier.  The list holds every logit at or above the row's K-th largest
-// and the row's largest.  Lane l owns buckets 255 - 4l .. 252 - 4l
-// (descending) of hc / hm.
-template <bool BF16>
-__device__ inline void wave_list_stats(const float *cand, int n, float zmax, float invT, int K, bool topp_on,
+// barrier.  each(f) calls f(key) with the order key of every candidate of
+// this lane (0: none); the candidates hold every logit at or above the row's
+// K-th largest and the row's largest.  Lane l owns buckets 255 - 4l ..
+// 252 - 4l (descending) of hc / hm.
+template <bool BF16, class Each>
+__device__ inline void wave_list_stats(Each &&each, float zmax, float invT, int K, bool topp_on,
                                        float top_p, uint32_t *hc, unsigned long long *hm, ProcStats &st) {
   constexpr int kLevels = BF16 ? 2 : 4;
   const int lane = threadIdx.x & (kWave - 1);
@@ -267,10 +285,9 @@ __device__ inline void wave_list_stats(const float *cand, int n, float zmax, flo
     for (int lvl = 0; lvl < kLevels; ++lvl) {
       const int shift = 24 - 8 * lvl;
       clear();
-      for (int i = lane; i < n; i += kWave) {
-        const uint32_t key = f32_order_key(cand[i]);
-        if ((key & kmask) == kprefix) atomicAdd(&hc[(key >> shift) & 255u], 1u);
-      }
+      each([&](uint32_t key) {
+        if (key != 0u && (key & kmask) == kprefix) atomicAdd(&hc[(key >> shift) & 255u], 1u);
+      });
       __builtin_amdgcn_wave_barrier();
       uint32_t c[4];
 #pragma unroll
@@ -288,8 +305,8 @@ __device__ inline void wave_list_stats(const float *cand, int n, float zmax, flo
       }
       const unsigned long long m = __ballot(found >= 0);
       const int src = __ffsll(static_cast<long long>(m)) - 1;
-      const int b = __shfl(found, src, kWave);
-      need = static_cast<uint32_t>(__shfl(static_cast<int>(rest), src, kWave));
+      const int b = read_lane(found, src);
+      need = read_lane(rest, src);
       kprefix |= static_cast<uint32_t>(b) << shift;
       kmask |= 255u << shift;
     }
@@ -306,15 +323,13 @@ __device__ inline void wave_list_stats(const float *cand, int n, float zmax, flo
     for (int lvl = 0; lvl < kLevels; ++lvl) {
       const int shift = 24 - 8 * lvl;
       clear();
-      for (int i = lane; i < n; i += kWave) {
-        const float z = cand[i];
-        const uint32_t key = f32_order_key(z);
-        if (key >= tau && (key & pmask) == pprefix) {
+      each([&](uint32_t key) {
+        if (key != 0u && key >= tau && (key & pmask) == pprefix) {
           const uint32_t d = (key >> shift) & 255u;
           atomicAdd(&hc[d], 1u);
-          atomicAdd(&hm[d], fixed_weight(proc_weight(z, zmax, invT)));
+          atomicAdd(&hm[d], fixed_weight(proc_weight(f32_from_order_key(key), zmax, invT)));
         }
-      }
+      });
       __builtin_amdgcn_wave_barrier();
       uint32_t c[4];
       unsigned long long mw[4];
@@ -341,7 +356,7 @@ __device__ inline void wave_list_stats(const float *cand, int n, float zmax, flo
         dead = true;
         break;
       }
-      above += static_cast<unsigned long long>(__shfl(static_cast<long long>(sbest), pos >> 2, kWave));
+      above += read_lane(sbest, pos >> 2);
       pprefix |= static_cast<uint32_t>(255 - pos) << shift;
       pmask |= 255u << shift;
     }
@@ -350,21 +365,70 @@ __device__ inline void wave_list_stats(const float *cand, int n, float zmax, flo
   // ---- kept weight and smallest kept logit
   unsigned long long acc = 0ull;
   float zlo = INFINITY;
-  for (int i = lane; i < n; i += kWave) {
-    const float z = cand[i];
-    if (f32_order_key(z) >= theta) {
+  each([&](uint32_t key) {
+    if (key != 0u && key >= theta) {
+      const float z = f32_from_order_key(key);
       acc += fixed_weight(proc_weight(z, zmax, invT));
       zlo = fminf(zlo, z);
     }
-  }
+  });
   acc = wave_sum_u64(acc);
-  zlo = -wave_max(-zlo);
+  zlo = -wave_max_dpp(-zlo);
   const double mass = static_cast<double>(acc) / kFixScale;
   st.zmax = zmax;
   st.theta = theta;
   st.mass = mass;
   st.inv_mass = mass > 0.0 ? static_cast<float>(1.0 / mass) : 0.0f;
   st.zmin_kept = zlo;
+}
+
+// Wave 0 of the statistics kernel, top-k lists of at most kGatherS slices of
+// at most one wave (64 entries) each: one round of loads (every slice's
+// count, cut and bound, and the first 64 entries of every list, issued
+// together), then the entries at or above lo = max(largest cut, smallest
+// bound) are appended to `cand` in lane order.  lo is at most the row's K-th
+// largest key: some slice's cut is at most its own K-th largest, and the
+// slices' bounds put ceil(K / S) * S >= K entries at or above the smallest.
+// So `cand` holds every logit at or above the row's K-th largest, and the
+// row's largest.  Returns the count (zmax: the largest), or -1 when the lists
+// do not fit this shape (nothing written).
+__device__ inline int wave_gather_topk(const ProcParams &P, int r, float *cand, float &zmax) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int S = P.S;
+  if (S > kGatherS || P.list_lb == nullptr) return -1;
+  const size_t rs = static_cast<size_t>(r) * S;
+  int cnt = 0;
+  uint32_t cut = 0u, lb = 0xFFFFFFFFu;
+  if (lane < S) {
+    cnt = P.list_cnt[rs + lane];
+    cut = P.list_cut[rs + lane];
+    lb = P.list_lb[rs + lane];
+  }
+  // entry `lane` of every list (inside its segment: seg_cap >= 512 > lane)
+  const uint32_t *base = reinterpret_cast<const uint32_t *>(P.lists) + static_cast<size_t>(r) * kCandCap + lane;
+  uint32_t raw[kGatherS];
+#pragma unroll
+  for (int q = 0; q < kGatherS; ++q) raw[q] = q < S ? base[static_cast<size_t>(q) * P.seg_cap] : 0u;
+  if (__ballot(cnt > kWave) != 0ull) return -1;
+  const uint32_t lo = max(wave_max_u(cut), wave_min_u(lb));
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int n = 0;            // uniform
+  uint32_t mk = 0u;
+#pragma unroll
+  for (int q = 0; q < kGatherS; ++q) {
+    if (q < S) {
+      const uint32_t k = lane < read_lane(cnt, q) ? f32_order_key(__uint_as_float(raw[q])) : 0u;
+      const bool keep = k != 0u && k >= lo;
+      const unsigned long long m = __ballot(keep);
+      if (keep) {
+        cand[n + __popcll(m & below)] = f32_from_order_key(k);
+        mk = max(mk, k);
+      }
+      n += __popcll(m);
+    }
+  }
+  zmax = f32_from_order_key(wave_max_u(mk));
+  return n;
 }
 
 template <bool BF16>
@@ -382,6 +446,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   __shared__ unsigned long long sh_u[kProcWaves];
   __shared__ int sh_seg[kSliceMaxS + 1];
   __shared__ uint32_t sh_cutw[kSliceMaxS];
+  __shared__ uint32_t sh_lbw[kSliceMaxS];
   __shared__ bool sh_fast;
   __shared__ ProcStats sh_st;
 
@@ -403,6 +468,71 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   //      slice's fit (their union holds every logit at or above the K-th
   //      largest, and the largest); else pass 1 over the row: maximum, and the
   //      first top-k digit histogram
+  // ---- temperature only, through the slice kernels: every logit is kept, so
+  //      the slices' maxima, exact weights and minima are the whole answer
+  //      (one wave, one round of loads)
+  if (P.sl_max != nullptr && !topk && !topp) {
+    if (t < kWave) {
+      uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+      unsigned long long tot = 0ull;
+      for (int q = lane; q < P.S; q += kWave) {
+        const size_t i = static_cast<size_t>(r) * P.S + q;
+        mx = max(mx, P.sl_max[i]);
+        mn = min(mn, P.sl_min[i]);
+        tot += P.sl_tot[i];
+      }
+      mx = wave_max_u(mx);
+      mn = wave_min_u(mn);
+      tot = wave_sum_u64(tot);
+      if (t == 0) {
+        ProcStats st;
+        st.zmax = f32_from_order_key(mx);
+        st.theta = 0u;
+        st.mass = static_cast<double>(tot) / kFixScale;
+        st.inv_mass = st.mass > 0.0 ? static_cast<float>(1.0 / st.mass) : 0.0f;
+        st.zmin_kept = f32_from_order_key(mn);
+        P.stats[r] = st;
+        sh_st = st;
+      }
+    }
+    if (P.probs) {
+      __syncthreads();
+      const ProcStats st = sh_st;
+      float *out = P.probs + static_cast<size_t>(r) * V;
+      row_foreach<BF16>(row, V, [&](int v, float z) { out[v] = proc_prob(z, st, invT); });
+    }
+    return;
+  }
+
+  // ---- top-k lists of one wave per slice: wave 0 gathers the candidates
+  //      and decides everything, with no workgroup barrier before the result
+  if (P.lists && topk) {
+    if (t < kWave) {
+      float zm;
+      const int n = wave_gather_topk(P, r, cand, zm);
+      if (n >= 0) {
+        ProcStats st;
+        wave_list_stats<BF16>(
+            [&](auto &&f) {
+              for (int i = lane; i < n; i += kWave) f(f32_order_key(cand[i]));
+            },
+            zm, invT, K, topp && zm != -INFINITY, P.cfg.top_p, h_cnt, h_mass, st);
+        if (t == 0) sh_st = st;
+      }
+      if (t == 0) sh_fast = n >= 0;
+    }
+    __syncthreads();
+    if (sh_fast) {
+      const ProcStats st = sh_st;
+      if (t == 0) P.stats[r] = st;
+      if (P.probs) {
+        float *out = P.probs + static_cast<size_t>(r) * V;
+        row_foreach<BF16>(row, V, [&](int v, float z) { out[v] = proc_prob(z, st, invT); });
+      }
+      return;
+    }
+  }
+
   bool fast = false;
   int nfast = 0;
   uint32_t cutmax = 0;
@@ -412,11 +542,12 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
       const int c = P.list_cnt[static_cast<size_t>(r) * P.S + t];
       sh_seg[t] = c;
       sh_cutw[t] = P.list_cut[static_cast<size_t>(r) * P.S + t];
+      sh_lbw[t] = topk && P.list_lb ? P.list_lb[static_cast<size_t>(r) * P.S + t] : 0u;
     }
     __syncthreads();
     if (t == 0) {
       int off = 0;
-      uint32_t cm = 0;
+      uint32_t cm = 0, lbm = 0xFFFFFFFFu;
       bool ok = true;
       for (int q = 0; q < P.S; ++q) {
         const int c = sh_seg[q];
@@ -424,10 +555,11 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
         sh_seg[q] = off;
         off += c;
         cm = max(cm, sh_cutw[q]);
+        lbm = min(lbm, sh_lbw[q]);
       }
       sh_seg[P.S] = off;
       sh_fast = ok;
-      sh_cutw[0] = cm;
+      sh_cutw[0] = max(cm, lbm);     // with top-k: also the smallest slice bound
       sh_n = 0;
     }
     __syncthreads();
@@ -480,7 +612,11 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   if (fast && topk && nfast <= kWaveList) {
     if (t < kWave) {
       ProcStats st;
-      wave_list_stats<BF16>(cand, nfast, zmax, invT, K, topp_on, P.cfg.top_p, h_cnt, h_mass, st);
+      wave_list_stats<BF16>(
+          [&](auto &&f) {
+            for (int i = lane; i < nfast; i += kWave) f(f32_order_key(cand[i]));
+          },
+          zmax, invT, K, topp_on, P.cfg.top_p, h_cnt, h_mass, st);
       if (t == 0) sh_st = st;
     }
     __syncthreads();
@@ -738,66 +874,111 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   }
 }
 
-// The order keys of slice s of row r (kSliceThreads * kSliceLoads 16-byte
-// vectors): lane t holds entries (u * kSliceThreads + t) * VEC + e.  0 marks
-// an entry past the row (every real key is at least the key of -inf,
-// 0x007FFFFF).  16-byte loads when the slice is aligned, else scalar loads.
+// Slice s of row r: kSliceThreads * kSliceLoads 16-byte vectors; lane t
+// owns vectors u * kSliceThreads + t (u < kSliceLoads), whose entry e is entry
+// (u * kSliceThreads + t) * VEC + e of the slice.  The kernels below work on
+// the raw vectors: the float value of an entry is one shift or mask away,
+// and float maxima and minima agree with the order keys (f32_order_key is
+// monotone and maps -0 and +0 to one key).
 template <bool BF16>
-__device__ inline void slice_keys(const ProcParams &P, int r, int s, uint32_t (&key)[kSliceLoads * (BF16 ? 8 : 4)]) {
-  constexpr int VEC = BF16 ? 8 : 4, SL = kSliceThreads * kSliceLoads * VEC;
-  const int t = threadIdx.x;
-  const int v0 = s * SL;
-  const int n = min(P.V - v0, SL);
-  const unsigned char *base = static_cast<const unsigned char *>(proc_row<BF16>(P, r)) + static_cast<size_t>(v0) * (BF16 ? 2 : 4);
-  const bool vec = (reinterpret_cast<uintptr_t>(base) & 15u) == 0;
+struct Slice {
+  static constexpr int VEC = BF16 ? 8 : 4;                 // entries per vector
+  static constexpr int SL = kSliceThreads * kSliceLoads * VEC;
+  const unsigned char *base;   // first entry of the slice
+  int n;                       // entries in the slice
+  bool vec;                    // 16-byte aligned: whole vectors load as they are
+
+  __device__ Slice(const ProcParams &P, int r, int s) {
+    const int v0 = s * SL;
+    n = min(P.V - v0, SL);
+    base = static_cast<const unsigned char *>(proc_row<BF16>(P, r)) + static_cast<size_t>(v0) * (BF16 ? 2 : 4);
+    vec = (reinterpret_cast<uintptr_t>(base) & 15u) == 0;
+  }
+  __device__ int first(int u) const { return (u * kSliceThreads + static_cast<int>(threadIdx.x)) * VEC; }
+  __device__ bool whole(int u) const { return vec && first(u) + VEC <= n; }
+  // Every vector of this lane; an entry past the row reads as -inf.
+  __device__ void load(uint4 (&q)[kSliceLoads]) const {
 #pragma unroll
-  for (int u = 0; u < kSliceLoads; ++u) {
-    const int i0 = (u * kSliceThreads + t) * VEC;
-    if (vec && i0 + VEC <= n) {
-      const uint4 q = reinterpret_cast<const uint4 *>(base)[u * kSliceThreads + t];
-      const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    for (int u = 0; u < kSliceLoads; ++u) {
+      const int i0 = first(u);
+      if (whole(u)) {
+        q[u] = reinterpret_cast<const uint4 *>(base)[u * kSliceThreads + threadIdx.x];
+      } else {
+        uint32_t wd[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if constexpr (BF16) {
-          key[u * VEC + 2 * c] = f32_order_key(__uint_as_float(wd[c] << 16));
-          key[u * VEC + 2 * c + 1] = f32_order_key(__uint_as_float(wd[c] & 0xFFFF0000u));
-        } else {
-          key[u * VEC + c] = f32_order_key(__uint_as_float(wd[c]));
+        for (int e = 0; e < VEC; ++e) {
+          const uint32_t x = __float_as_uint(i0 + e < n ? logit_at<BF16>(base, i0 + e) : -INFINITY);
+          if constexpr (BF16)
+            wd[e >> 1] |= (e & 1) ? (x & 0xFFFF0000u) : (x >> 16);
+          else
+            wd[e] = x;
         }
+        q[u] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        key[u * VEC + e] = i0 + e < n ? f32_order_key(logit_at<BF16>(base, i0 + e)) : 0u;
     }
   }
+};
+
+// Entry e of a loaded vector as a float.
+template <bool BF16>
+__device__ inline float vec_entry(const uint4 &q, int e) {
+  const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+  if constexpr (BF16)
+    return __uint_as_float((e & 1) ? (wd[e >> 1] & 0xFFFF0000u) : (wd[e >> 1] << 16));
+  else
+    return __uint_as_float(wd[e]);
 }
 
-// Top-k candidates of one slice of a row (kSliceThreads * kSliceLoads 16-byte
-// vectors).  Each lane keeps its entries' order keys in registers and takes
-// their maximum; theta is the K-th largest of the 256 lane maxima.  At least K
-// entries (those maxima) are at or above theta, so theta is at most the
-// slice's K-th largest key, and the lanes list every entry at or above it.  A
-// logit at or above the row's K-th largest is among the K largest of its
-// slice, so the union of the slices' lists holds all of them, and no slice's
-// theta exceeds the row's K-th largest key.  A list that does not fit reports
-// its length; the statistics kernel then reads the row whole.  (K <= 256.)
+template <bool BF16>
+__device__ inline float vec_max(const uint4 &q) {
+  float m = vec_entry<BF16>(q, 0);
+#pragma unroll
+  for (int e = 1; e < Slice<BF16>::VEC; ++e) m = fmaxf(m, vec_entry<BF16>(q, e));
+  return m;
+}
+
+// Top-k candidates of one slice.  Each lane takes the float maximum of each
+// of its vectors and of all of them; theta is the K-th largest of the 256
+// lane maxima (as order keys).  At least K entries (those maxima) are at or
+// above theta, so theta is at most the slice's K-th largest key, and the
+// slice lists every entry at or above it.  A logit at or above the row's K-th
+// largest is among the K largest of its slice, so the union of the slices'
+// lists holds all of them, and no slice's theta exceeds the row's K-th
+// largest key.  Listing: the vectors whose maximum reaches theta (about K of
+// them) are staged in LDS and the whole workgroup filters their entries, so
+// only those vectors are looked at twice; when more than kStageCap qualify
+// every lane filters its own.  A list that does not fit reports its length;
+// the statistics kernel then reads the row whole.  (K <= 256.)
+constexpr int kStageCap = 512;
 static_assert(kSliceThreads == 256 && (kSliceThreads & (kSliceThreads - 1)) == 0, "bitonic sort over the lanes");
+static_assert(kSliceThreads * kSliceLoads <= 65536, "vector ids fit 16 bits");
 template <bool BF16>
 __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P) {
-  constexpr int EPL = kSliceLoads * (BF16 ? 8 : 4);
+  using SV = Slice<BF16>;
+  constexpr int VEC = SV::VEC;
   __shared__ uint32_t sh_m[kSliceThreads];
+  __shared__ uint4 sh_vec[kStageCap];
+  __shared__ uint16_t sh_vid[kStageCap];
   __shared__ uint32_t sh_theta;
-  __shared__ int sh_n;
-  const int t = threadIdx.x;
+  __shared__ int sh_nv, sh_n;
+  const int t = threadIdx.x, lane = t & (kWave - 1);
   const int r = blockIdx.x / P.S, s = blockIdx.x - r * P.S;
   const int K = P.cut_rank;
-  uint32_t key[EPL];
-  slice_keys<BF16>(P, r, s, key);
-  uint32_t ml = 0;
+  const SV sl(P, r, s);
+  uint4 q[kSliceLoads];
+  sl.load(q);
+  float fm[kSliceLoads];
+  float fl = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) ml = max(ml, key[i]);
-  if (t == 0) sh_n = 0;
+  for (int u = 0; u < kSliceLoads; ++u) {
+    fm[u] = vec_max<BF16>(q[u]);
+    fl = fmaxf(fl, fm[u]);
+  }
+  const uint32_t ml = sl.first(0) < sl.n ? f32_order_key(fl) : 0u;   // 0: a lane with no entry
+  if (t == 0) {
+    sh_nv = 0;
+    sh_n = 0;
+  }
   // bitonic sort of the 256 lane maxima, descending (strides below a wave by
   // lane shuffles, the others through LDS); lane K - 1 then holds theta
   uint32_t v = ml;
@@ -821,16 +1002,69 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P)
   }
   if (t == K - 1) sh_theta = v;
   if (t == 0 && P.sl_max) P.sl_max[static_cast<size_t>(r) * P.S + s] = v;   // the slice's largest key
+  if (P.list_lb && t == P.lb_rank - 1) P.list_lb[static_cast<size_t>(r) * P.S + s] = v;
   __syncthreads();
   const uint32_t cut = max(sh_theta, 1u);    // a maximum of 0 (no entry) lists every entry
+  // a vector holds a key >= cut iff its float maximum is >= the cut's value
+  // (every real key is at least the key of -inf)
+  const float cutf = cut <= f32_order_key(-INFINITY) ? -INFINITY : f32_from_order_key(cut);
   const int cap = P.seg_cap;
   float *out = P.lists + static_cast<size_t>(r) * kCandCap + static_cast<size_t>(s) * cap;
-  if (ml >= cut) {
+  bool stage[kSliceLoads];
+  int c = 0;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      if (key[i] >= cut) {
-        const int pos = atomicAdd(&sh_n, 1);
-        if (pos < cap) out[pos] = f32_from_order_key(key[i]);
+  for (int u = 0; u < kSliceLoads; ++u) {
+    stage[u] = fm[u] >= cutf && sl.first(u) < sl.n;
+    c += stage[u];
+  }
+  // stage this lane's qualifying vectors at a wave-wide prefix sum
+  const int x = wave_incl_scan(c);
+  const int wtot = read_lane(x, kWave - 1);
+  int pos = 0;
+  if (wtot != 0) {
+    if (lane == kWave - 1) pos = atomicAdd(&sh_nv, wtot);
+    pos = read_lane(pos, kWave - 1);
+  }
+  pos += x - c;
+#pragma unroll
+  for (int u = 0; u < kSliceLoads; ++u) {
+    if (stage[u]) {
+      if (pos < kStageCap) {
+        sh_vec[pos] = q[u];
+        sh_vid[pos] = static_cast<uint16_t>(u * kSliceThreads + t);
+      }
+      ++pos;
+    }
+  }
+  __syncthreads();
+  const int nv = sh_nv;
+  if (nv <= kStageCap) {
+    const int items = nv * VEC;
+    for (int i0 = 0; i0 < items; i0 += kSliceThreads) {     // same trip count in every lane
+      const int i = i0 + t;
+      uint32_t key = 0u;
+      if (i < items) {
+        const int j = i / VEC, e = i - j * VEC;
+        const uint32_t w = reinterpret_cast<const uint32_t *>(&sh_vec[j])[BF16 ? (e >> 1) : e];
+        const float z = __uint_as_float(BF16 ? ((e & 1) ? (w & 0xFFFF0000u) : (w << 16)) : w);
+        if (static_cast<int>(sh_vid[j]) * VEC + e < sl.n) key = f32_order_key(z);
+      }
+      const bool want = key >= cut;
+      const int p = wave_append(want, &sh_n);
+      if (want && p < cap) out[p] = f32_from_order_key(key);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kSliceLoads; ++u) {
+      if (stage[u]) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const uint32_t key = sl.first(u) + e < sl.n ? f32_order_key(vec_entry<BF16>(q[u], e)) : 0u;
+          if (key >= cut) {
+            const int p = atomicAdd(&sh_n, 1);
+            if (p < cap) out[p] = f32_from_order_key(key);
+          }
+        }
       }
     }
   }
@@ -841,30 +1075,20 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P)
   }
 }
 
-__device__ inline uint32_t wave_max_u(uint32_t v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, kWave)));
-  return v;
-}
-__device__ inline uint32_t wave_min_u(uint32_t v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, kWave)));
-  return v;
-}
-
 // Rows without top-k or top-p, step 1: the largest key of each slice.
 template <bool BF16>
 __global__ __launch_bounds__(kSliceThreads) void proc_slrange_kernel(ProcParams P) {
-  constexpr int EPL = kSliceLoads * (BF16 ? 8 : 4), NW = kSliceThreads / kWave;
+  constexpr int NW = kSliceThreads / kWave;
   __shared__ uint32_t sh_hi[NW];
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
   const int r = blockIdx.x / P.S, s = blockIdx.x - r * P.S;
-  uint32_t key[EPL];
-  slice_keys<BF16>(P, r, s, key);
-  uint32_t hi = 0u;
+  const Slice<BF16> sl(P, r, s);
+  uint4 q[kSliceLoads];
+  sl.load(q);
+  float fl = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) hi = max(hi, key[i]);
-  hi = wave_max_u(hi);
+  for (int u = 0; u < kSliceLoads; ++u) fl = fmaxf(fl, vec_max<BF16>(q[u]));
+  uint32_t hi = wave_max_u(sl.first(0) < sl.n ? f32_order_key(fl) : 0u);
   if (lane == 0) sh_hi[w] = hi;
   __syncthreads();
   if (t == 0) {
@@ -875,30 +1099,64 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slrange_kernel(ProcParams 
 
 // Rows without top-k, step 2: the row maximum from the slices' maxima, then
 // each slice's fixed-point weight (an exact integer sum) and smallest key.
+// With a finite row maximum the weight of a -inf logit is exp2(-inf) = 0, as
+// proc_weight gives it, so whole vectors need no test per entry; a lane sums
+// the two 20-bit parts of its fixed-point weights in 32-bit words (at most 64
+// entries of at most 2^20 each) and combines them once.
 template <bool BF16>
 __global__ __launch_bounds__(kSliceThreads) void proc_slmass_kernel(ProcParams P) {
-  constexpr int EPL = kSliceLoads * (BF16 ? 8 : 4), NW = kSliceThreads / kWave;
+  using SV = Slice<BF16>;
+  constexpr int NW = kSliceThreads / kWave, VEC = SV::VEC;
+  static_assert(kSliceLoads * VEC <= 64, "per-lane part sums fit 32 bits");
   __shared__ unsigned long long sh_t[NW];
   __shared__ uint32_t sh_lo[NW];
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
   const int r = blockIdx.x / P.S, s = blockIdx.x - r * P.S;
   uint32_t mk = 0u;
-  for (int q = 0; q < P.S; ++q) mk = max(mk, P.sl_max[static_cast<size_t>(r) * P.S + q]);
+  for (int j = 0; j < P.S; ++j) mk = max(mk, P.sl_max[static_cast<size_t>(r) * P.S + j]);
   const float zmax = f32_from_order_key(mk);
+  const bool finite = zmax != -INFINITY;      // else every weight is 0
   const float invT = P.cfg.invT;
-  uint32_t key[EPL];
-  slice_keys<BF16>(P, r, s, key);
-  unsigned long long tot = 0ull;
-  uint32_t lo = 0xFFFFFFFFu;
+  const SV sl(P, r, s);
+  uint4 q[kSliceLoads];
+  sl.load(q);
+  uint32_t sum_hi = 0u, sum_lo = 0u;
+  float zlo = INFINITY;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    if (key[i] != 0u) {
-      tot += fixed_weight(proc_weight(f32_from_order_key(key[i]), zmax, invT));
-      lo = min(lo, key[i]);
+  for (int u = 0; u < kSliceLoads; ++u) {
+    if (sl.whole(u)) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) zlo = fminf(zlo, vec_entry<BF16>(q[u], e));
+    } else {
+      const int i0 = sl.first(u);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        if (i0 + e < sl.n) {
+          const float z = vec_entry<BF16>(q[u], e);
+          zlo = fminf(zlo, z);
+          const unsigned long long f = finite ? fixed_weight(proc_weight(z, zmax, invT)) : 0ull;
+          sum_hi += static_cast<uint32_t>(f >> 20);
+          sum_lo += static_cast<uint32_t>(f & 0xFFFFFu);
+        }
+      }
     }
   }
-  tot = wave_sum_u64(tot);
-  lo = wave_min_u(lo);
+  if (finite) {
+#pragma unroll
+    for (int u = 0; u < kSliceLoads; ++u) {
+      if (sl.whole(u)) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float a = __expf((vec_entry<BF16>(q[u], e) - zmax) * invT) * 1048576.0f;
+          const uint32_t hi = static_cast<uint32_t>(a);
+          sum_hi += hi;
+          sum_lo += static_cast<uint32_t>((a - static_cast<float>(hi)) * 1048576.0f);
+        }
+      }
+    }
+  }
+  unsigned long long tot = wave_sum_u64((static_cast<unsigned long long>(sum_hi) << 20) + sum_lo);
+  uint32_t lo = wave_min_u(sl.first(0) < sl.n ? f32_order_key(zlo) : 0xFFFFFFFFu);
   if (lane == 0) {
     sh_t[w] = tot;
     sh_lo[w] = lo;
@@ -932,7 +1190,7 @@ __global__ __launch_bounds__(256) void proc_export_kernel(const ProcStats *stats
 // Workspace after the row statistics: candidate lists, then the per-slice
 // arrays, sized for the larger slice count (float32 slices of 8192 logits).
 struct ProcWs {
-  size_t lists, cnt, cut, smax, smin, stot, total;
+  size_t lists, cnt, cut, lb, smax, smin, stot, total;
 };
 static ProcWs proc_ws_layout(int rows, int V) {
   const size_t R = static_cast<size_t>(rows);
@@ -941,7 +1199,8 @@ static ProcWs proc_ws_layout(int rows, int V) {
   L.lists = 0;
   L.cnt = L.lists + round_up(R * kCandCap * sizeof(float), 256);
   L.cut = L.cnt + round_up(R * S * sizeof(int), 256);
-  L.smax = L.cut + round_up(R * S * sizeof(uint32_t), 256);
+  L.lb = L.cut + round_up(R * S * sizeof(uint32_t), 256);
+  L.smax = L.lb + round_up(R * S * sizeof(uint32_t), 256);
   L.smin = L.smax + round_up(R * S * sizeof(uint32_t), 256);
   L.stot = L.smin + round_up(R * S * sizeof(uint32_t), 256);
   L.total = L.stot + round_up(R * S * sizeof(unsigned long long), 256);
@@ -967,6 +1226,8 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
   P.lists = nullptr;
   P.list_cnt = nullptr;
   P.list_cut = nullptr;
+  P.list_lb = nullptr;
+  P.lb_rank = 0;
   P.sl_max = P.sl_min = nullptr;
   P.sl_tot = nullptr;
   const int slice = kSliceThreads * kSliceLoads * (bf16 ? 8 : 4);
@@ -977,11 +1238,15 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
     const ProcWs L = proc_ws_layout(rows, V);
     unsigned char *w = static_cast<unsigned char *>(list_ws);
     const dim3 g(static_cast<unsigned>(rows * P.S)), blk(kSliceThreads);
-    auto lists = [&](int rank) {
+    auto lists = [&](int rank, bool bounds) {
       P.lists = reinterpret_cast<float *>(w + L.lists);
       P.list_cnt = reinterpret_cast<int *>(w + L.cnt);
       P.list_cut = reinterpret_cast<uint32_t *>(w + L.cut);
       P.cut_rank = rank;
+      if (bounds) {               // top-k lists: each slice also gives its ceil(K / S)-th largest lane maximum
+        P.list_lb = reinterpret_cast<uint32_t *>(w + L.lb);
+        P.lb_rank = (top_k + P.S - 1) / P.S;
+      }
       if (bf16)
         hipLaunchKernelGGL(proc_slice_kernel<true>, g, blk, 0, s, P);
       else
@@ -989,7 +1254,7 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
     };
     if (top_k > 0 && top_k < V) {
       // top-k through the slice lists (the cut is the K-th largest of a slice's 256 lane maxima)
-      if (top_k <= kSliceThreads && top_k <= P.seg_cap / 2) lists(top_k);
+      if (top_k <= kSliceThreads && top_k <= P.seg_cap / 2) lists(top_k, true);
     } else {
       // no top-k: slice maxima (with top-p: the lists cut at the kToppRank-th
       // largest lane maximum, which also give them), then slice weights and
@@ -998,7 +1263,7 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
       P.sl_min = reinterpret_cast<uint32_t *>(w + L.smin);
       P.sl_tot = reinterpret_cast<unsigned long long *>(w + L.stot);
       if (top_p < 1.0f && kToppRank <= P.seg_cap / 2) {
-        lists(kToppRank);
+        lists(kToppRank, false);
       } else if (bf16) {
         hipLaunchKernelGGL(proc_slrange_kernel<true>, g, blk, 0, s, P);
       } else {
