@@ -121,6 +121,36 @@ def test_process_topk_crowded_rows(dtype):
         _check_rows(zw, host(process(zd, T, K, P)), T, K, P)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_process_topk_concentrated_rows(dtype):
+    """Rows whose largest logits sit in one slice (the first, the short last
+    one, or two of them): the slices' lower bounds of the K-th largest are far
+    apart, and the candidates the statistics keep must still hold every logit
+    at or above the row's K-th largest."""
+    rng = np.random.default_rng(15)
+    V = 100003
+    sl = 16384 if dtype == "bf16" else 8192
+    S = (V + sl - 1) // sl
+    z = (rng.standard_normal((5, V)) * 1.0).astype(np.float32)
+    hot = [(0, 0), (1, S - 1), (2, 1), (2, S // 2), (3, S // 2)]
+    for r, s in hot:
+        lo = s * sl
+        n = min(400, V - lo)
+        z[r, lo:lo + n] = (8.0 + rng.standard_normal(n)).astype(np.float32)
+    z[4, :] = np.float32(-3.0)
+    z[4, rng.choice(V, 300, replace=False)] = (6.0 + rng.standard_normal(300)).astype(np.float32)
+    if dtype == "bf16":
+        dev_in = W.bf16_bits_from_f32(z)
+        zw = oracle.widen_bf16(dev_in)
+    else:
+        dev_in, zw = z, z
+    zd = logits_to_device(dev_in, dtype)
+    for T, K, P in [(1.0, 1, 1.0), (0.7, 7, 1.0), (0.7, 50, 0.9), (1.0, 200, 1.0), (0.9, 256, 0.95),
+                    (1.0, 64, 0.5)]:
+        note(f"process concentrated {dtype} T={T} K={K} P={P}")
+        _check_rows(zw, host(process(zd, T, K, P)), T, K, P)
+
+
 def test_process_misaligned_rows():
     rng = np.random.default_rng(12)
     V = 1001                                                        # odd: bf16 rows start misaligned
