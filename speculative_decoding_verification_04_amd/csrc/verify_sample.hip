@@ -259,6 +259,7 @@ template <class Src>
 __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleParams P) {
   __shared__ int sh_acc[SPEC_MAX_K];
   __shared__ int sh_st[SPEC_MAX_K];
+  __shared__ int sh_d[SPEC_MAX_K];
   __shared__ int sh_mode, sh_row;
   __shared__ double sh_red[kWaves];
 
@@ -268,10 +269,12 @@ __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleParams P) 
   const int k = P.k, kp1 = k + 1, V = P.V;
   const int32_t *d = P.draft + static_cast<size_t>(b) * k;
   const float *ub = P.u + static_cast<size_t>(b) * kp1;
+  const int rem = P.remaining ? P.remaining[b] : -1;   // negative: no budget (loaded with the drafts)
 
   // ---- acceptance chain: every workgroup of the sequence derives the same row
   for (int j = t; j < k; j += kThreads) {
     const int x = d[j];
+    sh_d[j] = x;
     int st = 0, acc = 0;
     if (x >= 0 && x < V) {
       const float px = Src::p_at(P, b, j, x);
@@ -294,7 +297,6 @@ __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleParams P) 
   }
   __syncthreads();
   if (t == 0) {
-    const int rem = P.remaining ? P.remaining[b] : -1;   // negative: no budget
     int mode = MODE_ROW, row = k, m = 0, st = 0;
     if (rem == 0) {
       mode = MODE_NONE;
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleParams P) 
         st |= sh_st[j];
         if (sh_acc[j]) {
           ++m;
-          if ((P.eos >= 0 && d[j] == P.eos) || m == rem) {
+          if ((P.eos >= 0 && sh_d[j] == P.eos) || m == rem) {
             mode = MODE_NONE;
             break;
           }
@@ -348,19 +350,23 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
     return;
   }
   const int b = blockIdx.x;
+  const int nc = P.chunks;
+  // every load that does not depend on the chain is issued with it: the chunk
+  // masses (read only when a token is drawn), the draw's uniform, the drafts
   const int4 ch = P.chain[b];
+  for (int i = t; i < nc; i += kThreads) sh_part[i] = P.partial[static_cast<size_t>(b) * nc + i];
+  const float u_draw = P.u[static_cast<size_t>(b) * kp1 + k];
+  const int32_t *d = P.draft + static_cast<size_t>(b) * k;
+  const int d_t = t < k ? d[t] : -1;
   const int mode = ch.x, jrow = ch.y, m = ch.z;
   int st = ch.w;
-  const int32_t *d = P.draft + static_cast<size_t>(b) * k;
   int tok = -1;
   double S = 0.0;
   if (mode != MODE_NONE) {
     typename Src::RowT r = Src::row(P, b, jrow, mode == MODE_RESID);
     const bool vec = P.vec != 0;
-    const int nc = P.chunks;
     const int per = (nc + kThreads - 1) / kThreads;  // chunks per lane, consecutive
     const int c0 = t * per;
-    for (int i = t; i < nc; i += kThreads) sh_part[i] = P.partial[static_cast<size_t>(b) * nc + i];
     __syncthreads();
     // total mass and each lane's exclusive prefix over the chunk masses
     double pre = 0.0;
@@ -389,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
     } else if (!(S > 0.0)) {
       tok = 0;
     } else {
-      const double T = static_cast<double>(P.u[static_cast<size_t>(b) * kp1 + k]) * S;
+      const double T = static_cast<double>(u_draw) * S;
       // the first chunk whose running mass exceeds T (else the last chunk with mass)
       int cand = INT_MAX, last = -1;
       {
@@ -465,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
   }
   if (t < kp1) {                                      // accepted drafts, then the drawn token
     int val = -1;
-    if (t < m) val = d[t];
+    if (t < m) val = d_t;
     else if (t == m && mode != MODE_NONE) val = tok;
     P.out_tokens[static_cast<size_t>(b) * kp1 + t] = val;
   }
