@@ -257,17 +257,31 @@ __device__ inline int wave_append(bool want, int *counter) {
 }
 
 
+// Radix levels of 8 bits from bit `top` down to bit `low` (the last one may
+// be narrower).  Keys in [klo, khi] share every bit above the highest bit in
+// which klo and khi differ, so a selection among them starts there: top is
+// that bit, or low - 1 (no level at all) when they agree on every bit from
+// low up.
+__device__ inline int digit_top(uint32_t klo, uint32_t khi, int low) {
+  const uint32_t d = klo ^ khi;
+  return max(d != 0u ? 31 - static_cast<int>(__clz(d)) : -1, low - 1);
+}
+__device__ inline uint32_t bits_above(int top) { return top >= 31 ? 0u : (0xFFFFFFFFu << (top + 1)); }
+
 // Statistics of a short top-k candidate list by one wave, with the choices
 // of the workgroup-wide code below: the same radix digits, tie rules and
 // exact fixed-point sums, in one wave so that no step waits at a workgroup
 // barrier.  each(f) calls f(key) with the order key of every candidate of
 // this lane (0: none); the candidates hold every logit at or above the row's
-// K-th largest and the row's largest.  Lane l owns buckets 255 - 4l ..
-// 252 - 4l (descending) of hc / hm.
+// K-th largest and the row's largest, and their keys lie in [klo, khi].  The
+// digits start below the bits all candidates share (one level instead of two
+// for most bf16 lists); the keys chosen are the same as with fixed digits.
+// Lane l owns buckets 255 - 4l .. 252 - 4l (descending) of hc / hm.
 template <bool BF16, class Each>
-__device__ inline void wave_list_stats(Each &&each, float zmax, float invT, int K, bool topp_on,
-                                       float top_p, uint32_t *hc, unsigned long long *hm, ProcStats &st) {
-  constexpr int kLevels = BF16 ? 2 : 4;
+__device__ inline void wave_list_stats(Each &&each, uint32_t klo, uint32_t khi, float zmax, float invT, int K,
+                                       bool topp_on, float top_p, uint32_t *hc, unsigned long long *hm,
+                                       ProcStats &st) {
+  constexpr int kLow = BF16 ? 16 : 0;            // bf16 keys carry no information below bit 16
   const int lane = threadIdx.x & (kWave - 1);
   auto clear = [&]() {
 #pragma unroll
@@ -278,15 +292,17 @@ __device__ inline void wave_list_stats(Each &&each, float zmax, float invT, int 
     __builtin_amdgcn_wave_barrier();
   };
   auto excl_scan_u64 = [&](unsigned long long v) { return wave_incl_scan(v) - v; };
-  // ---- top-k: the K-th largest key, one 8-bit digit per level
-  uint32_t kprefix = 0u, kmask = 0u;
+  // ---- top-k: the K-th largest key, one digit per level
+  const int ktop = digit_top(klo, khi, kLow);
+  uint32_t kmask = bits_above(ktop), kprefix = klo & kmask;
   if (K > 0) {
     uint32_t need = static_cast<uint32_t>(K);
-    for (int lvl = 0; lvl < kLevels; ++lvl) {
-      const int shift = 24 - 8 * lvl;
+    for (int hi = ktop; hi >= kLow; hi -= 8) {
+      const int shift = max(hi - 7, kLow);
+      const uint32_t dmask = (2u << (hi - shift)) - 1u;
       clear();
       each([&](uint32_t key) {
-        if (key != 0u && (key & kmask) == kprefix) atomicAdd(&hc[(key >> shift) & 255u], 1u);
+        if (key != 0u && (key & kmask) == kprefix) atomicAdd(&hc[(key >> shift) & dmask], 1u);
       });
       __builtin_amdgcn_wave_barrier();
       uint32_t c[4];
@@ -308,24 +324,27 @@ __device__ inline void wave_list_stats(Each &&each, float zmax, float invT, int 
       const int b = read_lane(found, src);
       need = read_lane(rest, src);
       kprefix |= static_cast<uint32_t>(b) << shift;
-      kmask |= 255u << shift;
+      kmask |= dmask << shift;
     }
   }
-  const uint32_t tau = kprefix;
+  const uint32_t tau = K > 0 ? kprefix : 0u;
   // ---- top-p over the survivors: the lowest non-empty bucket whose heavier
   //      buckets weigh less than top_p times the total, one digit per level
   uint32_t theta = tau;
   if (topp_on) {
-    uint32_t pprefix = 0u, pmask = 0u;
+    const uint32_t plo = max(tau, klo);          // the survivors' keys lie in [plo, khi]
+    const int ptop = digit_top(plo, khi, kLow);
+    uint32_t pmask = bits_above(ptop), pprefix = plo & pmask;
     unsigned long long above = 0ull;
     double thr = 0.0;
-    bool dead = false;
-    for (int lvl = 0; lvl < kLevels; ++lvl) {
-      const int shift = 24 - 8 * lvl;
+    bool dead = false, first = true;
+    for (int hi = ptop; hi >= kLow; hi -= 8) {
+      const int shift = max(hi - 7, kLow);
+      const uint32_t dmask = (2u << (hi - shift)) - 1u;
       clear();
       each([&](uint32_t key) {
         if (key != 0u && key >= tau && (key & pmask) == pprefix) {
-          const uint32_t d = (key >> shift) & 255u;
+          const uint32_t d = (key >> shift) & dmask;
           atomicAdd(&hc[d], 1u);
           atomicAdd(&hm[d], fixed_weight(proc_weight(f32_from_order_key(key), zmax, invT)));
         }
@@ -340,7 +359,8 @@ __device__ inline void wave_list_stats(Each &&each, float zmax, float invT, int 
       }
       const unsigned long long lsum = mw[0] + mw[1] + mw[2] + mw[3];
       unsigned long long run = excl_scan_u64(lsum);
-      if (lvl == 0) thr = static_cast<double>(top_p) * static_cast<double>(wave_sum_u64(lsum));
+      if (first) thr = static_cast<double>(top_p) * static_cast<double>(wave_sum_u64(lsum));   // every survivor
+      first = false;
       int best = -1;
       unsigned long long sbest = 0ull;
 #pragma unroll
@@ -358,7 +378,7 @@ __device__ inline void wave_list_stats(Each &&each, float zmax, float invT, int 
       }
       above += read_lane(sbest, pos >> 2);
       pprefix |= static_cast<uint32_t>(255 - pos) << shift;
-      pmask |= 255u << shift;
+      pmask |= dmask << shift;
     }
     if (!dead) theta = pprefix;
   }
@@ -392,7 +412,8 @@ __device__ inline void wave_list_stats(Each &&each, float zmax, float invT, int 
 // So `cand` holds every logit at or above the row's K-th largest, and the
 // row's largest.  Returns the count (zmax: the largest), or -1 when the lists
 // do not fit this shape (nothing written).
-__device__ inline int wave_gather_topk(const ProcParams &P, int r, float *cand, float &zmax) {
+__device__ inline int wave_gather_topk(const ProcParams &P, int r, float *cand, float &zmax, uint32_t &klo,
+                                       uint32_t &khi) {
   const int lane = threadIdx.x & (kWave - 1);
   const int S = P.S;
   if (S > kGatherS || P.list_lb == nullptr) return -1;
@@ -427,7 +448,9 @@ __device__ inline int wave_gather_topk(const ProcParams &P, int r, float *cand, 
       n += __popcll(m);
     }
   }
-  zmax = f32_from_order_key(wave_max_u(mk));
+  khi = wave_max_u(mk);
+  klo = min(max(lo, 1u), khi);
+  zmax = f32_from_order_key(khi);
   return n;
 }
 
@@ -509,14 +532,15 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   if (P.lists && topk) {
     if (t < kWave) {
       float zm;
-      const int n = wave_gather_topk(P, r, cand, zm);
+      uint32_t klo, khi;
+      const int n = wave_gather_topk(P, r, cand, zm, klo, khi);
       if (n >= 0) {
         ProcStats st;
         wave_list_stats<BF16>(
             [&](auto &&f) {
               for (int i = lane; i < n; i += kWave) f(f32_order_key(cand[i]));
             },
-            zm, invT, K, topp && zm != -INFINITY, P.cfg.top_p, h_cnt, h_mass, st);
+            klo, khi, zm, invT, K, topp && zm != -INFINITY, P.cfg.top_p, h_cnt, h_mass, st);
         if (t == 0) sh_st = st;
       }
       if (t == 0) sh_fast = n >= 0;
@@ -612,11 +636,12 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   if (fast && topk && nfast <= kWaveList) {
     if (t < kWave) {
       ProcStats st;
+      const uint32_t khi = f32_order_key(zmax);
       wave_list_stats<BF16>(
           [&](auto &&f) {
             for (int i = lane; i < nfast; i += kWave) f(f32_order_key(cand[i]));
           },
-          zmax, invT, K, topp_on, P.cfg.top_p, h_cnt, h_mass, st);
+          min(max(cutmax, 1u), khi), khi, zmax, invT, K, topp_on, P.cfg.top_p, h_cnt, h_mass, st);
       if (t == 0) sh_st = st;
     }
     __syncthreads();
