@@ -479,7 +479,6 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   const int r = blockIdx.x;
   const int V = P.V;
   const void *row = proc_row<BF16>(P, r);
-  constexpr int kLevels = BF16 ? 2 : 4;        // 8-bit digits of the significant key bits
   const float invT = P.cfg.invT;
   const int K = P.cfg.top_k;
   const bool topk = K > 0 && K < V;
@@ -663,10 +662,18 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   unsigned long long above = 0;
   double thr = 0.0;
   bool p_started = false, p_dead = false;
+  // Digits: 8 bits from a top bit down to kLow (the last may be narrower).
+  // Whole-row histograms start at bit 31; a list whose keys lie in [klo, khi]
+  // starts below the bits they all share (at least one full digit).
+  constexpr int kLow = BF16 ? 16 : 0;            // bf16 keys carry no information below bit 16
+  int k_hi = 31, p_hi = 31;                      // top bit of the next top-k / top-p digit
+  const uint32_t khi = f32_order_key(zmax);
+  auto list_top = [&](uint32_t klo) { return max(digit_top(min(max(klo, 1u), khi), khi, kLow), kLow + 7); };
+  auto digit_mask = [](int hi, int shift) { return (2u << (hi - shift)) - 1u; };
 
   // Picks the top-k bucket at `shift` from h_cnt; returns the count of keys
   // in the chosen bucket and above.  Barriers.
-  auto select_k = [&](int shift) -> int {
+  auto select_k = [&](int shift, uint32_t dmask) -> int {
     const int tb = 255 - t;
     const unsigned long long c = t < 256 ? h_cnt[tb] : 0ull;
     const unsigned long long S = sum_above(c, sh4);
@@ -678,7 +685,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
     __syncthreads();
     need = sh_need;
     kprefix = sh_prefix;
-    kmask |= 255u << shift;
+    kmask |= dmask << shift;
     const int n = sh_ncand;
     __syncthreads();
     return n;
@@ -686,7 +693,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   // Picks the top-p bucket at `shift` from h_cnt / h_mass (level 0 also fixes
   // the threshold top_p * total); returns the count in the bucket and above.
   unsigned long long hist_total = 0;          // level 0: the weight the histogram saw
-  auto select_p = [&](int shift, bool first, unsigned long long row_total) -> int {
+  auto select_p = [&](int shift, uint32_t dmask, bool first, unsigned long long row_total) -> int {
     const int tb = 255 - t;
     const unsigned long long mw = t < 256 ? h_mass[tb] : 0ull;
     const unsigned long long cw = t < 256 ? h_cnt[tb] : 0ull;
@@ -715,7 +722,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
     } else {
       pprefix = np;
       above = sh_above;
-      pmask |= 255u << shift;
+      pmask |= dmask << shift;
     }
     __syncthreads();
     return n;
@@ -725,10 +732,15 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   uint32_t cutoff = 0;
   bool use_list = fast && topk;                // every level runs on the slice lists
   if (fast && topk) {
-    // every top-k level, the first included, runs on the list below
+    // every top-k level, the first included, runs on the list below, whose
+    // keys lie in [cutmax, khi]
+    k_hi = list_top(cutmax);
+    kmask = bits_above(k_hi);
+    kprefix = min(max(cutmax, 1u), khi) & kmask;
   } else if (topk) {
     fold_columns(lh, h_cnt, h_mass);
-    ncand = select_k(24);
+    ncand = select_k(24, 255u);
+    k_hi = 23;
     cutoff = kprefix;
   } else if (topp_on) {
     if (fast) {
@@ -742,18 +754,24 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
         h_cnt[t] = 0u;
         h_mass[t] = 0ull;
       }
+      const int top = list_top(cutmax);          // the union's keys lie in [cutmax, khi]
+      const int shift = max(top - 7, kLow);
+      const uint32_t dmask = digit_mask(top, shift);
+      pmask = bits_above(top);
+      pprefix = min(max(cutmax, 1u), khi) & pmask;
       __syncthreads();
       for (int i = t; i < nfast; i += kProcThreads) {
         const float z = cand[i];
-        const uint32_t key = f32_order_key(z);
-        atomicAdd(&h_cnt[key >> 24], 1u);
-        atomicAdd(&h_mass[key >> 24], fixed_weight(proc_weight(z, zmax, invT)));
+        const uint32_t d = (f32_order_key(z) >> shift) & dmask;
+        atomicAdd(&h_cnt[d], 1u);
+        atomicAdd(&h_mass[d], fixed_weight(proc_weight(z, zmax, invT)));
       }
       __syncthreads();
-      ncand = select_p(24, true, row_total);
+      ncand = select_p(shift, dmask, true, row_total);
       if (!p_dead && static_cast<double>(hist_total) >= thr) {
         use_list = true;
         p_started = true;
+        p_hi = shift - 1;
         cutoff = pprefix;
       } else {                                   // read the row after all
         p_dead = false;
@@ -771,8 +789,9 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
       });
       __syncthreads();
       fold_columns(lh, h_cnt, h_mass);
-      ncand = select_p(24, true, 0ull);
+      ncand = select_p(24, 255u, true, 0ull);
       p_started = true;
+      p_hi = 23;
       if (!p_dead) cutoff = pprefix;
     }
   }
@@ -797,9 +816,9 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
       row_foreach<BF16>(row, V, [&](int, float z) { f(z); });
     }
   };
-  // Histogram of digit (key >> shift) & 255 over the logits passing `pred`,
+  // Histogram of digit (key >> shift) & dmask over the logits passing `pred`,
   // with weights if asked, into h_cnt / h_mass.  Barriers.
-  auto histogram = [&](int shift, bool weights, auto &&pred) {
+  auto histogram = [&](int shift, uint32_t dmask, bool weights, auto &&pred) {
     if (listed) {
       for (int i = t; i < 256; i += kProcThreads) {
         h_cnt[i] = 0;
@@ -809,7 +828,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
       each([&](float z) {
         const uint32_t key = f32_order_key(z);
         if (pred(key)) {
-          const uint32_t d = (key >> shift) & 255u;
+          const uint32_t d = (key >> shift) & dmask;
           atomicAdd(&h_cnt[d], 1u);
           if (weights) atomicAdd(&h_mass[d], fixed_weight(proc_weight(z, zmax, invT)));
         }
@@ -823,7 +842,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
         if (pred(key)) {
           unsigned long long add = one;
           if (weights) add += fixed_weight(proc_weight(z, zmax, invT));
-          atomicAdd(&lh[((key >> shift) & 255u) * kWave + lane], add);
+          atomicAdd(&lh[((key >> shift) & dmask) * kWave + lane], add);
         }
       });
       __syncthreads();
@@ -834,11 +853,12 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   // ---- top-k: remaining digits
   uint32_t tau = 0;
   if (topk) {
-    for (int lvl = use_list ? 0 : 1; lvl < kLevels; ++lvl) {
-      const int shift = 24 - 8 * lvl;
+    for (int hi = k_hi; hi >= kLow; hi -= 8) {
+      const int shift = max(hi - 7, kLow);
+      const uint32_t dmask = digit_mask(hi, shift);
       const uint32_t pf = kprefix, pm = kmask;
-      histogram(shift, false, [&](uint32_t key) { return (key & pm) == pf; });
-      select_k(shift);
+      histogram(shift, dmask, false, [&](uint32_t key) { return (key & pm) == pf; });
+      select_k(shift, dmask);
     }
     tau = kprefix;   // the smallest key with the selected significant bits
   }
@@ -846,11 +866,19 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   // ---- top-p over the top-k survivors
   uint32_t theta = tau;
   if (topp_on) {
-    for (int lvl = p_started ? 1 : 0; lvl < kLevels && !p_dead; ++lvl) {
-      const int shift = 24 - 8 * lvl;
+    if (!p_started && topk) {                    // the survivors' keys lie in [tau, khi]
+      p_hi = list_top(tau);
+      pmask = bits_above(p_hi);
+      pprefix = min(max(tau, 1u), khi) & pmask;
+    }
+    bool first = !p_started;
+    for (int hi = p_hi; hi >= kLow && !p_dead; hi -= 8) {
+      const int shift = max(hi - 7, kLow);
+      const uint32_t dmask = digit_mask(hi, shift);
       const uint32_t pf = pprefix, pm = pmask, tk = tau;
-      histogram(shift, true, [&](uint32_t key) { return key >= tk && (key & pm) == pf; });
-      select_p(shift, lvl == 0, 0ull);
+      histogram(shift, dmask, true, [&](uint32_t key) { return key >= tk && (key & pm) == pf; });
+      select_p(shift, dmask, first, 0ull);
+      first = false;
     }
     if (!p_dead) theta = pprefix;
   }
