@@ -470,6 +470,10 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   __shared__ int sh_seg[kSliceMaxS + 1];
   __shared__ uint32_t sh_cutw[kSliceMaxS];
   __shared__ uint32_t sh_lbw[kSliceMaxS];
+  __shared__ unsigned long long sh_stot[kSliceMaxS];
+  __shared__ uint32_t sh_smax[kSliceMaxS];
+  __shared__ uint32_t sh_mk;
+  __shared__ unsigned long long sh_rowtot;
   __shared__ bool sh_fast;
   __shared__ ProcStats sh_st;
 
@@ -559,18 +563,30 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   bool fast = false;
   int nfast = 0;
   uint32_t cutmax = 0;
+  // rows without top-k through the slice kernels: the maximum (and the exact
+  // weight) from the slices
+  const bool smode = P.sl_max != nullptr && !topk;
+  float m = -INFINITY;
+  bool have_slices = false;                      // sh_mk / sh_rowtot hold the slices' maximum and weight
   if (P.lists && (topk || (P.sl_max != nullptr && topp))) {
-    // segment offsets (prefix of the list lengths) and the largest slice cut
+    // segment offsets (prefix of the list lengths) and the largest slice cut;
+    // in slice mode the slices' maxima and weights come in the same round
     if (t < P.S) {
-      const int c = P.list_cnt[static_cast<size_t>(r) * P.S + t];
+      const size_t i = static_cast<size_t>(r) * P.S + t;
+      const int c = P.list_cnt[i];
       sh_seg[t] = c;
-      sh_cutw[t] = P.list_cut[static_cast<size_t>(r) * P.S + t];
-      sh_lbw[t] = topk && P.list_lb ? P.list_lb[static_cast<size_t>(r) * P.S + t] : 0u;
+      sh_cutw[t] = P.list_cut[i];
+      sh_lbw[t] = topk && P.list_lb ? P.list_lb[i] : 0u;
+      if (smode) {
+        sh_smax[t] = P.sl_max[i];
+        sh_stot[t] = P.sl_tot[i];
+      }
     }
     __syncthreads();
     if (t == 0) {
       int off = 0;
-      uint32_t cm = 0, lbm = 0xFFFFFFFFu;
+      uint32_t cm = 0, lbm = 0xFFFFFFFFu, mk = 0u;
+      unsigned long long tw = 0ull;
       bool ok = true;
       for (int q = 0; q < P.S; ++q) {
         const int c = sh_seg[q];
@@ -579,42 +595,58 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
         off += c;
         cm = max(cm, sh_cutw[q]);
         lbm = min(lbm, sh_lbw[q]);
+        if (smode) {
+          mk = max(mk, sh_smax[q]);
+          tw += sh_stot[q];
+        }
       }
       sh_seg[P.S] = off;
       sh_fast = ok;
       sh_cutw[0] = max(cm, lbm);     // with top-k: also the smallest slice bound
+      sh_mk = mk;
+      sh_rowtot = tw;
       sh_n = 0;
     }
     __syncthreads();
     fast = sh_fast;
     cutmax = sh_cutw[0];
+    have_slices = smode;
   }
-  // rows without top-k through the slice kernels: the maximum from the slices
-  const bool smode = P.sl_max != nullptr && !topk;
-  float m = -INFINITY;
   if (smode) {
     uint32_t mk = 0;
-    for (int q = 0; q < P.S; ++q) mk = max(mk, P.sl_max[static_cast<size_t>(r) * P.S + q]);
+    if (have_slices)
+      mk = sh_mk;
+    else
+      for (int q = 0; q < P.S; ++q) mk = max(mk, P.sl_max[static_cast<size_t>(r) * P.S + q]);
     m = f32_from_order_key(mk);
   }
   if (fast) {
     // every slice's cut is at most the row's K-th largest key: entries below
-    // the largest cut cannot be kept.  One independent load per entry.
+    // the largest cut cannot be kept.  kCopyU independent loads per lane are
+    // issued before any entry is appended.
+    constexpr int kCopyU = 4;
     const int tot = sh_seg[P.S];
-    for (int g0 = 0; g0 < tot; g0 += kProcThreads) {   // same trip count in every lane
-      const int g = g0 + t;
-      float z = -INFINITY;
-      bool keep = false;
-      if (g < tot) {
-        int q = 0;
-        while (sh_seg[q + 1] <= g) ++q;
-        z = P.lists[static_cast<size_t>(r) * kCandCap + static_cast<size_t>(q) * P.seg_cap + (g - sh_seg[q])];
-        keep = f32_order_key(z) >= cutmax;
+    for (int g0 = 0; g0 < tot; g0 += kProcThreads * kCopyU) {   // same trip count in every lane
+      float z[kCopyU];
+#pragma unroll
+      for (int u = 0; u < kCopyU; ++u) {
+        const int g = g0 + u * kProcThreads + t;
+        z[u] = 0.0f;
+        if (g < tot) {
+          int q = 0;
+          while (sh_seg[q + 1] <= g) ++q;
+          z[u] = P.lists[static_cast<size_t>(r) * kCandCap + static_cast<size_t>(q) * P.seg_cap + (g - sh_seg[q])];
+        }
       }
-      const int slot = wave_append(keep, &sh_n);
-      if (keep) {
-        cand[slot] = z;
-        m = fmaxf(m, z);
+#pragma unroll
+      for (int u = 0; u < kCopyU; ++u) {
+        const int g = g0 + u * kProcThreads + t;
+        const bool keep = g < tot && f32_order_key(z[u]) >= cutmax;
+        const int slot = wave_append(keep, &sh_n);
+        if (keep) {
+          cand[slot] = z[u];
+          m = fmaxf(m, z[u]);
+        }
       }
     }
   } else if (!smode) {
@@ -748,8 +780,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
       // largest slice cut.  Level 0 from the union's histogram, with the
       // threshold from the row's exact weight; valid when the union itself
       // weighs at least top_p of the row (then no logit outside it is kept).
-      unsigned long long row_total = 0;
-      for (int q = 0; q < P.S; ++q) row_total += P.sl_tot[static_cast<size_t>(r) * P.S + q];
+      const unsigned long long row_total = sh_rowtot;   // read with the lists (slice mode)
       if (t < 256) {
         h_cnt[t] = 0u;
         h_mass[t] = 0ull;
