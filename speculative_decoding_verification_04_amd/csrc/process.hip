@@ -207,16 +207,17 @@ __device__ inline void clear_columns(unsigned long long *lh) {
   for (int i = threadIdx.x; i < 256 * kWave; i += kProcThreads) lh[i] = 0ull;
 }
 
-// Lanes t < 256 own bucket 255 - t (descending buckets in lane order).  Returns
-// for those lanes the sum of v over the buckets above their own (an exclusive
-// prefix in lane order).  Every lane of the block must call it (barriers).
-__device__ inline unsigned long long sum_above(unsigned long long v, unsigned long long *sh4) {
+// Lane t owns bucket nb - 1 - t (descending buckets in lane order; lanes past
+// the buckets pass 0).  Returns the sum of v over the lanes before this one:
+// for a bucket lane, the sum over the buckets above its own.  `sh` holds one
+// word per wave.  Every lane of the block must call it (barriers).
+__device__ inline unsigned long long sum_above(unsigned long long v, unsigned long long *sh) {
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
   const unsigned long long inc = wave_incl_scan(v);
-  if (lane == kWave - 1 && w < 4) sh4[w] = inc;
+  if (lane == kWave - 1) sh[w] = inc;
   __syncthreads();
   unsigned long long base = 0;
-  for (int i = 0; i < w && i < 4; ++i) base += sh4[i];
+  for (int i = 0; i < w; ++i) base += sh[i];
   __syncthreads();
   return base + inc - v;
 }
@@ -458,13 +459,13 @@ template <bool BF16>
 __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) {
   // per-lane histogram columns (128 KB); reused as the candidate list
   __shared__ unsigned long long lh[256 * kWave];
-  __shared__ uint32_t h_cnt[256];
-  __shared__ unsigned long long h_mass[256];
+  __shared__ uint32_t h_cnt[kProcThreads];     // one bucket per lane (10-bit digits on lists)
+  __shared__ unsigned long long h_mass[kProcThreads];
   __shared__ float sh_f[kProcWaves];
   __shared__ uint32_t sh_prefix;
   __shared__ int sh_need, sh_ncand, sh_n;
   __shared__ unsigned long long sh_above, sh_tot;
-  __shared__ unsigned long long sh4[4];
+  __shared__ unsigned long long sh4[kProcWaves];
   __shared__ int sh_i[kProcWaves];
   __shared__ unsigned long long sh_u[kProcWaves];
   __shared__ int sh_seg[kSliceMaxS + 1];
@@ -694,10 +695,13 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   unsigned long long above = 0;
   double thr = 0.0;
   bool p_started = false, p_dead = false;
-  // Digits: 8 bits from a top bit down to kLow (the last may be narrower).
-  // Whole-row histograms start at bit 31; a list whose keys lie in [klo, khi]
-  // starts below the bits they all share (at least one full digit).
+  // Digits from a top bit down to kLow (the last may be narrower): 8 bits on
+  // whole-row histograms (256 buckets x 64 lane columns), 10 bits on LDS
+  // lists (one bucket per lane).  Whole-row histograms start at bit 31; a
+  // list whose keys lie in [klo, khi] starts below the bits they all share.
   constexpr int kLow = BF16 ? 16 : 0;            // bf16 keys carry no information below bit 16
+  constexpr int kRowDigit = 8, kListDigit = 10;
+  static_assert((1 << kListDigit) == kProcThreads, "one list bucket per lane");
   int k_hi = 31, p_hi = 31;                      // top bit of the next top-k / top-p digit
   const uint32_t khi = f32_order_key(zmax);
   auto list_top = [&](uint32_t klo) { return max(digit_top(min(max(klo, 1u), khi), khi, kLow), kLow + 7); };
@@ -706,10 +710,11 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   // Picks the top-k bucket at `shift` from h_cnt; returns the count of keys
   // in the chosen bucket and above.  Barriers.
   auto select_k = [&](int shift, uint32_t dmask) -> int {
-    const int tb = 255 - t;
-    const unsigned long long c = t < 256 ? h_cnt[tb] : 0ull;
+    const int nb = static_cast<int>(dmask) + 1;
+    const int tb = nb - 1 - t;
+    const unsigned long long c = t < nb ? h_cnt[tb] : 0ull;
     const unsigned long long S = sum_above(c, sh4);
-    if (t < 256 && S < static_cast<unsigned long long>(need) && static_cast<unsigned long long>(need) <= S + c) {
+    if (t < nb && S < static_cast<unsigned long long>(need) && static_cast<unsigned long long>(need) <= S + c) {
       sh_need = need - static_cast<int>(S);
       sh_prefix = kprefix | (static_cast<uint32_t>(tb) << shift);
       sh_ncand = static_cast<int>(S + c);
@@ -726,18 +731,19 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   // the threshold top_p * total); returns the count in the bucket and above.
   unsigned long long hist_total = 0;          // level 0: the weight the histogram saw
   auto select_p = [&](int shift, uint32_t dmask, bool first, unsigned long long row_total) -> int {
-    const int tb = 255 - t;
-    const unsigned long long mw = t < 256 ? h_mass[tb] : 0ull;
-    const unsigned long long cw = t < 256 ? h_cnt[tb] : 0ull;
+    const int nb = static_cast<int>(dmask) + 1;
+    const int tb = nb - 1 - t;
+    const unsigned long long mw = t < nb ? h_mass[tb] : 0ull;
+    const unsigned long long cw = t < nb ? h_cnt[tb] : 0ull;
     const unsigned long long S = sum_above(mw, sh4);
     const unsigned long long SC = sum_above(cw, sh4);
     if (first) {
-      if (t == 255) sh_tot = S + mw;
+      if (t == nb - 1) sh_tot = S + mw;
       __syncthreads();
       hist_total = sh_tot;
       thr = static_cast<double>(P.cfg.top_p) * static_cast<double>(row_total ? row_total : hist_total);
     }
-    const bool ok = t < 256 && cw > 0 && static_cast<double>(above + S) < thr;
+    const bool ok = t < nb && cw > 0 && static_cast<double>(above + S) < thr;
     const int win = block_max_int(ok ? t : -1, sh_i);   // largest lane = lowest bucket
     if (win < 0) {
       if (t == 0) sh_prefix = 0xFFFFFFFFu;
@@ -781,12 +787,10 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
       // threshold from the row's exact weight; valid when the union itself
       // weighs at least top_p of the row (then no logit outside it is kept).
       const unsigned long long row_total = sh_rowtot;   // read with the lists (slice mode)
-      if (t < 256) {
-        h_cnt[t] = 0u;
-        h_mass[t] = 0ull;
-      }
+      h_cnt[t] = 0u;                             // one bucket per lane
+      h_mass[t] = 0ull;
       const int top = list_top(cutmax);          // the union's keys lie in [cutmax, khi]
-      const int shift = max(top - 7, kLow);
+      const int shift = max(top - (kListDigit - 1), kLow);
       const uint32_t dmask = digit_mask(top, shift);
       pmask = bits_above(top);
       pprefix = min(max(cutmax, 1u), khi) & pmask;
@@ -851,10 +855,8 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   // with weights if asked, into h_cnt / h_mass.  Barriers.
   auto histogram = [&](int shift, uint32_t dmask, bool weights, auto &&pred) {
     if (listed) {
-      for (int i = t; i < 256; i += kProcThreads) {
-        h_cnt[i] = 0;
-        h_mass[i] = 0ull;
-      }
+      h_cnt[t] = 0u;                             // one bucket per lane
+      h_mass[t] = 0ull;
       __syncthreads();
       each([&](float z) {
         const uint32_t key = f32_order_key(z);
@@ -883,9 +885,10 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
 
   // ---- top-k: remaining digits
   uint32_t tau = 0;
+  const int digit = listed ? kListDigit : kRowDigit;
   if (topk) {
-    for (int hi = k_hi; hi >= kLow; hi -= 8) {
-      const int shift = max(hi - 7, kLow);
+    for (int hi = k_hi; hi >= kLow; hi -= digit) {
+      const int shift = max(hi - (digit - 1), kLow);
       const uint32_t dmask = digit_mask(hi, shift);
       const uint32_t pf = kprefix, pm = kmask;
       histogram(shift, dmask, false, [&](uint32_t key) { return (key & pm) == pf; });
@@ -903,8 +906,8 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
       pprefix = min(max(tau, 1u), khi) & pmask;
     }
     bool first = !p_started;
-    for (int hi = p_hi; hi >= kLow && !p_dead; hi -= 8) {
-      const int shift = max(hi - 7, kLow);
+    for (int hi = p_hi; hi >= kLow && !p_dead; hi -= digit) {
+      const int shift = max(hi - (digit - 1), kLow);
       const uint32_t dmask = digit_mask(hi, shift);
       const uint32_t pf = pprefix, pm = pmask, tk = tau;
       histogram(shift, dmask, true, [&](uint32_t key) { return key >= tk && (key & pm) == pf; });
