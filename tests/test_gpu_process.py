@@ -151,6 +151,18 @@ def test_process_topk_concentrated_rows(dtype):
         _check_rows(zw, host(process(zd, T, K, P)), T, K, P)
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 393216), ("bf16", 393217), ("f32", 196608), ("f32", 196609)])
+def test_process_topk_slice_count_boundary(dtype, V):
+    """Rows of 24 slices (one wave gathers the lists) and of 25 (the workgroup
+    path), with K such that some lists hold about 64 entries."""
+    rng = np.random.default_rng(16)
+    dev_in, zw = _rows(rng, 3, V, dtype, sd=2.0)
+    zd = logits_to_device(dev_in, dtype)
+    for T, K, P in [(0.7, 50, 0.9), (1.0, 60, 1.0), (1.0, 200, 0.95)]:
+        note(f"process slice-count boundary {dtype} V={V} T={T} K={K} P={P}")
+        _check_rows(zw, host(process(zd, T, K, P)), T, K, P)
+
+
 def test_process_misaligned_rows():
     rng = np.random.default_rng(12)
     V = 1001                                                        # odd: bf16 rows start misaligned
