@@ -299,14 +299,21 @@ __global__ __launch_bounds__(kCompactThreads) void tree_compact_kernel(CompactPa
   const int rest = blk / P.B;
   const int hs = rest % P.hsplit;
   const int lk = rest / P.hsplit;           // layer * 2 + (K or V)
+  // the path row is read with the counts (one round of loads): lanes t < N
+  // read entries t and t - 1, used where t < e
+  const int32_t *pb = P.path + static_cast<size_t>(b) * P.N;
+  int node_t = -1, prev_t = -1;
+  if (t < P.N) {
+    node_t = pb[t];
+    if (t > 0) prev_t = pb[t - 1];
+  }
   const int E = P.end_col[0];
   const int e = P.emit_count[b];
   const bool shape_ok = E >= 0 && E <= P.C - P.N && e >= 0 && e <= P.N;
   int node = -1, prev = -1;
   if (shape_ok && t < e) {
-    const int32_t *pb = P.path + static_cast<size_t>(b) * P.N;
-    node = pb[t];
-    prev = t > 0 ? pb[t - 1] : -1;
+    node = node_t;
+    prev = prev_t;
   }
   const bool lane_ok = t >= e || (node > prev && node < P.N && (t > 0 || node == 0));
   const bool ok = shape_ok && __syncthreads_and(lane_ok);
