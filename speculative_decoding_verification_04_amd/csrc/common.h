@@ -3,7 +3,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
 #include <stdint.h>
 
 #include "spec_verify.h"
@@ -139,35 +138,25 @@ __device__ inline int wave_max_i(int v) {
   return wave_reduce(v, [](int a, int b) { return max(a, b); });
 }
 __device__ inline double wave_sum_d(double v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  return wave_reduce(v, [](double a, double b) { return a + b; });
 }
 
 // Inclusive scan across one wavefront (lane order); every lane of the wave
-// must be active.  Integers: DPP row shifts give each row of 16 its own
-// prefix, then the rows' totals (lanes 15, 31, 47) are added to the rows
-// above.  Floating point keeps the lane-shuffle order of additions.
+// must be active.  DPP row shifts give each row of 16 its own prefix, then the
+// rows' totals (lanes 15, 31, 47) are added to the rows above.  For floating
+// point this is a fixed order of additions (the same in every call).
 template <typename T>
 __device__ inline T wave_incl_scan(T v) {
   const int lane = threadIdx.x & (kWave - 1);
-  if constexpr (std::is_integral<T>::value) {
-    v += dpp_move<kDppRowShr1>(v, T(0));
-    v += dpp_move<kDppRowShr2>(v, T(0));
-    v += dpp_move<kDppRowShr4>(v, T(0));
-    v += dpp_move<kDppRowShr8>(v, T(0));
-    const T r0 = read_lane(v, 15), r1 = read_lane(v, 31), r2 = read_lane(v, 47);
-    const int row = lane >> 4;
-    if (row >= 1) v += r0;
-    if (row >= 2) v += r1;
-    if (row >= 3) v += r2;
-  } else {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      T o = __shfl_up(v, d, kWave);
-      if (lane >= d) v += o;
-    }
-  }
+  v += dpp_move<kDppRowShr1>(v, T(0));
+  v += dpp_move<kDppRowShr2>(v, T(0));
+  v += dpp_move<kDppRowShr4>(v, T(0));
+  v += dpp_move<kDppRowShr8>(v, T(0));
+  const T r0 = read_lane(v, 15), r1 = read_lane(v, 31), r2 = read_lane(v, 47);
+  const int row = lane >> 4;
+  if (row >= 1) v += r0;
+  if (row >= 2) v += r1;
+  if (row >= 3) v += r2;
   return v;
 }
 
