@@ -198,6 +198,7 @@ __global__ __launch_bounds__(kThreads) void greedy_chunk_kernel(GreedyParams P) 
 constexpr int kCommitThreads = 1024;
 constexpr int kCommitRows = 1024;   // row keys folded per tile (LDS)
 constexpr int kKeysPerThread = 16;  // chunk keys in flight per lane
+static_assert(kCommitRows == kCommitThreads, "one row (and at most one draft) per lane of a tile");
 
 // One workgroup.  Per tile of sequences, every global read (chunk keys, drafts,
 // budgets) is issued at once into LDS; the walk then runs from LDS only.
@@ -214,13 +215,16 @@ __global__ __launch_bounds__(kCommitThreads) void greedy_commit_kernel(GreedyPar
     const int ns = min(per_tile, P.B - s0);
     const int nrows = ns * kp1;
     // one round trip: drafts, budgets and every chunk key are requested before
-    // any is used; lane r folds row r's keys in registers (no LDS atomics)
+    // any is used (into registers; LDS is written once all have landed); lane
+    // r folds row r's keys (no LDS atomics).  A tile holds at most one draft
+    // and one row per lane: ns * k < ns * (k + 1) <= kCommitRows.
     const uint64_t *kb = P.keys + static_cast<size_t>(s0) * kp1 * P.chunks;
-    for (int i = t; i < ns * P.k; i += kCommitThreads) sh_d[i] = P.draft[static_cast<size_t>(s0) * P.k + i];
-    if (t < ns) sh_rem[t] = P.remaining ? P.remaining[s0 + t] : -1;   // negative: no budget
-    for (int r = t; r < nrows; r += kCommitThreads) {
-      const uint64_t *rk = kb + static_cast<size_t>(r) * P.chunks;
-      uint64_t best = 0ull;
+    const bool has_d = t < ns * P.k, has_r = t < nrows;
+    const int dv = has_d ? P.draft[static_cast<size_t>(s0) * P.k + t] : 0;
+    const int rv = t < ns && P.remaining ? P.remaining[s0 + t] : -1;   // negative: no budget
+    uint64_t best = 0ull;
+    if (has_r) {
+      const uint64_t *rk = kb + static_cast<size_t>(t) * P.chunks;
       for (int c0 = 0; c0 < P.chunks; c0 += kKeysPerThread) {
         uint64_t kr[kKeysPerThread];
 #pragma unroll
@@ -228,8 +232,10 @@ __global__ __launch_bounds__(kCommitThreads) void greedy_commit_kernel(GreedyPar
 #pragma unroll
         for (int q = 0; q < kKeysPerThread; ++q) best = kr[q] > best ? kr[q] : best;
       }
-      sh_row[r] = best;
     }
+    if (has_d) sh_d[t] = dv;
+    if (t < ns) sh_rem[t] = rv;
+    if (has_r) sh_row[t] = best;
     __syncthreads();
     int cnt = 0;
     if (t < ns) {
