@@ -126,11 +126,6 @@ __device__ inline float wave_max_dpp(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
-}
 __device__ inline int wave_min(int v) {
   return wave_reduce(v, [](int a, int b) { return min(a, b); });
 }
