@@ -8,12 +8,13 @@
 // include/spec_verify.h.
 //
 // Design.  The window is small (<= SPEC_GROUP_MAX_N), so one workgroup does
-// it all in LDS: a bitonic sort of 64-bit keys (length in the high word,
+// it all: a bitonic sort of 64-bit keys (length in the high word,
 // order-corrected for sign; window index in the low word), which makes every
-// key distinct and the sort stable by construction; then run detection and
-// four block-wide scans give each sorted position its run, the run's offsets
-// among same-length members, same-length batches and fallback members, and
-// every position writes its own output slots.  The work is latency-bound
+// key distinct and the sort stable by construction (up to 1024 keys one per
+// lane, strides below a wave by lane shuffles; larger windows in LDS); then
+// run detection and four block-wide scans give each sorted position its run,
+// the run's offsets among same-length members, same-length batches and
+// fallback members, and every position writes its own output slots.  The work is latency-bound
 // (microseconds); there is nothing to stream.
 #include "common.h"
 
@@ -23,6 +24,29 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kPer = SPEC_GROUP_MAX_N / kThreads;   // sorted positions per lane
 
+// Block-wide exclusive sum of one 64-bit value per lane (lane order); `sh`
+// holds kThreads / kWave + 1 words; *total receives the block total.
+// Barriers: call from every lane.
+__device__ inline unsigned long long block_excl_scan_u64(unsigned long long v, unsigned long long *sh,
+                                                         unsigned long long *total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  constexpr int nw = kThreads / kWave;
+  const unsigned long long inc = wave_incl_scan(v);
+  if (lane == kWave - 1) sh[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    const unsigned long long x = lane < nw ? sh[lane] : 0ull;
+    const unsigned long long xi = wave_incl_scan(x);
+    if (lane < nw) sh[lane] = xi - x;
+    if (lane == nw - 1) sh[nw] = xi;
+  }
+  __syncthreads();
+  const unsigned long long r = inc - v + sh[w];
+  *total = sh[nw];
+  __syncthreads();
+  return r;
+}
+
 __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t *lengths, int N, int B, int mg,
                                                           int P2, int32_t *perm, int32_t *batch_start,
                                                           int32_t *batch_len, int32_t *num_batches,
@@ -31,6 +55,7 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t *lengths,
   unsigned long long *keys = smem;                                  // [P2]
   int *run_start = reinterpret_cast<int *>(smem + P2);              // [N + 1]
   __shared__ int sh[kThreads / kWave + 1];
+  __shared__ unsigned long long sh64[kThreads / kWave + 1];
   const int t = threadIdx.x;
 
   if (N == 0) {
@@ -41,27 +66,51 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t *lengths,
     }
     return;
   }
-  for (int i = t; i < P2; i += kThreads) {
-    keys[i] = i < N ? (static_cast<unsigned long long>(static_cast<uint32_t>(lengths[i]) ^ 0x80000000u) << 32) |
-                          static_cast<uint32_t>(i)
-                    : ~0ull;
-  }
-  __syncthreads();
-  for (int size = 2; size <= P2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = t; i < P2 / 2; i += kThreads) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const unsigned long long a = keys[lo], c = keys[hi];
-        if ((a > c) == up) {
-          keys[lo] = c;
-          keys[hi] = a;
+  auto key_of = [&](int i) {
+    return i < N ? (static_cast<unsigned long long>(static_cast<uint32_t>(lengths[i]) ^ 0x80000000u) << 32) |
+                       static_cast<uint32_t>(i)
+                 : ~0ull;
+  };
+  if (P2 <= kThreads) {
+    // one key per lane: strides below a wave by lane shuffles, the others
+    // through LDS (lanes past P2 hold padding and pair among themselves)
+    unsigned long long v = key_of(t);
+    for (int size = 2; size <= P2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        unsigned long long o = v;
+        if (stride >= kWave) {
+          if (t < P2) keys[t] = v;
+          __syncthreads();
+          if (t < P2) o = keys[t ^ stride];
+          __syncthreads();
+        } else {
+          o = __shfl_xor(v, stride, kWave);
         }
+        const bool lower = (t & stride) == 0, up = (t & size) == 0;
+        v = (lower == up) ? (o < v ? o : v) : (o > v ? o : v);
       }
-      __syncthreads();
+    }
+    if (t < P2) keys[t] = v;
+  } else {
+    for (int i = t; i < P2; i += kThreads) keys[i] = key_of(i);
+    __syncthreads();
+    for (int size = 2; size <= P2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = t; i < P2 / 2; i += kThreads) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const unsigned long long a = keys[lo], c = keys[hi];
+          if ((a > c) == up) {
+            keys[lo] = c;
+            keys[hi] = a;
+          }
+        }
+        __syncthreads();
+      }
     }
   }
+  __syncthreads();
 
   // lane t owns sorted positions [t*per, t*per + per) within [0, N)
   const int per = (N + kThreads - 1) / kThreads;
@@ -117,10 +166,23 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t *lengths,
       }
     }
   }
-  int TU, TB, TF;
-  int xu = block_excl_scan(su, sh, &TU);
-  int xb = block_excl_scan(sb, sh, &TB);
-  int xf = block_excl_scan(sf, sh, &TF);
+  // the three counts scanned at once: 21-bit fields of one 64-bit word (every
+  // sum is at most N <= SPEC_GROUP_MAX_N < 2^21, so no field carries over)
+  static_assert(SPEC_GROUP_MAX_N < (1 << 21), "21-bit count fields");
+  int TU, TB, TF, xu, xb, xf;
+  {
+    const unsigned long long packed = (static_cast<unsigned long long>(su) << 42) |
+                                      (static_cast<unsigned long long>(sb) << 21) | static_cast<unsigned long long>(sf);
+    unsigned long long tot;
+    const unsigned long long ex = block_excl_scan_u64(packed, sh64, &tot);
+    constexpr unsigned long long m21 = (1ull << 21) - 1;
+    xu = static_cast<int>(ex >> 42);
+    xb = static_cast<int>((ex >> 21) & m21);
+    xf = static_cast<int>(ex & m21);
+    TU = static_cast<int>(tot >> 42);
+    TB = static_cast<int>((tot >> 21) & m21);
+    TF = static_cast<int>(tot & m21);
+  }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if (p0 + i >= p1) continue;
