@@ -12,6 +12,8 @@
  *   [Atlas]       "Speculative decoding: proposals and verified output" (Atlas
  *                 lesson), The mechanism; Acceptance and rejection correction;
  *                 Interfaces.
+ *   [Design]      speculative-decoding-real "Design Document", Standard Greedy
+ *                 Algorithm; KV Cache Synchronization.
  *
  * Conventions shared by every call
  *   - Every array argument is a DEVICE pointer owned by the caller; the library

@@ -12,9 +12,10 @@
 // order-corrected for sign; window index in the low word), which makes every
 // key distinct and the sort stable by construction (up to 1024 keys one per
 // lane, strides below a wave by lane shuffles; larger windows in LDS); then
-// run detection and four block-wide scans give each sorted position its run,
-// the run's offsets among same-length members, same-length batches and
-// fallback members, and every position writes its own output slots.  The work is latency-bound
+// run detection and two block-wide scans give each sorted position its run
+// and the run's offsets among same-length members, same-length batches and
+// fallback members (three 21-bit counts packed in one 64-bit scan), and every
+// position writes its own output slots.  The work is latency-bound
 // (microseconds); there is nothing to stream.
 #include "common.h"
 

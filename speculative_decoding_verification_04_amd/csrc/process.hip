@@ -9,7 +9,7 @@
 // vectors in registers and working on float values (a shift or mask per bf16
 // entry, three-operand maxima); a statistics workgroup per row then finishes.
 //   * Top-k (K <= 256): proc_slice_kernel cuts each slice at the K-th largest
-//     of its 256 lane maxima (a bitonic sort of the maxima) and lists the
+//     of its 256 lane maxima (found bit by bit with wave ballots) and lists the
 //     entries at or above that cut: the vectors whose maximum reaches the cut
 //     (about K) are staged in LDS and filtered by the whole workgroup.  The
 //     union of the lists holds every logit at or above the row's K-th
@@ -1037,8 +1037,56 @@ __device__ inline float vec_max(const uint4 &q) {
 // every lane filters its own.  A list that does not fit reports its length;
 // the statistics kernel then reads the row whole.  (K <= 256.)
 constexpr int kStageCap = 512;
-static_assert(kSliceThreads == 256 && (kSliceThreads & (kSliceThreads - 1)) == 0, "bitonic sort over the lanes");
-static_assert(kSliceThreads * kSliceLoads <= 65536, "vector ids fit 16 bits");
+static_assert(kSliceThreads == 4 * kWave, "four lane maxima per lane of a wave");
+
+// The r1-th and r2-th largest (1 <= r <= 256, counting repeats) of the 256
+// keys m, four per lane, every lane of the wave active, and the largest key:
+// for each rank, the largest c with at least r keys >= c, decided one bit at
+// a time by counting the keys >= the candidate with wave ballots.  Every key
+// shares the bits above the highest bit in which the smallest and the largest
+// differ, so the search starts below them.  Keys of bf16 logits (kLow = 16)
+// carry nothing below bit 16: keys with equal top halves are equal, their low
+// half all zeros for a non-negative logit (and for the key 0 of a lane with no
+// entry) and all ones for a negative one, so only the top 16 bits are searched
+// and the low half is filled in.  With two == false only r1 is searched.
+template <int kLow>
+__device__ inline void kth_keys(const uint32_t (&m)[4], int r1, int r2, bool two, uint32_t &x1, uint32_t &x2,
+                                uint32_t &kmax) {
+  const uint32_t hi = wave_max_u(max(max(m[0], m[1]), max(m[2], m[3])));
+  const uint32_t lo = wave_min_u(min(min(m[0], m[1]), min(m[2], m[3])));
+  const int top = digit_top(lo, hi, kLow);
+  uint32_t p1 = lo & bits_above(top), p2 = p1;
+  if (two) {
+    for (int b = top; b >= kLow; --b) {
+      const uint32_t c1 = p1 | (1u << b), c2 = p2 | (1u << b);
+      int n1 = 0, n2 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        n1 += __popcll(__ballot(m[i] >= c1));
+        n2 += __popcll(__ballot(m[i] >= c2));
+      }
+      if (n1 >= r1) p1 = c1;
+      if (n2 >= r2) p2 = c2;
+    }
+  } else {
+    for (int b = top; b >= kLow; --b) {
+      const uint32_t c1 = p1 | (1u << b);
+      int n1 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) n1 += __popcll(__ballot(m[i] >= c1));
+      if (n1 >= r1) p1 = c1;
+    }
+    p2 = p1;
+  }
+  if constexpr (kLow == 16) {
+    if (p1 != 0u && p1 < 0x80000000u) p1 |= 0xFFFFu;
+    if (p2 != 0u && p2 < 0x80000000u) p2 |= 0xFFFFu;
+  }
+  x1 = p1;
+  x2 = p2;
+  kmax = hi;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P) {
   using SV = Slice<BF16>;
@@ -1046,7 +1094,6 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P)
   __shared__ uint32_t sh_m[kSliceThreads];
   __shared__ uint4 sh_vec[kStageCap];
   __shared__ uint16_t sh_vid[kStageCap];
-  __shared__ uint32_t sh_theta;
   __shared__ int sh_nv, sh_n;
   const int t = threadIdx.x, lane = t & (kWave - 1);
   const int r = blockIdx.x / P.S, s = blockIdx.x - r * P.S;
@@ -1066,32 +1113,19 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P)
     sh_nv = 0;
     sh_n = 0;
   }
-  // bitonic sort of the 256 lane maxima, descending (strides below a wave by
-  // lane shuffles, the others through LDS); lane K - 1 then holds theta
-  uint32_t v = ml;
-#pragma unroll
-  for (int k = 2; k <= kSliceThreads; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      uint32_t o;
-      if (j >= kWave) {
-        sh_m[t] = v;
-        __syncthreads();
-        o = sh_m[t ^ j];
-        __syncthreads();
-      } else {
-        o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), j, kWave));
-      }
-      const bool desc = (t & k) == 0;        // this run is sorted descending
-      const bool low = (t & j) == 0;         // lower index of the pair
-      v = (desc == low) ? max(v, o) : min(v, o);
-    }
-  }
-  if (t == K - 1) sh_theta = v;
-  if (t == 0 && P.sl_max) P.sl_max[static_cast<size_t>(r) * P.S + s] = v;   // the slice's largest key
-  if (P.list_lb && t == P.lb_rank - 1) P.list_lb[static_cast<size_t>(r) * P.S + s] = v;
+  // every wave reads all 256 lane maxima and finds the ranks it needs itself
+  sh_m[t] = ml;
   __syncthreads();
-  const uint32_t cut = max(sh_theta, 1u);    // a maximum of 0 (no entry) lists every entry
+  uint32_t m4[kSliceThreads / kWave];
+#pragma unroll
+  for (int i = 0; i < kSliceThreads / kWave; ++i) m4[i] = sh_m[lane + i * kWave];
+  uint32_t theta, lb, smax;
+  kth_keys<BF16 ? 16 : 0>(m4, K, P.lb_rank, P.list_lb != nullptr, theta, lb, smax);
+  if (t == 0) {
+    if (P.sl_max) P.sl_max[static_cast<size_t>(r) * P.S + s] = smax;   // the slice's largest key
+    if (P.list_lb) P.list_lb[static_cast<size_t>(r) * P.S + s] = lb;
+  }
+  const uint32_t cut = max(theta, 1u);    // a maximum of 0 (no entry) lists every entry
   // a vector holds a key >= cut iff its float maximum is >= the cut's value
   // (every real key is at least the key of -inf)
   const float cutf = cut <= f32_order_key(-INFINITY) ? -INFINITY : f32_from_order_key(cut);
@@ -1158,7 +1192,7 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P)
   __syncthreads();
   if (t == 0) {
     P.list_cnt[static_cast<size_t>(r) * P.S + s] = sh_n;
-    P.list_cut[static_cast<size_t>(r) * P.S + s] = sh_theta;
+    P.list_cut[static_cast<size_t>(r) * P.S + s] = theta;
   }
 }
 
