@@ -146,7 +146,7 @@ def test_process_topk_concentrated_rows(dtype):
         dev_in, zw = z, z
     zd = logits_to_device(dev_in, dtype)
     for T, K, P in [(1.0, 1, 1.0), (0.7, 7, 1.0), (0.7, 50, 0.9), (1.0, 200, 1.0), (0.9, 256, 0.95),
-                    (1.0, 64, 0.5)]:
+                    (0.9, 257, 0.95), (1.0, 64, 0.5)]:           # 256: largest slice-path K; 257: whole rows
         note(f"process concentrated {dtype} T={T} K={K} P={P}")
         _check_rows(zw, host(process(zd, T, K, P)), T, K, P)
 
@@ -322,3 +322,21 @@ def test_process_largest_vocabulary(dtype):
     for T, K, P in [(0.7, 50, 0.9), (1.0, 128, 1.0), (0.7, 0, 0.9), (1.0, 0, 1.0), (0.7, 300, 0.95)]:
         note(f"process largest V {dtype} T={T} K={K} P={P}")
         _check_rows(zw, host(process(zd, T, K, P)), T, K, P)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_verify_from_logits_largest_k(dtype):
+    """k = SPEC_MAX_K (127) through the processed path: draft logits close to
+    the target's keep most drafts accepted, so the chains run long."""
+    k = sv.SPEC_MAX_K
+    rng = np.random.default_rng(1270)
+    B, V = 3, 300
+    zt = (rng.standard_normal((B, k + 1, V)) * 2).astype(np.float32)
+    zd_ = zt[:, :k].copy()
+    zd_[1] += (rng.standard_normal((k, V)) * 0.05).astype(np.float32)
+    zd_[2] += (rng.standard_normal((k, V)) * 0.5).astype(np.float32)
+    note(f"verify logits k={k} {dtype}")
+    exact, got, ref = _verify_case(zt, zd_, 0.8, 10, 0.9, 7, dtype)
+    assert ref["accept_len"][0] == k                  # identical p' and q': every draft accepted
+    assert exact >= B - 1
+    assert got["emit_offsets"][-1] == got["emit_count"].sum()

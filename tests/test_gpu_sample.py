@@ -238,3 +238,31 @@ def test_repeatable_bitwise():
         again = host(verify_sample(P, Q, r["drafts"], r["uniforms"], ws_key="srep"))
         for key in first:
             assert np.array_equal(first[key], again[key]), key
+
+
+def test_largest_k():
+    """k = SPEC_MAX_K (127): a sequence that accepts every draft and draws the
+    bonus token, one rejected late (at draft 100), a random one, and one that
+    stops on its budget of 120 tokens with every draft accepted."""
+    import speculative_decoding_verification_04_amd as sv
+    k = sv.SPEC_MAX_K
+    note(f"sample k={k}")
+    rng = np.random.default_rng(127)
+    B, V = 4, 97
+    p, q, d, u = _small_case(rng, B, k, V)
+    p[0, :k] = q[0]                                  # a = 1 at every draft
+    p[1, :k] = q[1]
+    x = int(d[1, 100])
+    p[1, 100] = rng.dirichlet(np.ones(V)).astype(np.float32)
+    p[1, 100, x] = 0.2 * q[1, 100, x]                # a = 0.2 < u: rejected at draft 100
+    u[1, 100] = 0.9
+    p[3, :k] = q[3]
+    remaining = np.array([-1, -1, -1, 120], np.int32)
+    got = _run(p, q, d, u, remaining=remaining)
+    ref = oracle.sample_verify(p, q, d, u, remaining=remaining)
+    assert ref["accept_len"][0] == k and ref["emit_count"][0] == k + 1
+    assert ref["accept_len"][1] == 100 and ref["emit_count"][1] == 101
+    assert ref["emit_count"][3] == 120
+    exact, tol = check_within_tolerance(p, q, d, u, got, ref)
+    assert exact + tol == B
+    assert np.array_equal(got["emit_offsets"], ref["emit_offsets"])
