@@ -146,7 +146,7 @@ def main() -> int:
         record_traffic(*args.record_traffic)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the step shards "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the step shards "
               "by sequence with no exchange); run it with --gpus 1.", file=sys.stderr)
         return 2
 
