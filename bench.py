@@ -285,6 +285,7 @@ def main() -> int:
         "verify_us_per_call": statistics.mean(t_ver) * 1e6,
         "realign_GBps": rea_GBps / 1e9,
         "realign_ms_per_call": statistics.mean(t_rea) * 1e3,
+        "per_call_spread": {"verify_us": _spread(t_ver, 1e6), "realign_ms": _spread(t_rea, 1e3)},
         "copy_probe_GBps": None if probe is None else probe / 1e9,
         "parity_checked": parity,
         "secondary": secondary,
@@ -292,6 +293,16 @@ def main() -> int:
     }
     print(json.dumps(result))
     return 0
+
+
+def _spread(ts, scale: float) -> dict:
+    """p10, median and p90 of per-call times (HIP events), scaled."""
+    q = sorted(ts)
+
+    def pct(f: float) -> float:                  # nearest rank
+        return q[min(len(q) - 1, max(0, int(round(f * (len(q) - 1)))))] * scale
+
+    return {"p10": pct(0.1), "median": statistics.median(q) * scale, "p90": pct(0.9)}
 
 
 def _time_calls(torch, fn, reps: int, inner: int = 24):
