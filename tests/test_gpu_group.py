@@ -43,6 +43,18 @@ def test_random_windows(N, B, mg):
         _compare(lengths, B, mg)
 
 
+@pytest.mark.parametrize("N", [63, 64, 65, 511, 512, 513, 1023, 1024, 1025, 2047, 2049])
+def test_sort_path_boundaries(N):
+    """Windows on either side of the sort's limits: one key per lane up to
+    1024 keys (lane shuffles below a wave), LDS above; lengths with many ties,
+    and lengths spread over the whole int32 range."""
+    note(f"group boundary N={N}")
+    rng = np.random.default_rng(9000 + N)
+    for B, mg in [(1, 1), (8, 2), (64, 8)]:
+        _compare(rng.integers(0, 5, size=N).tolist(), B, mg)
+        _compare(rng.integers(-2 ** 31, 2 ** 31 - 1, size=N, dtype=np.int64).tolist(), B, mg)
+
+
 def test_all_equal_and_extremes():
     note("group extremes")
     _compare([5] * 4096, 8, 2)
