@@ -1,5 +1,6 @@
 """Host-side logic of bench.py (no GPU): the one-GPU guard, the choice of the
-step loop's dispatches in counter runs, and the counter scaling."""
+step loop's dispatches in counter runs, the counter scaling, and the per-call
+percentiles."""
 import csv
 import json
 import os
@@ -61,3 +62,15 @@ def test_traffic_scaled_by_the_copy_probe(tmp_path, monkeypatch):
     t["sources_sha256"] = "stale"
     out.write_text(json.dumps(t))
     assert bench.traffic_bytes("realign_kernel") is None      # counters of other sources are not used
+
+
+def test_per_call_spread_nearest_rank():
+    ts = [0.005, 0.001, 0.004, 0.002, 0.003]             # seconds, unsorted
+    sp = bench._spread(ts, 1e3)                          # in ms
+    assert sp == {"p10": pytest.approx(1.0), "median": pytest.approx(3.0), "p90": pytest.approx(5.0)}
+    many = [i * 1e-6 for i in range(1, 21)]              # 1 .. 20 us
+    sp = bench._spread(many, 1e6)
+    assert sp["p10"] == pytest.approx(3.0) and sp["p90"] == pytest.approx(18.0)
+    assert sp["median"] == pytest.approx(10.5)
+    assert bench._spread([2e-3], 1e3) == {"p10": pytest.approx(2.0), "median": pytest.approx(2.0),
+                                          "p90": pytest.approx(2.0)}
