@@ -26,11 +26,19 @@
  *     sequence status bits (SPEC_ST_*).
  *   - Output arrays must not overlap input arrays or each other.
  *   - Workspaces ("ws") are device memory of at least the queried size, 256-byte
- *     aligned, holding per-call partial results.  Their contents on entry are
- *     ignored (no initialisation is needed).  Calls that may run at the same
- *     time (different streams) need different workspaces.
- *   - A verify call launches two kernels on `stream` (a streaming pass and a
- *     small commit pass); the stream order is their only synchronisation.
+ *     aligned, holding per-call partial results.  Calls that may run at the
+ *     same time (different streams) need different workspaces.
+ *   - The greedy verification workspace also carries the completion flags of
+ *     its single launch: it must be zero-filled before its first use (e.g.
+ *     hipMemset, torch.zeros) and no other call may write into it; every
+ *     completed greedy or tree verification call leaves it zero-filled again.
+ *     (A tree verification call accepts any contents.)  Every other
+ *     workspace's contents on entry are ignored.
+ *   - A greedy verify call is one launch: streaming workgroups publish per-
+ *     chunk results and one workgroup of the same launch commits them.  Calls
+ *     whose rows need more chunk results than that workgroup holds at once
+ *     (more than 1024 per sequence), and tree verification, launch a streaming
+ *     pass and a commit pass, synchronised by the stream order.
  *   - Token ids are int32 in [0, V).  Layouts are row-major, last index fastest.
  */
 #ifndef SPEC_VERIFY_H
@@ -61,6 +69,9 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 #define SPEC_ST_NONFINITE 8   /* a gathered probability or a drawn row's mass is not finite */
 #define SPEC_ST_BAD_STATE 16  /* commit: n_b outside [0, E] or e_b outside [0, k+1] */
 #define SPEC_ST_CAPACITY 32   /* commit: E < 0 or E + k + 1 > C */
+#define SPEC_ST_INCOMPLETE 64 /* greedy verify: a chunk result did not arrive within the
+                                 call's wait bound (seconds); this sequence's outputs are
+                                 unspecified (not expected in normal operation) */
 
 #define SPEC_MAX_K 127          /* largest number of proposals k per sequence */
 #define SPEC_GROUP_MAX_N 4096   /* largest window for spec_group_same_length */
@@ -92,7 +103,11 @@ const char *spec_strerror(int code);
  *   emit_offsets[B+1] out or NULL: exclusive prefix sum of emit_count
  *   status      [B]   out or NULL: SPEC_ST_DRAFT_OOR if any draft[b, j] is
  *                     outside [0, V)
- *   ws          workspace of spec_verify_greedy_workspace_bytes(B, k, V, dt)
+ *   ws          workspace of spec_verify_greedy_workspace_bytes(B, k, V, dt),
+ *               zero-filled before its first use (see the conventions above)
+ *   status      also SPEC_ST_INCOMPLETE if the commit stopped waiting for a
+ *               chunk result (a bound of seconds that normal operation never
+ *               reaches)
  * Errors: SPEC_EINVAL for NULL required pointers, B < 1, k < 1, V < 1,
  * V >= 2^31 - 1 or a misaligned logits pointer; SPEC_ECAPACITY for
  * k > SPEC_MAX_K; SPEC_EWORKSPACE.

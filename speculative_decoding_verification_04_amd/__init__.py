@@ -15,7 +15,7 @@ from . import _lib
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_OK, SPEC_EINVAL, SPEC_EWORKSPACE, SPEC_ECAPACITY, SPEC_EHIP = 0, -1, -2, -3, -4
 SPEC_ST_DRAFT_OOR, SPEC_ST_Q_ZERO, SPEC_ST_RESID_ZERO = 1, 2, 4
-SPEC_ST_NONFINITE, SPEC_ST_BAD_STATE, SPEC_ST_CAPACITY = 8, 16, 32
+SPEC_ST_NONFINITE, SPEC_ST_BAD_STATE, SPEC_ST_CAPACITY, SPEC_ST_INCOMPLETE = 8, 16, 32, 64
 SPEC_MAX_K, SPEC_GROUP_MAX_N, SPEC_PROC_MAX_V, SPEC_TREE_MAX_N = 127, 4096, 524288, 256
 
 __all__ = [
@@ -96,9 +96,11 @@ def _dtype_code(t) -> int:
 
 
 def workspace(nbytes: int, device=None):
-    """A device workspace of at least nbytes (its contents need no initialisation)."""
+    """A zero-filled device workspace of at least nbytes.  Greedy verification
+    needs a zero-filled workspace that no other call writes into (it keeps it
+    zero-filled between calls); the other calls ignore the contents."""
     import torch
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
 
 
 def spec_verify_greedy_workspace_bytes(B: int, k: int, V: int, dtype_code: int) -> int:

@@ -7,31 +7,41 @@
 // bonus row) is the walkthrough's 3.3 table.
 //
 // Design.  The logits are the only large input (B*(k+1)*V elements), so the
-// step is one streaming pass over them, bound by HBM bandwidth, followed by a
-// tiny commit pass.
-//   * greedy_chunk_kernel: each row is cut into chunks of kThreads*VEC*U
-//     elements; one workgroup per (row, chunk) loads its chunk with 16-byte
-//     non-temporal loads (U in flight per lane).  The chunk maximum comes from
-//     plain max instructions, DPP lane moves inside each wave and LDS across
-//     waves; then only the lanes holding it search their own elements for its
-//     first index (an LDS minimum picks the lowest), and one 64-bit key is
-//     stored (value order high, UINT32_MAX - index low; the largest key is
-//     the argmax at the lowest index).  Searching in every lane, or reducing
-//     64-bit keys through LDS permutes, measured about 0.5 us slower.  No workgroup waits for another: cross-workgroup completion
-//     tickets cost far more than this whole pass on a multi-XCD part (device-
-//     scope atomics on one address serialise, and waiting on them holds the
-//     CU's wave slots), so the kernel boundary is the synchronisation.
-//   * greedy_commit_kernel: one workgroup; one lane per row folds that row's
-//     chunk keys in registers, then one lane per sequence walks its drafts and
-//     writes its outputs, and the emit counts are scanned into offsets, a tile
-//     of sequences at a time.
+// step is one streaming pass over them, bound by HBM bandwidth, plus a tiny
+// commit.  One launch does both:
+//   * producer workgroups (one per (row, chunk of kThreads*VEC*U elements))
+//     load their chunk with 16-byte non-temporal loads (U in flight per lane).
+//     The chunk maximum comes from plain max instructions, DPP lane moves
+//     inside each wave and LDS across waves; only the lanes holding it search
+//     their own elements for its first index (an LDS minimum picks the
+//     lowest).  The chunk's 64-bit key (value order high, UINT32_MAX - index
+//     low; the largest key is the argmax at the lowest index) is published
+//     with one agent-scope store into its workspace slot.  A published key is
+//     never 0 (an empty chunk publishes 1), so a slot is its own flag.
+//   * workgroup 0, the finisher, walks the batch in tiles of sequences: it
+//     polls a tile's slots with agent-scope loads (one round of loads per
+//     poll, only missing slots re-read) and, while the next tile's slots and
+//     drafts are already being loaded, commits the tile in LDS with one lane
+//     per row: fold the row's chunk keys, test its stop conditions (mismatch,
+//     EOS) with an LDS minimum per sequence, then one lane per sequence applies
+//     the budget, counts the accepted drafts and scans the emit counts, and
+//     the rows write their tokens.  Finally it returns every slot it read to
+//     0 (the workspace stays zero-filled between calls).
+// Producers never wait: the finisher is one workgroup whose wait ends when
+// every producer has published, and producers depend on nothing.  Device-
+// scope atomics on shared counters are avoided altogether (on a multi-XCD
+// part they serialise per address).  Sequences whose rows need more chunk
+// keys than one finisher tile holds fall back to two launches: the streaming
+// kernel, then a one-workgroup commit (tree verification uses the same
+// streaming kernel with its own commit).
 #include "common.h"
 
 namespace specv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
+constexpr uint64_t kEmptyKey = 1ull;   // published by a chunk with no elements (below every real key)
 
 template <bool BF16>
 struct GreedyTraits;
@@ -51,7 +61,8 @@ struct GreedyParams {
   int32_t eos;
   const int32_t *remaining;
   int32_t *accept_len, *emit_count, *out_tokens, *emit_offsets, *status;
-  uint64_t *keys;     // [B*(k+1)*chunks]
+  uint64_t *keys;     // [B*(k+1)*chunks]; zero between calls (the slot flags)
+  int nprod;          // producer workgroups of the single-launch path
   // tree verification only (k + 1 = N nodes per sequence)
   const int32_t *first_child, *next_sibling;
   int32_t *path;
@@ -130,16 +141,19 @@ __device__ inline int vec_find(uint4 x, float m) {
   return q;
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void greedy_chunk_kernel(GreedyParams P) {
+// One producer: the key of chunk c of row `row`.  PUBLISH stores it with an
+// agent-scope store (visible to the finisher of the same launch); otherwise
+// with a plain store (read by a later kernel).
+template <bool BF16, bool PUBLISH>
+__device__ inline void stream_chunk(const GreedyParams &P, int blk) {
   using Tr = GreedyTraits<BF16>;
   constexpr int ELT = Tr::ELT, VEC = Tr::VEC, U = Tr::U;
   __shared__ float sh_max[kWaves];
   __shared__ int sh_first;
 
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-  const int row = blockIdx.x / P.chunks;
-  const int c = blockIdx.x - row * P.chunks;
+  const int row = blk / P.chunks;
+  const int c = blk - row * P.chunks;
   const unsigned char *rowp = P.logits + static_cast<size_t>(row) * P.V * ELT;
   // Elements before the row's first 16-byte boundary are handled one per lane
   // by chunk 0; the body starts aligned.
@@ -191,17 +205,211 @@ __global__ __launch_bounds__(kThreads) void greedy_chunk_kernel(GreedyParams P) 
     if (cand != INT_MAX) atomicMin(&sh_first, cand);
   }
   __syncthreads();
-  if (t == 0)
-    P.keys[static_cast<size_t>(row) * P.chunks + c] = sh_first == INT_MAX ? 0ull : argmax_key(bmax, sh_first);
+  if (t == 0) {
+    const uint64_t key = sh_first == INT_MAX ? kEmptyKey : argmax_key(bmax, sh_first);
+    uint64_t *slot = P.keys + static_cast<size_t>(row) * P.chunks + c;
+    if constexpr (PUBLISH) __hip_atomic_store(slot, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *slot = key;
+  }
 }
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void greedy_chunk_kernel(GreedyParams P) {
+  stream_chunk<BF16, false>(P, blockIdx.x);
+}
+
+// ---------------------------------------------------------------- commit ----
+// The finisher commits a tile of sequences in LDS: kTileKeys chunk keys per
+// tile (at most kTileSeq sequences), rows = ns * (k + 1) <= kTileKeys / chunks.
+// Its last wave only stores results; the other waves only load.  A wave's
+// memory counter covers its loads and its stores alike, so a wave that waits
+// for its loads never waits for stores as well.
+constexpr int kTileKeys = 1024;
+constexpr int kTileSeq = 256;
+constexpr int kLoadLanes = kThreads - kWave;                              // waves 0 .. kWaves-2
+constexpr int kKPL = (kTileKeys + kLoadLanes - 1) / kLoadLanes;           // slots per loading lane
+static_assert(kTileSeq <= kLoadLanes, "one loading lane per sequence of a tile");
+
+struct TileShared {
+  uint64_t key[kTileKeys];   // the tile's chunk keys, row-major
+  int tok[kTileKeys];        // argmax of each row
+  int d[kTileKeys];          // the tile's drafts (ns * k <= kTileKeys)
+  int stop[kTileSeq];        // first row that stops the sequence (LDS minimum)
+  int rem[kTileSeq];         // budgets
+  int st[kTileSeq];          // status bits
+  int e[kTileSeq];           // emit counts
+  int acc[kTileSeq];         // accepted drafts
+  int off[kTileSeq];         // emit offsets
+  int scan[kThreads / kWave + 1];
+};
+
+__host__ __device__ inline int tile_sequences(int k, int chunks) {
+  const int rows = kTileKeys / chunks;
+  return min(kTileSeq, rows / (k + 1));
+}
+
+// Commits the ns sequences starting at s0 whose chunk keys, drafts and budgets
+// are in LDS (stop[] holds k and st[] the status on entry).  Every lane of the
+// workgroup calls it; only the last wave writes global memory.  Returns the
+// carry of the emit offsets.
+__device__ inline int commit_tile(const GreedyParams &P, TileShared &S, int s0, int ns, int carry) {
+  const int t = threadIdx.x, kp1 = P.k + 1, nrows = ns * kp1;
+  // one lane per row: fold its chunk keys, then test the row's stop
+  // conditions (draft j < k: a mismatch or EOS stops after emitting row j)
+  for (int r = t; r < nrows; r += kThreads) {
+    const uint64_t *kr = S.key + r * P.chunks;
+    uint64_t best = 0ull;
+    int c = 0;
+    for (; c + 8 <= P.chunks; c += 8) {
+      uint64_t x[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = kr[c + q];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) best = x[q] > best ? x[q] : best;
+    }
+    for (; c < P.chunks; ++c) best = kr[c] > best ? kr[c] : best;
+    const int tok = argmax_key_index(best);
+    S.tok[r] = tok;
+    const int b = r / kp1, j = r - b * kp1;
+    if (j < P.k) {
+      const int d = S.d[b * P.k + j];
+      if (d < 0 || d >= P.V) atomicOr(&S.st[b], SPEC_ST_DRAFT_OOR);
+      if (tok != d || (P.eos >= 0 && tok == P.eos)) atomicMin(&S.stop[b], j);
+    }
+  }
+  __syncthreads();
+  // one lane per sequence: emitted count (first stop row + 1, capped by the
+  // budget) and accepted drafts (every emitted row before the last matched;
+  // the last emitted row counts if it matched its draft)
+  int cnt = 0;
+  if (t < ns) {
+    const int rem = S.rem[t];
+    cnt = S.stop[t] + 1;
+    if (rem >= 0) cnt = min(cnt, rem);
+    int acc = 0;
+    if (cnt > 0) {
+      const int last = cnt - 1;
+      acc = last + ((last < P.k && S.tok[t * kp1 + last] == S.d[t * P.k + last]) ? 1 : 0);
+    }
+    S.e[t] = cnt;
+    S.acc[t] = acc;
+  }
+  int total;
+  const int ex = block_excl_scan(t < ns ? cnt : 0, S.scan, &total);   // ends with a barrier
+  if (t < ns) S.off[t] = carry + ex;
+  __syncthreads();
+  // the store wave writes the tile's results
+  if (t >= kLoadLanes) {
+    const int l = t - kLoadLanes;
+    int32_t *out = P.out_tokens + static_cast<size_t>(s0) * kp1;
+    for (int r = l; r < nrows; r += kWave) {
+      const int b = r / kp1, j = r - b * kp1;
+      out[r] = j < S.e[b] ? S.tok[r] : -1;
+    }
+    for (int i = l; i < ns; i += kWave) {
+      P.accept_len[s0 + i] = S.acc[i];
+      P.emit_count[s0 + i] = S.e[i];
+      if (P.status) P.status[s0 + i] = S.st[i];
+      if (P.emit_offsets) P.emit_offsets[s0 + i] = S.off[i];
+    }
+  }
+  return carry + total;
+}
+
+// Loads of one tile, issued together by the loading lanes: the tile's slots
+// (agent scope; absent slots read 0), its drafts and budgets.
+struct TileLoads {
+  uint64_t v[kKPL];
+  int d[kKPL];
+  int rem;
+};
+
+__device__ inline void issue_tile(const GreedyParams &P, int s0, int ns, TileLoads &L) {
+  const int t = threadIdx.x, kp1 = P.k + 1, nk = ns * kp1 * P.chunks, nd = ns * P.k;
+  const uint64_t *slot0 = P.keys + static_cast<size_t>(s0) * kp1 * P.chunks;
+#pragma unroll
+  for (int i = 0; i < kKPL; ++i) {
+    const int f = t + i * kLoadLanes;
+    L.v[i] = f < nk ? load_agent(slot0 + f) : kEmptyKey;
+    L.d[i] = f < nd ? P.draft[static_cast<size_t>(s0) * P.k + f] : 0;
+  }
+  L.rem = (t < ns && P.remaining) ? P.remaining[s0 + t] : -1;
+}
+
+constexpr int kMaxPolls = 1 << 22;   // about 4 s of polling: a bound every wait reaches
+
+// Workgroup 0 of the single-launch verify.
+__device__ void finish_verify(const GreedyParams &P) {
+  __shared__ TileShared S;
+  const int t = threadIdx.x, kp1 = P.k + 1;
+  const bool loader = t < kLoadLanes;
+  const int per = tile_sequences(P.k, P.chunks);
+  int carry = 0, polls = 0;
+  bool timed_out = false;
+  TileLoads L;
+#pragma unroll
+  for (int i = 0; i < kKPL; ++i) L.v[i] = kEmptyKey;
+  if (loader) issue_tile(P, 0, min(per, P.B), L);
+  for (int s0 = 0; s0 < P.B; s0 += per) {
+    const int ns = min(per, P.B - s0), nk = ns * kp1 * P.chunks;
+    const uint64_t *slot0 = P.keys + static_cast<size_t>(s0) * kp1 * P.chunks;
+    // wait until every slot of the tile is published (re-reading only the
+    // missing ones); the bound keeps the wait finite
+    while (true) {
+      bool present = true;
+#pragma unroll
+      for (int i = 0; i < kKPL; ++i) present = present && L.v[i] != 0ull;
+      if (__syncthreads_and(present)) break;
+      if (++polls >= kMaxPolls) { timed_out = true; break; }
+      __builtin_amdgcn_s_sleep(1);
+      if (loader) {
+#pragma unroll
+        for (int i = 0; i < kKPL; ++i) {
+          const int f = t + i * kLoadLanes;
+          if (L.v[i] == 0ull) L.v[i] = load_agent(slot0 + f);
+        }
+      }
+    }
+    if (loader) {
+#pragma unroll
+      for (int i = 0; i < kKPL; ++i) {
+        const int f = t + i * kLoadLanes;
+        if (f < nk) S.key[f] = L.v[i];
+        if (f < ns * P.k) S.d[f] = L.d[i];
+      }
+      if (t < ns) {
+        S.rem[t] = L.rem;
+        S.stop[t] = P.k;
+        S.st[t] = timed_out ? SPEC_ST_INCOMPLETE : 0;
+      }
+    }
+    __syncthreads();
+    // the next tile's loads are in flight while this one is committed
+    if (loader && s0 + per < P.B) issue_tile(P, s0 + per, min(per, P.B - s0 - per), L);
+    carry = commit_tile(P, S, s0, ns, carry);
+  }
+  if (P.emit_offsets && t == kLoadLanes) P.emit_offsets[P.B] = carry;
+  // every slot back to 0 for the next call (ordered before it by the launch)
+  for (int f = t; f < P.nprod; f += kThreads) P.keys[f] = 0ull;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void greedy_verify_kernel(GreedyParams P) {
+  if (blockIdx.x == 0) finish_verify(P);
+  else stream_chunk<BF16, true>(P, static_cast<int>(blockIdx.x) - 1);
+}
+
+
 
 constexpr int kCommitThreads = 1024;
 constexpr int kCommitRows = 1024;   // row keys folded per tile (LDS)
 constexpr int kKeysPerThread = 16;  // chunk keys in flight per lane
 static_assert(kCommitRows == kCommitThreads, "one row (and at most one draft) per lane of a tile");
 
-// One workgroup.  Per tile of sequences, every global read (chunk keys, drafts,
-// budgets) is issued at once into LDS; the walk then runs from LDS only.
+// Two-launch path (rows with more chunk keys than a finisher tile holds): one
+// workgroup.  Per tile of sequences, every global read (chunk keys, drafts,
+// budgets) is issued at once into LDS; the walk then runs from LDS only.  The
+// slots read are returned to 0.
 __global__ __launch_bounds__(kCommitThreads) void greedy_commit_kernel(GreedyParams P) {
   __shared__ unsigned long long sh_row[kCommitRows];
   __shared__ int sh_d[kCommitRows];
@@ -218,13 +426,13 @@ __global__ __launch_bounds__(kCommitThreads) void greedy_commit_kernel(GreedyPar
     // any is used (into registers; LDS is written once all have landed); lane
     // r folds row r's keys (no LDS atomics).  A tile holds at most one draft
     // and one row per lane: ns * k < ns * (k + 1) <= kCommitRows.
-    const uint64_t *kb = P.keys + static_cast<size_t>(s0) * kp1 * P.chunks;
+    uint64_t *kb = P.keys + static_cast<size_t>(s0) * kp1 * P.chunks;
     const bool has_d = t < ns * P.k, has_r = t < nrows;
     const int dv = has_d ? P.draft[static_cast<size_t>(s0) * P.k + t] : 0;
     const int rv = t < ns && P.remaining ? P.remaining[s0 + t] : -1;   // negative: no budget
     uint64_t best = 0ull;
     if (has_r) {
-      const uint64_t *rk = kb + static_cast<size_t>(t) * P.chunks;
+      uint64_t *rk = kb + static_cast<size_t>(t) * P.chunks;
       for (int c0 = 0; c0 < P.chunks; c0 += kKeysPerThread) {
         uint64_t kr[kKeysPerThread];
 #pragma unroll
@@ -232,6 +440,7 @@ __global__ __launch_bounds__(kCommitThreads) void greedy_commit_kernel(GreedyPar
 #pragma unroll
         for (int q = 0; q < kKeysPerThread; ++q) best = kr[q] > best ? kr[q] : best;
       }
+      for (int c = 0; c < P.chunks; ++c) rk[c] = 0ull;   // the workspace returns to zero
     }
     if (has_d) sh_d[t] = dv;
     if (t < ns) sh_rem[t] = rv;
@@ -315,7 +524,7 @@ __global__ __launch_bounds__(kCommitThreads) void tree_commit_kernel(GreedyParam
       d = P.draft[r0 + t];
       fc = P.first_child[r0 + t];
       ns = P.next_sibling[r0 + t];
-      const uint64_t *rk = P.keys + (r0 + t) * P.chunks;
+      uint64_t *rk = P.keys + (r0 + t) * P.chunks;
       for (int c0 = 0; c0 < P.chunks; c0 += kKeysPerThread) {
         uint64_t kr[kKeysPerThread];
 #pragma unroll
@@ -323,6 +532,7 @@ __global__ __launch_bounds__(kCommitThreads) void tree_commit_kernel(GreedyParam
 #pragma unroll
         for (int q = 0; q < kKeysPerThread; ++q) best = kr[q] > best ? kr[q] : best;
       }
+      for (int c = 0; c < P.chunks; ++c) rk[c] = 0ull;   // the workspace returns to zero
     }
     if (t < nseq) {
       sh_st[t] = 0;
@@ -452,10 +662,18 @@ extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int 
   P.emit_offsets = emit_offsets;
   P.status = status;
   P.keys = static_cast<uint64_t *>(ws);
+  P.nprod = static_cast<int>(nblocks);
   P.first_child = P.next_sibling = nullptr;
   P.path = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  if (tile_sequences(k, chunks) >= 1 && nblocks + 1 < INT32_MAX) {
+    // one launch: workgroup 0 commits, the others stream
+    const dim3 grid(static_cast<unsigned>(nblocks + 1));
+    if (dt == SPEC_BF16) hipLaunchKernelGGL(greedy_verify_kernel<true>, grid, dim3(kThreads), 0, s, P);
+    else hipLaunchKernelGGL(greedy_verify_kernel<false>, grid, dim3(kThreads), 0, s, P);
+    return launch_status();
+  }
   if (dt == SPEC_BF16)
     hipLaunchKernelGGL(greedy_chunk_kernel<true>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
   else
@@ -515,6 +733,7 @@ extern "C" int spec_verify_tree(const void *logits, spec_dtype dt, int B, int N,
   P.emit_offsets = emit_offsets;
   P.status = status;
   P.keys = static_cast<uint64_t *>(ws);
+  P.nprod = static_cast<int>(nblocks);
   P.first_child = first_child;
   P.next_sibling = next_sibling;
   P.path = path;

@@ -21,7 +21,8 @@ def note(msg: str) -> None:
 
 
 def ws(nbytes: int, key=None):
-    """A cached zero-filled workspace of at least nbytes."""
+    """A cached zero-filled workspace of at least nbytes (greedy and tree
+    verification use their own keys: their workspace must stay zero-filled)."""
     key = key or "default"
     w = _WS.get(key)
     if w is None or w.numel() < nbytes:
@@ -49,7 +50,7 @@ def verify_greedy(logits_dev, drafts, eos_id=-1, remaining=None, ws_key=None):
                out_tokens=torch.empty(B, kp1, dtype=torch.int32, device=DEV),
                emit_offsets=torch.empty(B + 1, dtype=torch.int32, device=DEV),
                status=torch.empty(B, dtype=torch.int32, device=DEV))
-    w = ws(sv.spec_verify_greedy_workspace_bytes(B, k, V, dt), ws_key)
+    w = ws(sv.spec_verify_greedy_workspace_bytes(B, k, V, dt), ("greedy", ws_key))
     d = drafts if torch.is_tensor(drafts) else i32(drafts)
     rem = None if remaining is None else i32(remaining)
     sv.spec_verify_greedy(logits_dev, d, out["accept_len"], out["emit_count"], out["out_tokens"], w,
@@ -199,7 +200,7 @@ def verify_tree(logits_dev, draft, first_child, next_sibling, eos_id=-1, remaini
                path=torch.empty(B, N, dtype=torch.int32, device=DEV),
                emit_offsets=torch.empty(B + 1, dtype=torch.int32, device=DEV),
                status=torch.empty(B, dtype=torch.int32, device=DEV))
-    w = ws(sv.spec_verify_tree_workspace_bytes(B, N, V, dt), ws_key)
+    w = ws(sv.spec_verify_tree_workspace_bytes(B, N, V, dt), ("greedy", ws_key))
     dev = [a if torch.is_tensor(a) else i32(a) for a in (draft, first_child, next_sibling)]
     rem = None if remaining is None else i32(remaining)
     sv.spec_verify_tree(logits_dev, dev[0], dev[1], dev[2], out["accept_len"], out["emit_count"],

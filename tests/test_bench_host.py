@@ -47,10 +47,10 @@ def test_traffic_scaled_by_the_copy_probe(tmp_path, monkeypatch):
     probe_kib = bench.PROBE_BYTES / 1024
     fetch = _counter_dir(tmp_path, "f", "FETCH_SIZE",
                          [("neg_kernel", 1, 0.5 * probe_kib)] + [("realign_kernel<16>", 7, 1000.0)] * 3
-                         + [("greedy_chunk_kernel<true>", 9, 40.0)] * 2)
+                         + [("greedy_verify_kernel<true>", 9, 40.0)] * 2)
     write = _counter_dir(tmp_path, "w", "WRITE_SIZE",
                          [("neg_kernel", 1, probe_kib)] + [("realign_kernel<16>", 7, 3000.0)] * 3
-                         + [("greedy_chunk_kernel<true>", 9, 1.0)] * 2)
+                         + [("greedy_verify_kernel<true>", 9, 1.0)] * 2)
     out = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_JSON", str(out))
     bench.record_traffic(fetch, write)
@@ -58,7 +58,7 @@ def test_traffic_scaled_by_the_copy_probe(tmp_path, monkeypatch):
     assert t["probe"]["fetch_factor"] == pytest.approx(0.5) and t["probe"]["write_factor"] == pytest.approx(1.0)
     # bytes = 1024 * (FETCH / 0.5 + WRITE / 1.0)
     assert bench.traffic_bytes("realign_kernel") == pytest.approx(1024 * (2000.0 + 3000.0))
-    assert bench.traffic_bytes("greedy_chunk_kernel") == pytest.approx(1024 * (80.0 + 1.0))
+    assert bench.traffic_bytes("greedy_verify_kernel") == pytest.approx(1024 * (80.0 + 1.0))
     t["sources_sha256"] = "stale"
     out.write_text(json.dumps(t))
     assert bench.traffic_bytes("realign_kernel") is None      # counters of other sources are not used

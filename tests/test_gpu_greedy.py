@@ -140,17 +140,69 @@ def test_large_batch_offsets():
     _compare(z, "f32", drafts)
 
 
-def test_repeatable_and_workspace_contents_ignored():
-    note("greedy repeat x50, garbage workspace")
+def test_repeatable_and_workspace_left_zero():
+    """50 calls on one workspace give identical outputs, and every call leaves
+    the workspace zero-filled (the completion flags of the next call)."""
+    note("greedy repeat x50, workspace zero after each call")
     g = W.greedy_round(1, round_=4)
     dev = logits_to_device(g["logits"], "bf16")
     first = host(verify_greedy(dev, g["drafts"], ws_key="rep"))
     B, kp1, V = g["logits"].shape
     import speculative_decoding_verification_04_amd as sv
-    w = ws(sv.spec_verify_greedy_workspace_bytes(B, kp1 - 1, V, sv.SPEC_BF16), "rep")
+    w = ws(sv.spec_verify_greedy_workspace_bytes(B, kp1 - 1, V, sv.SPEC_BF16), ("greedy", "rep"))
+    assert int(torch.count_nonzero(w).item()) == 0
     for it in range(49):
-        if it % 7 == 0:
-            w.fill_(0xA5 if it % 2 else 0xFF)     # whatever the workspace holds on entry
         again = host(verify_greedy(dev, g["drafts"], ws_key="rep"))
         for k in KEYS:
             assert np.array_equal(again[k], first[k])
+        assert int(torch.count_nonzero(w).item()) == 0
+
+
+@pytest.mark.parametrize("k", [31, 32])
+def test_single_launch_and_two_launch_paths(k):
+    """Float32 rows of V = 262144 hold 32 chunk results each: with k + 1 = 32
+    rows a sequence needs 1024 of them (the single launch's tile), with 33 it
+    needs more and the call takes the two-launch path.  Both are exact and
+    both leave the workspace zero-filled."""
+    note(f"greedy path boundary k={k}")
+    import speculative_decoding_verification_04_amd as sv
+    rng = np.random.default_rng(100 + k)
+    B, V = 3, 262144
+    z = (rng.standard_normal((B, k + 1, V)) * 2).astype(np.float32)
+    amax = np.argmax(z, axis=-1)
+    drafts = np.where(rng.random((B, k)) < 0.9, amax[:, :k], rng.integers(0, V, (B, k))).astype(np.int32)
+    for eos in (-1, int(amax[1, 3])):
+        _compare(z, "f32", drafts, eos_id=eos, remaining=np.array([-1, 5, 0], np.int32))
+    w = ws(sv.spec_verify_greedy_workspace_bytes(B, k, V, sv.SPEC_F32), ("greedy", None))
+    assert int(torch.count_nonzero(w).item()) == 0
+
+
+def test_greedy_and_tree_share_a_workspace():
+    """Greedy and tree verification alternate on one workspace: the tree call
+    accepts any contents and, like the greedy call, leaves it zero-filled."""
+    note("greedy/tree shared workspace")
+    import speculative_decoding_verification_04_amd as sv
+    from tests._gpu import verify_tree
+    rng = np.random.default_rng(31)
+    B, k, V = 5, 4, 40000
+    w = ws(max(sv.spec_verify_greedy_workspace_bytes(B, k, V, sv.SPEC_BF16),
+               sv.spec_verify_tree_workspace_bytes(B, k + 1, V, sv.SPEC_BF16)), ("greedy", "shared"))
+    for it in range(4):
+        z = (rng.standard_normal((B, k + 1, V)) * 2).astype(np.float32)
+        bits = W.bf16_bits_from_f32(z)
+        amax = np.argmax(oracle.widen_bf16(bits), axis=-1)
+        drafts = np.where(rng.random((B, k)) < 0.7, amax[:, :k], rng.integers(0, V, (B, k))).astype(np.int32)
+        dev = logits_to_device(bits, "bf16")
+        got = host(verify_greedy(dev, drafts, ws_key="shared"))
+        ref = oracle.greedy_verify(bits, "bf16", drafts)
+        for key in KEYS:
+            assert np.array_equal(got[key], ref[key]), key
+        assert int(torch.count_nonzero(w).item()) == 0
+        # the same rows as a chain-shaped tree: node i's only child is i + 1
+        fc = np.tile(np.append(np.arange(1, k + 1), -1), (B, 1)).astype(np.int32)
+        ns = np.full((B, k + 1), -1, np.int32)
+        tdraft = np.concatenate([np.zeros((B, 1), np.int32), drafts], axis=1)
+        gt = host(verify_tree(dev, tdraft, fc, ns, ws_key="shared"))
+        assert np.array_equal(gt["emit_count"], ref["emit_count"])
+        assert np.array_equal(gt["out_tokens"], ref["out_tokens"])
+        assert int(torch.count_nonzero(w).item()) == 0
