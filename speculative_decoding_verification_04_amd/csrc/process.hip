@@ -46,9 +46,14 @@
 // Whole-row histograms are kept per lane index: bucket b, column l (256 x 64
 // packed 64-bit words, 128 KB of LDS), so the 64 lanes of an atomic add hit 64
 // different words.  Logits cluster in a few buckets of the top digit; one
-// shared histogram serialised those adds.  A word packs a count (top 10 bits)
-// and a weight (low 54 bits); columns are summed per bucket afterwards.  The
-// bucket scans are parallel suffix sums.
+// shared histogram serialised those adds.  A lane column receives up to about
+// V/64 logits of the row.  A count-only histogram (top-k) keeps a plain count
+// per word.  A histogram of counts and weights packs a count (top 10 bits) and
+// a weight (low 54 bits) into one word only while no column can receive more
+// than 1023 logits (V below about 57000); larger rows take two passes, one of
+// counts and one of weights (at most V/64 weights of at most 2^40 units each,
+// below 2^54).  Columns are summed per bucket afterwards.  The bucket scans
+// are parallel suffix sums.
 // Every selection keeps all logits at or above one threshold, so ties at a
 // boundary are kept, as the definitions require.
 #include "process.h"
@@ -62,6 +67,9 @@ constexpr int kProcU = 4;                      // 16-byte loads in flight per la
 constexpr double kFixScale = 1099511627776.0;  // 2^40 fixed-point units per unit weight
 constexpr int kCntShift = 54;                   // packed histogram word: count << 54 | weight
 constexpr unsigned long long kMassMask = (1ull << kCntShift) - 1;
+constexpr int kPackedMaxColumn = (1 << (64 - kCntShift)) - 1;   // logits a packed column may receive
+// What a whole-row histogram word holds.
+enum HistMode { kHistPacked, kHistCount, kHistMass };
 constexpr int kSliceThreads = 256;              // top-k slice kernel
 constexpr int kSliceLoads = 8;                  // 16-byte loads per lane: one slice
 constexpr int kSliceMaxS = (SPEC_PROC_MAX_V + kSliceThreads * kSliceLoads * 4 - 1) / (kSliceThreads * kSliceLoads * 4);
@@ -167,18 +175,19 @@ __device__ inline float block_max_f(float v, float *sh) {
   return m;
 }
 
-// Sums the 64 columns of every bucket of the per-lane histogram into
-// h_cnt / h_mass.  Contains barriers.
+// Sums the 64 columns of every bucket of the per-lane histogram into h_cnt
+// (packed and count words; count words also set h_mass to 0) and h_mass
+// (packed and weight words).  Contains barriers.
 __device__ inline void fold_columns(const unsigned long long *lh, uint32_t *h_cnt,
-                                   unsigned long long *h_mass) {
+                                   unsigned long long *h_mass, HistMode mode) {
   const int t = threadIdx.x;
   const int b = t >> 2, part = t & 3;          // 4 lanes per bucket, 16 columns each
   unsigned long long c = 0, m = 0;
 #pragma unroll
   for (int i = 0; i < kWave / 4; ++i) {        // columns visited in a bucket-rotated order: no bank conflicts
     const unsigned long long x = lh[b * kWave + part * (kWave / 4) + ((i + b) & (kWave / 4 - 1))];
-    c += x >> kCntShift;
-    m += x & kMassMask;
+    c += mode == kHistPacked ? x >> kCntShift : (mode == kHistCount ? x : 0ull);
+    m += mode == kHistPacked ? x & kMassMask : (mode == kHistMass ? x : 0ull);
   }
 #pragma unroll
   for (int o = 1; o < 4; o <<= 1) {
@@ -186,8 +195,8 @@ __device__ inline void fold_columns(const unsigned long long *lh, uint32_t *h_cn
     m += __shfl_xor(m, o, kWave);
   }
   if (part == 0) {
-    h_cnt[b] = static_cast<uint32_t>(c);
-    h_mass[b] = m;
+    if (mode != kHistMass) h_cnt[b] = static_cast<uint32_t>(c);
+    h_mass[b] = mode == kHistCount ? 0ull : m;
   }
   __syncthreads();
 }
@@ -490,6 +499,12 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   const bool topp = P.cfg.top_p < 1.0f;
   const unsigned long long one = 1ull << kCntShift;
   float *cand = reinterpret_cast<float *>(lh);
+  // counts and weights share one histogram word only while no lane column can
+  // receive more than kPackedMaxColumn logits (16 threads per column, each at
+  // most ceil(V / VEC / kProcThreads) vectors, plus one head and one tail entry)
+  constexpr int kVecElems = BF16 ? 8 : 4;
+  const bool packed = kProcWaves * ((V / kVecElems + kProcThreads - 1) / kProcThreads) * kVecElems + 2 <=
+                      kPackedMaxColumn;
 
   // ---- the row's candidates: with top-k, the slice kernel's lists when every
   //      slice's fit (their union holds every logit at or above the K-th
@@ -655,7 +670,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
     __syncthreads();
     row_foreach<BF16>(row, V, [&](int, float z) {
       m = fmaxf(m, z);
-      if (topk) atomicAdd(&lh[(f32_order_key(z) >> 24) * kWave + lane], one);
+      if (topk) atomicAdd(&lh[(f32_order_key(z) >> 24) * kWave + lane], 1ull);
     });
   }
   const float zmax = block_max_f(m, sh_f);     // (contains barriers)
@@ -776,7 +791,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
     kmask = bits_above(k_hi);
     kprefix = min(max(cutmax, 1u), khi) & kmask;
   } else if (topk) {
-    fold_columns(lh, h_cnt, h_mass);
+    fold_columns(lh, h_cnt, h_mass, kHistCount);
     ncand = select_k(24, 255u);
     k_hi = 23;
     cutoff = kprefix;
@@ -815,15 +830,25 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
       }
     }
     if (!use_list) {
-      // pass 2 over the row: first top-p digit histogram (counts and weights)
+      // pass 2 over the row: first top-p digit histogram (counts and weights;
+      // counts, then weights, when a packed column could overflow)
       clear_columns(lh);
       __syncthreads();
       row_foreach<BF16>(row, V, [&](int, float z) {
         const uint32_t key = f32_order_key(z);
-        atomicAdd(&lh[(key >> 24) * kWave + lane], one + fixed_weight(proc_weight(z, zmax, invT)));
+        atomicAdd(&lh[(key >> 24) * kWave + lane], packed ? one + fixed_weight(proc_weight(z, zmax, invT)) : 1ull);
       });
       __syncthreads();
-      fold_columns(lh, h_cnt, h_mass);
+      fold_columns(lh, h_cnt, h_mass, packed ? kHistPacked : kHistCount);
+      if (!packed) {
+        clear_columns(lh);
+        __syncthreads();
+        row_foreach<BF16>(row, V, [&](int, float z) {
+          atomicAdd(&lh[(f32_order_key(z) >> 24) * kWave + lane], fixed_weight(proc_weight(z, zmax, invT)));
+        });
+        __syncthreads();
+        fold_columns(lh, h_cnt, h_mass, kHistMass);
+      }
       ncand = select_p(24, 255u, true, 0ull);
       p_started = true;
       p_hi = 23;
@@ -834,18 +859,26 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   int n = use_list ? nfast : 0;
   if (listed && !use_list) {
     // pass over the row: copy every logit at or above the cutoff into LDS
+    // (ncand counted them; the bound keeps every write inside the list)
     if (t == 0) sh_n = 0;
     __syncthreads();
     row_foreach<BF16>(row, V, [&](int, float z) {
-      if (f32_order_key(z) >= cutoff) cand[atomicAdd(&sh_n, 1)] = z;
+      if (f32_order_key(z) >= cutoff) {
+        const int slot = atomicAdd(&sh_n, 1);
+        if (slot < kCandCap) cand[slot] = z;
+      }
     });
     __syncthreads();
     n = sh_n;
   }
+  // A list that did not fit (the histogram's count was exact, so this does
+  // not happen) is dropped: the remaining levels then read the row.
+  const bool listed_ok = !(listed && !use_list) || n <= kCandCap;
 
   // Visits every logit that can still matter: the LDS list, or the row.
+  const bool on_list = listed && listed_ok;
   auto each = [&](auto &&f) {
-    if (listed) {
+    if (on_list) {
       for (int i = t; i < n; i += kProcThreads) f(cand[i]);
     } else {
       row_foreach<BF16>(row, V, [&](int, float z) { f(z); });
@@ -854,7 +887,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   // Histogram of digit (key >> shift) & dmask over the logits passing `pred`,
   // with weights if asked, into h_cnt / h_mass.  Barriers.
   auto histogram = [&](int shift, uint32_t dmask, bool weights, auto &&pred) {
-    if (listed) {
+    if (on_list) {
       h_cnt[t] = 0u;                             // one bucket per lane
       h_mass[t] = 0ull;
       __syncthreads();
@@ -868,24 +901,37 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
       });
       __syncthreads();
     } else {
+      // whole-row words: counts alone, counts and weights packed, or (when a
+      // packed column could overflow) a pass of counts and a pass of weights
+      const HistMode first = !weights ? kHistCount : (packed ? kHistPacked : kHistCount);
       clear_columns(lh);
       __syncthreads();
       each([&](float z) {
         const uint32_t key = f32_order_key(z);
         if (pred(key)) {
-          unsigned long long add = one;
-          if (weights) add += fixed_weight(proc_weight(z, zmax, invT));
+          const unsigned long long add =
+              first == kHistPacked ? one + fixed_weight(proc_weight(z, zmax, invT)) : 1ull;
           atomicAdd(&lh[((key >> shift) & dmask) * kWave + lane], add);
         }
       });
       __syncthreads();
-      fold_columns(lh, h_cnt, h_mass);
+      fold_columns(lh, h_cnt, h_mass, first);
+      if (weights && !packed) {
+        clear_columns(lh);
+        __syncthreads();
+        each([&](float z) {
+          const uint32_t key = f32_order_key(z);
+          if (pred(key)) atomicAdd(&lh[((key >> shift) & dmask) * kWave + lane], fixed_weight(proc_weight(z, zmax, invT)));
+        });
+        __syncthreads();
+        fold_columns(lh, h_cnt, h_mass, kHistMass);
+      }
     }
   };
 
   // ---- top-k: remaining digits
   uint32_t tau = 0;
-  const int digit = listed ? kListDigit : kRowDigit;
+  const int digit = on_list ? kListDigit : kRowDigit;
   if (topk) {
     for (int hi = k_hi; hi >= kLow; hi -= digit) {
       const int shift = max(hi - (digit - 1), kLow);

@@ -340,3 +340,18 @@ def test_verify_from_logits_largest_k(dtype):
     assert ref["accept_len"][0] == k                  # identical p' and q': every draft accepted
     assert exact >= B - 1
     assert got["emit_offsets"][-1] == got["emit_count"].sum()
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 256000), ("f32", 256000), ("bf16", 524288)])
+def test_process_whole_row_histograms_of_long_rows(dtype, V):
+    """Rows long enough that one lane column of the whole-row histogram
+    receives thousands of logits (about V/64), most of them in a few buckets
+    of the top digit: large top-k (the row path) and top-p with most of the
+    weight spread over the row (the slices' union carries too little of it).
+    N(0, 1) logits at T = 1 put about 4% of a row in one bucket."""
+    rng = np.random.default_rng(V % 1000 + (1 if dtype == "bf16" else 0))
+    dev_in, zw = _rows(rng, 3, V, dtype, sd=1.0)
+    zd = logits_to_device(dev_in, dtype)
+    for T, K, P in [(1.0, 10000, 1.0), (1.0, 0, 0.5), (1.0, 10000, 0.5), (1.0, 0, 0.9), (0.8, 40000, 0.97)]:
+        note(f"process long rows {dtype} V={V} T={T} K={K} P={P}")
+        _check_rows(zw, host(process(zd, T, K, P)), T, K, P)
