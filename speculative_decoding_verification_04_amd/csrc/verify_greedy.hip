@@ -615,37 +615,18 @@ extern "C" size_t spec_verify_greedy_workspace_bytes(int B, int k, int V, spec_d
   return greedy_ws_bytes(B, k, greedy_chunks(V, dt));
 }
 
-extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int k, int V,
-                                  const int32_t *draft, int32_t eos_id, const int32_t *remaining,
-                                  int32_t *accept_len, int32_t *emit_count, int32_t *out_tokens,
-                                  int32_t *emit_offsets, int32_t *status, void *ws,
-                                  size_t ws_bytes, spec_stream_t stream) {
-  if (!logits || !draft || !accept_len || !emit_count || !out_tokens || !ws) return SPEC_EINVAL;
-  if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_EINVAL;
-  if (B < 1 || k < 1 || V < 1 || V >= INT32_MAX - 1) return SPEC_EINVAL;
-  if (k > SPEC_MAX_K) return SPEC_ECAPACITY;
+// Argument checks and launch of a greedy verification on the chunk-key array
+// `keys` (wsb bytes).  noalloc: the keys are the library's static scratch (any
+// contents on entry), so the two-launch path is taken, whose streaming kernel
+// writes every slot before the commit reads it.
+static int greedy_verify_launch(const void *logits, spec_dtype dt, int B, int k, int V,
+                                const int32_t *draft, int32_t eos_id, const int32_t *remaining,
+                                int32_t *accept_len, int32_t *emit_count, int32_t *out_tokens,
+                                int32_t *emit_offsets, int32_t *status, void *keys, bool noalloc,
+                                spec_stream_t stream) {
   const size_t elt = dt == SPEC_BF16 ? 2 : 4;
-  if (!aligned(logits, elt)) return SPEC_EINVAL;
   const int chunks = greedy_chunks(V, dt);
   const long long nblocks = static_cast<long long>(B) * (k + 1) * chunks;
-  if (nblocks >= INT32_MAX) return SPEC_EINVAL;
-  const size_t wsb = greedy_ws_bytes(B, k, chunks);
-  if (ws_bytes < wsb || !aligned(ws, 256)) return SPEC_EWORKSPACE;
-
-  const size_t nl = static_cast<size_t>(B) * (k + 1) * V * elt;
-  const void *ins[] = {logits, draft, remaining, ws};
-  const size_t in_n[] = {nl, static_cast<size_t>(B) * k * 4, static_cast<size_t>(B) * 4, wsb};
-  const void *outs[] = {accept_len, emit_count, out_tokens, emit_offsets, status};
-  const size_t out_n[] = {static_cast<size_t>(B) * 4, static_cast<size_t>(B) * 4,
-                          static_cast<size_t>(B) * (k + 1) * 4, static_cast<size_t>(B + 1) * 4,
-                          static_cast<size_t>(B) * 4};
-  for (int i = 0; i < 5; ++i) {
-    for (int j = 0; j < 4; ++j)
-      if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return SPEC_EINVAL;
-    for (int j = i + 1; j < 5; ++j)
-      if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return SPEC_EINVAL;
-  }
-
   GreedyParams P;
   P.logits = static_cast<const unsigned char *>(logits);
   P.B = B;
@@ -661,13 +642,14 @@ extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int 
   P.out_tokens = out_tokens;
   P.emit_offsets = emit_offsets;
   P.status = status;
-  P.keys = static_cast<uint64_t *>(ws);
+  P.keys = static_cast<uint64_t *>(keys);
   P.nprod = static_cast<int>(nblocks);
   P.first_child = P.next_sibling = nullptr;
   P.path = nullptr;
+  (void)elt;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (tile_sequences(k, chunks) >= 1 && nblocks + 1 < INT32_MAX) {
+  if (!noalloc && tile_sequences(k, chunks) >= 1 && nblocks + 1 < INT32_MAX) {
     // one launch: workgroup 0 commits, the others stream
     const dim3 grid(static_cast<unsigned>(nblocks + 1));
     if (dt == SPEC_BF16) hipLaunchKernelGGL(greedy_verify_kernel<true>, grid, dim3(kThreads), 0, s, P);
@@ -680,6 +662,53 @@ extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int 
     hipLaunchKernelGGL(greedy_chunk_kernel<false>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
   hipLaunchKernelGGL(greedy_commit_kernel, dim3(1), dim3(kCommitThreads), 0, s, P);
   return launch_status();
+}
+
+// Host checks shared by both greedy entry points; ws may be null (no-alloc).
+static int greedy_verify_check(const void *logits, spec_dtype dt, int B, int k, int V, const int32_t *draft,
+                               const int32_t *remaining, int32_t *accept_len, int32_t *emit_count,
+                               int32_t *out_tokens, int32_t *emit_offsets, int32_t *status,
+                               const void *ws, size_t *wsb_out) {
+  if (!logits || !draft || !accept_len || !emit_count || !out_tokens) return SPEC_EINVAL;
+  if (dt != SPEC_F32 && dt != SPEC_BF16) return SPEC_EINVAL;
+  if (B < 1 || k < 1 || V < 1 || V >= INT32_MAX - 1) return SPEC_EINVAL;
+  if (k > SPEC_MAX_K) return SPEC_ECAPACITY;
+  const size_t elt = dt == SPEC_BF16 ? 2 : 4;
+  if (!aligned(logits, elt)) return SPEC_EINVAL;
+  const int chunks = greedy_chunks(V, dt);
+  const long long nblocks = static_cast<long long>(B) * (k + 1) * chunks;
+  if (nblocks >= INT32_MAX) return SPEC_EINVAL;
+  const size_t wsb = greedy_ws_bytes(B, k, chunks);
+  *wsb_out = wsb;
+  const size_t nl = static_cast<size_t>(B) * (k + 1) * V * elt;
+  const void *ins[] = {logits, draft, remaining, ws};
+  const size_t in_n[] = {nl, static_cast<size_t>(B) * k * 4, static_cast<size_t>(B) * 4, ws ? wsb : 0};
+  const void *outs[] = {accept_len, emit_count, out_tokens, emit_offsets, status};
+  const size_t out_n[] = {static_cast<size_t>(B) * 4, static_cast<size_t>(B) * 4,
+                          static_cast<size_t>(B) * (k + 1) * 4, static_cast<size_t>(B + 1) * 4,
+                          static_cast<size_t>(B) * 4};
+  for (int i = 0; i < 5; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return SPEC_EINVAL;
+    for (int j = i + 1; j < 5; ++j)
+      if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return SPEC_EINVAL;
+  }
+  return SPEC_OK;
+}
+
+extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int k, int V,
+                                  const int32_t *draft, int32_t eos_id, const int32_t *remaining,
+                                  int32_t *accept_len, int32_t *emit_count, int32_t *out_tokens,
+                                  int32_t *emit_offsets, int32_t *status, void *ws,
+                                  size_t ws_bytes, spec_stream_t stream) {
+  if (!ws) return SPEC_EINVAL;
+  size_t wsb = 0;
+  const int rc = greedy_verify_check(logits, dt, B, k, V, draft, remaining, accept_len, emit_count, out_tokens,
+                                     emit_offsets, status, ws, &wsb);
+  if (rc != SPEC_OK) return rc;
+  if (ws_bytes < wsb || !aligned(ws, 256)) return SPEC_EWORKSPACE;
+  return greedy_verify_launch(logits, dt, B, k, V, draft, eos_id, remaining, accept_len, emit_count, out_tokens,
+                              emit_offsets, status, ws, false, stream);
 }
 
 extern "C" size_t spec_verify_tree_workspace_bytes(int B, int N, int V, spec_dtype dt) {
