@@ -120,6 +120,27 @@ int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int k, int V,
                        void *ws, size_t ws_bytes, spec_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * Greedy verification that allocates nothing and takes no workspace.
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, outputs and errors as spec_verify_greedy without ws / ws_bytes;
+ * the chunk results live in a static device array of
+ * SPEC_GREEDY_SCRATCH_BYTES per GPU (held until the process ends), so a call
+ * needs spec_verify_greedy_workspace_bytes(B, k, V, dt) <=
+ * SPEC_GREEDY_SCRATCH_BYTES, else it returns SPEC_ECAPACITY.  It launches the
+ * streaming pass and the commit pass (two launches; no memory needs clearing
+ * first).  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (different streams, threads) race and give undefined
+ * results; calls in one stream are ordered and safe.  SPEC_EHIP if the
+ * array's device address cannot be obtained.
+ * ------------------------------------------------------------------------ */
+#define SPEC_GREEDY_SCRATCH_BYTES (8u << 20)
+int spec_verify_greedy_noalloc(const void *logits, spec_dtype dt, int B, int k, int V,
+                               const int32_t *draft, int32_t eos_id, const int32_t *remaining,
+                               int32_t *accept_len, int32_t *emit_count, int32_t *out_tokens,
+                               int32_t *emit_offsets, int32_t *status, spec_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Stochastic (Leviathan-style) verification.
  * [Atlas] The mechanism steps 2-5 and Acceptance and rejection correction;
  * [Walkthrough] 5.1.  For j = 0, 1, ...: x = draft[b, j],

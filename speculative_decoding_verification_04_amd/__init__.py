@@ -17,9 +17,11 @@ SPEC_OK, SPEC_EINVAL, SPEC_EWORKSPACE, SPEC_ECAPACITY, SPEC_EHIP = 0, -1, -2, -3
 SPEC_ST_DRAFT_OOR, SPEC_ST_Q_ZERO, SPEC_ST_RESID_ZERO = 1, 2, 4
 SPEC_ST_NONFINITE, SPEC_ST_BAD_STATE, SPEC_ST_CAPACITY, SPEC_ST_INCOMPLETE = 8, 16, 32, 64
 SPEC_MAX_K, SPEC_GROUP_MAX_N, SPEC_PROC_MAX_V, SPEC_TREE_MAX_N = 127, 4096, 524288, 256
+SPEC_GREEDY_SCRATCH_BYTES = 8 << 20
 
 __all__ = [
     "SpecError", "spec_strerror", "spec_verify_greedy_workspace_bytes", "spec_verify_greedy",
+    "spec_verify_greedy_noalloc", "SPEC_GREEDY_SCRATCH_BYTES",
     "spec_verify_sample_workspace_bytes", "spec_verify_sample", "spec_process_workspace_bytes",
     "spec_process_logits", "spec_verify_sample_logits_workspace_bytes", "spec_verify_sample_logits",
     "spec_commit_realign_kv", "spec_resync_draft_kv", "spec_commit_paged",
@@ -124,6 +126,22 @@ def spec_verify_greedy(logits, draft, accept_len, emit_count, out_tokens, ws, *,
         _arg(emit_offsets, "int32", B + 1, "emit_offsets", True), _arg(status, "int32", B, "status", True),
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(code, "spec_verify_greedy")
+
+
+def spec_verify_greedy_noalloc(logits, draft, accept_len, emit_count, out_tokens, *,
+                               eos_id: int = -1, remaining=None, emit_offsets=None, status=None,
+                               stream=None) -> None:
+    """spec_verify_greedy without a workspace: the library's static per-GPU
+    array holds the chunk results (calls overlapping on one GPU race)."""
+    B, kp1, V = logits.shape
+    k = kp1 - 1
+    code = library().spec_verify_greedy_noalloc(
+        _ptr(logits), _dtype_code(logits), B, k, V, _arg(draft, "int32", B * k, "draft"), int(eos_id),
+        _arg(remaining, "int32", B, "remaining", True), _arg(accept_len, "int32", B, "accept_len"),
+        _arg(emit_count, "int32", B, "emit_count"), _arg(out_tokens, "int32", B * kp1, "out_tokens"),
+        _arg(emit_offsets, "int32", B + 1, "emit_offsets", True), _arg(status, "int32", B, "status", True),
+        _stream(stream))
+    _check(code, "spec_verify_greedy_noalloc")
 
 
 def spec_verify_sample(p, q, draft, uniforms, accept_len, emit_count, out_tokens, ws, *,

@@ -17,6 +17,7 @@ PROTOTYPES = {
     "spec_verify_greedy_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "spec_verify_greedy": (_I, [_P, _I, _I, _I, _I, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
                                 _P, _SZ, _P]),
+    "spec_verify_greedy_noalloc": (_I, [_P, _I, _I, _I, _I, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
     "spec_verify_sample_workspace_bytes": (_SZ, [_I, _I, _I]),
     "spec_verify_sample": (_I, [_P, _P, _P, _P, _I, _I, _I, ctypes.c_int32, _P, _P, _P, _P, _P,
                                 _P, _P, _P, _SZ, _P]),

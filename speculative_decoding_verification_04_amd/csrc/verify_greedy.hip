@@ -36,6 +36,8 @@
 // streaming kernel with its own commit).
 #include "common.h"
 
+#include <mutex>
+
 namespace specv {
 namespace {
 
@@ -709,6 +711,51 @@ extern "C" int spec_verify_greedy(const void *logits, spec_dtype dt, int B, int 
   if (ws_bytes < wsb || !aligned(ws, 256)) return SPEC_EWORKSPACE;
   return greedy_verify_launch(logits, dt, B, k, V, draft, eos_id, remaining, accept_len, emit_count, out_tokens,
                               emit_offsets, status, ws, false, stream);
+}
+
+// ----------------------------------------------------------- no-alloc ----
+// Chunk keys of spec_verify_greedy_noalloc: a static array on every device the
+// library runs on (kept until the process ends).  Host code never passes the
+// array's name to a kernel or a copy: the name is a host-side stand-in, not a
+// device address.  The device address comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+static __device__ __align__(256) uint64_t scratch[SPEC_GREEDY_SCRATCH_BYTES / sizeof(uint64_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device).
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPEC_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return SPEC_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_OK;
+}
+}  // namespace
+
+extern "C" int spec_verify_greedy_noalloc(const void *logits, spec_dtype dt, int B, int k, int V,
+                                          const int32_t *draft, int32_t eos_id, const int32_t *remaining,
+                                          int32_t *accept_len, int32_t *emit_count, int32_t *out_tokens,
+                                          int32_t *emit_offsets, int32_t *status, spec_stream_t stream) {
+  size_t wsb = 0;
+  int rc = greedy_verify_check(logits, dt, B, k, V, draft, remaining, accept_len, emit_count, out_tokens,
+                               emit_offsets, status, nullptr, &wsb);
+  if (rc != SPEC_OK) return rc;
+  if (wsb > SPEC_GREEDY_SCRATCH_BYTES) return SPEC_ECAPACITY;
+  void *keys = nullptr;
+  rc = scratch_address(&keys);
+  if (rc != SPEC_OK) return rc;
+  return greedy_verify_launch(logits, dt, B, k, V, draft, eos_id, remaining, accept_len, emit_count, out_tokens,
+                              emit_offsets, status, keys, true, stream);
 }
 
 extern "C" size_t spec_verify_tree_workspace_bytes(int B, int N, int V, spec_dtype dt) {
