@@ -189,12 +189,15 @@ int spec_verify_sample(const float *p, const float *q, const int32_t *draft,
  *         top_p times their total weight (ties at the boundary are kept);
  *   p'(v) = w(v) / (sum of the kept w), 0 for dropped entries and for rows
  *         with no weight.
- * Arithmetic: w in float32, the hardware exp2 of (z - max z) * (1/T) * log2(e);
- * sums and the top-p comparison use the weights truncated to 2^-40 units and
- * added exactly, so results are reproducible run to run.  Against a float64
- * evaluation, p' agrees to a relative 2e-5 (the error of a weight grows with
- * |z - max z| / T), and a top-p boundary can differ only where the weight
- * above it is within about V * 2^-40 of top_p times the total.
+ * Arithmetic: w in float32, the accurate expf of (z - max z) / T with the
+ * argument's rounding errors (the difference's, the product by 1/T's and that
+ * of 1/T itself) folded back in to first order, so a weight is within
+ * 2^-23 + 2^-24 relative of exp((z - max z) / T) whatever the argument; sums
+ * and the top-p comparison use the weights truncated to 2^-40 units and added
+ * exactly, so results are reproducible run to run.  Against a float64
+ * evaluation, p' agrees to a relative 4.8e-7 + 9.1e-13 * V, and a top-p
+ * boundary can differ only where the weight above it is within about
+ * V * 2^-40 of top_p times the total.
  * Logits must be finite or -inf.
  *
  * spec_process_logits -- processes R rows:

@@ -288,7 +288,7 @@ __device__ inline uint32_t bits_above(int top) { return top >= 31 ? 0u : (0xFFFF
 // for most bf16 lists); the keys chosen are the same as with fixed digits.
 // Lane l owns buckets 255 - 4l .. 252 - 4l (descending) of hc / hm.
 template <bool BF16, class Each>
-__device__ inline void wave_list_stats(Each &&each, uint32_t klo, uint32_t khi, float zmax, float invT, int K,
+__device__ inline void wave_list_stats(Each &&each, uint32_t klo, uint32_t khi, float zmax, Temper invT, int K,
                                        bool topp_on, float top_p, uint32_t *hc, unsigned long long *hm,
                                        ProcStats &st) {
   constexpr int kLow = BF16 ? 16 : 0;            // bf16 keys carry no information below bit 16
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   const int r = blockIdx.x;
   const int V = P.V;
   const void *row = proc_row<BF16>(P, r);
-  const float invT = P.cfg.invT;
+  const Temper invT = P.cfg.invT;
   const int K = P.cfg.top_k;
   const bool topk = K > 0 && K < V;
   const bool topp = P.cfg.top_p < 1.0f;
@@ -1283,7 +1283,7 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slmass_kernel(ProcParams P
   for (int j = 0; j < P.S; ++j) mk = max(mk, P.sl_max[static_cast<size_t>(r) * P.S + j]);
   const float zmax = f32_from_order_key(mk);
   const bool finite = zmax != -INFINITY;      // else every weight is 0
-  const float invT = P.cfg.invT;
+  const Temper invT = P.cfg.invT;
   const SV sl(P, r, s);
   uint4 q[kSliceLoads];
   sl.load(q);
@@ -1314,7 +1314,7 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slmass_kernel(ProcParams P
       if (sl.whole(u)) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float a = __expf((vec_entry<BF16>(q[u], e) - zmax) * invT) * 1048576.0f;
+          const float a = proc_weight(vec_entry<BF16>(q[u], e), zmax, invT) * 1048576.0f;
           const uint32_t hi = static_cast<uint32_t>(a);
           sum_hi += hi;
           sum_lo += static_cast<uint32_t>((a - static_cast<float>(hi)) * 1048576.0f);
@@ -1377,7 +1377,7 @@ static ProcWs proc_ws_layout(int rows, int V) {
 size_t proc_list_bytes(int rows, int V) { return proc_ws_layout(rows, V).total; }
 
 int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int V, bool bf16,
-                      float invT, int top_k, float top_p, ProcStats *stats, float *probs,
+                      Temper invT, int top_k, float top_p, ProcStats *stats, float *probs,
                       void *list_ws, hipStream_t s) {
   ProcParams P;
   P.za = za;
@@ -1490,7 +1490,7 @@ extern "C" int spec_process_logits(const void *logits, spec_dtype dt, int R, int
   ProcStats *stats = static_cast<ProcStats *>(ws);
   void *lists = static_cast<unsigned char *>(ws) + round_up(static_cast<size_t>(R) * sizeof(ProcStats), 256);
   (void)hipGetLastError();
-  launch_proc_stats(logits, logits, R, R, V, dt == SPEC_BF16, 1.0f / temperature, top_k, top_p, stats,
+  launch_proc_stats(logits, logits, R, R, V, dt == SPEC_BF16, make_temper(temperature), top_k, top_p, stats,
                     probs, lists, s);
   if (row_max || row_threshold || row_mass)
     hipLaunchKernelGGL(proc_export_kernel, dim3((R + 255) / 256), dim3(256), 0, s, stats, R, row_max,

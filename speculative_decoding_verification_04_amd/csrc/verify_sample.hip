@@ -43,7 +43,7 @@ struct SampleParams {
   const float *p, *q;           // dense rows (spec_verify_sample)
   const void *zp, *zq;          // logits (spec_verify_sample_logits)
   const ProcStats *sp, *sq;     // statistics of the processed rows
-  float invT;                   // 1 / temperature
+  Temper invT;                  // 1 / temperature
   const int32_t *draft;
   const float *u;
   int B, k, V, chunks;
@@ -114,7 +114,7 @@ template <bool BF16>
 struct LogitRow {
   const void *a, *b;
   ProcStats sa, sb;
-  float invT;
+  Temper invT;
   bool resid;
   __device__ inline float at(int v) const {
     const float pa = proc_prob(logit_at<BF16>(a, v), sa, invT);
@@ -531,7 +531,7 @@ extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t 
   P.q = q;
   P.zp = P.zq = nullptr;
   P.sp = P.sq = nullptr;
-  P.invT = 1.0f;
+  P.invT = make_temper(1.0f);
   P.draft = draft;
   P.u = uniforms;
   P.B = B;
@@ -618,7 +618,7 @@ extern "C" int spec_verify_sample_logits(const void *target_logits, const void *
   P.zq = draft_logits;
   P.sp = stats;                                   // target rows first
   P.sq = stats + static_cast<size_t>(B) * (k + 1); // then the draft rows
-  P.invT = 1.0f / temperature;
+  P.invT = make_temper(temperature);
   P.draft = draft;
   P.u = uniforms;
   P.B = B;

@@ -1,13 +1,28 @@
 """GPU parity of the processed-distribution calls (temperature, top-k, top-p)
 against the oracle.
 
-Tolerances (from the arithmetic stated in include/spec_verify.h): the GPU
-weights are float32 (expf of one IEEE division), the oracle's float64, so a
-kept probability agrees to a relative 2e-5 and a row's kept weight to 2e-5;
-the row maximum is exact; a kept set is exact except that a top-p boundary
-may move where the oracle, run with top_p -/+ 1e-5, brackets the GPU's
-threshold.  Verification decisions then follow the rules of the stochastic
-parity tests with the same relative allowance.
+Tolerances, from the arithmetic stated in include/spec_verify.h.  A GPU
+weight is the accurate float32 expf of (z - max z) / T with the argument's
+rounding error folded back in (relative error <= 2^-23 + 2^-24); the kept
+weight is an exact sum of weights truncated to 2^-40 (error <= V * 2^-40,
+and the kept weight is at least 1); 1 / mass and p' = w * (1 / mass) are each
+rounded once.  So a kept probability p' agrees with the oracle's float64 value
+to a relative
+
+    E_P(V) = 2 (2^-23 + 2^-24) + 2 * 2^-24 + V * 2^-40   (4.8e-7 + 9.1e-13 V),
+
+checked against RTOL = 1e-5; the row maximum is exact; a kept set is exact
+except that a top-p boundary may move where the oracle, run with top_p -/+
+1e-5, brackets the GPU's threshold.  Verification: a = min(1, p'(x) / q'(x))
+differs by at most ACCEPT(V) = 2 E_P(V) + 2^-24 (1.0e-6 + 1.8e-12 V: the
+the benchmark spec's 1e-6, widened by the kept-weight truncation), so a decision may
+differ only where |u - a| < ACCEPT(V); the residual mass S = sum max(p' - q', 0)
+and every prefix sum of the drawn row differ by at most 2 E_P(V) absolute, so
+S must agree to 1e-5 * S + 2 E_P(V) and a drawn token may differ only where
+u * S lies within that distance of a prefix boundary.  Decisions near the
+boundary occur with probability about ACCEPT(V) per decision (none expected
+in these cases, so none is allowed); a draw differs with probability about
+4 E_P(V) / p'(token) per draw, so at most one per case is allowed.
 """
 import numpy as np
 import pytest
@@ -22,8 +37,17 @@ from tests._gpu import DEV, _WS, host, logits_to_device, note, process, requires
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
-RTOL = 2e-5
+RTOL = 1e-5
 PTOL = 1e-5
+
+
+def e_p(V: int) -> float:
+    """Relative bound on a GPU p' against the oracle's (module docstring)."""
+    return 2 * (2.0 ** -23 + 2.0 ** -24) + 2 * 2.0 ** -24 + V * 2.0 ** -40
+
+
+def accept_allowance(V: int) -> float:
+    return 2 * e_p(V) + 2.0 ** -24
 
 
 def _rows(rng, R, V, dtype, sd=3.0, ties=False):
@@ -191,18 +215,23 @@ def test_process_workload_rows_full_size(dtype, T, K, P):
     _check_rows(zw, got, T, K, P)
 
 
-def _check_verify(p, q, d, u, got, ref, tol=RTOL):
-    """Verification outputs on processed rows p, q (the oracle's)."""
+def _check_verify(p, q, d, u, got, ref):
+    """Verification outputs on processed rows p, q (the oracle's).  Returns
+    counts: exact (identical outputs), accept_tol (a decision differing inside
+    ACCEPT(V)), draw_tol (a draw differing inside the window), draws."""
     B, kp1, V = p.shape
     k = kp1 - 1
-    exact = 0
+    A = accept_allowance(V)
+    D = 2 * e_p(V)
+    c = dict(exact=0, accept_tol=0, draw_tol=0, draws=0)
     for b in range(B):
         mr, mg = int(ref["accept_len"][b]), int(got["accept_len"][b])
         if mr != mg:
             j = min(mr, mg)
             x = int(d[b, j])
             a = min(1.0, float(p[b, j, x]) / float(q[b, j, x])) if q[b, j, x] > 0 else float(p[b, j, x] > 0)
-            assert abs(float(u[b, j]) - a) <= 3 * tol * max(a, 1e-30), (b, j, u[b, j], a)
+            assert abs(float(u[b, j]) - a) < A, (b, j, u[b, j], a)
+            c["accept_tol"] += 1
             continue
         assert got["emit_count"][b] == ref["emit_count"][b], b
         assert got["status"][b] == ref["status"][b], b
@@ -212,12 +241,14 @@ def _check_verify(p, q, d, u, got, ref, tol=RTOL):
         Sr, Sg = float(ref["final_mass"][b]), float(got["final_mass"][b])
         if e == mr:
             assert Sg == 0.0 and Sr == 0.0
-            exact += 1
+            c["exact"] += 1
             continue
-        assert abs(Sg - Sr) <= 3 * tol * abs(Sr), (b, Sg, Sr)
+        c["draws"] += 1
+        w = 1e-5 * abs(Sr) + D
+        assert abs(Sg - Sr) <= w, (b, Sg, Sr)
         vg, vr = int(got["out_tokens"][b, e - 1]), int(ref["out_tokens"][b, e - 1])
         if vg == vr:
-            exact += 1
+            c["exact"] += 1
             continue
         row = np.maximum(p[b, mr] - q[b, mr], 0) if mr < k else p[b, k]
         if mr < k and ref["status"][b] & oracle.ST_RESID_ZERO:
@@ -225,8 +256,15 @@ def _check_verify(p, q, d, u, got, ref, tol=RTOL):
         C = np.cumsum(row.astype(np.float64))
         Tt = float(u[b, k]) * Sr
         lo = C[vg - 1] if vg > 0 else 0.0
-        assert row[vg] > 0 and lo - 3 * tol * Sr <= Tt <= C[vg] + 3 * tol * Sr, (b, vg, vr)
-    return exact
+        assert row[vg] > 0 and lo - w <= Tt <= C[vg] + w, (b, vg, vr)
+        c["draw_tol"] += 1
+    return c
+
+
+def _assert_counts(c, B):
+    assert c["accept_tol"] == 0, c
+    assert c["draw_tol"] <= 1, c
+    assert c["exact"] + c["draw_tol"] == B, c
 
 
 def _verify_case(zt, zd_, T, K, P, seed, dtype):
@@ -259,8 +297,8 @@ def test_verify_from_logits_parity(dtype, V):
     zd_ = (zt[:, :k] + rng.standard_normal((B, k, V)) * 0.7).astype(np.float32)
     for T, K, P in [(1.0, 0, 1.0), (0.7, 20, 0.9), (1.5, 0, 0.8), (0.6, 3, 1.0)]:
         note(f"verify logits {dtype} V={V} T={T} K={K} P={P}")
-        exact, got, ref = _verify_case(zt, zd_, T, K, P, V, dtype)
-        assert exact >= B - 1
+        counts, got, ref = _verify_case(zt, zd_, T, K, P, V, dtype)
+        _assert_counts(counts, B)
         assert got["emit_offsets"][-1] == got["emit_count"].sum()
 
 
@@ -269,8 +307,8 @@ def test_verify_from_logits_workload_full_size(dtype):
     """Stochastic workload: B=8, k=4, V=151936, T=0.7, top-k 50, top-p 0.9."""
     g = W.sample_logits(2)
     note(f"verify logits workload {dtype}")
-    exact, got, ref = _verify_case(g["zt"], g["zd"], g["temperature"], 50, 0.9, 2, dtype)
-    assert exact >= 7
+    counts, got, ref = _verify_case(g["zt"], g["zd"], g["temperature"], 50, 0.9, 2, dtype)
+    _assert_counts(counts, 8)
 
 
 def test_verify_from_logits_output_law():
@@ -336,9 +374,9 @@ def test_verify_from_logits_largest_k(dtype):
     zd_[1] += (rng.standard_normal((k, V)) * 0.05).astype(np.float32)
     zd_[2] += (rng.standard_normal((k, V)) * 0.5).astype(np.float32)
     note(f"verify logits k={k} {dtype}")
-    exact, got, ref = _verify_case(zt, zd_, 0.8, 10, 0.9, 7, dtype)
+    counts, got, ref = _verify_case(zt, zd_, 0.8, 10, 0.9, 7, dtype)
     assert ref["accept_len"][0] == k                  # identical p' and q': every draft accepted
-    assert exact >= B - 1
+    _assert_counts(counts, B)
     assert got["emit_offsets"][-1] == got["emit_count"].sum()
 
 
