@@ -1,11 +1,16 @@
 """GPU parity of spec_verify_sample against the oracle.
 
-Acceptance decisions use the same float32 division and uniforms on both
-sides and are expected bit-exact; the acceptance rule of the check still
-tolerates a differing decision where |u - a| < 1e-6.  Drawn tokens may differ
-only where u * S lies within 1e-5 * S of a boundary of the oracle's prefix
-sums, and the drawn row's mass S must agree to 1e-5 relative.  Small cases
-are compared exactly (including the exact output law by enumeration)."""
+Acceptance decisions use the same float32 division of the same float32
+values and the same uniforms on both sides, so accept lengths, emit counts,
+status bits and the accepted tokens must be bit-exact (the spec rule
+would tolerate a decision where |u - a| < 1e-6; none is needed).  The drawn
+row's mass S must agree to 1e-5 relative, and a drawn token may differ only
+where u * S lies within 1e-5 * S of a boundary of the oracle's prefix sums.
+Both sides add the same float32 terms in float64, in different orders, so
+their prefix sums differ by about V * 2^-53 * S: a draw differs only if u * S
+falls that close to a boundary (probability ~1e-10 per draw), and every
+seeded case below requires every draw to be exact.  Small cases are compared
+exactly (including the exact output law by enumeration)."""
 import math
 from fractions import Fraction
 import itertools
@@ -33,18 +38,16 @@ def _run(p, q, d, u, eos_id=-1, remaining=None, p_dev=None, q_dev=None):
 
 
 def check_within_tolerance(p, q, d, u, got, ref):
-    """Apply the acceptance rule; returns (exact, tolerated) sequence counts."""
+    """Decisions bit-exact; S within 1e-5 relative; a differing draw only
+    inside the 1e-5 * S window.  Returns (exact, tolerated): sequences whose
+    outputs are identical, and sequences whose draw differs within the window
+    (callers require 0)."""
     B, kp1, V = p.shape
     k = kp1 - 1
     exact = tolerated = 0
     for b in range(B):
         mr, mg = int(ref["accept_len"][b]), int(got["accept_len"][b])
-        if mr != mg:
-            j = min(mr, mg)
-            a, _ = oracle.accept_probability(p[b, j, d[b, j]], q[b, j, d[b, j]])
-            assert abs(float(u[b, j]) - float(a)) < 1e-6, (b, j, u[b, j], a)
-            tolerated += 1
-            continue
+        assert mr == mg, (b, mr, mg)                  # same float32 division, same uniform
         assert got["emit_count"][b] == ref["emit_count"][b], b
         assert got["status"][b] == ref["status"][b], b
         e = int(ref["emit_count"][b])
@@ -148,7 +151,7 @@ def test_stochastic_workload_parity_full_size(rnd):
     got = _run(r["p"], r["q"], r["drafts"], r["uniforms"])
     ref = oracle.sample_verify(r["p"], r["q"], r["drafts"], r["uniforms"])
     exact, tol = check_within_tolerance(r["p"], r["q"], r["drafts"], r["uniforms"], got, ref)
-    assert exact + tol == r["B"]
+    assert tol == 0 and exact == r["B"]
     assert np.array_equal(got["emit_offsets"][:1], [0])
 
 
@@ -160,7 +163,7 @@ def test_grouped_workload_batches_full_size(batch):
     got = _run(r["p"], r["q"], r["drafts"], r["uniforms"])
     ref = oracle.sample_verify(r["p"], r["q"], r["drafts"], r["uniforms"])
     exact, tol = check_within_tolerance(r["p"], r["q"], r["drafts"], r["uniforms"], got, ref)
-    assert exact + tol == 8
+    assert tol == 0 and exact == 8
 
 
 def _small_case(rng, B, k, V, sharp=1.0):
@@ -183,7 +186,7 @@ def test_ragged_vocab_sizes(V):
     got = _run(p, q, d, u)
     ref = oracle.sample_verify(p, q, d, u)
     exact, tol = check_within_tolerance(p, q, d, u, got, ref)
-    assert exact + tol == 16
+    assert tol == 0 and exact == 16
 
 
 def test_misaligned_rows():
@@ -198,7 +201,7 @@ def test_misaligned_rows():
     got = _run(p, q, d, u, p_dev=fp[1:].view(B, k + 1, V), q_dev=fq[1:].view(B, k, V))
     ref = oracle.sample_verify(p, q, d, u)
     exact, tol = check_within_tolerance(p, q, d, u, got, ref)
-    assert exact + tol == B
+    assert tol == 0 and exact == B
 
 
 def test_anomalies_and_stops():
@@ -264,5 +267,5 @@ def test_largest_k():
     assert ref["accept_len"][1] == 100 and ref["emit_count"][1] == 101
     assert ref["emit_count"][3] == 120
     exact, tol = check_within_tolerance(p, q, d, u, got, ref)
-    assert exact + tol == B
+    assert tol == 0 and exact == B
     assert np.array_equal(got["emit_offsets"], ref["emit_offsets"])

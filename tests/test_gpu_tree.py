@@ -251,9 +251,10 @@ def test_tree_bench_shape():
     assert (st == 0).all()
     for (l, c, b, h), pre in zip(planes, before):
         got = iv[l, c, b, h, E:, :].cpu().numpy()
-        want = pre.copy()
-        for j in range(int(ref["emit_count"][b])):
-            want[j] = pre[int(ref["path"][b, j])]
+        # the oracle's compaction of this one plane (its columns E.. as a
+        # cache of one layer, one K/V half, one sequence and one head)
+        want = oracle.compact_tree_slots(pre[None, None, None, None], 0, ref["path"][b:b + 1],
+                                         ref["emit_count"][b:b + 1])[0, 0, 0, 0]
         assert np.array_equal(got, want), (l, c, b, h)
     del kv, iv
     torch.cuda.empty_cache()
