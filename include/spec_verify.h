@@ -276,6 +276,46 @@ int spec_commit_realign_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, 
                            int64_t *bytes_moved, int32_t *status, spec_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * Ragged caches and the unpad-append-repad fallback.
+ * [Forensics] 3.2: EXSPEC keeps sequences in ragged states and batches
+ * sequences of identical length (no realignment); when no same-length group
+ * forms it falls back to unpad-append-repad.  The ragged caches form one pool
+ * [L][2][N][H][Cs][D] in which pool sequence s holds its rows at columns
+ * [0, n_s) of each (layer, K/V, head) plane; a batch is B pool sequences
+ * index[0..B) (distinct), in a rectangle [L][2][B][H][C][D].
+ *
+ * spec_repad_kv -- copies member i's rows [0, kv_len[i]) of pool sequence
+ * index[i] to columns [E - kv_len[i], E) of rectangle sequence i, E the device
+ * scalar end_col (left padding: cells outside those ranges are not written).
+ *
+ * spec_unpad_kv -- after the verify forward wrote k+1 slots at [E, E + k + 1)
+ * of the rectangle and a verify call gave emit_count, copies member i's rows
+ * [E - kv_len[i], E + emit_count[i]) (its cached rows and the slots it keeps,
+ * as in spec_commit_realign_kv) to columns [0, kv_len[i] + emit_count[i]) of
+ * its pool sequence, and writes kv_len_out[i] = kv_len[i] + emit_count[i].
+ *
+ *   pool        [L][2][N][H][Cs][D] of dt (read by repad, written by unpad)
+ *   rect        [L][2][B][H][C][D] of dt (written by repad, read by unpad)
+ *   index       [B] int32 pool sequence of each member
+ *   kv_len      [B] int32 cached rows n_i of each member
+ *   emit_count  [B] int32 (unpad)
+ *   end_col     device scalar E (int32)
+ *   kv_len_out  [B] int32 out (unpad): n_i + e_i (n_i for a rejected member)
+ *   status      [B] out or NULL: SPEC_ST_CAPACITY if E < 0 or E > C;
+ *               SPEC_ST_BAD_STATE if index[i] is outside [0, N), n_i outside
+ *               [0, E], or (unpad) e_i < 0, E + e_i > C or n_i + e_i > Cs;
+ *               such members are not copied.
+ * Errors: SPEC_EINVAL for NULL required pointers, sizes < 1, buffers not
+ * aligned to the element size, or outputs overlapping inputs.
+ * ------------------------------------------------------------------------ */
+int spec_repad_kv(const void *pool, void *rect, spec_dtype dt, int L, int N, int H, int Cs, int D,
+                  int B, int C, const int32_t *index, const int32_t *kv_len, const int32_t *end_col,
+                  int32_t *status, spec_stream_t stream);
+int spec_unpad_kv(const void *rect, void *pool, spec_dtype dt, int L, int N, int H, int Cs, int D,
+                  int B, int C, const int32_t *index, const int32_t *kv_len, const int32_t *emit_count,
+                  const int32_t *end_col, int32_t *kv_len_out, int32_t *status, spec_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Draft-cache re-sync.
  * [Design] Standard Greedy Algorithm step 7 and "KV Cache Synchronization":
  * after each step the draft model's cache must hold the accepted prefix,

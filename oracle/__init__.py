@@ -25,7 +25,8 @@ Pins (what ties each function to something other than itself) live in
 tests/test_oracle_*.py.  Functions without such a pin say so here:
   group_same_length -- parity unpinned against the paper's own scheduler
   (its algorithm body is not on the page); pinned only by properties and
-  brute force.
+  brute force.  The EXSPEC loop (policy.py) inherits that: its grouping is
+  this reading, and its pins are the per-sequence invariants.
 """
 from .status import (  # noqa: F401
     ST_DRAFT_OOR, ST_Q_ZERO, ST_RESID_ZERO, ST_NONFINITE, ST_BAD_STATE, ST_CAPACITY,
@@ -39,4 +40,6 @@ from .realign import commit_bookkeeping, position_and_mask, commit_realign, resy
 from .group import group_same_length  # noqa: F401
 from .paged import commit_paged  # noqa: F401
 from .tree import tree_verify, compact_tree_slots  # noqa: F401
-from .unbatched import UnbatchedModel  # noqa: F401
+from .unbatched import UnbatchedModel, check_ragged  # noqa: F401
+from .ragged import repad_kv, unpad_kv, ragged_bytes  # noqa: F401
+from .policy import eqspec_round, exspec_round  # noqa: F401

@@ -75,3 +75,27 @@ class UnbatchedModel:
             if not np.array_equal(got, want):
                 bad.append(f"I2 kv b={b}")
         return bad
+
+
+def check_ragged(tokens, pool, n, content) -> list:
+    """Invariants of a ragged pool [L, 2, N, H, Cs, D] ([Forensics] 3.2: EXSPEC
+    keeps sequences ragged): sequence s holds exactly n_s = len(tokens[s]) - 1
+    rows at columns [0, n_s), each the KV of (s, position, token at that
+    position).  content(s, pos, tok, plane, d) as in UnbatchedModel.check."""
+    L, _, N, H, Cs, D = pool.shape
+    bad = []
+    plane = np.arange(L * 2 * H, dtype=np.int64).reshape(L, 2, H)
+    for s in range(N):
+        ns = len(tokens[s]) - 1
+        if int(n[s]) != ns:
+            bad.append(f"length s={s}")
+            continue
+        if ns == 0:
+            continue
+        p = np.arange(ns, dtype=np.int64)
+        tok = np.array(tokens[s][:ns], np.int64)
+        want = content(s, p[None, None, None, :, None], tok[None, None, None, :, None],
+                       plane[:, :, :, None, None], np.arange(D)[None, None, None, None, :])
+        if not np.array_equal(pool[:, :, s, :, 0:ns, :], want):
+            bad.append(f"I2 pool s={s}")
+    return bad

@@ -24,7 +24,7 @@ __all__ = [
     "spec_verify_greedy_noalloc", "SPEC_GREEDY_SCRATCH_BYTES",
     "spec_verify_sample_workspace_bytes", "spec_verify_sample", "spec_process_workspace_bytes",
     "spec_process_logits", "spec_verify_sample_logits_workspace_bytes", "spec_verify_sample_logits",
-    "spec_commit_realign_kv", "spec_resync_draft_kv", "spec_commit_paged",
+    "spec_commit_realign_kv", "spec_resync_draft_kv", "spec_repad_kv", "spec_unpad_kv", "spec_commit_paged",
     "spec_verify_tree_workspace_bytes", "spec_verify_tree", "spec_compact_tree_kv",
     "spec_group_same_length", "workspace", "library",
 ]
@@ -236,6 +236,37 @@ def spec_resync_draft_kv(kv, k: int, end_col, kv_len_in, emit_count, end_col_out
         _arg(bytes_moved, "int64", 1, "bytes_moved", True), _arg(status, "int32", B, "status", True),
         _stream(stream))
     _check(code, "spec_resync_draft_kv")
+
+
+def _ragged_shapes(pool, rect):
+    L, two, N, H, Cs, D = pool.shape
+    L2, two2, B, H2, C, D2 = rect.shape
+    if two != 2 or two2 != 2 or (L, H, D) != (L2, H2, D2) or pool.dtype != rect.dtype:
+        raise ValueError(f"pool {tuple(pool.shape)} and rectangle {tuple(rect.shape)} do not match")
+    return L, N, H, Cs, D, B, C
+
+
+def spec_repad_kv(pool, rect, index, kv_len, end_col, *, status=None, stream=None) -> None:
+    """pool [L, 2, N, H, Cs, D] (ragged rows at columns 0..n-1), rect
+    [L, 2, B, H, C, D]; index, kv_len [B] int32; end_col device int32 [1]."""
+    L, N, H, Cs, D, B, C = _ragged_shapes(pool, rect)
+    code = library().spec_repad_kv(
+        _ptr(pool), _ptr(rect), _dtype_code(pool), L, N, H, Cs, D, B, C, _arg(index, "int32", B, "index"),
+        _arg(kv_len, "int32", B, "kv_len"), _arg(end_col, "int32", 1, "end_col"),
+        _arg(status, "int32", B, "status", True), _stream(stream))
+    _check(code, "spec_repad_kv")
+
+
+def spec_unpad_kv(rect, pool, index, kv_len, emit_count, end_col, kv_len_out, *, status=None,
+                  stream=None) -> None:
+    """Copies each member's rows [E - n, E + e) of rect back to pool columns [0, n + e)."""
+    L, N, H, Cs, D, B, C = _ragged_shapes(pool, rect)
+    code = library().spec_unpad_kv(
+        _ptr(rect), _ptr(pool), _dtype_code(pool), L, N, H, Cs, D, B, C, _arg(index, "int32", B, "index"),
+        _arg(kv_len, "int32", B, "kv_len"), _arg(emit_count, "int32", B, "emit_count"),
+        _arg(end_col, "int32", 1, "end_col"), _arg(kv_len_out, "int32", B, "kv_len_out"),
+        _arg(status, "int32", B, "status", True), _stream(stream))
+    _check(code, "spec_unpad_kv")
 
 
 def spec_commit_paged(k: int, page_size: int, kv_len_in, emit_count, block_table, kv_len_out,

@@ -28,6 +28,8 @@ PROTOTYPES = {
                                        _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "spec_commit_realign_kv": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _P]),
+    "spec_repad_kv": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "spec_unpad_kv": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "spec_resync_draft_kv": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                   _P, _P, _P]),
     "spec_commit_paged": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),

@@ -27,6 +27,8 @@ from .configs import (  # noqa: F401
     kv_geometry,
     prefix_tokens,
     pool_lengths,
+    policy_pool,
+    policy_round,
 )
 from .kvfill import (  # noqa: F401
     kv_bits_np,
@@ -35,5 +37,7 @@ from .kvfill import (  # noqa: F401
     fill_kv_torch,
     write_forward_slots_np,
     write_forward_slots_torch,
+    write_rows_np,
+    write_rows_torch,
     KV_PAD_POS,
 )

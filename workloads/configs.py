@@ -43,6 +43,7 @@ WORKLOADS = [
 _STREAM_IDS = {
     "lengths": 1, "alpha": 2, "logits": 3, "drafts": 4, "uniforms": 5,
     "kv": 6, "tokens": 7, "eps": 8, "pool": 9, "accept": 10,
+    "policy_logits": 11, "policy_drafts": 12,
 }
 
 
@@ -287,3 +288,37 @@ def pool_lengths(c: int = 4) -> np.ndarray:
         lead = np.argmin(np.concatenate([trials, np.zeros((P.size, 1), bool)], axis=1), axis=1)
         P = P + lead + 1
     return P.astype(np.int64)
+
+
+def policy_pool(kind: str = "drifted") -> dict:
+    """Pool of the multi-round scheduling comparison (the grouped workload's
+    256 sequences, their acceptance rates, k = 4 drafts, batches of 8).
+
+    drifted: the grouped workload's pool after its warm-up rounds (lengths
+             spread over about 2000 values);
+    four:    the same sequences with lengths drawn from four values, a
+             homogeneous workload.
+    P holds confirmed-token counts; the caches hold P - 1 rows."""
+    cfg = WORKLOADS[4]
+    P = pool_lengths(4)
+    if kind == "four":
+        P = stream(4, "pool", 99).choice(np.array([512, 513, 900, 1500]), size=P.size)
+    elif kind != "drifted":
+        raise ValueError(kind)
+    return dict(P=P.astype(np.int64), alpha=alphas(4), k=cfg["k"], B=cfg["B"], min_group=cfg["min_group"],
+                N=int(P.size))
+
+
+def policy_round(r: int, N: int, k: int, V: int, dtype: str, sd: float, alpha) -> dict:
+    """Greedy verification inputs of every pool sequence for round r: sequence
+    s gets logits [k+1, V] ~ N(0, sd) and drafts planted with alpha[s] from
+    its own streams, so the inputs do not depend on how sequences are
+    batched."""
+    logits = np.empty((N, k + 1, V), np.uint16 if dtype == "bf16" else np.float32)
+    drafts = np.empty((N, k), np.int32)
+    for s in range(N):
+        g = planted_greedy(stream(4, "policy_logits", r, s), stream(4, "policy_drafts", r, s), 1, k, V, sd,
+                           dtype, np.asarray(alpha)[s:s + 1])
+        logits[s] = g["logits"][0]
+        drafts[s] = g["drafts"][0]
+    return dict(logits=logits, drafts=drafts, dtype=dtype)

@@ -73,21 +73,25 @@ def _np_dtype(dtype: str):
     return np.uint16 if dtype == "bf16" else np.uint32
 
 
-def fill_kv_np(L, H, D, B, C, E, n, tokens, dtype: str) -> np.ndarray:
+def fill_kv_np(L, H, D, B, C, E, n, tokens, dtype: str, seq=None) -> np.ndarray:
     """Rectangle with sequence b's cached rows 0..n_b-1 at columns [E-n_b, E).
 
-    tokens[b, pos] is the confirmed token at position pos.  Returns element bits
-    (uint16 for bf16, uint32 for f32) of shape [L, 2, B, H, C, D].
+    tokens[b, pos] is the confirmed token at position pos.  E may be one end
+    column or one per sequence (E = n gives ragged rows at columns 0..n_b-1).
+    seq[b] (default b) is the sequence identity the contents are keyed by.
+    Returns element bits (uint16 for bf16, uint32 for f32) of shape
+    [L, 2, B, H, C, D].
     """
     n = np.asarray(n, dtype=np.int64)
+    Eb = np.broadcast_to(np.asarray(E, dtype=np.int64), n.shape)
     col = np.arange(C, dtype=np.int64)[None, :]
-    pos = col - (E - n[:, None])                       # [B, C]
+    pos = col - (Eb[:, None] - n[:, None])             # [B, C]
     valid = (pos >= 0) & (pos < n[:, None])
     tok = np.where(valid, np.take_along_axis(tokens, np.clip(pos, 0, tokens.shape[1] - 1), 1), 0)
     pos = np.where(valid, pos, KV_PAD_POS + col)
     out = np.empty((L, 2, B, H, C, D), dtype=_np_dtype(dtype))
     d = np.arange(D, dtype=np.int64)
-    bidx = np.arange(B, dtype=np.int64)[:, None, None]
+    bidx = (np.arange(B, dtype=np.int64) if seq is None else np.asarray(seq, np.int64))[:, None, None]
     for l in range(L):
         for kv in range(2):
             plane = ((l * 2 + kv) * H + np.arange(H, dtype=np.int64))[None, :, None]
@@ -157,24 +161,27 @@ def _int_view(kv):
     return kv.view(torch.int16) if kv.element_size() == 2 else kv.view(torch.int32)
 
 
-def fill_kv_torch(kv, E: int, n, tokens, dtype: str) -> None:
+def fill_kv_torch(kv, E, n, tokens, dtype: str, seq=None) -> None:
     """Device version of fill_kv_np, writing into kv [L, 2, B, H, C, D] in place.
 
-    tokens: int64 tensor [B, T] on kv's device.
+    tokens: int64 tensor [B, T] on kv's device; E and seq as in fill_kv_np.
     """
     import torch
     L, _, B, H, C, D = kv.shape
     dev = kv.device
-    n_t = torch.as_tensor(np.asarray(n, dtype=np.int64), device=dev)
+    n_np = np.asarray(n, dtype=np.int64)
+    n_t = torch.as_tensor(n_np, device=dev)
+    E_t = torch.as_tensor(np.broadcast_to(np.asarray(E, dtype=np.int64), n_np.shape).copy(), device=dev)
     col = torch.arange(C, device=dev, dtype=torch.int64)[None, :]
-    pos = col - (E - n_t[:, None])
+    pos = col - (E_t[:, None] - n_t[:, None])
     valid = (pos >= 0) & (pos < n_t[:, None])
     tok = torch.where(valid, torch.gather(tokens, 1, pos.clamp(0, tokens.shape[1] - 1)),
                       torch.zeros_like(pos))
     pos = torch.where(valid, pos, KV_PAD_POS + col)
     d = torch.arange(D, device=dev, dtype=torch.int64)
     dterm = _mul32_t(d, _K_D)
-    bidx = torch.arange(B, device=dev, dtype=torch.int64)[:, None, None]
+    bidx = (torch.arange(B, device=dev, dtype=torch.int64) if seq is None
+            else torch.as_tensor(np.asarray(seq, np.int64), device=dev))[:, None, None]
     iv = _int_view(kv)
     for l in range(L):
         for kvi in range(2):
@@ -201,3 +208,40 @@ def write_forward_slots_torch(kv, E: int, n, slot_tokens, dtype: str) -> None:
             plane = ((l * 2 + kvi) * H + torch.arange(H, device=dev, dtype=torch.int64))[None, :, None]
             key = _row_key_t(bidx, pos[:, None, :], slot_tokens[:, None, :], plane)
             iv[l, kvi, :, :, E:E + kp1, :].copy_(_finish_t(key[..., None] ^ dterm, dtype))
+
+
+# ------------------------------------------------------- chosen rows ----
+def write_rows_np(kv: np.ndarray, rows, seq, col0, pos0, tokens, dtype: str) -> None:
+    """For each i: the KV of sequence seq[i] at positions pos0[i] + t for the
+    tokens tokens[i, t] (t < T), written into row rows[i] of kv [L, 2, R, H,
+    C, D] at columns col0[i] + t.  Used for verify-forward slots of chosen
+    sequences of a pool or a rectangle."""
+    L, _, R, H, C, D = kv.shape
+    tokens = np.asarray(tokens, np.int64)
+    T = tokens.shape[1]
+    d = np.arange(D, dtype=np.int64)
+    plane = np.arange(L * 2 * H, dtype=np.int64).reshape(L, 2, H)[:, :, :, None, None]
+    for i in range(len(rows)):
+        pos = (int(pos0[i]) + np.arange(T, dtype=np.int64))[None, None, None, :, None]
+        key = _row_key_np(int(seq[i]), pos, tokens[i][None, None, None, :, None], plane)
+        c0 = int(col0[i])
+        kv[:, :, int(rows[i]), :, c0:c0 + T, :] = _finish_np(key ^ (_u32(d) * np.uint32(_K_D)), dtype)
+
+
+def write_rows_torch(kv, rows, seq, col0, pos0, tokens, dtype: str) -> None:
+    """Device version of write_rows_np (tokens: int64 array [R', T])."""
+    import torch
+    L, _, R, H, C, D = kv.shape
+    dev = kv.device
+    tokens = np.asarray(tokens, np.int64)
+    T = tokens.shape[1]
+    dterm = _mul32_t(torch.arange(D, device=dev, dtype=torch.int64), _K_D)
+    plane = torch.arange(L * 2 * H, device=dev, dtype=torch.int64).reshape(L, 2, H)[:, :, :, None, None]
+    iv = _int_view(kv)
+    tok_t = torch.as_tensor(tokens, device=dev)
+    for i in range(len(rows)):
+        pos = (int(pos0[i]) + torch.arange(T, device=dev, dtype=torch.int64))[None, None, None, :, None]
+        key = _row_key_t(torch.full((1,), int(seq[i]), device=dev, dtype=torch.int64), pos,
+                         tok_t[i][None, None, None, :, None], plane)
+        c0 = int(col0[i])
+        iv[:, :, int(rows[i]), :, c0:c0 + T, :].copy_(_finish_t(key ^ dterm, dtype))
