@@ -263,6 +263,16 @@ def main() -> int:
         secondary = secondary_measurements(dev, np, torch, sv, W)
         log("batch scaling: realign cost and grouping rate against batch size")
         secondary.update(batch_scaling(dev, np, torch, sv, W))
+        cpu_side = not args.no_cpu_baseline
+        for c in (0, 1, 2):
+            log(f"workload {c}: verify + commit step")
+            secondary[f"workload_{c}_step"] = config_step(dev, np, torch, sv, W, c, cpu=cpu_side)
+        log("workload 4: grouping, per-batch verify, realign-based commit")
+        secondary["workload_4_grouped"] = grouped_workload(dev, np, torch, sv, W, cpu=cpu_side)
+        log("draft-cache re-sync")
+        secondary["draft_resync"] = draft_resync(dev, np, torch, sv, W)
+        log("EQSPEC vs EXSPEC loop")
+        secondary["policy_loop"] = policy_loop(dev, np, torch, sv, W)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -530,6 +540,318 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
     out["group_same_length"] = {"workload": f"same-length grouping, pool {N}, batch {cfg['B']}, min_group {cfg['min_group']}",
                                 "us_per_call": t * 1e6, "us_per_call_host": th * 1e6, "num_batches": int(nb.item()),
                                 "grouped_fraction": int(ng.item()) / N}
+    return out
+
+
+def _dev_logits(torch, dev, np, arr, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
+
+
+def _back_to_back(torch, fn, n: int) -> float:
+    """Seconds per launch of n back-to-back calls between two HIP events."""
+    fn(0)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / n
+
+
+def config_step(dev, np, torch, sv, W, c: int, steps: int = 12, warm: int = 3, nbuf: int = 4,
+                cpu: bool = True) -> dict:
+    """One workload's whole step (verify + commit, chained on the device over
+    `steps` rounds) and its parts; the oracle's step on the host beside it."""
+    import oracle
+    cfg = W.workload(c)
+    R = warm + steps
+    g = W.kv_geometry(c, rounds=R)
+    L, H, D, B, k, n, E, C = (g[x] for x in ("L", "H", "D", "B", "k", "n", "E", "C"))
+    V = cfg["V"]
+    mode = cfg["mode"]
+    i32 = dict(dtype=torch.int32, device=dev)
+    kvdt = g["dtype"]
+    kv = torch.empty((L, 2, B, H, C, D), dtype=torch.bfloat16 if kvdt == "bf16" else torch.float32, device=dev)
+    W.fill_kv_torch(kv, E, n, torch.as_tensor(W.prefix_tokens(c, B, E + 1), device=dev), kvdt)
+    acc, emit, toks = torch.empty(B, **i32), torch.empty(B, **i32), torch.empty(B, k + 1, **i32)
+    offs = torch.empty(B + 1, **i32)
+    if mode == "greedy":
+        rounds = [W.greedy_round(c, round_=r) for r in range(nbuf)]
+        ins = [(_dev_logits(torch, dev, np, r["logits"], r["dtype"]), torch.as_tensor(r["drafts"]).to(dev))
+               for r in rounds]
+        ws = sv.workspace(sv.spec_verify_greedy_workspace_bytes(B, k, V, sv.SPEC_BF16 if cfg["logit_dtype"] == "bf16"
+                                                                else sv.SPEC_F32), dev)
+
+        def verify(i):
+            z, d = ins[i % nbuf]
+            sv.spec_verify_greedy(z, d, acc, emit, toks, ws, emit_offsets=offs)
+        elt = 2 if cfg["logit_dtype"] == "bf16" else 4
+        ver_bytes = B * (k + 1) * V * elt + B * k * 4 + B * (k + 1) * 4 + (3 * B + 1) * 4
+    else:
+        rounds = [W.sample_round(c, round_=r) for r in range(nbuf)]
+        ins = [tuple(torch.from_numpy(r[x]).to(dev) for x in ("p", "q", "drafts", "uniforms")) for r in rounds]
+        mass = torch.empty(B, dtype=torch.float64, device=dev)
+        ws = sv.workspace(sv.spec_verify_sample_workspace_bytes(B, k, V), dev)
+
+        def verify(i):
+            p_, q_, d, u = ins[i % nbuf]
+            sv.spec_verify_sample(p_, q_, d, u, acc, emit, toks, ws, emit_offsets=offs, final_mass=mass)
+        ver_bytes = None                        # realized per call (rows drawn from), below
+    Eb = [torch.tensor([E], **i32), torch.empty(1, **i32)]
+    Nb = [torch.as_tensor(n, **i32), torch.empty(B, **i32)]
+    pos, mask = torch.empty(B, C, **i32), torch.empty(B, C, **i32)
+    moved = torch.zeros(R, dtype=torch.int64, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(R)]
+
+    def step(r):
+        evs[r][0].record()
+        verify(r)
+        evs[r][1].record()
+        sv.spec_commit_realign_kv(kv, k, Eb[r % 2], Nb[r % 2], emit, Eb[(r + 1) % 2], Nb[(r + 1) % 2], pos, mask,
+                                  bytes_moved=moved[r:r + 1])
+        evs[r][2].record()
+
+    for r in range(warm):
+        step(r)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(warm, R):
+        step(r)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_rea = [evs[r][1].elapsed_time(evs[r][2]) * 1e-3 for r in range(warm, R)]
+    rea_bytes = [int(moved[r].item()) + 8 * B * C for r in range(warm, R)]
+    t_launch = _back_to_back(torch, verify, 6 * nbuf)
+    if ver_bytes is None:                       # stochastic: one verify of each buffer, realized bytes
+        vb = []
+        for i in range(nbuf):
+            verify(i)
+            m_, e_ = acc.cpu().numpy(), emit.cpu().numpy()
+            rowb = sum(8 * V if (e_[b] > m_[b] and m_[b] < k) else (4 * V if e_[b] > m_[b] else 0) for b in range(B))
+            vb.append(rowb + 8 * int(sum(min(int(m_[b]) + 1, k) for b in range(B))) + 4 * B * (k + 1) * 2)
+        ver_bytes = sum(vb) / nbuf
+    rows = B * (k + 1)
+    out = {"workload": f"{cfg['name']}: B={B} k={k} V={V} {cfg.get('logit_dtype', 'f32 p/q')}, KV {L}x{H}x{D} {kvdt}, "
+                       f"{nbuf} rotating inputs",
+           "rows_per_s": rows * steps / wall, "ms_per_step": wall / steps * 1e3,
+           "verify_us_per_launch": t_launch * 1e6, "verify_algorithmic_bytes": ver_bytes,
+           "verify_GBps": ver_bytes / t_launch / 1e9, "verify_frac_of_peak": ver_bytes / t_launch / PEAK_HBM,
+           "realign_ms_per_call": statistics.mean(t_rea) * 1e3,
+           "realign_GBps": sum(rea_bytes) / sum(t_rea) / 1e9,
+           "realign_frac_of_peak": sum(rea_bytes) / sum(t_rea) / PEAK_HBM,
+           "realign_bytes_per_call": sum(rea_bytes) / len(rea_bytes)}
+    # parity guard (outside the timed region): round 0 against the oracle
+    verify(0)
+    torch.cuda.synchronize()
+    r0 = rounds[0]
+    if mode == "greedy":
+        ref = oracle.greedy_verify(r0["logits"], r0["dtype"], r0["drafts"])
+    else:
+        ref = oracle.sample_verify(r0["p"], r0["q"], r0["drafts"], r0["uniforms"])
+    out["parity_checked"] = bool(np.array_equal(emit.cpu().numpy(), ref["emit_count"]) and
+                                 np.array_equal(toks.cpu().numpy(), ref["out_tokens"]))
+    del kv
+    torch.cuda.empty_cache()
+    if cpu:
+        out["cpu_baseline"] = _cpu_step(np, oracle, W, c, r0, ref, g)
+    return out
+
+
+def _cpu_step(np, oracle, W, c, r0, ref, g) -> dict:
+    """The oracle's verify + commit of one round on the host (median of 3),
+    on the workload's full KV (random contents: the oracle's cost does not
+    depend on them); at most 4 layers are copied, scaled to all."""
+    L, H, D, B, k, n, E, C = (g[x] for x in ("L", "H", "D", "B", "k", "n", "E", "C"))
+    tv = []
+    for _ in range(3):
+        t = time.perf_counter()
+        if "p" in r0:
+            oracle.sample_verify(r0["p"], r0["q"], r0["drafts"], r0["uniforms"])
+        else:
+            oracle.greedy_verify(r0["logits"], r0["dtype"], r0["drafts"])
+        tv.append(time.perf_counter() - t)
+    layers = min(L, 4)
+    u = np.uint16 if g["dtype"] == "bf16" else np.uint32
+    kv = np.random.default_rng(0).integers(0, 1 << 16, size=(layers, 2, B, H, C, D), dtype=u)
+    tr = []
+    for _ in range(3):
+        t = time.perf_counter()
+        oracle.commit_realign(kv, E, n, ref["emit_count"], k)
+        tr.append(time.perf_counter() - t)
+    step = statistics.median(tv) + statistics.median(tr) * L / layers
+    return {"value": B * (k + 1) / step, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"verify of one round's {B * (k + 1)} rows + realign of {layers} of {L} layers scaled to "
+                      f"{L}; median of 3; single-threaded numpy"}
+
+
+def grouped_workload(dev, np, torch, sv, W, batches: int = 4, cpu: bool = True) -> dict:
+    """The grouped workload: same-length grouping of the 256-sequence pool,
+    then, per batch, stochastic verification (k=4, V=256000, p/q as the
+    stochastic workload's) and the realign-based commit of the batch's
+    left-padded rectangle (28 layers x 4 KV heads x 128 bf16), each timed on
+    its own."""
+    import oracle
+    cfg = W.workload(4)
+    Bm, k, V, mg = cfg["B"], cfg["k"], cfg["V"], cfg["min_group"]
+    L, H, D = cfg["L"], cfg["H"], cfg["D"]
+    P = W.pool_lengths()
+    N = P.size
+    i32 = dict(dtype=torch.int32, device=dev)
+    lens = torch.as_tensor(P, **i32)
+    perm, bs, bl = torch.empty(N, **i32), torch.empty(N + 1, **i32), torch.empty(N, **i32)
+    nb, ng = torch.empty(1, **i32), torch.empty(1, **i32)
+    t_g, th_g = _time_calls(torch, lambda: sv.spec_group_same_length(lens, Bm, mg, perm, bs, bl, nb, ng), 52)
+    perm_h, bs_h, bl_h = perm.cpu().numpy(), bs.cpu().numpy(), bl.cpu().numpy()
+    nbat = int(nb.item())
+    # batches to time: mixed ones (the realign has something to move), at most `batches`
+    chosen = [b for b in range(nbat) if bl_h[b] < 0 and bs_h[b + 1] - bs_h[b] == Bm][:batches]
+    acc, emit, toks = torch.empty(Bm, **i32), torch.empty(Bm, **i32), torch.empty(Bm, k + 1, **i32)
+    offs, mass = torch.empty(Bm + 1, **i32), torch.empty(Bm, dtype=torch.float64, device=dev)
+    ws = sv.workspace(sv.spec_verify_sample_workspace_bytes(Bm, k, V), dev)
+    vt, vbytes, rt, rbytes, cpu_t = [], [], [], [], []
+    for j, b in enumerate(chosen):
+        r = W.sample_round(4, batch=j, B=Bm)
+        ins = [torch.from_numpy(r[x]).to(dev) for x in ("p", "q", "drafts", "uniforms")]
+        copies = [ins[:2]] + [[ins[0].clone(), ins[1].clone()] for _ in range(2)]     # 3 x 74 MB, rotated
+        it = itertools.count()
+
+        def call():
+            p_, q_ = copies[next(it) % len(copies)]
+            sv.spec_verify_sample(p_, q_, ins[2], ins[3], acc, emit, toks, ws, emit_offsets=offs, final_mass=mass)
+        t, _ = _time_calls(torch, call, 12, inner=6)
+        m_, e_ = acc.cpu().numpy(), emit.cpu().numpy()
+        rowb = sum(8 * V if (e_[q] > m_[q] and m_[q] < k) else (4 * V if e_[q] > m_[q] else 0) for q in range(Bm))
+        vt.append(t)
+        vbytes.append(rowb + 8 * int(sum(min(int(m_[q]) + 1, k) for q in range(Bm))) + 4 * Bm * (k + 1) * 2)
+        # the batch's rectangle: its members' cached rows, right-aligned at the longest
+        n = (P[perm_h[bs_h[b]:bs_h[b + 1]]] - 1).astype(np.int64)
+        E = int(n.max())
+        C = E + (k + 1) * 2
+        kv = torch.empty((L, 2, Bm, H, C, D), dtype=torch.bfloat16, device=dev)
+        W.fill_kv_torch(kv, E, n, torch.as_tensor(W.prefix_tokens(4, Bm, E + 1), device=dev), "bf16")
+        Eb, Eo = torch.tensor([E], **i32), torch.empty(1, **i32)
+        Nb, No = torch.as_tensor(n, **i32), torch.empty(Bm, **i32)
+        pos, mask = torch.empty(Bm, C, **i32), torch.empty(Bm, C, **i32)
+        mv = torch.zeros(1, dtype=torch.int64, device=dev)
+        # the same in-place move repeated: every call moves the same ranges
+        call = lambda: sv.spec_commit_realign_kv(kv, k, Eb, Nb, emit, Eo, No, pos, mask, bytes_moved=mv)
+        t, _ = _time_calls(torch, call, 8, inner=4)
+        rt.append(t)
+        rbytes.append(int(mv.item()) + 8 * Bm * C)
+        if cpu and j == 0:
+            ref = oracle.sample_verify(r["p"], r["q"], r["drafts"], r["uniforms"])
+            g4 = dict(L=L, H=H, D=D, B=Bm, k=k, n=n, E=E, C=C, dtype="bf16")
+            t0 = time.perf_counter()
+            oracle.group_same_length(P, Bm, mg)
+            tg_cpu = time.perf_counter() - t0
+            cpu_t.append((tg_cpu, _cpu_step(np, oracle, W, 4, r, ref, g4)))
+        del kv, copies, ins
+        torch.cuda.empty_cache()
+    out = {"workload": f"{cfg['name']}: pool {N}, batches of {Bm}, min_group {mg}; stochastic verify k={k} V={V} f32 "
+                       f"p/q; realign of a mixed batch's rectangle, KV {L}x{H}x{D} bf16",
+           "grouping_us": t_g * 1e6, "grouping_us_host": th_g * 1e6, "num_batches": nbat,
+           "grouped_fraction": int(ng.item()) / N, "batches_timed": len(chosen),
+           "verify_us_per_batch": statistics.mean(vt) * 1e6,
+           "verify_GBps": sum(vbytes) / sum(vt) / 1e9, "verify_frac_of_peak": sum(vbytes) / sum(vt) / PEAK_HBM,
+           "commit_ms_per_batch": statistics.mean(rt) * 1e3,
+           "commit_GBps": sum(rbytes) / sum(rt) / 1e9, "commit_frac_of_peak": sum(rbytes) / sum(rt) / PEAK_HBM}
+    if cpu_t:
+        tg_cpu, cb = cpu_t[0]
+        out["cpu_baseline"] = dict(cb, grouping_us=tg_cpu * 1e6)
+    return out
+
+
+def draft_resync(dev, np, torch, sv, W) -> dict:
+    """spec_resync_draft_kv at a small draft model's cache geometry (24 layers,
+    2 KV heads, head_dim 64, bf16), 64-token prefixes, k = 4."""
+    i32 = dict(dtype=torch.int32, device=dev)
+    L, H, D, k, P = 24, 2, 64, 4, 64
+    out = {"workload": f"draft-cache re-sync, KV {L}x{H}x{D} bf16, {P}-token prefixes, k={k} (the draft wrote k slots)"}
+    for B in (1, 8):
+        n = np.full(B, P - 1, np.int64)
+        E = P - 1
+        C = E + k + 1
+        kv = torch.empty((L, 2, B, H, C, D), dtype=torch.bfloat16, device=dev)
+        W.fill_kv_torch(kv, E, n, torch.as_tensor(W.prefix_tokens(4, B, E + 1), device=dev), "bf16")
+        e = torch.as_tensor(np.arange(B) % (k + 1) + 1, **i32)          # emitted counts 1 .. k+1
+        Eb, Eo = torch.tensor([E], **i32), torch.empty(1, **i32)
+        Nb, No = torch.as_tensor(n, **i32), torch.empty(B, **i32)
+        pos, mask = torch.empty(B, C, **i32), torch.empty(B, C, **i32)
+        mv = torch.zeros(1, dtype=torch.int64, device=dev)
+        call = lambda: sv.spec_resync_draft_kv(kv, k, Eb, Nb, e, Eo, No, pos_ids=pos, mask=mask, bytes_moved=mv)
+        t, th = _time_calls(torch, call, 22)
+        out[f"B{B}"] = {"us_per_call": t * 1e6, "us_per_call_host": th * 1e6, "bytes_moved": int(mv.item())}
+        del kv
+    return out
+
+
+def policy_loop(dev, np, torch, sv, W, rounds: int = 8) -> dict:
+    """EQSPEC against EXSPEC over several rounds on the grouped workload's pool
+    at its full KV geometry (28 layers x 4 KV heads x 128 bf16), greedy
+    verification of planted drafts (V = 256000 bf16 logits made on the
+    device each round), on the drifted pool and on a four-length pool.  Per
+    policy: verification calls, KV bytes moved, GPU time of grouping,
+    verification and commit, and GPU time per emitted token (the simulated
+    forward's slot writes are not timed)."""
+    from speculative_decoding_verification_04_amd.scheduler import EqspecPool, ExspecPool
+    cfg = W.workload(4)
+    L, H, D, V, k, B, mg = cfg["L"], cfg["H"], cfg["D"], cfg["V"], cfg["k"], cfg["B"], cfg["min_group"]
+    fw = lambda kv, rows, seq, c0, p0, tk: W.write_rows_torch(kv, rows, seq, c0, p0, tk, "bf16")
+    out = {"workload": f"pool 256, batches of {B}, k={k}, {rounds} rounds, greedy verify V={V} bf16, "
+                       f"KV {L}x{H}x{D} bf16; EQSPEC: fixed rectangles realigned every round; EXSPEC: ragged "
+                       f"caches regrouped every round, same-length batches by a length update, mixed batches "
+                       f"by repad / unpad"}
+    for kind in ("drifted", "four"):
+        pp = W.policy_pool(kind)
+        N, P = pp["N"], pp["P"]
+        rng = np.random.default_rng(7)
+        tokens = [list(rng.integers(0, V, size=int(x))) for x in P]
+        T = np.zeros((N, int(P.max()) + 1), np.int64)
+        for s in range(N):
+            T[s, :len(tokens[s])] = tokens[s]
+        T_d = torch.as_tensor(T).to(dev)
+        Cs = int((P - 1).max()) + (k + 1) * (rounds + 1)
+        gen = torch.Generator(device=dev).manual_seed(11)
+        alpha = torch.as_tensor(pp["alpha"], device=dev, dtype=torch.float32)
+        res = {}
+        for name in ("eqspec", "exspec"):
+            if name == "eqspec":
+                pol = EqspecPool(torch, tokens, L, H, D, "bf16", k, B, Cs, V, dev,
+                                 lambda kv, E, nn, seq: W.fill_kv_torch(kv, E, nn, T_d[torch.as_tensor(seq).to(dev)],
+                                                                        "bf16", seq=seq))
+            else:
+                pol = ExspecPool(torch, tokens, L, H, D, "bf16", k, B, mg, Cs, V, dev,
+                                 lambda pool, nn: W.fill_kv_torch(pool, nn, nn, T_d, "bf16"))
+            gen.manual_seed(11)
+            tot = dict(verify_calls=0, bytes_moved=0, emitted=0, mixed_batches=0, grouped=0)
+            times = {}
+            for r in range(rounds):
+                z = (torch.randn((N, k + 1, V), device=dev, generator=gen) * 2).to(torch.bfloat16)
+                am = z[:, :k].float().argmax(-1).to(torch.int32)
+                other = torch.randint(0, V, (N, k), device=dev, generator=gen, dtype=torch.int32)
+                keep = torch.rand((N, k), device=dev, generator=gen) < alpha[:, None]
+                dr = torch.where(keep, am, torch.where(other == am, (other + 1) % V, other)).contiguous()
+                st = pol.round(z, dr, dr.cpu().numpy(), fw)
+                tot["verify_calls"] += st["verify_calls"]
+                tot["bytes_moved"] += st["bytes_moved"]
+                tot["emitted"] += int(st["emit_count"].sum())
+                tot["mixed_batches"] += st.get("mixed_batches", 0)
+                tot["grouped"] += st.get("num_grouped", 0)
+                for kk, v in st["times"].items():
+                    times[kk] = times.get(kk, 0.0) + v
+                del z
+            gpu = sum(times.values())
+            res[name] = dict(tot, **{f"{kk}_ms": v * 1e3 for kk, v in times.items()},
+                             gpu_ms=gpu * 1e3, gpu_ms_per_emitted_token=gpu * 1e3 / tot["emitted"],
+                             commit_GBps=tot["bytes_moved"] / times.get("commit", 1e-30) / 1e9)
+            del pol
+            torch.cuda.empty_cache()
+        res["grouping_rate"] = res["exspec"]["grouped"] / (N * rounds)
+        out[kind] = res
     return out
 
 
