@@ -43,7 +43,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kTileVec = 4;              // 16-byte vectors per lane per tile (64 KB tiles)
+constexpr int kTileVec = 7;              // 16-byte vectors per lane per tile (112 KB tiles)
 constexpr int kReserveWords = 24 * 1024; // 96 KB of the CU's 160 KB LDS: one workgroup per CU
 
 struct RealignParams {
@@ -135,14 +135,27 @@ __device__ inline void commit_state(const RealignParams &P, int *sh, int &E, int
   M = mm;
 }
 
+// Address of vector i of a plane.  With 32-bit indices (planes under 2 GiB)
+// the byte offset is a 32-bit lane value added to the plane's base, which
+// sits in scalar registers: one VGPR per address instead of two, which leaves
+// room for wider tiles.
+template <typename VT, typename IT>
+__device__ inline VT *cell(unsigned char *pb, IT i) {
+  if constexpr (sizeof(IT) == 4)
+    return reinterpret_cast<VT *>(pb + static_cast<uint32_t>(i) * static_cast<uint32_t>(sizeof(VT)));
+  else
+    return reinterpret_cast<VT *>(pb + static_cast<size_t>(i) * sizeof(VT));
+}
+
 // One plane: the moved range [E - n, E + e) shifted right by M - e columns,
 // walked from right to left in tiles.  The plane's own sequence is read first
 // and, when it can move, the first tile's loads are issued before the
 // batch-wide state (M, validity) is reduced: the source range does not depend
 // on M.  Loads are checked against this sequence's own values, so they stay in
 // bounds whatever the rest of the batch holds; nothing is stored unless the
-// whole batch is valid.
-template <int VB>
+// whole batch is valid.  IT indexes vectors within the plane: int when the
+// plane is under 2 GiB, long long otherwise.
+template <int VB, typename IT>
 __device__ inline void move_plane(const RealignParams &P, int p, int b, int *sh) {
   using VT = typename VecOf<VB>::T;
   const int E0 = P.end_col[0];
@@ -151,53 +164,56 @@ __device__ inline void move_plane(const RealignParams &P, int p, int b, int *sh)
   // e == slots: this sequence kept the most any can, so it does not move
   const bool may_move = E0 >= 0 && E0 <= P.C - P.slots && n >= 0 && n <= E0 && e_in >= 0 &&
                         e_in <= P.k + 1 && e < P.slots && n + e > 0;
-  const long long per_col = P.R / VB;                       // vectors per column
-  VT *base = reinterpret_cast<VT *>(P.kv + static_cast<size_t>(p) * P.plane_bytes);
-  const long long lo = static_cast<long long>(E0 - n) * per_col;   // first source vector
+  const IT per_col = P.R / VB;                              // vectors per column
+  unsigned char *pb = P.kv + static_cast<size_t>(p) * P.plane_bytes;
+  const IT lo = static_cast<IT>(E0 - n) * per_col;          // first source vector
   constexpr int TV = kThreads * kTileVec;                    // vectors per tile
   const int t = threadIdx.x;
-  long long hi = lo + static_cast<long long>(n + e) * per_col; // one past the last source vector
+  IT hi = lo + static_cast<IT>(n + e) * per_col;             // one past the last source vector
 
-  VT cur[kTileVec], nxt[kTileVec];
+  // Every lane issues every load and store of a tile (no per-lane branches),
+  // so the compiler counts the memory operations in flight exactly and the
+  // wait for a tile's loads leaves the next tile's loads and the previous
+  // tile's stores in flight (a branch per access makes it wait for all of
+  // them).  Lanes left of the moved range (only in its leftmost tile) load
+  // its first cell and store that value back to the same cell: that cell is
+  // never a destination of the right shift, so the store changes nothing.
+  // Three register buffers rotate: no copy between them (a copy would wait
+  // for the next tile's loads), and a buffer is reloaded two steps after its
+  // stores were issued (reloading it right away waits for those stores).
+  VT buf0[kTileVec], buf1[kTileVec], buf2[kTileVec];
   if (may_move) {
 #pragma unroll
-    for (int u = 0; u < kTileVec; ++u) {
-      const long long i = hi - TV + u * kThreads + t;
-      if (i >= lo) cur[u] = stream_ld(base + i);
-    }
+    for (int u = 0; u < kTileVec; ++u) buf0[u] = stream_ld(cell<VT>(pb, max(hi - TV + u * kThreads + t, lo)));
   }
   int E, M;
   bool ok;
   commit_state(P, sh, E, M, ok);           // barriers: every lane of the workgroup gets here
   if (!ok || !may_move || M == e) return;  // uniform in the workgroup
-  const long long shift = static_cast<long long>(M - e) * per_col;
-  while (true) {
-    const long long nhi = hi - TV;
-    const bool more = nhi > lo;
-    if (more) {
+  const IT shift = static_cast<IT>(M - e) * per_col;
+  // One step: load the tile left of `hi` (after the last tile: the first
+  // cell again, unused), wait for the current tile's loads in every lane,
+  // store it `shift` to the right.  Returns whether a tile is left.
+  auto step = [&](VT (&cur)[kTileVec], VT (&nxt)[kTileVec]) {
+    const IT nhi = hi - TV;
 #pragma unroll
-      for (int u = 0; u < kTileVec; ++u) {
-        const long long i = nhi - TV + u * kThreads + t;
-        if (i >= lo) nxt[u] = stream_ld(base + i);
-      }
-    }
+    for (int u = 0; u < kTileVec; ++u) nxt[u] = stream_ld(cell<VT>(pb, max(nhi - TV + u * kThreads + t, lo)));
 #pragma unroll
-    for (int u = 0; u < kTileVec; ++u)
-      if (hi - TV + u * kThreads + t >= lo) hold(cur[u]);   // this tile's loads have landed
+    for (int u = 0; u < kTileVec; ++u) hold(cur[u]);          // this tile's loads have landed
     __syncthreads();                                           // ... in every lane
 #pragma unroll
     for (int u = 0; u < kTileVec; ++u) {
-      const long long i = hi - TV + u * kThreads + t;
-      if (i >= lo) stream_st(cur[u], base + i + shift);
+      const IT i = hi - TV + u * kThreads + t;
+      stream_st(cur[u], cell<VT>(pb, i >= lo ? i + shift : lo));
     }
-    if (!more) break;
-#pragma unroll
-    for (int u = 0; u < kTileVec; ++u) cur[u] = nxt[u];
     hi = nhi;
+    return nhi > lo;                        // uniform
+  };
+  while (step(buf0, buf1) && step(buf1, buf2) && step(buf2, buf0)) {
   }
 }
 
-template <int VB>
+template <int VB, typename IT>
 __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
   __shared__ int sh[2 * kWaves];
   __shared__ long long sh_bytes[kWaves];
@@ -207,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
   const int t = threadIdx.x;
   if (blk > P.B) {                         // one plane, address order: p = ((l * 2 + kv) * B + b) * H + h
     const int p = blk - P.B - 1;
-    move_plane<VB>(P, p, (p / P.H) % P.B, sh);
+    move_plane<VB, IT>(P, p, (p / P.H) % P.B, sh);
     return;
   }
   int E, M;
@@ -366,6 +382,19 @@ __global__ __launch_bounds__(kCompactThreads) void tree_compact_kernel(CompactPa
 
 using namespace specv;
 
+template <typename IT>
+static void launch_realign(const RealignParams &P, size_t R, const void *kv, dim3 grid, dim3 block,
+                           hipStream_t s) {
+  if (R % 16 == 0 && aligned(kv, 16))
+    hipLaunchKernelGGL((realign_kernel<16, IT>), grid, block, 0, s, P);
+  else if (R % 8 == 0 && aligned(kv, 8))
+    hipLaunchKernelGGL((realign_kernel<8, IT>), grid, block, 0, s, P);
+  else if (R % 4 == 0 && aligned(kv, 4))
+    hipLaunchKernelGGL((realign_kernel<4, IT>), grid, block, 0, s, P);
+  else
+    hipLaunchKernelGGL((realign_kernel<2, IT>), grid, block, 0, s, P);
+}
+
 static int realign_launch(void *kv, spec_dtype dt, int L, int B, int H, int C, int D, int k, int slots,
                           const int32_t *end_col, const int32_t *kv_len_in, const int32_t *emit_count,
                           int32_t *end_col_out, int32_t *kv_len_out, int32_t *pos_ids, int32_t *mask,
@@ -417,14 +446,10 @@ static int realign_launch(void *kv, spec_dtype dt, int L, int B, int H, int C, i
   const dim3 grid(static_cast<unsigned>(B + 1 + planes)), block(kThreads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (R % 16 == 0 && aligned(kv, 16))
-    hipLaunchKernelGGL(realign_kernel<16>, grid, block, 0, s, P);
-  else if (R % 8 == 0 && aligned(kv, 8))
-    hipLaunchKernelGGL(realign_kernel<8>, grid, block, 0, s, P);
-  else if (R % 4 == 0 && aligned(kv, 4))
-    hipLaunchKernelGGL(realign_kernel<4>, grid, block, 0, s, P);
+  if (P.plane_bytes < (1LL << 31))         // vector indices and byte offsets fit 32 bits
+    launch_realign<int>(P, R, kv, grid, block, s);
   else
-    hipLaunchKernelGGL(realign_kernel<2>, grid, block, 0, s, P);
+    launch_realign<long long>(P, R, kv, grid, block, s);
   return launch_status();
 }
 

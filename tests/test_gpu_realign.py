@@ -123,6 +123,55 @@ def test_largest_workload_full_size_sampled_and_invariant():
             del full, m
 
 
+def test_plane_of_2_gib_or_more():
+    """Planes of 2 GiB or more are walked with 64-bit indices (smaller ones
+    with 32-bit byte offsets).  One f32 cache with D = 512 and C = 2^20 + 64
+    columns holds 2.15 GB per plane; sequence 0 keeps its whole prefix and
+    moves 3 columns right, so its range crosses the 2 GiB mark.  Bookkeeping
+    exact against the oracle; sampled moved columns (both ends of the range
+    and the columns around the mark included) equal their pre-move bytes; the
+    sequence that does not move and the cells left of the destination range
+    are unchanged."""
+    note("realign plane over 2 GiB (64-bit indices)")
+    L, H, D, B, k, dt = 1, 1, 512, 2, 3, "f32"
+    C = (1 << 20) + 64
+    E = C - (k + 1) - 5
+    n = np.array([E, 1000])
+    e = np.array([1, k + 1])
+    tokens = np.random.default_rng(6).integers(0, 1000, (B, E + 1))
+    kv = _cache(L, H, D, B, C, E, n, tokens, dt)
+    assert C * D * 4 >= 1 << 31
+    book = oracle.commit_realign(None, E, n, e, k, C)
+    assert book["delta"].tolist() == [3, 0]
+    rng = np.random.default_rng(7)
+    n0 = int(book["n_new"][0])
+    mark = (1 << 31) // (D * 4)                       # first column at or past 2 GiB
+    off = np.concatenate([[0, 1, n0 - 2, n0 - 1], mark - 4 + np.arange(8), rng.integers(0, n0, 3000)])
+    iv = kv.view(torch.int32)
+    pl = [(l, kvi) for l in range(L) for kvi in range(2)]
+    src_cols = torch.as_tensor(E - n[0] + off).to(DEV)
+    before = [iv[l, kvi, 0, 0, src_cols].cpu().numpy() for l, kvi in pl]
+    still = rng.integers(0, C, 2000)
+    still_before = [iv[l, kvi, 1, 0, torch.as_tensor(still).to(DEV)].cpu().numpy() for l, kvi in pl]
+    left_before = [iv[l, kvi, 0, 0, :3].cpu().numpy() for l, kvi in pl]
+
+    got = host(commit(kv, k, E, n, e))
+    pos, mask = oracle.position_and_mask(book["E_new"], book["n_new"], C)
+    assert (got["status"] == 0).all()
+    assert np.array_equal(got["pos"], pos) and np.array_equal(got["mask"], mask)
+    assert np.array_equal(got["kv_len"], book["n_new"]) and int(got["end_col"][0]) == book["E_new"]
+    assert int(got["bytes_moved"][0]) == oracle.realign.moved_bytes(book["n_new"], book["delta"],
+                                                                      L * 2 * H * D * 4)
+    dst_cols = torch.as_tensor(book["E_new"] - n0 + off).to(DEV)
+    for i, (l, kvi) in enumerate(pl):
+        assert np.array_equal(iv[l, kvi, 0, 0, dst_cols].cpu().numpy(), before[i]), (l, kvi)
+        assert np.array_equal(iv[l, kvi, 1, 0, torch.as_tensor(still).to(DEV)].cpu().numpy(),
+                              still_before[i])
+        assert np.array_equal(iv[l, kvi, 0, 0, :3].cpu().numpy(), left_before[i])
+    del kv
+    torch.cuda.empty_cache()
+
+
 def _small(dt="bf16", L=2, H=3, D=64, seed=0):
     rng = np.random.default_rng(seed)
     return rng, L, H, D, dt
