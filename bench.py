@@ -23,7 +23,8 @@ around back-to-back launches: one call's events add microseconds of their own). 
 bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W]
-    python bench.py --record-traffic FETCH_DIR WRITE_DIR   (after two rocprofv3 --pmc runs)
+    python bench.py --record-traffic LOG DIR1 DIR2 DIR3 DIR4   (after the four rocprofv3 --pmc passes)
+    python bench.py --summarize-trace TRACE_DIR LOG            (after a rocprofv3 --kernel-trace run)
 """
 from __future__ import annotations
 
@@ -91,31 +92,192 @@ def _per_kernel(rows, key, step_grid=False):
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
 
-def record_traffic(fetch_dir: str, write_dir: str) -> None:
-    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
-    dispatch) of this benchmark into the committed traffic summary."""
-    f_rows, w_rows = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
-    pf, _ = _per_kernel([r for r in f_rows if "neg" in r[0].lower()], "", step_grid=True)
-    pw, _ = _per_kernel([r for r in w_rows if "neg" in r[0].lower()], "", step_grid=True)
-    out = {"probe": {"kernel": "torch int32 negation (one 4-byte read and one 4-byte write per element)",
-                     "bytes_read": PROBE_BYTES, "bytes_written": PROBE_BYTES,
-                     "fetch_kib": pf, "write_kib": pw,
-                     "fetch_factor": (pf * 1024 / PROBE_BYTES) if pf else None,
-                     "write_factor": (pw * 1024 / PROBE_BYTES) if pw else None},
-           "kernels": {}, "sources_sha256": sources_digest()}
-    for key in ("greedy_verify_kernel", "realign_kernel"):
-        fk, nf = _per_kernel(f_rows, key, step_grid=True)
-        wk, nw = _per_kernel(w_rows, key, step_grid=True)
-        out["kernels"][key] = {"fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
-                               "dispatches": [nf, nw]}
+# Counter passes (one rocprofv3 --pmc run each; at most 4 TCC counters a run).
+# FETCH_SIZE and WRITE_SIZE are rocprofv3's derived KiB per dispatch; the
+# request passes count the L2-to-memory requests by size, which gives the
+# bytes without any scale fitted to a probe.
+COUNTER_PASSES = [
+    ["FETCH_SIZE"],
+    ["WRITE_SIZE"],
+    ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"],
+    ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum",
+     "TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum"],
+]
+TRAFFIC_KERNELS = ("greedy_verify_kernel", "realign_kernel")
+TRAFFIC_MD = TRAFFIC_JSON[:-len(".json")] + ".md"
+TRACE_MD = os.path.join(ROOT, "profiles", "kernels_verify_realign_B32_k8_V128256.md")
+COUNTER_BENCH_ARGS = "--steps 3 --warmup 1 --step-only --no-cpu-baseline"
+
+
+def request_bytes(c: dict):
+    """(read, write) bytes over the L2-to-memory interface from request counts
+    and their sizes: reads of 32, 64 or 128 bytes, writes of 64 bytes or
+    else 32.  None if a count is missing."""
+    need = ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum",
+            "TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"]
+    if any(c.get(x) is None for x in need):
+        return None
+    rd = 32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 * c["TCC_EA0_RDREQ_64B_sum"] + 128 * c["TCC_EA0_RDREQ_128B_sum"]
+    wr = 64 * c["TCC_EA0_WRREQ_64B_sum"] + 32 * (c["TCC_EA0_WRREQ_sum"] - c["TCC_EA0_WRREQ_64B_sum"])
+    return rd, wr
+
+
+def _bench_line(log_path: str) -> dict:
+    with open(log_path) as f:
+        return json.loads([x for x in f if x.startswith("{")][-1])
+
+
+def record_traffic(bench_log: str, *dirs: str) -> None:
+    """Turn the counter passes of this benchmark (COUNTER_PASSES, in order,
+    each run as `bench.py COUNTER_BENCH_ARGS` under rocprofv3 --pmc) into the
+    committed traffic summary (JSON and markdown).  Each counter's mean per
+    dispatch is taken over the step loop's dispatches of each kernel and over
+    the copy probe (torch int32 negation of PROBE_BYTES: that many bytes read
+    and as many written).  bench_log: the output of one of those runs, for
+    the algorithmic bytes of the same dispatches."""
+    rows = {}
+    for d, names in zip(dirs, COUNTER_PASSES):
+        for c in names:
+            r = _counter_rows(d, c)
+            if r:
+                rows[c] = r
+
+    def per(c, key, probe=False):
+        if c not in rows:
+            return None
+        sel = [r for r in rows[c] if "neg" in r[0].lower()] if probe else rows[c]
+        v, _ = _per_kernel(sel, "" if probe else key, step_grid=True)
+        return v
+
+    probe = {"kernel": "torch int32 negation (one 4-byte read and one 4-byte write per element)",
+             "bytes_read": PROBE_BYTES, "bytes_written": PROBE_BYTES}
+    for c in rows:
+        probe[c] = per(c, "", probe=True)
+    pf, pw = probe.get("FETCH_SIZE"), probe.get("WRITE_SIZE")
+    probe["fetch_factor"] = (pf * 1024 / PROBE_BYTES) if pf else None
+    probe["write_factor"] = (pw * 1024 / PROBE_BYTES) if pw else None
+    rb = request_bytes(probe)
+    probe["request_read_bytes"], probe["request_write_bytes"] = rb if rb else (None, None)
+    bl = _bench_line(bench_log)
+    alg = {"greedy_verify_kernel": bl["roofline_verify"]["algorithmic_bytes_per_launch"],
+           "realign_kernel": bl["roofline"]["algorithmic_bytes_all_dispatches"]}
+    out = {"probe": probe, "kernels": {}, "sources_sha256": sources_digest(),
+           "counter_bench_args": COUNTER_BENCH_ARGS}
+    for key in TRAFFIC_KERNELS:
+        kk = {c: per(c, key) for c in rows}
+        kk["fetch_kib_per_dispatch"] = kk.pop("FETCH_SIZE", None)
+        kk["write_kib_per_dispatch"] = kk.pop("WRITE_SIZE", None)
+        kk["dispatches"] = _per_kernel(rows["FETCH_SIZE"], key, step_grid=True)[1] if "FETCH_SIZE" in rows else 0
+        rb = request_bytes(kk)
+        kk["request_read_bytes"], kk["request_write_bytes"] = rb if rb else (None, None)
+        kk["algorithmic_bytes"] = alg[key]
+        out["kernels"][key] = kk
     os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(out, f, indent=1)
+    with open(TRAFFIC_MD, "w") as f:
+        f.write(_traffic_md(out))
     print(json.dumps(out))
 
 
-def traffic_bytes(key: str):
-    """Measured HBM bytes per dispatch, scaled by the probe; None if stale or absent."""
+def _traffic_md(t: dict) -> str:
+    p = t["probe"]
+    fk = lambda v: "n/a" if v is None else f"{v:.4g}"
+    cmds = [f"timeout -s KILL 120 rocprofv3 --pmc {' '.join(c)} -f csv -d $R/gpurun_out/pmc{i + 1} -o run "
+            f"-- python3 $R/bench.py {COUNTER_BENCH_ARGS} > $R/gpurun_out/pmc{i + 1}.log"
+            for i, c in enumerate(COUNTER_PASSES)]
+    out = ["# HBM traffic per dispatch: verify + realign, B=32 k=8 V=128256", "",
+           "Four counter passes of the step loop (3 timed steps after 1 warm-up step, then the copy probe). "
+           "Each pass is its own run (R is the repository root):", "", "```",
+           "cd /tmp && export TMPDIR=/tmp", *cmds,
+           "python3 $R/bench.py --record-traffic $R/gpurun_out/pmc1.log " +
+           " ".join(f"$R/gpurun_out/pmc{i + 1}" for i in range(len(COUNTER_PASSES))), "```", "",
+           "Two independent byte counts:", "",
+           "- **scaled**: FETCH_SIZE and WRITE_SIZE, each divided by what it reads for the copy probe per byte "
+           f"moved (FETCH {fk(p['fetch_factor'])}, WRITE {fk(p['write_factor'])}).",
+           "- **requests**: the L2-to-memory requests counted by size (reads of 32, 64 and 128 bytes; "
+           "writes of 64 bytes, the rest 32), times their size. No scale is fitted.", "",
+           f"The copy probe moves {PROBE_BYTES} bytes each way. Its read requests give "
+           f"{fk(p.get('request_read_bytes'))} bytes and its write requests {fk(p.get('request_write_bytes'))}. "
+           "FETCH_SIZE counts every read request that is not 32 bytes as 64 bytes; its 128-byte term rests on "
+           "TCC_BUBBLE, which reads 0 here, while TCC_EA0_RDREQ_128B counts every read. That is why FETCH_SIZE "
+           "reads half.", "",
+           "| kernel | dispatches | algorithmic bytes | scaled bytes | request bytes (read + write) | "
+           "request / algorithmic |", "|---|---|---|---|---|---|"]
+    for key, k in t["kernels"].items():
+        sc = (1024 * (k["fetch_kib_per_dispatch"] / p["fetch_factor"] + k["write_kib_per_dispatch"] / p["write_factor"])
+              if k.get("fetch_kib_per_dispatch") is not None and p.get("fetch_factor") else None)
+        rq = (k["request_read_bytes"] + k["request_write_bytes"]) if k.get("request_read_bytes") is not None else None
+        ratio = f"{rq / k['algorithmic_bytes']:.4f}" if rq else "n/a"
+        out.append(f"| `{key}` | {k['dispatches']} | {k['algorithmic_bytes']:.6g} | {fk(sc)} | "
+                   f"{fk(k.get('request_read_bytes'))} + {fk(k.get('request_write_bytes'))} | {ratio} |")
+    out += ["", "DRAM credit stalls (cycles summed over the L2 channels) per memory request:", "",
+            "| kernel | read-credit stalls / read request | write-credit stalls / write request |", "|---|---|---|"]
+    for name, k in [("copy probe", p)] + list(t["kernels"].items()):
+        rs, ws_ = k.get("TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum"), k.get("TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum")
+        rr, wr = k.get("TCC_EA0_RDREQ_sum"), k.get("TCC_EA0_WRREQ_sum")
+        a = f"{rs / rr:.3f}" if rs is not None and rr else "n/a"
+        b = f"{ws_ / wr:.3f}" if ws_ is not None and wr else "n/a"
+        out.append(f"| {name} | {a} | {b} |")
+    out += ["", f"Kernel sources hash: `{t['sources_sha256'][:16]}` (bench.py reports `traffic` only while the "
+            "sources match).", ""]
+    return "\n".join(out)
+
+
+def _trace_rows(directory: str):
+    """(kernel label, grid) -> durations in us from a rocprofv3 kernel trace."""
+    import csv
+    import re
+    acc = {}
+    for path in glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                n = r["Kernel_Name"]
+                m = re.search(r"::(\w+_kernel)(<.*?>)?\(", n)
+                if "specv" in n and m:
+                    label = m.group(1) + (m.group(2) or "").replace("specv::(anonymous namespace)::", "")
+                elif "neg_kernel" in n:
+                    label = "torch neg (copy probe)"
+                else:
+                    continue
+                d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                acc.setdefault((label, int(r["Grid_Size_X"] if "Grid_Size_X" in r else r.get("Grid_Size", 0))),
+                               []).append(d)
+    return acc
+
+
+def summarize_trace(trace_dir: str, bench_log: str) -> None:
+    """Write the committed kernel-duration summary from a rocprofv3
+    --kernel-trace run of the default bench and that run's output."""
+    acc = _trace_rows(trace_dir)
+    b = _bench_line(bench_log)
+    out = ["# Kernel durations: verify + realign, B=32 k=8 V=128256, bf16 KV 32x8x128 (~18 GB)", "",
+           "Command (MI355X, one GPU; R is the repository root):", "", "```",
+           "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/trace -o run "
+           "-- python3 $R/bench.py > $R/gpurun_out/trace.log",
+           "python3 $R/bench.py --summarize-trace $R/gpurun_out/trace $R/gpurun_out/trace.log", "```", "",
+           "Every launch of the library's kernels in that run (the step loop, the back-to-back verify launches, "
+           "the secondary measurements and the batch-size sweeps), grouped by kernel and grid size:", "",
+           "| kernel | grid | calls | avg (us) | min (us) | max (us) |", "|---|---|---|---|---|---|"]
+    for (k, g), v in sorted(acc.items(), key=lambda x: -sum(x[1])):
+        out.append(f"| `{k}` | {g} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    rf, rv = b["roofline"], b["roofline_verify"]
+    out += ["", "From the bench line of the same run (HIP events on the launch stream):", "",
+            f"- value {b['value']:.0f} rows/s, {b['ms_per_step']:.3f} ms per step",
+            f"- `realign_kernel`: {b['realign_ms_per_call']:.3f} ms per call, {rf['achieved']:.0f} GB/s, "
+            f"{rf['frac']:.3f} of 8 TB/s",
+            f"- `greedy_verify_kernel` (the whole verify call): {b['verify_us_per_launch']:.2f} us per launch, "
+            f"{rv['achieved']:.0f} GB/s, {rv['frac']:.3f} of 8 TB/s",
+            f"- copy probe (torch int32 negation, 2 GiB each way): {b['copy_probe_GBps']:.0f} GB/s", ""]
+    with open(TRACE_MD, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
+
+
+def traffic_bytes(key: str, requests: bool = False):
+    """Measured HBM bytes per dispatch, None if stale or absent: FETCH_SIZE and
+    WRITE_SIZE scaled by the copy probe's per-byte readings, or (requests)
+    the request counts times their sizes."""
     try:
         with open(TRAFFIC_JSON) as f:
             t = json.load(f)
@@ -124,6 +286,10 @@ def traffic_bytes(key: str):
     if t.get("sources_sha256") != sources_digest():
         return None
     k = t["kernels"].get(key, {})
+    if requests:
+        if k.get("request_read_bytes") is None:
+            return None
+        return k["request_read_bytes"] + k["request_write_bytes"]
     p = t["probe"]
     if not k.get("fetch_kib_per_dispatch") or not p.get("fetch_factor") or not p.get("write_factor"):
         return None
@@ -141,10 +307,15 @@ def main() -> int:
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step only: no secondary calls or batch-size sweeps (for counter runs)")
-    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--record-traffic", nargs=len(COUNTER_PASSES) + 1, metavar="PATH",
+                    help="the log of one counter run, then the output directory of each counter pass")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"))
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(*args.record_traffic)
+        return 0
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (the step shards "
@@ -282,6 +453,8 @@ def main() -> int:
     tr_rea = traffic_bytes("realign_kernel")
     tr_ver = traffic_bytes("greedy_verify_kernel")
     avg_rea_bytes = sum(rea_bytes) / len(rea_bytes)
+    # every dispatch of the step loop, warm-up included: what the counter runs average over
+    all_rea_bytes = sum(int(moved_h[r]) + 8 * B * C for r in range(R)) / R
     result = {
         "metric": METRIC,
         "value": rows * args.steps / wall,
@@ -300,11 +473,15 @@ def main() -> int:
                    "prefix": "512-4096", "capacity_columns": C, "logit_buffers": nbuf},
         "roofline": {"bound": "hbm", "kernel": "realign_kernel", "achieved": rea_GBps / 1e9,
                      "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": rea_GBps / PEAK_HBM,
-                     "traffic": tr_rea, "algorithmic_bytes_per_launch": avg_rea_bytes},
+                     "traffic": tr_rea, "traffic_requests": traffic_bytes("realign_kernel", requests=True),
+                     "algorithmic_bytes_per_launch": avg_rea_bytes,
+                     "algorithmic_bytes_all_dispatches": all_rea_bytes},
         "roofline_verify": {"bound": "hbm", "kernel": "greedy_verify_kernel (the whole spec_verify_greedy call: one launch)",
                             "achieved": ver_bytes / t_launch / 1e9,
                             "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": ver_bytes / t_launch / PEAK_HBM,
-                            "traffic": tr_ver, "algorithmic_bytes_per_launch": ver_bytes,
+                            "traffic": tr_ver,
+                            "traffic_requests": traffic_bytes("greedy_verify_kernel", requests=True),
+                            "algorithmic_bytes_per_launch": ver_bytes,
                             "timing": f"HIP events around {n_back} back-to-back launches over the rotating buffers"},
         "verify_rows_per_s": rows / t_launch,
         "verify_us_per_launch": t_launch * 1e6,
