@@ -28,17 +28,24 @@
  *   - Workspaces ("ws") are device memory of at least the queried size, 256-byte
  *     aligned, holding per-call partial results.  Calls that may run at the
  *     same time (different streams) need different workspaces.
- *   - The greedy verification workspace also carries the completion flags of
- *     its single launch: it must be zero-filled before its first use (e.g.
- *     hipMemset, torch.zeros) and no other call may write into it; every
- *     completed greedy or tree verification call leaves it zero-filled again.
- *     (A tree verification call accepts any contents.)  Every other
- *     workspace's contents on entry are ignored.
+ *   - The greedy and the stochastic verification workspaces also carry the
+ *     completion flags of their single launch: such a workspace must be
+ *     zero-filled before its first use (e.g. hipMemset, torch.zeros) and no
+ *     call of another kind may write into it; every completed call leaves it
+ *     zero-filled again.  A greedy workspace may be shared with tree
+ *     verification (which accepts any contents and also leaves it zero-
+ *     filled).  For verification from logits only the last
+ *     spec_verify_sample_workspace_bytes(B, k, V) bytes are such flags; the
+ *     leading part is rewritten by every call.  Every other workspace's
+ *     contents on entry are ignored.
  *   - A greedy verify call is one launch: streaming workgroups publish per-
  *     chunk results and one workgroup of the same launch commits them.  Calls
  *     whose rows need more chunk results than that workgroup holds at once
  *     (more than 1024 per sequence), and tree verification, launch a streaming
  *     pass and a commit pass, synchronised by the stream order.
+ *   - A stochastic verify call is one launch too: streaming workgroups publish
+ *     the chunk masses of the row each sequence draws from, and one workgroup
+ *     per sequence of the same launch, dispatched after them, draws.
  *   - Token ids are int32 in [0, V).  Layouts are row-major, last index fastest.
  */
 #ifndef SPEC_VERIFY_H
@@ -69,9 +76,9 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 #define SPEC_ST_NONFINITE 8   /* a gathered probability or a drawn row's mass is not finite */
 #define SPEC_ST_BAD_STATE 16  /* commit: n_b outside [0, E] or e_b outside [0, k+1] */
 #define SPEC_ST_CAPACITY 32   /* commit: E < 0 or E + k + 1 > C */
-#define SPEC_ST_INCOMPLETE 64 /* greedy verify: a chunk result did not arrive within the
-                                 call's wait bound (seconds); this sequence's outputs are
-                                 unspecified (not expected in normal operation) */
+#define SPEC_ST_INCOMPLETE 64 /* greedy or stochastic verify: a chunk result did not arrive
+                                 within the call's wait bound (seconds); this sequence's
+                                 outputs are unspecified (not expected in normal operation) */
 
 #define SPEC_MAX_K 127          /* largest number of proposals k per sequence */
 #define SPEC_GROUP_MAX_N 4096   /* largest window for spec_group_same_length */

@@ -98,9 +98,10 @@ def _dtype_code(t) -> int:
 
 
 def workspace(nbytes: int, device=None):
-    """A zero-filled device workspace of at least nbytes.  Greedy verification
-    needs a zero-filled workspace that no other call writes into (it keeps it
-    zero-filled between calls); the other calls ignore the contents."""
+    """A zero-filled device workspace of at least nbytes.  Greedy, tree and
+    stochastic verification need a zero-filled workspace that no other kind
+    of call writes into (they keep it zero-filled between calls); the other
+    calls ignore the contents."""
     import torch
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
 

@@ -11,18 +11,22 @@
 // Design.  The acceptance chain only gathers 2 scalars per draft.  The bytes
 // are in the single full row each sequence draws from: the residual
 // p_j - q_j at the first rejection (8 bytes per vocabulary entry) or the
-// target row p_k after full acceptance (4 bytes).
-//   * sample_chunk_kernel: one workgroup per (sequence, chunk) re-derives the
+// target row p_k after full acceptance (4 bytes).  One launch:
+//   * Producers, one workgroup per (sequence, chunk): each re-derives the
 //     chain from the gathers, streams its chunk of the row with 16-byte loads
-//     and stores the chunk's mass as a float64 partial; chunk 0 also records
-//     the chain's outcome (accepted count, emitted count, row, status).
-//   * sample_draw_kernel: one workgroup per sequence adds the partials in
-//     chunk order (S), finds the chunk whose running sum first exceeds u * S,
-//     scans that chunk in index order and writes the token; one extra
-//     workgroup scans the emit counts into offsets.
-// No workgroup waits on another (the kernel boundary is the synchronisation:
-// device-scope completion tickets serialise on a multi-XCD part).  All sums
-// are float64 over the float32 r_v in a fixed order, so results are
+//     and publishes the chunk's float64 mass as a nonzero 64-bit key with an
+//     agent-scope store.
+//   * Finishers, one workgroup per sequence, after every producer in the
+//     grid (workgroups are dispatched in index order, so a finisher is only
+//     dispatched once every producer it waits on has been): each derives the
+//     chain, writes the counts, polls its row's keys until all are present
+//     (bounded), adds the masses in chunk order (S), finds the chunk whose
+//     running sum first exceeds u * S, scans that chunk in index order and
+//     writes the token; then it clears its keys, so the workspace is
+//     zero-filled again for the next call.
+//   * One last workgroup turns the emit counts (published by the finishers as
+//     soon as their chains are known) into offsets.
+// All sums are float64 over the float32 r_v in a fixed order, so results are
 // reproducible run to run and within ~1e-16 relative of a correctly rounded
 // sum.
 #include "process.h"
@@ -53,18 +57,20 @@ struct SampleParams {
   int32_t *accept_len, *emit_count, *out_tokens, *emit_offsets;
   double *final_mass;
   int32_t *status;
-  double *partial;              // [B * chunks]
-  int4 *chain;                  // [B]: mode, row, accepted, status bits
+  unsigned long long *keys;     // [B * chunks] published chunk masses (0: not yet written)
+  int32_t *ecnt;                // [B] published emit_count + 1 (0: not yet written)
 };
 
+// Workspace: the chunk-mass slots, then the emit-count slots; zero-filled on
+// entry and left zero-filled by every call.
 struct SampleWs {
-  size_t part, chain, total;
+  size_t keys, ecnt, total;
 };
 inline SampleWs sample_ws_layout(int B, int chunks) {
   SampleWs w;
-  w.part = 0;
-  w.chain = round_up(static_cast<size_t>(B) * chunks * sizeof(double), 256);
-  w.total = w.chain + round_up(static_cast<size_t>(B) * sizeof(int4), 256);
+  w.keys = 0;
+  w.ecnt = round_up(static_cast<size_t>(B) * chunks * sizeof(unsigned long long), 256);
+  w.total = w.ecnt + round_up(static_cast<size_t>(B) * sizeof(int32_t), 256);
   return w;
 }
 
@@ -255,23 +261,18 @@ __device__ inline double chunk_mass(const RowT &r, int c, int V, bool vec, doubl
 template <typename T>
 __device__ inline bool finite_val(T x) { return isfinite(x); }
 
+// The acceptance chain of sequence b, derived by every workgroup that needs
+// it from the same gathers and the same float32 arithmetic (so all of them
+// agree): x.mode, y.row drawn from, z.accepted drafts, w.status bits.
+// Contains barriers.
 template <class Src>
-__global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleParams P) {
-  __shared__ int sh_acc[SPEC_MAX_K];
-  __shared__ int sh_st[SPEC_MAX_K];
-  __shared__ int sh_d[SPEC_MAX_K];
-  __shared__ int sh_mode, sh_row;
-  __shared__ double sh_red[kWaves];
-
+__device__ inline int4 derive_chain(const SampleParams &P, int b, int *sh_acc, int *sh_st, int *sh_d,
+                                    int4 *sh_ch) {
   const int t = threadIdx.x;
-  const int b = blockIdx.x / P.chunks;
-  const int c = blockIdx.x - b * P.chunks;
   const int k = P.k, kp1 = k + 1, V = P.V;
   const int32_t *d = P.draft + static_cast<size_t>(b) * k;
   const float *ub = P.u + static_cast<size_t>(b) * kp1;
   const int rem = P.remaining ? P.remaining[b] : -1;   // negative: no budget (loaded with the drafts)
-
-  // ---- acceptance chain: every workgroup of the sequence derives the same row
   for (int j = t; j < k; j += kThreads) {
     const int x = d[j];
     sh_d[j] = x;
@@ -316,24 +317,42 @@ __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(SampleParams P) 
         }
       }
     }
-    sh_mode = mode;
-    sh_row = row;
-    if (c == 0) {
-      P.chain[b] = make_int4(mode, row, m, st);
-      P.accept_len[b] = m;
-      P.emit_count[b] = m + (mode != MODE_NONE ? 1 : 0);
-    }
+    *sh_ch = make_int4(mode, row, m, st);
   }
   __syncthreads();
-  const int mode = sh_mode, jrow = sh_row;
-  if (mode == MODE_NONE) return;
-  const typename Src::RowT r = Src::row(P, b, jrow, mode == MODE_RESID);
-  const double part = chunk_mass(r, c, V, P.vec != 0, sh_red);
-  if (t == 0) P.partial[static_cast<size_t>(b) * P.chunks + c] = part;
+  return *sh_ch;
 }
 
+// Chunk masses travel as 64-bit keys: the mass's bits XOR kMassSentinel.
+// The sentinel is a NaN whose low 29 bits are not all zero, a pattern no mass
+// here can take (a float32 widened to float64, and any arithmetic on such
+// values, gives NaNs with those bits zero), so every published key is nonzero
+// and a zero slot means "not yet written".
+constexpr unsigned long long kMassSentinel = 0x7FF4000000000001ull;
+constexpr int kMaxPolls = 1 << 22;      // about 4 s of polling: a bound every wait reaches
+
+// Producer: chunk c of the row sequence b draws from; its mass published.
 template <class Src>
-__global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
+__device__ inline void produce_chunk(const SampleParams &P, int b, int c) {
+  __shared__ int sh_acc[SPEC_MAX_K], sh_st[SPEC_MAX_K], sh_d[SPEC_MAX_K];
+  __shared__ int4 sh_ch;
+  __shared__ double sh_red[kWaves];
+  const int4 ch = derive_chain<Src>(P, b, sh_acc, sh_st, sh_d, &sh_ch);
+  if (ch.x == MODE_NONE) return;                 // no draw: the finisher expects no mass
+  const typename Src::RowT r = Src::row(P, b, ch.y, ch.x == MODE_RESID);
+  const double part = chunk_mass(r, c, P.V, P.vec != 0, sh_red);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(P.keys + static_cast<size_t>(b) * P.chunks + c,
+                       static_cast<unsigned long long>(__double_as_longlong(part)) ^ kMassSentinel,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Finisher of sequence b: the chain's outputs, then (when a token is drawn)
+// the chunk masses as they arrive, the draw, and every slot back to zero.
+template <class Src>
+__device__ inline void finish_sequence(const SampleParams &P, int b) {
+  __shared__ int sh_acc[SPEC_MAX_K], sh_st[SPEC_MAX_K], sh_d[SPEC_MAX_K];
+  __shared__ int4 sh_ch;
   __shared__ double sh_red[kWaves];
   __shared__ double sh_part[kMaxChunks];
   __shared__ int sh_scan[kWaves + 1];
@@ -345,128 +364,149 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), w = t / kWave;
   const int k = P.k, kp1 = k + 1, V = P.V;
-  if (static_cast<int>(blockIdx.x) == P.B) {     // emit offsets
-    if (P.emit_offsets) block_offsets(P.emit_count, P.emit_offsets, P.B, sh_scan);
-    return;
-  }
-  const int b = blockIdx.x;
   const int nc = P.chunks;
-  // every load that does not depend on the chain is issued with it: the chunk
-  // masses (read only when a token is drawn), the draw's uniform, the drafts
-  const int4 ch = P.chain[b];
-  for (int i = t; i < nc; i += kThreads) sh_part[i] = P.partial[static_cast<size_t>(b) * nc + i];
+  // loads that do not depend on the chain are issued with it
   const float u_draw = P.u[static_cast<size_t>(b) * kp1 + k];
-  const int32_t *d = P.draft + static_cast<size_t>(b) * k;
-  const int d_t = t < k ? d[t] : -1;
+  const int d_t = t < k ? P.draft[static_cast<size_t>(b) * k + t] : -1;
+  const int4 ch = derive_chain<Src>(P, b, sh_acc, sh_st, sh_d, &sh_ch);
   const int mode = ch.x, jrow = ch.y, m = ch.z;
+  const int emit = m + (mode != MODE_NONE ? 1 : 0);
+  if (t == 0) {
+    P.accept_len[b] = m;
+    P.emit_count[b] = emit;
+    if (P.emit_offsets) __hip_atomic_store(P.ecnt + b, emit + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   int st = ch.w;
   int tok = -1;
   double S = 0.0;
   if (mode != MODE_NONE) {
-    typename Src::RowT r = Src::row(P, b, jrow, mode == MODE_RESID);
-    const bool vec = P.vec != 0;
-    const int per = (nc + kThreads - 1) / kThreads;  // chunks per lane, consecutive
-    const int c0 = t * per;
-    __syncthreads();
-    // total mass and each lane's exclusive prefix over the chunk masses
-    double pre = 0.0;
-    auto scan_parts = [&]() {
-      double mine = 0.0;
-      for (int i = 0; i < per; ++i)
-        if (c0 + i < nc) mine += sh_part[c0 + i];
-      pre = block_excl_scan_d(mine, sh_dscan, &S);
-    };
-    scan_parts();
-    if (isfinite(S) && !(S > 0.0)) {
-      st |= SPEC_ST_RESID_ZERO;
-      if (mode == MODE_RESID) {         // fall back to the target row p_j itself
-        r.resid = false;
-        for (int i = 0; i < nc; ++i) {
-          const double part = chunk_mass(r, i, V, vec, sh_red);
-          if (t == 0) sh_part[i] = part;
+    unsigned long long *keys = P.keys + static_cast<size_t>(b) * nc;
+    // wait until every chunk mass of the row is published (re-reading only
+    // the missing ones); the bound keeps the wait finite
+    int polls = 0;
+    bool timed_out = false;
+    while (true) {
+      bool present = true;
+      for (int i = t; i < nc; i += kThreads) {
+        const unsigned long long key = load_agent(keys + i);
+        if (key == 0ull) present = false;
+        else sh_part[i] = __longlong_as_double(static_cast<long long>(key ^ kMassSentinel));
+      }
+      if (__syncthreads_and(present)) break;
+      if (++polls >= kMaxPolls) {
+        timed_out = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    for (int i = t; i < nc; i += kThreads) keys[i] = 0ull;   // ordered before the next call by the launch
+    if (timed_out) {
+      st |= SPEC_ST_INCOMPLETE;
+    } else {
+      typename Src::RowT r = Src::row(P, b, jrow, mode == MODE_RESID);
+      const bool vec = P.vec != 0;
+      const int per = (nc + kThreads - 1) / kThreads;  // chunks per lane, consecutive
+      const int c0 = t * per;
+      // total mass and each lane's exclusive prefix over the chunk masses
+      double pre = 0.0;
+      auto scan_parts = [&]() {
+        double mine = 0.0;
+        for (int i = 0; i < per; ++i)
+          if (c0 + i < nc) mine += sh_part[c0 + i];
+        pre = block_excl_scan_d(mine, sh_dscan, &S);
+      };
+      scan_parts();
+      if (isfinite(S) && !(S > 0.0)) {
+        st |= SPEC_ST_RESID_ZERO;
+        if (mode == MODE_RESID) {         // fall back to the target row p_j itself
+          r.resid = false;
+          for (int i = 0; i < nc; ++i) {
+            const double part = chunk_mass(r, i, V, vec, sh_red);
+            if (t == 0) sh_part[i] = part;
+          }
+          __syncthreads();
+          scan_parts();
+        }
+      }
+      if (!isfinite(S)) {
+        st |= SPEC_ST_NONFINITE;
+        tok = 0;
+      } else if (!(S > 0.0)) {
+        tok = 0;
+      } else {
+        const double T = static_cast<double>(u_draw) * S;
+        // the first chunk whose running mass exceeds T (else the last chunk with mass)
+        int cand = INT_MAX, last = -1;
+        {
+          double run = pre;
+          for (int i = 0; i < per; ++i) {
+            const int c = c0 + i;
+            if (c >= nc) break;
+            const double pc = sh_part[c];
+            if (pc > 0.0) last = c;
+            if (cand == INT_MAX && run + pc > T) cand = c;
+            run += pc;
+          }
+        }
+        const int wc = wave_min(cand), wl = wave_max_i(last);
+        if (lane == 0) {
+          sh_scan[w] = wc;
+          sh_last[w] = wl;
         }
         __syncthreads();
-        scan_parts();
-      }
-    }
-    if (!isfinite(S)) {
-      st |= SPEC_ST_NONFINITE;
-      tok = 0;
-    } else if (!(S > 0.0)) {
-      tok = 0;
-    } else {
-      const double T = static_cast<double>(u_draw) * S;
-      // the first chunk whose running mass exceeds T (else the last chunk with mass)
-      int cand = INT_MAX, last = -1;
-      {
-        double run = pre;
-        for (int i = 0; i < per; ++i) {
-          const int c = c0 + i;
-          if (c >= nc) break;
-          const double pc = sh_part[c];
-          if (pc > 0.0) last = c;
-          if (cand == INT_MAX && run + pc > T) cand = c;
-          run += pc;
+        if (t == 0) {
+          int best = INT_MAX, lp = -1;
+          for (int i = 0; i < kWaves; ++i) {
+            best = min(best, sh_scan[i]);
+            lp = max(lp, sh_last[i]);
+          }
+          sh_cs = best != INT_MAX ? best : lp;
         }
-      }
-      const int wc = wave_min(cand), wl = wave_max_i(last);
-      if (lane == 0) {
-        sh_scan[w] = wc;
-        sh_last[w] = wl;
-      }
-      __syncthreads();
-      if (t == 0) {
-        int best = INT_MAX, lp = -1;
-        for (int i = 0; i < kWaves; ++i) {
-          best = min(best, sh_scan[i]);
-          lp = max(lp, sh_last[i]);
+        __syncthreads();
+        const int cs = sh_cs;
+        if (cs >= c0 && cs < c0 + per) {                // the lane owning chunk cs: mass before it
+          double run = pre;
+          for (int c = c0; c < cs; ++c) run += sh_part[c];
+          sh_base = run;
         }
-        sh_cs = best != INT_MAX ? best : lp;
-      }
-      __syncthreads();
-      const int cs = sh_cs;
-      if (cs >= c0 && cs < c0 + per) {                // the lane owning chunk cs: mass before it
-        double run = pre;
-        for (int c = c0; c < cs; ++c) run += sh_part[c];
-        sh_base = run;
-      }
-      __syncthreads();
-      const double base = sh_base;
-      // in-chunk scan in index order: lane t owns kEPT consecutive entries
-      const int lo = cs * kChunk + t * kEPT;
-      float x[kEPT];
-      r.load16(x, lo, V, vec);
-      double mine = 0.0;
+        __syncthreads();
+        const double base = sh_base;
+        // in-chunk scan in index order: lane t owns kEPT consecutive entries
+        const int lo = cs * kChunk + t * kEPT;
+        float x[kEPT];
+        r.load16(x, lo, V, vec);
+        double mine = 0.0;
 #pragma unroll
-      for (int i = 0; i < kEPT; ++i) mine += static_cast<double>(x[i]);
-      double ctot;
-      double run = base + block_excl_scan_d(mine, sh_dscan, &ctot);
-      int cpos = INT_MAX, lastpos = -1;
+        for (int i = 0; i < kEPT; ++i) mine += static_cast<double>(x[i]);
+        double ctot;
+        double run = base + block_excl_scan_d(mine, sh_dscan, &ctot);
+        int cpos = INT_MAX, lastpos = -1;
 #pragma unroll
-      for (int i = 0; i < kEPT; ++i) {
-        const int v = lo + i;
-        if (v < V) {
-          if (x[i] > 0.0f) lastpos = v;
-          run += static_cast<double>(x[i]);
-          if (cpos == INT_MAX && run > T) cpos = v;
+        for (int i = 0; i < kEPT; ++i) {
+          const int v = lo + i;
+          if (v < V) {
+            if (x[i] > 0.0f) lastpos = v;
+            run += static_cast<double>(x[i]);
+            if (cpos == INT_MAX && run > T) cpos = v;
+          }
         }
-      }
-      const int wcp = wave_min(cpos), wlp = wave_max_i(lastpos);
-      if (lane == 0) {
-        sh_scan[w] = wcp;
-        sh_last[w] = wlp;
-      }
-      __syncthreads();
-      if (t == 0) {
-        int best = INT_MAX, lp = -1;
-        for (int i = 0; i < kWaves; ++i) {
-          best = min(best, sh_scan[i]);
-          lp = max(lp, sh_last[i]);
+        const int wcp = wave_min(cpos), wlp = wave_max_i(lastpos);
+        if (lane == 0) {
+          sh_scan[w] = wcp;
+          sh_last[w] = wlp;
         }
-        sh_tok = best != INT_MAX ? best : lp;
+        __syncthreads();
+        if (t == 0) {
+          int best = INT_MAX, lp = -1;
+          for (int i = 0; i < kWaves; ++i) {
+            best = min(best, sh_scan[i]);
+            lp = max(lp, sh_last[i]);
+          }
+          sh_tok = best != INT_MAX ? best : lp;
+        }
+        __syncthreads();
+        tok = sh_tok;
       }
-      __syncthreads();
-      tok = sh_tok;
     }
   }
   if (t < kp1) {                                      // accepted drafts, then the drawn token
@@ -481,7 +521,51 @@ __global__ __launch_bounds__(kThreads) void sample_draw_kernel(SampleParams P) {
   }
 }
 
+// Emit offsets: the finishers publish emit_count + 1 per sequence as soon as
+// their chains are known; one workgroup scans them and clears the slots.
+__device__ inline void finish_offsets(const SampleParams &P) {
+  __shared__ int sh[kWaves + 1];
+  const int n = P.B, T = kThreads;
+  const int per = (n + T - 1) / T;
+  const int lo = min(n, static_cast<int>(threadIdx.x) * per), hi = min(n, lo + per);
+  int polls = 0;
+  while (true) {
+    bool present = true;
+    for (int i = lo; i < hi; ++i) present = present && load_agent(P.ecnt + i) != 0;
+    if (__syncthreads_and(present)) break;
+    if (++polls >= kMaxPolls) break;              // outputs unspecified; the wait still ends
+    __builtin_amdgcn_s_sleep(1);
+  }
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += max(load_agent(P.ecnt + i) - 1, 0);
+  int total;
+  int base = block_excl_scan(s, sh, &total);
+  for (int i = lo; i < hi; ++i) {
+    P.emit_offsets[i] = base;
+    base += max(load_agent(P.ecnt + i) - 1, 0);
+    P.ecnt[i] = 0;
+  }
+  if (threadIdx.x == 0) P.emit_offsets[n] = total;
+}
+
+// One launch: B * chunks producers, then the B finishers, then (with
+// offsets) the offsets workgroup.  Workgroups are dispatched in index order,
+// so a waiting workgroup is dispatched only after every producer it waits on
+// (producers never wait).
+template <class Src>
+__global__ __launch_bounds__(kThreads) void sample_verify_kernel(SampleParams P) {
+  const int blk = blockIdx.x;
+  const int nprod = P.B * P.chunks;
+  if (blk < nprod) produce_chunk<Src>(P, blk / P.chunks, blk % P.chunks);
+  else if (blk < nprod + P.B) finish_sequence<Src>(P, blk - nprod);
+  else finish_offsets(P);
+}
+
 inline int sample_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+inline dim3 sample_grid(int B, int chunks, const void *emit_offsets) {
+  return dim3(static_cast<unsigned>(static_cast<long long>(B) * chunks + B + (emit_offsets ? 1 : 0)));
+}
 
 }  // namespace
 }  // namespace specv
@@ -506,8 +590,8 @@ extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t 
   const int chunks = sample_chunks(V);
   if (chunks > kMaxChunks) return SPEC_ECAPACITY;
   if (!aligned(p, 4) || !aligned(q, 4) || !aligned(uniforms, 4)) return SPEC_EINVAL;
-  const long long nblocks = static_cast<long long>(B) * chunks;
-  if (nblocks >= INT32_MAX || B >= INT32_MAX - 1) return SPEC_EINVAL;
+  const long long nblocks = static_cast<long long>(B) * (chunks + 1) + 1;
+  if (nblocks >= INT32_MAX) return SPEC_EINVAL;
   const SampleWs lay = sample_ws_layout(B, chunks);
   if (ws_bytes < lay.total || !aligned(ws, 256)) return SPEC_EWORKSPACE;
 
@@ -548,12 +632,11 @@ extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t 
   P.final_mass = final_mass;
   P.status = status;
   unsigned char *wb = static_cast<unsigned char *>(ws);
-  P.partial = reinterpret_cast<double *>(wb + lay.part);
-  P.chain = reinterpret_cast<int4 *>(wb + lay.chain);
+  P.keys = reinterpret_cast<unsigned long long *>(wb + lay.keys);
+  P.ecnt = reinterpret_cast<int32_t *>(wb + lay.ecnt);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(sample_chunk_kernel<DenseSrc>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
-  hipLaunchKernelGGL(sample_draw_kernel<DenseSrc>, dim3(static_cast<unsigned>(B) + 1u), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(sample_verify_kernel<DenseSrc>, sample_grid(B, chunks, emit_offsets), dim3(kThreads), 0, s, P);
   return launch_status();
 }
 
@@ -588,9 +671,9 @@ extern "C" int spec_verify_sample_logits(const void *target_logits, const void *
   if (chunks > kMaxChunks) return SPEC_ECAPACITY;
   const size_t elt = dt == SPEC_BF16 ? 2 : 4;
   if (!aligned(target_logits, elt) || !aligned(draft_logits, elt) || !aligned(uniforms, 4)) return SPEC_EINVAL;
-  const long long nblocks = static_cast<long long>(B) * chunks;
+  const long long nblocks = static_cast<long long>(B) * (chunks + 1) + 1;
   const long long rows = static_cast<long long>(B) * (2 * k + 1);
-  if (nblocks >= INT32_MAX || rows >= INT32_MAX || B >= INT32_MAX - 1) return SPEC_EINVAL;
+  if (nblocks >= INT32_MAX || rows >= INT32_MAX) return SPEC_EINVAL;
   const size_t stats_bytes = sample_logits_stats_bytes(B, k, V);
   const SampleWs lay = sample_ws_layout(B, chunks);
   if (ws_bytes < stats_bytes + lay.total || !aligned(ws, 256)) return SPEC_EWORKSPACE;
@@ -634,21 +717,18 @@ extern "C" int spec_verify_sample_logits(const void *target_logits, const void *
   P.emit_offsets = emit_offsets;
   P.final_mass = final_mass;
   P.status = status;
-  P.partial = reinterpret_cast<double *>(wb + stats_bytes + lay.part);
-  P.chain = reinterpret_cast<int4 *>(wb + stats_bytes + lay.chain);
+  P.keys = reinterpret_cast<unsigned long long *>(wb + stats_bytes + lay.keys);
+  P.ecnt = reinterpret_cast<int32_t *>(wb + stats_bytes + lay.ecnt);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dt == SPEC_BF16;
   (void)hipGetLastError();
   launch_proc_stats(target_logits, draft_logits, B * (k + 1), static_cast<int>(rows), V, bf16, P.invT,
                     top_k, top_p, stats, nullptr,
                     wb + round_up(static_cast<size_t>(rows) * sizeof(ProcStats), 256), s);
-  const dim3 g1(static_cast<unsigned>(nblocks)), g2(static_cast<unsigned>(B) + 1u), blk(kThreads);
-  if (bf16) {
-    hipLaunchKernelGGL(sample_chunk_kernel<LogitSrc<true>>, g1, blk, 0, s, P);
-    hipLaunchKernelGGL(sample_draw_kernel<LogitSrc<true>>, g2, blk, 0, s, P);
-  } else {
-    hipLaunchKernelGGL(sample_chunk_kernel<LogitSrc<false>>, g1, blk, 0, s, P);
-    hipLaunchKernelGGL(sample_draw_kernel<LogitSrc<false>>, g2, blk, 0, s, P);
-  }
+  const dim3 grid = sample_grid(B, chunks, emit_offsets), blk(kThreads);
+  if (bf16)
+    hipLaunchKernelGGL(sample_verify_kernel<LogitSrc<true>>, grid, blk, 0, s, P);
+  else
+    hipLaunchKernelGGL(sample_verify_kernel<LogitSrc<false>>, grid, blk, 0, s, P);
   return launch_status();
 }

@@ -21,8 +21,9 @@ def note(msg: str) -> None:
 
 
 def ws(nbytes: int, key=None):
-    """A cached zero-filled workspace of at least nbytes (greedy and tree
-    verification use their own keys: their workspace must stay zero-filled)."""
+    """A cached zero-filled workspace of at least nbytes.  Greedy, tree and
+    stochastic verification use keys of their own: their workspaces carry
+    completion flags and must stay zero-filled between calls."""
     key = key or "default"
     w = _WS.get(key)
     if w is None or w.numel() < nbytes:
@@ -68,7 +69,7 @@ def verify_sample(p_dev, q_dev, drafts, uniforms, eos_id=-1, remaining=None, ws_
                emit_offsets=torch.empty(B + 1, dtype=torch.int32, device=DEV),
                final_mass=torch.empty(B, dtype=torch.float64, device=DEV),
                status=torch.empty(B, dtype=torch.int32, device=DEV))
-    w = ws(sv.spec_verify_sample_workspace_bytes(B, k, V), ws_key)
+    w = ws(sv.spec_verify_sample_workspace_bytes(B, k, V), ("sample", ws_key))
     d = drafts if torch.is_tensor(drafts) else i32(drafts)
     u = uniforms if torch.is_tensor(uniforms) else torch.from_numpy(np.ascontiguousarray(uniforms, np.float32)).to(DEV)
     rem = None if remaining is None else i32(remaining)
@@ -146,7 +147,7 @@ def verify_sample_logits(zp_dev, zq_dev, drafts, uniforms, T, top_k=0, top_p=1.0
                emit_offsets=torch.empty(B + 1, dtype=torch.int32, device=DEV),
                final_mass=torch.empty(B, dtype=torch.float64, device=DEV),
                status=torch.empty(B, dtype=torch.int32, device=DEV))
-    w = ws(sv.spec_verify_sample_logits_workspace_bytes(B, k, V), ws_key)
+    w = ws(sv.spec_verify_sample_logits_workspace_bytes(B, k, V), ("sample_logits", ws_key))
     d = drafts if torch.is_tensor(drafts) else i32(drafts)
     u = uniforms if torch.is_tensor(uniforms) else torch.from_numpy(np.ascontiguousarray(uniforms, np.float32)).to(DEV)
     rem = None if remaining is None else i32(remaining)

@@ -342,11 +342,19 @@ def test_verify_from_logits_repeatable():
     d = rng.integers(0, g["V"], size=(4, g["k"])).astype(np.int32)
     note("verify logits repeatable")
     first = host(verify_sample_logits(zt, zd_, d, g["uniforms"], 0.7, 40, 0.9, ws_key="vl"))
+    # the leading part (row statistics, candidate lists) is rewritten by
+    # every call, whatever it holds; the trailing completion flags are left
+    # zero-filled by every call
+    B, k, V = 4, g["k"], g["V"]
+    flags = sv.spec_verify_sample_workspace_bytes(B, k, V)
+    lead = sv.spec_verify_sample_logits_workspace_bytes(B, k, V) - flags
+    w = _WS[("sample_logits", "vl")]
     for it in range(6):
-        _WS["vl"].fill_(0x5A)
+        w[:lead].fill_(0x5A)
         again = host(verify_sample_logits(zt, zd_, d, g["uniforms"], 0.7, 40, 0.9, ws_key="vl"))
         for key in first:
             assert np.array_equal(first[key], again[key]), key
+        assert int(torch.count_nonzero(w[lead:lead + flags]).item()) == 0
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -229,18 +229,21 @@ def test_anomalies_and_stops():
     assert got["status"][0] & oracle.ST_DRAFT_OOR
 
 
-def test_repeatable_bitwise():
-    note("sample repeat x20")
+def test_repeatable_bitwise_and_workspace_left_zero():
+    """20 calls on one workspace give identical outputs, and every call leaves
+    the workspace zero-filled (the completion flags of the next call)."""
+    note("sample repeat x20, workspace zero after each call")
     r = W.sample_round(2, round_=5, B=4)
     P, Q = _dev(r["p"]), _dev(r["q"])
     first = host(verify_sample(P, Q, r["drafts"], r["uniforms"], ws_key="srep"))
     from tests._gpu import _WS
+    w = _WS[("sample", "srep")]
+    assert int(torch.count_nonzero(w).item()) == 0
     for it in range(19):
-        if it % 5 == 0:
-            _WS["srep"].fill_(0x7F)               # workspace contents on entry are ignored
         again = host(verify_sample(P, Q, r["drafts"], r["uniforms"], ws_key="srep"))
         for key in first:
             assert np.array_equal(first[key], again[key]), key
+        assert int(torch.count_nonzero(w).item()) == 0
 
 
 def test_largest_k():
