@@ -40,6 +40,7 @@ from .realign import commit_bookkeeping, position_and_mask, commit_realign, resy
 from .group import group_same_length  # noqa: F401
 from .paged import commit_paged  # noqa: F401
 from .tree import tree_verify, compact_tree_slots  # noqa: F401
+from .tree_sample import tree_sample_verify  # noqa: F401
 from .unbatched import UnbatchedModel, check_ragged  # noqa: F401
 from .ragged import repad_kv, unpad_kv, ragged_bytes  # noqa: F401
 from .policy import eqspec_round, exspec_round  # noqa: F401
