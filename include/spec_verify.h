@@ -427,6 +427,58 @@ int spec_compact_tree_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, in
                          int32_t *status, spec_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * Stochastic verification of a candidate tree.
+ * [Forensics] 5 names tree verification and [Walkthrough] 5.2 lists the draft
+ * tokens and their draft probabilities among a tree verifier's fields, but
+ * neither gives the sampling rule.  This call implements multi-draft
+ * speculative sampling: the children of a node, drawn independently from the
+ * draft's distribution q at that node, are tried in sibling order against the
+ * current residual of the target row there ([Atlas] Acceptance and rejection
+ * correction; [Walkthrough] 5.1); every rejection replaces the residual by the
+ * normalised positive part of (residual - q); an accepted child becomes the
+ * current node; when no child is accepted, or at a leaf, one token is drawn
+ * from the current residual and the round stops.  Every emitted token then
+ * follows the target's row at its node.  A chain tree is exactly
+ * spec_verify_sample.
+ *   Residual mass vectors at the current node after i rejections: R_0 = p as
+ *   given; R_1 = max(p - q, 0) in float32; R_j = max(R_{j-1} - q * m_{j-1}, 0)
+ *   in float64 with m_j = sum of R_j (each operation separately rounded).  The
+ *   first try compares u with min(1, p(x)/q(x)) (one float32 division); a try
+ *   after i >= 1 rejections compares u with min(1, R_i(x) / (m_i * q(x))) in
+ *   float64.  A rejection whose residual has no mass keeps the previous one
+ *   (SPEC_ST_RESID_ZERO); a non-finite residual mass ends the round with token 0
+ *   (SPEC_ST_NONFINITE).  Draws are the inverse CDF of spec_verify_sample.
+ *   Trees, links, EOS, the budget and SPEC_ST_BAD_STATE are as in
+ *   spec_verify_tree; q(x) == 0 and out-of-range drafts as in
+ *   spec_verify_sample.
+ *
+ *   p            [B, N, V] float32: p[b, i] is the target's distribution after
+ *                the path ending at node i
+ *   q            [B, N, V] float32: q[b, i] is the draft's distribution at node
+ *                i, which its children were drawn from (unused at leaves)
+ *   draft, first_child, next_sibling  [B, N] int32 (draft[b, 0] is ignored)
+ *   uniforms     [B, N] float32 in [0, 1): u[b, c] (c >= 1) decides the try
+ *                of node c; u[b, 0] is the single draw
+ *   out_tokens   [B, N] out, -1 padded; accept_len, emit_count [B] out
+ *   path         [B, N] out, -1 padded: the nodes whose rows were read (their
+ *                KV slots are kept; spec_compact_tree_kv applies)
+ *   emit_offsets [B + 1] out or NULL; final_mass [B] float64 out or NULL: the
+ *                mass S of the vector drawn from, 0 without a draw
+ *   status       [B] out or NULL
+ * No workspace.  One workgroup per sequence walks its tree; each rejection
+ * reads the node's p and q rows once.
+ * Errors: SPEC_EINVAL for NULL required pointers, B, N or V < 1, misaligned
+ * p, q or uniforms (4 bytes), overlapping outputs; SPEC_ECAPACITY for
+ * N > SPEC_TREE_MAX_N or V > 4194304.
+ * ------------------------------------------------------------------------ */
+int spec_verify_tree_sample(const float *p, const float *q, const int32_t *draft,
+                            const int32_t *first_child, const int32_t *next_sibling,
+                            const float *uniforms, int B, int N, int V, int32_t eos_id,
+                            const int32_t *remaining, int32_t *accept_len, int32_t *emit_count,
+                            int32_t *out_tokens, int32_t *path, int32_t *emit_offsets,
+                            double *final_mass, int32_t *status, spec_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Same-length grouping of a window of ragged sequences.
  * [Forensics] 3.2 (EXSPEC: batches of identical-length sequences drawn from a
  * window larger than the batch size, with unpad-append-repad as the fallback).

@@ -25,7 +25,7 @@ __all__ = [
     "spec_verify_sample_workspace_bytes", "spec_verify_sample", "spec_process_workspace_bytes",
     "spec_process_logits", "spec_verify_sample_logits_workspace_bytes", "spec_verify_sample_logits",
     "spec_commit_realign_kv", "spec_resync_draft_kv", "spec_repad_kv", "spec_unpad_kv", "spec_commit_paged",
-    "spec_verify_tree_workspace_bytes", "spec_verify_tree", "spec_compact_tree_kv",
+    "spec_verify_tree_workspace_bytes", "spec_verify_tree", "spec_compact_tree_kv", "spec_verify_tree_sample",
     "spec_group_same_length", "workspace", "library",
 ]
 
@@ -301,6 +301,24 @@ def spec_verify_tree(logits, draft, first_child, next_sibling, accept_len, emit_
         _arg(path, "int32", B * N, "path"), _arg(emit_offsets, "int32", B + 1, "emit_offsets", True),
         _arg(status, "int32", B, "status", True), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(code, "spec_verify_tree")
+
+
+def spec_verify_tree_sample(p, q, draft, first_child, next_sibling, uniforms, accept_len, emit_count,
+                            out_tokens, path, *, eos_id: int = -1, remaining=None, emit_offsets=None,
+                            final_mass=None, status=None, stream=None) -> None:
+    """p, q [B, N, V] f32; draft, first_child, next_sibling [B, N] int32; uniforms [B, N] f32."""
+    B, N, V = p.shape
+    code = library().spec_verify_tree_sample(
+        _arg(p, "float32", B * N * V, "p"), _arg(q, "float32", B * N * V, "q"),
+        _arg(draft, "int32", B * N, "draft"), _arg(first_child, "int32", B * N, "first_child"),
+        _arg(next_sibling, "int32", B * N, "next_sibling"), _arg(uniforms, "float32", B * N, "uniforms"),
+        B, N, V, int(eos_id), _arg(remaining, "int32", B, "remaining", True),
+        _arg(accept_len, "int32", B, "accept_len"), _arg(emit_count, "int32", B, "emit_count"),
+        _arg(out_tokens, "int32", B * N, "out_tokens"), _arg(path, "int32", B * N, "path"),
+        _arg(emit_offsets, "int32", B + 1, "emit_offsets", True),
+        _arg(final_mass, "float64", B, "final_mass", True), _arg(status, "int32", B, "status", True),
+        _stream(stream))
+    _check(code, "spec_verify_tree_sample")
 
 
 def spec_compact_tree_kv(kv, N: int, end_col, path, emit_count, *, status=None, stream=None) -> None:

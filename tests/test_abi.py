@@ -229,6 +229,33 @@ def test_compact_argument_errors(args, code):
     assert LIB.spec_compact_tree_kv(*args) == code
 
 
+I_, J_, K_ = (ctypes.c_void_p(0x10000 * (i + 9)) for i in range(3))
+
+
+def _tree_sample_args(**kw):
+    a = dict(p=A, q=B_, draft=C_, fc=D_, ns=E_, u=F_, B=2, N=4, V=100, eos=-1, rem=N, acc=G_, emit=H_,
+             toks=I_, path=J_, offs=K_, mass=N, st=N, stream=N)
+    a.update(kw)
+    return tuple(a.values())
+
+
+@needs_lib
+@pytest.mark.parametrize("args,code", [
+    (_tree_sample_args(p=N), sv.SPEC_EINVAL),                       # NULL p
+    (_tree_sample_args(path=N), sv.SPEC_EINVAL),                    # NULL path
+    (_tree_sample_args(B=0), sv.SPEC_EINVAL),
+    (_tree_sample_args(N=0), sv.SPEC_EINVAL),
+    (_tree_sample_args(V=0), sv.SPEC_EINVAL),
+    (_tree_sample_args(N=300), sv.SPEC_ECAPACITY),                 # N > SPEC_TREE_MAX_N
+    (_tree_sample_args(V=(1 << 22) + 1), sv.SPEC_ECAPACITY),       # more chunks than one workgroup holds
+    (_tree_sample_args(q=ctypes.c_void_p(0x20002)), sv.SPEC_EINVAL),   # misaligned q
+    (_tree_sample_args(toks=G_), sv.SPEC_EINVAL),                  # outputs alias
+    (_tree_sample_args(path=C_), sv.SPEC_EINVAL),                  # output over an input
+])
+def test_tree_sample_argument_errors(args, code):
+    assert LIB.spec_verify_tree_sample(*args) == code
+
+
 @needs_lib
 @pytest.mark.parametrize("args,code", [
     ((N, 10, 8, 2, B_, C_, D_, E_, F_, N), sv.SPEC_EINVAL),

@@ -19,6 +19,7 @@ from .configs import (  # noqa: F401
     planted_greedy,
     random_tree,
     planted_tree,
+    sampled_tree,
     greedy_round,
     sample_round,
     sample_logits,

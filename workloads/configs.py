@@ -206,6 +206,34 @@ def sample_round(c: int, round_: int = 0, batch: int = 0, B: int | None = None,
     return dict(p=p, q=q, drafts=drafts, uniforms=u, B=B, k=k, V=V)
 
 
+def sampled_tree(rng: np.random.Generator, B: int, N: int, V: int, z_sd: float = 3.0, eps_sd: float = 1.0,
+                 temperature: float = 0.7, branching: int = 3) -> dict:
+    """Candidate trees for stochastic tree verification: per sequence a
+    random_tree of N nodes; per node a target row p = softmax(z / T) and a
+    draft row q = softmax((z + eps) / T) (z ~ N(0, z_sd), eps ~ N(0, eps_sd),
+    float32); node c > 0 proposes an id drawn from q of its parent by inverse
+    CDF (drafting, outside the step under test), so siblings are independent
+    draws; uniforms [B, N] float32 in [0, 1)."""
+    z = rng.standard_normal((B, N, V), dtype=np.float32)
+    z *= np.float32(z_sd)
+    eps = rng.standard_normal((B, N, V), dtype=np.float32)
+    eps *= np.float32(eps_sd)
+    p = _softmax_f32(z.astype(np.float64) / temperature)
+    q = _softmax_f32((z.astype(np.float64) + eps.astype(np.float64)) / temperature)
+    del z, eps
+    fc = np.full((B, N), -1, np.int32)
+    ns = np.full((B, N), -1, np.int32)
+    draft = np.zeros((B, N), np.int32)
+    ud = rng.random((B, N))
+    for b in range(B):
+        parent, fc[b], ns[b] = random_tree(rng, N, branching)
+        for c in range(1, N):
+            cq = np.cumsum(q[b, parent[c]].astype(np.float64))
+            draft[b, c] = min(int(np.searchsorted(cq, ud[b, c] * cq[-1], side="right")), V - 1)
+    u = rng.random((B, N), dtype=np.float32)
+    return dict(p=p, q=q, draft=draft, first_child=fc, next_sibling=ns, uniforms=u, B=B, N=N, V=V)
+
+
 def sample_logits(c: int, round_: int = 0, batch: int = 0, B: int | None = None,
                   V: int | None = None, k: int | None = None) -> dict:
     """Raw logits of the stochastic workloads before any processing: target
