@@ -686,6 +686,38 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
                           **_rates(t, th, nbytes), "rows_per_s": B3 * NT / t,
                           "mean_accept_len": sum(accs) / nbt}
     del trees, wst
+    # stochastic tree verification: 16-node trees whose siblings are draws
+    # from the parent's q, float32 p and q over the stochastic workload's
+    # vocabulary, rotating over 3 input sets (467 MB)
+    Bs, Ns, Vs, nbs = 8, 16, W.workload(2)["V"], 3
+    rng_s = W.stream(2, "tree", 0, 0)
+    sets = []
+    for i in range(nbs):
+        gs_ = W.sampled_tree(rng_s, Bs, Ns, Vs)
+        sets.append([torch.from_numpy(gs_["p"]).to(dev), torch.from_numpy(gs_["q"]).to(dev)] +
+                    [torch.from_numpy(gs_[key]).to(dev) for key in ("draft", "first_child", "next_sibling",
+                                                                   "uniforms")])
+        del gs_
+    accs_, emits_ = torch.empty(Bs, **i32), torch.empty(Bs, **i32)
+    toks_, paths_, offs_ = torch.empty(Bs, Ns, **i32), torch.empty(Bs, Ns, **i32), torch.empty(Bs + 1, **i32)
+    its = itertools.count()
+
+    def tree_sample_call():
+        ps, qs, ds, fcs, nss, us = sets[next(its) % nbs]
+        sv.spec_verify_tree_sample(ps, qs, ds, fcs, nss, us, accs_, emits_, toks_, paths_, emit_offsets=offs_)
+
+    t, th = _time_calls(torch, tree_sample_call, 22, inner=3 * nbs)
+    acc_s, emit_s = [], []
+    for i in range(nbs):
+        tree_sample_call()
+        acc_s.append(float(accs_.float().mean().item()))
+        emit_s.append(float(emits_.float().mean().item()))
+    out["tree_sample_verify"] = {
+        "workload": f"stochastic tree verify, B={Bs} N={Ns} nodes (parents among the 3 below, siblings drawn "
+                    f"from the parent's q), V={Vs} f32 p/q, {nbs} rotating input sets",
+        "us_per_call": t * 1e6, "us_per_call_host": th * 1e6,
+        "mean_accept_len": sum(acc_s) / nbs, "mean_emit_count": sum(emit_s) / nbs}
+    del sets
     # compaction of the last buffer's paths; successive calls use end columns
     # NT apart, so 48 calls touch 48 disjoint column ranges (more than the
     # last-level cache holds) and each call moves cold bytes

@@ -43,7 +43,7 @@ WORKLOADS = [
 _STREAM_IDS = {
     "lengths": 1, "alpha": 2, "logits": 3, "drafts": 4, "uniforms": 5,
     "kv": 6, "tokens": 7, "eps": 8, "pool": 9, "accept": 10,
-    "policy_logits": 11, "policy_drafts": 12,
+    "policy_logits": 11, "policy_drafts": 12, "tree": 13,
 }
 
 
