@@ -225,7 +225,8 @@ def _traffic_md(t: dict) -> str:
 
 
 def _trace_rows(directory: str):
-    """(kernel label, grid) -> durations in us from a rocprofv3 kernel trace."""
+    """(kernel label, grid) -> (durations in us, start times) from a rocprofv3
+    kernel trace, for the library's kernels and the copy probe."""
     import csv
     import re
     acc = {}
@@ -240,27 +241,37 @@ def _trace_rows(directory: str):
                     label = "torch neg (copy probe)"
                 else:
                     continue
-                d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-                acc.setdefault((label, int(r["Grid_Size_X"] if "Grid_Size_X" in r else r.get("Grid_Size", 0))),
-                               []).append(d)
+                t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+                grid = int(r["Grid_Size_X"] if "Grid_Size_X" in r else r.get("Grid_Size", 0))
+                d = acc.setdefault((label, grid), ([], []))
+                d[0].append((t1 - t0) / 1e3)
+                d[1].append(t0)
     return acc
 
 
 def summarize_trace(trace_dir: str, bench_log: str) -> None:
     """Write the committed kernel-duration summary from a rocprofv3
-    --kernel-trace run of the default bench and that run's output."""
+    --kernel-trace run of the default bench and that run's output.  Launches
+    before the copy probe are the step workload's own (the timed steps, the
+    back-to-back verify launches and the parity check); they are marked."""
     acc = _trace_rows(trace_dir)
     b = _bench_line(bench_log)
+    probe = [min(v[1]) for (k, _), v in acc.items() if k.startswith("torch neg")]
+    t_probe = min(probe) if probe else None
     out = ["# Kernel durations: verify + realign, B=32 k=8 V=128256, bf16 KV 32x8x128 (~18 GB)", "",
            "Command (MI355X, one GPU; R is the repository root):", "", "```",
            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/trace -o run "
            "-- python3 $R/bench.py > $R/gpurun_out/trace.log",
            "python3 $R/bench.py --summarize-trace $R/gpurun_out/trace $R/gpurun_out/trace.log", "```", "",
-           "Every launch of the library's kernels in that run (the step loop, the back-to-back verify launches, "
-           "the secondary measurements and the batch-size sweeps), grouped by kernel and grid size:", "",
-           "| kernel | grid | calls | avg (us) | min (us) | max (us) |", "|---|---|---|---|---|---|"]
-    for (k, g), v in sorted(acc.items(), key=lambda x: -sum(x[1])):
-        out.append(f"| `{k}` | {g} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+           "Every launch of the library's kernels in that run, grouped by kernel and grid size. Rows marked "
+           "**step** hold only launches of the B=32 k=8 V=128256 step workload: the warm-up and timed steps, "
+           "the back-to-back verify launches and the parity check, all before the copy probe. The other rows "
+           "are the secondary measurements and the batch-size sweeps.", "",
+           "| kernel | grid | calls | avg (us) | min (us) | max (us) | |", "|---|---|---|---|---|---|---|"]
+    for (k, g), (v, starts) in sorted(acc.items(), key=lambda x: -sum(x[1][0])):
+        step = t_probe is not None and max(starts) < t_probe and not k.startswith("torch neg")
+        out.append(f"| `{k}` | {g} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+                   f"{'**step**' if step else ''} |")
     rf, rv = b["roofline"], b["roofline_verify"]
     out += ["", "From the bench line of the same run (HIP events on the launch stream):", "",
             f"- value {b['value']:.0f} rows/s, {b['ms_per_step']:.3f} ms per step",

@@ -117,10 +117,11 @@ def test_trace_summary(tmp_path, monkeypatch):
     with open(d / "run_kernel_trace.csv", "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size_X", "Start_Timestamp", "End_Timestamp"])
         w.writeheader()
-        for i, n in enumerate(names):
+        for i, n in enumerate(names):                 # the probe (i = 2) starts at 10^6
             for j in range(2):
-                w.writerow(dict(Kernel_Name=n, Grid_Size_X=64 * (i + 1), Start_Timestamp=1000 * j,
-                                End_Timestamp=1000 * j + 2000 * (i + 1) + 1000 * j))
+                t0 = 1000 * j + (10 ** 6 if i >= 2 else 0) + (10 ** 7 if i == 1 and j == 1 else 0)
+                w.writerow(dict(Kernel_Name=n, Grid_Size_X=64 * (i + 1), Start_Timestamp=t0,
+                                End_Timestamp=t0 + 2000 * (i + 1) + 1000 * j))
     logp = tmp_path / "trace.log"
     logp.write_text(json.dumps({"value": 1.0, "ms_per_step": 2.0, "realign_ms_per_call": 3.0,
                                 "verify_us_per_launch": 18.0, "copy_probe_GBps": 6000.0,
@@ -129,8 +130,9 @@ def test_trace_summary(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRACE_MD", str(tmp_path / "k.md"))
     bench.summarize_trace(str(tmp_path / "trace"), str(logp))
     md = (tmp_path / "k.md").read_text()
-    assert "| `realign_kernel<16, int>` | 64 | 2 | 2.50 | 2.00 | 3.00 |" in md
-    assert "| `greedy_verify_kernel<true>` | 128 | 2 | 4.50 | 4.00 | 5.00 |" in md
+    assert "| `realign_kernel<16, int>` | 64 | 2 | 2.50 | 2.00 | 3.00 | **step** |" in md
+    # one launch after the probe: not only the step workload's
+    assert "| `greedy_verify_kernel<true>` | 128 | 2 | 4.50 | 4.00 | 5.00 |  |" in md
     assert "torch neg (copy probe)" in md and "some_other_kernel" not in md
 
 
