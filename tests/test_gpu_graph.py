@@ -68,18 +68,37 @@ def test_stochastic_verify_replay(K, P):
     p, q = torch.from_numpy(r["p"]).to(DEV), torch.from_numpy(r["q"]).to(DEV)
     d, u = i32(r["drafts"]), torch.from_numpy(r["uniforms"]).to(DEV)
     out = [torch.empty(B, dtype=torch.int32, device=DEV), torch.empty(B, dtype=torch.int32, device=DEV),
-           torch.empty(B, k + 1, dtype=torch.int32, device=DEV), torch.empty(B, dtype=torch.float64, device=DEV)]
+           torch.empty(B, k + 1, dtype=torch.int32, device=DEV), torch.empty(B, dtype=torch.float64, device=DEV),
+           torch.empty(B + 1, dtype=torch.int32, device=DEV)]
     ws = sv.workspace(sv.spec_verify_sample_workspace_bytes(B, k, V), DEV)
     note("graph: stochastic verify")
-    _replay_matches(lambda: sv.spec_verify_sample(p, q, d, u, out[0], out[1], out[2], ws, final_mass=out[3]), out)
+    _replay_matches(lambda: sv.spec_verify_sample(p, q, d, u, out[0], out[1], out[2], ws, final_mass=out[3],
+                                                  emit_offsets=out[4]), out)
+    assert int(torch.count_nonzero(ws).item()) == 0          # the completion flags are clear again
     g = W.sample_logits(2, B=4)
     zt = torch.from_numpy(g["zt"]).to(DEV).to(torch.bfloat16)
     zd = torch.from_numpy(g["zd"]).to(DEV).to(torch.bfloat16)
     wsl = sv.workspace(sv.spec_verify_sample_logits_workspace_bytes(B, k, V), DEV)
     note(f"graph: stochastic verify from logits K={K} P={P}")
     _replay_matches(lambda: sv.spec_verify_sample_logits(zt, zd, d, u, out[0], out[1], out[2], wsl,
-                                                         temperature=0.7, top_k=K, top_p=P, final_mass=out[3]),
+                                                         temperature=0.7, top_k=K, top_p=P, final_mass=out[3],
+                                                         emit_offsets=out[4]),
                     out)
+
+
+def test_tree_sample_replay():
+    rng = np.random.default_rng(12)
+    g = W.sampled_tree(rng, 6, 10, 5000)
+    B, N = 6, 10
+    p, q = torch.from_numpy(g["p"]).to(DEV), torch.from_numpy(g["q"]).to(DEV)
+    d, fc, ns = i32(g["draft"]), i32(g["first_child"]), i32(g["next_sibling"])
+    u = torch.from_numpy(g["uniforms"]).to(DEV)
+    out = [torch.empty(B, dtype=torch.int32, device=DEV), torch.empty(B, dtype=torch.int32, device=DEV),
+           torch.empty(B, N, dtype=torch.int32, device=DEV), torch.empty(B, N, dtype=torch.int32, device=DEV),
+           torch.empty(B + 1, dtype=torch.int32, device=DEV), torch.empty(B, dtype=torch.float64, device=DEV)]
+    note("graph: stochastic tree verify")
+    _replay_matches(lambda: sv.spec_verify_tree_sample(p, q, d, fc, ns, u, out[0], out[1], out[2], out[3],
+                                                       emit_offsets=out[4], final_mass=out[5]), out)
 
 
 def test_paged_and_grouping_replay():
