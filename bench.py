@@ -279,7 +279,10 @@ def summarize_trace(trace_dir: str, bench_log: str) -> None:
             f"{rf['frac']:.3f} of 8 TB/s",
             f"- `greedy_verify_kernel` (the whole verify call): {b['verify_us_per_launch']:.2f} us per launch, "
             f"{rv['achieved']:.0f} GB/s, {rv['frac']:.3f} of 8 TB/s",
-            f"- copy probe (torch int32 negation, 2 GiB each way): {b['copy_probe_GBps']:.0f} GB/s", ""]
+            f"- copy probe (torch int32 negation, 2 GiB each way): {b['copy_probe_GBps']:.0f} GB/s", "",
+            "Under the tracer every dispatch carries the tracer's own overhead, so the bench's back-to-back "
+            "timings in a traced run are slower than untraced ones; the kernel rows above are the kernels' own "
+            "durations, to set beside an untraced bench line.", ""]
     with open(TRACE_MD, "w") as f:
         f.write("\n".join(out))
     print("\n".join(out))
