@@ -418,6 +418,29 @@ def main() -> int:
     t_launch = a_ev.elapsed_time(b_ev) * 1e-3 / n_back
     log(f"verify launch {t_launch * 1e6:.2f} us (back-to-back)")
 
+    # Reference for the verify call's floor: the framework's own reductions
+    # over the same bytes (every logit of the same rotating buffers, the same
+    # back-to-back timing).  Not part of the step.
+    stream_ref = None
+    if not args.step_only:
+        stream_ref = {}
+        flat = [x.view(rows, V) for x in logits]
+        for name, fn in (("torch.amax", lambda x: torch.amax(x, dim=-1)),
+                         ("torch.argmax", lambda x: torch.argmax(x, dim=-1))):
+            for i in range(nbuf):
+                fn(flat[i])
+            torch.cuda.synchronize()
+            a_r, b_r = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_r.record()
+            for i in range(n_back):
+                fn(flat[i % nbuf])
+            b_r.record()
+            torch.cuda.synchronize()
+            t_r = a_r.elapsed_time(b_r) * 1e-3 / n_back
+            stream_ref[name] = {"us_per_call": t_r * 1e6, "GBps": rows * V * 2 / t_r / 1e9,
+                                "frac_of_peak": rows * V * 2 / t_r / PEAK_HBM}
+        log("stream reference: " + ", ".join(f"{k} {v['us_per_call']:.2f} us" for k, v in stream_ref.items()))
+
     # parity guard: one more verify of buffer 0 against the oracle (outside the timed region)
     import oracle
     sv.spec_verify_greedy(logits[0], drafts[0], acc, emit, toks, ws, emit_offsets=offs)
@@ -497,6 +520,7 @@ def main() -> int:
                             "traffic_requests": traffic_bytes("greedy_verify_kernel", requests=True),
                             "algorithmic_bytes_per_launch": ver_bytes,
                             "timing": f"HIP events around {n_back} back-to-back launches over the rotating buffers"},
+        "verify_stream_reference": stream_ref,
         "verify_rows_per_s": rows / t_launch,
         "verify_us_per_launch": t_launch * 1e6,
         "verify_us_per_call_in_step": statistics.mean(t_ver) * 1e6,
