@@ -14,9 +14,9 @@
 // It is a pure copy bound by HBM bandwidth (read + write of every moved byte).
 //   * One workgroup per moving plane.  The moved bytes form one contiguous
 //     range; the workgroup walks it from the right end to the left in tiles of
-//     kThreads * kTileVec 16-byte vectors (64 KB), consecutive lanes on
-//     consecutive vectors, with non-temporal loads and stores (every byte is
-//     touched once).
+//     kThreads * kTileVec 16-byte vectors (112 KB for the wide walker),
+//     consecutive lanes on consecutive vectors, with non-temporal loads and
+//     stores (every byte is touched once).
 //   * In-place overlap: a tile is loaded into registers, every lane waits for
 //     its loads to land, a workgroup barrier follows, and only then is the
 //     tile stored delta columns to the right.  The tile to its left is loaded
@@ -30,6 +30,11 @@
 //     of memory.  Many narrow walkers (several per CU, each on its own plane
 //     far from the others) keep more DRAM pages open at once and measured
 //     about 10% slower on MI355X; so did longest-move-first dispatch.
+//   * Planes smaller than one wide tile take narrow walkers instead (256
+//     lanes, 16 KB tiles, no reservation, several per CU): there a wide tile
+//     leaves most lanes idle and one plane per CU leaves the memory system
+//     idle between planes (a draft cache of 64-token prefixes re-synced 3x
+//     faster).
 //   * A plane's workgroup reads its own sequence first and issues its first
 //     tile's loads before reducing the batch-wide state (M, validity): the
 //     source range does not depend on M.
@@ -41,10 +46,14 @@
 namespace specv {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kTileVec = 7;              // 16-byte vectors per lane per tile (112 KB tiles)
-constexpr int kReserveWords = 24 * 1024; // 96 KB of the CU's 160 KB LDS: one workgroup per CU
+// Walker shapes: lanes, 16-byte vectors per lane per tile, LDS words reserved
+// (limiting residency, holding no data).
+struct WalkWide {                        // 112 KB tiles; 96 KB of the CU's 160 KB LDS: one per CU
+  static constexpr int kThreads = 1024, kTileVec = 7, kReserveWords = 24 * 1024;
+};
+struct WalkNarrow {                      // 16 KB tiles; several per CU
+  static constexpr int kThreads = 256, kTileVec = 4, kReserveWords = 0;
+};
 
 struct RealignParams {
   unsigned char *kv;
@@ -108,7 +117,9 @@ __device__ inline void stream_st(uint2 v, uint2 *p) {
 
 // Shared by every workgroup: E, M = max e_b and whether the state is valid.
 // Every workgroup computes the same values from the same inputs.
+template <class W>
 __device__ inline void commit_state(const RealignParams &P, int *sh, int &E, int &M, bool &ok) {
+  constexpr int kWaves = W::kThreads / kWave;
   E = P.end_col[0];
   int bad = (E < 0 || E > P.C - P.slots) ? 1 : 0;
   int m = 0;
@@ -155,9 +166,10 @@ __device__ inline VT *cell(unsigned char *pb, IT i) {
 // bounds whatever the rest of the batch holds; nothing is stored unless the
 // whole batch is valid.  IT indexes vectors within the plane: int when the
 // plane is under 2 GiB, long long otherwise.
-template <int VB, typename IT>
+template <class W, int VB, typename IT>
 __device__ inline void move_plane(const RealignParams &P, int p, int b, int *sh) {
   using VT = typename VecOf<VB>::T;
+  constexpr int kThreads = W::kThreads, kTileVec = W::kTileVec;
   const int E0 = P.end_col[0];
   const int n = P.kv_len_in[b], e_in = P.emit_count[b];
   const int e = min(e_in, P.slots);
@@ -188,7 +200,7 @@ __device__ inline void move_plane(const RealignParams &P, int p, int b, int *sh)
   }
   int E, M;
   bool ok;
-  commit_state(P, sh, E, M, ok);           // barriers: every lane of the workgroup gets here
+  commit_state<W>(P, sh, E, M, ok);        // barriers: every lane of the workgroup gets here
   if (!ok || !may_move || M == e) return;  // uniform in the workgroup
   const IT shift = static_cast<IT>(M - e) * per_col;
   // One step: load the tile left of `hi` (after the last tile: the first
@@ -213,22 +225,25 @@ __device__ inline void move_plane(const RealignParams &P, int p, int b, int *sh)
   }
 }
 
-template <int VB, typename IT>
-__global__ __launch_bounds__(kThreads) void realign_kernel(RealignParams P) {
+template <class W, int VB, typename IT>
+__global__ __launch_bounds__(W::kThreads) void realign_kernel(RealignParams P) {
+  constexpr int kThreads = W::kThreads, kWaves = kThreads / kWave;
   __shared__ int sh[2 * kWaves];
   __shared__ long long sh_bytes[kWaves];
-  __shared__ uint32_t sh_reserve[kReserveWords];
-  asm volatile("" ::"s"(sh_reserve));      // keep the reservation (it limits residency, holds no data)
+  if constexpr (W::kReserveWords > 0) {
+    __shared__ uint32_t sh_reserve[W::kReserveWords];
+    asm volatile("" ::"s"(sh_reserve));    // keep the reservation (it limits residency, holds no data)
+  }
   const int blk = blockIdx.x;
   const int t = threadIdx.x;
   if (blk > P.B) {                         // one plane, address order: p = ((l * 2 + kv) * B + b) * H + h
     const int p = blk - P.B - 1;
-    move_plane<VB, IT>(P, p, (p / P.H) % P.B, sh);
+    move_plane<W, VB, IT>(P, p, (p / P.H) % P.B, sh);
     return;
   }
   int E, M;
   bool ok;
-  commit_state(P, sh, E, M, ok);
+  commit_state<W>(P, sh, E, M, ok);
 
   if (blk < P.B) {                         // position ids and mask of one sequence
     if (!ok) return;
@@ -382,17 +397,17 @@ __global__ __launch_bounds__(kCompactThreads) void tree_compact_kernel(CompactPa
 
 using namespace specv;
 
-template <typename IT>
-static void launch_realign(const RealignParams &P, size_t R, const void *kv, dim3 grid, dim3 block,
-                           hipStream_t s) {
+template <class W, typename IT>
+static void launch_realign(const RealignParams &P, size_t R, const void *kv, dim3 grid, hipStream_t s) {
+  const dim3 block(W::kThreads);
   if (R % 16 == 0 && aligned(kv, 16))
-    hipLaunchKernelGGL((realign_kernel<16, IT>), grid, block, 0, s, P);
+    hipLaunchKernelGGL((realign_kernel<W, 16, IT>), grid, block, 0, s, P);
   else if (R % 8 == 0 && aligned(kv, 8))
-    hipLaunchKernelGGL((realign_kernel<8, IT>), grid, block, 0, s, P);
+    hipLaunchKernelGGL((realign_kernel<W, 8, IT>), grid, block, 0, s, P);
   else if (R % 4 == 0 && aligned(kv, 4))
-    hipLaunchKernelGGL((realign_kernel<4, IT>), grid, block, 0, s, P);
+    hipLaunchKernelGGL((realign_kernel<W, 4, IT>), grid, block, 0, s, P);
   else
-    hipLaunchKernelGGL((realign_kernel<2, IT>), grid, block, 0, s, P);
+    hipLaunchKernelGGL((realign_kernel<W, 2, IT>), grid, block, 0, s, P);
 }
 
 static int realign_launch(void *kv, spec_dtype dt, int L, int B, int H, int C, int D, int k, int slots,
@@ -443,13 +458,16 @@ static int realign_launch(void *kv, spec_dtype dt, int L, int B, int H, int C, i
   P.mask = mask;
   P.bytes_moved = bytes_moved;
   P.status = status;
-  const dim3 grid(static_cast<unsigned>(B + 1 + planes)), block(kThreads);
+  const dim3 grid(static_cast<unsigned>(B + 1 + planes));
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (P.plane_bytes < (1LL << 31))         // vector indices and byte offsets fit 32 bits
-    launch_realign<int>(P, R, kv, grid, block, s);
+  constexpr long long kWideTileBytes = 16LL * WalkWide::kThreads * WalkWide::kTileVec;
+  if (P.plane_bytes < kWideTileBytes)      // a plane smaller than one wide tile: narrow walkers
+    launch_realign<WalkNarrow, int>(P, R, kv, grid, s);
+  else if (P.plane_bytes < (1LL << 31))    // vector indices and byte offsets fit 32 bits
+    launch_realign<WalkWide, int>(P, R, kv, grid, s);
   else
-    launch_realign<long long>(P, R, kv, grid, block, s);
+    launch_realign<WalkWide, long long>(P, R, kv, grid, s);
   return launch_status();
 }
 
