@@ -159,9 +159,9 @@ __device__ double residual_pass(const TreeSampleParams &P, const float *prow, co
       xq[e] = nq[e];
     }
   }
-  // total in chunk order: each lane a run of consecutive chunks, then a
-  // fixed-order scan across lanes
-  const int per = (P.chunks + kThreads - 1) / kThreads;
+  // total in chunk order as the linear verification adds it: 256 lanes, each a
+  // run of consecutive chunks, then a fixed-order scan across lanes
+  const int per = (P.chunks + kQuarter - 1) / kQuarter;
   double mine = 0.0;
   for (int k = 0; k < per; ++k) {
     const int cc = t * per + k;
@@ -202,7 +202,7 @@ __device__ int draw_token(const TreeSampleParams &P, const float *prow, const fl
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
   const double T = static_cast<double>(u) * Stot;
   const int nc = P.chunks;
-  const int per = (nc + kThreads - 1) / kThreads;
+  const int per = (nc + kQuarter - 1) / kQuarter;   // lanes 0 .. 255 hold the chunks, as in the linear draw
   const int c0 = t * per;
   double mine = 0.0;
   for (int k = 0; k < per; ++k)

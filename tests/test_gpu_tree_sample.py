@@ -110,6 +110,24 @@ def test_chain_is_spec_verify_sample():
     assert np.array_equal(got["final_mass"], lin["final_mass"])
 
 
+def test_chain_is_spec_verify_sample_on_long_rows():
+    """Rows of more than 256 chunks (V = 1200003: 293 chunks of 4096), where
+    the chunk masses are added in runs of two per lane: still bit for bit."""
+    note("tree sample chain vs spec_verify_sample, V=1200003")
+    r = W.sample_round(2, round_=1, B=2, V=1200003, k=2)
+    p, q, d, u = r["p"], r["q"], r["drafts"], r["uniforms"]
+    B, kp1, V = p.shape
+    k = kp1 - 1
+    fc, ns = chain_links(B, kp1)
+    g = dict(p=p, q=np.concatenate([q, np.zeros((B, 1, V), np.float32)], axis=1),
+             draft=np.concatenate([np.zeros((B, 1), np.int32), d], axis=1), first_child=fc, next_sibling=ns,
+             uniforms=np.concatenate([u[:, k:], u[:, :k]], axis=1))
+    got, _ = compare(g)
+    lin = host(verify_sample(_dev_f32(p), _dev_f32(q), d, u))
+    for key in ["accept_len", "emit_count", "emit_offsets", "status", "out_tokens", "final_mass"]:
+        assert np.array_equal(got[key], lin[key]), key
+
+
 def test_edge_cases():
     rng = np.random.default_rng(5)
     B, N, V = 6, 6, 513
