@@ -739,10 +739,12 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
     accs_, emits_ = torch.empty(Bs, **i32), torch.empty(Bs, **i32)
     toks_, paths_, offs_ = torch.empty(Bs, Ns, **i32), torch.empty(Bs, Ns, **i32), torch.empty(Bs + 1, **i32)
     its = itertools.count()
+    ws_s = sv.workspace(sv.spec_verify_tree_sample_workspace_bytes(Bs, Ns, Vs), dev)
 
     def tree_sample_call():
         ps, qs, ds, fcs, nss, us = sets[next(its) % nbs]
-        sv.spec_verify_tree_sample(ps, qs, ds, fcs, nss, us, accs_, emits_, toks_, paths_, emit_offsets=offs_)
+        sv.spec_verify_tree_sample(ps, qs, ds, fcs, nss, us, accs_, emits_, toks_, paths_, ws_s,
+                                   emit_offsets=offs_)
 
     t, th = _time_calls(torch, tree_sample_call, 22, inner=3 * nbs)
     acc_s, emit_s = [], []
@@ -754,7 +756,8 @@ def secondary_measurements(dev, np, torch, sv, W) -> dict:
         "workload": f"stochastic tree verify, B={Bs} N={Ns} nodes (parents among the 3 below, siblings drawn "
                     f"from the parent's q), V={Vs} f32 p/q, {nbs} rotating input sets",
         "us_per_call": t * 1e6, "us_per_call_host": th * 1e6,
-        "mean_accept_len": sum(acc_s) / nbs, "mean_emit_count": sum(emit_s) / nbs}
+        "mean_accept_len": sum(acc_s) / nbs, "mean_emit_count": sum(emit_s) / nbs,
+        "workgroups_per_sequence": "several (workspace given)" if ws_s.numel() > 256 else 1}
     del sets
     # compaction of the last buffer's paths; successive calls use end columns
     # NT apart, so 48 calls touch 48 disjoint column ranges (more than the

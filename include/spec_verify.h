@@ -45,7 +45,9 @@
  *     pass and a commit pass, synchronised by the stream order.
  *   - A stochastic verify call is one launch too: streaming workgroups publish
  *     the chunk masses of the row each sequence draws from, and one workgroup
- *     per sequence of the same launch, dispatched after them, draws.
+ *     per sequence of the same launch, dispatched after them, draws.  The
+ *     stochastic tree verification's workspace, when given, is of the same
+ *     kind.
  *   - Token ids are int32 in [0, V).  Layouts are row-major, last index fastest.
  */
 #ifndef SPEC_VERIFY_H
@@ -465,18 +467,30 @@ int spec_compact_tree_kv(void *kv, spec_dtype dt, int L, int B, int H, int C, in
  *   emit_offsets [B + 1] out or NULL; final_mass [B] float64 out or NULL: the
  *                mass S of the vector drawn from, 0 without a draw
  *   status       [B] out or NULL
- * No workspace.  One workgroup per sequence walks its tree; each rejection
- * reads the node's p and q rows once.
+ *   ws           NULL, or a workspace of
+ *                spec_verify_tree_sample_workspace_bytes(B, N, V) bytes
+ *                (zero-filled on first use, left zero-filled by every call;
+ *                it carries completion flags, so no other kind of call may
+ *                write into it)
+ * Each sequence's tree is walked by one workgroup; each rejection reads the
+ * node's p and q rows once.  With a workspace, and when the query returns a
+ * nonzero size (small batches), up to 16 workgroups per sequence share those
+ * passes, exchanging chunk masses through the workspace; the results are the
+ * same.  The query returns 0 for shapes that run one workgroup per sequence
+ * (then ws may be NULL or anything: it is not used).
  * Errors: SPEC_EINVAL for NULL required pointers, B, N or V < 1, misaligned
  * p, q or uniforms (4 bytes), overlapping outputs; SPEC_ECAPACITY for
- * N > SPEC_TREE_MAX_N or V > 4194304.
+ * N > SPEC_TREE_MAX_N or V > 4194304; SPEC_EWORKSPACE for a non-NULL ws
+ * smaller than the query or not 256-byte aligned (when the query is nonzero).
  * ------------------------------------------------------------------------ */
+size_t spec_verify_tree_sample_workspace_bytes(int B, int N, int V);
 int spec_verify_tree_sample(const float *p, const float *q, const int32_t *draft,
                             const int32_t *first_child, const int32_t *next_sibling,
                             const float *uniforms, int B, int N, int V, int32_t eos_id,
                             const int32_t *remaining, int32_t *accept_len, int32_t *emit_count,
                             int32_t *out_tokens, int32_t *path, int32_t *emit_offsets,
-                            double *final_mass, int32_t *status, spec_stream_t stream);
+                            double *final_mass, int32_t *status, void *ws, size_t ws_bytes,
+                            spec_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * Same-length grouping of a window of ragged sequences.

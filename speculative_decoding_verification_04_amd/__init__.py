@@ -25,7 +25,8 @@ __all__ = [
     "spec_verify_sample_workspace_bytes", "spec_verify_sample", "spec_process_workspace_bytes",
     "spec_process_logits", "spec_verify_sample_logits_workspace_bytes", "spec_verify_sample_logits",
     "spec_commit_realign_kv", "spec_resync_draft_kv", "spec_repad_kv", "spec_unpad_kv", "spec_commit_paged",
-    "spec_verify_tree_workspace_bytes", "spec_verify_tree", "spec_compact_tree_kv", "spec_verify_tree_sample",
+    "spec_verify_tree_workspace_bytes", "spec_verify_tree", "spec_compact_tree_kv", "spec_verify_tree_sample_workspace_bytes",
+    "spec_verify_tree_sample",
     "spec_group_same_length", "workspace", "library",
 ]
 
@@ -303,10 +304,16 @@ def spec_verify_tree(logits, draft, first_child, next_sibling, accept_len, emit_
     _check(code, "spec_verify_tree")
 
 
+def spec_verify_tree_sample_workspace_bytes(B: int, N: int, V: int) -> int:
+    return int(library().spec_verify_tree_sample_workspace_bytes(B, N, V))
+
+
 def spec_verify_tree_sample(p, q, draft, first_child, next_sibling, uniforms, accept_len, emit_count,
-                            out_tokens, path, *, eos_id: int = -1, remaining=None, emit_offsets=None,
+                            out_tokens, path, ws=None, *, eos_id: int = -1, remaining=None, emit_offsets=None,
                             final_mass=None, status=None, stream=None) -> None:
-    """p, q [B, N, V] f32; draft, first_child, next_sibling [B, N] int32; uniforms [B, N] f32."""
+    """p, q [B, N, V] f32; draft, first_child, next_sibling [B, N] int32; uniforms [B, N] f32;
+    ws: None (one workgroup per sequence) or a zero-filled workspace of
+    spec_verify_tree_sample_workspace_bytes(B, N, V) bytes."""
     B, N, V = p.shape
     code = library().spec_verify_tree_sample(
         _arg(p, "float32", B * N * V, "p"), _arg(q, "float32", B * N * V, "q"),
@@ -317,7 +324,7 @@ def spec_verify_tree_sample(p, q, draft, first_child, next_sibling, uniforms, ac
         _arg(out_tokens, "int32", B * N, "out_tokens"), _arg(path, "int32", B * N, "path"),
         _arg(emit_offsets, "int32", B + 1, "emit_offsets", True),
         _arg(final_mass, "float64", B, "final_mass", True), _arg(status, "int32", B, "status", True),
-        _stream(stream))
+        None if ws is None else _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(code, "spec_verify_tree_sample")
 
 

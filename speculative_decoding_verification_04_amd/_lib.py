@@ -37,8 +37,9 @@ PROTOTYPES = {
     "spec_verify_tree": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
                               _P, _P, _SZ, _P]),
     "spec_compact_tree_kv": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "spec_verify_tree_sample_workspace_bytes": (_SZ, [_I, _I, _I]),
     "spec_verify_tree_sample": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_int32, _P, _P, _P, _P,
-                                     _P, _P, _P, _P, _P]),
+                                     _P, _P, _P, _P, _P, _SZ, _P]),
     "spec_group_same_length": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
 }
 

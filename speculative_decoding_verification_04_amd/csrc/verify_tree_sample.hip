@@ -53,7 +53,20 @@ struct TreeSampleParams {
   int32_t *accept_len, *emit_count, *out_tokens, *path, *emit_offsets;
   double *final_mass;
   int32_t *status;
+  int W;                         // workgroups per sequence (1: one walks alone)
+  unsigned long long *slots;     // [B][N][chunks] published chunk masses, per pass (W > 1)
+  int32_t *done;                 // [B][W] members finished with the slots (W > 1)
 };
+
+// Chunk masses travel between the workgroups of a sequence as 64-bit keys: the
+// mass's bits XOR kMassSentinel, a NaN whose low 29 bits are not all zero --
+// a pattern no sum of float32 values widened to float64 takes -- so every
+// published key is nonzero and a zero slot means "not yet written".
+constexpr unsigned long long kMassSentinel = 0x7FF4000000000001ull;
+constexpr int kMaxPolls = 1 << 22;               // about 4 s of polling: a bound every wait reaches
+constexpr int kMaxCoopGroups = 128;              // B * W: one workgroup per CU, all resident at once
+constexpr int kMaxMembers = 16;
+constexpr long long kMaxCoopSlots = 8LL << 20;   // B * N * chunks: 64 MB of slots at most
 
 // R_i(v) from p(v), q(v) and the masses m[1 .. i-1] (m[0] unused).  R_0 = p as
 // given, R_1 = max(p - q, 0) in float32, then float64 steps.
@@ -117,50 +130,84 @@ struct Shared {
   double base;
 };
 
+__device__ inline unsigned long long mass_key(double m) {
+  return static_cast<unsigned long long>(__double_as_longlong(m)) ^ kMassSentinel;
+}
+
 // Chunk masses of R_i over the row pair (p, q) into part[], and their total in
-// chunk order.  Each quarter of the workgroup takes one chunk per step: a lane
-// adds its 16 entries in index order, the quarter's four waves are added in
-// order.  Contains barriers.
+// chunk order.  Member w of the W workgroups of a sequence computes chunks
+// w, w + W, w + 2W, ...: each quarter of the workgroup takes one of them per
+// step (the next step's loads issued before this step's sums), a lane adds
+// its 16 entries in index order and the quarter's four waves are added in
+// order (the order of the linear verification's chunk masses).  With W > 1 the
+// masses are published into this pass's slots and the member waits (bounded)
+// for every other chunk's; *timed_out reports a wait that did not end.  The
+// total adds the masses as the linear verification does: 256 lanes, each a run
+// of consecutive chunks, then a fixed-order scan.  Contains barriers.
 __device__ double residual_pass(const TreeSampleParams &P, const float *prow, const float *qrow, int i,
-                                Shared &S, double *part) {
+                                Shared &S, double *part, int w, unsigned long long *slots, bool *timed_out) {
   const int t = threadIdx.x, quarter = t / kQuarter, ql = t % kQuarter, lane = t & (kWave - 1);
-  const int w = t / kWave;
+  const int wv = t / kWave;
   const bool vec = P.vec != 0;
-  const int steps = (P.chunks + kChunksPerStep - 1) / kChunksPerStep;
+  const int W = P.W;
+  const int nown = w < P.chunks ? (P.chunks - w + W - 1) / W : 0;   // this member's chunks
+  const int steps = (nown + kChunksPerStep - 1) / kChunksPerStep;
   float xp[kEPT], xq[kEPT], np_[kEPT], nq[kEPT];
 #pragma unroll
-  for (int e = 0; e < kEPT; ++e) xq[e] = np_[e] = nq[e] = 0.0f;   // q is not read for R_0
-  int c = quarter;
-  load16(xp, prow, c * kChunk + ql * kEPT, P.V, vec);
-  if (i > 0) load16(xq, qrow, c * kChunk + ql * kEPT, P.V, vec);
+  for (int e = 0; e < kEPT; ++e) xp[e] = xq[e] = np_[e] = nq[e] = 0.0f;   // q is not read for R_0
+  int j = quarter;                            // this quarter's own-chunk index
+  if (steps > 0) {
+    const int c = w + W * j;
+    load16(xp, prow, c * kChunk + ql * kEPT, P.V, vec);
+    if (i > 0) load16(xq, qrow, c * kChunk + ql * kEPT, P.V, vec);
+  }
   for (int s = 0; s < steps; ++s) {
-    const int cn = c + kChunksPerStep;
+    const int jn = j + kChunksPerStep;
     if (s + 1 < steps) {                     // the next step's loads before this step's sums
+      const int cn = w + W * jn;
       load16(np_, prow, cn * kChunk + ql * kEPT, P.V, vec);
       if (i > 0) load16(nq, qrow, cn * kChunk + ql * kEPT, P.V, vec);
     }
     double acc = 0.0;
 #pragma unroll
-    for (int e = 0; e < kEPT; ++e) acc += resid_at(xp[e], i > 0 ? xq[e] : 0.0f, i, S.m);
+    for (int e = 0; e < kEPT; ++e) acc += resid_at(xp[e], xq[e], i, S.m);
     acc = wave_sum_d(acc);
-    if (lane == 0) S.wsum[w] = acc;
+    if (lane == 0) S.wsum[wv] = acc;
     __syncthreads();
-    if (ql == 0 && c < P.chunks) {
+    if (ql == 0 && j < nown) {
+      const int c = w + W * j;
       const int w0 = quarter * (kQuarter / kWave);
       double tot = 0.0;
       for (int k = 0; k < kQuarter / kWave; ++k) tot += S.wsum[w0 + k];
       part[c] = tot;
+      if (W > 1) __hip_atomic_store(slots + c, mass_key(tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    c = cn;
+    j = jn;
 #pragma unroll
     for (int e = 0; e < kEPT; ++e) {
       xp[e] = np_[e];
       xq[e] = nq[e];
     }
   }
-  // total in chunk order as the linear verification adds it: 256 lanes, each a
-  // run of consecutive chunks, then a fixed-order scan across lanes
+  if (W > 1) {                               // every other member's chunks
+    int polls = 0;
+    while (true) {
+      bool present = true;
+      for (int c = t; c < P.chunks; c += kThreads) {
+        if (c % W == w) continue;
+        const unsigned long long key = load_agent(slots + c);
+        if (key == 0ull) present = false;
+        else part[c] = __longlong_as_double(static_cast<long long>(key ^ kMassSentinel));
+      }
+      if (__syncthreads_and(present)) break;
+      if (++polls >= kMaxPolls) {
+        *timed_out = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
   const int per = (P.chunks + kQuarter - 1) / kQuarter;
   double mine = 0.0;
   for (int k = 0; k < per; ++k) {
@@ -168,7 +215,7 @@ __device__ double residual_pass(const TreeSampleParams &P, const float *prow, co
     if (cc < P.chunks) mine += part[cc];
   }
   double inc = wave_incl_scan(mine);
-  if (lane == kWave - 1) S.dscan[w] = inc;
+  if (lane == kWave - 1) S.dscan[wv] = inc;
   __syncthreads();
   double tot = 0.0;
   for (int k = 0; k < kWaves; ++k) tot += S.dscan[k];
@@ -295,7 +342,7 @@ enum : int { kTry = 0, kAccepted = 1, kRejected = 2, kNoChild = 3 };
 
 __global__ __launch_bounds__(kThreads) void tree_sample_kernel(TreeSampleParams P) {
   __shared__ Shared S;
-  const int b = blockIdx.x, t = threadIdx.x;
+  const int b = blockIdx.x / P.W, w = blockIdx.x % P.W, t = threadIdx.x;
   const int N = P.N, V = P.V;
   const size_t rowb = static_cast<size_t>(b) * N;
   const float *pb = P.p + rowb * V;
@@ -315,6 +362,9 @@ __global__ __launch_bounds__(kThreads) void tree_sample_kernel(TreeSampleParams 
   int st = valid ? 0 : SPEC_ST_BAD_STATE;
   int e = 0, acc = 0;
   double fmass = 0.0;
+  int ps = 0;                                 // passes so far (each has its own slots)
+  bool timed_out = false;
+  auto slots_of = [&](int pass) { return P.slots + (static_cast<size_t>(b) * N + pass) * P.chunks; };
   if (valid && rem != 0) {
     int cur = 0;
     int buf = 0;                              // part[buf] holds the current residual's chunk masses
@@ -363,7 +413,13 @@ __global__ __launch_bounds__(kThreads) void tree_sample_kernel(TreeSampleParams 
           break;
         }
         // rejected: the chunk masses and mass of R_{i+1} into the other buffer
-        const double mn = residual_pass(P, prow, qrow, i + 1, S, S.part[buf ^ 1]);
+        const double mn = residual_pass(P, prow, qrow, i + 1, S, S.part[buf ^ 1], w, slots_of(ps), &timed_out);
+        ++ps;
+        if (timed_out) {                      // outputs unspecified; every wait still ends
+          st |= SPEC_ST_INCOMPLETE;
+          done = true;
+          break;
+        }
         if (!isfinite(mn)) {                  // the round emits token 0 and stops
           st |= SPEC_ST_NONFINITE;
           if (t == 0) S.out[e] = 0;
@@ -396,8 +452,16 @@ __global__ __launch_bounds__(kThreads) void tree_sample_kernel(TreeSampleParams 
       }
       // no child accepted, or a leaf: one draw from the current residual
       double Stot;
-      if (i == 0) Stot = residual_pass(P, prow, qrow, 0, S, S.part[buf]);
-      else Stot = S.m[i];
+      if (i == 0) {
+        Stot = residual_pass(P, prow, qrow, 0, S, S.part[buf], w, slots_of(ps), &timed_out);
+        ++ps;
+        if (timed_out) {
+          st |= SPEC_ST_INCOMPLETE;
+          break;
+        }
+      } else {
+        Stot = S.m[i];
+      }
       int tok;
       if (!isfinite(Stot)) {
         st |= SPEC_ST_NONFINITE;
@@ -415,7 +479,12 @@ __global__ __launch_bounds__(kThreads) void tree_sample_kernel(TreeSampleParams 
     }
   }
   __syncthreads();
-  // outputs: tokens and kept nodes (-1 padded), counts, mass, status
+  if (w > 0) {                                // every read of this sequence's slots is done
+    if (t == 0) __hip_atomic_store(P.done + static_cast<size_t>(b) * P.W + w, 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  // member 0: outputs (tokens and kept nodes -1 padded, counts, mass, status)
   if (t < N) {
     P.out_tokens[rowb + t] = t < e ? S.out[t] : -1;
     P.path[rowb + t] = t < e ? S.nodes[t] : -1;
@@ -425,6 +494,21 @@ __global__ __launch_bounds__(kThreads) void tree_sample_kernel(TreeSampleParams 
     P.emit_count[b] = e;
     if (P.final_mass) P.final_mass[b] = fmass;
     if (P.status) P.status[b] = st;
+  }
+  if (P.W > 1) {
+    // once every other member is done with the slots, they and the flags
+    // return to zero for the next call (bounded wait)
+    int32_t *dn = P.done + static_cast<size_t>(b) * P.W;
+    int polls = 0;
+    while (true) {
+      const bool present = t == 0 || t >= P.W || load_agent(dn + t) != 0;
+      if (__syncthreads_and(present)) break;
+      if (++polls >= kMaxPolls) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (t > 0 && t < P.W) dn[t] = 0;
+    unsigned long long *sl = slots_of(0);
+    for (size_t f = t; f < static_cast<size_t>(ps) * P.chunks; f += kThreads) sl[f] = 0ull;
   }
 }
 
@@ -437,17 +521,46 @@ __global__ __launch_bounds__(kThreads) void tree_sample_offsets_kernel(const int
 
 inline int tree_sample_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
+// Workgroups per sequence: up to 16 while the whole grid fits one workgroup per
+// CU on half of the chip (so every member of a sequence is resident at once)
+// and the slots stay within 64 MB; else 1 (no workspace).
+inline int tree_sample_members(int B, int N, int chunks) {
+  if (B > kMaxCoopGroups / 2) return 1;
+  if (static_cast<long long>(B) * N * chunks > kMaxCoopSlots) return 1;
+  return max(1, min(min(kMaxMembers, kMaxCoopGroups / B), chunks));
+}
+
+struct TreeSampleWs {
+  size_t slots, done, total;
+};
+inline TreeSampleWs tree_sample_ws(int B, int N, int chunks, int W) {
+  TreeSampleWs l;
+  l.slots = 0;
+  l.done = round_up(static_cast<size_t>(B) * N * chunks * 8, 256);
+  l.total = l.done + round_up(static_cast<size_t>(B) * W * 4, 256);
+  return l;
+}
+
 }  // namespace
 }  // namespace specv
 
 using namespace specv;
+
+extern "C" size_t spec_verify_tree_sample_workspace_bytes(int B, int N, int V) {
+  if (B < 1 || N < 1 || V < 1 || N > SPEC_TREE_MAX_N || V >= INT32_MAX - kChunk) return 0;
+  const int chunks = tree_sample_chunks(V);
+  if (chunks > kMaxChunks) return 0;
+  const int W = tree_sample_members(B, N, chunks);
+  return W > 1 ? tree_sample_ws(B, N, chunks, W).total : 0;
+}
 
 extern "C" int spec_verify_tree_sample(const float *p, const float *q, const int32_t *draft,
                                        const int32_t *first_child, const int32_t *next_sibling,
                                        const float *uniforms, int B, int N, int V, int32_t eos_id,
                                        const int32_t *remaining, int32_t *accept_len, int32_t *emit_count,
                                        int32_t *out_tokens, int32_t *path, int32_t *emit_offsets,
-                                       double *final_mass, int32_t *status, spec_stream_t stream) {
+                                       double *final_mass, int32_t *status, void *ws, size_t ws_bytes,
+                                       spec_stream_t stream) {
   if (!p || !q || !draft || !first_child || !next_sibling || !uniforms || !accept_len || !emit_count ||
       !out_tokens || !path)
     return SPEC_EINVAL;
@@ -458,12 +571,17 @@ extern "C" int spec_verify_tree_sample(const float *p, const float *q, const int
   if (!aligned(p, 4) || !aligned(q, 4) || !aligned(uniforms, 4)) return SPEC_EINVAL;
   const size_t rows = static_cast<size_t>(B) * N;
   const size_t nrow = rows * V * 4, nb = static_cast<size_t>(B) * 4, nbn = rows * 4;
-  const void *ins[] = {p, q, draft, first_child, next_sibling, uniforms, remaining};
-  const size_t in_n[] = {nrow, nrow, nbn, nbn, nbn, nbn, nb};
+  // with a workspace, up to 16 workgroups share each sequence's passes
+  const int W = ws ? tree_sample_members(B, N, chunks) : 1;
+  const TreeSampleWs lay = tree_sample_ws(B, N, chunks, W);
+  if (W > 1 && (ws_bytes < lay.total || !aligned(ws, 256))) return SPEC_EWORKSPACE;
+  const size_t wsn = W > 1 ? lay.total : 0;
+  const void *ins[] = {p, q, draft, first_child, next_sibling, uniforms, remaining, W > 1 ? ws : nullptr};
+  const size_t in_n[] = {nrow, nrow, nbn, nbn, nbn, nbn, nb, wsn};
   const void *outs[] = {accept_len, emit_count, out_tokens, path, emit_offsets, final_mass, status};
   const size_t out_n[] = {nb, nb, nbn, nbn, nb + 4, static_cast<size_t>(B) * 8, nb};
   for (int i = 0; i < 7; ++i) {
-    for (int j = 0; j < 7; ++j)
+    for (int j = 0; j < 8; ++j)
       if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return SPEC_EINVAL;
     for (int j = i + 1; j < 7; ++j)
       if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return SPEC_EINVAL;
@@ -489,9 +607,13 @@ extern "C" int spec_verify_tree_sample(const float *p, const float *q, const int
   P.emit_offsets = emit_offsets;
   P.final_mass = final_mass;
   P.status = status;
+  P.W = W;
+  unsigned char *wb = static_cast<unsigned char *>(ws);
+  P.slots = W > 1 ? reinterpret_cast<unsigned long long *>(wb + lay.slots) : nullptr;
+  P.done = W > 1 ? reinterpret_cast<int32_t *>(wb + lay.done) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(tree_sample_kernel, dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(tree_sample_kernel, dim3(static_cast<unsigned>(B * W)), dim3(kThreads), 0, s, P);
   if (emit_offsets)
     hipLaunchKernelGGL(tree_sample_offsets_kernel, dim3(1), dim3(kThreads), 0, s, emit_count, emit_offsets, B);
   return launch_status();

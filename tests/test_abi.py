@@ -234,7 +234,7 @@ I_, J_, K_ = (ctypes.c_void_p(0x10000 * (i + 9)) for i in range(3))
 
 def _tree_sample_args(**kw):
     a = dict(p=A, q=B_, draft=C_, fc=D_, ns=E_, u=F_, B=2, N=4, V=100, eos=-1, rem=N, acc=G_, emit=H_,
-             toks=I_, path=J_, offs=K_, mass=N, st=N, stream=N)
+             toks=I_, path=J_, offs=K_, mass=N, st=N, ws=N, ws_bytes=0, stream=N)
     a.update(kw)
     return tuple(a.values())
 
@@ -251,9 +251,21 @@ def _tree_sample_args(**kw):
     (_tree_sample_args(q=ctypes.c_void_p(0x20002)), sv.SPEC_EINVAL),   # misaligned q
     (_tree_sample_args(toks=G_), sv.SPEC_EINVAL),                  # outputs alias
     (_tree_sample_args(path=C_), sv.SPEC_EINVAL),                  # output over an input
+    # several chunks (V = 20000): the workspace is used, and checked
+    (_tree_sample_args(V=20000, ws=WS, ws_bytes=8), sv.SPEC_EWORKSPACE),     # workspace below the query
+    (_tree_sample_args(V=20000, ws=ctypes.c_void_p(0x7000008), ws_bytes=1 << 20), sv.SPEC_EWORKSPACE),
 ])
 def test_tree_sample_argument_errors(args, code):
     assert LIB.spec_verify_tree_sample(*args) == code
+
+
+@needs_lib
+def test_tree_sample_workspace_query():
+    small = sv.spec_verify_tree_sample_workspace_bytes(8, 16, 151936)
+    assert small >= 8 * 16 * 38 * 8 and small % 256 == 0            # slots for every pass of every chunk
+    assert sv.spec_verify_tree_sample_workspace_bytes(200, 16, 151936) == 0   # large batch: one workgroup each
+    assert sv.spec_verify_tree_sample_workspace_bytes(8, 300, 1000) == 0       # N beyond the maximum
+    assert sv.spec_verify_tree_sample_workspace_bytes(64, 256, 1 << 22) == 0   # slots beyond 64 MB
 
 
 @needs_lib

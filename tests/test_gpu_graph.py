@@ -96,9 +96,11 @@ def test_tree_sample_replay():
     out = [torch.empty(B, dtype=torch.int32, device=DEV), torch.empty(B, dtype=torch.int32, device=DEV),
            torch.empty(B, N, dtype=torch.int32, device=DEV), torch.empty(B, N, dtype=torch.int32, device=DEV),
            torch.empty(B + 1, dtype=torch.int32, device=DEV), torch.empty(B, dtype=torch.float64, device=DEV)]
+    wst = sv.workspace(sv.spec_verify_tree_sample_workspace_bytes(B, N, 5000), DEV)
     note("graph: stochastic tree verify")
-    _replay_matches(lambda: sv.spec_verify_tree_sample(p, q, d, fc, ns, u, out[0], out[1], out[2], out[3],
+    _replay_matches(lambda: sv.spec_verify_tree_sample(p, q, d, fc, ns, u, out[0], out[1], out[2], out[3], wst,
                                                        emit_offsets=out[4], final_mass=out[5]), out)
+    assert int(torch.count_nonzero(wst).item()) == 0
 
 
 def test_paged_and_grouping_replay():

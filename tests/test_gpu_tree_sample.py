@@ -5,7 +5,10 @@ rounding of the oracle's correctly rounded sum; random trees (drafts drawn
 from the parent's q) from tiny to full-vocabulary rows, many siblings (many
 residual levels at one node), ragged and unaligned rows, EOS, budgets,
 invalid links, out-of-range drafts, q(x) = 0 and rows without residual
-mass; and a chain tree against spec_verify_sample, bit for bit."""
+mass; and a chain tree against spec_verify_sample, bit for bit.  Every case
+runs twice: one workgroup per sequence (no workspace), and, where the shape
+allows it, several workgroups per sequence exchanging chunk masses through
+the workspace, which every call must leave zero-filled."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +17,7 @@ import oracle
 import speculative_decoding_verification_04_amd as sv
 import workloads as W
 from oracle.tree import chain_links
-from tests._gpu import DEV, host, i32, note, requires_gpu, verify_sample
+from tests._gpu import DEV, host, i32, note, requires_gpu, verify_sample, ws
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -25,8 +28,12 @@ def _dev_f32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
 
 
-def run(g, eos_id=-1, remaining=None, p_dev=None, q_dev=None):
+def run(g, eos_id=-1, remaining=None, p_dev=None, q_dev=None, coop=False):
     B, N, V = g["p"].shape
+    w = None
+    if coop:
+        nb = sv.spec_verify_tree_sample_workspace_bytes(B, N, V)
+        w = ws(nb, ("tree_sample", None)) if nb else None
     out = dict(accept_len=torch.full((B,), -7, dtype=torch.int32, device=DEV),
                emit_count=torch.full((B,), -7, dtype=torch.int32, device=DEV),
                out_tokens=torch.full((B, N), -7, dtype=torch.int32, device=DEV),
@@ -39,25 +46,34 @@ def run(g, eos_id=-1, remaining=None, p_dev=None, q_dev=None):
         i32(g["draft"]), i32(g["first_child"]), i32(g["next_sibling"]), _dev_f32(g["uniforms"]),
         out["accept_len"], out["emit_count"], out["out_tokens"], out["path"], eos_id=eos_id,
         remaining=None if remaining is None else i32(remaining), emit_offsets=out["emit_offsets"],
-        final_mass=out["final_mass"], status=out["status"])
-    return host(out)
+        final_mass=out["final_mass"], status=out["status"], ws=w)
+    got = host(out)
+    if w is not None:
+        assert int(torch.count_nonzero(w).item()) == 0          # slots and flags clear again
+    return got
 
 
 def compare(g, eos_id=-1, remaining=None, **kw):
+    """Both launch shapes against the oracle; they must also agree with each
+    other bit for bit (the same sums in the same order)."""
     ref = oracle.tree_sample_verify(g["p"], g["q"], g["draft"], g["first_child"], g["next_sibling"],
                                     g["uniforms"], eos_id=eos_id, remaining=remaining)
-    got = run(g, eos_id, remaining, **kw)
-    for k in KEYS:
-        assert np.array_equal(got[k], ref[k]), (k, got[k], ref[k])
-    fm, rm = got["final_mass"], ref["final_mass"]
-    fin = np.isfinite(rm)
-    assert np.array_equal(np.isfinite(fm), fin)
-    assert np.allclose(fm[fin], rm[fin], rtol=1e-12, atol=0)
-    return got, ref
+    gots = [run(g, eos_id, remaining, coop=c, **kw) for c in (False, True)]
+    for got in gots:
+        for k in KEYS:
+            assert np.array_equal(got[k], ref[k]), (k, got[k], ref[k])
+        fm, rm = got["final_mass"], ref["final_mass"]
+        fin = np.isfinite(rm)
+        assert np.array_equal(np.isfinite(fm), fin)
+        assert np.allclose(fm[fin], rm[fin], rtol=1e-12, atol=0)
+    for k in gots[0]:
+        assert np.array_equal(gots[0][k], gots[1][k], equal_nan=True), k
+    return gots[1], ref
 
 
 @pytest.mark.parametrize("B,N,V,branching", [
     (4, 8, 1000, 3), (8, 16, 151936, 3), (3, 32, 4099, 5), (5, 64, 37, 8), (2, 256, 300, 2), (6, 5, 8192, 4),
+    (100, 6, 9000, 3),
 ])
 def test_random_trees(B, N, V, branching):
     rng = np.random.default_rng(1000 * N + B)
