@@ -80,18 +80,31 @@ __global__ __launch_bounds__(kThreads) void ragged_copy_kernel(RaggedParams P) {
   const T *src = reinterpret_cast<const T *>(P.src + (P.unpad ? rect_off : pool_off));
   T *dst = reinterpret_cast<T *>(P.dst + (P.unpad ? pool_off : rect_off));
   const long long nw = rows * P.row_bytes / VB;
-  for (long long w0 = 0; w0 < nw; w0 += static_cast<long long>(kThreads) * kU) {
-    T x[kU];
+  if (nw <= 0) return;
+  // Every lane issues every load and store (no per-lane branches), so the wait
+  // for one step's loads leaves the next step's loads and the previous step's
+  // stores in flight; indices past the run are clamped to its last vector,
+  // which such lanes copy again (the same value to the same cell).  Three
+  // register buffers rotate, so none is reloaded right after its stores.
+  const long long last = nw - 1;
+  const int t = threadIdx.x;
+  constexpr long long kStep = static_cast<long long>(kThreads) * kU;
+  long long w0 = 0;
+  T b0[kU], b1[kU], b2[kU];
+  auto load = [&](T (&x)[kU], long long base) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const long long w = w0 + u * kThreads + threadIdx.x;
-      if (w < nw) x[u] = __builtin_nontemporal_load(src + w);
-    }
+    for (int u = 0; u < kU; ++u) x[u] = __builtin_nontemporal_load(src + min(base + u * kThreads + t, last));
+  };
+  auto step = [&](T (&cur)[kU], T (&nxt)[kU]) __attribute__((always_inline)) {
+    const long long nb = w0 + kStep;
+    load(nxt, nb);
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const long long w = w0 + u * kThreads + threadIdx.x;
-      if (w < nw) __builtin_nontemporal_store(x[u], dst + w);
-    }
+    for (int u = 0; u < kU; ++u) __builtin_nontemporal_store(cur[u], dst + min(w0 + u * kThreads + t, last));
+    w0 = nb;
+    return nb < nw;
+  };
+  load(b0, 0);
+  while (step(b0, b1) && step(b1, b2) && step(b2, b0)) {
   }
 }
 
