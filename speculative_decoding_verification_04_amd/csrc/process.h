@@ -56,6 +56,8 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
                       Temper invT, int top_k, float top_p, ProcStats *stats, float *probs,
                       void *list_ws, hipStream_t s);
 size_t proc_list_bytes(int rows, int V);
+// Workspace of the slice lists' entry indices (the verification from logits).
+size_t proc_list_idx_bytes(int rows);
 bool proc_args_ok(float T, int top_k, float top_p, int V);
 
 struct ProcConfig {

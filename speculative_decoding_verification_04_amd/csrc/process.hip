@@ -56,7 +56,7 @@
 // are parallel suffix sums.
 // Every selection keeps all logits at or above one threshold, so ties at a
 // boundary are kept, as the definitions require.
-#include "process.h"
+#include "sample_src.h"
 
 namespace specv {
 namespace {
@@ -95,6 +95,9 @@ struct ProcParams {
   int S, seg_cap;        // slices per row, entries per segment
   int cut_rank;          // the slice kernel's cut: the cut_rank-th largest lane maximum
   uint32_t *list_lb;     // [rows][S] or null: each slice's lb_rank-th largest lane maximum
+  int32_t *list_idx;     // [rows][kCandCap] or null: each listed entry's index in its row
+  unsigned long long *row_pub;   // [rows][3] or null: each row's statistics as published words
+                                 // (the slice kernel clears them, so they may hold anything on entry)
   int lb_rank;           // ceil(K / S): at least K logits of the row are at or above the smallest
   // rows without top-k: per slice, the key range and the fixed-point weight
   // (null: read the whole row)
@@ -464,10 +467,13 @@ __device__ inline int wave_gather_topk(const ProcParams &P, int r, float *cand, 
   return n;
 }
 
+// Statistics of row r by one workgroup of kProcThreads lanes: stored at
+// P.stats[r] and returned, both by lane 0 (other lanes return zeros).  lh:
+// the workgroup's per-lane histogram columns (256 * kWave words of LDS),
+// reused as the candidate list.
 template <bool BF16>
-__global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) {
-  // per-lane histogram columns (128 KB); reused as the candidate list
-  __shared__ unsigned long long lh[256 * kWave];
+__device__ __forceinline__ ProcStats proc_row_stats(const ProcParams &P, int r, unsigned long long *lh) {
+  ProcStats res = {};
   __shared__ uint32_t h_cnt[kProcThreads];     // one bucket per lane (10-bit digits on lists)
   __shared__ unsigned long long h_mass[kProcThreads];
   __shared__ float sh_f[kProcWaves];
@@ -490,7 +496,6 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   static_assert(kProcThreads == 4 * 256, "fold_columns assigns 4 lanes per bucket");
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
-  const int r = blockIdx.x;
   const int V = P.V;
   const void *row = proc_row<BF16>(P, r);
   const Temper invT = P.cfg.invT;
@@ -534,6 +539,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
         st.inv_mass = st.mass > 0.0 ? static_cast<float>(1.0 / st.mass) : 0.0f;
         st.zmin_kept = f32_from_order_key(mn);
         P.stats[r] = st;
+        res = st;
         sh_st = st;
       }
     }
@@ -543,7 +549,7 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
       float *out = P.probs + static_cast<size_t>(r) * V;
       row_foreach<BF16>(row, V, [&](int v, float z) { out[v] = proc_prob(z, st, invT); });
     }
-    return;
+    return res;
   }
 
   // ---- top-k lists of one wave per slice: wave 0 gathers the candidates
@@ -567,12 +573,15 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
     __syncthreads();
     if (sh_fast) {
       const ProcStats st = sh_st;
-      if (t == 0) P.stats[r] = st;
+      if (t == 0) {
+    P.stats[r] = st;
+    res = st;
+  }
       if (P.probs) {
         float *out = P.probs + static_cast<size_t>(r) * V;
         row_foreach<BF16>(row, V, [&](int v, float z) { out[v] = proc_prob(z, st, invT); });
       }
-      return;
+      return res;
     }
   }
 
@@ -693,12 +702,15 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
     }
     __syncthreads();
     const ProcStats st = sh_st;
-    if (t == 0) P.stats[r] = st;
+    if (t == 0) {
+    P.stats[r] = st;
+    res = st;
+  }
     if (P.probs) {
       float *out = P.probs + static_cast<size_t>(r) * V;
       row_foreach<BF16>(row, V, [&](int v, float z) { out[v] = proc_prob(z, st, invT); });
     }
-    return;
+    return res;
   }
 
   // Selection state.  Level-0 digits are chosen from whole-row histograms;
@@ -1000,11 +1012,21 @@ __global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) 
   st.mass = mass;
   st.inv_mass = mass > 0.0 ? static_cast<float>(1.0 / mass) : 0.0f;
   st.zmin_kept = zmin_kept;
-  if (t == 0) P.stats[r] = st;
+  if (t == 0) {
+    P.stats[r] = st;
+    res = st;
+  }
   if (P.probs) {
     float *out = P.probs + static_cast<size_t>(r) * V;
     row_foreach<BF16>(row, V, [&](int v, float z) { out[v] = proc_prob(z, st, invT); });
   }
+  return res;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kProcThreads) void proc_stats_kernel(ProcParams P) {
+  __shared__ unsigned long long lh[256 * kWave];
+  (void)proc_row_stats<BF16>(P, blockIdx.x, lh);
 }
 
 // Slice s of row r: kSliceThreads * kSliceLoads 16-byte vectors; lane t
@@ -1170,13 +1192,18 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P)
   if (t == 0) {
     if (P.sl_max) P.sl_max[static_cast<size_t>(r) * P.S + s] = smax;   // the slice's largest key
     if (P.list_lb) P.list_lb[static_cast<size_t>(r) * P.S + s] = lb;
+    if (P.row_pub && s == 0)                        // written by the next launch's statistics
+      for (int i = 0; i < 3; ++i) P.row_pub[3 * static_cast<size_t>(r) + i] = 0ull;
   }
   const uint32_t cut = max(theta, 1u);    // a maximum of 0 (no entry) lists every entry
   // a vector holds a key >= cut iff its float maximum is >= the cut's value
   // (every real key is at least the key of -inf)
   const float cutf = cut <= f32_order_key(-INFINITY) ? -INFINITY : f32_from_order_key(cut);
   const int cap = P.seg_cap;
-  float *out = P.lists + static_cast<size_t>(r) * kCandCap + static_cast<size_t>(s) * cap;
+  const size_t seg = static_cast<size_t>(r) * kCandCap + static_cast<size_t>(s) * cap;
+  float *out = P.lists + seg;
+  int32_t *out_idx = P.list_idx ? P.list_idx + seg : nullptr;
+  const int v0 = s * SV::SL;                    // the slice's first index in the row
   bool stage[kSliceLoads];
   int c = 0;
 #pragma unroll
@@ -1210,15 +1237,20 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P)
     for (int i0 = 0; i0 < items; i0 += kSliceThreads) {     // same trip count in every lane
       const int i = i0 + t;
       uint32_t key = 0u;
+      int ve = 0;                               // the entry's index in the slice
       if (i < items) {
         const int j = i / VEC, e = i - j * VEC;
         const uint32_t w = reinterpret_cast<const uint32_t *>(&sh_vec[j])[BF16 ? (e >> 1) : e];
         const float z = __uint_as_float(BF16 ? ((e & 1) ? (w & 0xFFFF0000u) : (w << 16)) : w);
-        if (static_cast<int>(sh_vid[j]) * VEC + e < sl.n) key = f32_order_key(z);
+        ve = static_cast<int>(sh_vid[j]) * VEC + e;
+        if (ve < sl.n) key = f32_order_key(z);
       }
       const bool want = key >= cut;
       const int p = wave_append(want, &sh_n);
-      if (want && p < cap) out[p] = f32_from_order_key(key);
+      if (want && p < cap) {
+        out[p] = f32_from_order_key(key);
+        if (out_idx) out_idx[p] = v0 + ve;
+      }
     }
   } else {
 #pragma unroll
@@ -1229,7 +1261,10 @@ __global__ __launch_bounds__(kSliceThreads) void proc_slice_kernel(ProcParams P)
           const uint32_t key = sl.first(u) + e < sl.n ? f32_order_key(vec_entry<BF16>(q[u], e)) : 0u;
           if (key >= cut) {
             const int p = atomicAdd(&sh_n, 1);
-            if (p < cap) out[p] = f32_from_order_key(key);
+            if (p < cap) {
+              out[p] = f32_from_order_key(key);
+              if (out_idx) out_idx[p] = v0 + sl.first(u) + e;
+            }
           }
         }
       }
@@ -1350,6 +1385,436 @@ __global__ __launch_bounds__(256) void proc_export_kernel(const ProcStats *stats
   if (row_mass) row_mass[r] = st.mass;
 }
 
+// ---------------------------------------------------------------------------
+// Statistics and stochastic verification in one launch (top-k rows).
+//
+// With top-k through the slice lists, every entry a processed row keeps (its
+// order key at or above the row's threshold, itself at or above the row's
+// K-th largest key) is in that row's lists whenever every list fit its
+// segment.  So the token drawn at the end of a round, from p'_j - q'_j (first
+// rejection) or p'_k (all accepted), needs only the target row's kept entries
+// (p'_j is zero elsewhere, so is the residual): the finisher takes them from
+// the lists, orders them by index, and draws by the inverse CDF over them.
+// Two launches: the slice kernel (which also clears each row's published
+// words), then the statistics workgroups, one per row, each publishing its
+// row's statistics, and behind them (dispatch is in index order) one
+// finisher per sequence and, with offsets, one offsets workgroup.  While the
+// statistics are computed, a finisher loads everything that does not depend
+// on them: the drafts, uniforms and budget, the logits at the drafted tokens,
+// and the lengths and first 64 entries of every list of its k + 1 target
+// rows.  Once its 2k + 1 rows are published it takes the tries (the rule and
+// arithmetic of the other stochastic kernels), keeps the listed entries of
+// the row drawn from that reach its threshold, orders them by index, gathers
+// the draft's logits there (residual only) and draws.  A row whose lists
+// overflowed, or that keeps more than one entry per lane, is drawn from the
+// whole rows instead (chunk masses, then one chunk scanned in index order).
+
+struct ProcVerifyParams {
+  ProcParams proc;   // statistics of rows [0, B(k+1)) target, [B(k+1), B(2k+1)) draft;
+                     // proc.row_pub: cleared by the slice kernel, published here
+  SampleParams smp;  // the verification (smp.sp / smp.sq unused: the statistics travel
+                     // in proc.row_pub)
+};
+
+// A row's statistics travel as three 64-bit words written with agent-scope
+// atomic stores, each carrying a pattern no value here takes, so that every
+// published word is nonzero and a zero word means "not yet written": a NaN
+// in the half that holds zmax (inv_mass), which are never NaN, and the NaN
+// sentinel XOR-ed onto the mass (a finite non-negative double).
+constexpr uint32_t kHalfSentinel = 0x7FC00001u;
+constexpr unsigned long long kStatSentinel = 0x7FF4000000000001ull;
+__device__ inline void publish_stats(unsigned long long *w, const ProcStats &st) {
+  const unsigned long long w0 =
+      (static_cast<unsigned long long>(__float_as_uint(st.zmax) ^ kHalfSentinel) << 32) | st.theta;
+  const unsigned long long w1 = static_cast<unsigned long long>(__double_as_longlong(st.mass)) ^ kStatSentinel;
+  const unsigned long long w2 =
+      (static_cast<unsigned long long>(__float_as_uint(st.inv_mass) ^ kHalfSentinel) << 32) |
+      __float_as_uint(st.zmin_kept);
+  __hip_atomic_store(w + 0, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(w + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(w + 2, w2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Word f (0, 1, 2) of a row's statistics into st.
+__device__ inline void unpack_stats(ProcStats &st, int f, unsigned long long w) {
+  if (f == 0) {
+    st.zmax = __uint_as_float(static_cast<uint32_t>(w >> 32) ^ kHalfSentinel);
+    st.theta = static_cast<uint32_t>(w);
+  } else if (f == 1) {
+    st.mass = __longlong_as_double(static_cast<long long>(w ^ kStatSentinel));
+  } else {
+    st.inv_mass = __uint_as_float(static_cast<uint32_t>(w >> 32) ^ kHalfSentinel);
+    st.zmin_kept = __uint_as_float(static_cast<uint32_t>(w));
+  }
+}
+
+constexpr int kDenseChunk = kProcThreads * 16;                       // whole-row draw: entries per chunk
+constexpr int kDenseMaxChunks = (SPEC_PROC_MAX_V + kDenseChunk - 1) / kDenseChunk;
+constexpr int kPfPairs = 128;          // (target row, slice) lists whose head a finisher loads early
+constexpr int kPfHead = kWave;         // entries of a list's head
+constexpr int kMaxRows = 2 * SPEC_MAX_K + 1;
+
+// A finisher's LDS, carved from the statistics workgroups' histogram buffer
+// (the two roles never share a workgroup).
+struct FinishLds {
+  float pf_val[kPfPairs * kPfHead];    // list heads: logits, indices
+  int pf_idx[kPfPairs * kPfHead];
+  ProcStats stat[kMaxRows];            // the sequence's rows: target 0..k, then draft 0..k-1
+  int cnt[kPfPairs];                   // list lengths of the target rows (prefetched)
+  int cnt_row[kSliceMaxS];             // list lengths of the row drawn from (when not prefetched)
+  int idx[kProcThreads];               // kept entries: indices, in list order
+  float val[kProcThreads];             //   and logits
+  int ord[kProcThreads];               // ... in index order
+  float ordv[kProcThreads];
+  double cm[kDenseMaxChunks];          // whole-row draw: chunk masses
+};
+static_assert(sizeof(FinishLds) <= sizeof(unsigned long long) * 256 * kWave, "finisher LDS fits the histogram buffer");
+
+// Workgroup reductions over kProcThreads lanes in a fixed order (lanes of a
+// wave, then waves).  `sh` holds kProcWaves values; each contains barriers.
+__device__ inline double pv_sum(double v, double *sh) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  v = wave_sum_d(v);
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < kProcWaves; ++i) s += sh[i];
+  __syncthreads();
+  return s;
+}
+// Inclusive prefix sum of v in lane order; *total: the workgroup's sum.
+__device__ inline double pv_incl_scan(double v, double *sh, double *total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const double inc = wave_incl_scan(v);
+  if (lane == kWave - 1) sh[w] = inc;
+  __syncthreads();
+  double base = 0.0, tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < kProcWaves; ++i) {
+    if (i < w) base += sh[i];
+    tot += sh[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc;
+}
+// The smallest a and the largest b over the workgroup (one exchange).
+__device__ inline int2 pv_min_max(int a, int b, int2 *sh) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  a = wave_min(a);
+  b = wave_max_i(b);
+  if (lane == 0) sh[w] = make_int2(a, b);
+  __syncthreads();
+  int2 m = sh[0];
+#pragma unroll
+  for (int i = 1; i < kProcWaves; ++i) {
+    m.x = min(m.x, sh[i].x);
+    m.y = max(m.y, sh[i].y);
+  }
+  __syncthreads();
+  return m;
+}
+
+// Draw from the whole row r (LogitRow: p'_j - q'_j or p'_j): chunk masses
+// (16 consecutive entries per lane, in order), their sum S, the chunk whose
+// running sum first exceeds u * S (else the last with mass), then that chunk
+// scanned in index order.  Sets S (the mass drawn from) and st's bits as the
+// other stochastic kernels do.
+template <bool BF16>
+__device__ __forceinline__ int pv_draw_dense(LogitRow<BF16> r, int V, bool vec, float u_draw, double &S, int &st,
+                                             double *sh_cm, double *sh_d, int2 *sh_i) {
+  const int t = threadIdx.x;
+  const int nch = (V + kDenseChunk - 1) / kDenseChunk;
+  auto masses = [&]() {
+    for (int c = 0; c < nch; ++c) {
+      float x[16];
+      r.load16(x, c * kDenseChunk + t * 16, V, vec);
+      double a = 0.0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a += static_cast<double>(x[i]);
+      a = pv_sum(a, sh_d);
+      if (t == 0) sh_cm[c] = a;
+    }
+    __syncthreads();
+    double tot = 0.0;
+    for (int c = 0; c < nch; ++c) tot += sh_cm[c];
+    return tot;
+  };
+  S = masses();
+  if (isfinite(S) && !(S > 0.0)) {
+    st |= SPEC_ST_RESID_ZERO;
+    if (r.resid) {                      // fall back to the target row p'_j itself
+      r.resid = false;
+      __syncthreads();
+      S = masses();
+    }
+  }
+  if (!isfinite(S)) {
+    st |= SPEC_ST_NONFINITE;
+    return 0;
+  }
+  if (!(S > 0.0)) return 0;
+  const double T = static_cast<double>(u_draw) * S;
+  int cs = -1, last = -1;
+  double base = 0.0, lbase = 0.0, run = 0.0;
+  for (int c = 0; c < nch; ++c) {       // the same in every lane
+    const double m = sh_cm[c];
+    if (m > 0.0) {
+      last = c;
+      lbase = run;
+    }
+    if (run + m > T) {
+      cs = c;
+      base = run;
+      break;
+    }
+    run += m;
+  }
+  if (cs < 0) {
+    cs = last;
+    base = lbase;
+  }
+  const int lo = cs * kDenseChunk + t * 16;
+  float x[16];
+  r.load16(x, lo, V, vec);
+  double mine = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mine += static_cast<double>(x[i]);
+  double ctot;
+  double acc = base + (pv_incl_scan(mine, sh_d, &ctot) - mine);
+  int cpos = INT_MAX, lastpos = -1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int v = lo + i;
+    if (v < V) {
+      if (x[i] > 0.0f) lastpos = v;
+      acc += static_cast<double>(x[i]);
+      if (cpos == INT_MAX && acc > T) cpos = v;
+    }
+  }
+  const int2 mm = pv_min_max(cpos, lastpos, sh_i);
+  return mm.x != INT_MAX ? mm.x : mm.y;
+}
+
+// Finisher of sequence b (see above); lh: the workgroup's LDS buffer.
+template <bool BF16>
+__device__ __forceinline__ void pv_finish(const ProcVerifyParams &X, int b, unsigned long long *lh) {
+  using Src = LogitSrc<BF16>;
+  __shared__ int sh_acc[SPEC_MAX_K], sh_st[SPEC_MAX_K], sh_d[SPEC_MAX_K];
+  __shared__ int4 sh_ch;
+  __shared__ int sh_n;
+  __shared__ double sh_dw[kProcWaves];
+  __shared__ int2 sh_iw[kProcWaves];
+  FinishLds &L = *reinterpret_cast<FinishLds *>(lh);
+  const SampleParams &P = X.smp;
+  const ProcParams &Q = X.proc;
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+  const int k = P.k, kp1 = k + 1, nr = 2 * k + 1, V = P.V;
+  const int nS = Q.S, cap = Q.seg_cap;
+  auto row_of = [&](int i) { return i < kp1 ? b * kp1 + i : P.B * kp1 + b * k + (i - kp1); };
+  auto seg_of = [&](int j, int q) {            // list segment q of target row j
+    return static_cast<size_t>(b * kp1 + j) * kCandCap + static_cast<size_t>(q) * cap;
+  };
+
+  // ---- before the statistics: drafts, uniforms, budget, logits at the
+  //      drafted tokens, and the target rows' list lengths and heads
+  const float u_draw = P.u[static_cast<size_t>(b) * kp1 + k];
+  const int rem = P.remaining ? P.remaining[b] : -1;       // negative: no budget
+  int x_t = -1;
+  float u_t = 0.0f, zp_t = 0.0f, zq_t = 0.0f;
+  if (t < k) {
+    x_t = P.draft[static_cast<size_t>(b) * k + t];
+    u_t = P.u[static_cast<size_t>(b) * kp1 + t];
+    if (x_t >= 0 && x_t < V) {
+      zp_t = logit_at<BF16>(Src::prow(P, b, t), x_t);
+      zq_t = logit_at<BF16>(Src::qrow(P, b, t), x_t);
+    }
+  }
+  const int npair = kp1 * nS;
+  const bool pre = npair <= kPfPairs;
+  if (pre) {
+    if (t < npair) L.cnt[t] = Q.list_cnt[static_cast<size_t>(b * kp1 + t / nS) * nS + t % nS];
+    for (int pr = w; pr < npair; pr += kProcWaves) {   // the head of every list (inside its segment)
+      const size_t e = seg_of(pr / nS, pr % nS) + lane;
+      L.pf_val[pr * kPfHead + lane] = Q.lists[e];
+      L.pf_idx[pr * kPfHead + lane] = Q.list_idx[e];
+    }
+  }
+
+  // ---- the statistics of the sequence's 2k + 1 rows (bounded wait); they
+  //      arrive in the published words themselves
+  const int nwords = 3 * nr;
+  unsigned long long word = 0ull;
+  const unsigned long long *src = t < nwords ? Q.row_pub + 3 * static_cast<size_t>(row_of(t / 3)) + t % 3 : nullptr;
+  int polls = 0;
+  bool timed_out = false;
+  while (true) {
+    if (t < nwords && word == 0ull) word = load_agent(src);
+    if (__syncthreads_and(t >= nwords || word != 0ull)) break;
+    if (++polls >= kMaxPolls) {
+      timed_out = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (timed_out) {                                    // no chain without the statistics: nothing emitted
+    if (t < kp1) P.out_tokens[static_cast<size_t>(b) * kp1 + t] = -1;
+    if (t == 0) {
+      P.accept_len[b] = 0;
+      P.emit_count[b] = 0;
+      if (P.emit_offsets) __hip_atomic_store(P.ecnt + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (P.final_mass) P.final_mass[b] = 0.0;
+      if (P.status) P.status[b] = SPEC_ST_INCOMPLETE;
+    }
+    return;
+  }
+  if (t < nwords) unpack_stats(L.stat[t / 3], t % 3, word);
+  __syncthreads();
+
+  // ---- the tries and the chain
+  if (t < k) {
+    int2 r = make_int2(0, SPEC_ST_DRAFT_OOR);
+    if (x_t >= 0 && x_t < V)
+      r = try_draft(proc_prob(zp_t, L.stat[t], P.invT), proc_prob(zq_t, L.stat[kp1 + t], P.invT), u_t);
+    sh_acc[t] = r.x;
+    sh_st[t] = r.y;
+    sh_d[t] = x_t;
+  }
+  __syncthreads();
+  if (t == 0) sh_ch = fold_chain(k, rem, P.eos, sh_acc, sh_st, sh_d);
+  __syncthreads();
+  const int4 ch = sh_ch;
+  const int mode = ch.x, jrow = ch.y, m = ch.z;
+  const int emit = m + (mode != MODE_NONE ? 1 : 0);
+  if (t == 0) {
+    P.accept_len[b] = m;
+    P.emit_count[b] = emit;
+    if (P.emit_offsets) __hip_atomic_store(P.ecnt + b, emit + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  int st = ch.w;
+  int tok = -1;
+  double S = 0.0;
+  if (mode != MODE_NONE) {
+    const bool resid = mode == MODE_RESID;
+    LogitRow<BF16> r;
+    r.a = Src::prow(P, b, jrow);
+    r.sa = L.stat[jrow];
+    r.b = resid ? Src::qrow(P, b, jrow) : nullptr;
+    if (resid) r.sb = L.stat[kp1 + jrow];
+    r.invT = P.invT;
+    r.resid = resid;
+    const int *cnt = pre ? L.cnt + jrow * nS : L.cnt_row;
+    if (!pre) {
+      if (t < nS) L.cnt_row[t] = Q.list_cnt[static_cast<size_t>(b * kp1 + jrow) * nS + t];
+    }
+    if (t == 0) sh_n = 0;
+    __syncthreads();
+    bool complete = true;
+    for (int q = 0; q < nS; ++q) complete = complete && cnt[q] <= cap;
+    if (complete && r.sa.mass > 0.0) {
+      // the kept entries of the row drawn from (wave w: lists w, w + 16, ...)
+      for (int q = w; q < nS; q += kProcWaves) {
+        const int c = cnt[q];
+        const size_t seg = seg_of(jrow, q);
+        for (int i0 = 0; i0 < c; i0 += kWave) {
+          const int i = i0 + lane;
+          bool keep = false;
+          float z = 0.0f;
+          int v = 0;
+          if (i < c) {
+            if (pre && i < kPfHead) {
+              z = L.pf_val[(jrow * nS + q) * kPfHead + i];
+              v = L.pf_idx[(jrow * nS + q) * kPfHead + i];
+            } else {
+              z = Q.lists[seg + i];
+              v = Q.list_idx[seg + i];
+            }
+            keep = f32_order_key(z) >= r.sa.theta;
+          }
+          const int slot = wave_append(keep, &sh_n);
+          if (keep && slot < kProcThreads) {
+            L.idx[slot] = v;
+            L.val[slot] = z;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int n = sh_n;
+    if (complete && n <= kProcThreads) {
+      // order the n kept entries by index (distinct), one per lane
+      if (t >= n && t < ((n + 3) & ~3)) L.idx[t] = INT_MAX;
+      if (t < n) L.ord[t] = -1;
+      __syncthreads();
+      if (t < n) {
+        const int my = L.idx[t];
+        const int4 *q4 = reinterpret_cast<const int4 *>(L.idx);
+        int rank = 0;
+        for (int i = 0; i < (n + 3) >> 2; ++i) {
+          const int4 e = q4[i];
+          rank += (e.x < my) + (e.y < my) + (e.z < my) + (e.w < my);
+        }
+        L.ord[rank] = my;
+        L.ordv[rank] = L.val[t];
+      }
+      __syncthreads();
+      const int v = t < n ? L.ord[t] : -1;
+      float pa = 0.0f, x = 0.0f;
+      if (v >= 0 && v < V) {
+        // a listed logit is the row's (a -0 comes back as +0, with the same
+        // key and weight)
+        pa = proc_prob(L.ordv[t], r.sa, r.invT);
+        x = resid ? fmaxf(pa - proc_prob(logit_at<BF16>(r.b, v), r.sb, r.invT), 0.0f) : pa;
+      }
+      double incl = pv_incl_scan(static_cast<double>(x), sh_dw, &S);
+      if (isfinite(S) && !(S > 0.0)) {
+        st |= SPEC_ST_RESID_ZERO;
+        if (resid) {                                  // fall back to the target row p'_j itself
+          x = pa;
+          incl = pv_incl_scan(static_cast<double>(x), sh_dw, &S);
+        }
+      }
+      if (!isfinite(S)) {
+        st |= SPEC_ST_NONFINITE;
+        tok = 0;
+      } else if (!(S > 0.0)) {
+        tok = 0;
+      } else {
+        const double T = static_cast<double>(u_draw) * S;
+        const int2 mm = pv_min_max(t < n && incl > T ? t : INT_MAX, t < n && x > 0.0f ? t : -1, sh_iw);
+        tok = max(L.ord[mm.x != INT_MAX ? mm.x : mm.y], 0);
+      }
+    } else {
+      tok = pv_draw_dense<BF16>(r, V, P.vec != 0, u_draw, S, st, L.cm, sh_dw, sh_iw);
+    }
+  }
+  if (t < kp1) {                                      // accepted drafts, then the drawn token
+    int val = -1;
+    if (t < m) val = x_t;
+    else if (t == m && mode != MODE_NONE) val = tok;
+    P.out_tokens[static_cast<size_t>(b) * kp1 + t] = val;
+  }
+  if (t == 0) {
+    if (P.final_mass) P.final_mass[b] = mode != MODE_NONE ? S : 0.0;
+    if (P.status) P.status[b] = st;
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kProcThreads) void proc_verify_kernel(ProcVerifyParams X) {
+  // the statistics' histograms, or a finisher's staging
+  __shared__ unsigned long long lh[256 * kWave];
+  const int blk = blockIdx.x, rows = X.proc.rows;
+  if (blk < rows) {
+    const ProcStats st = proc_row_stats<BF16>(X.proc, blk, lh);
+    if (threadIdx.x == 0) publish_stats(X.proc.row_pub + 3 * static_cast<size_t>(blk), st);
+  } else if (blk < rows + X.smp.B) {
+    pv_finish<BF16>(X, blk - rows, lh);
+  } else {
+    finish_offsets(X.smp);
+  }
+}
+
 }  // namespace
 
 // Launches the statistics kernel over rows [0, rows); shared with the
@@ -1376,9 +1841,8 @@ static ProcWs proc_ws_layout(int rows, int V) {
 
 size_t proc_list_bytes(int rows, int V) { return proc_ws_layout(rows, V).total; }
 
-int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int V, bool bf16,
-                      Temper invT, int top_k, float top_p, ProcStats *stats, float *probs,
-                      void *list_ws, hipStream_t s) {
+static ProcParams proc_params(const void *za, const void *zb, int rows_a, int rows, int V, bool bf16, Temper invT,
+                              int top_k, float top_p, ProcStats *stats, float *probs) {
   ProcParams P;
   P.za = za;
   P.zb = zb;
@@ -1394,6 +1858,8 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
   P.list_cnt = nullptr;
   P.list_cut = nullptr;
   P.list_lb = nullptr;
+  P.list_idx = nullptr;
+  P.row_pub = nullptr;
   P.lb_rank = 0;
   P.sl_max = P.sl_min = nullptr;
   P.sl_tot = nullptr;
@@ -1401,27 +1867,44 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
   P.S = (V + slice - 1) / slice;
   P.seg_cap = kCandCap / P.S;
   P.cut_rank = 0;
+  return P;
+}
+
+// Top-k through the slice lists: K <= 256 (the cut is the K-th largest of a
+// slice's 256 lane maxima) and lists of at most half a segment.
+static bool topk_lists(const ProcParams &P, int top_k, int V) {
+  return top_k > 0 && top_k < V && top_k <= kSliceThreads && top_k <= P.seg_cap / 2;
+}
+
+// The slice kernel, listing each slice at its rank-th largest lane maximum
+// (bounds: also each slice's ceil(K / S)-th largest, for top-k).
+static void launch_slices(ProcParams &P, const ProcWs &L, unsigned char *w, int rank, bool bounds, int top_k,
+                          bool bf16, hipStream_t s) {
+  P.lists = reinterpret_cast<float *>(w + L.lists);
+  P.list_cnt = reinterpret_cast<int *>(w + L.cnt);
+  P.list_cut = reinterpret_cast<uint32_t *>(w + L.cut);
+  P.cut_rank = rank;
+  if (bounds) {
+    P.list_lb = reinterpret_cast<uint32_t *>(w + L.lb);
+    P.lb_rank = (top_k + P.S - 1) / P.S;
+  }
+  const dim3 g(static_cast<unsigned>(P.rows * P.S)), blk(kSliceThreads);
+  if (bf16)
+    hipLaunchKernelGGL(proc_slice_kernel<true>, g, blk, 0, s, P);
+  else
+    hipLaunchKernelGGL(proc_slice_kernel<false>, g, blk, 0, s, P);
+}
+
+int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int V, bool bf16,
+                      Temper invT, int top_k, float top_p, ProcStats *stats, float *probs,
+                      void *list_ws, hipStream_t s) {
+  ProcParams P = proc_params(za, zb, rows_a, rows, V, bf16, invT, top_k, top_p, stats, probs);
   if (list_ws) {
     const ProcWs L = proc_ws_layout(rows, V);
     unsigned char *w = static_cast<unsigned char *>(list_ws);
     const dim3 g(static_cast<unsigned>(rows * P.S)), blk(kSliceThreads);
-    auto lists = [&](int rank, bool bounds) {
-      P.lists = reinterpret_cast<float *>(w + L.lists);
-      P.list_cnt = reinterpret_cast<int *>(w + L.cnt);
-      P.list_cut = reinterpret_cast<uint32_t *>(w + L.cut);
-      P.cut_rank = rank;
-      if (bounds) {               // top-k lists: each slice also gives its ceil(K / S)-th largest lane maximum
-        P.list_lb = reinterpret_cast<uint32_t *>(w + L.lb);
-        P.lb_rank = (top_k + P.S - 1) / P.S;
-      }
-      if (bf16)
-        hipLaunchKernelGGL(proc_slice_kernel<true>, g, blk, 0, s, P);
-      else
-        hipLaunchKernelGGL(proc_slice_kernel<false>, g, blk, 0, s, P);
-    };
     if (top_k > 0 && top_k < V) {
-      // top-k through the slice lists (the cut is the K-th largest of a slice's 256 lane maxima)
-      if (top_k <= kSliceThreads && top_k <= P.seg_cap / 2) lists(top_k, true);
+      if (topk_lists(P, top_k, V)) launch_slices(P, L, w, top_k, true, top_k, bf16, s);
     } else {
       // no top-k: slice maxima (with top-p: the lists cut at the kToppRank-th
       // largest lane maximum, which also give them), then slice weights and
@@ -1430,7 +1913,7 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
       P.sl_min = reinterpret_cast<uint32_t *>(w + L.smin);
       P.sl_tot = reinterpret_cast<unsigned long long *>(w + L.stot);
       if (top_p < 1.0f && kToppRank <= P.seg_cap / 2) {
-        lists(kToppRank, false);
+        launch_slices(P, L, w, kToppRank, false, top_k, bf16, s);
       } else if (bf16) {
         hipLaunchKernelGGL(proc_slrange_kernel<true>, g, blk, 0, s, P);
       } else {
@@ -1447,6 +1930,26 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
   else
     hipLaunchKernelGGL(proc_stats_kernel<false>, dim3(static_cast<unsigned>(rows)), dim3(kProcThreads), 0, s, P);
   return 0;
+}
+
+size_t proc_list_idx_bytes(int rows) { return round_up(static_cast<size_t>(rows) * kCandCap * sizeof(int32_t), 256); }
+
+bool launch_sample_logits_topk(const SampleParams &S, bool bf16, int top_k, float top_p, ProcStats *stats,
+                               void *list_ws, int32_t *list_idx, unsigned long long *row_pub, hipStream_t s) {
+  const int rows_a = S.B * (S.k + 1), rows = S.B * (2 * S.k + 1);
+  ProcVerifyParams X;
+  X.proc = proc_params(S.zp, S.zq, rows_a, rows, S.V, bf16, S.invT, top_k, top_p, stats, nullptr);
+  if (!topk_lists(X.proc, top_k, S.V)) return false;
+  X.proc.list_idx = list_idx;
+  X.proc.row_pub = row_pub;
+  launch_slices(X.proc, proc_ws_layout(rows, S.V), static_cast<unsigned char *>(list_ws), top_k, true, top_k, bf16, s);
+  X.smp = S;
+  const dim3 g(static_cast<unsigned>(rows + S.B + (S.emit_offsets ? 1 : 0))), blk(kProcThreads);
+  if (bf16)
+    hipLaunchKernelGGL(proc_verify_kernel<true>, g, blk, 0, s, X);
+  else
+    hipLaunchKernelGGL(proc_verify_kernel<false>, g, blk, 0, s, X);
+  return true;
 }
 
 bool proc_args_ok(float T, int top_k, float top_p, int V) {

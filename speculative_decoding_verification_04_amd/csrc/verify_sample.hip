@@ -29,37 +29,10 @@
 // All sums are float64 over the float32 r_v in a fixed order, so results are
 // reproducible run to run and within ~1e-16 relative of a correctly rounded
 // sum.
-#include "process.h"
+#include "sample_src.h"
 
 namespace specv {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kU = 4;                               // float4 loads in flight per lane
-constexpr int kChunk = kThreads * 4 * kU;           // elements per chunk
-constexpr int kEPT = kChunk / kThreads;             // elements per lane in the in-chunk scan
-constexpr int kMaxChunks = 1024;                    // V <= kMaxChunks * kChunk
-
-enum : int { MODE_NONE = 0, MODE_RESID = 1, MODE_ROW = 2 };
-
-struct SampleParams {
-  const float *p, *q;           // dense rows (spec_verify_sample)
-  const void *zp, *zq;          // logits (spec_verify_sample_logits)
-  const ProcStats *sp, *sq;     // statistics of the processed rows
-  Temper invT;                  // 1 / temperature
-  const int32_t *draft;
-  const float *u;
-  int B, k, V, chunks;
-  int vec;                      // rows are 16-byte aligned (V % 4 == 0 and aligned bases)
-  int32_t eos;
-  const int32_t *remaining;
-  int32_t *accept_len, *emit_count, *out_tokens, *emit_offsets;
-  double *final_mass;
-  int32_t *status;
-  unsigned long long *keys;     // [B * chunks] published chunk masses (0: not yet written)
-  int32_t *ecnt;                // [B] published emit_count + 1 (0: not yet written)
-};
 
 // Workspace: the chunk-mass slots, then the emit-count slots; zero-filled on
 // entry and left zero-filled by every call.
@@ -73,145 +46,6 @@ inline SampleWs sample_ws_layout(int B, int chunks) {
   w.total = w.ecnt + round_up(static_cast<size_t>(B) * sizeof(int32_t), 256);
   return w;
 }
-
-// The mass vector a drawn token comes from: r_v = max(a_v - b_v, 0) when
-// `resid` is set, else r_v = a_v.  DenseRow reads given float32 rows;
-// LogitRow<BF16> computes the processed rows p', q' from logits on the fly.
-struct DenseRow {
-  const float *a, *b;
-  bool resid;
-  __device__ inline float at(int v) const { return resid ? fmaxf(a[v] - b[v], 0.0f) : a[v]; }
-  // The 16 values v0 .. v0 + 15 (0 past V); 16-byte loads when `vec` (16-byte
-  // aligned rows, v0 a multiple of 4) and the run is inside the row.
-  __device__ inline void load16(float (&x)[16], int v0, int V, bool vec) const {
-    if (vec && v0 + 16 <= V) {
-      float4 A[4], Bv[4];
-      const float4 *pa = reinterpret_cast<const float4 *>(a + v0);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) A[u] = pa[u];
-      if (resid) {
-        const float4 *pb = reinterpret_cast<const float4 *>(b + v0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) Bv[u] = pb[u];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          x[4 * u + 0] = fmaxf(A[u].x - Bv[u].x, 0.0f);
-          x[4 * u + 1] = fmaxf(A[u].y - Bv[u].y, 0.0f);
-          x[4 * u + 2] = fmaxf(A[u].z - Bv[u].z, 0.0f);
-          x[4 * u + 3] = fmaxf(A[u].w - Bv[u].w, 0.0f);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          x[4 * u + 0] = A[u].x;
-          x[4 * u + 1] = A[u].y;
-          x[4 * u + 2] = A[u].z;
-          x[4 * u + 3] = A[u].w;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = v0 + i < V ? at(v0 + i) : 0.0f;
-    }
-  }
-};
-
-template <bool BF16>
-struct LogitRow {
-  const void *a, *b;
-  ProcStats sa, sb;
-  Temper invT;
-  bool resid;
-  __device__ inline float at(int v) const {
-    const float pa = proc_prob(logit_at<BF16>(a, v), sa, invT);
-    return resid ? fmaxf(pa - proc_prob(logit_at<BF16>(b, v), sb, invT), 0.0f) : pa;
-  }
-  // 16 logits from v0 (a multiple of 8 for bf16, 4 for f32) as float32.
-  __device__ static inline void load_z(float (&z)[16], const void *row, int v0) {
-    if constexpr (BF16) {
-      const uint4 *pr = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(row) + v0);
-      const uint4 w0 = pr[0], w1 = pr[1];
-      const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        z[2 * i] = __uint_as_float(w[i] << 16);
-        z[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-    } else {
-      const float4 *pr = reinterpret_cast<const float4 *>(static_cast<const float *>(row) + v0);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float4 f = pr[u];
-        z[4 * u + 0] = f.x;
-        z[4 * u + 1] = f.y;
-        z[4 * u + 2] = f.z;
-        z[4 * u + 3] = f.w;
-      }
-    }
-  }
-  // The 16 processed values v0 .. v0 + 15 (0 past V); 16-byte loads when
-  // `vec` (16-byte aligned rows) and the run is inside the row.
-  __device__ inline void load16(float (&x)[16], int v0, int V, bool vec) const {
-    if (vec && v0 + 16 <= V) {
-      float za[16], zb[16];
-      load_z(za, a, v0);
-      if (resid) load_z(zb, b, v0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pa = proc_prob(za[i], sa, invT);
-        x[i] = resid ? fmaxf(pa - proc_prob(zb[i], sb, invT), 0.0f) : pa;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = v0 + i < V ? at(v0 + i) : 0.0f;
-    }
-  }
-};
-
-struct DenseSrc {
-  using RowT = DenseRow;
-  __device__ static inline float p_at(const SampleParams &P, int b, int j, int x) {
-    return P.p[(static_cast<size_t>(b) * (P.k + 1) + j) * P.V + x];
-  }
-  __device__ static inline float q_at(const SampleParams &P, int b, int j, int x) {
-    return P.q[(static_cast<size_t>(b) * P.k + j) * P.V + x];
-  }
-  __device__ static inline DenseRow row(const SampleParams &P, int b, int j, bool resid) {
-    DenseRow r;
-    r.a = P.p + (static_cast<size_t>(b) * (P.k + 1) + j) * P.V;
-    r.b = resid ? P.q + (static_cast<size_t>(b) * P.k + j) * P.V : nullptr;
-    r.resid = resid;
-    return r;
-  }
-};
-
-template <bool BF16>
-struct LogitSrc {
-  using RowT = LogitRow<BF16>;
-  static constexpr size_t kElt = BF16 ? 2 : 4;
-  __device__ static inline const void *prow(const SampleParams &P, int b, int j) {
-    return static_cast<const unsigned char *>(P.zp) + (static_cast<size_t>(b) * (P.k + 1) + j) * P.V * kElt;
-  }
-  __device__ static inline const void *qrow(const SampleParams &P, int b, int j) {
-    return static_cast<const unsigned char *>(P.zq) + (static_cast<size_t>(b) * P.k + j) * P.V * kElt;
-  }
-  __device__ static inline float p_at(const SampleParams &P, int b, int j, int x) {
-    return proc_prob(logit_at<BF16>(prow(P, b, j), x), P.sp[static_cast<size_t>(b) * (P.k + 1) + j], P.invT);
-  }
-  __device__ static inline float q_at(const SampleParams &P, int b, int j, int x) {
-    return proc_prob(logit_at<BF16>(qrow(P, b, j), x), P.sq[static_cast<size_t>(b) * P.k + j], P.invT);
-  }
-  __device__ static inline LogitRow<BF16> row(const SampleParams &P, int b, int j, bool resid) {
-    LogitRow<BF16> r;
-    r.a = prow(P, b, j);
-    r.sa = P.sp[static_cast<size_t>(b) * (P.k + 1) + j];
-    r.b = resid ? qrow(P, b, j) : nullptr;
-    if (resid) r.sb = P.sq[static_cast<size_t>(b) * P.k + j];
-    r.invT = P.invT;
-    r.resid = resid;
-    return r;
-  }
-};
 
 __device__ inline double block_sum_d(double v, double *sh) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -258,70 +92,6 @@ __device__ inline double chunk_mass(const RowT &r, int c, int V, bool vec, doubl
   return block_sum_d(acc, sh);
 }
 
-template <typename T>
-__device__ inline bool finite_val(T x) { return isfinite(x); }
-
-// The acceptance chain of sequence b, derived by every workgroup that needs
-// it from the same gathers and the same float32 arithmetic (so all of them
-// agree): x.mode, y.row drawn from, z.accepted drafts, w.status bits.
-// Contains barriers.
-template <class Src>
-__device__ inline int4 derive_chain(const SampleParams &P, int b, int *sh_acc, int *sh_st, int *sh_d,
-                                    int4 *sh_ch) {
-  const int t = threadIdx.x;
-  const int k = P.k, kp1 = k + 1, V = P.V;
-  const int32_t *d = P.draft + static_cast<size_t>(b) * k;
-  const float *ub = P.u + static_cast<size_t>(b) * kp1;
-  const int rem = P.remaining ? P.remaining[b] : -1;   // negative: no budget (loaded with the drafts)
-  for (int j = t; j < k; j += kThreads) {
-    const int x = d[j];
-    sh_d[j] = x;
-    int st = 0, acc = 0;
-    if (x >= 0 && x < V) {
-      const float px = Src::p_at(P, b, j, x);
-      const float qx = Src::q_at(P, b, j, x);
-      if (!finite_val(px) || !finite_val(qx)) st |= SPEC_ST_NONFINITE;
-      float a;
-      if (qx == 0.0f) {
-        a = px > 0.0f ? 1.0f : 0.0f;
-        st |= SPEC_ST_Q_ZERO;
-      } else {
-        const float ratio = __fdiv_rn(px, qx);
-        a = ratio < 1.0f ? ratio : 1.0f;
-      }
-      acc = ub[j] < a;
-    } else {
-      st |= SPEC_ST_DRAFT_OOR;
-    }
-    sh_acc[j] = acc;
-    sh_st[j] = st;
-  }
-  __syncthreads();
-  if (t == 0) {
-    int mode = MODE_ROW, row = k, m = 0, st = 0;
-    if (rem == 0) {
-      mode = MODE_NONE;
-    } else {
-      for (int j = 0; j < k; ++j) {
-        st |= sh_st[j];
-        if (sh_acc[j]) {
-          ++m;
-          if ((P.eos >= 0 && sh_d[j] == P.eos) || m == rem) {
-            mode = MODE_NONE;
-            break;
-          }
-        } else {
-          mode = MODE_RESID;
-          row = j;
-          break;
-        }
-      }
-    }
-    *sh_ch = make_int4(mode, row, m, st);
-  }
-  __syncthreads();
-  return *sh_ch;
-}
 
 // Chunk masses travel as 64-bit keys: the mass's bits XOR kMassSentinel.
 // The sentinel is a NaN whose low 29 bits are not all zero, a pattern no mass
@@ -329,7 +99,6 @@ __device__ inline int4 derive_chain(const SampleParams &P, int b, int *sh_acc, i
 // values, gives NaNs with those bits zero), so every published key is nonzero
 // and a zero slot means "not yet written".
 constexpr unsigned long long kMassSentinel = 0x7FF4000000000001ull;
-constexpr int kMaxPolls = 1 << 22;      // about 4 s of polling: a bound every wait reaches
 
 // Producer: chunk c of the row sequence b draws from; its mass published.
 template <class Src>
@@ -521,33 +290,6 @@ __device__ inline void finish_sequence(const SampleParams &P, int b) {
   }
 }
 
-// Emit offsets: the finishers publish emit_count + 1 per sequence as soon as
-// their chains are known; one workgroup scans them and clears the slots.
-__device__ inline void finish_offsets(const SampleParams &P) {
-  __shared__ int sh[kWaves + 1];
-  const int n = P.B, T = kThreads;
-  const int per = (n + T - 1) / T;
-  const int lo = min(n, static_cast<int>(threadIdx.x) * per), hi = min(n, lo + per);
-  int polls = 0;
-  while (true) {
-    bool present = true;
-    for (int i = lo; i < hi; ++i) present = present && load_agent(P.ecnt + i) != 0;
-    if (__syncthreads_and(present)) break;
-    if (++polls >= kMaxPolls) break;              // outputs unspecified; the wait still ends
-    __builtin_amdgcn_s_sleep(1);
-  }
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += max(load_agent(P.ecnt + i) - 1, 0);
-  int total;
-  int base = block_excl_scan(s, sh, &total);
-  for (int i = lo; i < hi; ++i) {
-    P.emit_offsets[i] = base;
-    base += max(load_agent(P.ecnt + i) - 1, 0);
-    P.ecnt[i] = 0;
-  }
-  if (threadIdx.x == 0) P.emit_offsets[n] = total;
-}
-
 // One launch: B * chunks producers, then the B finishers, then (with
 // offsets) the offsets workgroup.  Workgroups are dispatched in index order,
 // so a waiting workgroup is dispatched only after every producer it waits on
@@ -641,11 +383,22 @@ extern "C" int spec_verify_sample(const float *p, const float *q, const int32_t 
 }
 
 // Workspace of the verification from logits: per-row statistics of the
-// B * (k+1) target and B * k draft rows, then the layout of spec_verify_sample.
-static size_t sample_logits_stats_bytes(int B, int k, int V) {
-  return round_up(static_cast<size_t>(B) * (2 * k + 1) * sizeof(ProcStats), 256) +
-         proc_list_bytes(B * (2 * k + 1), V);
+// B * (k+1) target and B * k draft rows, the slice lists, their entries'
+// indices and three published words per row (all rewritten by every call),
+// then the layout of spec_verify_sample.
+struct LogitsWs {
+  size_t lists, idx, flags, total;
+};
+static LogitsWs sample_logits_layout(int B, int k, int V) {
+  const int rows = B * (2 * k + 1);
+  LogitsWs w;
+  w.lists = round_up(static_cast<size_t>(rows) * sizeof(ProcStats), 256);
+  w.idx = w.lists + proc_list_bytes(rows, V);
+  w.flags = w.idx + proc_list_idx_bytes(rows);
+  w.total = w.flags + round_up(static_cast<size_t>(rows) * 3 * sizeof(unsigned long long), 256);
+  return w;
 }
+static size_t sample_logits_stats_bytes(int B, int k, int V) { return sample_logits_layout(B, k, V).total; }
 
 extern "C" size_t spec_verify_sample_logits_workspace_bytes(int B, int k, int V) {
   if (B < 1 || k < 1 || V < 1 || k > SPEC_MAX_K || V > SPEC_PROC_MAX_V || sample_chunks(V) > kMaxChunks) return 0;
@@ -721,10 +474,16 @@ extern "C" int spec_verify_sample_logits(const void *target_logits, const void *
   P.ecnt = reinterpret_cast<int32_t *>(wb + stats_bytes + lay.ecnt);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dt == SPEC_BF16;
+  const LogitsWs lw = sample_logits_layout(B, k, V);
   (void)hipGetLastError();
+  // top-k through the slice lists: the slice kernel, then statistics and
+  // verification in one launch
+  if (launch_sample_logits_topk(P, bf16, top_k, top_p, stats, wb + lw.lists,
+                                reinterpret_cast<int32_t *>(wb + lw.idx),
+                                reinterpret_cast<unsigned long long *>(wb + lw.flags), s))
+    return launch_status();
   launch_proc_stats(target_logits, draft_logits, B * (k + 1), static_cast<int>(rows), V, bf16, P.invT,
-                    top_k, top_p, stats, nullptr,
-                    wb + round_up(static_cast<size_t>(rows) * sizeof(ProcStats), 256), s);
+                    top_k, top_p, stats, nullptr, wb + lw.lists, s);
   const dim3 grid = sample_grid(B, chunks, emit_offsets), blk(kThreads);
   if (bf16)
     hipLaunchKernelGGL(sample_verify_kernel<LogitSrc<true>>, grid, blk, 0, s, P);

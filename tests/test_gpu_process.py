@@ -311,6 +311,50 @@ def test_verify_from_logits_workload_full_size(dtype):
     _assert_counts(counts, 8)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_verify_from_logits_crowded_and_tied_rows(dtype):
+    """Top-k rows whose kept entries are not a short list: every logit equal
+    (the slice lists overflow), 2000 logits tied at the top (the lists hold
+    them, but more than one per lane of the drawing workgroup), half -inf and
+    half equal, a narrow spread; beside ordinary rows and a target row of
+    -inf only (no mass: the draw gives token 0 with SPEC_ST_RESID_ZERO).
+    The draws then come from the whole rows instead of the lists."""
+    rng = np.random.default_rng(61)
+    B, k, V = 6, 2, 60000
+    zt = (rng.standard_normal((B, k + 1, V)) * 1.0).astype(np.float32)
+    zt[0] = 0.0
+    top = rng.choice(V, 2000, replace=False)
+    zt[1] *= 0.5
+    zt[1][:, top] = 5.0
+    zt[2][:, ::2] = -np.inf
+    zt[2][:, 1::2] = 1.5
+    zt[3] *= 3.0
+    zt[4] *= 0.01
+    zt[5, 0] = -np.inf
+    zd_ = (zt[:, :k] + rng.standard_normal((B, k, V)) * 0.3).astype(np.float32)
+    zd_[2] = np.where(np.isinf(zt[2, :k]), -np.inf, 1.5).astype(np.float32)
+    zd_[2][:, rng.choice(np.arange(1, V, 2), 100, replace=False)] = 2.0
+    for T, K, P in [(1.0, 50, 1.0), (0.7, 50, 0.9), (1.0, 256, 0.95)]:
+        note(f"verify logits crowded {dtype} T={T} K={K} P={P}")
+        counts, got, ref = _verify_case(zt, zd_, T, K, P, 62, dtype)
+        _assert_counts(counts, B)
+        assert got["emit_offsets"][-1] == got["emit_count"].sum()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_verify_from_logits_largest_vocabulary(dtype):
+    """V = SPEC_PROC_MAX_V with top-k: the most slices per row (64 for f32,
+    more than the drawing workgroup has waves) and the smallest lists."""
+    rng = np.random.default_rng(524)
+    B, k, V = 2, 1, sv.SPEC_PROC_MAX_V
+    zt = (rng.standard_normal((B, k + 1, V)) * 2.0).astype(np.float32)
+    zd_ = (zt[:, :k] + rng.standard_normal((B, k, V)) * 0.7).astype(np.float32)
+    for T, K, P in [(0.7, 50, 0.9), (1.0, 200, 1.0)]:
+        note(f"verify logits largest V {dtype} T={T} K={K} P={P}")
+        counts, got, ref = _verify_case(zt, zd_, T, K, P, 63, dtype)
+        _assert_counts(counts, B)
+
+
 def test_verify_from_logits_output_law():
     """The emitted token follows p' (drafts weighted by q', stratified grids)."""
     zt1 = np.log(np.array([0.5, 0.3, 0.15, 0.05])).astype(np.float32)
