@@ -1703,18 +1703,20 @@ __device__ __forceinline__ void pv_finish(const ProcVerifyParams &X, int b, unsi
     if (resid) r.sb = L.stat[kp1 + jrow];
     r.invT = P.invT;
     r.resid = resid;
-    const int *cnt = pre ? L.cnt + jrow * nS : L.cnt_row;
+    // list lengths of the row drawn from (indexed, not through a pointer
+    // that may point anywhere: LDS reads then wait for LDS only)
+    auto cnt = [&](int q) { return pre ? L.cnt[jrow * nS + q] : L.cnt_row[q]; };
     if (!pre) {
       if (t < nS) L.cnt_row[t] = Q.list_cnt[static_cast<size_t>(b * kp1 + jrow) * nS + t];
     }
     if (t == 0) sh_n = 0;
     __syncthreads();
     bool complete = true;
-    for (int q = 0; q < nS; ++q) complete = complete && cnt[q] <= cap;
+    for (int q = 0; q < nS; ++q) complete = complete && cnt(q) <= cap;
     if (complete && r.sa.mass > 0.0) {
       // the kept entries of the row drawn from (wave w: lists w, w + 16, ...)
       for (int q = w; q < nS; q += kProcWaves) {
-        const int c = cnt[q];
+        const int c = cnt(q);
         const size_t seg = seg_of(jrow, q);
         for (int i0 = 0; i0 < c; i0 += kWave) {
           const int i = i0 + lane;
@@ -1725,9 +1727,11 @@ __device__ __forceinline__ void pv_finish(const ProcVerifyParams &X, int b, unsi
             if (pre && i < kPfHead) {
               z = L.pf_val[(jrow * nS + q) * kPfHead + i];
               v = L.pf_idx[(jrow * nS + q) * kPfHead + i];
-            } else {
-              z = Q.lists[seg + i];
-              v = Q.list_idx[seg + i];
+            } else {                  // (atomic loads, which the compiler does not merge with the
+                                      // LDS reads above into generic ones; those would wait for
+                                      // every outstanding global access)
+              z = load_agent(Q.lists + seg + i);
+              v = load_agent(Q.list_idx + seg + i);
             }
             keep = f32_order_key(z) >= r.sa.theta;
           }
