@@ -318,8 +318,7 @@ def test_verify_from_logits_crowded_and_tied_rows(dtype):
     them, but more than one per lane of the drawing workgroup), half -inf and
     half equal, a narrow spread; beside ordinary rows and a target row of
     -inf only (no mass: the draw gives token 0 with SPEC_ST_RESID_ZERO).
-    The draws then come from the whole rows instead of the lists, or from
-    the lists by the whole workgroup."""
+    The draws then come from the whole rows instead of the lists."""
     rng = np.random.default_rng(61)
     B, k, V = 6, 2, 60000
     zt = (rng.standard_normal((B, k + 1, V)) * 1.0).astype(np.float32)
@@ -336,7 +335,7 @@ def test_verify_from_logits_crowded_and_tied_rows(dtype):
     zd_[2] = np.where(np.isinf(zt[2, :k]), -np.inf, 1.5).astype(np.float32)
     zd_[2][:, rng.choice(np.arange(1, V, 2), 100, replace=False)] = 2.0
     # K = 256 without top-p keeps 256 entries of an ordinary row (more with
-    # bf16 ties): the one-wave draw at its limit, and the workgroup draw
+    # bf16 ties): the largest kept sets drawn from the lists
     for T, K, P in [(1.0, 50, 1.0), (0.7, 50, 0.9), (1.0, 256, 0.95), (1.0, 256, 1.0)]:
         note(f"verify logits crowded {dtype} T={T} K={K} P={P}")
         counts, got, ref = _verify_case(zt, zd_, T, K, P, 62, dtype)
