@@ -47,7 +47,9 @@
  *     the chunk masses of the row each sequence draws from, and one workgroup
  *     per sequence of the same launch, dispatched after them, draws.  The
  *     stochastic tree verification's workspace, when given, is of the same
- *     kind.
+ *     kind.  Verification from logits with top-k (K <= 256) takes two
+ *     launches: the slices' candidate lists, then the row statistics and,
+ *     in the same launch, the draw from the lists.
  *   - Token ids are int32 in [0, V).  Layouts are row-major, last index fastest.
  */
 #ifndef SPEC_VERIFY_H
