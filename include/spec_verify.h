@@ -36,8 +36,9 @@
  *     verification (which accepts any contents and also leaves it zero-
  *     filled).  For verification from logits only the last
  *     spec_verify_sample_workspace_bytes(B, k, V) bytes are such flags; the
- *     leading part is rewritten by every call.  Every other workspace's
- *     contents on entry are ignored.
+ *     leading part is rewritten by every call (so a workspace taken over from
+ *     calls of another B, k or V is zero-filled again first).  Every other
+ *     workspace's contents on entry are ignored.
  *   - A greedy verify call is one launch: streaming workgroups publish per-
  *     chunk results and one workgroup of the same launch commits them.  Calls
  *     whose rows need more chunk results than that workgroup holds at once

@@ -20,6 +20,9 @@ def note(msg: str) -> None:
     sys.stderr.flush()
 
 
+_WS_SHAPE = {}
+
+
 def ws(nbytes: int, key=None):
     """A cached zero-filled workspace of at least nbytes.  Greedy, tree and
     stochastic verification use keys of their own: their workspaces carry
@@ -147,7 +150,13 @@ def verify_sample_logits(zp_dev, zq_dev, drafts, uniforms, T, top_k=0, top_p=1.0
                emit_offsets=torch.empty(B + 1, dtype=torch.int32, device=DEV),
                final_mass=torch.empty(B, dtype=torch.float64, device=DEV),
                status=torch.empty(B, dtype=torch.int32, device=DEV))
-    w = ws(sv.spec_verify_sample_logits_workspace_bytes(B, k, V), ("sample_logits", ws_key))
+    key = ("sample_logits", ws_key)
+    w = ws(sv.spec_verify_sample_logits_workspace_bytes(B, k, V), key)
+    if _WS_SHAPE.get(key) != (B, k, V):
+        # the flags are the workspace's last part, so where they sit depends
+        # on the shape: a workspace taken over from another shape starts zeroed
+        w.zero_()
+        _WS_SHAPE[key] = (B, k, V)
     d = drafts if torch.is_tensor(drafts) else i32(drafts)
     u = uniforms if torch.is_tensor(uniforms) else torch.from_numpy(np.ascontiguousarray(uniforms, np.float32)).to(DEV)
     rem = None if remaining is None else i32(remaining)
