@@ -574,9 +574,9 @@ __device__ __forceinline__ ProcStats proc_row_stats(const ProcParams &P, int r, 
     if (sh_fast) {
       const ProcStats st = sh_st;
       if (t == 0) {
-    P.stats[r] = st;
-    res = st;
-  }
+        P.stats[r] = st;
+        res = st;
+      }
       if (P.probs) {
         float *out = P.probs + static_cast<size_t>(r) * V;
         row_foreach<BF16>(row, V, [&](int v, float z) { out[v] = proc_prob(z, st, invT); });
@@ -703,9 +703,9 @@ __device__ __forceinline__ ProcStats proc_row_stats(const ProcParams &P, int r, 
     __syncthreads();
     const ProcStats st = sh_st;
     if (t == 0) {
-    P.stats[r] = st;
-    res = st;
-  }
+      P.stats[r] = st;
+      res = st;
+    }
     if (P.probs) {
       float *out = P.probs + static_cast<size_t>(r) * V;
       row_foreach<BF16>(row, V, [&](int v, float z) { out[v] = proc_prob(z, st, invT); });
@@ -1452,6 +1452,7 @@ constexpr int kDenseMaxChunks = (SPEC_PROC_MAX_V + kDenseChunk - 1) / kDenseChun
 constexpr int kPfPairs = 128;          // (target row, slice) lists whose head a finisher loads early
 constexpr int kPfHead = kWave;         // entries of a list's head
 constexpr int kMaxRows = 2 * SPEC_MAX_K + 1;
+constexpr int kRankAll = 128;          // kept entries up to this many are ranked among all of them
 
 // A finisher's LDS, carved from the statistics workgroups' histogram buffer
 // (the two roles never share a workgroup).
@@ -1461,10 +1462,17 @@ struct FinishLds {
   ProcStats stat[kMaxRows];            // the sequence's rows: target 0..k, then draft 0..k-1
   int cnt[kPfPairs];                   // list lengths of the target rows (prefetched)
   int cnt_row[kSliceMaxS];             // list lengths of the row drawn from (when not prefetched)
-  int idx[kProcThreads];               // kept entries: indices, in list order
-  float val[kProcThreads];             //   and logits
+  int idx[kProcThreads];               // kept entries: indices, logits and slices, in list order
+  float val[kProcThreads];
+  int qs[kProcThreads];
+  int gidx[kProcThreads];              // ... grouped by slice
+  float gval[kProcThreads];
+  int gq[kProcThreads];
   int ord[kProcThreads];               // ... in index order
   float ordv[kProcThreads];
+  int qn[kSliceMaxS];                  // kept entries per slice, their offsets, placement counters
+  int qbase[kSliceMaxS];
+  int qpos[kSliceMaxS];
   double cm[kDenseMaxChunks];          // whole-row draw: chunk masses
 };
 static_assert(sizeof(FinishLds) <= sizeof(unsigned long long) * 256 * kWave, "finisher LDS fits the histogram buffer");
@@ -1603,6 +1611,7 @@ __device__ __forceinline__ void pv_finish(const ProcVerifyParams &X, int b, unsi
   __shared__ int sh_acc[SPEC_MAX_K], sh_st[SPEC_MAX_K], sh_d[SPEC_MAX_K];
   __shared__ int4 sh_ch;
   __shared__ int sh_n;
+  __shared__ unsigned sh_cutmax;
   __shared__ double sh_dw[kProcWaves];
   __shared__ int2 sh_iw[kProcWaves];
   FinishLds &L = *reinterpret_cast<FinishLds *>(lh);
@@ -1709,9 +1718,19 @@ __device__ __forceinline__ void pv_finish(const ProcVerifyParams &X, int b, unsi
     if (!pre) {
       if (t < nS) L.cnt_row[t] = Q.list_cnt[static_cast<size_t>(b * kp1 + jrow) * nS + t];
     }
+    // without top-k the lists hold every entry at or above their slice's cut
+    // (and nothing below it), so they hold the kept entries when the row's
+    // threshold reaches the largest cut
+    const bool topk = Q.cfg.top_k > 0 && Q.cfg.top_k < V;
+    if (!topk && t < kWave) {
+      const uint32_t c = t < nS ? Q.list_cut[static_cast<size_t>(b * kp1 + jrow) * nS + t] : 0u;
+      const uint32_t cm = wave_max_u(c);
+      if (t == 0) sh_cutmax = cm;
+    }
     if (t == 0) sh_n = 0;
+    if (t < nS) L.qn[t] = 0;
     __syncthreads();
-    bool complete = true;
+    bool complete = topk || r.sa.theta >= sh_cutmax;
     for (int q = 0; q < nS; ++q) complete = complete && cnt(q) <= cap;
     if (complete && r.sa.mass > 0.0) {
       // the kept entries of the row drawn from (wave w: lists w, w + 16, ...)
@@ -1739,7 +1758,10 @@ __device__ __forceinline__ void pv_finish(const ProcVerifyParams &X, int b, unsi
           if (keep && slot < kProcThreads) {
             L.idx[slot] = v;
             L.val[slot] = z;
+            L.qs[slot] = q;
           }
+          const int kq = __popcll(__ballot(keep));
+          if (lane == 0 && kq > 0) atomicAdd(&L.qn[q], kq);
         }
       }
     }
@@ -1747,19 +1769,51 @@ __device__ __forceinline__ void pv_finish(const ProcVerifyParams &X, int b, unsi
     const int n = sh_n;
     if (complete && n <= kProcThreads) {
       // order the n kept entries by index (distinct), one per lane
-      if (t >= n && t < ((n + 3) & ~3)) L.idx[t] = INT_MAX;
       if (t < n) L.ord[t] = -1;
-      __syncthreads();
-      if (t < n) {
-        const int my = L.idx[t];
-        const int4 *q4 = reinterpret_cast<const int4 *>(L.idx);
-        int rank = 0;
-        for (int i = 0; i < (n + 3) >> 2; ++i) {
-          const int4 e = q4[i];
-          rank += (e.x < my) + (e.y < my) + (e.z < my) + (e.w < my);
+      if (n <= kRankAll) {
+        // few: each ranks itself among all of them
+        if (t >= n && t < ((n + 3) & ~3)) L.idx[t] = INT_MAX;
+        __syncthreads();
+        if (t < n) {
+          const int my = L.idx[t];
+          const int4 *q4 = reinterpret_cast<const int4 *>(L.idx);
+          int rank = 0;
+          for (int i = 0; i < (n + 3) >> 2; ++i) {
+            const int4 e = q4[i];
+            rank += (e.x < my) + (e.y < my) + (e.z < my) + (e.w < my);
+          }
+          L.ord[rank] = my;
+          L.ordv[rank] = L.val[t];
         }
-        L.ord[rank] = my;
-        L.ordv[rank] = L.val[t];
+      } else {
+        // many: a slice's indices lie in one range, so the entries are
+        // grouped by slice (offsets from the slices' counts) and ranked
+        // within their slice
+        if (t < kWave) {
+          const int c = t < nS ? L.qn[t] : 0;
+          const int x = wave_incl_scan(c) - c;
+          if (t < nS) {
+            L.qbase[t] = x;
+            L.qpos[t] = 0;
+          }
+        }
+        __syncthreads();
+        if (t < n) {
+          const int q = L.qs[t];
+          const int pos = L.qbase[q] + atomicAdd(&L.qpos[q], 1);
+          L.gidx[pos] = L.idx[t];
+          L.gval[pos] = L.val[t];
+          L.gq[pos] = q;
+        }
+        __syncthreads();
+        if (t < n) {
+          const int q = L.gq[t], b0 = L.qbase[q], nq = L.qn[q];
+          const int my = L.gidx[t];
+          int rank = 0;
+          for (int i = 0; i < nq; ++i) rank += L.gidx[b0 + i] < my;
+          L.ord[b0 + rank] = my;
+          L.ordv[b0 + rank] = L.gval[t];
+        }
       }
       __syncthreads();
       const int v = t < n ? L.ord[t] : -1;
@@ -1938,15 +1992,33 @@ int launch_proc_stats(const void *za, const void *zb, int rows_a, int rows, int 
 
 size_t proc_list_idx_bytes(int rows) { return round_up(static_cast<size_t>(rows) * kCandCap * sizeof(int32_t), 256); }
 
-bool launch_sample_logits_topk(const SampleParams &S, bool bf16, int top_k, float top_p, ProcStats *stats,
-                               void *list_ws, int32_t *list_idx, unsigned long long *row_pub, hipStream_t s) {
+bool launch_sample_logits_lists(const SampleParams &S, bool bf16, int top_k, float top_p, ProcStats *stats,
+                                void *list_ws, int32_t *list_idx, unsigned long long *row_pub, hipStream_t s) {
   const int rows_a = S.B * (S.k + 1), rows = S.B * (2 * S.k + 1);
   ProcVerifyParams X;
   X.proc = proc_params(S.zp, S.zq, rows_a, rows, S.V, bf16, S.invT, top_k, top_p, stats, nullptr);
-  if (!topk_lists(X.proc, top_k, S.V)) return false;
   X.proc.list_idx = list_idx;
   X.proc.row_pub = row_pub;
-  launch_slices(X.proc, proc_ws_layout(rows, S.V), static_cast<unsigned char *>(list_ws), top_k, true, top_k, bf16, s);
+  const ProcWs L = proc_ws_layout(rows, S.V);
+  unsigned char *w = static_cast<unsigned char *>(list_ws);
+  if (top_k > 0 && top_k < S.V) {
+    if (!topk_lists(X.proc, top_k, S.V)) return false;
+    launch_slices(X.proc, L, w, top_k, true, top_k, bf16, s);
+  } else if (top_p < 1.0f && kToppRank <= X.proc.seg_cap / 2) {
+    // top-p alone: lists at the kToppRank-th lane maximum, then the slices'
+    // exact weights (the statistics' union check needs the row's total)
+    X.proc.sl_max = reinterpret_cast<uint32_t *>(w + L.smax);
+    X.proc.sl_min = reinterpret_cast<uint32_t *>(w + L.smin);
+    X.proc.sl_tot = reinterpret_cast<unsigned long long *>(w + L.stot);
+    launch_slices(X.proc, L, w, kToppRank, false, top_k, bf16, s);
+    const dim3 gs(static_cast<unsigned>(rows * X.proc.S)), bs(kSliceThreads);
+    if (bf16)
+      hipLaunchKernelGGL(proc_slmass_kernel<true>, gs, bs, 0, s, X.proc);
+    else
+      hipLaunchKernelGGL(proc_slmass_kernel<false>, gs, bs, 0, s, X.proc);
+  } else {
+    return false;
+  }
   X.smp = S;
   const dim3 g(static_cast<unsigned>(rows + S.B + (S.emit_offsets ? 1 : 0))), blk(kProcThreads);
   if (bf16)

@@ -29,13 +29,14 @@ struct SampleParams {
   int32_t *ecnt;                // [B] published emit_count + 1 (0: not yet written)
 };
 
-// Stochastic verification from logits in two launches when the top-k slice
-// lists apply (the statistics and the verification share the second launch);
-// returns false, launching nothing, otherwise.  P as for the verification,
-// with P.sp / P.sq the statistics rows; list_ws the slice lists' workspace,
-// list_idx proc_list_idx_bytes(rows), row_pub [rows][3] words (any contents).
-bool launch_sample_logits_topk(const SampleParams &P, bool bf16, int top_k, float top_p, ProcStats *stats,
-                               void *list_ws, int32_t *list_idx, unsigned long long *row_pub, hipStream_t s);
+// Stochastic verification from logits through the slices' candidate lists
+// (top-k up to 256, or top-p alone): the slice launches, then the statistics
+// and the draw in one launch; returns false, launching nothing, otherwise.
+// P as for the verification, with P.sp / P.sq the statistics rows; list_ws
+// the slice lists' workspace, list_idx proc_list_idx_bytes(rows), row_pub
+// [rows][3] words (any contents).
+bool launch_sample_logits_lists(const SampleParams &P, bool bf16, int top_k, float top_p, ProcStats *stats,
+                                void *list_ws, int32_t *list_idx, unsigned long long *row_pub, hipStream_t s);
 
 namespace {
 

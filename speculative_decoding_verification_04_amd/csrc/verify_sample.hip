@@ -476,9 +476,9 @@ extern "C" int spec_verify_sample_logits(const void *target_logits, const void *
   const bool bf16 = dt == SPEC_BF16;
   const LogitsWs lw = sample_logits_layout(B, k, V);
   (void)hipGetLastError();
-  // top-k through the slice lists: the slice kernel, then statistics and
-  // verification in one launch
-  if (launch_sample_logits_topk(P, bf16, top_k, top_p, stats, wb + lw.lists,
+  // through the slice lists (top-k, or top-p alone): the slice launches,
+  // then statistics and verification in one launch
+  if (launch_sample_logits_lists(P, bf16, top_k, top_p, stats, wb + lw.lists,
                                 reinterpret_cast<int32_t *>(wb + lw.idx),
                                 reinterpret_cast<unsigned long long *>(wb + lw.flags), s))
     return launch_status();
