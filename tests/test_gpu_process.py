@@ -303,11 +303,14 @@ def test_verify_from_logits_parity(dtype, V):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_verify_from_logits_workload_full_size(dtype):
-    """Stochastic workload: B=8, k=4, V=151936, T=0.7, top-k 50, top-p 0.9."""
+@pytest.mark.parametrize("K", [50, 0])
+def test_verify_from_logits_workload_full_size(dtype, K):
+    """Stochastic workload: B=8, k=4, V=151936, T=0.7, top-p 0.9, with top-k
+    50 and without (rows then keep several hundred entries: the draw orders
+    them slice by slice)."""
     g = W.sample_logits(2)
-    note(f"verify logits workload {dtype}")
-    counts, got, ref = _verify_case(g["zt"], g["zd"], g["temperature"], 50, 0.9, 2, dtype)
+    note(f"verify logits workload {dtype} K={K}")
+    counts, got, ref = _verify_case(g["zt"], g["zd"], g["temperature"], K, 0.9, 2, dtype)
     _assert_counts(counts, 8)
 
 
@@ -336,7 +339,7 @@ def test_verify_from_logits_crowded_and_tied_rows(dtype):
     zd_[2][:, rng.choice(np.arange(1, V, 2), 100, replace=False)] = 2.0
     # K = 256 without top-p keeps 256 entries of an ordinary row (more with
     # bf16 ties): the largest kept sets drawn from the lists
-    for T, K, P in [(1.0, 50, 1.0), (0.7, 50, 0.9), (1.0, 256, 0.95), (1.0, 256, 1.0)]:
+    for T, K, P in [(1.0, 50, 1.0), (0.7, 50, 0.9), (1.0, 256, 0.95), (1.0, 256, 1.0), (1.0, 0, 0.9), (0.7, 0, 0.5)]:
         note(f"verify logits crowded {dtype} T={T} K={K} P={P}")
         counts, got, ref = _verify_case(zt, zd_, T, K, P, 62, dtype)
         _assert_counts(counts, B)
@@ -351,7 +354,7 @@ def test_verify_from_logits_largest_vocabulary(dtype):
     B, k, V = 2, 1, sv.SPEC_PROC_MAX_V
     zt = (rng.standard_normal((B, k + 1, V)) * 2.0).astype(np.float32)
     zd_ = (zt[:, :k] + rng.standard_normal((B, k, V)) * 0.7).astype(np.float32)
-    for T, K, P in [(0.7, 50, 0.9), (1.0, 200, 1.0)]:
+    for T, K, P in [(0.7, 50, 0.9), (1.0, 200, 1.0), (0.7, 0, 0.9)]:
         note(f"verify logits largest V {dtype} T={T} K={K} P={P}")
         counts, got, ref = _verify_case(zt, zd_, T, K, P, 63, dtype)
         _assert_counts(counts, B)
