@@ -1386,19 +1386,24 @@ __global__ __launch_bounds__(256) void proc_export_kernel(const ProcStats *stats
 }
 
 // ---------------------------------------------------------------------------
-// Statistics and stochastic verification in one launch (top-k rows).
+// Statistics and stochastic verification in one launch (rows processed
+// through the slice lists: top-k, or top-p alone).
 //
 // With top-k through the slice lists, every entry a processed row keeps (its
 // order key at or above the row's threshold, itself at or above the row's
 // K-th largest key) is in that row's lists whenever every list fit its
-// segment.  So the token drawn at the end of a round, from p'_j - q'_j (first
-// rejection) or p'_k (all accepted), needs only the target row's kept entries
-// (p'_j is zero elsewhere, so is the residual): the finisher takes them from
-// the lists, orders them by index, and draws by the inverse CDF over them.
-// Two launches: the slice kernel (which also clears each row's published
-// words), then the statistics workgroups, one per row, each publishing its
-// row's statistics, and behind them (dispatch is in index order) one
-// finisher per sequence and, with offsets, one offsets workgroup.  While the
+// segment.  Without top-k (top-p alone) the lists hold every entry at or
+// above their slice's cut, so they hold the kept entries whenever the row's
+// threshold reaches the largest cut (the finisher checks).  So the token
+// drawn at the end of a round, from p'_j - q'_j (first rejection) or p'_k
+// (all accepted), needs only the target row's kept entries (p'_j is zero
+// elsewhere, so is the residual): the finisher takes them from the lists,
+// orders them by index, and draws by the inverse CDF over them.
+// After the slice launches (the slice kernel also clears each row's
+// published words; top-p alone adds the slices' exact weights), one launch:
+// the statistics workgroups, one per row, each publishing its row's
+// statistics, and behind them (dispatch is in index order) one finisher per
+// sequence and, with offsets, one offsets workgroup.  While the
 // statistics are computed, a finisher loads everything that does not depend
 // on them: the drafts, uniforms and budget, the logits at the drafted tokens,
 // and the lengths and first 64 entries of every list of its k + 1 target
@@ -1406,8 +1411,9 @@ __global__ __launch_bounds__(256) void proc_export_kernel(const ProcStats *stats
 // arithmetic of the other stochastic kernels), keeps the listed entries of
 // the row drawn from that reach its threshold, orders them by index, gathers
 // the draft's logits there (residual only) and draws.  A row whose lists
-// overflowed, or that keeps more than one entry per lane, is drawn from the
-// whole rows instead (chunk masses, then one chunk scanned in index order).
+// overflowed, that the lists do not cover, or that keeps more than one entry
+// per lane, is drawn from the whole rows instead (chunk masses, then one
+// chunk scanned in index order).
 
 struct ProcVerifyParams {
   ProcParams proc;   // statistics of rows [0, B(k+1)) target, [B(k+1), B(2k+1)) draft;
