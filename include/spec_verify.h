@@ -50,7 +50,8 @@
  *     stochastic tree verification's workspace, when given, is of the same
  *     kind.  Verification from logits with top-k (K <= 256) takes two
  *     launches: the slices' candidate lists, then the row statistics and,
- *     in the same launch, the draw from the lists.
+ *     in the same launch, the draw from the lists; with top-p alone a launch
+ *     of the slices' exact weights comes between them.
  *   - Token ids are int32 in [0, V).  Layouts are row-major, last index fastest.
  */
 #ifndef SPEC_VERIFY_H
