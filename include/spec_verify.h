@@ -33,17 +33,18 @@
  *     zero-filled before its first use (e.g. hipMemset, torch.zeros) and no
  *     call of another kind may write into it; every completed call leaves it
  *     zero-filled again.  A greedy workspace may be shared with tree
- *     verification (which accepts any contents and also leaves it zero-
- *     filled).  For verification from logits only the last
+ *     verification, whose workspace is of the same kind.  For verification
+ *     from logits only the last
  *     spec_verify_sample_workspace_bytes(B, k, V) bytes are such flags; the
  *     leading part is rewritten by every call (so a workspace taken over from
  *     calls of another B, k or V is zero-filled again first).  Every other
  *     workspace's contents on entry are ignored.
  *   - A greedy verify call is one launch: streaming workgroups publish per-
- *     chunk results and one workgroup of the same launch commits them.  Calls
- *     whose rows need more chunk results than that workgroup holds at once
- *     (more than 1024 per sequence), and tree verification, launch a streaming
- *     pass and a commit pass, synchronised by the stream order.
+ *     chunk results and one workgroup of the same launch commits them; tree
+ *     verification does the same over whole trees.  Calls whose rows need
+ *     more chunk results than that workgroup holds at once (more than 1024
+ *     per sequence or tree) launch a streaming pass and a commit pass,
+ *     synchronised by the stream order.
  *   - A stochastic verify call is one launch too: streaming workgroups publish
  *     the chunk masses of the row each sequence draws from, and one workgroup
  *     per sequence of the same launch, dispatched after them, draws.  The

@@ -401,6 +401,158 @@ __global__ __launch_bounds__(kThreads) void greedy_verify_kernel(GreedyParams P)
   else stream_chunk<BF16, true>(P, static_cast<int>(blockIdx.x) - 1);
 }
 
+// ------------------------------------------------ tree, single launch ----
+// The same single launch for candidate trees (N = k + 1 nodes per sequence):
+// workgroup 0 polls a tile of sequences' chunk keys as finish_verify does,
+// then commits the tile in LDS with the rule of tree_commit_kernel (one lane
+// per node folds its row and finds the child that proposed the row's
+// argmax, one lane per sequence walks from the root).  Used when one whole
+// tree's chunk keys fit a tile.
+struct TreeTileShared {
+  uint64_t key[kTileKeys];   // the tile's chunk keys, node-major
+  int d[kTileKeys];          // drafts; after the walk: emitted tokens
+  int fc[kTileKeys];         // first child; after the walk: path nodes
+  int ns[kTileKeys];         // next sibling
+  int tok[kTileKeys];        // argmax of each node's row
+  int nxt[kTileKeys];        // child proposing that argmax, or -1
+  int st[kTileSeq];          // status bits
+  int cnt[kTileSeq];         // budgets, then emit counts
+  int scan[kThreads / kWave + 1];
+};
+
+__host__ __device__ inline int tree_tile_sequences(int N, int chunks) {
+  return min(kTileSeq, (kTileKeys / chunks) / N);
+}
+
+__device__ void finish_tree(const GreedyParams &P) {
+  __shared__ TreeTileShared S;
+  const int t = threadIdx.x, N = P.k + 1;
+  const bool loader = t < kLoadLanes;
+  const int per = tree_tile_sequences(N, P.chunks);
+  int carry = 0, polls = 0;
+  bool timed_out = false;
+  uint64_t v[kKPL];
+  for (int s0 = 0; s0 < P.B; s0 += per) {
+    const int nseq = min(per, P.B - s0), nrows = nseq * N, nk = nrows * P.chunks;
+    const uint64_t *slot0 = P.keys + static_cast<size_t>(s0) * N * P.chunks;
+    const size_t r0 = static_cast<size_t>(s0) * N;
+    // the tile's slots, drafts, links and budgets, issued together
+#pragma unroll
+    for (int i = 0; i < kKPL; ++i) {
+      const int f = t + i * kLoadLanes;
+      v[i] = loader && f < nk ? load_agent(slot0 + f) : kEmptyKey;
+    }
+    for (int r = t; r < nrows; r += kThreads) {
+      S.d[r] = P.draft[r0 + r];
+      S.fc[r] = P.first_child[r0 + r];
+      S.ns[r] = P.next_sibling[r0 + r];
+    }
+    if (t < nseq) {
+      S.st[t] = 0;
+      S.cnt[t] = P.remaining ? P.remaining[s0 + t] : -1;
+    }
+    // wait until every slot of the tile is published (re-reading only the
+    // missing ones); the bound keeps the wait finite
+    while (true) {
+      bool present = true;
+#pragma unroll
+      for (int i = 0; i < kKPL; ++i) present = present && v[i] != 0ull;
+      if (__syncthreads_and(present)) break;
+      if (++polls >= kMaxPolls) { timed_out = true; break; }
+      __builtin_amdgcn_s_sleep(1);
+      if (loader) {
+#pragma unroll
+        for (int i = 0; i < kKPL; ++i) {
+          const int f = t + i * kLoadLanes;
+          if (v[i] == 0ull) v[i] = load_agent(slot0 + f);
+        }
+      }
+    }
+    if (loader) {
+#pragma unroll
+      for (int i = 0; i < kKPL; ++i) {
+        const int f = t + i * kLoadLanes;
+        if (f < nk) S.key[f] = v[i];
+      }
+    }
+    __syncthreads();
+    // one lane per node: fold its row's chunk keys; check its draft and links
+    for (int r = t; r < nrows; r += kThreads) {
+      const uint64_t *kr = S.key + r * P.chunks;
+      uint64_t best = 0ull;
+      for (int c = 0; c < P.chunks; ++c) best = kr[c] > best ? kr[c] : best;
+      S.tok[r] = argmax_key_index(best);
+      const int seq = r / N, node = r - seq * N;
+      const int d = S.d[r], fc = S.fc[r], ns = S.ns[r];
+      int bits = timed_out ? SPEC_ST_INCOMPLETE : 0;
+      if (node > 0 && (d < 0 || d >= P.V)) bits |= SPEC_ST_DRAFT_OOR;
+      if ((fc != -1 && (fc <= node || fc >= N)) || (ns != -1 && (ns <= node || ns >= N)))
+        bits |= SPEC_ST_BAD_STATE;
+      if (bits) atomicOr(&S.st[seq], bits);
+    }
+    __syncthreads();
+    // the child proposing each node's argmax (only in trees whose every link
+    // points forward, so each walk ends)
+    for (int r = t; r < nrows; r += kThreads) {
+      const int seq = r / N, base = seq * N;
+      int c = -1;
+      if (!(S.st[seq] & SPEC_ST_BAD_STATE)) {
+        c = S.fc[r];
+        while (c != -1 && S.d[base + c] != S.tok[r]) c = S.ns[base + c];
+      }
+      S.nxt[r] = c;
+    }
+    __syncthreads();
+    // one lane per sequence: the walk from the root
+    int cnt = 0;
+    if (t < nseq) {
+      const int b = s0 + t, sb = t * N;
+      const int st = S.st[t], rem = S.cnt[t];
+      int acc = 0;
+      if (!(st & SPEC_ST_BAD_STATE) && rem != 0) {
+        int cur = 0;
+        while (true) {
+          const int tk = S.tok[sb + cur];
+          const int c = S.nxt[sb + cur];
+          S.d[sb + cnt] = tk;                          // drafts and links are no longer read:
+          S.fc[sb + cnt] = cur;                        // their rows now hold tokens and path
+          ++cnt;
+          if (c != -1) ++acc;
+          if ((P.eos >= 0 && tk == P.eos) || cnt == rem || c == -1) break;
+          cur = c;
+        }
+      }
+      S.cnt[t] = cnt;
+      P.accept_len[b] = acc;
+      P.emit_count[b] = cnt;
+      if (P.status) P.status[b] = st;
+    }
+    __syncthreads();
+    for (int r = t; r < nrows; r += kThreads) {
+      const int seq = r / N, node = r - seq * N;
+      const bool kept = node < S.cnt[seq];
+      P.out_tokens[r0 + r] = kept ? S.d[r] : -1;
+      P.path[r0 + r] = kept ? S.fc[r] : -1;
+    }
+    if (P.emit_offsets) {
+      int total;
+      const int ex = block_excl_scan(t < nseq ? cnt : 0, S.scan, &total);
+      if (t < nseq) P.emit_offsets[s0 + t] = carry + ex;
+      carry += total;
+    }
+    __syncthreads();
+  }
+  if (P.emit_offsets && t == 0) P.emit_offsets[P.B] = carry;
+  // every slot back to 0 for the next call (ordered before it by the launch)
+  for (int f = t; f < P.nprod; f += kThreads) P.keys[f] = 0ull;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void tree_verify_kernel(GreedyParams P) {
+  if (blockIdx.x == 0) finish_tree(P);
+  else stream_chunk<BF16, true>(P, static_cast<int>(blockIdx.x) - 1);
+}
+
 
 
 constexpr int kCommitThreads = 1024;
@@ -815,6 +967,15 @@ extern "C" int spec_verify_tree(const void *logits, spec_dtype dt, int B, int N,
   P.path = path;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  if (tree_tile_sequences(N, chunks) >= 1 && nblocks + 1 < INT32_MAX) {
+    // one launch: workgroup 0 commits tiles of trees while the rest stream
+    const dim3 g(static_cast<unsigned>(nblocks + 1));
+    if (dt == SPEC_BF16)
+      hipLaunchKernelGGL(tree_verify_kernel<true>, g, dim3(kThreads), 0, s, P);
+    else
+      hipLaunchKernelGGL(tree_verify_kernel<false>, g, dim3(kThreads), 0, s, P);
+    return launch_status();
+  }
   if (dt == SPEC_BF16)
     hipLaunchKernelGGL(greedy_chunk_kernel<true>, dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s, P);
   else

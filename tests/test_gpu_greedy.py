@@ -178,8 +178,8 @@ def test_single_launch_and_two_launch_paths(k):
 
 
 def test_greedy_and_tree_share_a_workspace():
-    """Greedy and tree verification alternate on one workspace: the tree call
-    accepts any contents and, like the greedy call, leaves it zero-filled."""
+    """Greedy and tree verification alternate on one workspace: each takes it
+    zero-filled and leaves it zero-filled."""
     note("greedy/tree shared workspace")
     import speculative_decoding_verification_04_amd as sv
     from tests._gpu import verify_tree
