@@ -11,22 +11,23 @@
 // commit.  One launch does both:
 //   * producer workgroups (one per (row, chunk of kThreads*VEC*U elements))
 //     load their chunk with 16-byte non-temporal loads (U in flight per lane).
-//     The chunk maximum comes from plain max instructions, DPP lane moves
-//     inside each wave and LDS across waves; only the lanes holding it search
-//     their own elements for its first index (an LDS minimum picks the
-//     lowest).  The chunk's 64-bit key (value order high, UINT32_MAX - index
-//     low; the largest key is the argmax at the lowest index) is published
+//     Each wave's maximum comes from plain max instructions and DPP lane
+//     moves; only the lanes holding it search their own elements for its
+//     first index (a DPP minimum picks the lowest), and the waves' 64-bit
+//     keys meet in LDS (value order high, UINT32_MAX - index low; the largest
+//     key is the argmax at the lowest index).  The chunk's key is published
 //     with one agent-scope store into its workspace slot.  A published key is
 //     never 0 (an empty chunk publishes 1), so a slot is its own flag.
-//   * workgroup 0, the finisher, walks the batch in tiles of sequences: it
-//     polls a tile's slots with agent-scope loads (one round of loads per
-//     poll, only missing slots re-read) and, while the next tile's slots and
-//     drafts are already being loaded, commits the tile in LDS with one lane
-//     per row: fold the row's chunk keys, test its stop conditions (mismatch,
-//     EOS) with an LDS minimum per sequence, then one lane per sequence applies
-//     the budget, counts the accepted drafts and scans the emit counts, and
-//     the rows write their tokens.  Finally it returns every slot it read to
-//     0 (the workspace stays zero-filled between calls).
+//   * workgroup 0, the finisher, takes the batch in tiles of sequences whose
+//     slots are laid out in its polling order.  Each lane polls its own few
+//     slots with agent-scope loads (no workgroup barrier between polls, only
+//     missing slots re-read), folds what arrived per row in registers and
+//     into the row's maximum in LDS, and returns each arrived slot to 0 (the
+//     workspace stays zero-filled between calls).  The lane that completes a
+//     row tests its stop conditions (mismatch, EOS) with an LDS minimum per
+//     sequence.  After the tile's last arrival wave 0 applies the budgets,
+//     counts the accepted drafts and scans the emit counts, and the rows
+//     write their tokens.
 // Producers never wait: the finisher is one workgroup whose wait ends when
 // every producer has published, and producers depend on nothing.  Device-
 // scope atomics on shared counters are avoided altogether (on a multi-XCD
@@ -36,6 +37,7 @@
 // streaming kernel with its own commit).
 #include "common.h"
 
+#include <algorithm>
 #include <mutex>
 
 namespace specv {
@@ -63,15 +65,65 @@ struct GreedyParams {
   int32_t eos;
   const int32_t *remaining;
   int32_t *accept_len, *emit_count, *out_tokens, *emit_offsets, *status;
-  uint64_t *keys;     // [B*(k+1)*chunks]; zero between calls (the slot flags)
+  uint64_t *keys;     // chunk-key slots; zero between calls (the slot flags)
   int nprod;          // producer workgroups of the single-launch path
+  int tile_seq;       // linear single launch: sequences per finisher tile (slots
+                      // in the tile's polling order); 0: slot row * chunks + c
+  int tile_span;      // slots per full tile in that order
   // tree verification only (k + 1 = N nodes per sequence)
   const int32_t *first_child, *next_sibling;
   int32_t *path;
 };
 
+// Finisher tiles of the linear single launch.  The finisher's lanes poll a
+// tile's chunk-key slots kSlotsPerLane at a time per lane, in phases of
+// kPhaseSlots slots; a tile holds at most kArrRows rows and kArrSlots slots.
+constexpr int kSlotsPerLane = 4;                        // few enough that nothing spills to scratch
+constexpr int kPhaseSlots = kThreads * kSlotsPerLane;   // chunk keys polled at once
+constexpr int kArrSlots = 8 * kPhaseSlots;              // chunk keys per tile
+constexpr int kArrRows = 1024;                          // rows per tile
+constexpr int kTileSeq = 256;                           // sequences per tile (both finishers)
+
+__host__ __device__ inline int tile_sequences(int k, int chunks) {
+  const int rows = min(kArrRows, kArrSlots / chunks);
+  return min(kTileSeq, rows / (k + 1));
+}
+
+// Slots per lane n and lanes L of a phase of m slots: as many slots per lane
+// as keep L >= 16 (a lane's slots then sit in different 128-byte lines), at
+// most kSlotsPerLane.
+__host__ __device__ inline void phase_shape(int m, int &n, int &L) {
+  n = max(1, min(kSlotsPerLane, m / 16));
+  L = (m + n - 1) / n;
+}
+
+// Where logical slot f (0 <= f < nk; row-major over the tile's rows and
+// chunks) of a tile of nk slots is stored.  In a phase of m slots, lane t
+// polls the n consecutive logical slots n*t .. n*t+n-1 (chunks of one or two
+// rows, so they fold in registers), stored at positions i*L + t: each of a
+// lane's loads reaches a different cache line and one load instruction of a
+// wave reads consecutive positions.  Several loads of one line by one lane
+// were measured to wait on each other (2 us more per call on small batches).
+// A phase takes n*L <= m + 3 positions.
+__host__ __device__ inline int slot_position(int f, int nk) {
+  const int ph = f / kPhaseSlots, w = f - ph * kPhaseSlots;
+  int n, L;
+  phase_shape(min(kPhaseSlots, nk - ph * kPhaseSlots), n, L);
+  return ph * kPhaseSlots + (w % n) * L + w / n;
+}
+
+// Positions between the starts of consecutive tiles (a full tile's slots and
+// the last phase's padding).
+inline size_t tile_span(int k, int chunks) {
+  return round_up(static_cast<size_t>(tile_sequences(k, chunks)) * (k + 1) * chunks + 3, 4);
+}
+
+// Slots of either layout: whole tiles in polling order, or B*(k+1)*chunks.
 inline size_t greedy_ws_bytes(int B, int k, int chunks) {
-  return round_up(static_cast<size_t>(B) * (k + 1) * chunks * sizeof(uint64_t), 256);
+  size_t slots = static_cast<size_t>(B) * (k + 1) * chunks;
+  const int per = tile_sequences(k, chunks);
+  if (per >= 1) slots = std::max(slots, static_cast<size_t>((B + per - 1) / per) * tile_span(k, chunks));
+  return round_up(slots * sizeof(uint64_t), 256);
 }
 
 template <bool BF16>
@@ -150,8 +202,7 @@ template <bool BF16, bool PUBLISH>
 __device__ inline void stream_chunk(const GreedyParams &P, int blk) {
   using Tr = GreedyTraits<BF16>;
   constexpr int ELT = Tr::ELT, VEC = Tr::VEC, U = Tr::U;
-  __shared__ float sh_max[kWaves];
-  __shared__ int sh_first;
+  __shared__ uint64_t sh_key[kWaves];
 
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
   const int row = blk / P.chunks;
@@ -178,38 +229,43 @@ __device__ inline void stream_chunk(const GreedyParams &P, int blk) {
   if (has_tail) tv = load_elem<BF16>(rowp, s + nv * VEC + t);
 
   // Lane maximum (the -inf filler of missing vectors cannot exceed it unless
-  // the lane holds no element at all), then the chunk maximum: DPP inside each
-  // wave, LDS across the waves.
+  // the lane holds no element at all), then each wave's maximum through DPP.
   float lmax = fmaxf(hv, tv);
 #pragma unroll
   for (int u = 0; u < U; ++u) lmax = fmaxf(lmax, vec_max<BF16>(buf[u]));
   const float wm = wave_max_dpp(lmax);
-  if (t == 0) sh_first = INT_MAX;
-  if (lane == 0) sh_max[w] = wm;
-  __syncthreads();
-  float bmax = sh_max[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) bmax = fmaxf(bmax, sh_max[i]);
 
-  // Only lanes holding the chunk maximum look for its first index among their
-  // own elements, visited in increasing index order (head, vectors u = 0..U-1,
-  // tail); an LDS minimum across those lanes gives the chunk's first index.
-  if (lmax == bmax) {
-    int cand = INT_MAX;
-    if (has_tail && tv == bmax) cand = s + nv * VEC + t;
+  // Only lanes holding their wave's maximum look for its first index among
+  // their own elements, visited in increasing index order (head, vectors
+  // u = 0..U-1, tail); a DPP minimum gives the wave's first index and one
+  // 64-bit key per wave goes to LDS.  The largest of the waves' keys is the
+  // chunk's (larger value first, then the lower index).
+  int cand = INT_MAX;
+  if (lmax == wm) {
+    if (has_tail && tv == wm) cand = s + nv * VEC + t;
 #pragma unroll
     for (int u = U - 1; u >= 0; --u) {
       const int vi = t + u * kThreads;
-      const int q = vec_find<BF16>(buf[u], bmax);
+      const int q = vec_find<BF16>(buf[u], wm);
       if (vi < nv && q < VEC) cand = s + vi * VEC + q;
     }
-    if (has_head && hv == bmax) cand = t;
-    if (cand != INT_MAX) atomicMin(&sh_first, cand);
+    if (has_head && hv == wm) cand = t;
   }
+  cand = wave_min(cand);
+  if (lane == 0) sh_key[w] = cand == INT_MAX ? kEmptyKey : argmax_key(wm, cand);
   __syncthreads();
   if (t == 0) {
-    const uint64_t key = sh_first == INT_MAX ? kEmptyKey : argmax_key(bmax, sh_first);
-    uint64_t *slot = P.keys + static_cast<size_t>(row) * P.chunks + c;
+    uint64_t key = sh_key[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) key = sh_key[i] > key ? sh_key[i] : key;
+    size_t pos = static_cast<size_t>(row) * P.chunks + c;
+    if (PUBLISH && P.tile_seq > 0) {
+      // the linear finisher's polling order: tile q, then slot_position
+      const int kp1 = P.k + 1, q = row / kp1 / P.tile_seq, s0 = q * P.tile_seq;
+      const int nk = min(P.tile_seq, P.B - s0) * kp1 * P.chunks;
+      pos = static_cast<size_t>(q) * P.tile_span + slot_position((row - s0 * kp1) * P.chunks + c, nk);
+    }
+    uint64_t *slot = P.keys + pos;
     if constexpr (PUBLISH) __hip_atomic_store(slot, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else *slot = key;
   }
@@ -221,182 +277,229 @@ __global__ __launch_bounds__(kThreads) void greedy_chunk_kernel(GreedyParams P) 
 }
 
 // ---------------------------------------------------------------- commit ----
-// The finisher commits a tile of sequences in LDS: kTileKeys chunk keys per
-// tile (at most kTileSeq sequences), rows = ns * (k + 1) <= kTileKeys / chunks.
-// Its last wave only stores results; the other waves only load.  A wave's
-// memory counter covers its loads and its stores alike, so a wave that waits
-// for its loads never waits for stores as well.
-constexpr int kTileKeys = 1024;
-constexpr int kTileSeq = 256;
+// Slot polling shared by the finishers: a tile's chunk-key slots are read
+// with agent-scope loads (absent slots read 0) and re-read until present.
+constexpr int kTileKeys = 1024;     // chunk keys per tile of the tree finisher
 constexpr int kLoadLanes = kThreads - kWave;                              // waves 0 .. kWaves-2
 constexpr int kKPL = (kTileKeys + kLoadLanes - 1) / kLoadLanes;           // slots per loading lane
 static_assert(kTileSeq <= kLoadLanes, "one loading lane per sequence of a tile");
-
-struct TileShared {
-  uint64_t key[kTileKeys];   // the tile's chunk keys, row-major
-  int tok[kTileKeys];        // argmax of each row
-  int d[kTileKeys];          // the tile's drafts (ns * k <= kTileKeys)
-  int stop[kTileSeq];        // first row that stops the sequence (LDS minimum)
-  int rem[kTileSeq];         // budgets
-  int st[kTileSeq];          // status bits
-  int e[kTileSeq];           // emit counts
-  int acc[kTileSeq];         // accepted drafts
-  int off[kTileSeq];         // emit offsets
-  int scan[kThreads / kWave + 1];
-};
-
-__host__ __device__ inline int tile_sequences(int k, int chunks) {
-  const int rows = kTileKeys / chunks;
-  return min(kTileSeq, rows / (k + 1));
-}
-
-// Commits the ns sequences starting at s0 whose chunk keys, drafts and budgets
-// are in LDS (stop[] holds k and st[] the status on entry).  Every lane of the
-// workgroup calls it; only the last wave writes global memory.  Returns the
-// carry of the emit offsets.
-__device__ inline int commit_tile(const GreedyParams &P, TileShared &S, int s0, int ns, int carry) {
-  const int t = threadIdx.x, kp1 = P.k + 1, nrows = ns * kp1;
-  // one lane per row: fold its chunk keys, then test the row's stop
-  // conditions (draft j < k: a mismatch or EOS stops after emitting row j)
-  for (int r = t; r < nrows; r += kThreads) {
-    const uint64_t *kr = S.key + r * P.chunks;
-    uint64_t best = 0ull;
-    int c = 0;
-    for (; c + 8 <= P.chunks; c += 8) {
-      uint64_t x[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) x[q] = kr[c + q];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) best = x[q] > best ? x[q] : best;
-    }
-    for (; c < P.chunks; ++c) best = kr[c] > best ? kr[c] : best;
-    const int tok = argmax_key_index(best);
-    S.tok[r] = tok;
-    const int b = r / kp1, j = r - b * kp1;
-    if (j < P.k) {
-      const int d = S.d[b * P.k + j];
-      if (d < 0 || d >= P.V) atomicOr(&S.st[b], SPEC_ST_DRAFT_OOR);
-      if (tok != d || (P.eos >= 0 && tok == P.eos)) atomicMin(&S.stop[b], j);
-    }
-  }
-  __syncthreads();
-  // one lane per sequence: emitted count (first stop row + 1, capped by the
-  // budget) and accepted drafts (every emitted row before the last matched;
-  // the last emitted row counts if it matched its draft)
-  int cnt = 0;
-  if (t < ns) {
-    const int rem = S.rem[t];
-    cnt = S.stop[t] + 1;
-    if (rem >= 0) cnt = min(cnt, rem);
-    int acc = 0;
-    if (cnt > 0) {
-      const int last = cnt - 1;
-      acc = last + ((last < P.k && S.tok[t * kp1 + last] == S.d[t * P.k + last]) ? 1 : 0);
-    }
-    S.e[t] = cnt;
-    S.acc[t] = acc;
-  }
-  int total;
-  const int ex = block_excl_scan(t < ns ? cnt : 0, S.scan, &total);   // ends with a barrier
-  if (t < ns) S.off[t] = carry + ex;
-  __syncthreads();
-  // the store wave writes the tile's results
-  if (t >= kLoadLanes) {
-    const int l = t - kLoadLanes;
-    int32_t *out = P.out_tokens + static_cast<size_t>(s0) * kp1;
-    for (int r = l; r < nrows; r += kWave) {
-      const int b = r / kp1, j = r - b * kp1;
-      out[r] = j < S.e[b] ? S.tok[r] : -1;
-    }
-    for (int i = l; i < ns; i += kWave) {
-      P.accept_len[s0 + i] = S.acc[i];
-      P.emit_count[s0 + i] = S.e[i];
-      if (P.status) P.status[s0 + i] = S.st[i];
-      if (P.emit_offsets) P.emit_offsets[s0 + i] = S.off[i];
-    }
-  }
-  return carry + total;
-}
-
-// Loads of one tile, issued together by the loading lanes: the tile's slots
-// (agent scope; absent slots read 0), its drafts and budgets.
-struct TileLoads {
-  uint64_t v[kKPL];
-  int d[kKPL];
-  int rem;
-};
-
-__device__ inline void issue_tile(const GreedyParams &P, int s0, int ns, TileLoads &L) {
-  const int t = threadIdx.x, kp1 = P.k + 1, nk = ns * kp1 * P.chunks, nd = ns * P.k;
-  const uint64_t *slot0 = P.keys + static_cast<size_t>(s0) * kp1 * P.chunks;
-#pragma unroll
-  for (int i = 0; i < kKPL; ++i) {
-    const int f = t + i * kLoadLanes;
-    L.v[i] = f < nk ? load_agent(slot0 + f) : kEmptyKey;
-    L.d[i] = f < nd ? P.draft[static_cast<size_t>(s0) * P.k + f] : 0;
-  }
-  L.rem = (t < ns && P.remaining) ? P.remaining[s0 + t] : -1;
-}
-
 constexpr int kMaxPolls = 1 << 22;   // about 4 s of polling: a bound every wait reaches
+constexpr int kWaitVm0 = 0x0F70;     // s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt not waited for
+
+// The linear finisher folds results as they arrive.  Every lane polls its own
+// few consecutive slots of the tile at a time (all in flight, no workgroup
+// barrier between polls; a tile of more slots than the lanes hold is polled in
+// phases, in the producers' order), folds the arrived keys of each row in
+// registers and then into the row's maximum in LDS.  The lane whose keys
+// complete a row decides that row (argmax, mismatch, EOS).  After the tile's
+// last arrival wave 0 commits the sequences (counts, offsets) and the tokens
+// are written.
+struct ArrivalShared {
+  unsigned long long best[kArrRows];   // running maximum key of each row
+  int cnt[kArrRows];                   // chunk keys seen per row
+  int tok[kArrRows];                   // argmax of each decided row
+  int d[kArrRows];                     // the tile's drafts (ns * k < rows)
+  int stop[kTileSeq];                  // first row that stops the sequence (LDS minimum)
+  int rem[kTileSeq];                   // budgets
+  int st[kTileSeq];                    // status bits
+  int e[kTileSeq];                     // emit counts
+  int timed_out;
+};
+
+// Row r (row j of the tile's sequence b) has its argmax key `best`: record
+// the argmax and test the row's stop conditions (draft j < k: a mismatch or
+// EOS stops after emitting row j).
+__device__ inline void decide_row(const GreedyParams &P, ArrivalShared &S, int r, int b, int j, uint64_t best) {
+  const int tok = argmax_key_index(best);
+  S.tok[r] = tok;
+  if (j < P.k) {
+    const int d = S.d[b * P.k + j];
+    if (d < 0 || d >= P.V) atomicOr(&S.st[b], SPEC_ST_DRAFT_OOR);
+    if (tok != d || (P.eos >= 0 && tok == P.eos)) atomicMin(&S.stop[b], j);
+  }
+}
+
+// n chunk keys of row r (row j of sequence b) arrived, their maximum is m.
+// The count is an acquire-release LDS increment: the lane that completes the
+// row sees every other lane's maximum of that row.
+__device__ inline void arrive(const GreedyParams &P, ArrivalShared &S, int r, int b, int j, uint64_t m, int n) {
+  atomicMax(&S.best[r], static_cast<unsigned long long>(m));
+  if (__hip_atomic_fetch_add(&S.cnt[r], n, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) + n == P.chunks)
+    decide_row(P, S, r, b, j, atomicMax(&S.best[r], 0ull));   // the row's maximum, every key folded in
+}
+
+// The tile of sequences starting at s0: its first slot.
+__device__ inline uint64_t *tile_slots(const GreedyParams &P, int s0) {
+  return P.keys + static_cast<size_t>(s0 / P.tile_seq) * P.tile_span;
+}
+
+// Polls of this lane's slots (bit i of mask: logical slot ph*kPhaseSlots +
+// n*t + i, at position ph*kPhaseSlots + i*L + t) of phase ph of a tile.
+__device__ inline void poll_slots(const uint64_t *slot0, int ph, int L, unsigned mask, uint64_t *v) {
+  const uint64_t *p = slot0 + ph * kPhaseSlots + threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kSlotsPerLane; ++i)
+    if ((mask >> i) & 1u) v[i] = load_agent(p + i * L);
+}
+
+// The slots lane t holds in phase ph of a tile of nk slots (n per lane), as a
+// bit mask.
+__device__ inline unsigned lane_slots(int ph, int nk, int n) {
+  const int f0 = ph * kPhaseSlots + threadIdx.x * n;
+  unsigned m = 0u;
+#pragma unroll
+  for (int i = 0; i < kSlotsPerLane; ++i)
+    if (i < n && f0 + i < nk) m |= 1u << i;
+  return m;
+}
+
+// Loads of one tile's slots (phase 0), drafts and budgets into registers.
+__device__ inline void issue_arrivals(const GreedyParams &P, int s0, int ns, uint64_t *v, int *dv, int &rv) {
+  const int t = threadIdx.x, kp1 = P.k + 1, nk = ns * kp1 * P.chunks, nd = ns * P.k;
+#pragma unroll
+  for (int i = 0; i < kSlotsPerLane; ++i) v[i] = 0ull;
+  int n, L;
+  phase_shape(min(kPhaseSlots, nk), n, L);
+  poll_slots(tile_slots(P, s0), 0, L, lane_slots(0, nk, n), v);
+#pragma unroll
+  for (int i = 0; i < kArrRows / kThreads; ++i) {
+    const int f = t + i * kThreads;
+    dv[i] = f < nd ? P.draft[static_cast<size_t>(s0) * P.k + f] : 0;
+  }
+  rv = (t < ns && P.remaining) ? P.remaining[s0 + t] : -1;
+}
 
 // Workgroup 0 of the single-launch verify.
 __device__ void finish_verify(const GreedyParams &P) {
-  __shared__ TileShared S;
-  const int t = threadIdx.x, kp1 = P.k + 1;
-  const bool loader = t < kLoadLanes;
+  __shared__ ArrivalShared S;
+  const int t = threadIdx.x, lane = t & (kWave - 1), kp1 = P.k + 1;
   const int per = tile_sequences(P.k, P.chunks);
   int carry = 0, polls = 0;
-  bool timed_out = false;
-  TileLoads L;
-#pragma unroll
-  for (int i = 0; i < kKPL; ++i) L.v[i] = kEmptyKey;
-  if (loader) issue_tile(P, 0, min(per, P.B), L);
+  uint64_t v[kSlotsPerLane];
+  int dv[kArrRows / kThreads];
+  int rv;
+  if (t == 0) S.timed_out = 0;
+  issue_arrivals(P, 0, min(per, P.B), v, dv, rv);
   for (int s0 = 0; s0 < P.B; s0 += per) {
-    const int ns = min(per, P.B - s0), nk = ns * kp1 * P.chunks;
-    const uint64_t *slot0 = P.keys + static_cast<size_t>(s0) * kp1 * P.chunks;
-    // wait until every slot of the tile is published (re-reading only the
-    // missing ones); the bound keeps the wait finite
-    while (true) {
-      bool present = true;
+    const int ns = min(per, P.B - s0), nrows = ns * kp1, nk = nrows * P.chunks;
+    uint64_t *slot0 = tile_slots(P, s0);
+    // the tile's LDS state
+    for (int r = t; r < nrows; r += kThreads) {
+      S.best[r] = 0ull;
+      S.cnt[r] = 0;
+    }
 #pragma unroll
-      for (int i = 0; i < kKPL; ++i) present = present && L.v[i] != 0ull;
-      if (__syncthreads_and(present)) break;
-      if (++polls >= kMaxPolls) { timed_out = true; break; }
-      __builtin_amdgcn_s_sleep(1);
-      if (loader) {
+    for (int i = 0; i < kArrRows / kThreads; ++i) {
+      const int f = t + i * kThreads;
+      if (f < ns * P.k) S.d[f] = dv[i];
+    }
+    if (t < ns) {
+      S.stop[t] = P.k;
+      S.rem[t] = rv;
+      S.st[t] = 0;
+    }
+    __syncthreads();
+    // poll this lane's slots until each has arrived, phase after phase; the
+    // bound keeps the wait finite (and a timeout anywhere ends every lane's wait)
+    for (int ph = 0; ph * kPhaseSlots < nk; ++ph) {
+      int n, L;                                               // slots per lane, lanes
+      phase_shape(min(kPhaseSlots, nk - ph * kPhaseSlots), n, L);
+      const int f0 = ph * kPhaseSlots + t * n;                // this lane's first logical slot of the phase
+      uint64_t *pos0 = slot0 + ph * kPhaseSlots + t;          // logical slot f0 + i is at pos0[i * L]
+      unsigned miss = lane_slots(ph, nk, n);
+      if (ph > 0) poll_slots(slot0, ph, L, miss, v);
+      const int r_lo = f0 / P.chunks, r_hi = (f0 + n - 1) / P.chunks;
+      const int b_lo = r_lo / kp1, j_lo = r_lo - b_lo * kp1;   // row r_lo is row j_lo of sequence b_lo
+      unsigned filled = 0u;                                     // slots counted as empty after a timeout
+      while (true) {
+        unsigned got = 0u;
 #pragma unroll
-        for (int i = 0; i < kKPL; ++i) {
-          const int f = t + i * kLoadLanes;
-          if (L.v[i] == 0ull) L.v[i] = load_agent(slot0 + f);
+        for (int i = 0; i < kSlotsPerLane; ++i)
+          if (((miss >> i) & 1u) && v[i] != 0ull) got |= 1u << i;
+        miss &= ~got;
+        // the arrivals are folded per row in registers first (a lane's slots
+        // are consecutive, so they span few rows), then once per row into LDS
+        for (int r = r_lo, b = b_lo, j = j_lo; got != 0u && r <= r_hi; ++r) {
+          const int lo = max(r * P.chunks - f0, 0), hi = min(n, (r + 1) * P.chunks - f0);
+          const unsigned g = got & ((1u << hi) - 1u) & ~((1u << lo) - 1u);   // row r's slots among them
+          const int rb = b, rj = j;
+          if (++j == kp1) {
+            j = 0;
+            ++b;
+          }
+          if (g == 0u) continue;
+          got &= ~g;
+          if (g & filled) atomicOr(&S.st[rb], SPEC_ST_INCOMPLETE);
+          uint64_t m = 0ull;
+#pragma unroll
+          for (int i = 0; i < kSlotsPerLane; ++i) {
+            if ((g >> i) & 1u) {
+              m = v[i] > m ? v[i] : m;
+              pos0[i * L] = 0ull;       // the workspace returns to zero (seen by the next launch)
+            }
+          }
+          arrive(P, S, r, rb, rj, m, __builtin_popcount(g));
         }
+        if (miss == 0u) break;
+        if (__hip_atomic_load(&S.timed_out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) || ++polls >= kMaxPolls) {
+          // the wait is over: the slots still missing count as empty chunks
+          // and their sequences are marked incomplete
+          __hip_atomic_store(&S.timed_out, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+          for (int i = 0; i < kSlotsPerLane; ++i)
+            if ((miss >> i) & 1u) v[i] = kEmptyKey;
+          filled = miss;
+          continue;
+        }
+        // this lane's stores (zeroed slots, outputs) complete before its next
+        // polls are issued, about 0.2 us apart (both measured faster than
+        // letting polls overtake the stores or polling back to back)
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_s_sleep(8);
+        poll_slots(slot0, ph, L, miss, v);
       }
     }
-    if (loader) {
-#pragma unroll
-      for (int i = 0; i < kKPL; ++i) {
-        const int f = t + i * kLoadLanes;
-        if (f < nk) S.key[f] = L.v[i];
-        if (f < ns * P.k) S.d[f] = L.d[i];
-      }
-      if (t < ns) {
-        S.rem[t] = L.rem;
-        S.stop[t] = P.k;
-        S.st[t] = timed_out ? SPEC_ST_INCOMPLETE : 0;
+    // the next tile's loads go out before the wait for the other lanes
+    if (s0 + per < P.B) issue_arrivals(P, s0 + per, min(per, P.B - s0 - per), v, dv, rv);
+    __syncthreads();
+    // wave 0 commits the tile's sequences, 64 at a time: emitted count
+    // (first stop row + 1, capped by the budget), accepted drafts (every
+    // emitted row before the last matched; the last emitted row counts if it
+    // matched its draft), the emit offsets after the carry
+    if (t < kWave) {
+      for (int base = 0; base < ns; base += kWave) {
+        const int b = base + lane;
+        int cnt = 0;
+        if (b < ns) {
+          const int rem = S.rem[b];
+          cnt = S.stop[b] + 1;
+          if (rem >= 0) cnt = min(cnt, rem);
+          int acc = 0;
+          if (cnt > 0) {
+            const int last = cnt - 1;
+            acc = last + ((last < P.k && S.tok[b * kp1 + last] == S.d[b * P.k + last]) ? 1 : 0);
+          }
+          S.e[b] = cnt;
+          P.accept_len[s0 + b] = acc;
+          P.emit_count[s0 + b] = cnt;
+          if (P.status) P.status[s0 + b] = S.st[b];
+        }
+        const int inc = wave_incl_scan(cnt);
+        if (P.emit_offsets && b < ns) P.emit_offsets[s0 + b] = carry + inc - cnt;
+        carry += read_lane(inc, kWave - 1);
       }
     }
     __syncthreads();
-    // the next tile's loads are in flight while this one is committed
-    if (loader && s0 + per < P.B) issue_tile(P, s0 + per, min(per, P.B - s0 - per), L);
-    carry = commit_tile(P, S, s0, ns, carry);
+    // the emitted tokens, one lane per row
+    int32_t *out = P.out_tokens + static_cast<size_t>(s0) * kp1;
+    for (int r = t; r < nrows; r += kThreads) out[r] = r % kp1 < S.e[r / kp1] ? S.tok[r] : -1;
+    if (s0 + per < P.B) __syncthreads();   // the next tile's LDS state overwrites this one's
   }
-  if (P.emit_offsets && t == kLoadLanes) P.emit_offsets[P.B] = carry;
-  // every slot back to 0 for the next call (ordered before it by the launch)
-  for (int f = t; f < P.nprod; f += kThreads) P.keys[f] = 0ull;
+  if (P.emit_offsets && t == 0) P.emit_offsets[P.B] = carry;
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void greedy_verify_kernel(GreedyParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void greedy_verify_kernel(GreedyParams P) {
   if (blockIdx.x == 0) finish_verify(P);
   else stream_chunk<BF16, true>(P, static_cast<int>(blockIdx.x) - 1);
 }
@@ -800,10 +903,14 @@ static int greedy_verify_launch(const void *logits, spec_dtype dt, int B, int k,
   P.nprod = static_cast<int>(nblocks);
   P.first_child = P.next_sibling = nullptr;
   P.path = nullptr;
+  P.tile_seq = 0;
+  P.tile_span = 0;
   (void)elt;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (!noalloc && tile_sequences(k, chunks) >= 1 && nblocks + 1 < INT32_MAX) {
+    P.tile_seq = tile_sequences(k, chunks);
+    P.tile_span = static_cast<int>(tile_span(k, chunks));
     // one launch: workgroup 0 commits, the others stream
     const dim3 grid(static_cast<unsigned>(nblocks + 1));
     if (dt == SPEC_BF16) hipLaunchKernelGGL(greedy_verify_kernel<true>, grid, dim3(kThreads), 0, s, P);
@@ -965,6 +1072,8 @@ extern "C" int spec_verify_tree(const void *logits, spec_dtype dt, int B, int N,
   P.first_child = first_child;
   P.next_sibling = next_sibling;
   P.path = path;
+  P.tile_seq = 0;
+  P.tile_span = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (tree_tile_sequences(N, chunks) >= 1 && nblocks + 1 < INT32_MAX) {
