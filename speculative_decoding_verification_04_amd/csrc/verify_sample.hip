@@ -60,9 +60,10 @@ __device__ inline double block_sum_d(double v, double *sh) {
 }
 
 // Block-wide exclusive sum of one double per lane, in a fixed order (lane
-// order within a wave, then waves).  `sh` holds kWaves + 1 doubles; *total
-// receives the block total.  Contains barriers.
-__device__ inline double block_excl_scan_d(double v, double *sh, double *total) {
+// order within a wave, then waves); *total receives the block total.  One
+// barrier: `sh` (kWaves doubles) must not be written again before a later
+// barrier.
+__device__ inline double block_excl_scan_d1(double v, double *sh, double *total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const double inc = wave_incl_scan(v);
   if (lane == kWave - 1) sh[w] = inc;
@@ -73,7 +74,6 @@ __device__ inline double block_excl_scan_d(double v, double *sh, double *total) 
     if (i < w) base += sh[i];
     tot += sh[i];
   }
-  __syncthreads();
   *total = tot;
   return base + (inc - v);
 }
@@ -124,11 +124,10 @@ __device__ inline void finish_sequence(const SampleParams &P, int b) {
   __shared__ int4 sh_ch;
   __shared__ double sh_red[kWaves];
   __shared__ double sh_part[kMaxChunks];
-  __shared__ int sh_scan[kWaves + 1];
-  __shared__ int sh_last[kWaves];
-  __shared__ double sh_dscan[kWaves + 1];
-  __shared__ int sh_cs, sh_tok;
-  __shared__ double sh_base;
+  __shared__ double sh_pre[kThreads];
+  __shared__ int sh_scan[2][kWaves];
+  __shared__ int sh_last[2][kWaves];
+  __shared__ double sh_dscan[3][kWaves + 1];
 
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), w = t / kWave;
@@ -168,7 +167,6 @@ __device__ inline void finish_sequence(const SampleParams &P, int b) {
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    for (int i = t; i < nc; i += kThreads) keys[i] = 0ull;   // ordered before the next call by the launch
     if (timed_out) {
       st |= SPEC_ST_INCOMPLETE;
     } else {
@@ -178,13 +176,13 @@ __device__ inline void finish_sequence(const SampleParams &P, int b) {
       const int c0 = t * per;
       // total mass and each lane's exclusive prefix over the chunk masses
       double pre = 0.0;
-      auto scan_parts = [&]() {
+      auto scan_parts = [&](double *sh) {
         double mine = 0.0;
         for (int i = 0; i < per; ++i)
           if (c0 + i < nc) mine += sh_part[c0 + i];
-        pre = block_excl_scan_d(mine, sh_dscan, &S);
+        pre = block_excl_scan_d1(mine, sh, &S);
       };
-      scan_parts();
+      scan_parts(sh_dscan[0]);
       if (isfinite(S) && !(S > 0.0)) {
         st |= SPEC_ST_RESID_ZERO;
         if (mode == MODE_RESID) {         // fall back to the target row p_j itself
@@ -194,7 +192,7 @@ __device__ inline void finish_sequence(const SampleParams &P, int b) {
             if (t == 0) sh_part[i] = part;
           }
           __syncthreads();
-          scan_parts();
+          scan_parts(sh_dscan[1]);
         }
       }
       if (!isfinite(S)) {
@@ -217,29 +215,24 @@ __device__ inline void finish_sequence(const SampleParams &P, int b) {
             run += pc;
           }
         }
+        sh_pre[t] = pre;
         const int wc = wave_min(cand), wl = wave_max_i(last);
         if (lane == 0) {
-          sh_scan[w] = wc;
-          sh_last[w] = wl;
+          sh_scan[0][w] = wc;
+          sh_last[0][w] = wl;
         }
         __syncthreads();
-        if (t == 0) {
-          int best = INT_MAX, lp = -1;
-          for (int i = 0; i < kWaves; ++i) {
-            best = min(best, sh_scan[i]);
-            lp = max(lp, sh_last[i]);
-          }
-          sh_cs = best != INT_MAX ? best : lp;
+        int cs = INT_MAX, lp = -1;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+          cs = min(cs, sh_scan[0][i]);
+          lp = max(lp, sh_last[0][i]);
         }
-        __syncthreads();
-        const int cs = sh_cs;
-        if (cs >= c0 && cs < c0 + per) {                // the lane owning chunk cs: mass before it
-          double run = pre;
-          for (int c = c0; c < cs; ++c) run += sh_part[c];
-          sh_base = run;
-        }
-        __syncthreads();
-        const double base = sh_base;
+        if (cs == INT_MAX) cs = lp;
+        // mass before chunk cs, added in its owner lane's order
+        const int owner = cs / per;
+        double base = sh_pre[owner];
+        for (int c = owner * per; c < cs; ++c) base += sh_part[c];
         // in-chunk scan in index order: lane t owns kEPT consecutive entries
         const int lo = cs * kChunk + t * kEPT;
         float x[kEPT];
@@ -248,7 +241,7 @@ __device__ inline void finish_sequence(const SampleParams &P, int b) {
 #pragma unroll
         for (int i = 0; i < kEPT; ++i) mine += static_cast<double>(x[i]);
         double ctot;
-        double run = base + block_excl_scan_d(mine, sh_dscan, &ctot);
+        double run = base + block_excl_scan_d1(mine, sh_dscan[2], &ctot);
         int cpos = INT_MAX, lastpos = -1;
 #pragma unroll
         for (int i = 0; i < kEPT; ++i) {
@@ -261,22 +254,22 @@ __device__ inline void finish_sequence(const SampleParams &P, int b) {
         }
         const int wcp = wave_min(cpos), wlp = wave_max_i(lastpos);
         if (lane == 0) {
-          sh_scan[w] = wcp;
-          sh_last[w] = wlp;
+          sh_scan[1][w] = wcp;
+          sh_last[1][w] = wlp;
         }
         __syncthreads();
-        if (t == 0) {
-          int best = INT_MAX, lp = -1;
-          for (int i = 0; i < kWaves; ++i) {
-            best = min(best, sh_scan[i]);
-            lp = max(lp, sh_last[i]);
-          }
-          sh_tok = best != INT_MAX ? best : lp;
+        int best = INT_MAX, lpos = -1;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+          best = min(best, sh_scan[1][i]);
+          lpos = max(lpos, sh_last[1][i]);
         }
-        __syncthreads();
-        tok = sh_tok;
+        tok = best != INT_MAX ? best : lpos;
       }
     }
+    // every slot back to zero (ordered before the next call by the launch);
+    // issued after the draw's loads, which would otherwise wait for them
+    for (int i = t; i < nc; i += kThreads) keys[i] = 0ull;
   }
   if (t < kp1) {                                      // accepted drafts, then the drawn token
     int val = -1;
