@@ -239,6 +239,8 @@ def _trace_rows(directory: str):
                     label = m.group(1) + (m.group(2) or "").replace("specv::(anonymous namespace)::", "")
                 elif "neg_kernel" in n:
                     label = "torch neg (copy probe)"
+                elif "floor_max_kernel" in n:
+                    label = "floor_max_kernel (read floor, bench_floor.hip)"
                 else:
                     continue
                 t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
@@ -269,7 +271,8 @@ def summarize_trace(trace_dir: str, bench_log: str) -> None:
            "are the secondary measurements and the batch-size sweeps.", "",
            "| kernel | grid | calls | avg (us) | min (us) | max (us) | |", "|---|---|---|---|---|---|---|"]
     for (k, g), (v, starts) in sorted(acc.items(), key=lambda x: -sum(x[1][0])):
-        step = t_probe is not None and max(starts) < t_probe and not k.startswith("torch neg")
+        step = (t_probe is not None and max(starts) < t_probe and not k.startswith("torch neg")
+                and not k.startswith("floor_max"))
         out.append(f"| `{k}` | {g} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
                    f"{'**step**' if step else ''} |")
     rf, rv = b["roofline"], b["roofline_verify"]
@@ -279,7 +282,11 @@ def summarize_trace(trace_dir: str, bench_log: str) -> None:
             f"{rf['frac']:.3f} of 8 TB/s",
             f"- `greedy_verify_kernel` (the whole verify call): {b['verify_us_per_launch']:.2f} us per launch, "
             f"{rv['achieved']:.0f} GB/s, {rv['frac']:.3f} of 8 TB/s",
-            f"- copy probe (torch int32 negation, 2 GiB each way): {b['copy_probe_GBps']:.0f} GB/s", "",
+            f"- copy probe (torch int32 negation, 2 GiB each way): {b['copy_probe_GBps']:.0f} GB/s",
+            (f"- read floor (`floor_max_kernel`, one pass over the verify call's logits): "
+             f"{b['verify_read_floor']['us_per_launch']:.2f} us per launch, "
+             f"{b['verify_read_floor']['frac_of_peak']:.3f} of 8 TB/s" if b.get("verify_read_floor") else
+             "- read floor: not measured"), "",
             "Under the tracer every dispatch carries the tracer's own overhead, so the bench's back-to-back "
             "timings in a traced run are slower than untraced ones; the kernel rows above are the kernels' own "
             "durations, to set beside an untraced bench line.", ""]
@@ -418,6 +425,15 @@ def main() -> int:
     t_launch = a_ev.elapsed_time(b_ev) * 1e-3 / n_back
     log(f"verify launch {t_launch * 1e6:.2f} us (back-to-back)")
 
+    # The verify call's floor: one plain pass over the same logits in the same
+    # chunks (bench_floor.hip, built beside this file by __graft_entry__.build),
+    # the same back-to-back timing.  Not part of the step.
+    read_floor = None
+    if not args.step_only:
+        read_floor = measure_read_floor(torch, logits, rows, V, n_back)
+        if read_floor:
+            log(f"read floor {read_floor['us_per_launch']:.2f} us per launch")
+
     # Reference for the verify call's floor: the framework's own reductions
     # over the same bytes (every logit of the same rotating buffers, the same
     # back-to-back timing).  Not part of the step.
@@ -520,6 +536,7 @@ def main() -> int:
                             "traffic_requests": traffic_bytes("greedy_verify_kernel", requests=True),
                             "algorithmic_bytes_per_launch": ver_bytes,
                             "timing": f"HIP events around {n_back} back-to-back launches over the rotating buffers"},
+        "verify_read_floor": read_floor,
         "verify_stream_reference": stream_ref,
         "verify_rows_per_s": rows / t_launch,
         "verify_us_per_launch": t_launch * 1e6,
@@ -535,6 +552,38 @@ def main() -> int:
     }
     print(json.dumps(result))
     return 0
+
+
+def measure_read_floor(torch, logits, rows: int, V: int, n_back: int):
+    """Per-launch time of bench_floor.so's one-pass chunk maximum over the
+    verify call's rotating logit buffers (HIP events around n_back
+    back-to-back launches), or None when the probe is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "bench_floor.so")
+    if not os.path.exists(path):
+        log("read floor: bench_floor.so is not built (run __graft_entry__.build())")
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.floor_chunk_max_bf16
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    nb = len(logits)
+    out = torch.empty(rows * ((V + 16383) // 16384), dtype=torch.float32, device=logits[0].device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def call(i):
+        if fn(ctypes.c_void_p(logits[i % nb].data_ptr()), rows, V, ctypes.c_void_p(out.data_ptr()), stream) < 0:
+            raise RuntimeError("floor_chunk_max_bf16 rejected its arguments")
+
+    call(0)
+    torch.cuda.synchronize()
+    if float(out.max()) != float(logits[0].float().max()):
+        raise RuntimeError("read floor: chunk maxima disagree with the buffer's maximum")
+    t = _back_to_back(torch, call, n_back)
+    nbytes = rows * V * 2
+    return {"kernel": "floor_max_kernel (bench_floor.hip: chunk maxima only, no argmax, no commit)",
+            "us_per_launch": t * 1e6, "GBps": nbytes / t / 1e9, "frac_of_peak": nbytes / t / PEAK_HBM,
+            "bytes": nbytes, "timing": f"HIP events around {n_back} back-to-back launches over the rotating buffers"}
 
 
 def _spread(ts, scale: float) -> dict:
@@ -875,7 +924,13 @@ def config_step(dev, np, torch, sv, W, c: int, steps: int = 12, warm: int = 3, n
     wall = time.perf_counter() - t0
     t_rea = [evs[r][1].elapsed_time(evs[r][2]) * 1e-3 for r in range(warm, R)]
     rea_bytes = [int(moved[r].item()) + 8 * B * C for r in range(warm, R)]
-    t_launch = _back_to_back(torch, verify, 6 * nbuf)
+    t_eager = _back_to_back(torch, verify, 6 * nbuf)
+    ctr = [0]
+
+    def verify_next():
+        verify(ctr[0])
+        ctr[0] += 1
+    t_launch, _ = _time_calls(torch, verify_next, 12, inner=6 * nbuf)
     if ver_bytes is None:                       # stochastic: one verify of each buffer, realized bytes
         vb = []
         for i in range(nbuf):
@@ -888,7 +943,12 @@ def config_step(dev, np, torch, sv, W, c: int, steps: int = 12, warm: int = 3, n
     out = {"workload": f"{cfg['name']}: B={B} k={k} V={V} {cfg.get('logit_dtype', 'f32 p/q')}, KV {L}x{H}x{D} {kvdt}, "
                        f"{nbuf} rotating inputs",
            "rows_per_s": rows * steps / wall, "ms_per_step": wall / steps * 1e3,
-           "verify_us_per_launch": t_launch * 1e6, "verify_algorithmic_bytes": ver_bytes,
+           "step_timing": "eager launches through the Python binding, host clock around the timed steps "
+                          "(for small workloads the host's launch rate bounds it)",
+           "verify_us_per_launch": t_launch * 1e6,
+           "verify_timing": f"GPU time: {6 * nbuf} calls over the rotating inputs captured in one HIP graph, "
+                            "median replay / calls",
+           "verify_us_per_launch_eager": t_eager * 1e6, "verify_algorithmic_bytes": ver_bytes,
            "verify_GBps": ver_bytes / t_launch / 1e9, "verify_frac_of_peak": ver_bytes / t_launch / PEAK_HBM,
            "realign_ms_per_call": statistics.mean(t_rea) * 1e3,
            "realign_GBps": sum(rea_bytes) / sum(t_rea) / 1e9,

@@ -46,5 +46,26 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+BENCH_FLOOR_SRC = os.path.join(ROOT, "bench_floor.hip")
+BENCH_FLOOR_LIB = os.path.join(ROOT, "bench_floor.so")
+
+
+def build_bench_floor(verbose: bool = False) -> str:
+    """Compile bench.py's read-floor probe (a measurement aid beside bench.py,
+    not part of the library) into bench_floor.so at the repository root."""
+    tmp = BENCH_FLOOR_LIB + ".tmp"
+    cmd = [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-Wno-unused-command-line-argument", BENCH_FLOOR_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {r.returncode}")
+    os.replace(tmp, BENCH_FLOOR_LIB)
+    return BENCH_FLOOR_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -118,12 +118,18 @@ inline size_t tile_span(int k, int chunks) {
   return round_up(static_cast<size_t>(tile_sequences(k, chunks)) * (k + 1) * chunks + 3, 4);
 }
 
-// Slots of either layout: whole tiles in polling order, or B*(k+1)*chunks.
+// Slots of the row-major layout (two-launch path): B*(k+1)*chunks.
+inline size_t greedy_plain_bytes(int B, int k, int chunks) {
+  return round_up(static_cast<size_t>(B) * (k + 1) * chunks * sizeof(uint64_t), 256);
+}
+
+// Slots of either layout: whole tiles in polling order, or row-major.
 inline size_t greedy_ws_bytes(int B, int k, int chunks) {
-  size_t slots = static_cast<size_t>(B) * (k + 1) * chunks;
   const int per = tile_sequences(k, chunks);
-  if (per >= 1) slots = std::max(slots, static_cast<size_t>((B + per - 1) / per) * tile_span(k, chunks));
-  return round_up(slots * sizeof(uint64_t), 256);
+  size_t b = greedy_plain_bytes(B, k, chunks);
+  if (per >= 1)
+    b = std::max(b, round_up(static_cast<size_t>((B + per - 1) / per) * tile_span(k, chunks) * sizeof(uint64_t), 256));
+  return b;
 }
 
 template <bool BF16>
@@ -1009,7 +1015,8 @@ extern "C" int spec_verify_greedy_noalloc(const void *logits, spec_dtype dt, int
   int rc = greedy_verify_check(logits, dt, B, k, V, draft, remaining, accept_len, emit_count, out_tokens,
                                emit_offsets, status, nullptr, &wsb);
   if (rc != SPEC_OK) return rc;
-  if (wsb > SPEC_GREEDY_SCRATCH_BYTES) return SPEC_ECAPACITY;
+  // the two-launch path keeps its chunk keys row-major
+  if (greedy_plain_bytes(B, k, greedy_chunks(V, dt)) > SPEC_GREEDY_SCRATCH_BYTES) return SPEC_ECAPACITY;
   void *keys = nullptr;
   rc = scratch_address(&keys);
   if (rc != SPEC_OK) return rc;
