@@ -42,9 +42,9 @@
  *   - A greedy verify call is one launch: streaming workgroups publish per-
  *     chunk results and one workgroup of the same launch commits them; tree
  *     verification does the same over whole trees.  Calls whose rows need
- *     more chunk results than that workgroup holds at once (more than 1024
- *     per sequence or tree) launch a streaming pass and a commit pass,
- *     synchronised by the stream order.
+ *     more chunk results than that workgroup holds at once (more than 16384
+ *     per sequence, or 1024 per tree) launch a streaming pass and a commit
+ *     pass, synchronised by the stream order.
  *   - A stochastic verify call is one launch too: streaming workgroups publish
  *     the chunk masses of the row each sequence draws from, and one workgroup
  *     per sequence of the same launch, dispatched after them, draws.  The
