@@ -206,3 +206,38 @@ def test_greedy_and_tree_share_a_workspace():
         assert np.array_equal(gt["emit_count"], ref["emit_count"])
         assert np.array_equal(gt["out_tokens"], ref["out_tokens"])
         assert int(torch.count_nonzero(w).item()) == 0
+
+
+def _finisher_regime(B, k, V):
+    """Tiles and last-phase shapes of the single launch's finisher for a
+    16-byte aligned bf16 batch: chunks per row, sequences per tile, and for
+    each tile the size m of its last polling phase and the slots per lane n
+    (phases of 2048 slots; n = min(4, m // 16), at least 1)."""
+    chunks = -(-V // 16384)
+    per = min(256, min(1024, 16384 // chunks) // (k + 1))
+    tiles = []
+    for s0 in range(0, B, per):
+        nk = min(per, B - s0) * (k + 1) * chunks
+        m = nk - (nk - 1) // 2048 * 2048
+        tiles.append((nk, m, max(1, min(4, m // 16))))
+    return chunks, per, tiles
+
+
+@pytest.mark.parametrize("B,k,V,want", [
+    (257, 3, 5 * 16384, (5, 1)),        # three phases in tile 0, a 20-slot tile 1 (one slot per lane)
+    (212, 4, 1000, (1, 2)),             # chunks of one row each, a 40-slot last tile (two per lane)
+    (130, 7, 3 * 16384 - 8, (3, 3)),    # three chunks per row, a 48-slot last tile (three per lane)
+    (300, 1, 2 * 16384, (2, 4)),        # rows split over two lanes' slots, a 176-slot last tile
+])
+def test_finisher_tiles_and_phases(B, k, V, want):
+    """The single launch's finisher polls each tile in phases of 2048 chunk
+    keys, each lane holding 1-4 consecutive keys stored one cache line apart;
+    these batches end in a tile whose last phase has each of those shapes,
+    after a tile of several phases.  Outputs are exact against the oracle."""
+    chunks, per, tiles = _finisher_regime(B, k, V)
+    assert (chunks, tiles[-1][2]) == want and len(tiles) == 2
+    note(f"greedy finisher tiles B={B} k={k} V={V}: {tiles}")
+    rng = np.random.default_rng(B * 1000 + k)
+    g = W.planted_greedy(rng, rng, B, k, V, 2.0, "bf16", rng.uniform(0.3, 0.95, B))
+    remaining = rng.integers(-1, k + 3, B).astype(np.int32)
+    _compare(g["logits"], "bf16", g["drafts"], eos_id=int(rng.integers(0, V)), remaining=remaining)
