@@ -7,8 +7,9 @@
 // body (App. C) is not on the page; the rule implemented here is stated in
 // include/spec_verify.h.
 //
-// Design.  The window is small (<= SPEC_GROUP_MAX_N), so one workgroup does
-// it all: a bitonic sort of 64-bit keys (length in the high word,
+// Design.  The window is small (<= SPEC_GROUP_MAX_N), so one workgroup (one
+// lane per key up to 1024 keys, at least one wave) does it all: a bitonic
+// sort of 64-bit keys (length in the high word,
 // order-corrected for sign; window index in the low word), which makes every
 // key distinct and the sort stable by construction (up to 1024 keys one per
 // lane, strides below a wave by lane shuffles; larger windows in LDS); then
@@ -22,12 +23,17 @@
 namespace specv {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kPer = SPEC_GROUP_MAX_N / kThreads;   // sorted positions per lane
+constexpr int kMaxThreads = 1024;
+
+// Workgroup size for a window of P2 (a power of two) keys: one key per lane
+// up to 1024 keys, at least one wave.  Smaller windows run on fewer waves, so
+// every barrier and every lane-shuffle stage involves fewer waves.
+inline int group_threads(int P2) { return P2 < kWave ? kWave : (P2 < kMaxThreads ? P2 : kMaxThreads); }
 
 // Block-wide exclusive sum of one 64-bit value per lane (lane order); `sh`
 // holds kThreads / kWave + 1 words; *total receives the block total.
 // Barriers: call from every lane.
+template <int kThreads>
 __device__ inline unsigned long long block_excl_scan_u64(unsigned long long v, unsigned long long *sh,
                                                          unsigned long long *total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -48,10 +54,13 @@ __device__ inline unsigned long long block_excl_scan_u64(unsigned long long v, u
   return r;
 }
 
+template <int kThreads>
 __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t *lengths, int N, int B, int mg,
                                                           int P2, int32_t *perm, int32_t *batch_start,
                                                           int32_t *batch_len, int32_t *num_batches,
                                                           int32_t *num_grouped) {
+  // sorted positions per lane: one below 1024 lanes (then N <= P2 <= kThreads)
+  constexpr int kPer = kThreads < kMaxThreads ? 1 : SPEC_GROUP_MAX_N / kMaxThreads;
   extern __shared__ unsigned long long smem[];
   unsigned long long *keys = smem;                                  // [P2]
   int *run_start = reinterpret_cast<int *>(smem + P2);              // [N + 1]
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t *lengths,
     const unsigned long long packed = (static_cast<unsigned long long>(su) << 42) |
                                       (static_cast<unsigned long long>(sb) << 21) | static_cast<unsigned long long>(sf);
     unsigned long long tot;
-    const unsigned long long ex = block_excl_scan_u64(packed, sh64, &tot);
+    const unsigned long long ex = block_excl_scan_u64<kThreads>(packed, sh64, &tot);
     constexpr unsigned long long m21 = (1ull << 21) - 1;
     xu = static_cast<int>(ex >> 42);
     xb = static_cast<int>((ex >> 21) & m21);
@@ -244,8 +253,22 @@ extern "C" int spec_group_same_length(const int32_t *lengths, int N, int B, int 
   int P2 = 2;
   while (P2 < N) P2 <<= 1;
   const size_t shmem = static_cast<size_t>(P2) * 8 + static_cast<size_t>(N + 1) * 4;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), shmem, static_cast<hipStream_t>(stream), lengths, N, B,
-                     min_group, P2, perm, batch_start, batch_len, num_batches, num_grouped);
+  switch (group_threads(P2)) {
+#define SPEC_GROUP_LAUNCH(NT)                                                                                   \
+  case NT:                                                                                                      \
+    hipLaunchKernelGGL(group_kernel<NT>, dim3(1), dim3(NT), shmem, s, lengths, N, B, min_group, P2, perm,      \
+                       batch_start, batch_len, num_batches, num_grouped);                                       \
+    break;
+    SPEC_GROUP_LAUNCH(64)
+    SPEC_GROUP_LAUNCH(128)
+    SPEC_GROUP_LAUNCH(256)
+    SPEC_GROUP_LAUNCH(512)
+    SPEC_GROUP_LAUNCH(1024)
+#undef SPEC_GROUP_LAUNCH
+    default:
+      return SPEC_EINVAL;
+  }
   return launch_status();
 }
