@@ -95,6 +95,16 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 /* Human-readable name of a return code. */
 const char *spec_strerror(int code);
 
+/* Bound on the polls of the single-launch greedy and tree verification's
+ * committing workgroup (each poll is one round trip to memory, plus about
+ * 0.2 us); polls <= 0 restores the default (about 4 s).  It applies to calls
+ * launched afterwards, from any thread, and returns the previous setting
+ * (0: the default).  Meant for tests of the incomplete path: a tiny bound
+ * makes the commit stop waiting, count the chunk results still missing as
+ * empty chunks and mark those sequences SPEC_ST_INCOMPLETE, while every
+ * workgroup still ends normally. */
+int spec_set_wait_bound(int polls);
+
 /* ------------------------------------------------------------------------ *
  * Greedy verification.
  * [Walkthrough] 3.3 (row alignment) and 4.1 (greedy commitment); [Forensics]
@@ -121,7 +131,9 @@ const char *spec_strerror(int code);
  *               zero-filled before its first use (see the conventions above)
  *   status      also SPEC_ST_INCOMPLETE if the commit stopped waiting for a
  *               chunk result (a bound of seconds that normal operation never
- *               reaches)
+ *               reaches; see spec_set_wait_bound).  Chunk results may still
+ *               land in the workspace after such a call: zero-fill it again
+ *               before its next use.
  * Errors: SPEC_EINVAL for NULL required pointers, B < 1, k < 1, V < 1,
  * V >= 2^31 - 1 or a misaligned logits pointer; SPEC_ECAPACITY for
  * k > SPEC_MAX_K; SPEC_EWORKSPACE.

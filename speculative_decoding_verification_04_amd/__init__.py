@@ -45,6 +45,12 @@ def spec_strerror(code: int) -> str:
     return library().spec_strerror(int(code)).decode()
 
 
+def spec_set_wait_bound(polls: int) -> int:
+    """Bound the single-launch greedy and tree commit's wait (polls; <= 0: the
+    default); returns the previous setting.  For tests of the incomplete path."""
+    return int(library().spec_set_wait_bound(int(polls)))
+
+
 def _check(code: int, name: str) -> None:
     if code != SPEC_OK:
         raise SpecError(code, name)

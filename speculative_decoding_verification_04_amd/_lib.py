@@ -14,6 +14,7 @@ _F = ctypes.c_float
 # name -> (restype, argtypes), mirroring include/spec_verify.h
 PROTOTYPES = {
     "spec_strerror": (ctypes.c_char_p, [_I]),
+    "spec_set_wait_bound": (_I, [_I]),
     "spec_verify_greedy_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "spec_verify_greedy": (_I, [_P, _I, _I, _I, _I, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
                                 _P, _SZ, _P]),

@@ -38,6 +38,7 @@
 #include "common.h"
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 namespace specv {
@@ -70,6 +71,7 @@ struct GreedyParams {
   int tile_seq;       // linear single launch: sequences per finisher tile (slots
                       // in the tile's polling order); 0: slot row * chunks + c
   int tile_span;      // slots per full tile in that order
+  int max_polls;      // the single-launch finishers' wait bound (polls)
   // tree verification only (k + 1 = N nodes per sequence)
   const int32_t *first_child, *next_sibling;
   int32_t *path;
@@ -289,7 +291,7 @@ constexpr int kTileKeys = 1024;     // chunk keys per tile of the tree finisher
 constexpr int kLoadLanes = kThreads - kWave;                              // waves 0 .. kWaves-2
 constexpr int kKPL = (kTileKeys + kLoadLanes - 1) / kLoadLanes;           // slots per loading lane
 static_assert(kTileSeq <= kLoadLanes, "one loading lane per sequence of a tile");
-constexpr int kMaxPolls = 1 << 22;   // about 4 s of polling: a bound every wait reaches
+constexpr int kMaxPolls = 1 << 22;   // about 4 s of polling: the default bound every wait reaches
 constexpr int kWaitVm0 = 0x0F70;     // s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt not waited for
 
 // The linear finisher folds results as they arrive.  Every lane polls its own
@@ -447,7 +449,7 @@ __device__ void finish_verify(const GreedyParams &P) {
           arrive(P, S, r, rb, rj, m, __builtin_popcount(g));
         }
         if (miss == 0u) break;
-        if (__hip_atomic_load(&S.timed_out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) || ++polls >= kMaxPolls) {
+        if (__hip_atomic_load(&S.timed_out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) || ++polls >= P.max_polls) {
           // the wait is over: the slots still missing count as empty chunks
           // and their sequences are marked incomplete
           __hip_atomic_store(&S.timed_out, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -567,7 +569,7 @@ __device__ void finish_tree(const GreedyParams &P) {
 #pragma unroll
       for (int i = 0; i < kKPL; ++i) present = present && v[i] != 0ull;
       if (__syncthreads_and(present)) break;
-      if (++polls >= kMaxPolls) { timed_out = true; break; }
+      if (++polls >= P.max_polls) { timed_out = true; break; }
       __builtin_amdgcn_s_sleep(1);
       if (loader) {
 #pragma unroll
@@ -873,6 +875,18 @@ __global__ __launch_bounds__(kCommitThreads) void tree_commit_kernel(GreedyParam
 
 using namespace specv;
 
+// Wait bound of the single-launch finishers (0: the default).
+static std::atomic<int> g_wait_bound{0};
+
+static int wait_bound() {
+  const int b = g_wait_bound.load(std::memory_order_relaxed);
+  return b > 0 ? b : kMaxPolls;
+}
+
+extern "C" int spec_set_wait_bound(int polls) {
+  return g_wait_bound.exchange(polls > 0 ? polls : 0, std::memory_order_relaxed);
+}
+
 extern "C" size_t spec_verify_greedy_workspace_bytes(int B, int k, int V, spec_dtype dt) {
   if (B < 1 || k < 1 || V < 1 || k > SPEC_MAX_K) return 0;
   return greedy_ws_bytes(B, k, greedy_chunks(V, dt));
@@ -911,6 +925,7 @@ static int greedy_verify_launch(const void *logits, spec_dtype dt, int B, int k,
   P.path = nullptr;
   P.tile_seq = 0;
   P.tile_span = 0;
+  P.max_polls = wait_bound();
   (void)elt;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
@@ -1081,6 +1096,7 @@ extern "C" int spec_verify_tree(const void *logits, spec_dtype dt, int B, int N,
   P.path = path;
   P.tile_seq = 0;
   P.tile_span = 0;
+  P.max_polls = wait_bound();
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (tree_tile_sequences(N, chunks) >= 1 && nblocks + 1 < INT32_MAX) {

@@ -241,3 +241,34 @@ def test_finisher_tiles_and_phases(B, k, V, want):
     g = W.planted_greedy(rng, rng, B, k, V, 2.0, "bf16", rng.uniform(0.3, 0.95, B))
     remaining = rng.integers(-1, k + 3, B).astype(np.int32)
     _compare(g["logits"], "bf16", g["drafts"], eos_id=int(rng.integers(0, V)), remaining=remaining)
+
+
+def test_incomplete_when_the_wait_bound_is_reached():
+    """A one-poll wait bound makes the committing workgroup stop waiting
+    before most chunk results have arrived: the call still ends, the
+    sequences it gave up on carry SPEC_ST_INCOMPLETE, and every sequence
+    whose status does not carry it is exact.  (The host sets the bound; no
+    kernel waits without end.)"""
+    import speculative_decoding_verification_04_amd as sv
+    note("greedy wait bound of one poll")
+    B, k, V = 64, 8, 128256
+    rng = np.random.default_rng(77)
+    g = W.planted_greedy(rng, rng, B, k, V, 2.0, "bf16", rng.uniform(0.3, 0.95, B))
+    dev = logits_to_device(g["logits"], "bf16")
+    ref = oracle.greedy_verify(g["logits"], "bf16", g["drafts"])
+    w = ws(sv.spec_verify_greedy_workspace_bytes(B, k, V, sv.SPEC_BF16), ("greedy", "bound"))
+    prev = sv.spec_set_wait_bound(1)
+    try:
+        out = host(verify_greedy(dev, g["drafts"], ws_key="bound"))
+    finally:
+        assert sv.spec_set_wait_bound(prev) == 1
+    torch.cuda.synchronize()
+    w.zero_()                       # late chunk results may have landed after the commit gave up
+    inc = (out["status"] & sv.SPEC_ST_INCOMPLETE) != 0
+    assert inc.any()
+    for key in ("accept_len", "emit_count", "out_tokens"):
+        assert np.array_equal(out[key][~inc], ref[key][~inc]), key
+    # with the default bound restored the same workspace gives exact results again
+    again = host(verify_greedy(dev, g["drafts"], ws_key="bound"))
+    for key in KEYS:
+        assert np.array_equal(again[key], ref[key]), key
