@@ -34,7 +34,10 @@
 //     lanes, 16 KB tiles, no reservation, several per CU): there a wide tile
 //     leaves most lanes idle and one plane per CU leaves the memory system
 //     idle between planes (a draft cache of 64-token prefixes re-synced 3x
-//     faster).
+//     faster).  Planes of up to 512 KB take two 512-lane walkers per CU
+//     (56 KB tiles): a CU then alternates between two planes of a few tiles
+//     each (0.60 -> 0.65 of peak for planes of 119 KB, 0.52 -> 0.54 for
+//     260 KB); wider planes keep one wide walker per CU.
 //   * A plane's workgroup reads its own sequence first and issues its first
 //     tile's loads before reducing the batch-wide state (M, validity): the
 //     source range does not depend on M.
@@ -50,6 +53,9 @@ namespace {
 // (limiting residency, holding no data).
 struct WalkWide {                        // 112 KB tiles; 96 KB of the CU's 160 KB LDS: one per CU
   static constexpr int kThreads = 1024, kTileVec = 7, kReserveWords = 24 * 1024;
+};
+struct WalkMid {                         // 56 KB tiles; 72 KB of LDS: two per CU
+  static constexpr int kThreads = 512, kTileVec = 7, kReserveWords = 18 * 1024;
 };
 struct WalkNarrow {                      // 16 KB tiles; several per CU
   static constexpr int kThreads = 256, kTileVec = 4, kReserveWords = 0;
@@ -462,8 +468,11 @@ static int realign_launch(void *kv, spec_dtype dt, int L, int B, int H, int C, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   constexpr long long kWideTileBytes = 16LL * WalkWide::kThreads * WalkWide::kTileVec;
+  constexpr long long kMidPlaneBytes = 512LL << 10;
   if (P.plane_bytes < kWideTileBytes)      // a plane smaller than one wide tile: narrow walkers
     launch_realign<WalkNarrow, int>(P, R, kv, grid, s);
+  else if (P.plane_bytes < kMidPlaneBytes) // planes of a few wide tiles: two walkers per CU
+    launch_realign<WalkMid, int>(P, R, kv, grid, s);
   else if (P.plane_bytes < (1LL << 31))    // vector indices and byte offsets fit 32 bits
     launch_realign<WalkWide, int>(P, R, kv, grid, s);
   else
