@@ -420,7 +420,9 @@ int spec_commit_paged(int B, int k, int page_size, int max_pages, const int32_t 
  *                the root, one per emitted token (their KV slots are kept)
  *   emit_offsets [B + 1] out or NULL; status [B] out or NULL
  *                (SPEC_ST_DRAFT_OOR; SPEC_ST_BAD_STATE for links that do not
- *                point forward inside the tree: that sequence emits nothing)
+ *                point forward inside the tree: that sequence emits nothing;
+ *                SPEC_ST_INCOMPLETE as in spec_verify_greedy, with the same
+ *                zero-fill of the workspace before its next use)
  *   ws           workspace of spec_verify_tree_workspace_bytes(B, N, V, dt)
  * Errors: as spec_verify_greedy; SPEC_ECAPACITY for N > SPEC_TREE_MAX_N.
  *

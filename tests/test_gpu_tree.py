@@ -258,3 +258,33 @@ def test_tree_bench_shape():
         assert np.array_equal(got, want), (l, c, b, h)
     del kv, iv
     torch.cuda.empty_cache()
+
+
+def test_tree_incomplete_when_the_wait_bound_is_reached():
+    """A one-poll wait bound makes the tree commit stop waiting before the
+    chunk results of its first tile have arrived: the call still ends, the
+    sequences it gave up on carry SPEC_ST_INCOMPLETE, and every sequence whose
+    status does not carry it is exact.  With the default bound restored, the
+    same workspace (zero-filled again) gives exact results."""
+    import speculative_decoding_verification_04_amd as sv
+    from tests._gpu import ws
+    B, N, V = 64, 16, 128256
+    note(f"tree wait bound of one poll B={B} N={N} V={V}")
+    g = _tree_case(91, B, N, V, "bf16")
+    ref = oracle.tree_verify(g["logits"], "bf16", g["draft"], g["first_child"], g["next_sibling"])
+    x = logits_to_device(g["logits"], "bf16")
+    w = ws(sv.spec_verify_tree_workspace_bytes(B, N, V, sv.SPEC_BF16), ("greedy", "tree_bound"))
+    prev = sv.spec_set_wait_bound(1)
+    try:
+        out = host(verify_tree(x, g["draft"], g["first_child"], g["next_sibling"], ws_key="tree_bound"))
+    finally:
+        assert sv.spec_set_wait_bound(prev) == 1
+    torch.cuda.synchronize()
+    w.zero_()                       # late chunk results may have landed after the commit gave up
+    inc = (out["status"] & sv.SPEC_ST_INCOMPLETE) != 0
+    assert inc.any()
+    for key in ("accept_len", "emit_count", "out_tokens", "path"):
+        assert np.array_equal(out[key][~inc], ref[key][~inc]), key
+    again = host(verify_tree(x, g["draft"], g["first_child"], g["next_sibling"], ws_key="tree_bound"))
+    for key in KEYS:
+        assert np.array_equal(again[key], ref[key]), key
