@@ -875,7 +875,8 @@ def config_step(dev, np, torch, sv, W, c: int, steps: int = 12, warm: int = 3, n
     i32 = dict(dtype=torch.int32, device=dev)
     kvdt = g["dtype"]
     kv = torch.empty((L, 2, B, H, C, D), dtype=torch.bfloat16 if kvdt == "bf16" else torch.float32, device=dev)
-    W.fill_kv_torch(kv, E, n, torch.as_tensor(W.prefix_tokens(c, B, E + 1), device=dev), kvdt)
+    tokens = torch.as_tensor(W.prefix_tokens(c, B, E + 1), device=dev)
+    W.fill_kv_torch(kv, E, n, tokens, kvdt)
     acc, emit, toks = torch.empty(B, **i32), torch.empty(B, **i32), torch.empty(B, k + 1, **i32)
     offs = torch.empty(B + 1, **i32)
     if mode == "greedy":
@@ -906,12 +907,15 @@ def config_step(dev, np, torch, sv, W, c: int, steps: int = 12, warm: int = 3, n
     moved = torch.zeros(R, dtype=torch.int64, device=dev)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(R)]
 
+    def commit(r):
+        sv.spec_commit_realign_kv(kv, k, Eb[r % 2], Nb[r % 2], emit, Eb[(r + 1) % 2], Nb[(r + 1) % 2], pos, mask,
+                                  bytes_moved=moved[r:r + 1])
+
     def step(r):
         evs[r][0].record()
         verify(r)
         evs[r][1].record()
-        sv.spec_commit_realign_kv(kv, k, Eb[r % 2], Nb[r % 2], emit, Eb[(r + 1) % 2], Nb[(r + 1) % 2], pos, mask,
-                                  bytes_moved=moved[r:r + 1])
+        commit(r)
         evs[r][2].record()
 
     for r in range(warm):
@@ -924,6 +928,27 @@ def config_step(dev, np, torch, sv, W, c: int, steps: int = 12, warm: int = 3, n
     wall = time.perf_counter() - t0
     t_rea = [evs[r][1].elapsed_time(evs[r][2]) * 1e-3 for r in range(warm, R)]
     rea_bytes = [int(moved[r].item()) + 8 * B * C for r in range(warm, R)]
+    # the same R rounds from the initial state, captured in one HIP graph and
+    # replayed once: the steps' GPU time with no host launches between calls;
+    # the replay must leave the cache and end column the eager rounds left
+    kv_eager, e_eager = kv.clone(), int(Eb[R % 2].item())
+    W.fill_kv_torch(kv, E, n, tokens, kvdt)
+    Eb[0].fill_(E)
+    Nb[0].copy_(torch.as_tensor(n, **i32))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(R):
+            verify(r)
+            commit(r)
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ga.record()
+    graph.replay()
+    gb.record()
+    torch.cuda.synchronize()
+    t_graph = ga.elapsed_time(gb) * 1e-3 / R
+    graph_same = bool(torch.equal(kv, kv_eager)) and int(Eb[R % 2].item()) == e_eager
+    del graph, kv_eager
     t_eager = _back_to_back(torch, verify, 6 * nbuf)
     ctr = [0]
 
@@ -945,6 +970,10 @@ def config_step(dev, np, torch, sv, W, c: int, steps: int = 12, warm: int = 3, n
            "rows_per_s": rows * steps / wall, "ms_per_step": wall / steps * 1e3,
            "step_timing": "eager launches through the Python binding, host clock around the timed steps "
                           "(for small workloads the host's launch rate bounds it)",
+           "rows_per_s_graph": rows / t_graph, "ms_per_step_graph": t_graph * 1e3,
+           "step_timing_graph": f"all {R} rounds (warm-up included) captured in one HIP graph from the initial "
+                                "state and replayed once, HIP events around the replay",
+           "graph_equals_eager": graph_same,
            "verify_us_per_launch": t_launch * 1e6,
            "verify_timing": f"GPU time: {6 * nbuf} calls over the rotating inputs captured in one HIP graph, "
                             "median replay / calls",
