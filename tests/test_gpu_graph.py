@@ -171,3 +171,77 @@ def test_commit_and_compaction_replay():
         torch.cuda.synchronize()
         for o, w in zip(outs + [kv], want):
             assert torch.equal(o, w), rep
+
+
+@pytest.mark.parametrize("c", [0, 2])
+def test_rounds_of_verify_and_commit_replay(c):
+    """Several rounds of verification and the realigning commit, chained on
+    the device (each round's end column and lengths feed the next), captured
+    in one graph from the initial state: every replay, after an eager reset of
+    the cache, the end column and the lengths, leaves exactly what the eager
+    rounds leave."""
+    cfg = W.workload(c)
+    R = 4
+    g = W.kv_geometry(c, rounds=R)
+    L, H, D, B, k, n, E, C = (g[x] for x in ("L", "H", "D", "B", "k", "n", "E", "C"))
+    V = cfg["V"]
+    kvdt = g["dtype"]
+    note(f"graph: {R} rounds of verify + commit, workload {c} (B={B} k={k} V={V})")
+    kv = torch.empty((L, 2, B, H, C, D), dtype=torch.bfloat16 if kvdt == "bf16" else torch.float32, device=DEV)
+    tokens = torch.as_tensor(W.prefix_tokens(c, B, E + 1), device=DEV)
+    i32e = dict(dtype=torch.int32, device=DEV)
+    acc, emit, toks, offs = (torch.empty(B, **i32e), torch.empty(B, **i32e), torch.empty(B, k + 1, **i32e),
+                             torch.empty(B + 1, **i32e))
+    if cfg["mode"] == "greedy":
+        rounds = [W.greedy_round(c, round_=r) for r in range(R)]
+        ins = [(logits_to_device(r["logits"], r["dtype"]), i32(r["drafts"])) for r in rounds]
+        dt = sv.SPEC_BF16 if rounds[0]["dtype"] == "bf16" else sv.SPEC_F32
+        ws = sv.workspace(sv.spec_verify_greedy_workspace_bytes(B, k, V, dt), DEV)
+
+        def verify(r):
+            z, d = ins[r]
+            sv.spec_verify_greedy(z, d, acc, emit, toks, ws, emit_offsets=offs)
+    else:
+        rounds = [W.sample_round(c, round_=r) for r in range(R)]
+        ins = [tuple(torch.from_numpy(r[x]).to(DEV) for x in ("p", "q", "drafts", "uniforms")) for r in rounds]
+        ws = sv.workspace(sv.spec_verify_sample_workspace_bytes(B, k, V), DEV)
+
+        def verify(r):
+            p_, q_, d, u = ins[r]
+            sv.spec_verify_sample(p_, q_, d, u, acc, emit, toks, ws, emit_offsets=offs)
+    Eb = [torch.empty(1, **i32e), torch.empty(1, **i32e)]
+    Nb = [torch.empty(B, **i32e), torch.empty(B, **i32e)]
+    pos, mask = torch.empty(B, C, **i32e), torch.empty(B, C, **i32e)
+
+    def reset():
+        W.fill_kv_torch(kv, E, n, tokens, kvdt)
+        Eb[0].fill_(E)
+        Nb[0].copy_(torch.as_tensor(n, **i32e))
+
+    def run_rounds():
+        for r in range(R):
+            verify(r)
+            sv.spec_commit_realign_kv(kv, k, Eb[r % 2], Nb[r % 2], emit, Eb[(r + 1) % 2], Nb[(r + 1) % 2],
+                                      pos, mask)
+
+    def state():
+        return (kv, Eb[R % 2], Nb[R % 2], pos, mask, toks, emit, offs)
+
+    reset()
+    run_rounds()
+    torch.cuda.synchronize()
+    want = [x.clone() for x in state()]
+    assert int(want[1].item()) > E                  # the rounds moved the end column
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_rounds()
+    for rep in range(2):
+        reset()
+        toks.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(state(), want):
+            assert torch.equal(a, b), rep
